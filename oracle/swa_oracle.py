@@ -1,0 +1,214 @@
+"""fp64 numpy oracle for SWA-with-sink, global causal attention and ring-buffer decode.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py, never by the library.  Parity is pinned by
+tests/test_oracle.py and tests/test_golden.py (closed forms, library routines,
+brute force, hand-worked fixtures); no function here is "parity unpinned".
+
+The operator (MiMo-V2-Flash Technical Report digest, section 2.2.2; the formula
+block there lost its symbols in extraction, so the reading below is rebuilt from
+the prose of that section and of the MiMo-V2 blog, section 2.2):
+
+  for query row i of head h, with key set J(i) = the last W keys of the same
+  sequence up to and including i (section 2.2.1: window of 128 tokens),
+      a_j  = scale * <q_i, k_j>                        (scaled logits)
+      m    = max(max_j a_j, sink_h)                    (stabilising max)
+      Z    = exp(sink_h - m) + sum_j exp(a_j - m)      (sink in the denominator)
+      o_i  = sum_j exp(a_j - m) v_j / Z                (the sink has no value)
+      lse  = m + ln Z
+  The sink is one learnable scalar per query head, compared with the scaled
+  logits (it is not multiplied by the scale).  Global-attention layers use the
+  same operator with an unbounded window and no sink (sink = -inf).
+  GQA: query head h reads KV head h // (Hq // Hkv).
+
+Arithmetic is fp64 on the exact input values (bf16 and fp32 convert to fp64
+exactly).  Rows are processed in blocks only to bound memory: every row is the
+definition above, computed independently, with no online rescaling and no
+reordering of its sums beyond numpy's own.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+def _as_f64(x) -> np.ndarray:
+    """Exact fp64 copy of a numpy array or a CPU torch tensor (bf16/fp32/fp64)."""
+    if hasattr(x, "detach"):  # torch tensor; imported lazily so numpy users need no torch
+        x = x.detach().to("cpu")
+        import torch
+
+        x = x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _attend_rows(qr, keys, vals, q_pos, k_pos, seq_start, window, sink, scale):
+    """The definition for a set of query rows of ONE head against candidate keys.
+
+    qr [R, D] query vectors; keys/vals [J, D]; q_pos [R] and k_pos [J] are positions
+    in one packed stream; seq_start [R] is the first position of each row's
+    sequence; window is an int >= 1 or None (unbounded); sink is a float or -inf.
+    Returns o [R, D], lse [R].
+    """
+    a = scale * (qr @ keys.T)  # [R, J] scaled logits
+    valid = (k_pos[None, :] <= q_pos[:, None]) & (k_pos[None, :] >= seq_start[:, None])
+    if window is not None:
+        valid &= k_pos[None, :] >= q_pos[:, None] - window + 1
+    a = np.where(valid, a, NEG_INF)
+    m = np.maximum(a.max(axis=1), sink)
+    e = np.exp(a - m[:, None])  # exp(-inf) == 0 for masked keys
+    z = np.exp(sink - m) + e.sum(axis=1)
+    o = (e @ vals) / z[:, None]
+    lse = m + np.log(z)
+    return o, lse
+
+
+def _check_common(q, k, v, cu_seqlens):
+    if q.ndim != 3 or k.ndim != 3 or v.ndim != 3:
+        raise ValueError("q, k, v must be [tokens, heads, head_dim]")
+    n, hq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != n or k.shape[2] != d:
+        raise ValueError("k and v must be [tokens, kv_heads, head_dim] matching q")
+    hkv = k.shape[1]
+    if hq % hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if cu[0] != 0 or cu[-1] != n or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must rise from 0 to total_tokens")
+    return n, hq, hkv, d, cu
+
+
+def _prefill(q, k, v, sinks, cu_seqlens, window, scale, block):
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    n, hq, hkv, d, cu = _check_common(q, k, v, cu_seqlens)
+    g = hq // hkv
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    sink = np.full(hq, NEG_INF) if sinks is None else _as_f64(sinks).reshape(hq)
+    o = np.zeros((n, hq, d))
+    lse = np.zeros((n, hq))
+    for s in range(len(cu) - 1):
+        c0, c1 = int(cu[s]), int(cu[s + 1])
+        for i0 in range(c0, c1, block):
+            i1 = min(i0 + block, c1)
+            k0 = c0 if window is None else max(c0, i0 - window + 1)
+            q_pos = np.arange(i0, i1)
+            k_pos = np.arange(k0, i1)
+            start = np.full(i1 - i0, c0)
+            for h in range(hq):
+                kvh = h // g
+                oo, ll = _attend_rows(q[i0:i1, h], k[k0:i1, kvh], v[k0:i1, kvh],
+                                      q_pos, k_pos, start, window, sink[h], scale)
+                o[i0:i1, h] = oo
+                lse[i0:i1, h] = ll
+    return o, lse
+
+
+def swa_sink_prefill(q, k, v, sinks, cu_seqlens, window=128, scale=None, block=128):
+    """Causal GQA sliding-window attention with a per-head sink over packed sequences.
+
+    q [N, Hq, D], k/v [N, Hkv, D], sinks [Hq], cu_seqlens [S+1] (0 .. N).  Keys of
+    row i are the last `window` positions of its own sequence up to i.  Returns
+    (o [N, Hq, D], lse [N, Hq]) in fp64.  Follows the operator of the technical
+    report digest, section 2.2.2, with the window of section 2.2.1.
+    """
+    if window is None or int(window) < 1:
+        raise ValueError("window must be an integer >= 1")
+    return _prefill(q, k, v, sinks, cu_seqlens, int(window), scale, block)
+
+
+def ga_causal_prefill(q, k, v, cu_seqlens, scale=None, block=128):
+    """Global-attention layer: the same operator with no window and no sink
+    (technical report digest, section 2.2: GA layers interleaved 1 per 5 SWA)."""
+    return _prefill(q, k, v, None, cu_seqlens, None, scale, block)
+
+
+def prefill_sample_rows(q, k, v, sinks, cu_seqlens, rows, window=128, scale=None):
+    """The definition evaluated only at the (token, head) pairs in `rows`.
+
+    For checks at sizes where the full fp64 output is too large.  window=None
+    means unbounded (GA); sinks=None means no sink.  Returns (o [R, D], lse [R]).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    n, hq, hkv, d, cu = _check_common(q, k, v, cu_seqlens)
+    g = hq // hkv
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    sink = np.full(hq, NEG_INF) if sinks is None else _as_f64(sinks).reshape(hq)
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 2)
+    o = np.zeros((len(rows), d))
+    lse = np.zeros(len(rows))
+    for r, (t, h) in enumerate(rows):
+        s = int(np.searchsorted(cu, t, side="right")) - 1
+        c0 = int(cu[s])
+        k0 = c0 if window is None else max(c0, int(t) - int(window) + 1)
+        kvh = int(h) // g
+        oo, ll = _attend_rows(q[t:t + 1, h], k[k0:t + 1, kvh], v[k0:t + 1, kvh],
+                              np.array([t]), np.arange(k0, t + 1), np.array([c0]),
+                              window, sink[h], scale)
+        o[r], lse[r] = oo[0], ll[0]
+    return o, lse
+
+
+def ring_logical_order(cache_b, head, window):
+    """Cache of one sequence [Hkv, W, D] reordered so logical slot l is first-to-last.
+
+    Logical slot l (0 = oldest cached token) lives at physical slot (head + l) mod W.
+    """
+    idx = (int(head) + np.arange(window)) % window
+    return cache_b[:, idx, :]
+
+
+def swa_sink_decode(q, k_new, v_new, k_cache, v_cache, ring_head, sinks, window=128,
+                    scale=None):
+    """Decode / MTP verify against a W-slot ring buffer per (sequence, KV head).
+
+    q [B, T, Hq, D]; k_new/v_new [B, T, Hkv, D] are the T new tokens (the current
+    one and T-1 drafts), not yet in the ring; k_cache/v_cache [B, Hkv, W, D];
+    ring_head [B] is the physical slot of the oldest cached token.  Each sequence
+    is the prefill definition applied to [ring in logical order] ++ [new tokens]
+    with the same window and sinks; the T new rows are returned.  Query t thus
+    sees cache slots t+1..W-1 and new tokens 0..t (drafts causal among
+    themselves).  The MTP drafts verified in one pass follow the technical report
+    digest, section 2.3.  Returns (o [B, T, Hq, D], lse [B, T, Hq]).
+    """
+    q, k_new, v_new = _as_f64(q), _as_f64(k_new), _as_f64(v_new)
+    k_cache, v_cache = _as_f64(k_cache), _as_f64(v_cache)
+    bsz, t_new, hq, d = q.shape
+    hkv = k_new.shape[2]
+    w = int(window)
+    if k_cache.shape[2] != w:
+        raise ValueError("cache slot count must equal the window")
+    heads = np.asarray(_as_f64(ring_head), dtype=np.int64).reshape(bsz)
+    o = np.zeros((bsz, t_new, hq, d))
+    lse = np.zeros((bsz, t_new, hq))
+    for b in range(bsz):
+        ks = np.concatenate([ring_logical_order(k_cache[b], heads[b], w).transpose(1, 0, 2),
+                             k_new[b]], axis=0)  # [W+T, Hkv, D]
+        vs = np.concatenate([ring_logical_order(v_cache[b], heads[b], w).transpose(1, 0, 2),
+                             v_new[b]], axis=0)
+        qs = np.zeros((w + t_new, hq, d))
+        qs[w:] = q[b]
+        ob, lb = _prefill(qs, ks, vs, sinks, [0, w + t_new], w, scale, block=w + t_new)
+        o[b] = ob[w:]
+        lse[b] = lb[w:]
+    return o, lse
+
+
+def hybrid_block(layers, window=128, scale=None):
+    """Five SWA-with-sink layers then one GA layer, each on its own inputs.
+
+    `layers` is a list of dicts with q, k, v, cu_seqlens and (SWA only) sinks; the
+    last entry is the GA layer.  There is no data flow between layers: only the
+    attention operators are evaluated (technical report digest, section 2.2.1:
+    5 SWA layers per GA layer).  Returns a list of (o, lse).
+    """
+    out = []
+    for li, lay in enumerate(layers):
+        if li == len(layers) - 1:
+            out.append(ga_causal_prefill(lay["q"], lay["k"], lay["v"], lay["cu_seqlens"], scale))
+        else:
+            out.append(swa_sink_prefill(lay["q"], lay["k"], lay["v"], lay["sinks"],
+                                        lay["cu_seqlens"], window, scale))
+    return out

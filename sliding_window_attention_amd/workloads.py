@@ -1,0 +1,205 @@
+"""Seeded synthetic workloads and closed-form work counters.
+
+This module holds no attention arithmetic: it draws the input tensors (shared by
+the GPU path and the CPU oracle so both see identical values) and counts the
+algorithmic FLOPs and bytes used for roofline reporting.
+
+Input recipe: every tensor is drawn in fp32 on the CPU from
+``torch.Generator().manual_seed(seed)`` in the order Q, K, V, sinks, then
+extras (ring heads, sequence lengths), values ~ N(0, 1); tensors of bf16
+workloads are then rounded to bf16 (round-to-nearest-even).  Sinks stay fp32.
+There is no dataset: the pages describe no public benchmark for this operator.
+
+Shapes follow the pages: window 128 (MiMo-V2-Flash Technical Report digest,
+section 2.2.1), GQA with 4 KV heads in SWA layers (ICML 2026 keynote write-up,
+section 02), a 5:1 SWA:GA interleave (digest, section 2.2.1) and 1 + 3 MTP draft
+tokens verified together (digest, section 2.3).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str  # "prefill" | "decode" | "hybrid" | "varlen"
+    dtype: str  # "f32" | "bf16"
+    seq_len: int = 0  # total packed tokens for prefill kinds
+    num_q_heads: int = 32
+    num_kv_heads: int = 4
+    head_dim: int = 128
+    window: int = 128
+    batch: int = 0  # decode sequences
+    t_new: int = 0  # decode query tokens per sequence
+    num_seqs: int = 1  # varlen sequence count
+    seed: int = 0
+    extra: dict = field(default_factory=dict)
+
+
+WORKLOADS = {
+    # Tiny fp32 SWA-sink forward; the oracle finishes in well under a second.
+    "tiny_fp32": Workload("tiny_fp32", "prefill", "f32", seq_len=512, num_q_heads=4,
+                          num_kv_heads=1, head_dim=64, seed=1000),
+    # One SWA layer prefill at 32K tokens, 32 q / 4 kv heads, head_dim 128.
+    "swa_prefill_32k": Workload("swa_prefill_32k", "prefill", "bf16", seq_len=32768, seed=2000),
+    # Batched ring-buffer decode, one query token per sequence.
+    "decode_t1": Workload("decode_t1", "decode", "bf16", batch=256, t_new=1, seed=3000),
+    # MTP verify: 1 + 3 draft tokens per sequence, causal among themselves.
+    "decode_t4": Workload("decode_t4", "decode", "bf16", batch=256, t_new=4, seed=3100),
+    # Hybrid block: 5 SWA-sink layers (seeds 4000..4004) + 1 GA layer (seed 4005).
+    "hybrid_5to1_32k": Workload("hybrid_5to1_32k", "hybrid", "bf16", seq_len=32768, seed=4000),
+    # Packed varlen prefill: 8 log-normal sequence lengths summing to 262144.
+    "varlen_262k": Workload("varlen_262k", "varlen", "bf16", seq_len=262144, num_seqs=8,
+                            seed=5000),
+}
+
+
+def _torch_dtype(name: str):
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def lognormal_lengths(total: int, num_seqs: int, seed: int, sigma: float = 1.0) -> list[int]:
+    """Sequence lengths x_s ~ LogNormal(0, sigma) rescaled to sum to `total`.
+
+    floor(x_s / sum(x) * total), the remainder handed out by largest fractional
+    part, every length at least 1.
+    """
+    rng = np.random.default_rng(seed)
+    x = rng.lognormal(mean=0.0, sigma=sigma, size=num_seqs)
+    raw = x / x.sum() * total
+    lens = np.floor(raw).astype(np.int64)
+    lens = np.maximum(lens, 1)
+    rem = int(total - lens.sum())
+    order = np.argsort(-(raw - np.floor(raw)), kind="stable")
+    i = 0
+    while rem != 0:
+        j = order[i % num_seqs]
+        if rem > 0:
+            lens[j] += 1
+            rem -= 1
+        elif lens[j] > 1:
+            lens[j] -= 1
+            rem += 1
+        i += 1
+    return [int(v) for v in lens]
+
+
+def cu_from_lengths(lengths) -> torch.Tensor:
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + int(n))
+    return torch.tensor(cu, dtype=torch.int32)
+
+
+def make_prefill(seq_lens, num_q_heads, num_kv_heads, head_dim, dtype, seed, with_sinks=True):
+    """Packed prefill inputs: q [N, Hq, D], k/v [N, Hkv, D], sinks [Hq] fp32 (or None),
+    cu_seqlens [S+1] int32.  All on the CPU."""
+    lens = [int(x) for x in seq_lens]
+    n = sum(lens)
+    gen = torch.Generator().manual_seed(int(seed))
+    td = _torch_dtype(dtype)
+    q = torch.randn(n, num_q_heads, head_dim, generator=gen).to(td)
+    k = torch.randn(n, num_kv_heads, head_dim, generator=gen).to(td)
+    v = torch.randn(n, num_kv_heads, head_dim, generator=gen).to(td)
+    sinks = torch.randn(num_q_heads, generator=gen) if with_sinks else None
+    return {"q": q, "k": k, "v": v, "sinks": sinks, "cu_seqlens": cu_from_lengths(lens),
+            "max_seqlen": max(lens) if lens else 0, "lengths": lens}
+
+
+def make_decode(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, dtype, seed):
+    """Decode inputs: q [B, T, Hq, D], k_new/v_new [B, T, Hkv, D], full caches
+    [B, Hkv, W, D], ring_head [B] int32 ~ U[0, W), sinks [Hq] fp32.  CPU tensors."""
+    gen = torch.Generator().manual_seed(int(seed))
+    td = _torch_dtype(dtype)
+    q = torch.randn(batch, t_new, num_q_heads, head_dim, generator=gen).to(td)
+    k_new = torch.randn(batch, t_new, num_kv_heads, head_dim, generator=gen).to(td)
+    v_new = torch.randn(batch, t_new, num_kv_heads, head_dim, generator=gen).to(td)
+    sinks = torch.randn(num_q_heads, generator=gen)
+    k_cache = torch.randn(batch, num_kv_heads, window, head_dim, generator=gen).to(td)
+    v_cache = torch.randn(batch, num_kv_heads, window, head_dim, generator=gen).to(td)
+    ring_head = torch.randint(0, window, (batch,), generator=gen, dtype=torch.int64).to(torch.int32)
+    return {"q": q, "k_new": k_new, "v_new": v_new, "k_cache": k_cache, "v_cache": v_cache,
+            "ring_head": ring_head, "sinks": sinks}
+
+
+def make_workload(name: str, layer: int = 0):
+    """Inputs of a named workload (for 'hybrid_5to1_32k', layer 0..4 are SWA, 5 is GA)."""
+    w = WORKLOADS[name]
+    if w.kind == "prefill":
+        return make_prefill([w.seq_len], w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype, w.seed)
+    if w.kind == "hybrid":
+        return make_prefill([w.seq_len], w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype,
+                            w.seed + layer, with_sinks=layer < 5)
+    if w.kind == "varlen":
+        lens = lognormal_lengths(w.seq_len, w.num_seqs, w.seed)
+        return make_prefill(lens, w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype, w.seed)
+    if w.kind == "decode":
+        return make_decode(w.batch, w.t_new, w.num_q_heads, w.num_kv_heads, w.head_dim, w.window,
+                           w.dtype, w.seed)
+    raise KeyError(name)
+
+
+# ---------------------------------------------------------------------------
+# Closed-form work counters (algorithmic work only: masked tile work never counts)
+# ---------------------------------------------------------------------------
+
+def pairs(length: int, window) -> int:
+    """Unmasked (query, key) pairs of one causal sequence of `length` tokens with
+    a window of `window` keys (None = unbounded)."""
+    n = int(length)
+    if window is None or n <= window:
+        return n * (n + 1) // 2
+    w = int(window)
+    return w * (w + 1) // 2 + w * (n - w)
+
+
+def prefill_flops(lengths, num_q_heads, head_dim, window) -> int:
+    """QK^T plus PV: 4 * D FLOPs per unmasked (query, key) pair per query head."""
+    return 4 * head_dim * num_q_heads * sum(pairs(n, window) for n in lengths)
+
+
+def prefill_bytes(total_tokens, num_q_heads, num_kv_heads, head_dim, elem_bytes, with_lse=True):
+    """Q, K, V read once, O written once, LSE (fp32) written once."""
+    per_tok = (2 * num_q_heads + 2 * num_kv_heads) * head_dim * elem_bytes
+    if with_lse:
+        per_tok += 4 * num_q_heads
+    return total_tokens * per_tok
+
+
+def decode_flops(batch, t_new, num_q_heads, head_dim, window) -> int:
+    """Every query row sees exactly `window` keys (W-1-t ring slots + t+1 new)."""
+    return 4 * head_dim * num_q_heads * batch * t_new * window
+
+
+def decode_bytes(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, elem_bytes,
+                 with_lse=True):
+    """Live ring slots (W-1: the oldest slot is outside every query's window),
+    the T new K/V rows, Q and O; LSE fp32."""
+    kv = 2 * batch * num_kv_heads * head_dim * elem_bytes * ((window - 1) + t_new)
+    qo = 2 * batch * t_new * num_q_heads * head_dim * elem_bytes
+    lse = 4 * batch * t_new * num_q_heads if with_lse else 0
+    return kv + qo + lse
+
+
+def workload_work(name: str):
+    """(flops, bytes) of one pass of a named workload as its kind defines it."""
+    w = WORKLOADS[name]
+    eb = 4 if w.dtype == "f32" else 2
+    if w.kind == "decode":
+        return (decode_flops(w.batch, w.t_new, w.num_q_heads, w.head_dim, w.window),
+                decode_bytes(w.batch, w.t_new, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                             w.window, eb))
+    if w.kind == "varlen":
+        lens = lognormal_lengths(w.seq_len, w.num_seqs, w.seed)
+    else:
+        lens = [w.seq_len]
+    fl = prefill_flops(lens, w.num_q_heads, w.head_dim, w.window)
+    by = prefill_bytes(sum(lens), w.num_q_heads, w.num_kv_heads, w.head_dim, eb)
+    if w.kind == "hybrid":
+        ga = prefill_flops(lens, w.num_q_heads, w.head_dim, None)
+        return 5 * fl + ga, 6 * by
+    return fl, by

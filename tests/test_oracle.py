@@ -1,0 +1,314 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test ties oracle.swa_oracle to something other than itself: a library routine
+(torch's scaled_dot_product_attention / logsumexp in fp64 on the CPU), a closed
+form, an invariant, or brute-force enumeration (oracle.brute).  The operator is
+the one of the MiMo-V2-Flash Technical Report digest, section 2.2.2 (learnable
+sink term in the softmax denominator), with the causal 128-token window of
+section 2.2.1 and GQA (ICML 2026 keynote write-up, section 02).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+from oracle import brute
+from oracle import swa_oracle as orc
+from sliding_window_attention_amd import workloads as wl
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _rand(shape, rng):
+    return rng.standard_normal(shape)
+
+
+def _inputs(lens, hq, hkv, d, seed, sink_scale=1.0):
+    rng = np.random.default_rng(seed)
+    n = sum(lens)
+    q = _rand((n, hq, d), rng)
+    k = _rand((n, hkv, d), rng)
+    v = _rand((n, hkv, d), rng)
+    sinks = sink_scale * _rand((hq,), rng)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return q, k, v, sinks, cu
+
+
+def _sdpa_reference(q, k, v, lens, window, scale):
+    """torch SDPA (fp64, CPU) with an explicit boolean band mask per sequence; no sink."""
+    hq, hkv = q.shape[1], k.shape[1]
+    outs, lses = [], []
+    c0 = 0
+    for n in lens:
+        qs = torch.from_numpy(q[c0:c0 + n]).permute(1, 0, 2)  # [Hq, n, D]
+        ks = torch.from_numpy(k[c0:c0 + n]).repeat_interleave(hq // hkv, dim=1).permute(1, 0, 2)
+        vs = torch.from_numpy(v[c0:c0 + n]).repeat_interleave(hq // hkv, dim=1).permute(1, 0, 2)
+        i = torch.arange(n)[:, None]
+        j = torch.arange(n)[None, :]
+        mask = j <= i
+        if window is not None:
+            mask &= j >= i - window + 1
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qs.unsqueeze(0), ks.unsqueeze(0), vs.unsqueeze(0), attn_mask=mask, scale=scale)[0]
+        logits = scale * (qs @ ks.transpose(1, 2))
+        logits = logits.masked_fill(~mask, float("-inf"))
+        outs.append(o.permute(1, 0, 2).numpy())
+        lses.append(torch.logsumexp(logits, dim=-1).permute(1, 0).numpy())
+        c0 += n
+    return np.concatenate(outs), np.concatenate(lses)
+
+
+# ---- pin 1: sink -> -inf is ordinary causal-window softmax attention -------------
+
+@pytest.mark.parametrize("lens,window", [([37], 5), ([64, 3, 30], 16), ([50], 1), ([20, 20], 128)])
+def test_pin1_no_sink_equals_library_sdpa(lens, window):
+    q, k, v, _, cu = _inputs(lens, 4, 2, 8, seed=1)
+    sinks = np.full(4, -np.inf)
+    o, lse = orc.swa_sink_prefill(q, k, v, sinks, cu, window, block=7)
+    o_ref, lse_ref = _sdpa_reference(q, k, v, lens, window, 1 / math.sqrt(8))
+    np.testing.assert_allclose(o, o_ref, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse, lse_ref, atol=1e-12, rtol=0)
+
+
+# ---- pin 2: W >= L is full causal attention; GA equals library causal SDPA --------
+
+def test_pin2_large_window_is_global_and_ga_is_causal_sdpa():
+    lens = [33, 17]
+    q, k, v, _, cu = _inputs(lens, 4, 4, 16, seed=2)
+    ga_o, ga_l = orc.ga_causal_prefill(q, k, v, cu)
+    sw_o, sw_l = orc.swa_sink_prefill(q, k, v, np.full(4, -np.inf), cu, window=max(lens))
+    np.testing.assert_allclose(sw_o, ga_o, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(sw_l, ga_l, atol=1e-12, rtol=0)
+    o_ref, l_ref = _sdpa_reference(q, k, v, lens, None, 0.25)
+    np.testing.assert_allclose(ga_o, o_ref, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(ga_l, l_ref, atol=1e-12, rtol=0)
+
+
+# ---- pin 3: a large sink drives outputs to 0 and lse to the sink -----------------
+
+def test_pin3_large_sink_drives_output_to_zero():
+    lens = [40]
+    q, k, v, _, cu = _inputs(lens, 2, 1, 8, seed=3)
+    sinks = np.array([50.0, 60.0])
+    o, lse = orc.swa_sink_prefill(q, k, v, sinks, cu, 16)
+    a_max = np.abs(q).sum(-1).max() * np.abs(k).max() / math.sqrt(8)  # crude logit bound
+    bound = math.exp(a_max - 50.0) * 16 * np.abs(v).max()
+    assert np.abs(o).max() < max(bound, 1e-15)
+    assert np.abs(o).max() < 1e-12
+    np.testing.assert_allclose(lse[:, 0], 50.0, atol=1e-12)
+    np.testing.assert_allclose(lse[:, 1], 60.0, atol=1e-12)
+
+
+# ---- pin 4: brute-force enumeration equals the vectorised oracle ------------------
+
+@settings(max_examples=40, deadline=None)
+@given(
+    lens=st.lists(st.integers(1, 9), min_size=1, max_size=3),
+    d=st.integers(1, 6),
+    g=st.sampled_from([1, 2, 4]),
+    hkv=st.integers(1, 2),
+    window=st.sampled_from([1, 2, 3, 5, None]),
+    sink_mode=st.sampled_from(["normal", "none", "big"]),
+    seed=st.integers(0, 10_000),
+)
+def test_pin4_brute_force_matches_oracle(lens, d, g, hkv, window, sink_mode, seed):
+    hq = g * hkv
+    q, k, v, sinks, cu = _inputs(lens, hq, hkv, d, seed, sink_scale=3.0)
+    if sink_mode == "none":
+        sinks = None
+    elif sink_mode == "big":
+        sinks = sinks + 20.0
+    if window is None and sinks is None:
+        o, lse = orc.ga_causal_prefill(q, k, v, cu, block=4)
+    else:
+        o, lse = orc.swa_sink_prefill(q, k, v, np.full(hq, -np.inf) if sinks is None else sinks,
+                                      cu, 10_000 if window is None else window, block=4)
+    ob, lb = brute.attention(q.tolist(), k.tolist(), v.tolist(),
+                             None if sinks is None else sinks.tolist(), cu.tolist(), window)
+    np.testing.assert_allclose(o, np.array(ob), atol=1e-13, rtol=1e-13)
+    np.testing.assert_allclose(lse, np.array(lb), atol=1e-13, rtol=1e-13)
+
+
+# ---- pin 5: closed form at W = 1 (and for the first row at any W) ----------------
+
+def test_pin5_window_one_closed_form():
+    lens = [12, 5]
+    q, k, v, sinks, cu = _inputs(lens, 4, 2, 8, seed=5)
+    o, lse = orc.swa_sink_prefill(q, k, v, sinks, cu, 1)
+    g = 2
+    for n in range(sum(lens)):
+        for h in range(4):
+            a = float(q[n, h] @ k[n, h // g]) / math.sqrt(8)
+            sig = 1.0 / (1.0 + math.exp(-(a - sinks[h])))
+            np.testing.assert_allclose(o[n, h], sig * v[n, h // g], atol=1e-14, rtol=1e-13)
+            np.testing.assert_allclose(lse[n, h], np.logaddexp(a, sinks[h]), atol=1e-13)
+    o128, l128 = orc.swa_sink_prefill(q, k, v, sinks, cu, 128)
+    for c0 in cu[:-1]:  # row 0 of every sequence sees only itself at any window
+        np.testing.assert_allclose(o128[c0], o[c0], atol=1e-14)
+        np.testing.assert_allclose(l128[c0], lse[c0], atol=1e-14)
+
+
+# ---- pin 6: exact sink identity against plain (sink-free) attention -------------
+
+@pytest.mark.parametrize("window", [1, 4, 128])
+def test_pin6_sink_identity(window):
+    lens = [30, 9]
+    q, k, v, sinks, cu = _inputs(lens, 4, 1, 8, seed=6, sink_scale=2.0)
+    o_s, l_s = orc.swa_sink_prefill(q, k, v, sinks, cu, window)
+    o_0, l_0 = orc.swa_sink_prefill(q, k, v, np.full(4, -np.inf), cu, window)
+    factor = 1.0 / (1.0 + np.exp(sinks[None, :] - l_0))  # sigmoid(lse0 - sink)
+    np.testing.assert_allclose(o_s, o_0 * factor[..., None], atol=1e-13, rtol=1e-12)
+    np.testing.assert_allclose(l_s, np.logaddexp(l_0, sinks[None, :]), atol=1e-13)
+
+
+# ---- pin 7: mass conservation -----------------------------------------------------
+
+def test_pin7_mass_conservation():
+    lens = [11, 6]
+    q, k, v, sinks, cu = _inputs(lens, 2, 1, 4, seed=7)
+    window = 4
+    _, lse = orc.swa_sink_prefill(q, k, v, sinks, cu, window)
+    _, _, weights = brute.attention(q.tolist(), k.tolist(), v.tolist(), sinks.tolist(),
+                                    cu.tolist(), window, return_weights=True)
+    for (n, h), (pk, ps) in weights.items():
+        assert math.isclose(math.fsum([p for _, p in pk] + [ps]), 1.0, abs_tol=1e-14)
+        # the oracle's lse normalises the same weights
+        s = next(i for i in range(len(cu) - 1) if cu[i] <= n < cu[i + 1])
+        lo = max(cu[s], n - window + 1)
+        a = [float(q[n, h] @ k[j, 0]) / 2.0 for j in range(lo, n + 1)]
+        tot = math.fsum([math.exp(x - lse[n, h]) for x in a] + [math.exp(sinks[h] - lse[n, h])])
+        assert math.isclose(tot, 1.0, abs_tol=1e-13)
+
+
+# ---- pin 8: constant V gives o = c * (1 - p_sink) --------------------------------
+
+def test_pin8_constant_values():
+    lens = [25]
+    q, k, v, sinks, cu = _inputs(lens, 4, 2, 8, seed=8)
+    c = np.linspace(-2, 3, 8)
+    v[:] = c
+    o, lse = orc.swa_sink_prefill(q, k, v, sinks, cu, 6)
+    expect = c[None, None, :] * (1.0 - np.exp(sinks[None, :] - lse))[..., None]
+    np.testing.assert_allclose(o, expect, atol=1e-14, rtol=1e-13)
+
+
+# ---- pin 9: decode == prefill on [ring in logical order ++ new]; brute; rotation ---
+
+def _decode_inputs(b, t, hq, hkv, w, d, seed):
+    rng = np.random.default_rng(seed)
+    return dict(q=_rand((b, t, hq, d), rng), k_new=_rand((b, t, hkv, d), rng),
+                v_new=_rand((b, t, hkv, d), rng), k_cache=_rand((b, hkv, w, d), rng),
+                v_cache=_rand((b, hkv, w, d), rng), ring_head=rng.integers(0, w, b),
+                sinks=_rand((hq,), rng))
+
+
+@pytest.mark.parametrize("t", [1, 2, 4])
+def test_pin9_decode_brute_and_prefill_equivalence(t):
+    w, d = 6, 4
+    x = _decode_inputs(3, t, 4, 2, w, d, seed=9 + t)
+    o, lse = orc.swa_sink_decode(**x, window=w)
+    ob, lb = brute.decode(x["q"].tolist(), x["k_new"].tolist(), x["v_new"].tolist(),
+                          x["k_cache"].tolist(), x["v_cache"].tolist(), x["ring_head"].tolist(),
+                          x["sinks"].tolist(), w)
+    np.testing.assert_allclose(o, np.array(ob), atol=1e-13, rtol=1e-13)
+    np.testing.assert_allclose(lse, np.array(lb), atol=1e-13)
+    # prefill of the concatenated stream, built here by explicit slot arithmetic
+    for b in range(3):
+        order = [(x["ring_head"][b] + l) % w for l in range(w)]
+        ks = np.concatenate([x["k_cache"][b][:, order].transpose(1, 0, 2), x["k_new"][b]])
+        vs = np.concatenate([x["v_cache"][b][:, order].transpose(1, 0, 2), x["v_new"][b]])
+        qs = np.concatenate([np.zeros((w, 4, d)), x["q"][b]])
+        op, lp = orc.swa_sink_prefill(qs, ks, vs, x["sinks"], [0, w + t], w)
+        np.testing.assert_allclose(o[b], op[w:], atol=1e-13)
+        np.testing.assert_allclose(lse[b], lp[w:], atol=1e-13)
+
+
+def test_pin9_ring_rotation_invariance():
+    w = 8
+    x = _decode_inputs(4, 3, 2, 1, w, 4, seed=90)
+    o, lse = orc.swa_sink_decode(**x, window=w)
+    for s in (1, 3, 7):
+        y = dict(x)
+        y["k_cache"] = np.roll(x["k_cache"], s, axis=2)
+        y["v_cache"] = np.roll(x["v_cache"], s, axis=2)
+        y["ring_head"] = (x["ring_head"] + s) % w
+        o2, l2 = orc.swa_sink_decode(**y, window=w)
+        np.testing.assert_allclose(o2, o, atol=1e-14)
+        np.testing.assert_allclose(l2, lse, atol=1e-14)
+
+
+def test_pin9_oldest_slot_is_never_read():
+    w = 5
+    x = _decode_inputs(2, 2, 2, 1, w, 4, seed=91)
+    o, _ = orc.swa_sink_decode(**x, window=w)
+    y = {kk: np.array(vv, copy=True) for kk, vv in x.items()}
+    for b in range(2):
+        y["k_cache"][b, :, y["ring_head"][b]] = 1e6
+        y["v_cache"][b, :, y["ring_head"][b]] = -1e6
+    o2, _ = orc.swa_sink_decode(**y, window=w)
+    np.testing.assert_allclose(o2, o, atol=1e-14)
+
+
+# ---- pin 10: GQA equals MHA with K, V repeated along heads -----------------------
+
+def test_pin10_gqa_equals_repeated_mha():
+    lens = [21, 8]
+    q, k, v, sinks, cu = _inputs(lens, 8, 2, 8, seed=10)
+    o, lse = orc.swa_sink_prefill(q, k, v, sinks, cu, 5)
+    o2, l2 = orc.swa_sink_prefill(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), sinks, cu, 5)
+    np.testing.assert_allclose(o, o2, atol=1e-14)
+    np.testing.assert_allclose(lse, l2, atol=1e-14)
+    # a head reads KV head h // G: changing KV head 1 must leave heads 0..3 untouched
+    k3 = k.copy()
+    k3[:, 1] += 1.0
+    o3, _ = orc.swa_sink_prefill(q, k3, v, sinks, cu, 5)
+    np.testing.assert_allclose(o3[:, :4], o[:, :4], atol=0)
+    assert np.abs(o3[:, 4:] - o[:, 4:]).max() > 1e-6
+
+
+# ---- pin 11: varlen == independent sequences; packing order does not matter --------
+
+def test_pin11_varlen_independence_and_order():
+    lens = [13, 1, 40, 7]
+    q, k, v, sinks, cu = _inputs(lens, 4, 2, 8, seed=11)
+    o, lse = orc.swa_sink_prefill(q, k, v, sinks, cu, 16)
+    for s in range(len(lens)):
+        a, b = cu[s], cu[s + 1]
+        os_, ls_ = orc.swa_sink_prefill(q[a:b], k[a:b], v[a:b], sinks, [0, b - a], 16)
+        np.testing.assert_allclose(o[a:b], os_, atol=1e-14)
+        np.testing.assert_allclose(lse[a:b], ls_, atol=1e-14)
+    perm = [2, 0, 3, 1]
+    idx = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in perm])
+    cu_p = np.concatenate([[0], np.cumsum([lens[s] for s in perm])])
+    o_p, l_p = orc.swa_sink_prefill(q[idx], k[idx], v[idx], sinks, cu_p, 16)
+    np.testing.assert_allclose(o_p, o[idx], atol=1e-14)
+    np.testing.assert_allclose(l_p, lse[idx], atol=1e-14)
+
+
+# ---- pin 12: the unmasked-pair counter equals the mask it counts -----------------
+
+@pytest.mark.parametrize("n,w", [(1, 128), (5, 128), (128, 128), (129, 128), (1000, 128),
+                                 (37, 1), (37, 5), (64, None)])
+def test_pin12_pair_count(n, w):
+    count = 0
+    for i in range(n):
+        lo = 0 if w is None else max(0, i - w + 1)
+        count += i - lo + 1
+    assert wl.pairs(n, w) == count
+
+
+# ---- pin 13: hybrid vs full attention FLOPs against the pages' "7x" claim ---------
+
+def test_pin13_hybrid_flop_ratio_consistent_with_pages():
+    # Keynote write-up, section 02: a 7:1 hybrid at 1M context cuts attention
+    # FLOPs and KV cache about 7x.  8 full layers vs 1 full + 7 SWA(128) layers:
+    n = 1 << 20
+    full = 8 * wl.pairs(n, None)
+    hyb = 1 * wl.pairs(n, None) + 7 * wl.pairs(n, 128)
+    ratio = full / hyb
+    assert 7.0 <= ratio < 8.0
+    assert abs(ratio - 7.99) < 0.01
+    kv_ratio = (8 * n) / (1 * n + 7 * 128)
+    assert 7.0 <= kv_ratio < 8.0
