@@ -1,0 +1,325 @@
+"""Benchmark of the hybrid sliding-window attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+
+A step is one sliding-window-with-sink prefill of the 32K-token layer (32 query
+heads / 4 KV heads, head_dim 128, window 128, bf16 in/out, fp32 LSE) with inputs
+resident in HBM.  Input sets are rotated across steps (distinct buffers, 4 x 608
+MB) so that no step finds its inputs in the 256 MB Infinity Cache.  Timing uses
+HIP events on the stream the kernels are launched on.  The printed JSON line
+reports the prefill TFLOP/s (unmasked (query, key) pairs only), the achieved
+HBM GB/s of the kernel against the 8 TB/s peak, and, under "extra", the batched
+decode / MTP-verify GB/s, the global-attention layer, the 5:1 hybrid block and the
+262K-token varlen prefill, each timed the same way.  "cpu_baseline" times the fp64
+oracle on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+PRIMARY = "swa_prefill_32k"
+METRIC = "SWA-sink prefill TFLOP/s (% MFMA peak); decode GB/s (% HBM peak)"
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _to(x, dev):
+    return {k: (v.to(dev) if hasattr(v, "to") and hasattr(v, "dtype") else v) for k, v in x.items()}
+
+
+def _clone_sets(x, n):
+    sets = [x]
+    for _ in range(n - 1):
+        sets.append({k: (v.clone() if hasattr(v, "clone") else v) for k, v in x.items()})
+    return sets
+
+
+def _time_calls(fn, sets, steps, warmup):
+    """Warm up, then time `steps` calls (set rotated per call) with HIP events.
+
+    Returns (per-call kernel milliseconds list, wall milliseconds of the timed region)."""
+    import torch
+
+    for s in range(warmup):
+        fn(sets[s % len(sets)])
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    region0.record()
+    for s in range(steps):
+        starts[s].record()
+        fn(sets[s % len(sets)])
+        ends[s].record()
+    region1.record()
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    return per, region0.elapsed_time(region1)
+
+
+def _prefill_fn(window, ga=False):
+    import sliding_window_attention_amd as swa
+
+    def fn(x):
+        if ga:
+            swa.ga_causal_prefill(x["q"], x["k"], x["v"], x["cu_seqlens"], x["max_seqlen"],
+                                  out=x["out"], lse=x["lse"])
+        else:
+            swa.swa_sink_prefill(x["q"], x["k"], x["v"], x["sinks"], x["cu_seqlens"], x["max_seqlen"],
+                                 window=window, out=x["out"], lse=x["lse"])
+    return fn
+
+
+def _decode_fn():
+    import sliding_window_attention_amd as swa
+
+    def fn(x):
+        swa.swa_sink_decode(x["q"], x["k_new"], x["v_new"], x["k_cache"], x["v_cache"], x["ring_head"],
+                            x["sinks"], out=x["out"], lse=x["lse"])
+    return fn
+
+
+def _with_outputs(x, kind):
+    import torch
+
+    if kind == "decode":
+        b, t, hq, _ = x["q"].shape
+        x["out"] = torch.empty_like(x["q"])
+        x["lse"] = torch.empty((b, t, hq), dtype=torch.float32, device=x["q"].device)
+    else:
+        n, hq, _ = x["q"].shape
+        x["out"] = torch.empty_like(x["q"])
+        x["lse"] = torch.empty((n, hq), dtype=torch.float32, device=x["q"].device)
+    return x
+
+
+def _stats(ms):
+    s = sorted(ms)
+    return {"mean_ms": sum(s) / len(s), "median_ms": s[len(s) // 2], "min_ms": s[0]}
+
+
+def kernel_source_digest() -> str:
+    """Hash of the HIP sources; traffic counters are only reported for the kernel
+    version they were taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sliding_window_attention_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel: str, algorithmic_bytes: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(sample_tokens=8192):
+    """The fp64 oracle on the first `sample_tokens` tokens of the 32K layer."""
+    import numpy as np
+
+    from oracle import swa_oracle as orc
+    from sliding_window_attention_amd import workloads as wl
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    x = wl.make_prefill([sample_tokens], 32, 4, 128, "bf16", seed=wl.WORKLOADS[PRIMARY].seed)
+    t0 = time.perf_counter()
+    orc.swa_sink_prefill(x["q"], x["k"], x["v"], x["sinks"], np.array([0, sample_tokens]), 128)
+    dt = time.perf_counter() - t0
+    flops = wl.prefill_flops([sample_tokens], 32, 128, 128)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {sample_tokens} of 32768 tokens (all 32 heads), fp64 numpy, {dt:.2f} s",
+            "seconds": dt}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true", help="time only the primary workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--only", choices=["prefill", "decode", "ga", "varlen"], default=None,
+                    help="time a single workload (for profiling runs); prints no JSON line")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import sliding_window_attention_amd as swa
+    from sliding_window_attention_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = "cuda:0"
+    swa.library()
+    steps, warmup = args.steps, args.warmup
+
+    if args.only is not None:
+        name = {"prefill": PRIMARY, "decode": "decode_t4", "ga": "hybrid_5to1_32k",
+                "varlen": "varlen_262k"}[args.only]
+        layer = 5 if args.only == "ga" else 0
+        x = _with_outputs(_to(wl.make_workload(name, layer), dev), "decode" if args.only == "decode" else "p")
+        fn = _decode_fn() if args.only == "decode" else _prefill_fn(128, ga=args.only == "ga")
+        per, _ = _time_calls(fn, _clone_sets(x, 4 if args.only != "varlen" else 1), steps, warmup)
+        _log(f"{name}: {_stats(per)}")
+        return 0
+
+    # ---------------- primary: SWA-sink prefill, 32K tokens ----------------
+    _log("generating swa_prefill_32k inputs")
+    x = _with_outputs(_to(wl.make_workload(PRIMARY), dev), "prefill")
+    sets = _clone_sets(x, 4)
+    per, region_ms = _time_calls(_prefill_fn(128), sets, steps, warmup)
+    flops, nbytes = wl.workload_work(PRIMARY)
+    st = _stats(per)
+    ms_per_step = region_ms / steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    kernel_s = st["mean_ms"] * 1e-3
+    achieved = nbytes / kernel_s / 1e9
+    traffic = _traffic("swa_window_kernel", nbytes)
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                "kernel": "swa_window_kernel", "kernel_mean_ms": st["mean_ms"],
+                "algorithmic_bytes_per_launch": nbytes,
+                "mfma_frac": flops / kernel_s / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+    _log(f"prefill 32K: {st}  {value:.1f} TFLOP/s  {achieved:.0f} GB/s")
+    del sets, x
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not args.no_extra:
+        extra = run_extra(dev, max(steps, 20), warmup)
+
+    cpu = None
+    if not args.no_cpu:
+        _log("timing the fp64 oracle on the host cores")
+        cpu = cpu_baseline()
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v rounded to bf16, N(0,1) fp32 sinks)",
+        "config": {"workload": PRIMARY, "tokens": 32768, "q_heads": 32, "kv_heads": 4,
+                   "head_dim": 128, "window": 128, "sink": True, "lse": True},
+        "mfma_peak_frac": value / BF16_MFMA_PEAK_TFLOPS,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_extra(dev, steps, warmup):
+    """Decode / MTP verify, the GA layer, the hybrid block, the varlen prefill and a
+    plain device copy (achievable-bandwidth ceiling)."""
+    import torch
+
+    from sliding_window_attention_amd import workloads as wl
+
+    extra = {}
+    # plain copy: read + write of 1 GiB
+    a = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).normal_()
+    b = torch.empty_like(a)
+    per, _ = _time_calls(lambda _: b.copy_(a), [None], 20, 3)
+    extra["copy_ceiling_gbps"] = 2 * a.numel() * 2 / (min(per) * 1e-3) / 1e9
+    del a, b
+
+    for name in ("decode_t1", "decode_t4"):
+        _log(f"{name}")
+        x = _with_outputs(_to(wl.make_workload(name), dev), "decode")
+        sets = _clone_sets(x, 32)  # 32 x 71-86 MB: more than the Infinity Cache
+        per, _ = _time_calls(_decode_fn(), sets, max(200, steps), warmup)
+        fl, by = wl.workload_work(name)
+        st = _stats(per)
+        extra[name] = {**st, "gbps": by / (st["mean_ms"] * 1e-3) / 1e9,
+                       "hbm_frac": by / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       "tflops": fl / (st["mean_ms"] * 1e-3) / 1e12, "bytes": by}
+        del sets, x
+        torch.cuda.empty_cache()
+
+    _log("hybrid_5to1_32k (5 SWA + 1 GA layers)")
+    layers = []
+    for layer in range(6):
+        layers.append(_with_outputs(_to(wl.make_workload("hybrid_5to1_32k", layer), dev), "prefill"))
+    swa_fn, ga_fn = _prefill_fn(128), _prefill_fn(None, ga=True)
+    ga_steps = 3
+    per_ga, _ = _time_calls(ga_fn, [layers[5]], ga_steps, 1)
+    fl_swa = wl.prefill_flops([32768], 32, 128, 128)
+    fl_ga = wl.prefill_flops([32768], 32, 128, None)
+    by = wl.prefill_bytes(32768, 32, 4, 128, 2)
+    st_ga = _stats(per_ga)
+    extra["ga_32k"] = {**st_ga, "tflops": fl_ga / (st_ga["mean_ms"] * 1e-3) / 1e12,
+                       "mfma_frac": fl_ga / (st_ga["mean_ms"] * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+
+    def block(_):
+        for li in range(5):
+            swa_fn(layers[li])
+        ga_fn(layers[5])
+    per_blk, _ = _time_calls(block, [None], ga_steps, 1)
+    per_swa, _ = _time_calls(swa_fn, layers[:5], 20, 2)
+    st_blk = _stats(per_blk)
+    extra["hybrid_block"] = {**st_blk, "tflops": (5 * fl_swa + fl_ga) / (st_blk["mean_ms"] * 1e-3) / 1e12,
+                             "swa_layer_mean_ms": _stats(per_swa)["mean_ms"],
+                             "swa_layer_gbps": by / (_stats(per_swa)["mean_ms"] * 1e-3) / 1e9}
+    del layers
+    torch.cuda.empty_cache()
+
+    _log("varlen_262k")
+    x = _with_outputs(_to(wl.make_workload("varlen_262k"), dev), "prefill")
+    per, _ = _time_calls(_prefill_fn(128), [x], 10, 2)
+    fl, by = wl.workload_work("varlen_262k")
+    st = _stats(per)
+    extra["varlen_262k"] = {**st, "tflops": fl / (st["mean_ms"] * 1e-3) / 1e12,
+                            "gbps": by / (st["mean_ms"] * 1e-3) / 1e9,
+                            "lengths": wl.lognormal_lengths(262144, 8, wl.WORKLOADS["varlen_262k"].seed)}
+    del x
+    torch.cuda.empty_cache()
+    return extra
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,138 @@
+/*
+ * libswasink -- hybrid sliding-window attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * The operator (MiMo-V2-Flash Technical Report digest, section 2.2.2 "Learnable
+ * Attention Sink Bias"; MiMo-V2 blog, section 2.2): for query row i of head h with
+ * key set J(i) = the last `window` positions of its own sequence up to and
+ * including i (digest, section 2.2.1: window of 128 tokens),
+ *
+ *     a_j = scale * <q_i, k_j>,  m = max(max_j a_j, sink_h),
+ *     Z   = exp(sink_h - m) + sum_j exp(a_j - m),
+ *     o_i = sum_j exp(a_j - m) v_j / Z,      lse_i = m + ln Z.
+ *
+ * The sink is a learnable per-head scalar that only enters the softmax
+ * denominator (a virtual key with no value); it is compared with the scaled
+ * logits.  Global-attention layers (digest, section 2.2: one GA layer per five SWA
+ * layers) are the same operator with an unbounded window and no sink.  GQA
+ * (ICML 2026 keynote write-up, section 02): query head h reads KV head
+ * h / (num_q_heads / num_kv_heads).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers, row-major and contiguous, owned by
+ *    the caller.  The library allocates nothing and keeps no state across calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
+ *    call only enqueues work on `stream` and returns without synchronising.
+ *  - Arguments are validated on the host before anything is launched.  On error
+ *    a negative swa_status is returned, nothing is launched, and
+ *    swa_last_error() (thread-local) describes the problem.  SWA_ERR_HIP reports
+ *    a failed launch with the HIP runtime's message.  No C++ exception crosses
+ *    this interface.
+ *  - dtype selects the element type of q, k, v, caches and out: SWA_DTYPE_F32
+ *    (fp32) or SWA_DTYPE_BF16 (bfloat16).  Arithmetic is fp32 in both cases
+ *    (bf16 inputs feed bf16 matrix cores with fp32 accumulation; softmax
+ *    weights are rounded to bf16 before the weighted sum of values).  sinks and
+ *    lse are always fp32; out is written in dtype, rounded to nearest even.
+ *  - head_dim must be 64 or 128; num_q_heads must be a multiple of num_kv_heads.
+ *  - scale <= 0 selects 1/sqrt(head_dim).
+ *  - lse may be NULL (not written).  It holds the natural-log normaliser of each
+ *    row, sink included.
+ */
+#ifndef SWASINK_H
+#define SWASINK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SWA_OK = 0,
+  SWA_ERR_NULL = -1,        /* a required pointer is NULL */
+  SWA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+  SWA_ERR_DTYPE = -3,       /* unknown dtype */
+  SWA_ERR_UNSUPPORTED = -4, /* valid request this library does not implement */
+  SWA_ERR_HIP = -5          /* the HIP runtime reported an error */
+} swa_status;
+
+typedef enum { SWA_DTYPE_F32 = 0, SWA_DTYPE_BF16 = 1 } swa_dtype;
+
+#define SWASINK_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SWASINK_API __attribute__((visibility("default")))
+#else
+#define SWASINK_API
+#endif
+
+/*
+ * Causal GQA sliding-window attention with a per-head sink over packed
+ * variable-length sequences (technical report digest, sections 2.2.1-2.2.2).
+ *
+ *  q          [total_tokens, num_q_heads, head_dim]   dtype
+ *  k, v       [total_tokens, num_kv_heads, head_dim]  dtype
+ *  sinks      [num_q_heads] fp32: the learnable sink logit of each query head
+ *  cu_seqlens [num_seqs + 1] int32: sequence s holds tokens cu_seqlens[s] ..
+ *             cu_seqlens[s+1]-1; must rise from 0 to total_tokens (not checked on
+ *             the device; a violating array gives unspecified output, never an
+ *             out-of-bounds access).  No attention crosses a sequence boundary.
+ *  max_seqlen upper bound on any sequence length (1 .. total_tokens); only
+ *             validated, the kernels derive their tiling from total_tokens.
+ *  window     >= 1: row i attends keys max(seq_start, i-window+1) .. i.
+ *  out        [total_tokens, num_q_heads, head_dim]   dtype
+ *  lse        [total_tokens, num_q_heads] fp32, or NULL
+ * total_tokens == 0 is accepted and launches nothing.
+ */
+SWASINK_API int swa_sink_prefill(const void* q, const void* k, const void* v, const float* sinks,
+                     const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                     int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t window, float scale, swa_dtype dtype,
+                     void* out, float* lse, void* stream);
+
+/*
+ * Global causal attention: the same operator with an unbounded window and no
+ * sink (the GA layers of the hybrid block, technical report digest, section 2.2).
+ * Arguments as for swa_sink_prefill without sinks and window.
+ */
+SWASINK_API int ga_causal_prefill(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                      int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale,
+                      swa_dtype dtype, void* out, float* lse, void* stream);
+
+/*
+ * Decode / MTP verify against a window-slot ring buffer per (sequence, KV head).
+ * T query tokens per sequence (the current token and T-1 drafts, verified in one
+ * pass: technical report digest, section 2.3) attend the cached window plus the
+ * new tokens, causal among themselves.
+ *
+ *  q            [batch, T, num_q_heads, head_dim]   dtype
+ *  k_new, v_new [batch, T, num_kv_heads, head_dim]  dtype: the T new tokens, NOT in
+ *               the ring (committing accepted tokens is the caller's job)
+ *  k_cache, v_cache [batch, num_kv_heads, window, head_dim] dtype, read only
+ *  ring_head    [batch] int32: physical slot of the OLDEST cached token (logical
+ *               slot 0); logical slot l lives at physical (ring_head + l) mod window.
+ *               Values outside [0, window) are reduced modulo window.
+ *  sinks        [num_q_heads] fp32
+ *  out          [batch, T, num_q_heads, head_dim] dtype
+ *  lse          [batch, T, num_q_heads] fp32, or NULL
+ * Query t sees logical slots t+1 .. window-1 and new tokens 0 .. t, i.e. exactly
+ * `window` keys; logical slot 0 is never read.  Requires 1 <= T < window.
+ * batch == 0 is accepted and launches nothing.
+ */
+SWASINK_API int swa_sink_decode(const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                    const void* v_cache, const int32_t* ring_head, const float* sinks,
+                    int32_t batch, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t window, float scale, swa_dtype dtype, void* out,
+                    float* lse, void* stream);
+
+/* Message for the last non-OK return on the calling thread ("" if none). */
+SWASINK_API const char* swa_last_error(void);
+
+/* SWASINK_ABI_VERSION of the built library. */
+SWASINK_API int32_t swa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWASINK_H */

@@ -1,1 +1,211 @@
-"""libswasink: hybrid sliding-window attention forward for MI355X (gfx950)."""
+"""libswasink: hybrid sliding-window attention forward for MI355X (gfx950).
+
+Thin ctypes binding over the C ABI declared in include/swasink.h.  The functions
+below only marshal arguments: they check that tensors are contiguous device
+tensors of the right dtype, allocate the outputs with torch on the current
+stream, and call the library entry point of the same name.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.  If the
+library is not built, or the GPU is missing, calls raise.
+
+    swa_sink_prefill(q, k, v, sinks, cu_seqlens, max_seqlen=None, window=128, scale=None)
+    ga_causal_prefill(q, k, v, cu_seqlens, max_seqlen=None, scale=None)
+    swa_sink_decode(q, k_new, v_new, k_cache, v_cache, ring_head, sinks, scale=None)
+
+Each returns (out, lse): out like q (same dtype), lse fp32 [..., num_q_heads].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["swa_sink_prefill", "ga_causal_prefill", "swa_sink_decode", "library", "library_path",
+           "abi_version", "SwaError"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libswasink.so"
+_lib = None
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+
+_SIGNATURES = {
+    "swa_sink_prefill": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P],
+    "ga_causal_prefill": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P],
+    "swa_sink_decode": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P],
+}
+
+
+class SwaError(RuntimeError):
+    """A libswasink entry point returned a non-zero status."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"libswasink error {code}: {message}")
+        self.code = code
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def library() -> ctypes.CDLL:
+    """Load the in-tree libswasink.so (built by sliding_window_attention_amd.build)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m sliding_window_attention_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, args in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        lib.swa_last_error.argtypes = []
+        lib.swa_last_error.restype = ctypes.c_char_p
+        lib.swa_abi_version.argtypes = []
+        lib.swa_abi_version.restype = ctypes.c_int32
+        _lib = lib
+    return _lib
+
+
+def abi_version() -> int:
+    return int(library().swa_abi_version())
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        msg = library().swa_last_error().decode(errors="replace")
+        raise SwaError(rc, msg)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def _dev(t, name, dtype=None):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype} (got {t.dtype})")
+    return t
+
+
+def _stream(device) -> ctypes.c_void_p:
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _scale(scale) -> float:
+    return 0.0 if scale is None else float(scale)
+
+
+def swa_sink_prefill(q, k, v, sinks, cu_seqlens, max_seqlen=None, window=128, scale=None,
+                     return_lse=True, out=None, lse=None):
+    """Causal GQA sliding-window attention with per-head sinks over packed sequences.
+
+    q [N, Hq, D], k/v [N, Hkv, D] (fp32 or bf16, one dtype), sinks [Hq] fp32,
+    cu_seqlens [S+1] int32, all on one GPU.  max_seqlen defaults to N (an upper
+    bound; the kernels do not need the exact value).
+    """
+    import torch
+
+    _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    _dev(sinks, "sinks", torch.float32)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("q must be [N, Hq, D] and k, v [N, Hkv, D]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    n, hq, d = q.shape
+    if k.shape[0] != n or k.shape[2] != d or sinks.numel() != hq:
+        raise ValueError("inconsistent shapes")
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    if return_lse and lse is None:
+        lse = torch.empty((n, hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+    ms = n if max_seqlen is None else int(max_seqlen)
+    rc = library().swa_sink_prefill(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), sinks.data_ptr(), cu_seqlens.data_ptr(),
+        cu_seqlens.numel() - 1, n, ms, hq, k.shape[1], d, int(window), _scale(scale),
+        _dtype_code(q), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def ga_causal_prefill(q, k, v, cu_seqlens, max_seqlen=None, scale=None, return_lse=True, out=None,
+                      lse=None):
+    """Global causal GQA attention (no window, no sink) over packed sequences."""
+    import torch
+
+    _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("q must be [N, Hq, D] and k, v [N, Hkv, D]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    n, hq, d = q.shape
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    if return_lse and lse is None:
+        lse = torch.empty((n, hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+    ms = n if max_seqlen is None else int(max_seqlen)
+    rc = library().ga_causal_prefill(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, n,
+        ms, hq, k.shape[1], d, _scale(scale), _dtype_code(q), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def swa_sink_decode(q, k_new, v_new, k_cache, v_cache, ring_head, sinks, scale=None,
+                    return_lse=True, out=None, lse=None):
+    """Decode / MTP verify against a ring buffer.
+
+    q [B, T, Hq, D]; k_new/v_new [B, T, Hkv, D]; k_cache/v_cache [B, Hkv, W, D]
+    (W = window = ring slots); ring_head [B] int32; sinks [Hq] fp32.
+    """
+    import torch
+
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
+                  (v_cache, "v_cache")):
+        _dev(t, nm, q.dtype)
+    _dev(ring_head, "ring_head", torch.int32)
+    _dev(sinks, "sinks", torch.float32)
+    if q.dim() != 4 or k_new.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q, k_new must be [B, T, H, D] and caches [B, Hkv, W, D]")
+    b, t, hq, d = q.shape
+    hkv, w = k_cache.shape[1], k_cache.shape[2]
+    if (k_new.shape != (b, t, hkv, d) or v_new.shape != k_new.shape or v_cache.shape != k_cache.shape
+            or k_cache.shape[0] != b or k_cache.shape[3] != d or ring_head.numel() != b
+            or sinks.numel() != hq):
+        raise ValueError("inconsistent shapes")
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    if return_lse and lse is None:
+        lse = torch.empty((b, t, hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+    rc = library().swa_sink_decode(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        ring_head.data_ptr(), sinks.data_ptr(), b, t, hq, hkv, d, w, _scale(scale), _dtype_code(q),
+        out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(q.device))
+    _check(rc)
+    return out, lse

@@ -1,0 +1,159 @@
+// C ABI of libswasink: argument validation, kernel selection, error reporting.
+// The operator and the conventions are documented in include/swasink.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/swasink.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return SWA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SWA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_dtype(int dtype) {
+  if (dtype != SWA_DTYPE_F32 && dtype != SWA_DTYPE_BF16)
+    return fail(SWA_ERR_DTYPE, "unknown dtype %d (0 = f32, 1 = bf16)", dtype);
+  return SWA_OK;
+}
+
+int check_heads(int32_t hq, int32_t hkv, int32_t d) {
+  if (hq < 1 || hkv < 1) return fail(SWA_ERR_SHAPE, "head counts must be >= 1 (got %d, %d)", hq, hkv);
+  if (hq % hkv != 0)
+    return fail(SWA_ERR_SHAPE, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)", hq, hkv);
+  if (d != 64 && d != 128) return fail(SWA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d);
+  return SWA_OK;
+}
+
+float resolve_scale(float scale, int32_t d) {
+  return (scale > 0.f && isfinite(scale)) ? scale : 1.0f / sqrtf((float)d);
+}
+
+int prefill_common(const void* q, const void* k, const void* v, const float* sinks,
+                   bool need_sinks, const int32_t* cu_seqlens, int32_t num_seqs,
+                   int32_t total_tokens, int32_t max_seqlen, int32_t hq, int32_t hkv, int32_t d,
+                   int32_t window, float scale, int dtype, void* out, float* lse, void* stream,
+                   const char* name) {
+  int rc = check_dtype(dtype);
+  if (rc) return rc;
+  if (total_tokens < 0) return fail(SWA_ERR_SHAPE, "%s: total_tokens must be >= 0", name);
+  if (num_seqs < 1) return fail(SWA_ERR_SHAPE, "%s: num_seqs must be >= 1", name);
+  if (num_seqs > total_tokens && total_tokens > 0)
+    return fail(SWA_ERR_SHAPE, "%s: num_seqs (%d) exceeds total_tokens (%d)", name, num_seqs,
+                total_tokens);
+  if (total_tokens > 0 && (max_seqlen < 1 || max_seqlen > total_tokens))
+    return fail(SWA_ERR_SHAPE, "%s: max_seqlen must be in [1, total_tokens]", name);
+  if ((rc = check_heads(hq, hkv, d))) return rc;
+  if (window < 1) return fail(SWA_ERR_SHAPE, "%s: window must be >= 1 (got %d)", name, window);
+  if ((long long)total_tokens * hq * d > (1LL << 40))
+    return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
+  if (!q || !k || !v || !cu_seqlens || !out || (need_sinks && !sinks))
+    return fail(SWA_ERR_NULL, "%s: q, k, v, %scu_seqlens and out must be non-NULL", name,
+                need_sinks ? "sinks, " : "");
+  if (total_tokens == 0) return ok();
+
+  swa::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v;
+  a.sinks = sinks;
+  a.cu_seqlens = cu_seqlens;
+  a.out = out; a.lse = lse;
+  a.num_seqs = num_seqs;
+  a.total_tokens = total_tokens;
+  a.num_q_heads = hq; a.num_kv_heads = hkv; a.head_dim = d;
+  a.window = window;
+  a.scale = resolve_scale(scale, d);
+  const bool bf = dtype == SWA_DTYPE_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (swa::swa_window_mfma_supported(a, bf)) e = swa::launch_swa_window_mfma(a, s);
+  else if (swa::online_mfma_supported(a, bf)) e = swa::launch_online_mfma(a, s);
+  else e = swa::launch_generic_prefill(a, bf, s);
+  return hip_status(e, name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int swa_sink_prefill(const void* q, const void* k, const void* v, const float* sinks,
+                     const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                     int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t window, float scale, swa_dtype dtype, void* out,
+                     float* lse, void* stream) {
+  return prefill_common(q, k, v, sinks, true, cu_seqlens, num_seqs, total_tokens, max_seqlen,
+                        num_q_heads, num_kv_heads, head_dim, window, scale, (int)dtype, out, lse,
+                        stream, "swa_sink_prefill");
+}
+
+int ga_causal_prefill(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                      int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale,
+                      swa_dtype dtype, void* out, float* lse, void* stream) {
+  return prefill_common(q, k, v, nullptr, false, cu_seqlens, num_seqs, total_tokens, max_seqlen,
+                        num_q_heads, num_kv_heads, head_dim, 0x7fffffff, scale, (int)dtype, out,
+                        lse, stream, "ga_causal_prefill");
+}
+
+int swa_sink_decode(const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                    const void* v_cache, const int32_t* ring_head, const float* sinks,
+                    int32_t batch, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t window, float scale, swa_dtype dtype, void* out,
+                    float* lse, void* stream) {
+  const char* name = "swa_sink_decode";
+  int rc = check_dtype((int)dtype);
+  if (rc) return rc;
+  if (batch < 0) return fail(SWA_ERR_SHAPE, "%s: batch must be >= 0", name);
+  if ((rc = check_heads(num_q_heads, num_kv_heads, head_dim))) return rc;
+  if (window < 2) return fail(SWA_ERR_SHAPE, "%s: window must be >= 2 (got %d)", name, window);
+  if (T < 1 || T >= window)
+    return fail(SWA_ERR_SHAPE, "%s: T must satisfy 1 <= T < window (got T=%d, window=%d)", name, T,
+                window);
+  if ((long long)batch * num_kv_heads * window * head_dim > (1LL << 40))
+    return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !ring_head || !sinks || !out)
+    return fail(SWA_ERR_NULL,
+                "%s: q, k_new, v_new, k_cache, v_cache, ring_head, sinks and out must be non-NULL",
+                name);
+  if (batch == 0) return ok();
+
+  swa::DecodeArgs a;
+  a.q = q; a.k_new = k_new; a.v_new = v_new;
+  a.k_cache = k_cache; a.v_cache = v_cache;
+  a.ring_head = ring_head; a.sinks = sinks;
+  a.out = out; a.lse = lse;
+  a.batch = batch; a.t_new = T;
+  a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
+  a.window = window;
+  a.scale = resolve_scale(scale, head_dim);
+  const bool bf = dtype == SWA_DTYPE_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = swa::decode_mfma_supported(a, bf) ? swa::launch_decode_mfma(a, s)
+                                                   : swa::launch_generic_decode(a, bf, s);
+  return hip_status(e, name);
+}
+
+const char* swa_last_error(void) { return g_last_error; }
+
+int32_t swa_abi_version(void) { return SWASINK_ABI_VERSION; }
+
+}  // extern "C"

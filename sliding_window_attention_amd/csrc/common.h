@@ -1,0 +1,102 @@
+// Device-side vocabulary shared by the libswasink kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWave = 64;
+
+// Parameters of one prefill call (packed variable-length sequences).
+struct PrefillArgs {
+  const void* q;            // [N, Hq, D]
+  const void* k;            // [N, Hkv, D]
+  const void* v;            // [N, Hkv, D]
+  const float* sinks;       // [Hq] or nullptr (no sink)
+  const int32_t* cu_seqlens;  // [S+1]
+  void* out;                // [N, Hq, D]
+  float* lse;               // [N, Hq] or nullptr
+  int32_t num_seqs;
+  int32_t total_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t window;           // keys i-window+1 .. i; INT32_MAX for unbounded
+  float scale;              // logit scale (already resolved, > 0)
+};
+
+// Parameters of one decode / MTP-verify call against a ring buffer.
+struct DecodeArgs {
+  const void* q;            // [B, T, Hq, D]
+  const void* k_new;        // [B, T, Hkv, D]
+  const void* v_new;        // [B, T, Hkv, D]
+  const void* k_cache;      // [B, Hkv, W, D]
+  const void* v_cache;      // [B, Hkv, W, D]
+  const int32_t* ring_head;  // [B]
+  const float* sinks;       // [Hq]
+  void* out;                // [B, T, Hq, D]
+  float* lse;               // [B, T, Hq] or nullptr
+  int32_t batch;
+  int32_t t_new;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t window;
+  float scale;
+};
+
+// First token of the sequence that holds packed token `t`: the largest s with
+// cu[s] <= t (binary search; cu has num_seqs + 1 entries).  Clamped so that a
+// malformed cu_seqlens cannot produce an index outside [0, t].
+__device__ __forceinline__ int seq_start_of(const int32_t* __restrict__ cu, int num_seqs, int t) {
+  int lo = 0, hi = num_seqs;  // invariant: answer in [lo, hi)
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid;
+  }
+  int s = cu[lo];
+  s = s < 0 ? 0 : s;
+  return s > t ? t : s;
+}
+
+__device__ __forceinline__ float bf16_to_f32(bf16 x) { return (float)x; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Max / sum over the four lanes l, l^16, l^32, l^48 (the lanes that hold the
+// same column of a 16x16 MFMA result).
+__device__ __forceinline__ float quad_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+}  // namespace swa

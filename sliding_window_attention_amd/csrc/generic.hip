@@ -1,0 +1,205 @@
+// Shape-general attention kernels on the vector ALUs (fp32 arithmetic).
+//
+// One wavefront per output row (query token, query head).  Lanes own keys while
+// scoring (64 keys per step) and own head-dim elements while accumulating the
+// weighted values; the softmax runs online over 64-key steps, starting from the
+// sink (m = sink, running sum = 1) so that exp(sink - m) sits in the denominator
+// and contributes no value (MiMo-V2-Flash Technical Report digest, section 2.2.2).
+// These kernels serve every shape the matrix-core kernels do not: fp32 inputs,
+// head_dim 64, group sizes that are not a multiple of 8, and ring windows other
+// than 128.  They trade speed for generality.
+#include "common.h"
+#include "kernels.h"
+
+namespace swa {
+namespace {
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kVec = 4;  // elements per 16-byte load
+  __device__ static void load16(const float* p, float* dst) {
+    f32x4 x = *reinterpret_cast<const f32x4*>(p);
+    dst[0] = x[0]; dst[1] = x[1]; dst[2] = x[2]; dst[3] = x[3];
+  }
+  __device__ static float load1(const float* p) { return *p; }
+  __device__ static float store_cast(float x) { return x; }
+};
+template <> struct Elem<bf16> {
+  static constexpr int kVec = 8;
+  __device__ static void load16(const bf16* p, float* dst) {
+    bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e] = (float)x[e];
+  }
+  __device__ static float load1(const bf16* p) { return (float)*p; }
+  __device__ static bf16 store_cast(float x) { return (bf16)x; }
+};
+
+// Keys of one prefill row: positions jlo..jhi of the packed stream, KV head kvh.
+template <typename T, int D>
+struct PrefillKeys {
+  const T* k;
+  const T* v;
+  int row_stride;  // Hkv * D
+  int kvh;
+  __device__ const T* key(int j) const { return k + (size_t)j * row_stride + kvh * D; }
+  __device__ const T* val(int j) const { return v + (size_t)j * row_stride + kvh * D; }
+};
+
+// Keys of one decode row: virtual positions 0..W-1 are ring logical slots (physical
+// (head + l) mod W), W..W+T-1 are the new tokens.
+template <typename T, int D>
+struct DecodeKeys {
+  const T* kc;  // this (sequence, kv head)'s ring: [W, D]
+  const T* vc;
+  const T* kn;  // this sequence's new tokens: [T, Hkv, D], offset to kv head
+  const T* vn;
+  int W;
+  int head;
+  int new_stride;  // Hkv * D
+  __device__ const T* key(int j) const {
+    if (j < W) { int p = head + j; p -= (p >= W) ? W : 0; return kc + (size_t)p * D; }
+    return kn + (size_t)(j - W) * new_stride;
+  }
+  __device__ const T* val(int j) const {
+    if (j < W) { int p = head + j; p -= (p >= W) ? W : 0; return vc + (size_t)p * D; }
+    return vn + (size_t)(j - W) * new_stride;
+  }
+};
+
+// One wavefront computes one row against keys jlo..jhi (inclusive, jlo <= jhi).
+template <typename T, int D, class Keys>
+__device__ void attend_row(const T* __restrict__ qrow, const Keys& keys, int jlo, int jhi,
+                           float sink2, float c, T* __restrict__ orow, float* lse_out) {
+  using E = Elem<T>;
+  constexpr int kPer = D / kWave;  // output elements per lane
+  const int lane = threadIdx.x & (kWave - 1);
+  float q[D];
+#pragma unroll
+  for (int d = 0; d < D; d += E::kVec) E::load16(qrow + d, q + d);
+  float o[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) o[e] = 0.f;
+  float m = sink2;                        // running max (log2 units)
+  float l = (sink2 == -INFINITY) ? 0.f : 1.f;  // running sum, sink term included
+  for (int jb = jlo; jb <= jhi; jb += kWave) {
+    const int j = jb + lane;
+    const bool valid = j <= jhi;
+    float s = -INFINITY;
+    if (valid) {
+      const T* kr = keys.key(j);
+      float acc = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; d += E::kVec) {
+        float kk[E::kVec];
+        E::load16(kr + d, kk);
+#pragma unroll
+        for (int e = 0; e < E::kVec; ++e) acc = fmaf(q[d + e], kk[e], acc);
+      }
+      s = acc * c;
+    }
+    const float m_new = fmaxf(m, wave_max(s));
+    const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - m_new);
+    const float p = valid ? fast_exp2(s - m_new) : 0.f;
+    l = l * alpha + wave_sum(p);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) o[e] *= alpha;
+    const int nk = min(kWave, jhi - jb + 1);
+    for (int jj = 0; jj < nk; ++jj) {
+      const float pj = __shfl(p, jj);
+      const T* vr = keys.val(jb + jj);
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) o[e] = fmaf(pj, E::load1(vr + lane + e * kWave), o[e]);
+    }
+    m = m_new;
+  }
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) orow[lane + e * kWave] = E::store_cast(o[e] * inv);
+  if (lse_out != nullptr && lane == 0) *lse_out = (m + fast_log2(l)) * kLn2;
+}
+
+constexpr int kRowsPerBlock = 4;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void generic_prefill_kernel(PrefillArgs a) {
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int hq = a.num_q_heads;
+  if (row >= a.total_tokens * hq) return;
+  const int n = row / hq;
+  const int h = row - n * hq;
+  const int kvh = h / (hq / a.num_kv_heads);
+  const int start = seq_start_of(a.cu_seqlens, a.num_seqs, n);
+  const int lo = (a.window >= n - start + 1) ? start : n - a.window + 1;
+  PrefillKeys<T, D> keys{static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                         a.num_kv_heads * D, kvh};
+  const float sink2 = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
+  const T* qrow = static_cast<const T*>(a.q) + (size_t)row * D;
+  T* orow = static_cast<T*>(a.out) + (size_t)row * D;
+  attend_row<T, D>(qrow, keys, lo, n, sink2, a.scale * kLog2e, orow,
+                   a.lse ? a.lse + row : nullptr);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void generic_decode_kernel(DecodeArgs a) {
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int hq = a.num_q_heads;
+  const int T_ = a.t_new;
+  if (row >= a.batch * T_ * hq) return;
+  const int h = row % hq;
+  const int bt = row / hq;
+  const int t = bt % T_;
+  const int b = bt / T_;
+  const int hkv = a.num_kv_heads;
+  const int kvh = h / (hq / hkv);
+  const int W = a.window;
+  int head = a.ring_head[b] % W;
+  head += (head < 0) ? W : 0;
+  DecodeKeys<T, D> keys;
+  keys.kc = static_cast<const T*>(a.k_cache) + ((size_t)b * hkv + kvh) * W * D;
+  keys.vc = static_cast<const T*>(a.v_cache) + ((size_t)b * hkv + kvh) * W * D;
+  keys.kn = static_cast<const T*>(a.k_new) + ((size_t)b * T_ * hkv + kvh) * D;
+  keys.vn = static_cast<const T*>(a.v_new) + ((size_t)b * T_ * hkv + kvh) * D;
+  keys.W = W;
+  keys.head = head;
+  keys.new_stride = hkv * D;
+  const T* qrow = static_cast<const T*>(a.q) + (size_t)row * D;
+  T* orow = static_cast<T*>(a.out) + (size_t)row * D;
+  // query t sits at virtual position W + t and sees W keys: t+1 .. W+t
+  attend_row<T, D>(qrow, keys, t + 1, W + t, a.sinks[h] * kLog2e, a.scale * kLog2e, orow,
+                   a.lse ? a.lse + row : nullptr);
+}
+
+template <typename T, int D>
+hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
+  const long rows = (long)a.total_tokens * a.num_q_heads;
+  const long blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((generic_prefill_kernel<T, D>), dim3((unsigned)blocks),
+                     dim3(kRowsPerBlock * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
+  const long rows = (long)a.batch * a.t_new * a.num_q_heads;
+  const long blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((generic_decode_kernel<T, D>), dim3((unsigned)blocks),
+                     dim3(kRowsPerBlock * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_generic_prefill(const PrefillArgs& a, bool bf16_io, hipStream_t s) {
+  if (bf16_io) return a.head_dim == 64 ? launch_prefill_t<bf16, 64>(a, s) : launch_prefill_t<bf16, 128>(a, s);
+  return a.head_dim == 64 ? launch_prefill_t<float, 64>(a, s) : launch_prefill_t<float, 128>(a, s);
+}
+
+hipError_t launch_generic_decode(const DecodeArgs& a, bool bf16_io, hipStream_t s) {
+  if (bf16_io) return a.head_dim == 64 ? launch_decode_t<bf16, 64>(a, s) : launch_decode_t<bf16, 128>(a, s);
+  return a.head_dim == 64 ? launch_decode_t<float, 64>(a, s) : launch_decode_t<float, 128>(a, s);
+}
+
+}  // namespace swa

@@ -1,0 +1,26 @@
+// Host-side launchers of the libswasink kernels.  Each enqueues on `s` and
+// returns the launch status; argument validation happens before, in abi.hip.
+#pragma once
+
+#include "common.h"
+
+namespace swa {
+
+// Shape-general vector-ALU kernels (fp32 or bf16 I/O, head_dim 64 or 128).
+hipError_t launch_generic_prefill(const PrefillArgs& a, bool bf16_io, hipStream_t s);
+hipError_t launch_generic_decode(const DecodeArgs& a, bool bf16_io, hipStream_t s);
+
+// Matrix-core kernels: bf16 I/O, head_dim 128, query heads per KV head a multiple of 8.
+// Sliding window of at most 128 keys, whole window held in registers.
+hipError_t launch_swa_window_mfma(const PrefillArgs& a, hipStream_t s);
+// Any window (or none) with online softmax over key chunks; used for global
+// attention and for windows longer than 128.
+hipError_t launch_online_mfma(const PrefillArgs& a, hipStream_t s);
+// Ring decode, window 128, 1 <= T <= 4.
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
+
+bool swa_window_mfma_supported(const PrefillArgs& a, bool bf16_io);
+bool online_mfma_supported(const PrefillArgs& a, bool bf16_io);
+bool decode_mfma_supported(const DecodeArgs& a, bool bf16_io);
+
+}  // namespace swa

@@ -1,0 +1,130 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every symbol
+include/swasink.h declares, and rejects bad arguments on the host (before any HIP
+call) with the documented status codes and a message."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sliding_window_attention_amd as swa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swasink.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP = 0, -1, -2, -3, -4
+NULL = None
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"SWASINK_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert set(names) == {"swa_sink_prefill", "ga_causal_prefill", "swa_sink_decode",
+                          "swa_last_error", "swa_abi_version"}
+
+
+def test_library_exports_every_declared_symbol():
+    lib = swa.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define SWASINK_ABI_VERSION (\d+)", open(HEADER).read())
+    assert swa.abi_version() == int(m.group(1))
+
+
+def _prefill(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sinks=FAKE, cu=FAKE, num_seqs=1, n=16, max_seqlen=16, hq=8,
+             hkv=1, d=128, window=128, scale=0.0, dtype=1, out=FAKE, lse=NULL, stream=NULL)
+    a.update(kw)
+    return swa.library().swa_sink_prefill(a["q"], a["k"], a["v"], a["sinks"], a["cu"], a["num_seqs"],
+                                          a["n"], a["max_seqlen"], a["hq"], a["hkv"], a["d"],
+                                          a["window"], a["scale"], a["dtype"], a["out"], a["lse"],
+                                          a["stream"])
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, head=FAKE, sinks=FAKE, b=4, t=1, hq=8,
+             hkv=1, d=128, window=128, scale=0.0, dtype=1, out=FAKE, lse=NULL, stream=NULL)
+    a.update(kw)
+    return swa.library().swa_sink_decode(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["head"],
+                                         a["sinks"], a["b"], a["t"], a["hq"], a["hkv"], a["d"],
+                                         a["window"], a["scale"], a["dtype"], a["out"], a["lse"],
+                                         a["stream"])
+
+
+def _last():
+    return swa.library().swa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(q=NULL), E_NULL, "non-NULL"),
+    (dict(sinks=NULL), E_NULL, "sinks"),
+    (dict(cu=NULL), E_NULL, "cu_seqlens"),
+    (dict(out=NULL), E_NULL, "out"),
+    (dict(hq=6, hkv=4), E_SHAPE, "multiple"),
+    (dict(hq=0), E_SHAPE, ">= 1"),
+    (dict(d=96), E_UNSUP, "head_dim"),
+    (dict(window=0), E_SHAPE, "window"),
+    (dict(dtype=7), E_DTYPE, "dtype"),
+    (dict(n=-1), E_SHAPE, "total_tokens"),
+    (dict(num_seqs=0), E_SHAPE, "num_seqs"),
+    (dict(num_seqs=20), E_SHAPE, "num_seqs"),
+    (dict(max_seqlen=0), E_SHAPE, "max_seqlen"),
+    (dict(max_seqlen=17), E_SHAPE, "max_seqlen"),
+])
+def test_prefill_rejects_bad_arguments(kw, code, needle):
+    assert _prefill(**kw) == code
+    assert needle in _last()
+
+
+def test_prefill_empty_is_ok_and_launches_nothing():
+    assert _prefill(n=0, max_seqlen=0) == OK
+    assert _last() == ""
+
+
+def test_ga_rejects_bad_arguments():
+    lib = swa.library()
+    rc = lib.ga_causal_prefill(FAKE, FAKE, FAKE, NULL, 1, 16, 16, 8, 1, 128, 0.0, 1, FAKE, NULL, NULL)
+    assert rc == E_NULL and "cu_seqlens" in _last()
+    rc = lib.ga_causal_prefill(FAKE, FAKE, FAKE, FAKE, 1, 16, 16, 8, 3, 128, 0.0, 1, FAKE, NULL, NULL)
+    assert rc == E_SHAPE
+    # no sinks argument exists for GA; a NULL lse is fine but NULL out is not
+    rc = lib.ga_causal_prefill(FAKE, FAKE, FAKE, FAKE, 1, 16, 16, 8, 1, 128, 0.0, 1, NULL, NULL, NULL)
+    assert rc == E_NULL
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(t=0), E_SHAPE, "T must"),
+    (dict(t=128), E_SHAPE, "T must"),
+    (dict(window=1, t=1), E_SHAPE, "window"),
+    (dict(head=NULL), E_NULL, "ring_head"),
+    (dict(sinks=NULL), E_NULL, "sinks"),
+    (dict(kc=NULL), E_NULL, "k_cache"),
+    (dict(b=-2), E_SHAPE, "batch"),
+    (dict(hq=12, hkv=8), E_SHAPE, "multiple"),
+    (dict(d=32), E_UNSUP, "head_dim"),
+    (dict(dtype=-1), E_DTYPE, "dtype"),
+])
+def test_decode_rejects_bad_arguments(kw, code, needle):
+    assert _decode(**kw) == code
+    assert needle in _last()
+
+
+def test_decode_empty_batch_is_ok():
+    assert _decode(b=0) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros(4, 8, 128)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        swa.swa_sink_prefill(q, q[:, :1].contiguous(), q[:, :1].contiguous(), torch.zeros(8),
+                             torch.tensor([0, 4], dtype=torch.int32))

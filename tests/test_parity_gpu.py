@@ -1,0 +1,285 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Inputs are seeded synthetic tensors (sliding_window_attention_amd.workloads);
+the oracle runs on exactly the values the GPU saw.  Small cases compare every
+output element and span several 16-query tiles, ragged tails, short and length-1
+sequences, sequence boundaries inside tiles, windows below, at and above 128,
+and ring heads at both ends.  The full-size workloads compare every output where
+the oracle finishes in seconds and sampled rows otherwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sliding_window_attention_amd as swa
+from oracle import swa_oracle as orc
+from sliding_window_attention_amd import workloads as wl
+from tests.golden.load import array, load
+from tests.parity import assert_close, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _gpu(x):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+
+
+def _run_prefill(x, window, ga=False):
+    g = _gpu(x)
+    if ga:
+        o, lse = swa.ga_causal_prefill(g["q"], g["k"], g["v"], g["cu_seqlens"], x["max_seqlen"])
+    else:
+        o, lse = swa.swa_sink_prefill(g["q"], g["k"], g["v"], g["sinks"], g["cu_seqlens"],
+                                      x["max_seqlen"], window=window)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _oracle_prefill(x, window, ga=False):
+    cu = x["cu_seqlens"].numpy()
+    if ga:
+        return orc.ga_causal_prefill(x["q"], x["k"], x["v"], cu)
+    return orc.swa_sink_prefill(x["q"], x["k"], x["v"], x["sinks"], cu, window)
+
+
+# ---------------------------------------------------------------------------
+# hand-worked fixtures (exact rationals), fp32, through the library
+# ---------------------------------------------------------------------------
+
+def _pad_d(a, d=64):
+    out = np.zeros(a.shape[:-1] + (d,))
+    out[..., : a.shape[-1]] = a
+    return torch.tensor(out, dtype=torch.float32, device=DEV).contiguous()
+
+
+def test_golden_prefill_and_ga_through_library():
+    fx = load()["prefill"]
+    _say("golden prefill fp32 (head_dim 4 padded to 64, scale 1/2)")
+    q, k, v = _pad_d(array(fx["q"])), _pad_d(array(fx["k"])), _pad_d(array(fx["v"]))
+    sinks = torch.tensor(array(fx["sinks"]), dtype=torch.float32, device=DEV)
+    cu = torch.tensor(fx["cu_seqlens"], dtype=torch.int32, device=DEV)
+    o, lse = swa.swa_sink_prefill(q, k, v, sinks, cu, window=fx["window"], scale=0.5)
+    np.testing.assert_allclose(to_np(o)[..., :4], array(fx["swa_o"]), atol=2e-6)
+    np.testing.assert_allclose(to_np(lse), array(fx["swa_lse"]), atol=2e-6)
+    o, lse = swa.ga_causal_prefill(q, k, v, cu, scale=0.5)
+    np.testing.assert_allclose(to_np(o)[..., :4], array(fx["ga_o"]), atol=2e-6)
+    np.testing.assert_allclose(to_np(lse), array(fx["ga_lse"]), atol=2e-6)
+
+
+def test_golden_decode_through_library():
+    for n, fx in enumerate(load()["decode"]):
+        _say(f"golden decode {n} fp32 window {fx['window']}")
+        t = {k: _pad_d(array(fx[k])) for k in ("q", "k_new", "v_new", "k_cache", "v_cache")}
+        head = torch.tensor(fx["ring_head"], dtype=torch.int32, device=DEV)
+        sinks = torch.tensor(array(fx["sinks"]), dtype=torch.float32, device=DEV)
+        o, lse = swa.swa_sink_decode(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                                     head, sinks, scale=0.5)
+        np.testing.assert_allclose(to_np(o)[..., :4], array(fx["o"]), atol=2e-6)
+        np.testing.assert_allclose(to_np(lse), array(fx["lse"]), atol=2e-6)
+
+
+# ---------------------------------------------------------------------------
+# prefill, small sizes, every element
+# ---------------------------------------------------------------------------
+
+def test_tiny_fp32_workload_full():
+    _say("tiny_fp32: 512 tokens, 4/1 heads, D 64, W 128, fp32")
+    x = wl.make_workload("tiny_fp32")
+    o, lse = _run_prefill(x, 128)
+    o_ref, l_ref = _oracle_prefill(x, 128)
+    assert_close(torch.float32, o, o_ref, lse, l_ref, "tiny_fp32")
+
+
+PREFILL_CASES = [
+    # (lengths, Hq, Hkv, D, dtype, window)
+    ([700], 32, 4, 128, "bf16", 128),           # window kernel, ragged tail (700 = 43*16 + 12)
+    ([130, 1, 17, 300, 5, 64], 32, 4, 128, "bf16", 128),  # boundaries inside tiles, L=1, L<W
+    ([400], 16, 2, 128, "bf16", 1),             # window 1: only the diagonal
+    ([333, 90], 8, 1, 128, "bf16", 37),         # odd window, G = 8
+    ([260], 16, 1, 128, "bf16", 100),           # G = 16 (two head octets per KV head)
+    ([520, 45], 32, 4, 128, "bf16", 129),       # online kernel with window + sink
+    ([1000], 8, 1, 128, "bf16", 300),           # online kernel, long window
+    ([300, 77], 8, 2, 128, "bf16", 128),        # generic kernel (G = 4)
+    ([250], 8, 1, 64, "bf16", 128),             # generic kernel (D = 64)
+    ([200, 3], 4, 2, 128, "f32", 50),           # generic fp32
+    ([7], 32, 4, 128, "bf16", 128),             # fewer tokens than one tile
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: f"{c[0]}-{c[1]}/{c[2]}-D{c[3]}-{c[4]}-W{c[5]}")
+def test_swa_prefill_small(case):
+    lens, hq, hkv, d, dt, window = case
+    _say(f"swa prefill lens={lens} heads={hq}/{hkv} D={d} {dt} W={window}")
+    x = wl.make_prefill(lens, hq, hkv, d, dt, seed=sum(lens) + hq + window)
+    o, lse = _run_prefill(x, window)
+    o_ref, l_ref = _oracle_prefill(x, window)
+    assert_close(x["q"].dtype, o, o_ref, lse, l_ref, f"swa {case}")
+
+
+GA_CASES = [
+    ([600], 32, 4, 128, "bf16"),
+    ([129, 1, 400, 33], 16, 2, 128, "bf16"),
+    ([300], 8, 1, 64, "bf16"),   # generic
+    ([90, 40], 4, 4, 128, "f32"),  # generic fp32
+]
+
+
+@pytest.mark.parametrize("case", GA_CASES, ids=lambda c: f"{c[0]}-{c[1]}/{c[2]}-D{c[3]}-{c[4]}")
+def test_ga_prefill_small(case):
+    lens, hq, hkv, d, dt = case
+    _say(f"ga prefill lens={lens} heads={hq}/{hkv} D={d} {dt}")
+    x = wl.make_prefill(lens, hq, hkv, d, dt, seed=7 + sum(lens), with_sinks=False)
+    o, lse = _run_prefill(x, None, ga=True)
+    o_ref, l_ref = _oracle_prefill(x, None, ga=True)
+    assert_close(x["q"].dtype, o, o_ref, lse, l_ref, f"ga {case}")
+
+
+def test_prefill_large_sink_and_no_lse():
+    _say("swa prefill with sinks +40 (outputs ~0) and lse=None")
+    x = wl.make_prefill([300], 32, 4, 128, "bf16", seed=99)
+    x["sinks"] = x["sinks"] + 40.0
+    g = _gpu(x)
+    o, lse = swa.swa_sink_prefill(g["q"], g["k"], g["v"], g["sinks"], g["cu_seqlens"], return_lse=False)
+    torch.cuda.synchronize()
+    assert lse is None
+    assert float(o.float().abs().max()) < 1e-6
+    o_ref, _ = _oracle_prefill(x, 128)
+    assert_close(torch.bfloat16, o, o_ref, what="large sink")
+
+
+def test_prefill_deterministic():
+    _say("swa prefill run twice: bitwise identical (LDS race detector)")
+    x = wl.make_prefill([2000, 48], 32, 4, 128, "bf16", seed=5)
+    o1, l1 = _run_prefill(x, 128)
+    o2, l2 = _run_prefill(x, 128)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o1, l1 = _run_prefill(x, None, ga=True)
+    o2, l2 = _run_prefill(x, None, ga=True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------------------
+# decode / MTP verify
+# ---------------------------------------------------------------------------
+
+def _run_decode(x, window):
+    g = _gpu(x)
+    o, lse = swa.swa_sink_decode(g["q"], g["k_new"], g["v_new"], g["k_cache"], g["v_cache"],
+                                 g["ring_head"], g["sinks"])
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _oracle_decode(x, window):
+    return orc.swa_sink_decode(x["q"], x["k_new"], x["v_new"], x["k_cache"], x["v_cache"],
+                               x["ring_head"].numpy(), x["sinks"], window)
+
+
+@pytest.mark.parametrize("t_new", [1, 2, 3, 4])
+def test_decode_small_all_ring_heads(t_new):
+    _say(f"decode B=16 T={t_new} 32/4 D128 bf16, ring heads incl. 0 and 127")
+    x = wl.make_decode(16, t_new, 32, 4, 128, 128, "bf16", seed=300 + t_new)
+    x["ring_head"][0] = 0
+    x["ring_head"][1] = 127
+    x["ring_head"][2] = 1
+    o, lse = _run_decode(x, 128)
+    o_ref, l_ref = _oracle_decode(x, 128)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, f"decode T={t_new}")
+
+
+@pytest.mark.parametrize("case", [(6, 16, 2, 128, 128, "bf16"), (3, 8, 1, 64, 128, "bf16"),
+                                  (4, 8, 8, 128, 64, "bf16"), (5, 4, 1, 64, 128, "f32"),
+                                  (2, 8, 1, 128, 128, "bf16", 8)])
+def test_decode_generic_shapes(case):
+    b, hq, hkv, d, w, dt = case[:6]
+    t_new = case[6] if len(case) > 6 else 3
+    _say(f"decode generic B={b} T={t_new} {hq}/{hkv} D{d} W{w} {dt}")
+    x = wl.make_decode(b, t_new, hq, hkv, d, w, dt, seed=b * 7 + w)
+    o, lse = _run_decode(x, w)
+    o_ref, l_ref = _oracle_decode(x, w)
+    assert_close(x["q"].dtype, o, o_ref, lse, l_ref, f"decode generic {case}")
+
+
+def test_decode_never_reads_oldest_slot():
+    _say("decode: the oldest ring slot holds NaN and must not matter")
+    x = wl.make_decode(8, 4, 32, 4, 128, 128, "bf16", seed=77)
+    o_ref, l_ref = _oracle_decode(x, 128)
+    for b in range(8):
+        h = int(x["ring_head"][b])
+        x["k_cache"][b, :, h] = float("nan")
+        x["v_cache"][b, :, h] = float("nan")
+    o, lse = _run_decode(x, 128)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, "decode NaN oldest slot")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads (launch configuration of the benchmark)
+# ---------------------------------------------------------------------------
+
+def test_swa_prefill_32k_full():
+    _say("swa_prefill_32k: 32768 tokens, 32/4, D128, W128, every element")
+    x = wl.make_workload("swa_prefill_32k")
+    o, lse = _run_prefill(x, 128)
+    o_ref, l_ref = _oracle_prefill(x, 128)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, "swa_prefill_32k")
+
+
+@pytest.mark.parametrize("name", ["decode_t1", "decode_t4"])
+def test_decode_full(name):
+    _say(f"{name}: 256 sequences, every element")
+    x = wl.make_workload(name)
+    o, lse = _run_decode(x, 128)
+    o_ref, l_ref = _oracle_decode(x, 128)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, name)
+
+
+def _sample_rows(x, n_random, seed):
+    cu = x["cu_seqlens"].tolist()
+    n, hq = x["q"].shape[0], x["q"].shape[1]
+    rng = np.random.default_rng(seed)
+    toks = set(int(t) for t in rng.integers(0, n, n_random))
+    for s in range(len(cu) - 1):  # sequence starts, the first window, ends
+        for off in (0, 1, 15, 16, 127, 128, 129):
+            if cu[s] + off < cu[s + 1]:
+                toks.add(cu[s] + off)
+        toks.add(cu[s + 1] - 1)
+    rows = [(t, int(h)) for t in sorted(toks) for h in rng.choice(hq, 2, replace=False)]
+    return np.array(rows)
+
+
+def _check_rows(x, o, lse, rows, window, what):
+    sinks = None if window is None else x["sinks"]
+    o_ref, l_ref = orc.prefill_sample_rows(x["q"], x["k"], x["v"], sinks, x["cu_seqlens"].numpy(),
+                                           rows, window=window)
+    og = to_np(o)[rows[:, 0], rows[:, 1]]
+    lg = to_np(lse)[rows[:, 0], rows[:, 1]]
+    assert_close(torch.bfloat16, og, o_ref, lg, l_ref, what)
+
+
+def test_hybrid_block_full_size():
+    _say("hybrid_5to1_32k: 5 SWA layers (every element of layer 0, sampled rows of 1-4) + GA sampled")
+    for layer in range(6):
+        x = wl.make_workload("hybrid_5to1_32k", layer)
+        ga = layer == 5
+        o, lse = _run_prefill(x, None if ga else 128, ga=ga)
+        if layer == 0:
+            o_ref, l_ref = _oracle_prefill(x, 128)
+            assert_close(torch.bfloat16, o, o_ref, lse, l_ref, "hybrid layer 0")
+        else:
+            rows = _sample_rows(x, 96 if ga else 256, seed=layer)
+            _check_rows(x, o, lse, rows, None if ga else 128, f"hybrid layer {layer}")
+
+
+def test_varlen_262k_sampled():
+    _say("varlen_262k: 8 log-normal sequences, 262144 tokens, sampled rows")
+    x = wl.make_workload("varlen_262k")
+    o, lse = _run_prefill(x, 128)
+    rows = _sample_rows(x, 512, seed=5)
+    _check_rows(x, o, lse, rows, 128, "varlen_262k")
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
