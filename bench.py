@@ -169,7 +169,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="time only the primary workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["prefill", "decode", "ga", "varlen"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "decode1", "ga", "varlen", "copy"],
+                    default=None,
                     help="time a single workload (for profiling runs); prints no JSON line")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -189,14 +190,29 @@ def main(argv=None):
     swa.library()
     steps, warmup = args.steps, args.warmup
 
+    if args.only == "copy":
+        # plain device copy of 512 MiB (read 512 MiB + write 512 MiB): the reference
+        # kernel for scaling the HBM byte counters
+        a = torch.empty(1 << 28, dtype=torch.bfloat16, device=dev).normal_()
+        b = torch.empty_like(a)
+        per, _ = _time_calls(lambda _: b.copy_(a), [None], steps, warmup)
+        _log(f"copy 512 MiB: {_stats(per)}  {2 * a.numel() * 2 / (_stats(per)['mean_ms'] * 1e-3) / 1e9:.0f} GB/s")
+        return 0
     if args.only is not None:
-        name = {"prefill": PRIMARY, "decode": "decode_t4", "ga": "hybrid_5to1_32k",
-                "varlen": "varlen_262k"}[args.only]
+        name = {"prefill": PRIMARY, "decode": "decode_t4", "decode1": "decode_t1",
+                "ga": "hybrid_5to1_32k", "varlen": "varlen_262k"}[args.only]
         layer = 5 if args.only == "ga" else 0
-        x = _with_outputs(_to(wl.make_workload(name, layer), dev), "decode" if args.only == "decode" else "p")
-        fn = _decode_fn() if args.only == "decode" else _prefill_fn(128, ga=args.only == "ga")
-        per, _ = _time_calls(fn, _clone_sets(x, 4 if args.only != "varlen" else 1), steps, warmup)
-        _log(f"{name}: {_stats(per)}")
+        dec = args.only.startswith("decode")
+        x = _with_outputs(_to(wl.make_workload(name, layer), dev), "decode" if dec else "p")
+        fn = _decode_fn() if dec else _prefill_fn(128, ga=args.only == "ga")
+        nsets = 32 if dec else (1 if args.only in ("varlen", "ga") else 4)
+        per, _ = _time_calls(fn, _clone_sets(x, nsets), steps, warmup)
+        fl, by = wl.workload_work(name)
+        if args.only == "ga":
+            fl, by = wl.prefill_flops([32768], 32, 128, None), wl.prefill_bytes(32768, 32, 4, 128, 2)
+        st = _stats(per)
+        _log(f"{name}: {st}  {fl / (st['mean_ms'] * 1e-3) / 1e12:.1f} TFLOP/s  "
+             f"{by / (st['mean_ms'] * 1e-3) / 1e9:.0f} GB/s")
         return 0
 
     # ---------------- primary: SWA-sink prefill, 32K tokens ----------------

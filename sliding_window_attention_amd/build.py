@@ -29,6 +29,9 @@ HIPCC_FLAGS = [
     "-fvisibility=hidden",
     # packed fp32 arithmetic is kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # device code never relies on NaN semantics (masking uses -inf, which stays
+    # honoured); without NaN handling, max/min need no canonicalising moves
+    "-Xarch_device", "-fno-honor-nans", "-Xarch_device", "-mno-amdgpu-ieee",
     "-I", os.path.join(HERE, "..", "include"),
 ]
 

@@ -15,6 +15,16 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Read-only kernel inputs (sequence offsets, sinks) read through the constant
+// address space: wave-uniform reads then become scalar loads, which complete on
+// their own counter instead of waiting behind outstanding vector stores.
+template <typename T>
+using const_ptr = const __attribute__((address_space(4))) T*;
+template <typename T>
+__device__ __forceinline__ const_ptr<T> as_const(const T* p) {
+  return (const_ptr<T>)p;
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kWave = 64;

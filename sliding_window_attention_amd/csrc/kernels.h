@@ -19,6 +19,9 @@ hipError_t launch_online_mfma(const PrefillArgs& a, hipStream_t s);
 // Ring decode, window 128, 1 <= T <= 4.
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
 
+// Compute units of the current device (cached per device).
+hipError_t device_cu_count(int* out);
+
 bool swa_window_mfma_supported(const PrefillArgs& a, bool bf16_io);
 bool online_mfma_supported(const PrefillArgs& a, bool bf16_io);
 bool decode_mfma_supported(const DecodeArgs& a, bool bf16_io);

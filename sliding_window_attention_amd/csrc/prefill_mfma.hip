@@ -9,11 +9,11 @@
 // boundaries: every query row masks keys before its own sequence start, so the
 // grid depends only on the total token count and needs no host-side tile map.
 //
-// swa_window_kernel (window <= 128): the union of the 16 rows' windows is at most
-// 143 keys, so the whole band (9 blocks of 16 keys) is staged once and scored in
-// registers; the softmax is exact in one pass (no online rescaling), the sink
-// entering as the initial maximum candidate and as exp(sink - m) in the
-// denominator.
+// swa_ring_kernel (window <= 128): the union of the 16 rows' windows is at most
+// 143 keys, so the whole band (9 blocks of 16 keys) is scored in registers and
+// the softmax is exact in one pass (no online rescaling), the sink entering as
+// the initial maximum candidate and as exp(sink - m) in the denominator.
+// Workgroups are persistent and keep the band in an LDS ring across tiles.
 //
 // online_kernel (any window, or none): the band is streamed in 64-key chunks
 // with the next chunk prefetched into registers during the current one's
@@ -30,7 +30,6 @@ using namespace tile;
 constexpr int kQT = 16;        // query tokens per workgroup
 constexpr int kHG = 8;         // query heads per workgroup
 constexpr int kThreads = 256;  // 4 wavefronts x 2 heads
-constexpr int kBand = 144;     // keys staged by the window kernel (9 blocks of 16)
 constexpr int kChunk = 64;     // keys per step of the online kernel
 
 // Map a flat workgroup id to (head octet, query tile).  Workgroups are dispatched
@@ -126,111 +125,358 @@ __device__ __forceinline__ void write_out(const PrefillArgs& a, const RowInfo& r
 }
 
 // ---------------------------------------------------------------------------
-// Window <= 128: whole band in registers, exact one-pass softmax.
+// Window <= 128: persistent workgroups walking consecutive 16-query tiles.
+//
+// The 144 keys a tile needs (its 16 queries' windows, 9 blocks of 16) stay in an
+// LDS ring of 9 block slots; moving to the next tile of the same head octet
+// replaces only the oldest block with the 16 newest keys.  Those 16 K/V rows and
+// the next tile's Q are fetched into registers while the current tile finishes
+// its softmax and P*V, so HBM streams continuously.
+//
+// K ring layout: four planes (one per 32-element head-dim chunk), 64-byte rows;
+// the 16-byte unit of lane group g sits at g ^ kswz(key), which keeps the 16
+// rows an MFMA operand read touches on 16 distinct bank quads.
+// V ring layout: 264-byte rows (256 + 8, so consecutive rows shift banks by 8
+// bytes), read with ds_read_b64_tr_b16: within each 16-lane group, lane 4e+m
+// points at 4 consecutive head-dim elements of key row e, and lane 4m'+c receives
+// element c of rows e = 0..3 of group member m' -- the transposed operand the
+// P*V product needs, with no register shuffles.  Head-dim quad m of block b
+// starts at qoff(m, b); the resulting O^T rows put head-dim
+// 64(g>>1) + 16(g&1) + {0..15} and the same + 32 in lane group g.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads, 2) void swa_window_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kBand * kRowBytes];
-  char* ks = smem;
-  char* vs = smem + kBand * kRowBytes;
+namespace ring {
 
-  const int ntiles = (a.total_tokens + kQT - 1) / kQT;
-  const int item = xcd_item(blockIdx.x, gridDim.x);
-  const int oct = item / ntiles;
-  const int q0 = (item - oct * ntiles) * kQT;
-  const int h_base = oct * kHG;
-  const int kvh = h_base / (a.num_q_heads / a.num_kv_heads);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int i = lane & 15, g = lane >> 4;
-  const int kbase = q0 - 128;  // LDS row r holds key kbase + r
+constexpr int kSlots = 9;                    // ring slots of 16 keys
+constexpr int kRows = 16 * kSlots;           // 144 keys
+constexpr int kKPlane = kRows * 64;          // bytes of one 32-element chunk plane
+constexpr int kKBytes = 4 * kKPlane;         // 36864
+constexpr int kVPitch = 264;
+constexpr int kVBytes = kRows * kVPitch;     // 38016
 
-  const RowInfo ri = row_info(a, q0, h_base, w, i);
-  bf16x8 qa[4], qb[4];
-  load_q(a, ri, g, qa, qb);
-  stage_kv<kBand>(ks, vs, static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v), kbase,
-                  a.total_tokens, a.num_kv_heads, kvh);
+__device__ __forceinline__ int kswz(int key) { return ((key >> 3) ^ (key >> 2)) & 3; }
+// MFMA row -> key order of the last (single) block: lane groups 0/1 get keys
+// 0-3 / 8-11 so that their transposed V reads fall on different banks.
+__device__ __forceinline__ int pi8(int i) { return 8 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+__device__ __forceinline__ int qoff(int m, int b) {
+  return 64 * (m >> 1) + 32 * (b >> 2) + 16 * (m & 1) + 4 * (b & 3);
+}
+__device__ __forceinline__ int mod9(int x) { x %= kSlots; return x < 0 ? x + kSlots : x; }
 
-  // Row bounds relative to kbase; the lane's column is query qi.
-  const int rel_lo = ri.lo - kbase;  // >= 1 because window <= 128
-  const int rel_hi = ri.qi - kbase;  // = 128 + i
-  const int lo_min = __shfl(rel_lo, 0);   // rows are ordered, so lane 0 / 15 bound the tile
-  const int lo_max = __shfl(rel_lo, 15);
-  const float c = a.scale * kLog2e;
-  const float sink0 = a.sinks ? a.sinks[ri.h0] * kLog2e : -INFINITY;
-  const float sink1 = a.sinks ? a.sinks[ri.h1] * kLog2e : -INFINITY;
-  __syncthreads();
+__device__ __forceinline__ void put_k(char* ks, int phys, int key, int u, u32x4 x) {
+  *reinterpret_cast<u32x4*>(ks + (u >> 2) * kKPlane + phys * 64 + 16 * ((u & 3) ^ kswz(key))) = x;
+}
+__device__ __forceinline__ void put_v(char* vs, int phys, int u, u32x4 x) {
+  char* p = vs + phys * kVPitch + 16 * u;
+  *reinterpret_cast<u32x2*>(p) = (u32x2){x[0], x[1]};
+  *reinterpret_cast<u32x2*>(p + 8) = (u32x2){x[2], x[3]};
+}
 
-  // ---- S^T = K Q^T over 9 blocks of 16 keys ----
-  f32x4 s0[9], s1[9];
-  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 tr_read(const char* vs, int off) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + off));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// Load all 144 rows of a tile whose first key is kbase into the ring.
+__device__ __attribute__((noinline)) void fill(char* ks, char* vs, const bf16* __restrict__ k,
+                                     const bf16* __restrict__ v, int kbase, int N, int hkv, int kvh) {
+  const int t = threadIdx.x;
+  const int r = t >> 4, u = t & 15;
+  const int kblock0 = mod9(kbase >> 4);
+  u32x4 kr[kSlots], vr[kSlots];
 #pragma unroll
-  for (int bl = 0; bl < 9; ++bl) {
-    s0[bl] = zero4;
-    s1[bl] = zero4;
-    const int kr_max = bl < 8 ? 32 * (bl >> 1) + 4 * (bl & 1) + 27 : 143;
-    if (kr_max < lo_min) continue;  // whole block before every row's window
-    const int row = bl < 8 ? 32 * (bl >> 1) + pair_row(i, bl & 1) : 128 + i;
+  for (int j = 0; j < kSlots; ++j) {
+    const int key = kbase + 16 * j + r;
+    kr[j] = (u32x4){0, 0, 0, 0};
+    vr[j] = (u32x4){0, 0, 0, 0};
+    if (key >= 0 && key < N) {
+      const size_t off = ((size_t)key * hkv + kvh) * D + u * 8;
+      kr[j] = *reinterpret_cast<const u32x4*>(k + off);
+      vr[j] = *reinterpret_cast<const u32x4*>(v + off);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    const int phys = 16 * mod9(kblock0 + j) + r;
+    put_k(ks, phys, kbase + 16 * j + r, u, kr[j]);
+    put_v(vs, phys, u, vr[j]);
+  }
+}
+
+// Store 32 head-dim values of one query row held by lane group g, scaled by inv.
+__device__ __forceinline__ void store_row(bf16* row, int g, const f32x4 (&o)[8], float inv) {
+  const int d0 = 64 * (g >> 1) + 16 * (g & 1);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      bf16x8 v;
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const int b = 4 * half + 2 * q + bb;
+        bf16x2 lo = __builtin_convertvector((f32x2){o[b][0] * inv, o[b][1] * inv}, bf16x2);
+        bf16x2 hi = __builtin_convertvector((f32x2){o[b][2] * inv, o[b][3] * inv}, bf16x2);
+        v[4 * bb + 0] = lo[0]; v[4 * bb + 1] = lo[1];
+        v[4 * bb + 2] = hi[0]; v[4 * bb + 3] = hi[1];
+      }
+      *reinterpret_cast<bf16x8*>(row + d0 + 32 * half + 8 * q) = v;
+    }
+  }
+}
+
+}  // namespace ring
+
+// Index of the sequence holding packed token q: the largest s < num_seqs with
+// cu[s] <= q (wave-uniform binary search on scalar loads).
+__device__ __forceinline__ int find_seq(const_ptr<int32_t> cu, int num_seqs, int q) {
+  int lo = 0, hi = num_seqs;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= q) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, int items_per_wg) {
+  using namespace ring;
+  __shared__ __attribute__((aligned(16))) char smem[kKBytes + kVBytes];
+  char* ks = smem;
+  char* vs = smem + kKBytes;
+
+  const int N = a.total_tokens, Hq = a.num_q_heads, hkv = a.num_kv_heads;
+  const int ntiles = (N + kQT - 1) / kQT;
+  const int total = ntiles * (Hq / kHG);
+  int item = blockIdx.x * items_per_wg;
+  const int item_end = min(item + items_per_wg, total);
+  if (item >= item_end) return;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 15, g = lane >> 4;
+  const int t = threadIdx.x;
+  const int G = Hq / hkv;
+  const int S = a.num_seqs;
+  const const_ptr<int32_t> cu = as_const(a.cu_seqlens);
+  const const_ptr<float> sinks = as_const(a.sinks);
+  const bf16* kp = static_cast<const bf16*>(a.k);
+  const bf16* vp = static_cast<const bf16*>(a.v);
+  const bf16* qp = static_cast<const bf16*>(a.q);
+  const float c = a.scale * kLog2e;
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // Lane-constant parts of the LDS addresses.
+  const int pr0 = pair_row(i, 0), pr1 = pair_row(i, 1), p8 = pi8(i);
+  const int vrow = 8 * (g & 1) + (i >> 2);                  // row within a 16-key block, pairs
+  const int vrow8 = 8 * (g & 1) + 4 * (g >> 1) + (i >> 2);  // the single diagonal block
+  const int vquad = 2 * (64 * ((i & 3) >> 1) + 16 * (i & 1));  // bytes of qoff(i & 3, 0)
+
+  // Q of one tile: lane (i, g) holds head-dim 32cc + 8g .. +8 of query q0 + i.
+  bf16x8 qa[4], qb[4];
+  auto load_q_tile = [&](int q0n, int octn) {
+    const int qi = q0n + i;
+    const bool ok = qi < N;
+    const size_t r0 = ((size_t)qi * Hq + octn * kHG + 2 * w) * D + 8 * g;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      const bf16x8 kf = lds_read8(ks, row, 4 * cc + g);
-      s0[bl] = mfma32(kf, qa[cc], s0[bl]);
-      s1[bl] = mfma32(kf, qb[cc], s1[bl]);
+      qa[cc] = ok ? *reinterpret_cast<const bf16x8*>(qp + r0 + 32 * cc) : zero8();
+      qb[cc] = ok ? *reinterpret_cast<const bf16x8*>(qp + r0 + D + 32 * cc) : zero8();
     }
-  }
+  };
 
-  // ---- mask, row max ----
-  float mx0 = -INFINITY, mx1 = -INFINITY;
+  // Outer loop: runs of consecutive tiles of one head octet (the ring is filled
+  // once per run).  Inner loop: one tile per iteration, the ring advancing by
+  // one 16-key block.
+  while (item < item_end) {
+    item = __builtin_amdgcn_readfirstlane(item);
+    const int oct = item / ntiles;
+    int tile = item - oct * ntiles;
+    const int run_end = min(item_end, (oct + 1) * ntiles);
+    int seq = find_seq(cu, S, tile * kQT);  // sequence of the tile's first query
+    const int kvh = (oct * kHG) / G;
+    __syncthreads();  // the previous run is done with the ring
+    fill(ks, vs, kp, vp, tile * kQT - 128, N, hkv, kvh);
+    load_q_tile(tile * kQT, oct);
+    // Drain the run prologue's loads so that, at the loop head, no vector load
+    // is outstanding on any path: each iteration waits for its prefetches
+    // before it issues its stores.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    const int run_len = __builtin_amdgcn_readfirstlane(run_end - item);
+    const int tile0 = tile;
+    for (int k = 0; k < run_len; ++k) {
+      tile = tile0 + k;
+      const int q0 = tile * kQT;
+      const int kbase = q0 - 128;  // ring block j holds keys kbase + 16j ..
+      const int kblock0 = mod9(kbase >> 4);
+      const int par = (kbase >> 4) & 1;
+      int sk[kSlots];  // byte offset of ring block j in a K plane
 #pragma unroll
-  for (int bl = 0; bl < 9; ++bl) {
-    const int kr_min = bl < 8 ? 32 * (bl >> 1) + 4 * (bl & 1) : 128;
-    const int kr_max = bl < 8 ? kr_min + 27 : 143;
-    const bool full = kr_min >= lo_max && kr_max <= 128;  // valid for all 16 rows
-    if (!full) {
+      for (int j = 0; j < kSlots; ++j) sk[j] = 16 * mod9(kblock0 + j) * 64;
+      const int h0 = oct * kHG + 2 * w;
+
+      // ---- first visible key of each row: window and own-sequence start ----
+      while (seq + 1 < S && cu[seq + 1] <= q0) ++seq;
+      const int qi = q0 + i;
+      int start = cu[seq];
+      for (int s2 = seq + 1; s2 < S && cu[s2] < q0 + kQT; ++s2)  // boundaries inside the tile
+        start = qi >= cu[s2] ? cu[s2] : start;
+      const long lw = (long)qi - a.window + 1;
+      const int lo = lw > start ? (int)lw : start;
+      const int rel_lo = lo - kbase;
+      const int rel_hi = qi - kbase;
+      // rows are ordered, so lanes 0 and 15 bound the tile (wave-uniform values)
+      const int lo_min = __builtin_amdgcn_readfirstlane(rel_lo);
+      const int lo_max = __builtin_amdgcn_readlane(rel_lo, 15);
+      const unsigned span = (unsigned)(rel_hi - rel_lo);  // key kr is visible iff kr - rel_lo <= span
+      const float sink0 = a.sinks ? sinks[h0] * kLog2e : -INFINITY;
+      const float sink1 = a.sinks ? sinks[h0 + 1] * kLog2e : -INFINITY;
+
+      // ---- S^T = K Q^T over 9 blocks of 16 keys ----
+      f32x4 s0[9], s1[9];
+      {
+        const int ko0 = pr0 * 64 + 16 * (g ^ kswz(16 * par + pr0)) - (i >= 8 ? 16 * 64 : 0);
+        const int ko1 = pr1 * 64 + 16 * (g ^ kswz(16 * par + pr1)) - (i >= 8 ? 16 * 64 : 0);
+        const int ko8 = p8 * 64 + 16 * (g ^ kswz(16 * par + p8));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kr = bl < 8 ? 32 * (bl >> 1) + 8 * g + 4 * (bl & 1) + r : 128 + 4 * g + r;
-        const bool ok = kr >= rel_lo && kr <= rel_hi;
-        s0[bl][r] = ok ? s0[bl][r] : -INFINITY;
-        s1[bl][r] = ok ? s1[bl][r] : -INFINITY;
+        for (int bl = 0; bl < 9; ++bl) {
+          const int kr_max = bl < 8 ? 32 * (bl >> 1) + 4 * (bl & 1) + 27 : 143;
+          if (kr_max < lo_min) {  // whole block before every row's window
+            s0[bl] = zero4;
+            s1[bl] = zero4;
+            continue;
+          }
+          int off;
+          if (bl < 8) {
+            const int p = bl >> 1;
+            off = (i >= 8 ? sk[2 * p + 1] : sk[2 * p]) + ((bl & 1) ? ko1 : ko0);
+          } else {
+            off = sk[8] + ko8;
+          }
+          bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + off);
+          s0[bl] = mfma32(kf, qa[0], zero4);
+          s1[bl] = mfma32(kf, qb[0], zero4);
+#pragma unroll
+          for (int cc = 1; cc < 4; ++cc) {
+            kf = *reinterpret_cast<const bf16x8*>(ks + cc * kKPlane + off);
+            s0[bl] = mfma32(kf, qa[cc], s0[bl]);
+            s1[bl] = mfma32(kf, qb[cc], s1[bl]);
+          }
+        }
+      }
+
+      // ---- prefetch for the next tile: its 16 newest K/V rows and its Q ----
+      const bool has_next = k + 1 < run_len;
+      u32x4 pk = {0, 0, 0, 0}, pv = {0, 0, 0, 0};
+      const int nkey = q0 + 16 + (t >> 4);
+      if (has_next && nkey < N) {
+        const size_t off = ((size_t)nkey * hkv + kvh) * D + (t & 15) * 8;
+        pk = *reinterpret_cast<const u32x4*>(kp + off);
+        pv = *reinterpret_cast<const u32x4*>(vp + off);
+      }
+      if (has_next) load_q_tile(q0 + kQT, oct);
+
+      // ---- mask, row max ----
+      float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+      for (int bl = 0; bl < 9; ++bl) {
+        const int kr_min = bl < 8 ? 32 * (bl >> 1) + 4 * (bl & 1) : 128;
+        const int kr_max = bl < 8 ? kr_min + 27 : 143;
+        const bool full = kr_min >= lo_max && kr_max <= 128;  // valid for all 16 rows
+        if (!full) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kr = bl < 8 ? 32 * (bl >> 1) + 8 * g + 4 * (bl & 1) + r
+                                  : 128 + 8 * (g & 1) + 4 * (g >> 1) + r;
+            const bool ok = (unsigned)(kr - rel_lo) <= span;
+            s0[bl][r] = ok ? s0[bl][r] : -INFINITY;
+            s1[bl][r] = ok ? s1[bl][r] : -INFINITY;
+          }
+        }
+        mx0 = fmaxf(mx0, fmaxf(fmaxf(s0[bl][0], s0[bl][1]), fmaxf(s0[bl][2], s0[bl][3])));
+        mx1 = fmaxf(mx1, fmaxf(fmaxf(s1[bl][0], s1[bl][1]), fmaxf(s1[bl][2], s1[bl][3])));
+      }
+      const float m0 = fmaxf(quad_max(mx0) * c, sink0);
+      const float m1 = fmaxf(quad_max(mx1) * c, sink1);
+
+      // ---- exponentiate, sum, pack P to bf16 (pairs of blocks feed one k=32 product) ----
+      float l0 = 0.f, l1 = 0.f;
+      bf16x8 pa[4], pb[4];
+#pragma unroll
+      for (int bl = 0; bl < 9; ++bl) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s0[bl][r] = fast_exp2(fmaf(s0[bl][r], c, -m0));
+          s1[bl][r] = fast_exp2(fmaf(s1[bl][r], c, -m1));
+          l0 += s0[bl][r];
+          l1 += s1[bl][r];
+        }
+        if (bl & 1) {
+          pa[bl >> 1] = pack_pair(s0[bl - 1], s0[bl]);
+          pb[bl >> 1] = pack_pair(s1[bl - 1], s1[bl]);
+        }
+      }
+      const bf16x4 pa8 = pack_quad(s0[8]), pb8 = pack_quad(s1[8]);
+      const float z0 = quad_sum(l0) + fast_exp2(sink0 - m0);
+      const float z1 = quad_sum(l1) + fast_exp2(sink1 - m1);
+
+      // ---- O^T = V^T P^T: the single diagonal block first (initialises O), then pairs ----
+      f32x4 o0[8], o1[8];
+      {
+        const int vb8 = 16 * mod9(kblock0 + 8) * kVPitch + vrow8 * kVPitch + vquad;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const bf16x4 av = tr_read(vs, vb8 + 2 * (32 * (b >> 2) + 4 * (b & 3)));
+          o0[b] = mfma16(av, pa8, zero4);
+          o1[b] = mfma16(av, pb8, zero4);
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        if (32 * p + 31 < lo_min) continue;  // pair entirely before every window
+        // lane groups 0-1 read the pair's first 16-key block, groups 2-3 its second
+        const int slot_a = 16 * mod9(kblock0 + 2 * p) * kVPitch;
+        const int slot_b = 16 * mod9(kblock0 + 2 * p + 1) * kVPitch;
+        const int vb = (g >= 2 ? slot_b : slot_a) + vrow * kVPitch + vquad;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const int bo = 2 * (32 * (b >> 2) + 4 * (b & 3));
+          const bf16x4 lo4 = tr_read(vs, vb + bo);
+          const bf16x4 hi4 = tr_read(vs, vb + 4 * kVPitch + bo);
+          const bf16x8 av = (bf16x8){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+          o0[b] = mfma32(av, pa[p], o0[b]);
+          o1[b] = mfma32(av, pb[p], o1[b]);
+        }
+      }
+
+      // ---- ring update for the next tile.  Every load of this iteration is waited
+      // for here, before this tile's stores are issued: loads and stores share one
+      // completion counter, so a store issued ahead of a load's wait would make
+      // that wait cover the store too. ----
+      if (has_next) {
+        __syncthreads();  // every wavefront is done with the oldest ring block
+        const int phys = 16 * kblock0 + (t >> 4);  // the next tile's newest block
+        put_k(ks, phys, nkey, t & 15, pk);
+        put_v(vs, phys, t & 15, pv);
+        __syncthreads();
+      }
+
+      // ---- epilogue: O and LSE of this tile ----
+      if (qi < N) {
+        bf16* out = static_cast<bf16*>(a.out) + ((size_t)qi * Hq + h0) * D;
+        store_row(out, g, o0, __builtin_amdgcn_rcpf(z0));
+        store_row(out + D, g, o1, __builtin_amdgcn_rcpf(z1));
+        if (a.lse != nullptr && g == 0) {
+          float* l = a.lse + (size_t)qi * Hq + h0;
+          l[0] = (m0 + fast_log2(z0)) * kLn2;
+          l[1] = (m1 + fast_log2(z1)) * kLn2;
+        }
       }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      mx0 = fmaxf(mx0, s0[bl][r]);
-      mx1 = fmaxf(mx1, s1[bl][r]);
-    }
+    item = run_end;  // next run
   }
-  const float m0 = fmaxf(quad_max(mx0) * c, sink0);
-  const float m1 = fmaxf(quad_max(mx1) * c, sink1);
-
-  // ---- exponentiate, sum ----
-  float l0 = 0.f, l1 = 0.f;
-#pragma unroll
-  for (int bl = 0; bl < 9; ++bl) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s0[bl][r] = fast_exp2(fmaf(s0[bl][r], c, -m0));
-      s1[bl][r] = fast_exp2(fmaf(s1[bl][r], c, -m1));
-      l0 += s0[bl][r];
-      l1 += s1[bl][r];
-    }
-  }
-  const float z0 = quad_sum(l0) + fast_exp2(sink0 - m0);
-  const float z1 = quad_sum(l1) + fast_exp2(sink1 - m1);
-
-  // ---- O^T = V^T P^T ----
-  f32x4 o0[8], o1[8];
-#pragma unroll
-  for (int b = 0; b < 8; ++b) { o0[b] = zero4; o1[b] = zero4; }
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    if (32 * p + 31 < lo_min) continue;  // pair entirely before every window
-    pv_pair(vs, 32 * p, i, g, pack_pair(s0[2 * p], s0[2 * p + 1]), pack_pair(s1[2 * p], s1[2 * p + 1]),
-            o0, o1);
-  }
-  pv_single(vs, 128, i, g, pack_quad(s0[8]), pack_quad(s1[8]), o0, o1);
-
-  write_out(a, ri, g, o0, o1, z0, z1, m0, m1);
 }
+
 
 // ---------------------------------------------------------------------------
 // Any window: online softmax over 64-key chunks.
@@ -383,7 +629,15 @@ hipError_t launch_swa_window_mfma(const PrefillArgs& a, hipStream_t s) {
   const long ntiles = (a.total_tokens + kQT - 1) / kQT;
   const long total = ntiles * (a.num_q_heads / kHG);
   if (total > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(swa_window_kernel, dim3((unsigned)total), dim3(kThreads), 0, s, a);
+  // two resident workgroups per compute unit (LDS-bound), each walking a
+  // contiguous run of tiles
+  int cus = 0;
+  hipError_t e = device_cu_count(&cus);
+  if (e != hipSuccess) return e;
+  const long slots = 2L * cus;
+  const long per = (total + slots - 1) / slots;
+  const long grid = (total + per - 1) / per;
+  hipLaunchKernelGGL(swa_ring_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a, (int)per);
   return hipGetLastError();
 }
 
