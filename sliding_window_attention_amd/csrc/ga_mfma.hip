@@ -1,0 +1,259 @@
+// Matrix-core prefill with an online softmax: global causal attention (the GA
+// layers of the hybrid block: MiMo-V2-Flash Technical Report digest, section 2.2,
+// the same operator with no window and no sink) and sliding windows longer than
+// 128 keys (with the per-head sink of section 2.2.2).
+//
+// A workgroup of 8 wavefronts owns 32 consecutive query tokens and the 8 query
+// heads of one KV head; wavefront w takes query sub-tile w >> 2 and heads
+// 2(w & 3), 2(w & 3) + 1, i.e. two 16-query MFMA tiles sharing every K read.  Keys
+// are streamed in 64-key chunks through two LDS buffers: the next chunk is loaded
+// into registers while the current one is multiplied, written to the other
+// buffer, and one barrier per chunk hands it over.  The running maximum is raised
+// lazily: O and the running sum are rescaled only when some row's maximum grows
+// by more than kSlack (log2 units); otherwise the exponent keeps the older, smaller
+// reference and the weights may exceed 1 by at most 2^kSlack, which fp32 sums and
+// bf16 weights hold without loss of relative precision.
+#include "common.h"
+#include "kernels.h"
+#include "mfma_tile.h"
+
+namespace swa {
+namespace {
+
+using namespace tile;
+
+constexpr int kQT = 32;                  // query tokens per workgroup
+constexpr int kHG = 8;                   // query heads per workgroup
+constexpr int kThreads = 512;            // 8 wavefronts
+constexpr int kChunk = 64;               // keys per step
+constexpr int kKPlane = kChunk * 64;     // bytes of one 32-element chunk plane of K
+constexpr int kKBuf = 4 * kKPlane;       // 16384
+constexpr int kVBuf = kChunk * kVPitch;  // 16896
+constexpr int kBuf = kKBuf + kVBuf;
+constexpr float kSlack = 8.f;
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void ga_chunk_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kBuf];
+  const int N = a.total_tokens, Hq = a.num_q_heads, hkv = a.num_kv_heads;
+  const int ntiles = (N + kQT - 1) / kQT;
+  // latest (heaviest) tiles first; consecutive workgroups spread over the XCDs
+  const int item = __builtin_amdgcn_readfirstlane(gridDim.x - 1 - blockIdx.x);
+  const int oct = item / ntiles;
+  const int q0 = (item - oct * ntiles) * kQT;
+  const int kvh = (oct * kHG) / (Hq / hkv);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 15, g = lane >> 4;
+  const int t = threadIdx.x;
+  const int h0 = oct * kHG + 2 * (w & 3);
+  const int qw = q0 + 16 * (w >> 2);  // first query of this wavefront's tiles
+  const int qi = qw + i;
+  const bf16* kp = static_cast<const bf16*>(a.k);
+  const bf16* vp = static_cast<const bf16*>(a.v);
+  const bf16* qp = static_cast<const bf16*>(a.q);
+  const float c = a.scale * kLog2e;
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // ---- first visible key of each row, of this wavefront and of the workgroup ----
+  const int start = seq_start_of(a.cu_seqlens, a.num_seqs, qi < N ? qi : N - 1);
+  const long lw = (long)qi - a.window + 1;
+  const int lo = lw > start ? (int)lw : start;
+  const int lo_w_min = __builtin_amdgcn_readfirstlane(lo);  // rows are ordered
+  const int lo_w_max = __builtin_amdgcn_readlane(lo, 15);
+  const int s0q = seq_start_of(a.cu_seqlens, a.num_seqs, q0);
+  const long lw0 = (long)q0 - a.window + 1;
+  const int lo_wg = __builtin_amdgcn_readfirstlane(lw0 > s0q ? (int)lw0 : s0q);
+  const int kend = q0 + kQT;
+  const int nchunks = (kend - lo_wg + kChunk - 1) / kChunk;
+
+  // ---- Q of the two tiles: lane (i, g) holds head-dim 32cc + 8g .. +8 of query qi ----
+  bf16x8 qa[4], qb[4];
+  {
+    const bool ok = qi < N;
+    const size_t r0 = ((size_t)qi * Hq + h0) * D + 8 * g;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      qa[cc] = ok ? *reinterpret_cast<const bf16x8*>(qp + r0 + 32 * cc) : zero8();
+      qb[cc] = ok ? *reinterpret_cast<const bf16x8*>(qp + r0 + D + 32 * cc) : zero8();
+    }
+  }
+
+  // ---- chunk staging: thread t moves 16-byte units x = it*512 + t (K rows for
+  // it = 0, 1; V rows for it = 2, 3) ----
+  u32x4 pf[4];
+  auto prefetch = [&](int kb) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int x = it * kThreads + t;
+      const int row = (x & 1023) >> 4, u = x & 15;
+      const int key = kb + row;
+      pf[it] = (u32x4){0, 0, 0, 0};
+      if (key >= 0 && key < N)
+        pf[it] = *reinterpret_cast<const u32x4*>((it < 2 ? kp : vp) + ((size_t)key * hkv + kvh) * D + u * 8);
+    }
+  };
+  auto commit = [&](char* buf, int kb) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int x = it * kThreads + t;
+      const int row = (x & 1023) >> 4, u = x & 15;
+      if (it < 2) put_k(buf, kKPlane, row, kb + row, u, pf[it]);
+      else put_v(buf + kKBuf, row, u, pf[it]);
+    }
+  };
+
+  // Lane-constant LDS offsets.  Chunk bases are multiples of 32, so a key's low
+  // five bits equal its row's and the K swizzle depends on the row alone.
+  const int pr0 = pair_row(i, 0), pr1 = pair_row(i, 1);
+  const int ko0 = pr0 * 64 + 16 * (g ^ kswz(pr0));
+  const int ko1 = pr1 * 64 + 16 * (g ^ kswz(pr1));
+  const int vrow = 16 * (g >> 1) + 8 * (g & 1) + (i >> 2);  // V row of pair 0, first half
+  const int vo = kKBuf + vrow * kVPitch + vquad_bytes(i);
+
+  const float sink0 = a.sinks ? a.sinks[h0] * kLog2e : -INFINITY;
+  const float sink1 = a.sinks ? a.sinks[h0 + 1] * kLog2e : -INFINITY;
+  float m0 = sink0, m1 = sink1;  // reference maxima (log2 units)
+  float l0 = a.sinks ? 1.f : 0.f, l1 = l0;
+  f32x4 o0[8], o1[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) { o0[b] = zero4; o1[b] = zero4; }
+
+  prefetch(kend - nchunks * kChunk);
+  commit(smem, kend - nchunks * kChunk);
+  __syncthreads();
+
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int kb = kend - (nchunks - ch) * kChunk;  // first key of this chunk
+    const char* buf = smem + (ch & 1) * kBuf;
+    if (ch + 1 < nchunks) prefetch(kb + kChunk);
+
+    // chunk entirely outside this wavefront's rows (before every window / after
+    // every query): nothing to do
+    const bool skip = kb + kChunk - 1 < lo_w_min || kb > qw + 15;
+    if (!skip) {
+      // ---- S^T = K Q^T over 4 blocks of 16 keys (2 pairs) ----
+      f32x4 s0[4], s1[4];
+#pragma unroll
+      for (int bl = 0; bl < 4; ++bl) {
+        const int off = 32 * 64 * (bl >> 1) + ((bl & 1) ? ko1 : ko0);
+        bf16x8 kf = *reinterpret_cast<const bf16x8*>(buf + off);
+        s0[bl] = mfma32(kf, qa[0], zero4);
+        s1[bl] = mfma32(kf, qb[0], zero4);
+#pragma unroll
+        for (int cc = 1; cc < 4; ++cc) {
+          kf = *reinterpret_cast<const bf16x8*>(buf + cc * kKPlane + off);
+          s0[bl] = mfma32(kf, qa[cc], s0[bl]);
+          s1[bl] = mfma32(kf, qb[cc], s1[bl]);
+        }
+      }
+      // ---- mask (only chunks not fully visible to every row) and chunk maxima ----
+      const bool full = kb >= lo_w_max && kb + kChunk - 1 <= qw;
+      if (!full) {
+        const unsigned span = (unsigned)(qi - lo);
+#pragma unroll
+        for (int bl = 0; bl < 4; ++bl)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kb + 32 * (bl >> 1) + 8 * g + 4 * (bl & 1) + r;
+            const bool ok = (unsigned)(key - lo) <= span;
+            s0[bl][r] = ok ? s0[bl][r] : -INFINITY;
+            s1[bl][r] = ok ? s1[bl][r] : -INFINITY;
+          }
+      }
+      float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+      for (int bl = 0; bl < 4; ++bl) {
+        mx0 = fmaxf(mx0, fmaxf(fmaxf(s0[bl][0], s0[bl][1]), fmaxf(s0[bl][2], s0[bl][3])));
+        mx1 = fmaxf(mx1, fmaxf(fmaxf(s1[bl][0], s1[bl][1]), fmaxf(s1[bl][2], s1[bl][3])));
+      }
+      mx0 = quad_max(mx0) * c;
+      mx1 = quad_max(mx1) * c;
+      // ---- lazy rescale: only when some row's maximum outgrows its reference ----
+      if (__builtin_amdgcn_ballot_w64(mx0 > m0 + kSlack) != 0) {
+        const float mn = fmaxf(m0, mx0);
+        const float al = (m0 == -INFINITY) ? 0.f : fast_exp2(m0 - mn);
+        l0 *= al;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) o0[b] *= al;
+        m0 = mn;
+      }
+      if (__builtin_amdgcn_ballot_w64(mx1 > m1 + kSlack) != 0) {
+        const float mn = fmaxf(m1, mx1);
+        const float al = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - mn);
+        l1 *= al;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) o1[b] *= al;
+        m1 = mn;
+      }
+      // rows that have seen no visible key yet keep reference -inf: exponentiate
+      // against 0 so masked scores give exactly 0
+      const float e0 = (m0 == -INFINITY) ? 0.f : m0;
+      const float e1 = (m1 == -INFINITY) ? 0.f : m1;
+      // ---- exponentiate, sum, pack P ----
+      bf16x8 pa[2], pb[2];
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int bl = 0; bl < 4; ++bl) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s0[bl][r] = fast_exp2(fmaf(s0[bl][r], c, -e0));
+          s1[bl][r] = fast_exp2(fmaf(s1[bl][r], c, -e1));
+          ps0 += s0[bl][r];
+          ps1 += s1[bl][r];
+        }
+        if (bl & 1) {
+          pa[bl >> 1] = pack_pair(s0[bl - 1], s0[bl]);
+          pb[bl >> 1] = pack_pair(s1[bl - 1], s1[bl]);
+        }
+      }
+      l0 += quad_sum(ps0);
+      l1 += quad_sum(ps1);
+      // ---- O^T += V^T P^T ----
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const int off = vo + 32 * kVPitch * p + vblock_bytes(b);
+          const bf16x4 lo4 = tr_read(buf, off);
+          const bf16x4 hi4 = tr_read(buf, off + 4 * kVPitch);
+          const bf16x8 av = (bf16x8){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+          o0[b] = mfma32(av, pa[p], o0[b]);
+          o1[b] = mfma32(av, pb[p], o1[b]);
+        }
+      }
+    }
+
+    if (ch + 1 < nchunks) commit(smem + ((ch + 1) & 1) * kBuf, kb + kChunk);
+    __syncthreads();  // the next buffer is written; this one is no longer read
+  }
+
+  // ---- epilogue ----
+  if (qi < N) {
+    bf16* out = static_cast<bf16*>(a.out) + ((size_t)qi * Hq + h0) * D;
+    store_row_tr(out, g, o0, __builtin_amdgcn_rcpf(l0));
+    store_row_tr(out + D, g, o1, __builtin_amdgcn_rcpf(l1));
+    if (a.lse != nullptr && g == 0) {
+      float* l = a.lse + (size_t)qi * Hq + h0;
+      l[0] = (m0 + fast_log2(l0)) * kLn2;
+      l[1] = (m1 + fast_log2(l1)) * kLn2;
+    }
+  }
+}
+
+}  // namespace
+
+bool online_mfma_supported(const PrefillArgs& a, bool bf16_io) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+  return bf16_io && a.head_dim == 128 && G % kHG == 0 && a.window >= 1;
+}
+
+hipError_t launch_online_mfma(const PrefillArgs& a, hipStream_t s) {
+  const long ntiles = (a.total_tokens + kQT - 1) / kQT;
+  const long total = ntiles * (a.num_q_heads / kHG);
+  if (total > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(ga_chunk_kernel, dim3((unsigned)total), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace swa

@@ -15,9 +15,7 @@
 //    block b standing for head-dim element 8r + b.  Lane (i, g) then holds
 //    head-dim 32g .. 32g+31 of query i (element 32g + 8r + b in register r of
 //    block b), which is 64 contiguous output bytes.
-//  * K and V tiles live in LDS as 256-byte rows (128 bf16) whose 16-byte units are
-//    XOR-swizzled per row (unit u of row r at u ^ swz(r)); every access pattern
-//    below touches 16 distinct units per 16 lanes, i.e. no bank conflicts.
+//  * V operands of P*V are read from LDS with ds_read_b64_tr_b16 (see tr_read).
 #pragma once
 
 #include "common.h"
@@ -28,15 +26,6 @@ namespace tile {
 constexpr int D = 128;
 constexpr int kRowBytes = D * 2;
 constexpr int kUnitsPerRow = kRowBytes / 16;
-
-__device__ __forceinline__ int swz(int r) {
-  return (r & 3) | ((((r >> 3) ^ (r >> 2)) & 3) << 2);
-}
-__device__ __forceinline__ int lds_off(int r, int u) { return r * kRowBytes + ((u ^ swz(r)) << 4); }
-
-__device__ __forceinline__ bf16x8 lds_read8(const char* base, int r, int u) {
-  return *reinterpret_cast<const bf16x8*>(base + lds_off(r, u));
-}
 
 // Row (relative to the pair's first key) that MFMA row `row` of block s reads.
 __device__ __forceinline__ int pair_row(int row, int s) { return 8 * (row >> 2) + 4 * s + (row & 3); }
@@ -78,49 +67,63 @@ __device__ __forceinline__ bf16x4 column4(const bf16x8* rows, int e) {
   return (bf16x4){rows[0][e], rows[1][e], rows[2][e], rows[3][e]};
 }
 
-// O^T += V^T P^T over one 32-key pair for two query tiles.  `vs` is the LDS V
-// tile, `r0` the first row of the pair.  Lane (i, g) reads V rows r0 + 8g + e
-// (e = 0..7) at 16-byte unit i: head-dim 8i .. 8i+7 of its 8 keys; the 8x8
-// transpose turns them into the A operands of the 8 head-dim blocks.
-__device__ __forceinline__ void pv_pair(const char* vs, int r0, int i, int g, bf16x8 p0, bf16x8 p1,
-                                        f32x4 (&o0)[8], f32x4 (&o1)[8]) {
-  bf16x8 vr[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) vr[e] = lds_read8(vs, r0 + 8 * g + e, i);
-#pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const bf16x8 a = column8(vr, b);
-    o0[b] = mfma32(a, p0, o0[b]);
-    o1[b] = mfma32(a, p1, o1[b]);
-  }
+// K tiles in LDS: four planes (one per 32-element head-dim chunk) of 64-byte rows;
+// the 16-byte unit of lane group g sits at g ^ kswz(key), so the 16 rows an MFMA
+// operand read touches fall on 16 distinct bank quads (for any 16-aligned run of
+// keys, in the pair order of pair_row and in the order of pi8).
+__device__ __forceinline__ int kswz(int key) { return ((key >> 3) ^ (key >> 2)) & 3; }
+__device__ __forceinline__ void put_k(char* ks, int plane_bytes, int row, int key, int u, u32x4 x) {
+  *reinterpret_cast<u32x4*>(ks + (u >> 2) * plane_bytes + row * 64 + 16 * ((u & 3) ^ kswz(key))) = x;
 }
 
-// Same for a single 16-key block (k = 16 product); lane (i, g) holds keys 4g..4g+3.
-__device__ __forceinline__ void pv_single(const char* vs, int r0, int i, int g, bf16x4 p0, bf16x4 p1,
-                                          f32x4 (&o0)[8], f32x4 (&o1)[8]) {
-  bf16x8 vr[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) vr[e] = lds_read8(vs, r0 + 4 * g + e, i);
-#pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const bf16x4 a = (bf16x4){vr[0][b], vr[1][b], vr[2][b], vr[3][b]};
-    o0[b] = mfma16(a, p0, o0[b]);
-    o1[b] = mfma16(a, p1, o1[b]);
-  }
+// V tiles in LDS: rows of 264 bytes (256 + 8, so consecutive rows shift banks by
+// 8 bytes), read with ds_read_b64_tr_b16.  Within each 16-lane group, lane 4e+m
+// addresses 4 consecutive head-dim elements of key row e and lane 4m'+c receives
+// element c of rows e = 0..3 addressed by group member m' -- a 4x4 transpose that
+// yields the k-contiguous V^T operand.  Head-dim quad m of output block b starts
+// at qoff(m, b); the O^T result then holds head-dim 64(g>>1) + 16(g&1) + {0..15}
+// and the same + 32 in lane group g.
+constexpr int kVPitch = 264;
+__device__ __forceinline__ void put_v(char* vs, int row, int u, u32x4 x) {
+  char* p = vs + row * kVPitch + 16 * u;
+  *reinterpret_cast<u32x2*>(p) = (u32x2){x[0], x[1]};
+  *reinterpret_cast<u32x2*>(p + 8) = (u32x2){x[2], x[3]};
+}
+// Byte offset of quad (i & 3) of block 0 within a V row: lane-constant part.
+__device__ __forceinline__ int vquad_bytes(int i) { return 2 * (64 * ((i & 3) >> 1) + 16 * (i & 1)); }
+// Byte offset added for output block b (compile-time after unrolling).
+__device__ __forceinline__ int vblock_bytes(int b) { return 2 * (32 * (b >> 2) + 4 * (b & 3)); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 tr_read(const char* vs, int off) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + off));
+  return __builtin_bit_cast(bf16x4, r);
 }
 
-// Store 32 head-dim values (32g .. 32g+31) of one query row, scaled by inv, as bf16.
-__device__ __forceinline__ void store_row32(bf16* dst, const f32x4 (&o)[8], float inv) {
+// MFMA row -> key order of a single (unpaired) 16-key block: lane groups 0/1 get
+// keys 0-3 / 8-11 so that their transposed V reads fall on different banks.
+__device__ __forceinline__ int pi8(int i) { return 8 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+
+// Store the 32 head-dim values of one query row held by lane group g (O^T layout
+// of the transposed V reads), scaled by inv and rounded to bf16.
+__device__ __forceinline__ void store_row_tr(bf16* row, int g, const f32x4 (&o)[8], float inv) {
+  const int d0 = 64 * (g >> 1) + 16 * (g & 1);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    bf16x8 v;
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
-    for (int b = 0; b < 8; b += 2) {
-      bf16x2 t = __builtin_convertvector((f32x2){o[b][r] * inv, o[b + 1][r] * inv}, bf16x2);
-      v[b] = t[0];
-      v[b + 1] = t[1];
+    for (int q = 0; q < 2; ++q) {
+      bf16x8 v;
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const int b = 4 * half + 2 * q + bb;
+        bf16x2 lo = __builtin_convertvector((f32x2){o[b][0] * inv, o[b][1] * inv}, bf16x2);
+        bf16x2 hi = __builtin_convertvector((f32x2){o[b][2] * inv, o[b][3] * inv}, bf16x2);
+        v[4 * bb + 0] = lo[0]; v[4 * bb + 1] = lo[1];
+        v[4 * bb + 2] = hi[0]; v[4 * bb + 3] = hi[1];
+      }
+      *reinterpret_cast<bf16x8*>(row + d0 + 32 * half + 8 * q) = v;
     }
-    *reinterpret_cast<bf16x8*>(dst + 8 * r) = v;
   }
 }
 

@@ -140,6 +140,36 @@ def test_ga_prefill_small(case):
     assert_close(x["q"].dtype, o, o_ref, lse, l_ref, f"ga {case}")
 
 
+def _growing_keys(x, factor):
+    """Scale each key by 1 + factor * (position in its sequence) / length, so that
+    row maxima keep rising along the sequence (forces repeated online rescales)."""
+    cu = x["cu_seqlens"].tolist()
+    k = x["k"].float()
+    for s in range(len(cu) - 1):
+        n = cu[s + 1] - cu[s]
+        ramp = 1.0 + factor * torch.arange(n, dtype=torch.float32) / max(n, 1)
+        k[cu[s]:cu[s + 1]] *= ramp[:, None, None]
+    x["k"] = k.to(x["k"].dtype)
+    return x
+
+
+def test_ga_prefill_rising_maxima():
+    _say("ga prefill with key norms rising 6x along each sequence (lazy rescale path)")
+    x = _growing_keys(wl.make_prefill([900, 260], 16, 2, 128, "bf16", seed=31, with_sinks=False), 5.0)
+    o, lse = _run_prefill(x, None, ga=True)
+    o_ref, l_ref = _oracle_prefill(x, None, ga=True)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, "ga rising maxima")
+
+
+def test_long_window_sink_rising_maxima():
+    _say("swa prefill W=200 (online kernel) with sinks in [-3, 12] and rising key norms")
+    x = _growing_keys(wl.make_prefill([700, 90], 8, 1, 128, "bf16", seed=32), 4.0)
+    x["sinks"] = torch.linspace(-3.0, 12.0, 8)
+    o, lse = _run_prefill(x, 200)
+    o_ref, l_ref = _oracle_prefill(x, 200)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, "W=200 rising maxima")
+
+
 def test_prefill_large_sink_and_no_lse():
     _say("swa prefill with sinks +40 (outputs ~0) and lse=None")
     x = wl.make_prefill([300], 32, 4, 128, "bf16", seed=99)
