@@ -11,9 +11,10 @@
 // 32w .. 32w+31, wavefront 0 also the new tokens.  The four partial results are
 // merged exactly: the wavefronts first agree on each column's maximum (through
 // LDS), exponentiate against that common maximum, and their partial sums and
-// partial outputs then simply add.  Everything is read straight from HBM into
-// MFMA operand registers; V rows are loaded 16 lanes per 256-byte row (fully
-// coalesced) and transposed in registers.
+// partial outputs then simply add.  The ring is read straight from HBM into MFMA
+// operand registers (V rows 16 lanes per 256-byte row, fully coalesced, and
+// transposed in registers); the query columns and the new tokens' K/V, shared by
+// the four wavefronts, are staged once in LDS.
 #include "common.h"
 #include "kernels.h"
 #include "mfma_tile.h"
@@ -28,15 +29,60 @@ constexpr int kHG = 8;          // query heads per KV-head group handled togethe
 constexpr int kThreads = 256;
 constexpr int kColBytes = 528;  // fp32 partial row (512 B) padded against bank conflicts
 
+constexpr int kRowPitch = 272;  // staged bf16 row (256 B) padded: 16 rows hit 16 bank quads
+
 template <int NT>
 struct DecodeSmem {
   float m[4][NT * 16];
   float l[4][NT * 16];
-  char o[4][NT * 16][kColBytes];
+  union {
+    char o[2][NT * 16][kColBytes];  // two partial-output slots for the pairwise merge
+    struct {
+      char q[NT * 16][kRowPitch];  // query columns (dead once the scores are formed)
+      char kn[16][kRowPitch];      // new-token K rows, zero past T
+    } in;
+  } u;
+  char vn[16][kRowPitch];  // new-token V rows, zero past T
 };
 
+// Partial O^T of lane (i, g), column tt*16 + i, head-dim 32g + 8r + b, to/from LDS.
 template <int NT>
-__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
+__device__ __forceinline__ void put_partial(char (*slot)[kColBytes], int i, int g,
+                                            const f32x4 (&o)[NT][8]) {
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    char* row = slot[tt * 16 + i];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<f32x4*>(row + (32 * g + 8 * r) * 4) =
+          (f32x4){o[tt][0][r], o[tt][1][r], o[tt][2][r], o[tt][3][r]};
+      *reinterpret_cast<f32x4*>(row + (32 * g + 8 * r + 4) * 4) =
+          (f32x4){o[tt][4][r], o[tt][5][r], o[tt][6][r], o[tt][7][r]};
+    }
+  }
+}
+template <int NT>
+__device__ __forceinline__ void add_partial(const char (*slot)[kColBytes], int i, int g,
+                                            f32x4 (&o)[NT][8]) {
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const char* row = slot[tt * 16 + i];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(row + (32 * g + 8 * r) * 4);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(row + (32 * g + 8 * r + 4) * 4);
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        o[tt][bb][r] += lo[bb];
+        o[tt][bb + 4][r] += hi[bb];
+      }
+    }
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) DecodeSmem<NT> sm;
   const int noct = a.num_q_heads / kHG;
   const int b = blockIdx.x / noct;
@@ -46,9 +92,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   const int kvh = h_base / (a.num_q_heads / hkv);
   const int T = a.t_new;
   const int Hq = a.num_q_heads;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 15, g = lane >> 4;
-  int head = a.ring_head[b] % kW;
+  int head = as_const(a.ring_head)[b] % kW;  // scalar load: addresses wait on nothing else
   head += head < 0 ? kW : 0;
 
   const bf16* qp = static_cast<const bf16*>(a.q);
@@ -57,7 +104,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   const bf16* kn = static_cast<const bf16*>(a.k_new) + ((size_t)b * T * hkv + kvh) * D;
   const bf16* vn = static_cast<const bf16*>(a.v_new) + ((size_t)b * T * hkv + kvh) * D;
 
-  // ---- loads: ring K (A operand), ring V rows, Q (B operand) ----
+  // ---- loads: ring K (A operand) and ring V rows into registers; Q columns and
+  // the new tokens' K/V staged once in LDS for the four wavefronts ----
   bf16x8 kf[2][4];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -75,31 +123,40 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     const int phys = (head + kr) & (kW - 1);
     vr[e] = kr != 0 ? *reinterpret_cast<const bf16x8*>(vc + (size_t)phys * D + 8 * i) : zero8();
   }
-  bf16x8 qf[NT][4];
+  {
+    const int tid = threadIdx.x;
+    u32x4 st[NT + 2];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {  // Q column col = x >> 4: token col >> 3, head col & 7
+      const int x = k * kThreads + tid;
+      const int col = x >> 4, uu = x & 15, t = col >> 3;
+      st[k] = (u32x4){0, 0, 0, 0};
+      if (t < T)
+        st[k] = *reinterpret_cast<const u32x4*>(qp + (((size_t)b * T + t) * Hq + h_base + (col & 7)) * D + 8 * uu);
+    }
+    const int row = tid >> 4, uu = tid & 15;  // new token `row`
+    st[NT] = (u32x4){0, 0, 0, 0};
+    st[NT + 1] = (u32x4){0, 0, 0, 0};
+    if (row < T) {
+      st[NT] = *reinterpret_cast<const u32x4*>(kn + (size_t)row * hkv * D + 8 * uu);
+      st[NT + 1] = *reinterpret_cast<const u32x4*>(vn + (size_t)row * hkv * D + 8 * uu);
+    }
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+      const int x = k * kThreads + tid;
+      *reinterpret_cast<u32x4*>(&sm.u.in.q[x >> 4][16 * (x & 15)]) = st[k];
+    }
+    *reinterpret_cast<u32x4*>(&sm.u.in.kn[row][16 * uu]) = st[NT];
+    *reinterpret_cast<u32x4*>(&sm.vn[row][16 * uu]) = st[NT + 1];
+  }
   int tcol[NT];
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt) {
-    tcol[tt] = 2 * tt + (i >> 3);
-    const int h = h_base + (i & 7);
-    const bool ok = tcol[tt] < T;
-    const size_t off = (((size_t)b * T + tcol[tt]) * Hq + h) * D + 8 * g;
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-      qf[tt][cc] = ok ? *reinterpret_cast<const bf16x8*>(qp + off + 32 * cc) : zero8();
-  }
-  // new tokens (wavefront 0): K rows = token i, V rows = tokens 4g .. 4g+3
-  bf16x8 kfn[4], vrn[4];
-  if (w == 0) {
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-      kfn[cc] = i < T ? *reinterpret_cast<const bf16x8*>(kn + (size_t)i * hkv * D + 32 * cc + 8 * g)
-                      : zero8();
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int u = 4 * g + e;
-      vrn[e] = u < T ? *reinterpret_cast<const bf16x8*>(vn + (size_t)u * hkv * D + 8 * i) : zero8();
-    }
-  }
+  for (int tt = 0; tt < NT; ++tt) tcol[tt] = 2 * tt + (i >> 3);
+  __syncthreads();
+  // B operand (Q^T) of tile tt, head-dim chunk cc: column tt*16 + i, unit 4cc + g
+  auto qop = [&](int tt, int cc) {
+    return *reinterpret_cast<const bf16x8*>(&sm.u.in.q[tt * 16 + i][16 * (4 * cc + g)]);
+  };
 
   const float c = a.scale * kLog2e;
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -112,12 +169,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     for (int ss = 0; ss < 2; ++ss) {
       s[tt][ss] = zero4;
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) s[tt][ss] = mfma32(kf[ss][cc], qf[tt][cc], s[tt][ss]);
+      for (int cc = 0; cc < 4; ++cc) s[tt][ss] = mfma32(kf[ss][cc], qop(tt, cc), s[tt][ss]);
     }
     sn[tt] = zero4;
     if (w == 0) {
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) sn[tt] = mfma32(kfn[cc], qf[tt][cc], sn[tt]);
+      for (int cc = 0; cc < 4; ++cc)
+        sn[tt] = mfma32(*reinterpret_cast<const bf16x8*>(&sm.u.in.kn[i][16 * (4 * cc + g)]), qop(tt, cc), sn[tt]);
     }
   }
 
@@ -188,6 +246,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     for (int tt = 0; tt < NT; ++tt) o[tt][bb] = mfma32(av, pack_pair(s[tt][0], s[tt][1]), o[tt][bb]);
   }
   if (w == 0) {
+    bf16x8 vrn[4];  // V rows of new tokens 4g .. 4g+3, head-dim 8i .. 8i+7
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vrn[e] = *reinterpret_cast<const bf16x8*>(&sm.vn[4 * g + e][16 * i]);
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb) {
       const bf16x4 av = column4(vrn, bb);
@@ -195,51 +256,41 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
       for (int tt = 0; tt < NT; ++tt) o[tt][bb] = mfma16(av, pack_quad(sn[tt]), o[tt][bb]);
     }
   }
-  // lane (i, g) holds head-dim 32g + 8r + bb of column tt*16 + i
-#pragma unroll
-  for (int tt = 0; tt < NT; ++tt) {
-    char* row = sm.o[w][tt * 16 + i];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      f32x4 lo = {o[tt][0][r], o[tt][1][r], o[tt][2][r], o[tt][3][r]};
-      f32x4 hi = {o[tt][4][r], o[tt][5][r], o[tt][6][r], o[tt][7][r]};
-      *reinterpret_cast<f32x4*>(row + (32 * g + 8 * r) * 4) = lo;
-      *reinterpret_cast<f32x4*>(row + (32 * g + 8 * r + 4) * 4) = hi;
-    }
-  }
+  // ---- merge the four partials (they share the column maxima, so they add):
+  // wavefronts 2, 3 hand theirs to 0, 1; then 1 hands its sum to 0 ----
+  if (w >= 2) put_partial<NT>(sm.u.o[w - 2], i, g, o);
   __syncthreads();
+  if (w < 2) add_partial<NT>(sm.u.o[w], i, g, o);
+  __syncthreads();
+  if (w == 1) put_partial<NT>(sm.u.o[0], i, g, o);
+  __syncthreads();
+  if (w != 0) return;
+  add_partial<NT>(sm.u.o[0], i, g, o);
 
-  // ---- merge the four partials; 16 threads per column, 8 head-dim elements each ----
+  // ---- normalise and store: lane (i, g) owns head-dim 32g .. 32g+31 of column tt*16 + i ----
   bf16* out = static_cast<bf16*>(a.out);
 #pragma unroll
-  for (int it = 0; it < NT; ++it) {
-    const int item = it * kThreads + threadIdx.x;
-    const int col = item >> 4, dc = item & 15;
-    const int t = 2 * (col >> 4) + ((col & 15) >> 3);
-    const int h = h_base + (col & 7);
+  for (int tt = 0; tt < NT; ++tt) {
+    const int col = tt * 16 + i;
+    const int t = tcol[tt];
     if (t >= T) continue;
-    const float sink2 = a.sinks[h] * kLog2e;
-    const float m = fmaxf(fmaxf(fmaxf(sm.m[0][col], sm.m[1][col]), fmaxf(sm.m[2][col], sm.m[3][col])), sink2);
-    const float z = sm.l[0][col] + sm.l[1][col] + sm.l[2][col] + sm.l[3][col] + fast_exp2(sink2 - m);
-    const float inv = 1.f / z;
-    f32x4 acc0 = zero4, acc1 = zero4;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const char* row = sm.o[ww][col];
-      acc0 += *reinterpret_cast<const f32x4*>(row + dc * 32);
-      acc1 += *reinterpret_cast<const f32x4*>(row + dc * 32 + 16);
-    }
-    bf16x8 v8;
-#pragma unroll
-    for (int e = 0; e < 4; e += 2) {
-      bf16x2 x = __builtin_convertvector((f32x2){acc0[e] * inv, acc0[e + 1] * inv}, bf16x2);
-      bf16x2 y = __builtin_convertvector((f32x2){acc1[e] * inv, acc1[e + 1] * inv}, bf16x2);
-      v8[e] = x[0]; v8[e + 1] = x[1];
-      v8[4 + e] = y[0]; v8[4 + e + 1] = y[1];
-    }
+    const int h = h_base + (i & 7);
+    const float z = sm.l[0][col] + sm.l[1][col] + sm.l[2][col] + sm.l[3][col] +
+                    fast_exp2(a.sinks[h] * kLog2e - mcol[tt]);
+    const float inv = __builtin_amdgcn_rcpf(z);
     const size_t row_idx = ((size_t)b * T + t) * Hq + h;
-    *reinterpret_cast<bf16x8*>(out + row_idx * D + 8 * dc) = v8;
-    if (a.lse != nullptr && dc == 0) a.lse[row_idx] = (m + fast_log2(z)) * kLn2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      bf16x8 v8;
+#pragma unroll
+      for (int bb = 0; bb < 8; bb += 2) {
+        const bf16x2 x = __builtin_convertvector((f32x2){o[tt][bb][r] * inv, o[tt][bb + 1][r] * inv}, bf16x2);
+        v8[bb] = x[0];
+        v8[bb + 1] = x[1];
+      }
+      *reinterpret_cast<bf16x8*>(out + row_idx * D + 32 * g + 8 * r) = v8;
+    }
+    if (a.lse != nullptr && g == 0) a.lse[row_idx] = (mcol[tt] + fast_log2(z)) * kLn2;
   }
 }
 
