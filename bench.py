@@ -47,9 +47,15 @@ def _clone_sets(x, n):
     return sets
 
 
+SETTLE_S = 0.3
+
+
 def _time_calls(fn, sets, steps, warmup, per_call=True):
     """Warm up, then time `steps` calls (set rotated per call) with HIP events.
 
+    Before the `warmup` counted calls the GPU is kept busy with untimed calls for
+    at least SETTLE_S seconds, so that its clocks have left their idle state when
+    the timed region opens (a few calls of a 0.15 ms kernel do not get there).
     Returns (per-call milliseconds list, milliseconds of the whole timed region).
     per_call=False records events only around the region (kernels of a few tens of
     microseconds: an event pair per launch would add its own dispatch overhead);
@@ -58,6 +64,13 @@ def _time_calls(fn, sets, steps, warmup, per_call=True):
 
     for x in sets:  # marshal every input set once, outside the timed region
         fn(x)
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while time.perf_counter() - t0 < SETTLE_S:
+        fn(sets[n % len(sets)])
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     for s in range(warmup):
         fn(sets[s % len(sets)])
     torch.cuda.synchronize()
@@ -220,8 +233,8 @@ def cpu_baseline(sample_tokens=32768):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="time only the primary workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", choices=["prefill", "decode", "decode1", "ga", "varlen", "copy"],

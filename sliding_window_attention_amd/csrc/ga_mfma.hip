@@ -134,6 +134,9 @@ void ga_chunk_kernel(PrefillArgs a) {
     if (!skip) {
       // ---- S^T = K Q^T over 4 blocks of 16 keys (2 pairs) ----
       f32x4 s0[4], s1[4];
+      // Raised issue priority over the MFMA runs: the two waves sharing a SIMD then
+      // tend to alternate matrix work with the other's softmax instead of colliding.
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int bl = 0; bl < 4; ++bl) {
         const int off = 32 * 64 * (bl >> 1) + ((bl & 1) ? ko1 : ko0);
@@ -147,6 +150,7 @@ void ga_chunk_kernel(PrefillArgs a) {
           s1[bl] = mfma32(kf, qb[cc], s1[bl]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       // ---- mask (only chunks not fully visible to every row) and chunk maxima ----
       const bool full = kb >= lo_w_max && kb + kChunk - 1 <= qw;
       if (!full) {
@@ -210,6 +214,7 @@ void ga_chunk_kernel(PrefillArgs a) {
       l0 += quad_sum(ps0);
       l1 += quad_sum(ps1);
       // ---- O^T += V^T P^T ----
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
 #pragma unroll
@@ -224,6 +229,7 @@ void ga_chunk_kernel(PrefillArgs a) {
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     if (ch + 1 < nchunks) commit(smem + ((ch + 1) & 1) * kBuf, kb + kChunk);
     __syncthreads();  // the next buffer is written; this one is no longer read
   }
