@@ -98,15 +98,35 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// The value of lane l and of lane l ^ kStride (kStride 16 or 32), in an order that
+// depends on the lane.  v_permlane16_swap / v_permlane32_swap exchange 16-lane rows
+// (32-lane halves) between their two register operands in one VALU instruction;
+// with x in both operands the two results are x[l] and x[l ^ kStride].  Every lane
+// of the wavefront must be active.
+template <int kStride>
+__device__ __forceinline__ f32x2 with_partner(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  if constexpr (kStride == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return (f32x2){__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])};
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return (f32x2){__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])};
+  }
+}
+
 // Max / sum over the four lanes l, l^16, l^32, l^48 (the lanes that hold the
-// same column of a 16x16 MFMA result).
+// same column of a 16x16 MFMA result).  Both operations are commutative, so all
+// four lanes end with bitwise the same value.  Every lane must be active.
 __device__ __forceinline__ float quad_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  f32x2 p = with_partner<16>(x);
+  p = with_partner<32>(fmaxf(p[0], p[1]));
+  return fmaxf(p[0], p[1]);
 }
 __device__ __forceinline__ float quad_sum(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  f32x2 p = with_partner<16>(x);
+  p = with_partner<32>(p[0] + p[1]);
+  return p[0] + p[1];
 }
 
 }  // namespace swa

@@ -79,27 +79,57 @@ void ga_chunk_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- chunk staging: thread t moves 16-byte units x = it*512 + t (K rows for
-  // it = 0, 1; V rows for it = 2, 3) ----
+  // ---- chunk staging: thread t moves the 16-byte unit su = t & 15 of key rows
+  // srow = t >> 4 and srow + 32, of K (pf[0], pf[1]) and of V (pf[2], pf[3]) ----
+  const int srow = t >> 4, su = t & 15;
+  const size_t key_stride = (size_t)hkv * D;  // elements from one key's row to the next
+  const uint32_t goff0 = (uint32_t)((((size_t)srow * hkv + kvh) * D + su * 8) * sizeof(bf16));
+  const uint32_t goff1 = goff0 + (uint32_t)(32 * key_stride * sizeof(bf16));
   u32x4 pf[4];
+  bool edge = false;             // (uniform) the staged chunk reaches outside [0, N)
+  bool ok_lo = true, ok_hi = true;  // rows srow / srow + 32 of the staged chunk exist
   auto prefetch = [&](int kb) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int x = it * kThreads + t;
-      const int row = (x & 1023) >> 4, u = x & 15;
-      const int key = kb + row;
-      pf[it] = (u32x4){0, 0, 0, 0};
-      if (key >= 0 && key < N)
-        pf[it] = *reinterpret_cast<const u32x4*>((it < 2 ? kp : vp) + ((size_t)key * hkv + kvh) * D + u * 8);
+    edge = !(kb >= 0 && kb + kChunk <= N);
+    if (!edge) {
+      // whole chunk inside the token stream: a uniform base and lane-constant offsets
+      const char* kbase = reinterpret_cast<const char*>(kp + (size_t)kb * key_stride);
+      const char* vbase = reinterpret_cast<const char*>(vp + (size_t)kb * key_stride);
+      pf[0] = *reinterpret_cast<const u32x4*>(kbase + goff0);
+      pf[1] = *reinterpret_cast<const u32x4*>(kbase + goff1);
+      pf[2] = *reinterpret_cast<const u32x4*>(vbase + goff0);
+      pf[3] = *reinterpret_cast<const u32x4*>(vbase + goff1);
+    } else {
+      // rows outside the stream load a clamped row (no masked loads, which would
+      // force early waits) and are zeroed when committed
+      const int r0 = kb + srow, r1 = r0 + 32;
+      ok_lo = r0 >= 0 && r0 < N;
+      ok_hi = r1 >= 0 && r1 < N;
+      const size_t e0 = ((size_t)min(max(r0, 0), N - 1) * hkv + kvh) * D + su * 8;
+      const size_t e1 = ((size_t)min(max(r1, 0), N - 1) * hkv + kvh) * D + su * 8;
+      pf[0] = *reinterpret_cast<const u32x4*>(kp + e0);
+      pf[1] = *reinterpret_cast<const u32x4*>(kp + e1);
+      pf[2] = *reinterpret_cast<const u32x4*>(vp + e0);
+      pf[3] = *reinterpret_cast<const u32x4*>(vp + e1);
     }
   };
-  auto commit = [&](char* buf, int kb) {
+  // LDS byte offsets of the thread's units (put_k / put_v layouts).  Chunk bases are
+  // multiples of 32, so a key's swizzle equals that of its row in the chunk, and
+  // rows srow and srow + 32 share it.
+  const int ks_off = (su >> 2) * kKPlane + srow * 64 + 16 * ((su & 3) ^ kswz(srow));
+  const int vs_off = kKBuf + srow * kVPitch + 16 * su;
+  auto commit = [&](char* buf) {
+    if (edge) {
+      const u32x4 z = {0, 0, 0, 0};
+      if (!ok_lo) { pf[0] = z; pf[2] = z; }
+      if (!ok_hi) { pf[1] = z; pf[3] = z; }
+    }
+    *reinterpret_cast<u32x4*>(buf + ks_off) = pf[0];
+    *reinterpret_cast<u32x4*>(buf + ks_off + 32 * 64) = pf[1];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int x = it * kThreads + t;
-      const int row = (x & 1023) >> 4, u = x & 15;
-      if (it < 2) put_k(buf, kKPlane, row, kb + row, u, pf[it]);
-      else put_v(buf + kKBuf, row, u, pf[it]);
+    for (int h = 0; h < 2; ++h) {
+      char* v = buf + vs_off + 32 * kVPitch * h;
+      *reinterpret_cast<u32x2*>(v) = (u32x2){pf[2 + h][0], pf[2 + h][1]};
+      *reinterpret_cast<u32x2*>(v + 8) = (u32x2){pf[2 + h][2], pf[2 + h][3]};
     }
   };
 
@@ -120,7 +150,7 @@ void ga_chunk_kernel(PrefillArgs a) {
   for (int b = 0; b < 8; ++b) { o0[b] = zero4; o1[b] = zero4; }
 
   prefetch(kend - nchunks * kChunk);
-  commit(smem, kend - nchunks * kChunk);
+  commit(smem);
   __syncthreads();
 
   for (int ch = 0; ch < nchunks; ++ch) {
@@ -230,7 +260,7 @@ void ga_chunk_kernel(PrefillArgs a) {
     }
 
     __builtin_amdgcn_s_setprio(0);
-    if (ch + 1 < nchunks) commit(smem + ((ch + 1) & 1) * kBuf, kb + kChunk);
+    if (ch + 1 < nchunks) commit(smem + ((ch + 1) & 1) * kBuf);
     __syncthreads();  // the next buffer is written; this one is no longer read
   }
 
