@@ -83,6 +83,10 @@ __device__ __forceinline__ int seq_start_of(const int32_t* __restrict__ cu, int 
 
 __device__ __forceinline__ float bf16_to_f32(bf16 x) { return (float)x; }
 
+// s_waitcnt immediate for vmcnt(0) with the other counters left alone (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kVmcnt0 = 0x0F70;
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

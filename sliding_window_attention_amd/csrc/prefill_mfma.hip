@@ -299,6 +299,11 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
       }
 
       // ---- epilogue: O and LSE of this tile ----
+      // vmcnt(0) on every path (on the common one the ring update has already
+      // waited): it tells the compiler that no prefetch load is outstanding past
+      // this point, so the next tile need not wait at its head, where the wait
+      // would also cover this tile's stores.
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
       if (qi < N) {
         bf16* out = static_cast<bf16*>(a.out) + ((size_t)qi * Hq + h0) * D;
         store_row_tr(out, g, o0, __builtin_amdgcn_rcpf(z0));
