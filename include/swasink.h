@@ -81,7 +81,8 @@ typedef enum { SWA_DTYPE_F32 = 0, SWA_DTYPE_BF16 = 1 } swa_dtype;
  *  window     >= 1: row i attends keys max(seq_start, i-window+1) .. i.
  *  out        [total_tokens, num_q_heads, head_dim]   dtype
  *  lse        [total_tokens, num_q_heads] fp32, or NULL
- * total_tokens == 0 is accepted and launches nothing.
+ * total_tokens == 0 is accepted once the sizes validate: nothing is launched, read or
+ * written, and the data pointers may then be NULL.
  */
 SWASINK_API int swa_sink_prefill(const void* q, const void* k, const void* v, const float* sinks,
                      const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
@@ -117,7 +118,8 @@ SWASINK_API int ga_causal_prefill(const void* q, const void* k, const void* v, c
  *  lse          [batch, T, num_q_heads] fp32, or NULL
  * Query t sees logical slots t+1 .. window-1 and new tokens 0 .. t, i.e. exactly
  * `window` keys; logical slot 0 is never read.  Requires 1 <= T < window.
- * batch == 0 is accepted and launches nothing.
+ * batch == 0 is accepted once the sizes validate: nothing is launched, read or written,
+ * and the data pointers may then be NULL.
  */
 SWASINK_API int swa_sink_decode(const void* q, const void* k_new, const void* v_new, const void* k_cache,
                     const void* v_cache, const int32_t* ring_head, const float* sinks,

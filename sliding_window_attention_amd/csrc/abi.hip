@@ -91,10 +91,10 @@ int prefill_common(const void* q, const void* k, const void* v, const float* sin
   if (window < 1) return fail(SWA_ERR_SHAPE, "%s: window must be >= 1 (got %d)", name, window);
   if ((long long)total_tokens * hq * d > (1LL << 40))
     return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
+  if (total_tokens == 0) return ok();  // nothing is read or written: pointers may be NULL
   if (!q || !k || !v || !cu_seqlens || !out || (need_sinks && !sinks))
     return fail(SWA_ERR_NULL, "%s: q, k, v, %scu_seqlens and out must be non-NULL", name,
                 need_sinks ? "sinks, " : "");
-  if (total_tokens == 0) return ok();
 
   swa::PrefillArgs a;
   a.q = q; a.k = k; a.v = v;
@@ -154,11 +154,11 @@ int swa_sink_decode(const void* q, const void* k_new, const void* v_new, const v
                 window);
   if ((long long)batch * num_kv_heads * window * head_dim > (1LL << 40))
     return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
+  if (batch == 0) return ok();  // nothing is read or written: pointers may be NULL
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !ring_head || !sinks || !out)
     return fail(SWA_ERR_NULL,
                 "%s: q, k_new, v_new, k_cache, v_cache, ring_head, sinks and out must be non-NULL",
                 name);
-  if (batch == 0) return ok();
 
   swa::DecodeArgs a;
   a.q = q; a.k_new = k_new; a.v_new = v_new;

@@ -126,6 +126,46 @@ def make_decode(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, dtype
             "ring_head": ring_head, "sinks": sinks}
 
 
+def _randn_device(shape, gen, device, dtype, chunk_rows=1 << 18):
+    """N(0, 1) rounded to `dtype`, drawn on `device` a slab of rows at a time (so
+    that no fp32 copy of a multi-GB tensor is ever held)."""
+    out = torch.empty(shape, dtype=dtype, device=device)
+    for r0 in range(0, shape[0], chunk_rows):
+        r1 = min(shape[0], r0 + chunk_rows)
+        out[r0:r1] = torch.randn((r1 - r0,) + tuple(shape[1:]), generator=gen, device=device).to(dtype)
+    return out
+
+
+def make_prefill_device(seq_lens, num_q_heads, num_kv_heads, head_dim, seed, device):
+    """make_prefill for streams too large to draw on the host: bf16 q/k/v drawn on
+    `device` by a seeded device generator (different values from make_prefill for
+    the same seed), fp32 sinks and int32 cu_seqlens on the host."""
+    lens = [int(x) for x in seq_lens]
+    n = sum(lens)
+    gen = torch.Generator(device=device).manual_seed(int(seed))
+    q = _randn_device((n, num_q_heads, head_dim), gen, device, torch.bfloat16)
+    k = _randn_device((n, num_kv_heads, head_dim), gen, device, torch.bfloat16)
+    v = _randn_device((n, num_kv_heads, head_dim), gen, device, torch.bfloat16)
+    sinks = torch.randn(num_q_heads, generator=torch.Generator().manual_seed(int(seed)))
+    return {"q": q, "k": k, "v": v, "sinks": sinks, "cu_seqlens": cu_from_lengths(lens),
+            "max_seqlen": max(lens), "lengths": lens}
+
+
+def make_decode_device(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, seed, device):
+    """make_decode with bf16 tensors drawn on `device` (for batches whose caches
+    are too large to draw on the host); ring heads and sinks on the host."""
+    gen = torch.Generator(device=device).manual_seed(int(seed))
+    hgen = torch.Generator().manual_seed(int(seed))
+    bf = torch.bfloat16
+    return {"q": _randn_device((batch, t_new, num_q_heads, head_dim), gen, device, bf),
+            "k_new": _randn_device((batch, t_new, num_kv_heads, head_dim), gen, device, bf),
+            "v_new": _randn_device((batch, t_new, num_kv_heads, head_dim), gen, device, bf),
+            "k_cache": _randn_device((batch, num_kv_heads, window, head_dim), gen, device, bf, 4096),
+            "v_cache": _randn_device((batch, num_kv_heads, window, head_dim), gen, device, bf, 4096),
+            "ring_head": torch.randint(0, window, (batch,), generator=hgen, dtype=torch.int64).to(torch.int32),
+            "sinks": torch.randn(num_q_heads, generator=hgen)}
+
+
 def make_workload(name: str, layer: int = 0):
     """Inputs of a named workload (for 'hybrid_5to1_32k', layer 0..4 are SWA, 5 is GA)."""
     w = WORKLOADS[name]

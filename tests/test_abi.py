@@ -121,6 +121,19 @@ def test_decode_empty_batch_is_ok():
     assert _decode(b=0) == OK
 
 
+def test_empty_inputs_accept_null_pointers_but_still_validate_sizes():
+    lib = swa.library()
+    assert _prefill(n=0, max_seqlen=0, q=NULL, k=NULL, v=NULL, sinks=NULL, cu=NULL, out=NULL) == OK
+    assert lib.ga_causal_prefill(NULL, NULL, NULL, NULL, 1, 0, 0, 8, 1, 128, 0.0, 1, NULL, NULL,
+                                 NULL) == OK
+    assert _decode(b=0, q=NULL, kn=NULL, vn=NULL, kc=NULL, vc=NULL, head=NULL, sinks=NULL,
+                   out=NULL) == OK
+    assert _prefill(n=0, max_seqlen=0, hq=12, hkv=8) == E_SHAPE
+    assert _prefill(n=0, max_seqlen=0, window=0) == E_SHAPE
+    assert _decode(b=0, t=0) == E_SHAPE
+    assert _decode(b=0, d=32) == E_UNSUP
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
 

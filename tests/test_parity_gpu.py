@@ -249,6 +249,62 @@ def test_decode_never_reads_oldest_slot():
 
 
 # ---------------------------------------------------------------------------
+# degenerate inputs
+# ---------------------------------------------------------------------------
+
+ZERO_LEN_CASES = [
+    (32, 4, 128, "bf16", 128),  # window kernel
+    (32, 4, 128, "bf16", 200),  # online kernel with window and sink
+    (8, 2, 128, "bf16", 128),   # generic kernel
+]
+
+
+@pytest.mark.parametrize("case", ZERO_LEN_CASES, ids=lambda c: f"{c[0]}/{c[1]}-D{c[2]}-{c[3]}-W{c[4]}")
+def test_prefill_zero_length_sequences(case):
+    hq, hkv, d, dt, w = case
+    lens = [0, 37, 0, 0, 150, 1, 0, 16, 0]
+    _say(f"prefill with empty sequences {lens} {hq}/{hkv} W{w}")
+    x = wl.make_prefill(lens, hq, hkv, d, dt, seed=900 + w + hq)
+    o, lse = _run_prefill(x, w)
+    o_ref, l_ref = _oracle_prefill(x, w)
+    assert_close(x["q"].dtype, o, o_ref, lse, l_ref, f"zero-length sequences W{w}")
+    o, lse = _run_prefill(x, None, ga=True)
+    o_ref, l_ref = _oracle_prefill(x, None, ga=True)
+    assert_close(x["q"].dtype, o, o_ref, lse, l_ref, "zero-length sequences GA")
+
+
+def test_empty_stream_and_batch():
+    _say("empty prefill stream and empty decode batch")
+    x = wl.make_prefill([0, 0], 32, 4, 128, "bf16", seed=1)
+    for ga in (False, True):
+        o, lse = _run_prefill(x, None if ga else 128, ga=ga)
+        assert tuple(o.shape) == (0, 32, 128) and tuple(lse.shape) == (0, 32)
+    xd = wl.make_decode(0, 2, 32, 4, 128, 128, "bf16", seed=1)
+    o, lse = _run_decode(xd, 128)
+    assert tuple(o.shape) == (0, 2, 32, 128) and tuple(lse.shape) == (0, 2, 32)
+
+
+@pytest.mark.parametrize("case", [(32, 4, 128), (32, 4, 300), (8, 2, 128)],
+                         ids=["window", "online", "generic"])
+def test_prefill_minus_inf_sinks(case):
+    hq, hkv, w = case
+    _say(f"prefill with sinks = -inf on a third of the heads ({hq}/{hkv}, W{w})")
+    x = wl.make_prefill([333, 64], hq, hkv, 128, "bf16", seed=70 + w)
+    x["sinks"][::3] = float("-inf")  # a sink of -inf contributes exp(-inf) = 0: plain SWA
+    o, lse = _run_prefill(x, w)
+    o_ref, l_ref = _oracle_prefill(x, w)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, f"-inf sinks W{w}")
+
+
+def test_decode_longest_draft_run():
+    _say("decode T = W - 1 = 127 (generic path)")
+    x = wl.make_decode(2, 127, 8, 1, 128, 128, "bf16", seed=127)
+    o, lse = _run_decode(x, 128)
+    o_ref, l_ref = _oracle_decode(x, 128)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, "decode T=127")
+
+
+# ---------------------------------------------------------------------------
 # full-size workloads (launch configuration of the benchmark)
 # ---------------------------------------------------------------------------
 
@@ -313,3 +369,94 @@ def test_varlen_262k_sampled():
     rows = _sample_rows(x, 512, seed=5)
     _check_rows(x, o, lse, rows, 128, "varlen_262k")
     assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+
+
+# ---------------------------------------------------------------------------
+# maximum sizes: byte offsets of q / out beyond 2^32, caches beyond 2^31 elements
+# ---------------------------------------------------------------------------
+
+def _oracle_rows_from_device(x, rows, window):
+    """Oracle values at (token, head) pairs of a device-resident stream too large
+    for the host.  Each pair becomes the one-sequence problem made of its visible
+    keys (its window inside its own sequence, or the whole prefix for window=None),
+    to which the definition gives the same value."""
+    import bisect
+
+    cu = x["cu_seqlens"].tolist()
+    hq, d = x["q"].shape[1], x["q"].shape[2]
+    sinks = None if window is None else x["sinks"]
+    o_ref, l_ref = [], []
+    for t, h in rows:
+        t, h = int(t), int(h)
+        s = bisect.bisect_right(cu, t) - 1
+        k0 = cu[s] if window is None else max(cu[s], t - window + 1)
+        qs = torch.zeros((t - k0 + 1, hq, d), dtype=torch.bfloat16)
+        qs[-1] = x["q"][t].cpu()
+        ks, vs = x["k"][k0:t + 1].cpu(), x["v"][k0:t + 1].cpu()
+        oo, ll = orc.prefill_sample_rows(qs, ks, vs, sinks, np.array([0, t - k0 + 1]),
+                                         np.array([[t - k0, h]]), window=window)
+        o_ref.append(oo[0])
+        l_ref.append(ll[0])
+    return np.array(o_ref), np.array(l_ref)
+
+
+def _device_rows(o, lse, rows):
+    idx_t = torch.tensor(rows[:, 0], device=o.device)
+    idx_h = torch.tensor(rows[:, 1], device=o.device)
+    return to_np(o[idx_t, idx_h]), to_np(lse[idx_t, idx_h])
+
+
+def test_swa_prefill_max_size_sampled():
+    n1, n = 1_300_001, (1 << 21) + 37
+    _say(f"SWA prefill {n} tokens in 2 sequences, 32/4 D128 W128: q/out byte offsets past 2^33")
+    x = wl.make_prefill_device([n1, n - n1], 32, 4, 128, seed=6000, device=DEV)
+    o, lse = swa.swa_sink_prefill(x["q"], x["k"], x["v"], x["sinks"].to(DEV), x["cu_seqlens"].to(DEV),
+                                  x["max_seqlen"], window=128)
+    torch.cuda.synchronize()
+    per_tok = 32 * 128  # q elements per token: token 2^19 starts past 2^31 elements (2^32 bytes)
+    special = [0, 1, 15, 16, 127, 128, (1 << 31) // per_tok - 1, (1 << 31) // per_tok,
+               (1 << 32) // per_tok - 1, (1 << 32) // per_tok, n1 - 1, n1, n1 + 1, n1 + 127, n1 + 128,
+               n - 17, n - 1]
+    rng = np.random.default_rng(6000)
+    toks = special + [int(t) for t in rng.integers(0, n, 40)]
+    rows = np.array([(t, int(h)) for t in toks for h in rng.choice(32, 2, replace=False)])
+    og, lg = _device_rows(o, lse, rows)
+    o_ref, l_ref = _oracle_rows_from_device(x, rows, 128)
+    assert_close(torch.bfloat16, og, o_ref, lg, l_ref, "SWA max size")
+    del x, o, lse
+    torch.cuda.empty_cache()
+
+
+def test_ga_prefill_many_sequences_sampled():
+    lens = [4096] * 512
+    _say("GA prefill 512 x 4096 tokens, 32/4 D128: q/out byte offsets past 2^33")
+    x = wl.make_prefill_device(lens, 32, 4, 128, seed=6100, device=DEV)
+    o, lse = swa.ga_causal_prefill(x["q"], x["k"], x["v"], x["cu_seqlens"].to(DEV), x["max_seqlen"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6100)
+    toks = [0, 4095, 4096, 4097, (1 << 19) - 1, 1 << 19, (1 << 20) + 4095, (1 << 21) - 1]
+    toks += [int(t) for t in rng.integers(0, 1 << 21, 24)]
+    rows = np.array([(t, int(h)) for t in toks for h in rng.choice(32, 2, replace=False)])
+    og, lg = _device_rows(o, lse, rows)
+    o_ref, l_ref = _oracle_rows_from_device(x, rows, None)
+    assert_close(torch.bfloat16, og, o_ref, lg, l_ref, "GA many sequences")
+    del x, o, lse
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("t_new", [1, 3])
+def test_decode_max_batch_sampled(t_new):
+    b = 32771  # caches hold 4 x 128 x 128 elements per sequence: past 2^31 at sequence 32768
+    _say(f"decode B={b} T={t_new} 32/4 D128 W128: caches past 2^31 elements")
+    x = wl.make_decode_device(b, t_new, 32, 4, 128, 128, seed=6200 + t_new, device=DEV)
+    o, lse = swa.swa_sink_decode(x["q"], x["k_new"], x["v_new"], x["k_cache"], x["v_cache"],
+                                 x["ring_head"].to(DEV), x["sinks"].to(DEV))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6200)
+    picks = sorted(set([0, 1, 16383, 32766, 32767, 32768, 32769, b - 1] + [int(v) for v in rng.integers(0, b, 8)]))
+    for bi in picks:
+        sl = {k: (v[bi:bi + 1].cpu() if k not in ("sinks",) else v) for k, v in x.items()}
+        o_ref, l_ref = _oracle_decode(sl, 128)
+        assert_close(torch.bfloat16, o[bi:bi + 1], o_ref, lse[bi:bi + 1], l_ref, f"decode max batch b={bi}")
+    del x, o, lse
+    torch.cuda.empty_cache()
