@@ -6,9 +6,10 @@
 // A workgroup of 8 wavefronts owns 32 consecutive query tokens and the 8 query
 // heads of one KV head; wavefront w takes query sub-tile w >> 2 and heads
 // 2(w & 3), 2(w & 3) + 1, i.e. two 16-query MFMA tiles sharing every K read.  Keys
-// are streamed in 64-key chunks through two LDS buffers: the next chunk is loaded
-// into registers while the current one is multiplied, written to the other
-// buffer, and one barrier per chunk hands it over.  The running maximum is raised
+// are staged 128 at a time through two LDS buffers: the next stage is loaded into
+// registers while the current one is multiplied (as two 64-key steps), written to
+// the other buffer, and one barrier per stage hands it over (one per 64 keys cost
+// 3% more).  The running maximum is raised
 // lazily: O and the running sum are rescaled only when some row's maximum grows
 // by more than kSlack (log2 units); otherwise the exponent keeps the older, smaller
 // reference and the weights may exceed 1 by at most 2^kSlack, which fp32 sums and
@@ -25,10 +26,11 @@ using namespace tile;
 constexpr int kQT = 32;                  // query tokens per workgroup
 constexpr int kHG = 8;                   // query heads per workgroup
 constexpr int kThreads = 512;            // 8 wavefronts
-constexpr int kChunk = 64;               // keys per step
-constexpr int kKPlane = kChunk * 64;     // bytes of one 32-element chunk plane of K
-constexpr int kKBuf = 4 * kKPlane;       // 16384
-constexpr int kVBuf = kChunk * kVPitch;  // 16896
+constexpr int kChunk = 64;               // keys per compute step
+constexpr int kStage = 128;              // keys staged in LDS per barrier (two steps)
+constexpr int kKPlane = kStage * 64;     // bytes of one 32-element chunk plane of K
+constexpr int kKBuf = 4 * kKPlane;       // 32768
+constexpr int kVBuf = kStage * kVPitch;  // 33792
 constexpr int kBuf = kKBuf + kVBuf;
 constexpr float kSlack = 8.f;
 
@@ -65,7 +67,7 @@ void ga_chunk_kernel(PrefillArgs a) {
   const long lw0 = (long)q0 - a.window + 1;
   const int lo_wg = __builtin_amdgcn_readfirstlane(lw0 > s0q ? (int)lw0 : s0q);
   const int kend = q0 + kQT;
-  const int nchunks = (kend - lo_wg + kChunk - 1) / kChunk;
+  const int nstages = (kend - lo_wg + kStage - 1) / kStage;
 
   // ---- Q of the two tiles: lane (i, g) holds head-dim 32cc + 8g .. +8 of query qi ----
   bf16x8 qa[4], qb[4];
@@ -79,57 +81,56 @@ void ga_chunk_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- chunk staging: thread t moves the 16-byte unit su = t & 15 of key rows
-  // srow = t >> 4 and srow + 32, of K (pf[0], pf[1]) and of V (pf[2], pf[3]) ----
+  // ---- stage staging: thread t moves the 16-byte unit su = t & 15 of key rows
+  // srow + 32 j (j < 4), srow = t >> 4, of K (pf[j]) and of V (pf[4 + j]) ----
   const int srow = t >> 4, su = t & 15;
   const size_t key_stride = (size_t)hkv * D;  // elements from one key's row to the next
   const uint32_t goff0 = (uint32_t)((((size_t)srow * hkv + kvh) * D + su * 8) * sizeof(bf16));
-  const uint32_t goff1 = goff0 + (uint32_t)(32 * key_stride * sizeof(bf16));
-  u32x4 pf[4];
-  bool edge = false;             // (uniform) the staged chunk reaches outside [0, N)
-  bool ok_lo = true, ok_hi = true;  // rows srow / srow + 32 of the staged chunk exist
+  const size_t gstep = 32 * key_stride;  // elements from row r to row r + 32
+  u32x4 pf[8];
+  bool edge = false;  // (uniform) the staged keys reach outside [0, N)
+  bool ok[4] = {true, true, true, true};  // row srow + 32 j of the stage exists
   auto prefetch = [&](int kb) {
-    edge = !(kb >= 0 && kb + kChunk <= N);
+    edge = !(kb >= 0 && kb + kStage <= N);
     if (!edge) {
-      // whole chunk inside the token stream: a uniform base and lane-constant offsets
-      const char* kbase = reinterpret_cast<const char*>(kp + (size_t)kb * key_stride);
-      const char* vbase = reinterpret_cast<const char*>(vp + (size_t)kb * key_stride);
-      pf[0] = *reinterpret_cast<const u32x4*>(kbase + goff0);
-      pf[1] = *reinterpret_cast<const u32x4*>(kbase + goff1);
-      pf[2] = *reinterpret_cast<const u32x4*>(vbase + goff0);
-      pf[3] = *reinterpret_cast<const u32x4*>(vbase + goff1);
+      // whole stage inside the token stream: a uniform base and lane-constant offsets
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const char* kbase = reinterpret_cast<const char*>(kp + (size_t)kb * key_stride + j * gstep);
+        const char* vbase = reinterpret_cast<const char*>(vp + (size_t)kb * key_stride + j * gstep);
+        pf[j] = *reinterpret_cast<const u32x4*>(kbase + goff0);
+        pf[4 + j] = *reinterpret_cast<const u32x4*>(vbase + goff0);
+      }
     } else {
       // rows outside the stream load a clamped row (no masked loads, which would
       // force early waits) and are zeroed when committed
-      const int r0 = kb + srow, r1 = r0 + 32;
-      ok_lo = r0 >= 0 && r0 < N;
-      ok_hi = r1 >= 0 && r1 < N;
-      const size_t e0 = ((size_t)min(max(r0, 0), N - 1) * hkv + kvh) * D + su * 8;
-      const size_t e1 = ((size_t)min(max(r1, 0), N - 1) * hkv + kvh) * D + su * 8;
-      pf[0] = *reinterpret_cast<const u32x4*>(kp + e0);
-      pf[1] = *reinterpret_cast<const u32x4*>(kp + e1);
-      pf[2] = *reinterpret_cast<const u32x4*>(vp + e0);
-      pf[3] = *reinterpret_cast<const u32x4*>(vp + e1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = kb + srow + 32 * j;
+        ok[j] = r >= 0 && r < N;
+        const size_t e = ((size_t)min(max(r, 0), N - 1) * hkv + kvh) * D + su * 8;
+        pf[j] = *reinterpret_cast<const u32x4*>(kp + e);
+        pf[4 + j] = *reinterpret_cast<const u32x4*>(vp + e);
+      }
     }
   };
-  // LDS byte offsets of the thread's units (put_k / put_v layouts).  Chunk bases are
-  // multiples of 32, so a key's swizzle equals that of its row in the chunk, and
-  // rows srow and srow + 32 share it.
+  // LDS byte offsets of the thread's units (put_k / put_v layouts).  Stage bases are
+  // multiples of 32, so a key's swizzle equals that of its row in the stage, and
+  // rows srow + 32 j share it.
   const int ks_off = (su >> 2) * kKPlane + srow * 64 + 16 * ((su & 3) ^ kswz(srow));
   const int vs_off = kKBuf + srow * kVPitch + 16 * su;
   auto commit = [&](char* buf) {
     if (edge) {
-      const u32x4 z = {0, 0, 0, 0};
-      if (!ok_lo) { pf[0] = z; pf[2] = z; }
-      if (!ok_hi) { pf[1] = z; pf[3] = z; }
-    }
-    *reinterpret_cast<u32x4*>(buf + ks_off) = pf[0];
-    *reinterpret_cast<u32x4*>(buf + ks_off + 32 * 64) = pf[1];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      char* v = buf + vs_off + 32 * kVPitch * h;
-      *reinterpret_cast<u32x2*>(v) = (u32x2){pf[2 + h][0], pf[2 + h][1]};
-      *reinterpret_cast<u32x2*>(v + 8) = (u32x2){pf[2 + h][2], pf[2 + h][3]};
+      for (int j = 0; j < 4; ++j)
+        if (!ok[j]) { pf[j] = (u32x4){0, 0, 0, 0}; pf[4 + j] = (u32x4){0, 0, 0, 0}; }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<u32x4*>(buf + ks_off + 32 * 64 * j) = pf[j];
+      char* v = buf + vs_off + 32 * kVPitch * j;
+      *reinterpret_cast<u32x2*>(v) = (u32x2){pf[4 + j][0], pf[4 + j][1]};
+      *reinterpret_cast<u32x2*>(v + 8) = (u32x2){pf[4 + j][2], pf[4 + j][3]};
     }
   };
 
@@ -149,14 +150,21 @@ void ga_chunk_kernel(PrefillArgs a) {
 #pragma unroll
   for (int b = 0; b < 8; ++b) { o0[b] = zero4; o1[b] = zero4; }
 
-  prefetch(kend - nchunks * kChunk);
+  prefetch(kend - nstages * kStage);
   commit(smem);
   __syncthreads();
 
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int kb = kend - (nchunks - ch) * kChunk;  // first key of this chunk
-    const char* buf = smem + (ch & 1) * kBuf;
-    if (ch + 1 < nchunks) prefetch(kb + kChunk);
+  for (int st = 0; st < nstages; ++st) {
+    const int kst = kend - (nstages - st) * kStage;  // first key of this stage
+    const char* sbuf = smem + (st & 1) * kBuf;
+    if (st + 1 < nstages) prefetch(kst + kStage);
+#pragma unroll
+  for (int sub = 0; sub < kStage / kChunk; ++sub) {
+    const int kb = kst + sub * kChunk;  // first key of this step
+    // the step's K rows start 64 bytes x kChunk x sub into each plane, its V rows
+    // kChunk x sub rows in
+    const char* buf = sbuf + sub * kChunk * 64;
+    const char* vbuf = sbuf + sub * kChunk * kVPitch;
 
     // chunk entirely outside this wavefront's rows (before every window / after
     // every query): nothing to do
@@ -250,8 +258,8 @@ void ga_chunk_kernel(PrefillArgs a) {
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
           const int off = vo + 32 * kVPitch * p + vblock_bytes(b);
-          const bf16x4 lo4 = tr_read(buf, off);
-          const bf16x4 hi4 = tr_read(buf, off + 4 * kVPitch);
+          const bf16x4 lo4 = tr_read(vbuf, off);
+          const bf16x4 hi4 = tr_read(vbuf, off + 4 * kVPitch);
           const bf16x8 av = (bf16x8){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
           o0[b] = mfma32(av, pa[p], o0[b]);
           o1[b] = mfma32(av, pb[p], o1[b]);
@@ -260,7 +268,8 @@ void ga_chunk_kernel(PrefillArgs a) {
     }
 
     __builtin_amdgcn_s_setprio(0);
-    if (ch + 1 < nchunks) commit(smem + ((ch + 1) & 1) * kBuf);
+  }
+    if (st + 1 < nstages) commit(smem + ((st + 1) & 1) * kBuf);
     __syncthreads();  // the next buffer is written; this one is no longer read
   }
 
