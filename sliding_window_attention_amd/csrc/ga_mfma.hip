@@ -144,8 +144,9 @@ void ga_chunk_kernel(PrefillArgs a) {
 
   const float sink0 = a.sinks ? a.sinks[h0] * kLog2e : -INFINITY;
   const float sink1 = a.sinks ? a.sinks[h0 + 1] * kLog2e : -INFINITY;
-  float m0 = sink0, m1 = sink1;  // reference maxima (log2 units)
-  float l0 = a.sinks ? 1.f : 0.f, l1 = l0;
+  float m0 = sink0, m1 = sink1;  // reference maxima (log2 units), equal on a row's 4 lanes
+  // this lane's share of the running sums (the 4 lanes of a row are added at the end)
+  float l0 = (a.sinks && g == 0) ? 1.f : 0.f, l1 = l0;
   f32x4 o0[8], o1[8];
 #pragma unroll
   for (int b = 0; b < 8; ++b) { o0[b] = zero4; o1[b] = zero4; }
@@ -209,11 +210,11 @@ void ga_chunk_kernel(PrefillArgs a) {
         mx0 = fmaxf(mx0, fmaxf(fmaxf(s0[bl][0], s0[bl][1]), fmaxf(s0[bl][2], s0[bl][3])));
         mx1 = fmaxf(mx1, fmaxf(fmaxf(s1[bl][0], s1[bl][1]), fmaxf(s1[bl][2], s1[bl][3])));
       }
-      mx0 = quad_max(mx0) * c;
-      mx1 = quad_max(mx1) * c;
+      mx0 *= c;  // this lane's maxima: a row's maximum exceeds a bound iff one of
+      mx1 *= c;  // its 4 lanes does, so the row maximum is needed only to rescale
       // ---- lazy rescale: only when some row's maximum outgrows its reference ----
       if (__builtin_amdgcn_ballot_w64(mx0 > m0 + kSlack) != 0) {
-        const float mn = fmaxf(m0, mx0);
+        const float mn = fmaxf(m0, quad_max(mx0));
         const float al = (m0 == -INFINITY) ? 0.f : fast_exp2(m0 - mn);
         l0 *= al;
 #pragma unroll
@@ -221,7 +222,7 @@ void ga_chunk_kernel(PrefillArgs a) {
         m0 = mn;
       }
       if (__builtin_amdgcn_ballot_w64(mx1 > m1 + kSlack) != 0) {
-        const float mn = fmaxf(m1, mx1);
+        const float mn = fmaxf(m1, quad_max(mx1));
         const float al = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - mn);
         l1 *= al;
 #pragma unroll
@@ -249,8 +250,8 @@ void ga_chunk_kernel(PrefillArgs a) {
           pb[bl >> 1] = pack_pair(s1[bl - 1], s1[bl]);
         }
       }
-      l0 += quad_sum(ps0);
-      l1 += quad_sum(ps1);
+      l0 += ps0;
+      l1 += ps1;
       // ---- O^T += V^T P^T ----
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -274,6 +275,8 @@ void ga_chunk_kernel(PrefillArgs a) {
   }
 
   // ---- epilogue ----
+  l0 = quad_sum(l0);
+  l1 = quad_sum(l1);
   if (qi < N) {
     bf16* out = static_cast<bf16*>(a.out) + ((size_t)qi * Hq + h0) * D;
     store_row_tr(out, g, o0, __builtin_amdgcn_rcpf(l0));
