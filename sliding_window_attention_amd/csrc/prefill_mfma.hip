@@ -141,15 +141,19 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
 
     const int run_len = __builtin_amdgcn_readfirstlane(run_end - item);
     const int tile0 = tile;
+    // ring slot of the tile's oldest block: (kbase / 16) mod 9 with kbase = 16 tile
+    // - 128, i.e. (tile + 1) mod 9; it advances by one slot per tile
+    int kblock0 = __builtin_amdgcn_readfirstlane((tile0 + 1) % kSlots);
     for (int k = 0; k < run_len; ++k) {
       tile = tile0 + k;
       const int q0 = tile * kQT;
       const int kbase = q0 - 128;  // ring block j holds keys kbase + 16j ..
-      const int kblock0 = mod9(kbase >> 4);
-      const int par = (kbase >> 4) & 1;
-      int sk[kSlots];  // byte offset of ring block j in a K plane
+      const int par = tile & 1;    // (kbase / 16) & 1
+      // slot of ring block j, and its byte offsets in a K plane and in V
+      auto slot = [&](int j) { return kblock0 + j - (kblock0 + j >= kSlots ? kSlots : 0); };
+      int sk[kSlots];
 #pragma unroll
-      for (int j = 0; j < kSlots; ++j) sk[j] = 16 * mod9(kblock0 + j) * 64;
+      for (int j = 0; j < kSlots; ++j) sk[j] = 16 * 64 * slot(j);
       const int h0 = oct * kHG + 2 * w;
 
       // ---- first visible key of each row: window and own-sequence start ----
@@ -162,8 +166,10 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
       const int lo = lw > start ? (int)lw : start;
       const int rel_lo = lo - kbase;
       const int rel_hi = qi - kbase;
-      // rows are ordered, so lanes 0 and 15 bound the tile (wave-uniform values)
-      const int lo_min = __builtin_amdgcn_readfirstlane(rel_lo);
+      // rows are ordered, so lane 15 bounds the tile's window starts (wave-uniform);
+      // blocks and pairs before every row's window are not skipped: the mask gives
+      // their keys weight 0, and skipping would put a branch between the blocks'
+      // operand reads
       const int lo_max = __builtin_amdgcn_readlane(rel_lo, 15);
       const unsigned span = (unsigned)(rel_hi - rel_lo);  // key kr is visible iff kr - rel_lo <= span
       const float sink0 = a.sinks ? sinks[h0] * kLog2e : -INFINITY;
@@ -177,12 +183,6 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
         const int ko8 = p8 * 64 + 16 * (g ^ kswz(16 * par + p8));
 #pragma unroll
         for (int bl = 0; bl < 9; ++bl) {
-          const int kr_max = bl < 8 ? 32 * (bl >> 1) + 4 * (bl & 1) + 27 : 143;
-          if (kr_max < lo_min) {  // whole block before every row's window
-            s0[bl] = zero4;
-            s1[bl] = zero4;
-            continue;
-          }
           int off;
           if (bl < 8) {
             const int p = bl >> 1;
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
       // ---- O^T = V^T P^T: the single diagonal block first (initialises O), then pairs ----
       f32x4 o0[8], o1[8];
       {
-        const int vb8 = 16 * mod9(kblock0 + 8) * kVPitch + vrow8 * kVPitch + vquad;
+        const int vb8 = 16 * slot(8) * kVPitch + vrow8 * kVPitch + vquad;
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
           const bf16x4 av = tr_read(vs, vb8 + 2 * (32 * (b >> 2) + 4 * (b & 3)));
@@ -270,10 +270,9 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
       }
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        if (32 * p + 31 < lo_min) continue;  // pair entirely before every window
         // lane groups 0-1 read the pair's first 16-key block, groups 2-3 its second
-        const int slot_a = 16 * mod9(kblock0 + 2 * p) * kVPitch;
-        const int slot_b = 16 * mod9(kblock0 + 2 * p + 1) * kVPitch;
+        const int slot_a = 16 * slot(2 * p) * kVPitch;
+        const int slot_b = 16 * slot(2 * p + 1) * kVPitch;
         const int vb = (g >= 2 ? slot_b : slot_a) + vrow * kVPitch + vquad;
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
@@ -297,6 +296,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
         put_v(vs, phys, t & 15, pv);
         __syncthreads();
       }
+      kblock0 = kblock0 == kSlots - 1 ? 0 : kblock0 + 1;
 
       // ---- epilogue: O and LSE of this tile ----
       // vmcnt(0) on every path (on the common one the ring update has already
