@@ -287,7 +287,10 @@ def main(argv=None):
     _log("generating swa_prefill_32k inputs")
     x = _with_outputs(_to(wl.make_workload(PRIMARY), dev), "prefill")
     sets = _clone_sets(x, 4)
-    per, region_ms = _time_calls(_prefill_fn(128), sets, steps, warmup)
+    # K back-to-back launches between two HIP events on the launching stream: the
+    # region over K is both the time per step and the kernel's average launch
+    # duration (one launch per step); per-launch event pairs would add gaps
+    per, region_ms = _time_calls(_prefill_fn(128), sets, steps, warmup, per_call=False)
     flops, nbytes = wl.workload_work(PRIMARY)
     st = _stats(per)
     ms_per_step = region_ms / steps
