@@ -21,7 +21,10 @@ the prose of that section and of the MiMo-V2 blog, section 2.2):
   same operator with an unbounded window and no sink (sink = -inf).
   GQA: query head h reads KV head h // (Hq // Hkv).
 
-Arithmetic is fp64 on the exact input values (bf16 and fp32 convert to fp64
+Decode against an FP8 ring (swa_sink_decode_fp8kv) is the same decode on caches
+dequantised exactly (E4M3 code value times a per-tensor scale).
+
+Arithmetic is fp64 on the exact input values (bf16, fp32 and E4M3 convert to fp64
 exactly).  Rows are processed in blocks only to bound memory: every row is the
 definition above, computed independently, with no online rescaling and no
 reordering of its sums beyond numpy's own.
@@ -194,6 +197,36 @@ def swa_sink_decode(q, k_new, v_new, k_cache, v_cache, ring_head, sinks, window=
         o[b] = ob[w:]
         lse[b] = lb[w:]
     return o, lse
+
+
+def e4m3_to_float(codes) -> np.ndarray:
+    """Exact fp64 value of one-byte E4M3 codes (the FP8 (E4M3) format the MiMo-V2
+    blog, section 6, names for MiMo-V2.5-Pro; the bit layout is the OCP 8-bit
+    floating-point one): sign bit 7, exponent bits 6..3 with bias 7, mantissa bits
+    2..0.  Exponent field 0 holds the subnormals m/8 * 2^-6; otherwise the value is
+    (1 + m/8) * 2^(e - 7).  There are no infinities: S.1111.111 is NaN, so the
+    largest finite magnitude is 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where((e == 15) & (m == 7), np.nan, sign * mag)
+
+
+def swa_sink_decode_fp8kv(q, k_new, v_new, k_codes, v_codes, k_scale, v_scale, ring_head, sinks,
+                          window=128, scale=None):
+    """Decode / MTP verify against a ring whose K and V are stored as E4M3 codes.
+
+    The FP8 KV cache of the MiMo-V3 / HySparse2 report (cache sizes quoted "with an
+    FP8 cache") with one fp32 scale per tensor: cache element value = the code's
+    E4M3 value times k_scale (K) or v_scale (V).  The T new tokens keep their own
+    precision.  Everything else is swa_sink_decode on the dequantised caches.
+    """
+    kc = e4m3_to_float(k_codes) * float(k_scale)
+    vc = e4m3_to_float(v_codes) * float(v_scale)
+    return swa_sink_decode(q, k_new, v_new, kc, vc, ring_head, sinks, window=window, scale=scale)
 
 
 def hybrid_block(layers, window=128, scale=None):

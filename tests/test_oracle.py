@@ -312,3 +312,78 @@ def test_pin13_hybrid_flop_ratio_consistent_with_pages():
     assert abs(ratio - 7.99) < 0.01
     kv_ratio = (8 * n) / (1 * n + 7 * 128)
     assert 7.0 <= kv_ratio < 8.0
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) KV cache
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decoder_matches_library_routine():
+    """All 256 codes against torch's float8_e4m3fn (the same format: finite, NaN at S.1111.111)."""
+    codes = np.arange(256, dtype=np.uint8)
+    ours = orc.e4m3_to_float(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.array_equal(ours[~np.isnan(ours)], ref[~np.isnan(ref)])
+    assert np.array_equal(np.signbit(ours[~np.isnan(ours)]), np.signbit(ref[~np.isnan(ref)]))
+
+
+def test_e4m3_hand_values():
+    from tests.golden.load import load, value
+
+    fx = load("e4m3_hand.json")
+    for code, val in fx["values"].items():
+        assert orc.e4m3_to_float(np.array([int(code, 16)]))[0] == value(val), code
+    for code in fx["nan_codes"]:
+        assert np.isnan(orc.e4m3_to_float(np.array([int(code, 16)]))[0])
+    finite = orc.e4m3_to_float(np.arange(0, 0x7F, dtype=np.uint8))
+    assert np.all(np.diff(finite) > 0)  # codes 0x00..0x7E increase strictly
+    assert np.isnan(orc.e4m3_to_float(np.arange(256, dtype=np.uint8))).sum() == 2
+
+
+def test_fp8kv_decode_never_reads_oldest_slot():
+    """The largest codes (+-448) planted in the oldest ring slot of every (sequence, KV head) leave
+    the result bit-identical (the definition multiplies masked keys' zero weights by their values,
+    so NaN itself would propagate through the oracle's matrix product)."""
+    rng = np.random.default_rng(8)
+    b, t, hq, hkv, d, w = 3, 2, 4, 2, 16, 8
+    q = rng.standard_normal((b, t, hq, d))
+    kn = rng.standard_normal((b, t, hkv, d))
+    vn = rng.standard_normal((b, t, hkv, d))
+    kc = rng.integers(0, 0x70, (b, hkv, w, d)).astype(np.uint8) | (rng.integers(0, 2, (b, hkv, w, d)) << 7).astype(np.uint8)
+    vc = rng.integers(0, 0x70, (b, hkv, w, d)).astype(np.uint8)
+    heads = np.array([0, 5, 7])
+    sinks = rng.standard_normal(hq)
+    o1, l1 = orc.swa_sink_decode_fp8kv(q, kn, vn, kc, vc, 0.25, 0.5, heads, sinks, window=w)
+    kc2, vc2 = kc.copy(), vc.copy()
+    for bi in range(b):
+        kc2[bi, :, heads[bi]] = 0x7E
+        vc2[bi, :, heads[bi]] = 0xFE
+    o2, l2 = orc.swa_sink_decode_fp8kv(q, kn, vn, kc2, vc2, 0.25, 0.5, heads, sinks, window=w)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_fp8kv_scales_act_on_the_ring_only():
+    """Doubling v_scale equals raising every V code's exponent by one (ring values doubled exactly),
+    and k_scale multiplies ring logits: with k_scale = 2 and codes whose exponent is lowered by
+    one the result is unchanged."""
+    rng = np.random.default_rng(9)
+    b, t, hq, hkv, d, w = 2, 3, 4, 1, 8, 6
+    q = rng.standard_normal((b, t, hq, d))
+    kn = rng.standard_normal((b, t, hkv, d))
+    vn = rng.standard_normal((b, t, hkv, d))
+    exp_field = rng.integers(2, 12, (b, hkv, w, d))
+    mant = rng.integers(0, 8, (b, hkv, w, d))
+    sign = rng.integers(0, 2, (b, hkv, w, d))
+    codes = ((sign << 7) | (exp_field << 3) | mant).astype(np.uint8)
+    lower = ((sign << 7) | ((exp_field - 1) << 3) | mant).astype(np.uint8)
+    higher = ((sign << 7) | ((exp_field + 1) << 3) | mant).astype(np.uint8)
+    heads = np.array([1, 4])
+    sinks = rng.standard_normal(hq)
+    base = orc.swa_sink_decode_fp8kv(q, kn, vn, codes, codes, 1.0, 1.0, heads, sinks, window=w)
+    v2 = orc.swa_sink_decode_fp8kv(q, kn, vn, codes, codes, 1.0, 2.0, heads, sinks, window=w)
+    vh = orc.swa_sink_decode_fp8kv(q, kn, vn, codes, higher, 1.0, 1.0, heads, sinks, window=w)
+    k2 = orc.swa_sink_decode_fp8kv(q, kn, vn, lower, codes, 2.0, 1.0, heads, sinks, window=w)
+    np.testing.assert_allclose(v2[0], vh[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(k2[0], base[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(k2[1], base[1], rtol=0, atol=1e-12)
