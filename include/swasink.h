@@ -57,7 +57,7 @@ typedef enum {
 
 typedef enum { SWA_DTYPE_F32 = 0, SWA_DTYPE_BF16 = 1 } swa_dtype;
 
-#define SWASINK_ABI_VERSION 1
+#define SWASINK_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SWASINK_API __attribute__((visibility("default")))
@@ -126,6 +126,25 @@ SWASINK_API int swa_sink_decode(const void* q, const void* k_new, const void* v_
                     int32_t batch, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
                     int32_t head_dim, int32_t window, float scale, swa_dtype dtype, void* out,
                     float* lse, void* stream);
+
+/*
+ * swa_sink_decode against an FP8 ring: the caches hold one-byte E4M3 codes (the
+ * FP8 (E4M3) format of the MiMo-V2 blog, section 6, used for the KV cache as in the
+ * MiMo-V3 / HySparse2 report's FP8-cache sizes; bit layout: sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits, subnormals, no infinities, S.1111.111 = NaN).  The
+ * value of a cache element is its code's value times k_scale (K) or v_scale (V),
+ * one fp32 scale per tensor.  Every other argument, the masking and the outputs
+ * are those of swa_sink_decode; the T new tokens keep `dtype`.
+ *
+ *  k_cache, v_cache [batch, num_kv_heads, window, head_dim] uint8 E4M3 codes, read only
+ *  k_scale, v_scale host fp32, finite and > 0 (SWA_ERR_SHAPE otherwise)
+ * The ring bytes halve against a bf16 ring; decode is bound by them.
+ */
+SWASINK_API int swa_sink_decode_fp8kv(const void* q, const void* k_new, const void* v_new,
+                    const uint8_t* k_cache, const uint8_t* v_cache, float k_scale, float v_scale,
+                    const int32_t* ring_head, const float* sinks, int32_t batch, int32_t T,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                    float scale, swa_dtype dtype, void* out, float* lse, void* stream);
 
 /* Message for the last non-OK return on the calling thread ("" if none). */
 SWASINK_API const char* swa_last_error(void);

@@ -36,6 +36,8 @@ _SIGNATURES = {
     "swa_sink_prefill": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P],
     "ga_causal_prefill": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P],
     "swa_sink_decode": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P],
+    "swa_sink_decode_fp8kv": [_P, _P, _P, _P, _P, _F, _F, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
+                              _P, _P, _P],
 }
 
 
@@ -207,5 +209,39 @@ def swa_sink_decode(q, k_new, v_new, k_cache, v_cache, ring_head, sinks, scale=N
         q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         ring_head.data_ptr(), sinks.data_ptr(), b, t, hq, hkv, d, w, _scale(scale), _dtype_code(q),
         out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def swa_sink_decode_fp8kv(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, ring_head, sinks,
+                          scale=None, return_lse=True, out=None, lse=None):
+    """swa_sink_decode against an FP8 ring: k_cache/v_cache [B, Hkv, W, D] uint8 E4M3
+    codes, element value = code value * k_scale (K) or v_scale (V) (python floats)."""
+    import torch
+
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+        _dev(t, nm, q.dtype)
+    _dev(k_cache, "k_cache", torch.uint8)
+    _dev(v_cache, "v_cache", torch.uint8)
+    _dev(ring_head, "ring_head", torch.int32)
+    _dev(sinks, "sinks", torch.float32)
+    if q.dim() != 4 or k_new.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q, k_new must be [B, T, H, D] and caches [B, Hkv, W, D]")
+    b, t, hq, d = q.shape
+    hkv, w = k_cache.shape[1], k_cache.shape[2]
+    if (k_new.shape != (b, t, hkv, d) or v_new.shape != k_new.shape or v_cache.shape != k_cache.shape
+            or k_cache.shape[0] != b or k_cache.shape[3] != d or ring_head.numel() != b
+            or sinks.numel() != hq):
+        raise ValueError("inconsistent shapes")
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    if return_lse and lse is None:
+        lse = torch.empty((b, t, hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+    rc = library().swa_sink_decode_fp8kv(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        float(k_scale), float(v_scale), ring_head.data_ptr(), sinks.data_ptr(), b, t, hq, hkv, d, w,
+        _scale(scale), _dtype_code(q), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        _stream(q.device))
     _check(rc)
     return out, lse

@@ -115,6 +115,48 @@ int prefill_common(const void* q, const void* k, const void* v, const float* sin
   return hip_status(e, name);
 }
 
+int decode_common(const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                  const void* v_cache, bool fp8, float k_scale, float v_scale,
+                  const int32_t* ring_head, const float* sinks, int32_t batch, int32_t T,
+                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                  float scale, int dtype, void* out, float* lse, void* stream, const char* name) {
+  int rc = check_dtype(dtype);
+  if (rc) return rc;
+  if (batch < 0) return fail(SWA_ERR_SHAPE, "%s: batch must be >= 0", name);
+  if ((rc = check_heads(num_q_heads, num_kv_heads, head_dim))) return rc;
+  if (window < 2) return fail(SWA_ERR_SHAPE, "%s: window must be >= 2 (got %d)", name, window);
+  if (T < 1 || T >= window)
+    return fail(SWA_ERR_SHAPE, "%s: T must satisfy 1 <= T < window (got T=%d, window=%d)", name, T,
+                window);
+  if (fp8 && !(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f))
+    return fail(SWA_ERR_SHAPE, "%s: k_scale and v_scale must be finite and > 0", name);
+  if ((long long)batch * num_kv_heads * window * head_dim > (1LL << 40))
+    return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
+  if (batch == 0) return ok();  // nothing is read or written: pointers may be NULL
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !ring_head || !sinks || !out)
+    return fail(SWA_ERR_NULL,
+                "%s: q, k_new, v_new, k_cache, v_cache, ring_head, sinks and out must be non-NULL",
+                name);
+
+  swa::DecodeArgs a;
+  a.q = q; a.k_new = k_new; a.v_new = v_new;
+  a.k_cache = k_cache; a.v_cache = v_cache;
+  a.ring_head = ring_head; a.sinks = sinks;
+  a.out = out; a.lse = lse;
+  a.batch = batch; a.t_new = T;
+  a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
+  a.window = window;
+  a.scale = resolve_scale(scale, head_dim);
+  a.cache_fp8 = fp8;
+  a.k_scale = fp8 ? k_scale : 1.f;
+  a.v_scale = fp8 ? v_scale : 1.f;
+  const bool bf = dtype == SWA_DTYPE_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = swa::decode_mfma_supported(a, bf) ? swa::launch_decode_mfma(a, s)
+                                                   : swa::launch_generic_decode(a, bf, s);
+  return hip_status(e, name);
+}
+
 }  // namespace
 
 extern "C" {
@@ -143,37 +185,20 @@ int swa_sink_decode(const void* q, const void* k_new, const void* v_new, const v
                     int32_t batch, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
                     int32_t head_dim, int32_t window, float scale, swa_dtype dtype, void* out,
                     float* lse, void* stream) {
-  const char* name = "swa_sink_decode";
-  int rc = check_dtype((int)dtype);
-  if (rc) return rc;
-  if (batch < 0) return fail(SWA_ERR_SHAPE, "%s: batch must be >= 0", name);
-  if ((rc = check_heads(num_q_heads, num_kv_heads, head_dim))) return rc;
-  if (window < 2) return fail(SWA_ERR_SHAPE, "%s: window must be >= 2 (got %d)", name, window);
-  if (T < 1 || T >= window)
-    return fail(SWA_ERR_SHAPE, "%s: T must satisfy 1 <= T < window (got T=%d, window=%d)", name, T,
-                window);
-  if ((long long)batch * num_kv_heads * window * head_dim > (1LL << 40))
-    return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
-  if (batch == 0) return ok();  // nothing is read or written: pointers may be NULL
-  if (!q || !k_new || !v_new || !k_cache || !v_cache || !ring_head || !sinks || !out)
-    return fail(SWA_ERR_NULL,
-                "%s: q, k_new, v_new, k_cache, v_cache, ring_head, sinks and out must be non-NULL",
-                name);
+  return decode_common(q, k_new, v_new, k_cache, v_cache, false, 1.f, 1.f, ring_head, sinks, batch,
+                       T, num_q_heads, num_kv_heads, head_dim, window, scale, (int)dtype, out, lse,
+                       stream, "swa_sink_decode");
+}
 
-  swa::DecodeArgs a;
-  a.q = q; a.k_new = k_new; a.v_new = v_new;
-  a.k_cache = k_cache; a.v_cache = v_cache;
-  a.ring_head = ring_head; a.sinks = sinks;
-  a.out = out; a.lse = lse;
-  a.batch = batch; a.t_new = T;
-  a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
-  a.window = window;
-  a.scale = resolve_scale(scale, head_dim);
-  const bool bf = dtype == SWA_DTYPE_BF16;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = swa::decode_mfma_supported(a, bf) ? swa::launch_decode_mfma(a, s)
-                                                   : swa::launch_generic_decode(a, bf, s);
-  return hip_status(e, name);
+int swa_sink_decode_fp8kv(const void* q, const void* k_new, const void* v_new,
+                          const uint8_t* k_cache, const uint8_t* v_cache, float k_scale,
+                          float v_scale, const int32_t* ring_head, const float* sinks,
+                          int32_t batch, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t window, float scale, swa_dtype dtype,
+                          void* out, float* lse, void* stream) {
+  return decode_common(q, k_new, v_new, k_cache, v_cache, true, k_scale, v_scale, ring_head, sinks,
+                       batch, T, num_q_heads, num_kv_heads, head_dim, window, scale, (int)dtype,
+                       out, lse, stream, "swa_sink_decode_fp8kv");
 }
 
 const char* swa_last_error(void) { return g_last_error; }

@@ -65,6 +65,9 @@ struct DecodeArgs {
   int32_t head_dim;
   int32_t window;
   float scale;
+  bool cache_fp8 = false;  // k_cache / v_cache hold one-byte E4M3 codes
+  float k_scale = 1.f;     // with cache_fp8: element value = code value * scale
+  float v_scale = 1.f;
 };
 
 // First token of the sequence that holds packed token `t`: the largest s with
@@ -82,6 +85,22 @@ __device__ __forceinline__ int seq_start_of(const int32_t* __restrict__ cu, int 
 }
 
 __device__ __forceinline__ float bf16_to_f32(bf16 x) { return (float)x; }
+
+// E4M3 (OCP 8-bit float: bias 7, subnormals, no infinities) to wider types with the
+// gfx950 conversion instructions.  Every E4M3 value is exactly a bf16 and an fp32
+// value, so these conversions are exact.
+// Eight codes (bytes 0..7 of w, element k = byte k) as bf16x8.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(u32x2 w) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, true);
+  return (bf16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+// One code as fp32.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+}
 
 // s_waitcnt immediate for vmcnt(0) with the other counters left alone (gfx9
 // encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).

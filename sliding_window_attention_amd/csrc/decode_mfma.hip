@@ -15,6 +15,8 @@
 // operand registers (V rows 16 lanes per 256-byte row, fully coalesced, and
 // transposed in registers); the query columns and the new tokens' K/V, shared by
 // the four wavefronts, are staged once in LDS.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "mfma_tile.h"
@@ -80,7 +82,11 @@ __device__ __forceinline__ void add_partial(const char (*slot)[kColBytes], int i
   }
 }
 
-template <int NT>
+// FP8: the ring holds E4M3 codes (8-byte operand loads, converted to bf16 in
+// registers, exactly); the K scale joins the ring logits' multiplier and the V scale
+// multiplies the ring weights as they are packed for P*V (the running sums stay
+// unscaled), so no cache element is ever rescaled.
+template <int NT, bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) DecodeSmem<NT> sm;
@@ -99,8 +105,14 @@ void decode_kernel(DecodeArgs a) {
   head += head < 0 ? kW : 0;
 
   const bf16* qp = static_cast<const bf16*>(a.q);
-  const bf16* kc = static_cast<const bf16*>(a.k_cache) + ((size_t)b * hkv + kvh) * kW * D;
-  const bf16* vc = static_cast<const bf16*>(a.v_cache) + ((size_t)b * hkv + kvh) * kW * D;
+  using CacheT = typename std::conditional<FP8, uint8_t, bf16>::type;
+  const CacheT* kc = static_cast<const CacheT*>(a.k_cache) + ((size_t)b * hkv + kvh) * kW * D;
+  const CacheT* vc = static_cast<const CacheT*>(a.v_cache) + ((size_t)b * hkv + kvh) * kW * D;
+  // ring operand of 8 elements starting at element e0 of row `phys`
+  auto ring8 = [&](const CacheT* base, int phys, int e0) -> bf16x8 {
+    if constexpr (FP8) return e4m3x8_to_bf16x8(*reinterpret_cast<const u32x2*>(base + (size_t)phys * D + e0));
+    else return *reinterpret_cast<const bf16x8*>(base + (size_t)phys * D + e0);
+  };
   const bf16* kn = static_cast<const bf16*>(a.k_new) + ((size_t)b * T * hkv + kvh) * D;
   const bf16* vn = static_cast<const bf16*>(a.v_new) + ((size_t)b * T * hkv + kvh) * D;
 
@@ -113,15 +125,14 @@ void decode_kernel(DecodeArgs a) {
     const int phys = (head + kr) & (kW - 1);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
-      kf[s][cc] = kr != 0 ? *reinterpret_cast<const bf16x8*>(kc + (size_t)phys * D + 32 * cc + 8 * g)
-                          : zero8();
+      kf[s][cc] = kr != 0 ? ring8(kc, phys, 32 * cc + 8 * g) : zero8();
   }
   bf16x8 vr[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int kr = 32 * w + 8 * g + e;
     const int phys = (head + kr) & (kW - 1);
-    vr[e] = kr != 0 ? *reinterpret_cast<const bf16x8*>(vc + (size_t)phys * D + 8 * i) : zero8();
+    vr[e] = kr != 0 ? ring8(vc, phys, 8 * i) : zero8();
   }
   {
     const int tid = threadIdx.x;
@@ -158,7 +169,8 @@ void decode_kernel(DecodeArgs a) {
     return *reinterpret_cast<const bf16x8*>(&sm.u.in.q[tt * 16 + i][16 * (4 * cc + g)]);
   };
 
-  const float c = a.scale * kLog2e;
+  const float c = a.scale * kLog2e;       // new tokens' logits to log2 units
+  const float cr = FP8 ? c * a.k_scale : c;  // the ring's
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // ---- scores ----
@@ -183,7 +195,7 @@ void decode_kernel(DecodeArgs a) {
   float mx[NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
-    mx[tt] = -INFINITY;
+    float mr = -INFINITY, mn = -INFINITY;  // raw maxima of the ring and new-token logits
 #pragma unroll
     for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
@@ -192,18 +204,18 @@ void decode_kernel(DecodeArgs a) {
           const int kr = 8 * g + 4 * ss + r;
           s[tt][ss][r] = kr >= tcol[tt] + 1 ? s[tt][ss][r] : -INFINITY;
         }
-        mx[tt] = fmaxf(mx[tt], s[tt][ss][r]);
+        mr = fmaxf(mr, s[tt][ss][r]);
       }
     if (w == 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int u = 4 * g + r;
         sn[tt][r] = (u <= tcol[tt] && u < T) ? sn[tt][r] : -INFINITY;
-        mx[tt] = fmaxf(mx[tt], sn[tt][r]);
+        mn = fmaxf(mn, sn[tt][r]);
       }
     }
-    mx[tt] = quad_max(mx[tt]);
-    if (g == 0) sm.m[w][tt * 16 + i] = mx[tt] * c;
+    mx[tt] = quad_max(fmaxf(mr * cr, mn * c));  // both multipliers are > 0
+    if (g == 0) sm.m[w][tt * 16 + i] = mx[tt];
   }
   __syncthreads();
 
@@ -219,7 +231,7 @@ void decode_kernel(DecodeArgs a) {
     for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s[tt][ss][r] = fast_exp2(fmaf(s[tt][ss][r], c, -mcol[tt]));
+        s[tt][ss][r] = fast_exp2(fmaf(s[tt][ss][r], cr, -mcol[tt]));
         ps += s[tt][ss][r];
       }
     if (w == 0) {
@@ -243,7 +255,12 @@ void decode_kernel(DecodeArgs a) {
   for (int bb = 0; bb < 8; ++bb) {
     const bf16x8 av = column8(vr, bb);
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) o[tt][bb] = mfma32(av, pack_pair(s[tt][0], s[tt][1]), o[tt][bb]);
+    for (int tt = 0; tt < NT; ++tt) {
+      if constexpr (FP8)
+        o[tt][bb] = mfma32(av, pack_pair(s[tt][0] * a.v_scale, s[tt][1] * a.v_scale), o[tt][bb]);
+      else
+        o[tt][bb] = mfma32(av, pack_pair(s[tt][0], s[tt][1]), o[tt][bb]);
+    }
   }
   if (w == 0) {
     bf16x8 vrn[4];  // V rows of new tokens 4g .. 4g+3, head-dim 8i .. 8i+7
@@ -297,6 +314,7 @@ void decode_kernel(DecodeArgs a) {
 }  // namespace
 
 bool decode_mfma_supported(const DecodeArgs& a, bool bf16_io) {
+  // (an FP8 ring takes the same path: only the cache element type differs)
   const int G = a.num_q_heads / a.num_kv_heads;
   return bf16_io && a.head_dim == 128 && G % kHG == 0 && a.window == kW && a.t_new >= 1 &&
          a.t_new <= 4;
@@ -305,10 +323,14 @@ bool decode_mfma_supported(const DecodeArgs& a, bool bf16_io) {
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
   const long blocks = (long)a.batch * (a.num_q_heads / kHG);
   if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  if (a.t_new <= 2)
-    hipLaunchKernelGGL(decode_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(decode_kernel<2>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  const bool two = a.t_new > 2;
+  if (a.cache_fp8) {
+    if (two) hipLaunchKernelGGL((decode_kernel<2, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<1, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  } else {
+    if (two) hipLaunchKernelGGL((decode_kernel<2, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<1, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -8,6 +8,8 @@
 // These kernels serve every shape the matrix-core kernels do not: fp32 inputs,
 // head_dim 64, group sizes that are not a multiple of 8, and ring windows other
 // than 128.  They trade speed for generality.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -35,6 +37,9 @@ template <> struct Elem<bf16> {
   __device__ static bf16 store_cast(float x) { return (bf16)x; }
 };
 
+// Key sources hand attend_row fp32 values: load_key(j, d, dst) fills dst with
+// Elem<T>::kVec head-dim elements d.. of key j, load_val(j, e) is element e of value j.
+
 // Keys of one prefill row: positions jlo..jhi of the packed stream, KV head kvh.
 template <typename T, int D>
 struct PrefillKeys {
@@ -42,28 +47,44 @@ struct PrefillKeys {
   const T* v;
   int row_stride;  // Hkv * D
   int kvh;
-  __device__ const T* key(int j) const { return k + (size_t)j * row_stride + kvh * D; }
-  __device__ const T* val(int j) const { return v + (size_t)j * row_stride + kvh * D; }
+  __device__ void load_key(int j, int d, float* dst) const {
+    Elem<T>::load16(k + (size_t)j * row_stride + kvh * D + d, dst);
+  }
+  __device__ float load_val(int j, int e) const {
+    return Elem<T>::load1(v + (size_t)j * row_stride + kvh * D + e);
+  }
 };
 
 // Keys of one decode row: virtual positions 0..W-1 are ring logical slots (physical
-// (head + l) mod W), W..W+T-1 are the new tokens.
-template <typename T, int D>
+// (head + l) mod W), W..W+T-1 are the new tokens.  FP8: the ring holds E4M3 codes
+// whose values are scaled by k_scale / v_scale.
+template <typename T, int D, bool FP8>
 struct DecodeKeys {
-  const T* kc;  // this (sequence, kv head)'s ring: [W, D]
-  const T* vc;
+  using C = typename std::conditional<FP8, uint8_t, T>::type;
+  const C* kc;  // this (sequence, kv head)'s ring: [W, D]
+  const C* vc;
   const T* kn;  // this sequence's new tokens: [T, Hkv, D], offset to kv head
   const T* vn;
   int W;
   int head;
   int new_stride;  // Hkv * D
-  __device__ const T* key(int j) const {
-    if (j < W) { int p = head + j; p -= (p >= W) ? W : 0; return kc + (size_t)p * D; }
-    return kn + (size_t)(j - W) * new_stride;
+  float k_scale, v_scale;
+  __device__ int phys(int j) const { int p = head + j; return p - ((p >= W) ? W : 0); }
+  __device__ void load_key(int j, int d, float* dst) const {
+    if (j >= W) { Elem<T>::load16(kn + (size_t)(j - W) * new_stride + d, dst); return; }
+    const C* row = kc + (size_t)phys(j) * D + d;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int e = 0; e < Elem<T>::kVec; ++e) dst[e] = e4m3_to_f32(row[e]) * k_scale;
+    } else {
+      Elem<T>::load16(row, dst);
+    }
   }
-  __device__ const T* val(int j) const {
-    if (j < W) { int p = head + j; p -= (p >= W) ? W : 0; return vc + (size_t)p * D; }
-    return vn + (size_t)(j - W) * new_stride;
+  __device__ float load_val(int j, int e) const {
+    if (j >= W) return Elem<T>::load1(vn + (size_t)(j - W) * new_stride + e);
+    const C* p = vc + (size_t)phys(j) * D + e;
+    if constexpr (FP8) return e4m3_to_f32(*p) * v_scale;
+    else return Elem<T>::load1(p);
   }
 };
 
@@ -87,12 +108,11 @@ __device__ void attend_row(const T* __restrict__ qrow, const Keys& keys, int jlo
     const bool valid = j <= jhi;
     float s = -INFINITY;
     if (valid) {
-      const T* kr = keys.key(j);
       float acc = 0.f;
 #pragma unroll
       for (int d = 0; d < D; d += E::kVec) {
         float kk[E::kVec];
-        E::load16(kr + d, kk);
+        keys.load_key(j, d, kk);
 #pragma unroll
         for (int e = 0; e < E::kVec; ++e) acc = fmaf(q[d + e], kk[e], acc);
       }
@@ -107,9 +127,8 @@ __device__ void attend_row(const T* __restrict__ qrow, const Keys& keys, int jlo
     const int nk = min(kWave, jhi - jb + 1);
     for (int jj = 0; jj < nk; ++jj) {
       const float pj = __shfl(p, jj);
-      const T* vr = keys.val(jb + jj);
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) o[e] = fmaf(pj, E::load1(vr + lane + e * kWave), o[e]);
+      for (int e = 0; e < kPer; ++e) o[e] = fmaf(pj, keys.load_val(jb + jj, lane + e * kWave), o[e]);
     }
     m = m_new;
   }
@@ -140,7 +159,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void generic_prefill_kernel(
                    a.lse ? a.lse + row : nullptr);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool FP8>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void generic_decode_kernel(DecodeArgs a) {
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   const int hq = a.num_q_heads;
@@ -155,9 +174,12 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void generic_decode_kernel(D
   const int W = a.window;
   int head = a.ring_head[b] % W;
   head += (head < 0) ? W : 0;
-  DecodeKeys<T, D> keys;
-  keys.kc = static_cast<const T*>(a.k_cache) + ((size_t)b * hkv + kvh) * W * D;
-  keys.vc = static_cast<const T*>(a.v_cache) + ((size_t)b * hkv + kvh) * W * D;
+  using Keys = DecodeKeys<T, D, FP8>;
+  Keys keys;
+  keys.kc = static_cast<const typename Keys::C*>(a.k_cache) + ((size_t)b * hkv + kvh) * W * D;
+  keys.vc = static_cast<const typename Keys::C*>(a.v_cache) + ((size_t)b * hkv + kvh) * W * D;
+  keys.k_scale = a.k_scale;
+  keys.v_scale = a.v_scale;
   keys.kn = static_cast<const T*>(a.k_new) + ((size_t)b * T_ * hkv + kvh) * D;
   keys.vn = static_cast<const T*>(a.v_new) + ((size_t)b * T_ * hkv + kvh) * D;
   keys.W = W;
@@ -185,8 +207,12 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   const long rows = (long)a.batch * a.t_new * a.num_q_heads;
   const long blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((generic_decode_kernel<T, D>), dim3((unsigned)blocks),
-                     dim3(kRowsPerBlock * kWave), 0, s, a);
+  if (a.cache_fp8)
+    hipLaunchKernelGGL((generic_decode_kernel<T, D, true>), dim3((unsigned)blocks),
+                       dim3(kRowsPerBlock * kWave), 0, s, a);
+  else
+    hipLaunchKernelGGL((generic_decode_kernel<T, D, false>), dim3((unsigned)blocks),
+                       dim3(kRowsPerBlock * kWave), 0, s, a);
   return hipGetLastError();
 }
 

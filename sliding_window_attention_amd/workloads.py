@@ -26,7 +26,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "prefill" | "decode" | "hybrid" | "varlen"
+    kind: str  # "prefill" | "decode" | "decode_fp8" | "hybrid" | "varlen"
     dtype: str  # "f32" | "bf16"
     seq_len: int = 0  # total packed tokens for prefill kinds
     num_q_heads: int = 32
@@ -50,6 +50,9 @@ WORKLOADS = {
     "decode_t1": Workload("decode_t1", "decode", "bf16", batch=256, t_new=1, seed=3000),
     # MTP verify: 1 + 3 draft tokens per sequence, causal among themselves.
     "decode_t4": Workload("decode_t4", "decode", "bf16", batch=256, t_new=4, seed=3100),
+    # The same two decode workloads against an FP8 (E4M3) ring with per-tensor scales.
+    "decode_fp8_t1": Workload("decode_fp8_t1", "decode_fp8", "bf16", batch=256, t_new=1, seed=3200),
+    "decode_fp8_t4": Workload("decode_fp8_t4", "decode_fp8", "bf16", batch=256, t_new=4, seed=3300),
     # Hybrid block: 5 SWA-sink layers (seeds 4000..4004) + 1 GA layer (seed 4005).
     "hybrid_5to1_32k": Workload("hybrid_5to1_32k", "hybrid", "bf16", seq_len=32768, seed=4000),
     # Packed varlen prefill: 8 log-normal sequence lengths summing to 262144.
@@ -166,6 +169,28 @@ def make_decode_device(batch, t_new, num_q_heads, num_kv_heads, head_dim, window
             "sinks": torch.randn(num_q_heads, generator=hgen)}
 
 
+def e4m3_codes(shape, gen, exp_center=10.0, exp_spread=2.0):
+    """One-byte E4M3 codes shaped like a quantised N(0, s) tensor: random sign,
+    exponent field ~ round(N(exp_center, exp_spread)) clipped to 1..14 (normal
+    numbers, never the NaN pattern), uniform mantissa.  uint8, on the host."""
+    e = torch.clamp(torch.round(exp_center + exp_spread * torch.randn(shape, generator=gen)), 1, 14)
+    m = torch.randint(0, 8, shape, generator=gen)
+    sgn = torch.randint(0, 2, shape, generator=gen)
+    return ((sgn << 7) | (e.to(torch.int64) << 3) | m).to(torch.uint8)
+
+
+def make_decode_fp8(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, dtype, seed):
+    """make_decode with the caches as E4M3 codes [B, Hkv, W, D] uint8 and per-tensor
+    scales: k_scale = 1/32 and v_scale = 1/64 bring the values to about N(0, 1)."""
+    x = make_decode(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, dtype, seed)
+    gen = torch.Generator().manual_seed(int(seed) + 17)
+    shape = (batch, num_kv_heads, window, head_dim)
+    x["k_cache"] = e4m3_codes(shape, gen)
+    x["v_cache"] = e4m3_codes(shape, gen)
+    x["k_scale"], x["v_scale"] = 1.0 / 32, 1.0 / 64
+    return x
+
+
 def make_workload(name: str, layer: int = 0):
     """Inputs of a named workload (for 'hybrid_5to1_32k', layer 0..4 are SWA, 5 is GA)."""
     w = WORKLOADS[name]
@@ -180,6 +205,9 @@ def make_workload(name: str, layer: int = 0):
     if w.kind == "decode":
         return make_decode(w.batch, w.t_new, w.num_q_heads, w.num_kv_heads, w.head_dim, w.window,
                            w.dtype, w.seed)
+    if w.kind == "decode_fp8":
+        return make_decode_fp8(w.batch, w.t_new, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                               w.window, w.dtype, w.seed)
     raise KeyError(name)
 
 
@@ -216,10 +244,12 @@ def decode_flops(batch, t_new, num_q_heads, head_dim, window) -> int:
 
 
 def decode_bytes(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, elem_bytes,
-                 with_lse=True):
+                 with_lse=True, cache_elem_bytes=None):
     """Live ring slots (W-1: the oldest slot is outside every query's window),
-    the T new K/V rows, Q and O; LSE fp32."""
-    kv = 2 * batch * num_kv_heads * head_dim * elem_bytes * ((window - 1) + t_new)
+    the T new K/V rows, Q and O; LSE fp32.  cache_elem_bytes: ring element size
+    when it differs from the rest (1 for an FP8 ring)."""
+    cb = elem_bytes if cache_elem_bytes is None else cache_elem_bytes
+    kv = 2 * batch * num_kv_heads * head_dim * (cb * (window - 1) + elem_bytes * t_new)
     qo = 2 * batch * t_new * num_q_heads * head_dim * elem_bytes
     lse = 4 * batch * t_new * num_q_heads if with_lse else 0
     return kv + qo + lse
@@ -229,10 +259,10 @@ def workload_work(name: str):
     """(flops, bytes) of one pass of a named workload as its kind defines it."""
     w = WORKLOADS[name]
     eb = 4 if w.dtype == "f32" else 2
-    if w.kind == "decode":
+    if w.kind in ("decode", "decode_fp8"):
         return (decode_flops(w.batch, w.t_new, w.num_q_heads, w.head_dim, w.window),
                 decode_bytes(w.batch, w.t_new, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                             w.window, eb))
+                             w.window, eb, cache_elem_bytes=1 if w.kind == "decode_fp8" else None))
     if w.kind == "varlen":
         lens = lognormal_lengths(w.seq_len, w.num_seqs, w.seed)
     else:

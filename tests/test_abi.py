@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert set(names) == {"swa_sink_prefill", "ga_causal_prefill", "swa_sink_decode",
-                          "swa_last_error", "swa_abi_version"}
+                          "swa_sink_decode_fp8kv", "swa_last_error", "swa_abi_version"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -141,3 +141,47 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError, match="GPU tensor"):
         swa.swa_sink_prefill(q, q[:, :1].contiguous(), q[:, :1].contiguous(), torch.zeros(8),
                              torch.tensor([0, 4], dtype=torch.int32))
+
+
+def _decode_fp8(**kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, ks=0.5, vs=0.25, head=FAKE, sinks=FAKE, b=4,
+             t=1, hq=8, hkv=1, d=128, window=128, scale=0.0, dtype=1, out=FAKE, lse=NULL, stream=NULL)
+    a.update(kw)
+    return swa.library().swa_sink_decode_fp8kv(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["ks"],
+                                               a["vs"], a["head"], a["sinks"], a["b"], a["t"], a["hq"],
+                                               a["hkv"], a["d"], a["window"], a["scale"], a["dtype"],
+                                               a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(ks=0.0), E_SHAPE, "k_scale"),
+    (dict(vs=-1.0), E_SHAPE, "v_scale"),
+    (dict(ks=float("inf")), E_SHAPE, "finite"),
+    (dict(vs=float("nan")), E_SHAPE, "finite"),
+    (dict(t=0), E_SHAPE, "T must"),
+    (dict(kc=NULL), E_NULL, "k_cache"),
+    (dict(vc=NULL), E_NULL, "v_cache"),
+    (dict(d=32), E_UNSUP, "head_dim"),
+    (dict(dtype=7), E_DTYPE, "dtype"),
+])
+def test_decode_fp8kv_rejects_bad_arguments(kw, code, needle):
+    assert _decode_fp8(**kw) == code
+    assert needle in _last()
+    if code in (E_SHAPE, E_NULL):  # messages written by the decode checks name the entry point
+        assert "swa_sink_decode_fp8kv" in _last()
+
+
+def test_decode_fp8kv_empty_batch_accepts_null_pointers():
+    assert _decode_fp8(b=0, q=NULL, kn=NULL, vn=NULL, kc=NULL, vc=NULL, head=NULL, sinks=NULL,
+                       out=NULL) == OK
+    assert _decode_fp8(b=0, ks=0.0) == E_SHAPE  # the scales are still checked
+
+
+def test_binding_fp8_refuses_non_byte_caches():
+    import torch
+
+    q = torch.zeros(1, 1, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, TypeError)):
+        swa.swa_sink_decode_fp8kv(q, q[:, :, :1], q[:, :, :1], torch.zeros(1, 1, 128, 128),
+                                  torch.zeros(1, 1, 128, 128), 1.0, 1.0,
+                                  torch.zeros(1, dtype=torch.int32), torch.zeros(8), scale=None)

@@ -460,3 +460,102 @@ def test_decode_max_batch_sampled(t_new):
         assert_close(torch.bfloat16, o[bi:bi + 1], o_ref, lse[bi:bi + 1], l_ref, f"decode max batch b={bi}")
     del x, o, lse
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# decode against an FP8 (E4M3) ring
+# ---------------------------------------------------------------------------
+
+def _run_decode_fp8(x):
+    g = _gpu(x)
+    o, lse = swa.swa_sink_decode_fp8kv(g["q"], g["k_new"], g["v_new"], g["k_cache"], g["v_cache"],
+                                       x["k_scale"], x["v_scale"], g["ring_head"], g["sinks"])
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _oracle_decode_fp8(x, window):
+    return orc.swa_sink_decode_fp8kv(x["q"], x["k_new"], x["v_new"], x["k_cache"].numpy(),
+                                     x["v_cache"].numpy(), x["k_scale"], x["v_scale"],
+                                     x["ring_head"].numpy(), x["sinks"], window)
+
+
+@pytest.mark.parametrize("t_new", [1, 2, 3, 4])
+def test_decode_fp8_small_all_ring_heads(t_new):
+    _say(f"FP8 ring decode B=16 T={t_new} 32/4 D128 bf16, ring heads incl. 0 and 127")
+    x = wl.make_decode_fp8(16, t_new, 32, 4, 128, 128, "bf16", seed=700 + t_new)
+    x["ring_head"][0], x["ring_head"][1], x["ring_head"][2] = 0, 127, 1
+    o, lse = _run_decode_fp8(x)
+    o_ref, l_ref = _oracle_decode_fp8(x, 128)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, f"FP8 decode T={t_new}")
+
+
+def test_decode_fp8_every_finite_code():
+    _say("FP8 ring decode: every finite E4M3 code (subnormals, +-448) in K and V")
+    x = wl.make_decode_fp8(8, 3, 32, 4, 128, 128, "bf16", seed=777)
+    finite = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8)
+    n = x["k_cache"].numel()
+    idx = torch.arange(n)
+    x["k_cache"] = finite[idx % len(finite)].reshape(x["k_cache"].shape)
+    x["v_cache"] = finite[(idx * 7 + 3) % len(finite)].reshape(x["v_cache"].shape)
+    x["k_scale"], x["v_scale"] = 1.0 / 448, 1.0 / 448
+    o, lse = _run_decode_fp8(x)
+    o_ref, l_ref = _oracle_decode_fp8(x, 128)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, "FP8 every code")
+
+
+@pytest.mark.parametrize("case", [(6, 16, 2, 128, 128, "bf16", 3), (3, 8, 1, 64, 128, "bf16", 2),
+                                  (4, 8, 8, 128, 64, "bf16", 5), (5, 4, 1, 64, 128, "f32", 3),
+                                  (2, 8, 1, 128, 128, "bf16", 8)])
+def test_decode_fp8_generic_shapes(case):
+    b, hq, hkv, d, w, dt, t_new = case
+    _say(f"FP8 ring decode generic B={b} T={t_new} {hq}/{hkv} D{d} W{w} {dt}")
+    x = wl.make_decode_fp8(b, t_new, hq, hkv, d, w, dt, seed=b * 11 + w)
+    o, lse = _run_decode_fp8(x)
+    o_ref, l_ref = _oracle_decode_fp8(x, w)
+    assert_close(x["q"].dtype, o, o_ref, lse, l_ref, f"FP8 decode generic {case}")
+
+
+def test_decode_fp8_never_reads_oldest_slot():
+    _say("FP8 ring decode: the oldest ring slot holds the NaN code and must not matter")
+    x = wl.make_decode_fp8(8, 4, 32, 4, 128, 128, "bf16", seed=78)
+    o_ref, l_ref = _oracle_decode_fp8(x, 128)
+    for bi in range(8):
+        h = int(x["ring_head"][bi])
+        x["k_cache"][bi, :, h] = 0x7F
+        x["v_cache"][bi, :, h] = 0xFF
+    o, lse = _run_decode_fp8(x)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, "FP8 decode NaN oldest slot")
+
+
+@pytest.mark.parametrize("name", ["decode_fp8_t1", "decode_fp8_t4"])
+def test_decode_fp8_full(name):
+    _say(f"{name}: 256 sequences, FP8 ring, every element")
+    x = wl.make_workload(name)
+    o, lse = _run_decode_fp8(x)
+    o_ref, l_ref = _oracle_decode_fp8(x, 128)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, name)
+
+
+def test_decode_fp8_max_batch_sampled():
+    b = 32771  # FP8 caches of 4 x 128 x 128 bytes per sequence: past 2^31 bytes at sequence 32768
+    _say(f"FP8 ring decode B={b} T=2 32/4 D128: caches past 2^31 bytes")
+    x = wl.make_decode_device(b, 2, 32, 4, 128, 128, seed=6300, device=DEV)
+    gen = torch.Generator().manual_seed(6301)
+    shape = (b, 4, 128, 128)
+    x["k_cache"] = wl.e4m3_codes(shape, gen).to(DEV)
+    x["v_cache"] = wl.e4m3_codes(shape, gen).to(DEV)
+    x["k_scale"], x["v_scale"] = 1.0 / 32, 1.0 / 64
+    o, lse = swa.swa_sink_decode_fp8kv(x["q"], x["k_new"], x["v_new"], x["k_cache"], x["v_cache"],
+                                       x["k_scale"], x["v_scale"], x["ring_head"].to(DEV),
+                                       x["sinks"].to(DEV))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6300)
+    picks = sorted(set([0, 1, 32767, 32768, 32769, b - 1] + [int(v) for v in rng.integers(0, b, 8)]))
+    for bi in picks:
+        sl = {k: (v[bi:bi + 1].cpu() if isinstance(v, torch.Tensor) and k != "sinks" else v)
+              for k, v in x.items()}
+        o_ref, l_ref = _oracle_decode_fp8(sl, 128)
+        assert_close(torch.bfloat16, o[bi:bi + 1], o_ref, lse[bi:bi + 1], l_ref, f"FP8 max batch b={bi}")
+    del x, o, lse
+    torch.cuda.empty_cache()
