@@ -161,6 +161,36 @@ def _decode_fn():
     return fn
 
 
+def _decode_fp8_fn():
+    """Timed call of swa_sink_decode_fp8kv, arguments marshalled once per input set."""
+    import ctypes
+
+    import torch
+
+    import sliding_window_attention_amd as swa
+
+    lib = swa.library()
+    cache = {}
+
+    def fn(x):
+        key = id(x)
+        if key not in cache:
+            swa.swa_sink_decode_fp8kv(x["q"], x["k_new"], x["v_new"], x["k_cache"], x["v_cache"],
+                                      x["k_scale"], x["v_scale"], x["ring_head"], x["sinks"],
+                                      out=x["out"], lse=x["lse"])
+            b, t, hq, d = x["q"].shape
+            hkv, w = x["k_cache"].shape[1], x["k_cache"].shape[2]
+            cache[key] = (x["q"].data_ptr(), x["k_new"].data_ptr(), x["v_new"].data_ptr(),
+                          x["k_cache"].data_ptr(), x["v_cache"].data_ptr(), float(x["k_scale"]),
+                          float(x["v_scale"]), x["ring_head"].data_ptr(), x["sinks"].data_ptr(),
+                          b, t, hq, hkv, d, w, 0.0, 1, x["out"].data_ptr(), x["lse"].data_ptr(),
+                          ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        rc = lib.swa_sink_decode_fp8kv(*cache[key])
+        if rc != 0:
+            raise RuntimeError(lib.swa_last_error().decode())
+    return fn
+
+
 def _with_outputs(x, kind):
     import torch
 
@@ -237,7 +267,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="time only the primary workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["prefill", "decode", "decode1", "ga", "varlen", "copy"],
+    ap.add_argument("--only", choices=["prefill", "decode", "decode1", "decode_fp8", "decode_fp8_1",
+                                       "ga", "varlen", "copy"],
                     default=None,
                     help="time a single workload (for profiling runs); prints no JSON line")
     args = ap.parse_args(argv)
@@ -268,11 +299,15 @@ def main(argv=None):
         return 0
     if args.only is not None:
         name = {"prefill": PRIMARY, "decode": "decode_t4", "decode1": "decode_t1",
+                "decode_fp8": "decode_fp8_t4", "decode_fp8_1": "decode_fp8_t1",
                 "ga": "hybrid_5to1_32k", "varlen": "varlen_262k"}[args.only]
         layer = 5 if args.only == "ga" else 0
         dec = args.only.startswith("decode")
         x = _with_outputs(_to(wl.make_workload(name, layer), dev), "decode" if dec else "p")
-        fn = _decode_fn() if dec else _prefill_fn(128, ga=args.only == "ga")
+        if args.only.startswith("decode_fp8"):
+            fn = _decode_fp8_fn()
+        else:
+            fn = _decode_fn() if dec else _prefill_fn(128, ga=args.only == "ga")
         nsets = 32 if dec else (1 if args.only in ("varlen", "ga") else 4)
         per, _ = _time_calls(fn, _clone_sets(x, nsets), steps, warmup, per_call=not dec)
         fl, by = wl.workload_work(name)
@@ -341,8 +376,8 @@ def main(argv=None):
 
 
 def run_extra(dev, steps, warmup):
-    """Decode / MTP verify, the GA layer, the hybrid block, the varlen prefill and a
-    plain device copy (achievable-bandwidth ceiling)."""
+    """Decode / MTP verify (bf16 and FP8 rings), the GA layer, the hybrid block, the
+    varlen prefill and a plain device copy (achievable-bandwidth ceiling)."""
     import torch
 
     from sliding_window_attention_amd import workloads as wl
@@ -355,11 +390,12 @@ def run_extra(dev, steps, warmup):
     extra["copy_ceiling_gbps"] = 2 * a.numel() * 2 / (min(per) * 1e-3) / 1e9
     del a, b
 
-    for name in ("decode_t1", "decode_t4"):
+    for name in ("decode_t1", "decode_t4", "decode_fp8_t1", "decode_fp8_t4"):
         _log(f"{name}")
         x = _with_outputs(_to(wl.make_workload(name), dev), "decode")
-        sets = _clone_sets(x, 32)  # 32 x 71-86 MB: more than the Infinity Cache
-        per, _ = _time_calls(_decode_fn(), sets, max(200, steps), warmup, per_call=False)
+        sets = _clone_sets(x, 32)  # 32 x 38-86 MB: more than the Infinity Cache
+        fn = _decode_fp8_fn() if "fp8" in name else _decode_fn()
+        per, _ = _time_calls(fn, sets, max(200, steps), warmup, per_call=False)
         fl, by = wl.workload_work(name)
         st = _stats(per)
         extra[name] = {**st, "gbps": by / (st["mean_ms"] * 1e-3) / 1e9,
