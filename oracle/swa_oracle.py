@@ -109,6 +109,79 @@ def _prefill(q, k, v, sinks, cu_seqlens, window, scale, block):
     return o, lse
 
 
+def _grad_rows(qr, keys, vals, q_pos, k_pos, seq_start, window, sink, scale, do_r):
+    """Gradients of the definition for query rows of ONE head (see swa_sink_prefill_backward).
+
+    Returns (dq [R, D], dk [J, D], dv [J, D], dsink scalar) for these rows; dk and dv
+    are this head's contributions to the candidate keys.
+    """
+    a = scale * (qr @ keys.T)
+    valid = (k_pos[None, :] <= q_pos[:, None]) & (k_pos[None, :] >= seq_start[:, None])
+    if window is not None:
+        valid &= k_pos[None, :] > q_pos[:, None] - window
+    a = np.where(valid, a, NEG_INF)
+    m = np.maximum(a.max(axis=1), sink)
+    z = np.exp(sink - m) + np.exp(a - m[:, None]).sum(axis=1)
+    lse = m + np.log(z)
+    p = np.exp(a - lse[:, None])            # softmax weights of the keys (sink excluded)
+    p_sink = np.exp(sink - lse)             # the sink's weight
+    o = p @ vals
+    delta = (do_r * o).sum(axis=1)          # dO . O
+    dp = do_r @ vals.T                      # dO . v_j
+    da = p * (dp - delta[:, None])          # gradient of the scaled logits
+    dq = scale * (da @ keys)
+    dk = scale * (da.T @ qr)
+    dv = p.T @ do_r
+    dsink = -(p_sink * delta).sum()
+    return dq, dk, dv, dsink
+
+
+def swa_sink_prefill_backward(q, k, v, sinks, cu_seqlens, dout, window=128, scale=None,
+                              block=128):
+    """Gradients of swa_sink_prefill's output O with respect to q, k, v and the sinks.
+
+    For row i of head h with weights p_ij = exp(a_ij - lse_i) and sink weight
+    p_s = exp(sink_h - lse_i) (p_s + sum_j p_ij = 1), O_i = sum_j p_ij v_j, so
+        dv_j += p_ij dO_i,   delta_i = dO_i . O_i,   da_ij = p_ij (dO_i . v_j - delta_i),
+        dq_i = scale sum_j da_ij k_j,   dk_j += scale da_ij q_i,
+        dsink_h = -sum_i p_s(i) delta_i     (the sink carries no value: dO_i . (0 - O_i) p_s),
+    sums over every row and, for dk and dv, over the query heads sharing a KV head.
+    The sink is the learnable scalar of the technical report digest, section 2.2.2,
+    whose training stability the ICML keynote's Q&A (section 06) singles out; window=None
+    gives the GA layers (no sink).  Returns (dq [N, Hq, D], dk, dv [N, Hkv, D],
+    dsinks [Hq]) in fp64; LSE is not an input of the loss here.
+    """
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    n, hq, hkv, d, cu = _check_common(q, k, v, cu_seqlens)
+    if do.shape != q.shape:
+        raise ValueError("dout must have the shape of q")
+    g = hq // hkv
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    sink = np.full(hq, NEG_INF) if sinks is None else _as_f64(sinks).reshape(hq)
+    w = None if window is None else int(window)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dsink = np.zeros(hq)
+    for s in range(len(cu) - 1):
+        c0, c1 = int(cu[s]), int(cu[s + 1])
+        for i0 in range(c0, c1, block):
+            i1 = min(i0 + block, c1)
+            k0 = c0 if w is None else max(c0, i0 - w + 1)
+            q_pos = np.arange(i0, i1)
+            k_pos = np.arange(k0, i1)
+            start = np.full(i1 - i0, c0)
+            for h in range(hq):
+                kvh = h // g
+                dqr, dkr, dvr, dsr = _grad_rows(q[i0:i1, h], k[k0:i1, kvh], v[k0:i1, kvh], q_pos,
+                                                k_pos, start, w, sink[h], scale, do[i0:i1, h])
+                dq[i0:i1, h] = dqr
+                dk[k0:i1, kvh] += dkr
+                dv[k0:i1, kvh] += dvr
+                dsink[h] += dsr
+    return dq, dk, dv, dsink
+
+
 def swa_sink_prefill(q, k, v, sinks, cu_seqlens, window=128, scale=None, block=128):
     """Causal GQA sliding-window attention with a per-head sink over packed sequences.
 

@@ -387,3 +387,129 @@ def test_fp8kv_scales_act_on_the_ring_only():
     np.testing.assert_allclose(v2[0], vh[0], rtol=0, atol=1e-12)
     np.testing.assert_allclose(k2[0], base[0], rtol=0, atol=1e-12)
     np.testing.assert_allclose(k2[1], base[1], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# backward (gradients of O)
+# ---------------------------------------------------------------------------
+
+def _fd_grads(q, k, v, sinks, cu, do, window, eps=1e-6):
+    """Central finite differences of sum(O * dO) through the forward oracle."""
+    def loss(q_, k_, v_, s_):
+        return float((orc.swa_sink_prefill(q_, k_, v_, s_, cu, window)[0] * do).sum()) if window \
+            else float((orc.ga_causal_prefill(q_, k_, v_, cu)[0] * do).sum())
+    out = []
+    for which, x in enumerate((q, k, v, sinks)):
+        if x is None:
+            out.append(None)
+            continue
+        g = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [q, k, v, sinks]
+            args_m = [q, k, v, sinks]
+            args_p[which], args_m[which] = xp, xm
+            g[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        out.append(g)
+    return out
+
+
+@pytest.mark.parametrize("window,hq,hkv,sink", [(1, 2, 1, True), (3, 4, 2, True), (5, 2, 2, True),
+                                                (None, 4, 2, False), (4, 2, 1, False)])
+def test_backward_matches_finite_differences(window, hq, hkv, sink):
+    rng = np.random.default_rng(window or 99)
+    n, d = 9, 4
+    cu = np.array([0, 4, 9])
+    q, k, v = (rng.standard_normal((n, h, d)) for h in (hq, hkv, hkv))
+    sinks = rng.standard_normal(hq) if sink else None
+    do = rng.standard_normal((n, hq, d))
+    if window is None:
+        dq, dk, dv, ds = orc.swa_sink_prefill_backward(q, k, v, None, cu, do, window=None)
+    else:
+        dq, dk, dv, ds = orc.swa_sink_prefill_backward(q, k, v, sinks, cu, do, window=window)
+    fq, fk, fv, fs = _fd_grads(q, k, v, sinks, cu, do, window)
+    np.testing.assert_allclose(dq, fq, atol=1e-7, rtol=0)
+    np.testing.assert_allclose(dk, fk, atol=1e-7, rtol=0)
+    np.testing.assert_allclose(dv, fv, atol=1e-7, rtol=0)
+    if sink:
+        np.testing.assert_allclose(ds, fs, atol=1e-7, rtol=0)
+    else:
+        assert np.all(ds == 0)
+
+
+def test_backward_matches_torch_autograd():
+    """Autograd through a plain fp64 torch forward (band mask, sink as an extra logit with zero value)."""
+    rng = np.random.default_rng(3)
+    n, hq, hkv, d, w = 20, 4, 2, 8, 6
+    cu = [0, 7, 20]
+    q0, k0, v0 = (rng.standard_normal((n, h, d)) for h in (hq, hkv, hkv))
+    s0 = rng.standard_normal(hq)
+    do = rng.standard_normal((n, hq, d))
+    q, k, v, s = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q0, k0, v0, s0))
+    g = hq // hkv
+    outs = []
+    for a, b in zip(cu[:-1], cu[1:]):
+        L = b - a
+        pos = torch.arange(L)
+        band = (pos[None, :] <= pos[:, None]) & (pos[None, :] > pos[:, None] - w)
+        kk = k[a:b].repeat_interleave(g, dim=1).transpose(0, 1)  # [Hq, L, D]
+        vv = v[a:b].repeat_interleave(g, dim=1).transpose(0, 1)
+        qq = q[a:b].transpose(0, 1)
+        logits = (qq @ kk.transpose(1, 2)) / math.sqrt(d)
+        logits = logits.masked_fill(~band, float("-inf"))
+        sink_col = s[:, None, None].expand(hq, L, 1)
+        pr = torch.softmax(torch.cat([logits, sink_col], dim=2), dim=2)[:, :, :L]
+        outs.append((pr @ vv).transpose(0, 1))
+    o = torch.cat(outs, dim=0)
+    (o * torch.tensor(do)).sum().backward()
+    dq, dk, dv, ds = orc.swa_sink_prefill_backward(q0, k0, v0, s0, np.array(cu), do, window=w)
+    for ours, ref in ((dq, q.grad), (dk, k.grad), (dv, v.grad), (ds, s.grad)):
+        np.testing.assert_allclose(ours, ref.numpy(), atol=1e-12, rtol=0)
+
+
+def test_backward_constant_keys_closed_form():
+    """All keys equal to k: the logits of a row are equal, raising them moves weight from the sink
+    (which carries no value) onto the keys, so dO_i . dO_i/dlogit = p_sink(i) delta_i and
+    dq_i = scale * p_sink(i) * delta_i * k (with delta_i = dO_i . O_i)."""
+    rng = np.random.default_rng(4)
+    n, d, w = 11, 6, 4
+    kbar = rng.standard_normal(d)
+    q = rng.standard_normal((n, 1, d))
+    k = np.tile(kbar, (n, 1, 1))
+    v = rng.standard_normal((n, 1, d))
+    s = np.array([0.3])
+    do = rng.standard_normal((n, 1, d))
+    cu = np.array([0, n])
+    o, lse = orc.swa_sink_prefill(q, k, v, s, cu, w)
+    dq, _, _, _ = orc.swa_sink_prefill_backward(q, k, v, s, cu, do, window=w)
+    scale = 1 / math.sqrt(d)
+    delta = (do[:, 0] * o[:, 0]).sum(axis=1)
+    p_sink = np.exp(s[0] - lse[:, 0])
+    np.testing.assert_allclose(dq[:, 0], scale * (p_sink * delta)[:, None] * kbar[None, :], atol=1e-13)
+
+
+def test_backward_shift_invariance_and_gqa():
+    """Adding one constant to every logit of a row and to the sink changes nothing, so per head
+    the logit gradients (row sums p_sink(i) delta_i) cancel the sink gradient; and GQA gradients
+    equal those of MHA with repeated K/V, summed over each group."""
+    rng = np.random.default_rng(5)
+    n, hq, hkv, d, w = 12, 4, 2, 8, 5
+    cu = np.array([0, 5, 12])
+    q, k, v = (rng.standard_normal((n, h, d)) for h in (hq, hkv, hkv))
+    s = rng.standard_normal(hq)
+    do = rng.standard_normal((n, hq, d))
+    dq, dk, dv, ds = orc.swa_sink_prefill_backward(q, k, v, s, cu, do, window=w)
+    g = hq // hkv
+    dq2, dk2, dv2, ds2 = orc.swa_sink_prefill_backward(q, np.repeat(k, g, axis=1), np.repeat(v, g, axis=1),
+                                                       s, cu, do, window=w)
+    np.testing.assert_allclose(dq, dq2, atol=1e-13)
+    np.testing.assert_allclose(dk, dk2.reshape(n, hkv, g, d).sum(axis=2), atol=1e-12)
+    np.testing.assert_allclose(dv, dv2.reshape(n, hkv, g, d).sum(axis=2), atol=1e-12)
+    np.testing.assert_allclose(ds, ds2, atol=1e-13)
+    o, lse = orc.swa_sink_prefill(q, k, v, s, cu, w)
+    for h in range(hq):
+        delta = (do[:, h] * o[:, h]).sum(axis=1)
+        logit_grad_sum = (np.exp(s[h] - lse[:, h]) * delta).sum()
+        assert abs(logit_grad_sum + ds[h]) < 1e-12
