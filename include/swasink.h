@@ -57,7 +57,7 @@ typedef enum {
 
 typedef enum { SWA_DTYPE_F32 = 0, SWA_DTYPE_BF16 = 1 } swa_dtype;
 
-#define SWASINK_ABI_VERSION 2
+#define SWASINK_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SWASINK_API __attribute__((visibility("default")))
@@ -145,6 +145,41 @@ SWASINK_API int swa_sink_decode_fp8kv(const void* q, const void* k_new, const vo
                     const int32_t* ring_head, const float* sinks, int32_t batch, int32_t T,
                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t window,
                     float scale, swa_dtype dtype, void* out, float* lse, void* stream);
+
+/*
+ * Gradients of swa_sink_prefill's output: given dout = dL/dO, returns dL/dq, dL/dk,
+ * dL/dv and dL/dsinks, where the sink is the learnable per-head scalar of the
+ * technical report digest, section 2.2.2 (the ICML keynote's Q&A, section 06, names
+ * its training stability as critical).  With p_ij the forward weights and
+ * p_s(i) = exp(sink - lse_i) the sink's: delta_i = dout_i . out_i,
+ * da_ij = p_ij (dout_i . v_j - delta_i), dq_i = scale sum_j da_ij k_j,
+ * dk_j = scale sum_i da_ij q_i, dv_j = sum_i p_ij dout_i (dk, dv summed over the
+ * query heads of each KV head), dsink_h = -sum_i p_s(i) delta_i.  The LSE output is
+ * not differentiated.
+ *
+ *  q, k, v, sinks, cu_seqlens, num_seqs, total_tokens, max_seqlen, heads, head_dim,
+ *  window, scale, dtype: as swa_sink_prefill; sinks may be NULL (no sink, e.g. a GA
+ *  layer with window >= the longest sequence), and then dsinks must be NULL too.
+ *  out   [total_tokens, num_q_heads, head_dim] dtype: the forward output
+ *  lse   [total_tokens, num_q_heads] fp32: the forward log-sum-exp (required)
+ *  dout  like out
+ *  dq    like q;  dk, dv like k, v;  dsinks [num_q_heads] fp32 (written, not added to)
+ *  workspace  device memory of at least swa_sink_prefill_backward_workspace(...) bytes,
+ *             owned by the caller, overwritten; calls sharing one workspace must not
+ *             overlap.  The library allocates nothing.
+ * Deterministic (no atomics).  total_tokens == 0 writes zeros to dsinks (if given) and
+ * reads nothing: the other pointers and the workspace may then be NULL.
+ */
+SWASINK_API int swa_sink_prefill_backward(const void* q, const void* k, const void* v,
+                    const float* sinks, const int32_t* cu_seqlens, int32_t num_seqs,
+                    int32_t total_tokens, int32_t max_seqlen, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t window, float scale,
+                    swa_dtype dtype, const void* out, const float* lse, const void* dout,
+                    void* dq, void* dk, void* dv, float* dsinks, void* workspace,
+                    int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace swa_sink_prefill_backward needs (-1 for invalid sizes). */
+SWASINK_API int64_t swa_sink_prefill_backward_workspace(int32_t total_tokens, int32_t num_q_heads);
 
 /* Message for the last non-OK return on the calling thread ("" if none). */
 SWASINK_API const char* swa_last_error(void);

@@ -36,6 +36,8 @@ _SIGNATURES = {
     "swa_sink_prefill": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P],
     "ga_causal_prefill": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P],
     "swa_sink_decode": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P],
+    "swa_sink_prefill_backward": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P,
+                                  _P, _P, _P, _P, _P, ctypes.c_int64, _P],
     "swa_sink_decode_fp8kv": [_P, _P, _P, _P, _P, _F, _F, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
                               _P, _P, _P],
 }
@@ -67,6 +69,8 @@ def library() -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         lib.swa_last_error.argtypes = []
         lib.swa_last_error.restype = ctypes.c_char_p
+        lib.swa_sink_prefill_backward_workspace.argtypes = [_I, _I]
+        lib.swa_sink_prefill_backward_workspace.restype = ctypes.c_int64
         lib.swa_abi_version.argtypes = []
         lib.swa_abi_version.restype = ctypes.c_int32
         _lib = lib
@@ -245,3 +249,43 @@ def swa_sink_decode_fp8kv(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, r
         _stream(q.device))
     _check(rc)
     return out, lse
+
+
+def swa_sink_prefill_backward(q, k, v, sinks, cu_seqlens, out, lse, dout, max_seqlen=None,
+                              window=128, scale=None):
+    """Gradients of swa_sink_prefill's output O: (dq, dk, dv, dsinks) for dout = dL/dO.
+
+    q/out/dout [N, Hq, D], k/v [N, Hkv, D] in one dtype, lse [N, Hq] fp32 from the
+    forward, sinks [Hq] fp32 or None (no sink; dsinks is then None).  The workspace
+    the library needs is allocated here with torch.
+    """
+    import torch
+
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _dev(t, nm, q.dtype)
+    _dev(lse, "lse", torch.float32)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    if sinks is not None:
+        _dev(sinks, "sinks", torch.float32)
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, out, dout must be [N, Hq, D] and k, v [N, Hkv, D]")
+    n, hq, d = q.shape
+    if k.shape[0] != n or k.shape[2] != d or tuple(lse.shape) != (n, hq) or (
+            sinks is not None and sinks.numel() != hq):
+        raise ValueError("inconsistent shapes")
+    lib = library()
+    need = int(lib.swa_sink_prefill_backward_workspace(n, hq))
+    if need < 0:
+        raise ValueError("invalid sizes")
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dsinks = None if sinks is None else torch.empty(hq, dtype=torch.float32, device=q.device)
+    ms = n if max_seqlen is None else int(max_seqlen)
+    rc = lib.swa_sink_prefill_backward(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), None if sinks is None else sinks.data_ptr(),
+        cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, n, ms, hq, k.shape[1], d, int(window),
+        _scale(scale), _dtype_code(q), out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+        dk.data_ptr(), dv.data_ptr(), None if dsinks is None else dsinks.data_ptr(), ws.data_ptr(),
+        need, _stream(q.device))
+    _check(rc)
+    return dq, dk, dv, dsinks

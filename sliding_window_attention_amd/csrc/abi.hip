@@ -157,6 +157,12 @@ int decode_common(const void* q, const void* k_new, const void* v_new, const voi
   return hip_status(e, name);
 }
 
+int64_t backward_workspace_bytes(int32_t total_tokens, int32_t num_q_heads) {
+  if (total_tokens < 0 || num_q_heads < 1) return -1;
+  const int64_t rows = (int64_t)total_tokens * num_q_heads;
+  return ((2 * rows * (int64_t)sizeof(float)) + 255) / 256 * 256;  // delta and sink terms
+}
+
 }  // namespace
 
 extern "C" {
@@ -199,6 +205,55 @@ int swa_sink_decode_fp8kv(const void* q, const void* k_new, const void* v_new,
   return decode_common(q, k_new, v_new, k_cache, v_cache, true, k_scale, v_scale, ring_head, sinks,
                        batch, T, num_q_heads, num_kv_heads, head_dim, window, scale, (int)dtype,
                        out, lse, stream, "swa_sink_decode_fp8kv");
+}
+
+int64_t swa_sink_prefill_backward_workspace(int32_t total_tokens, int32_t num_q_heads) {
+  return backward_workspace_bytes(total_tokens, num_q_heads);
+}
+
+int swa_sink_prefill_backward(const void* q, const void* k, const void* v, const float* sinks,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                              int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t window, float scale, swa_dtype dtype,
+                              const void* out, const float* lse, const void* dout, void* dq,
+                              void* dk, void* dv, float* dsinks, void* workspace,
+                              int64_t workspace_bytes, void* stream) {
+  const char* name = "swa_sink_prefill_backward";
+  int rc = check_dtype((int)dtype);
+  if (rc) return rc;
+  if (total_tokens < 0) return fail(SWA_ERR_SHAPE, "%s: total_tokens must be >= 0", name);
+  if (num_seqs < 1) return fail(SWA_ERR_SHAPE, "%s: num_seqs must be >= 1", name);
+  if (num_seqs > total_tokens && total_tokens > 0)
+    return fail(SWA_ERR_SHAPE, "%s: num_seqs (%d) exceeds total_tokens (%d)", name, num_seqs,
+                total_tokens);
+  if (total_tokens > 0 && (max_seqlen < 1 || max_seqlen > total_tokens))
+    return fail(SWA_ERR_SHAPE, "%s: max_seqlen must be in [1, total_tokens]", name);
+  if ((rc = check_heads(num_q_heads, num_kv_heads, head_dim))) return rc;
+  if (window < 1) return fail(SWA_ERR_SHAPE, "%s: window must be >= 1 (got %d)", name, window);
+  if ((long long)total_tokens * num_q_heads * head_dim > (1LL << 40))
+    return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
+  if ((sinks == nullptr) != (dsinks == nullptr))
+    return fail(SWA_ERR_NULL, "%s: sinks and dsinks must both be given or both be NULL", name);
+  if (total_tokens == 0 && dsinks == nullptr) return ok();  // nothing to read or write
+  if (total_tokens > 0 && (!q || !k || !v || !cu_seqlens || !out || !lse || !dout || !dq || !dk || !dv))
+    return fail(SWA_ERR_NULL, "%s: q, k, v, cu_seqlens, out, lse, dout, dq, dk and dv must be non-NULL",
+                name);
+  const int64_t need = backward_workspace_bytes(total_tokens, num_q_heads);
+  if (total_tokens > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(SWA_ERR_SHAPE, "%s: workspace of %lld bytes needed (got %lld)", name, (long long)need,
+                (long long)workspace_bytes);
+  swa::BackwardArgs a;
+  a.q = q; a.k = k; a.v = v; a.sinks = sinks; a.cu_seqlens = cu_seqlens;
+  a.out = out; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dsinks = dsinks;
+  a.delta = static_cast<float*>(workspace);
+  a.sink_term = a.delta + (size_t)total_tokens * num_q_heads;
+  a.num_seqs = num_seqs; a.total_tokens = total_tokens;
+  a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
+  a.window = window;
+  a.scale = resolve_scale(scale, head_dim);
+  const hipError_t e = swa::launch_backward(a, dtype == SWA_DTYPE_BF16, static_cast<hipStream_t>(stream));
+  return hip_status(e, name);
 }
 
 const char* swa_last_error(void) { return g_last_error; }

@@ -70,6 +70,31 @@ struct DecodeArgs {
   float v_scale = 1.f;
 };
 
+// Arguments of the backward (gradients of O).  Pointers are device pointers.
+struct BackwardArgs {
+  const void* q;             // [N, Hq, D]
+  const void* k;             // [N, Hkv, D]
+  const void* v;             // [N, Hkv, D]
+  const float* sinks;        // [Hq] or nullptr (no sink)
+  const int32_t* cu_seqlens;  // [S + 1]
+  const void* out;           // [N, Hq, D] forward output
+  const float* lse;          // [N, Hq] forward log-sum-exp (natural log, sink included)
+  const void* dout;          // [N, Hq, D]
+  void* dq;                  // [N, Hq, D]
+  void* dk;                  // [N, Hkv, D]
+  void* dv;                  // [N, Hkv, D]
+  float* dsinks;             // [Hq] or nullptr (no sink)
+  float* delta;              // workspace [N, Hq]: dO . O
+  float* sink_term;          // workspace [N, Hq]: exp(sink - lse) * delta
+  int32_t num_seqs;
+  int32_t total_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t window;
+  float scale;
+};
+
 // First token of the sequence that holds packed token `t`: the largest s with
 // cu[s] <= t (binary search; cu has num_seqs + 1 entries).  Clamped so that a
 // malformed cu_seqlens cannot produce an index outside [0, t].

@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert set(names) == {"swa_sink_prefill", "ga_causal_prefill", "swa_sink_decode",
-                          "swa_sink_decode_fp8kv", "swa_last_error", "swa_abi_version"}
+                          "swa_sink_decode_fp8kv", "swa_sink_prefill_backward",
+                          "swa_sink_prefill_backward_workspace", "swa_last_error", "swa_abi_version"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -185,3 +186,45 @@ def test_binding_fp8_refuses_non_byte_caches():
         swa.swa_sink_decode_fp8kv(q, q[:, :, :1], q[:, :, :1], torch.zeros(1, 1, 128, 128),
                                   torch.zeros(1, 1, 128, 128), 1.0, 1.0,
                                   torch.zeros(1, dtype=torch.int32), torch.zeros(8), scale=None)
+
+
+def _backward(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sinks=FAKE, cu=FAKE, num_seqs=1, n=16, max_seqlen=16, hq=8,
+             hkv=1, d=128, window=128, scale=0.0, dtype=1, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE,
+             dk=FAKE, dv=FAKE, dsinks=FAKE, ws=FAKE, ws_bytes=1 << 20, stream=NULL)
+    a.update(kw)
+    return swa.library().swa_sink_prefill_backward(
+        a["q"], a["k"], a["v"], a["sinks"], a["cu"], a["num_seqs"], a["n"], a["max_seqlen"], a["hq"],
+        a["hkv"], a["d"], a["window"], a["scale"], a["dtype"], a["out"], a["lse"], a["dout"], a["dq"],
+        a["dk"], a["dv"], a["dsinks"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_backward_workspace_size():
+    lib = swa.library()
+    assert lib.swa_sink_prefill_backward_workspace(16, 8) == 1024  # 2 x 128 floats, 256-aligned
+    assert lib.swa_sink_prefill_backward_workspace(1000, 32) == 256000
+    assert lib.swa_sink_prefill_backward_workspace(0, 8) == 0
+    assert lib.swa_sink_prefill_backward_workspace(-1, 8) == -1
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(ws_bytes=1000), E_SHAPE, "workspace of 1024"),
+    (dict(ws=NULL), E_SHAPE, "workspace"),
+    (dict(lse=NULL), E_NULL, "lse"),
+    (dict(dout=NULL), E_NULL, "dout"),
+    (dict(dk=NULL), E_NULL, "dk"),
+    (dict(dsinks=NULL), E_NULL, "both"),
+    (dict(sinks=NULL), E_NULL, "both"),
+    (dict(window=0), E_SHAPE, "window"),
+    (dict(hq=12, hkv=8), E_SHAPE, "multiple"),
+    (dict(d=96), E_UNSUP, "head_dim"),
+    (dict(num_seqs=0), E_SHAPE, "num_seqs"),
+])
+def test_backward_rejects_bad_arguments(kw, code, needle):
+    assert _backward(**kw) == code
+    assert needle in _last()
+
+
+def test_backward_empty_stream_without_sinks_reads_nothing():
+    assert _backward(n=0, max_seqlen=0, q=NULL, k=NULL, v=NULL, cu=NULL, out=NULL, lse=NULL, dout=NULL,
+                     dq=NULL, dk=NULL, dv=NULL, sinks=NULL, dsinks=NULL, ws=NULL, ws_bytes=0) == OK

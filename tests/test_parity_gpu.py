@@ -559,3 +559,111 @@ def test_decode_fp8_max_batch_sampled():
         assert_close(torch.bfloat16, o[bi:bi + 1], o_ref, lse[bi:bi + 1], l_ref, f"FP8 max batch b={bi}")
     del x, o, lse
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# backward (gradients of O)
+# ---------------------------------------------------------------------------
+
+INT_MAX = 2 ** 31 - 1
+
+
+def assert_grads_close(dtype, got, ref, what):
+    """Gradient bar derived from the arithmetic: fp32 accumulation on exact inputs, outputs
+    rounded to the I/O type (bf16: 2^-9 relative), and delta = dO . O taken on the forward output
+    as stored (bf16-rounded), so bf16 errors are a few 2^-9 of the largest gradient: max-abs
+    <= 1e-2 * max(1, max |ref|) and rel-L2 <= 1e-2; fp32: 1e-4 and 1e-5."""
+    g = to_np(got).astype(np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.isfinite(g).all(), what
+    err = np.abs(g - r)
+    scale = max(1.0, float(np.abs(r).max(initial=0.0)))
+    rel = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))
+    tol_abs, tol_rel = (1e-2, 1e-2) if dtype == torch.bfloat16 else (1e-4, 1e-5)
+    msg = f"{what}: max_abs {err.max(initial=0.0):.3e} (scale {scale:.3e}), rel_l2 {rel:.3e}"
+    print(msg, flush=True)
+    assert err.max(initial=0.0) <= tol_abs * scale, msg
+    assert rel <= tol_rel or np.linalg.norm(r) < 1e-6, msg
+
+
+def _backward_case(lens, hq, hkv, d, dt, window, sink=True, seed=0):
+    """GPU backward against the oracle.  The forward output (rounded to the I/O type) and its
+    LSE come from the oracle, so no GPU value feeds the comparison."""
+    x = wl.make_prefill(lens, hq, hkv, d, dt, seed, with_sinks=sink)
+    gen = torch.Generator().manual_seed(seed + 1)
+    td = x["q"].dtype
+    dout = torch.randn(x["q"].shape, generator=gen).to(td)
+    cu = x["cu_seqlens"].numpy()
+    w = None if window is None else window
+    if w is None:
+        o_ref, l_ref = orc.ga_causal_prefill(x["q"], x["k"], x["v"], cu)
+    else:
+        o_ref, l_ref = orc.swa_sink_prefill(x["q"], x["k"], x["v"], x["sinks"], cu, w)
+    g = _gpu(x)
+    out = torch.tensor(o_ref).to(td).to(DEV)
+    lse = torch.tensor(l_ref, dtype=torch.float32, device=DEV)
+    dq, dk, dv, ds = swa.swa_sink_prefill_backward(
+        g["q"], g["k"], g["v"], g["sinks"] if sink else None, g["cu_seqlens"], out, lse, dout.to(DEV),
+        x["max_seqlen"], window=INT_MAX if w is None else w)
+    torch.cuda.synchronize()
+    rq, rk, rv, rs = orc.swa_sink_prefill_backward(x["q"], x["k"], x["v"], x["sinks"] if sink else None,
+                                                   cu, dout, window=w)
+    tag = f"{lens} {hq}/{hkv} D{d} {dt} W{window}"
+    assert_grads_close(td, dq, rq, f"dq {tag}")
+    assert_grads_close(td, dk, rk, f"dk {tag}")
+    assert_grads_close(td, dv, rv, f"dv {tag}")
+    if sink:
+        # dsink_h = -sum_i p_s(i) delta_i with delta_i = dO_i . O_i taken on O as stored: rounding
+        # each O element (2^-9 relative in bf16, 2^-24 in fp32) moves dsink_h by at most
+        # u * sum_i p_s(i) sum_d |dO_id O_id|; the bar is twice that plus fp32 accumulation slack
+        u = 2.0 ** -9 if td == torch.bfloat16 else 2.0 ** -24
+        p_s = np.exp(x["sinks"].double().numpy()[None, :] - l_ref)          # [N, Hq]
+        mag = (np.abs(dout.double().numpy()) * np.abs(o_ref)).sum(axis=2)   # [N, Hq]
+        bound = 2 * u * (p_s * mag).sum(axis=0) + 1e-5 * (p_s * mag).sum(axis=0) + 1e-6
+        err = np.abs(to_np(ds) - rs)
+        msg = f"dsinks {tag}: max err {err.max():.3e}, max err / bound {(err / bound).max():.3f}"
+        print(msg, flush=True)
+        assert np.all(err <= bound), msg
+    else:
+        assert ds is None
+    return dq, dk, dv, ds
+
+
+BACKWARD_CASES = [
+    ([300, 45], 32, 4, 128, "bf16", 128, True),
+    ([130, 1, 17], 8, 1, 128, "bf16", 37, True),
+    ([200], 8, 2, 64, "bf16", 128, True),        # group size 4, head_dim 64
+    ([150, 3], 4, 2, 128, "f32", 50, True),
+    ([200, 31], 16, 2, 128, "bf16", None, False),  # GA: no window, no sink
+    ([0, 37, 0, 60, 0], 8, 1, 128, "bf16", 128, True),  # zero-length sequences
+]
+
+
+@pytest.mark.parametrize("case", BACKWARD_CASES,
+                         ids=lambda c: f"{c[0]}-{c[1]}/{c[2]}-D{c[3]}-{c[4]}-W{c[5]}-{'sink' if c[6] else 'nosink'}")
+def test_backward_small(case):
+    lens, hq, hkv, d, dt, w, sink = case
+    _say(f"backward {lens} {hq}/{hkv} D{d} {dt} W{w} sink={sink}")
+    _backward_case(lens, hq, hkv, d, dt, w, sink, seed=8000 + sum(lens) + (w or 0))
+
+
+def test_backward_empty_stream_and_determinism():
+    _say("backward: empty stream writes zero sink gradients; two calls are bitwise identical")
+    x = wl.make_prefill([0, 0], 8, 1, 128, "bf16", seed=1)
+    z = torch.zeros((0, 8, 128), dtype=torch.bfloat16, device=DEV)
+    dq, dk, dv, ds = swa.swa_sink_prefill_backward(
+        z, torch.zeros((0, 1, 128), dtype=torch.bfloat16, device=DEV),
+        torch.zeros((0, 1, 128), dtype=torch.bfloat16, device=DEV), x["sinks"].to(DEV),
+        x["cu_seqlens"].to(DEV), z, torch.zeros((0, 8), device=DEV), z, 0)
+    torch.cuda.synchronize()
+    assert tuple(dq.shape) == (0, 8, 128) and bool((ds == 0).all())
+    a = _backward_case([257, 100], 32, 4, 128, "bf16", 128, True, seed=8100)
+    b = _backward_case([257, 100], 32, 4, 128, "bf16", 128, True, seed=8100)
+    for u, w_ in zip(a, b):
+        assert torch.equal(u, w_)
+
+
+def test_backward_32k_layer():
+    _say("backward of the 32K SWA-sink layer (32/4, D128, W128): every gradient element")
+    _backward_case([32768], 32, 4, 128, "bf16", 128, True, seed=wl.WORKLOADS["swa_prefill_32k"].seed)
