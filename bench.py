@@ -191,6 +191,55 @@ def _decode_fp8_fn():
     return fn
 
 
+def _backward_fn():
+    """Timed call of swa_sink_prefill_backward, arguments marshalled once per input set
+    (x holds q, k, v, sinks, cu_seqlens, out, lse, dout and the gradient buffers)."""
+    import ctypes
+
+    import torch
+
+    import sliding_window_attention_amd as swa
+
+    lib = swa.library()
+    cache = {}
+
+    def fn(x):
+        key = id(x)
+        if key not in cache:
+            n, hq, d = x["q"].shape
+            need = int(lib.swa_sink_prefill_backward_workspace(n, hq))
+            x["ws"] = torch.empty(need, dtype=torch.uint8, device=x["q"].device)
+            for nm in ("dq", "dk", "dv"):
+                x[nm] = torch.empty_like(x[nm[1]])
+            x["dsinks"] = torch.empty(hq, dtype=torch.float32, device=x["q"].device)
+            cache[key] = (x["q"].data_ptr(), x["k"].data_ptr(), x["v"].data_ptr(), x["sinks"].data_ptr(),
+                          x["cu_seqlens"].data_ptr(), x["cu_seqlens"].numel() - 1, n, n, hq,
+                          x["k"].shape[1], d, 128, 0.0, 1, x["out"].data_ptr(), x["lse"].data_ptr(),
+                          x["dout"].data_ptr(), x["dq"].data_ptr(), x["dk"].data_ptr(), x["dv"].data_ptr(),
+                          x["dsinks"].data_ptr(), x["ws"].data_ptr(), need,
+                          ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        rc = lib.swa_sink_prefill_backward(*cache[key])
+        if rc != 0:
+            raise RuntimeError(lib.swa_last_error().decode())
+    return fn
+
+
+def _backward_inputs(dev):
+    """The 32K layer's inputs, its forward output and LSE (from the library's forward,
+    untimed) and a seeded dout: the backward's workload."""
+    import torch
+
+    import sliding_window_attention_amd as swa
+    from sliding_window_attention_amd import workloads as wl
+
+    x = _to(wl.make_workload(PRIMARY), dev)
+    x["out"], x["lse"] = swa.swa_sink_prefill(x["q"], x["k"], x["v"], x["sinks"], x["cu_seqlens"],
+                                              x["max_seqlen"], window=128)
+    gen = torch.Generator(device=dev).manual_seed(wl.WORKLOADS[PRIMARY].seed + 7)
+    x["dout"] = torch.randn(x["q"].shape, generator=gen, device=dev).to(x["q"].dtype)
+    return x
+
+
 def _with_outputs(x, kind):
     import torch
 
@@ -268,7 +317,7 @@ def main(argv=None):
     ap.add_argument("--no-extra", action="store_true", help="time only the primary workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", choices=["prefill", "decode", "decode1", "decode_fp8", "decode_fp8_1",
-                                       "ga", "varlen", "copy"],
+                                       "ga", "varlen", "backward", "copy"],
                     default=None,
                     help="time a single workload (for profiling runs); prints no JSON line")
     args = ap.parse_args(argv)
@@ -296,6 +345,15 @@ def main(argv=None):
         b = torch.empty_like(a)
         per, _ = _time_calls(lambda _: b.copy_(a), [None], steps, warmup)
         _log(f"copy 512 MiB: {_stats(per)}  {2 * a.numel() * 2 / (_stats(per)['mean_ms'] * 1e-3) / 1e9:.0f} GB/s")
+        return 0
+    if args.only == "backward":
+        x = _backward_inputs(dev)
+        per, _ = _time_calls(_backward_fn(), [x], max(3, steps), warmup, per_call=False)
+        st = _stats(per)
+        fl = wl.backward_flops([32768], 32, 128, 128)
+        by = wl.backward_bytes(32768, 32, 4, 128, 2)
+        _log(f"backward 32K: {st}  {fl / (st['mean_ms'] * 1e-3) / 1e12:.1f} TFLOP/s  "
+             f"{by / (st['mean_ms'] * 1e-3) / 1e9:.0f} GB/s")
         return 0
     if args.only is not None:
         name = {"prefill": PRIMARY, "decode": "decode_t4", "decode1": "decode_t1",
@@ -429,6 +487,17 @@ def run_extra(dev, steps, warmup):
                              "swa_layer_mean_ms": _stats(per_swa)["mean_ms"],
                              "swa_layer_gbps": by / (_stats(per_swa)["mean_ms"] * 1e-3) / 1e9}
     del layers
+    torch.cuda.empty_cache()
+
+    _log("backward of the 32K layer")
+    x = _backward_inputs(dev)
+    per, _ = _time_calls(_backward_fn(), [x], 5, 1, per_call=False)
+    st = _stats(per)
+    fl = wl.backward_flops([32768], 32, 128, 128)
+    by = wl.backward_bytes(32768, 32, 4, 128, 2)
+    extra["backward_32k"] = {**st, "tflops": fl / (st["mean_ms"] * 1e-3) / 1e12,
+                             "gbps": by / (st["mean_ms"] * 1e-3) / 1e9, "flops": fl, "bytes": by}
+    del x
     torch.cuda.empty_cache()
 
     _log("varlen_262k")

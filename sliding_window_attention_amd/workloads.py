@@ -238,6 +238,19 @@ def prefill_bytes(total_tokens, num_q_heads, num_kv_heads, head_dim, elem_bytes,
     return total_tokens * per_tok
 
 
+def backward_flops(lengths, num_q_heads, head_dim, window) -> int:
+    """Gradients of O: per visible (query, key) pair and head, the recomputed logits,
+    dO . v, and the dv, dk and dq products: 5 contractions of 2 * head_dim."""
+    return 10 * head_dim * num_q_heads * sum(pairs(l, window) for l in lengths)
+
+
+def backward_bytes(total_tokens, num_q_heads, num_kv_heads, head_dim, elem_bytes):
+    """q, out, dout, dq ([N, Hq, D]); k, v, dk, dv ([N, Hkv, D]); the fp32 LSE: each
+    read or written once."""
+    return (4 * total_tokens * num_q_heads * head_dim * elem_bytes
+            + 4 * total_tokens * num_kv_heads * head_dim * elem_bytes + 4 * total_tokens * num_q_heads)
+
+
 def decode_flops(batch, t_new, num_q_heads, head_dim, window) -> int:
     """Every query row sees exactly `window` keys (W-1-t ring slots + t+1 new)."""
     return 4 * head_dim * num_q_heads * batch * t_new * window
