@@ -12,7 +12,8 @@
 // where dk and dv also sum over the query heads that share a KV head.  Four
 // kernels, one wavefront per row: (1) delta and the sink terms, (2) dq per query
 // row, (3) dk and dv per key row, (4) dsink per head by a fixed-order reduction
-// (deterministic: no atomics anywhere).
+// (deterministic: no atomics anywhere).  For bf16, head_dim 128, windows up to 128
+// and groups of 8k heads, the matrix-core kernels replace (2) and (3).
 #include "common.h"
 #include "kernels.h"
 
@@ -198,15 +199,22 @@ __global__ __launch_bounds__(kSinkThreads) void bwd_dsink_kernel(BackwardArgs a)
 }
 
 template <typename T, int D>
-hipError_t launch_t(const BackwardArgs& a, hipStream_t s) {
+hipError_t launch_t(const BackwardArgs& a, bool kMfma, hipStream_t s) {
   const long qrows = (long)a.total_tokens * a.num_q_heads;
   const long krows = (long)a.total_tokens * a.num_kv_heads;
   const long qblocks = (qrows + kRows - 1) / kRows, kblocks = (krows + kRows - 1) / kRows;
   if (qblocks > 0x7fffffffL || kblocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
   if (qrows > 0) {  // an empty stream only writes zero sink gradients
     hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)qblocks), dim3(kRows * kWave), 0, s, a);
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((unsigned)qblocks), dim3(kRows * kWave), 0, s, a);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3((unsigned)kblocks), dim3(kRows * kWave), 0, s, a);
+    if (kMfma) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const hipError_t m = launch_backward_mfma(a, s);
+      if (m != hipSuccess) return m;
+    } else {
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((unsigned)qblocks), dim3(kRows * kWave), 0, s, a);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3((unsigned)kblocks), dim3(kRows * kWave), 0, s, a);
+    }
   }
   if (a.dsinks != nullptr)
     hipLaunchKernelGGL(bwd_dsink_kernel, dim3((unsigned)a.num_q_heads), dim3(kSinkThreads), 0, s, a);
@@ -216,8 +224,11 @@ hipError_t launch_t(const BackwardArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_backward(const BackwardArgs& a, bool bf16_io, hipStream_t s) {
-  if (bf16_io) return a.head_dim == 64 ? launch_t<bf16, 64>(a, s) : launch_t<bf16, 128>(a, s);
-  return a.head_dim == 64 ? launch_t<float, 64>(a, s) : launch_t<float, 128>(a, s);
+  // bf16, head_dim 128, windows up to 128, groups of 8k heads: dq and dk/dv on the
+  // matrix cores (backward_mfma.hip); delta and dsink stay here
+  const bool mfma = backward_mfma_supported(a, bf16_io);
+  if (bf16_io) return a.head_dim == 64 ? launch_t<bf16, 64>(a, false, s) : launch_t<bf16, 128>(a, mfma, s);
+  return a.head_dim == 64 ? launch_t<float, 64>(a, false, s) : launch_t<float, 128>(a, false, s);
 }
 
 }  // namespace swa

@@ -19,8 +19,12 @@ hipError_t launch_online_mfma(const PrefillArgs& a, hipStream_t s);
 // Ring decode, window 128, 1 <= T <= 4.
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
 
-// Backward (gradients of O): the four kernels of backward.hip, in stream order.
+// Backward (gradients of O): delta, dq, dk/dv, dsink in stream order.
 hipError_t launch_backward(const BackwardArgs& a, bool bf16_io, hipStream_t s);
+// Matrix-core dq and dk/dv (bf16, head_dim 128, window <= 128, groups of 8k heads);
+// needs delta in the workspace.
+bool backward_mfma_supported(const BackwardArgs& a, bool bf16_io);
+hipError_t launch_backward_mfma(const BackwardArgs& a, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 hipError_t device_cu_count(int* out);

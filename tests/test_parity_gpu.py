@@ -637,6 +637,12 @@ BACKWARD_CASES = [
     ([150, 3], 4, 2, 128, "f32", 50, True),
     ([200, 31], 16, 2, 128, "bf16", None, False),  # GA: no window, no sink
     ([0, 37, 0, 60, 0], 8, 1, 128, "bf16", 128, True),  # zero-length sequences
+    # matrix-core path (bf16, D128, groups of 8k heads, window <= 128)
+    ([7], 8, 1, 128, "bf16", 128, True),                 # one partial tile
+    ([5, 0, 33, 17, 1, 200, 64], 32, 2, 128, "bf16", 128, True),  # group 16, boundaries inside tiles
+    ([333], 8, 1, 128, "bf16", 1, True),                 # window 1: the diagonal only
+    ([260, 19], 16, 2, 128, "bf16", 100, False),         # no sink, window 100
+    ([129, 127, 16], 8, 1, 128, "bf16", 16, True),       # window of one key block
 ]
 
 
