@@ -9,11 +9,12 @@
 //   delta_i = dO_i . O_i,   da_ij = p_ij (dO_i . v_j - delta_i),
 //   dq_i = scale sum_j da_ij k_j,   dk_j = scale sum_i da_ij q_i,   dv_j = sum_i p_ij dO_i,
 //   dsink_h = -sum_i p_s(i) delta_i,
-// where dk and dv also sum over the query heads that share a KV head.  Four
-// kernels, one wavefront per row: (1) delta and the sink terms, (2) dq per query
-// row, (3) dk and dv per key row, (4) dsink per head by a fixed-order reduction
-// (deterministic: no atomics anywhere).  For bf16, head_dim 128, windows up to 128
-// and groups of 8k heads, the matrix-core kernels replace (2) and (3).
+// where dk and dv also sum over the query heads that share a KV head.  Kernels:
+// (1) delta and the sink terms, a few lanes per row; (2) dq per query row and (3) dk
+// and dv per key row, one wavefront per row; (4) dsink per head by a two-pass
+// fixed-order reduction (deterministic: no atomics anywhere).  For bf16, head_dim
+// 128, windows up to 128 and groups of 8k heads, the matrix-core kernels replace
+// (2) and (3).
 #include "common.h"
 #include "kernels.h"
 
@@ -32,22 +33,48 @@ __device__ __forceinline__ int first_key(const BackwardArgs& a, int n) {
   return lw > start ? (int)lw : start;
 }
 
-// (1) delta = dO . O and the sink term exp(sink - lse) * delta of one (token, head) row.
+// (1) delta = dO . O and the sink term exp(sink - lse) * delta of each (token, head)
+// row: 16-byte loads, kLpr lanes per row, kPasses rows per lane in flight.
+constexpr int kPrepThreads = 256;
+constexpr int kPasses = 4;
 template <typename T, int D>
-__global__ __launch_bounds__(kRows * kWave) void bwd_prep_kernel(BackwardArgs a) {
-  const long row = (long)blockIdx.x * kRows + (threadIdx.x >> 6);
-  if (row >= (long)a.total_tokens * a.num_q_heads) return;
-  const int lane = threadIdx.x & (kWave - 1);
-  const T* o = static_cast<const T*>(a.out) + row * D;
-  const T* d_o = static_cast<const T*>(a.dout) + row * D;
-  float acc = 0.f;
+__global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BackwardArgs a) {
+  constexpr int kVec = 16 / sizeof(T);  // elements per 16-byte load
+  constexpr int kLpr = D / kVec;        // lanes per row (8 .. 32, a power of two)
+  constexpr int kRowsPerPass = kPrepThreads / kLpr;
+  const long nrows = (long)a.total_tokens * a.num_q_heads;
+  const int sub = threadIdx.x % kLpr;
+  const long row0 = (long)blockIdx.x * kRowsPerPass * kPasses + threadIdx.x / kLpr;
+  u32x4 ov[kPasses], dv[kPasses];
 #pragma unroll
-  for (int e = 0; e < D / kWave; ++e) acc = fmaf(ld(o + lane + e * kWave), ld(d_o + lane + e * kWave), acc);
-  const float delta = wave_sum(acc);
-  if (lane == 0) {
-    a.delta[row] = delta;
-    const int h = (int)(row % a.num_q_heads);
-    a.sink_term[row] = a.sinks ? expf(a.sinks[h] - a.lse[row]) * delta : 0.f;
+  for (int p = 0; p < kPasses; ++p) {
+    const long row = row0 + p * kRowsPerPass;
+    const long rr = row < nrows ? row : nrows - 1;  // every lane stays active for the shuffles
+    ov[p] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.out) + rr * D + sub * kVec);
+    dv[p] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dout) + rr * D + sub * kVec);
+  }
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    float acc = 0.f;
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8 o = __builtin_bit_cast(bf16x8, ov[p]), d = __builtin_bit_cast(bf16x8, dv[p]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)d[e], acc);
+    } else {
+      const f32x4 o = __builtin_bit_cast(f32x4, ov[p]), d = __builtin_bit_cast(f32x4, dv[p]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = fmaf(o[e], d[e], acc);
+    }
+#pragma unroll
+    for (int o = kLpr / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    const long row = row0 + p * kRowsPerPass;
+    if (sub == 0 && row < nrows) {
+      a.delta[row] = acc;
+      if (a.sinks) {
+        const int h = (int)(row % a.num_q_heads);
+        a.sink_term[row] = expf(a.sinks[h] - a.lse[row]) * acc;
+      }
+    }
   }
 }
 
@@ -181,14 +208,27 @@ __global__ __launch_bounds__(kRows * kWave) void bwd_dkdv_kernel(BackwardArgs a)
   }
 }
 
-// (4) dsink_h = -sum_n sink_term[n, h], one workgroup per head, fixed summation order.
+// (4) dsink_h = -sum_n sink_term[n, h] in a fixed order, in two passes: chunks of
+// kSinkChunk tokens summed per head (the sum replaces the chunk's first row, which
+// only the summing thread reads), then the chunk sums of each head by a tree.
+constexpr int kSinkChunk = 32;
 constexpr int kSinkThreads = 256;
+__global__ __launch_bounds__(kSinkThreads) void bwd_sink_chunk_kernel(BackwardArgs a) {
+  const int h = blockIdx.y * kSinkThreads + threadIdx.x;
+  if (h >= a.num_q_heads) return;
+  const long n0 = (long)blockIdx.x * kSinkChunk;
+  const long n1 = min(n0 + kSinkChunk, (long)a.total_tokens);
+  float acc = 0.f;
+  for (long n = n0; n < n1; ++n) acc += a.sink_term[n * a.num_q_heads + h];
+  a.sink_term[n0 * a.num_q_heads + h] = acc;
+}
 __global__ __launch_bounds__(kSinkThreads) void bwd_dsink_kernel(BackwardArgs a) {
   __shared__ float part[kSinkThreads];
   const int h = blockIdx.x;
+  const long nchunks = ((long)a.total_tokens + kSinkChunk - 1) / kSinkChunk;
   float acc = 0.f;
-  for (long n = threadIdx.x; n < a.total_tokens; n += kSinkThreads)
-    acc += a.sink_term[n * a.num_q_heads + h];
+  for (long c = threadIdx.x; c < nchunks; c += kSinkThreads)
+    acc += a.sink_term[c * kSinkChunk * a.num_q_heads + h];
   part[threadIdx.x] = acc;
   __syncthreads();
   for (int w = kSinkThreads / 2; w > 0; w >>= 1) {
@@ -203,9 +243,17 @@ hipError_t launch_t(const BackwardArgs& a, bool kMfma, hipStream_t s) {
   const long qrows = (long)a.total_tokens * a.num_q_heads;
   const long krows = (long)a.total_tokens * a.num_kv_heads;
   const long qblocks = (qrows + kRows - 1) / kRows, kblocks = (krows + kRows - 1) / kRows;
-  if (qblocks > 0x7fffffffL || kblocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const long prows = kPrepThreads / (D / (16 / (int)sizeof(T))) * kPasses;
+  const long pblocks = (qrows + prows - 1) / prows;
+  const long nchunks = ((long)a.total_tokens + kSinkChunk - 1) / kSinkChunk;
+  const long hgroups = (a.num_q_heads + kSinkThreads - 1) / kSinkThreads;
+  if (qblocks > 0x7fffffffL || kblocks > 0x7fffffffL || nchunks > 0x7fffffffL || hgroups > 0xffff)
+    return hipErrorInvalidConfiguration;
   if (qrows > 0) {  // an empty stream only writes zero sink gradients
-    hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)qblocks), dim3(kRows * kWave), 0, s, a);
+    hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)pblocks), dim3(kPrepThreads), 0, s, a);
+    if (a.dsinks != nullptr)
+      hipLaunchKernelGGL(bwd_sink_chunk_kernel, dim3((unsigned)nchunks, (unsigned)hgroups), dim3(kSinkThreads),
+                         0, s, a);
     if (kMfma) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;

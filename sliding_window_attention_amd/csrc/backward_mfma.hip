@@ -11,14 +11,15 @@
 //
 // Two kernels, both deterministic (no atomics):
 //  * bwd_dq_ring_kernel: the forward's decomposition -- a workgroup owns 16 query
-//    tokens x 8 heads sharing one KV head, the 144-key band sits in an LDS ring that
-//    advances by 16 keys per tile.  S^T = K Q^T and dP^T = V dO^T come out with
+//    tokens x 8 heads sharing one KV head (one head per wavefront), the 144-key band
+//    sits in an LDS ring that advances by 16 keys per tile.  S^T = K Q^T and dP^T = V dO^T come out with
 //    queries in columns, so dS^T feeds dQ^T = K^T dS^T straight from registers.
-//  * bwd_dkdv_kernel: the transpose -- a workgroup owns 16 keys of one KV head and
-//    walks the query blocks that see them (16 tokens x 2 heads per step and
-//    wavefront).  S = Q K^T and dP = dO V^T come out with queries in rows, so P and
-//    dS feed dV^T = dO^T P and dK^T = Q^T dS from registers; the four wavefronts'
-//    head partial sums are added in a fixed order through LDS.
+//  * bwd_dkdv_kernel: the transpose -- a workgroup owns 64 keys of one KV head (16
+//    per wavefront) and walks the (head pair, query block) steps that see them, one
+//    LDS-staged block of 16 tokens x 2 heads per step shared by the four wavefronts.
+//    S = Q K^T and dP = dO V^T come out with queries in rows, so P and dS feed
+//    dV^T = dO^T P and dK^T = Q^T dS from registers; each wavefront sums over all
+//    heads of the group itself.
 //
 // Both kernels keep their streamed operands in the chunk-plane layout of the
 // forward's K tiles and read it two ways: 16-byte row reads for the A operand of
@@ -38,7 +39,8 @@ using namespace tile;
 
 constexpr int kQT = 16;        // query tokens per dq tile
 constexpr int kHG = 8;         // query heads per dq workgroup
-constexpr int kThreads = 256;  // 4 wavefronts
+constexpr int kThreads = 256;  // 4 wavefronts (dk/dv)
+constexpr int kDqPerCu = 1;    // resident dq workgroups per compute unit
 
 // Byte offset (within a 64-byte-row plane buffer) of the 8 bytes lane (i, g) hands to
 // ds_read_b64_tr_b16 for row `row` holding token/key `key`, output block 0: quad
@@ -51,30 +53,35 @@ __device__ __forceinline__ int tr_at(int base, int b, int plane_bytes) {
   return (b >> 1) * plane_bytes + (base ^ (16 * (b & 1)));
 }
 
-// Store block pair (2p, 2p+1) of a gradient row held in the transposed-read output
-// layout: lane group g holds, in block b, head-dim 32 (b >> 1) + 8 (b & 1) +
-// 16 (g >> 1) + 4 (g & 1) + r.  v_permlane16_swap hands the even block to the even
-// group and the odd block to the odd group, so that every lane stores 8
-// consecutive elements.  All lanes must be active; the store itself is guarded.
-__device__ __forceinline__ void store_pair_tr(bf16* row, int g, int p, f32x4 e, f32x4 o, float mul,
-                                              bool ok) {
-  const bf16x2 e0 = __builtin_convertvector((f32x2){e[0] * mul, e[1] * mul}, bf16x2);
-  const bf16x2 e1 = __builtin_convertvector((f32x2){e[2] * mul, e[3] * mul}, bf16x2);
-  const bf16x2 o0 = __builtin_convertvector((f32x2){o[0] * mul, o[1] * mul}, bf16x2);
-  const bf16x2 o1 = __builtin_convertvector((f32x2){o[2] * mul, o[3] * mul}, bf16x2);
-  const auto r0 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, e0),
-                                                   __builtin_bit_cast(unsigned, o0), false, false);
-  const auto r1 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, e1),
-                                                   __builtin_bit_cast(unsigned, o1), false, false);
-  const u32x4 v = {(unsigned)r0[0], (unsigned)r1[0], (unsigned)r0[1], (unsigned)r1[1]};
-  if (ok) *reinterpret_cast<u32x4*>(row + 32 * p + 16 * (g >> 1) + 8 * (g & 1)) = v;
+// Store a gradient row held in the transposed-read output layout: lane group g holds,
+// in block b, head-dim 32 (b >> 1) + 8 (b & 1) + 16 (g >> 1) + 4 (g & 1) + r.
+// v_permlane16_swap hands, per block pair, the even block to the even group and the
+// odd block to the odd group, so that every lane stores 8 consecutive elements.
+// All lanes must be active; the stores themselves are guarded by ok.
+__device__ __forceinline__ void store_grad_row(bf16* row, int g, const f32x4 (&o)[8], float mul, bool ok) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const f32x4 e = o[2 * p], od = o[2 * p + 1];
+    const bf16x2 e0 = __builtin_convertvector((f32x2){e[0] * mul, e[1] * mul}, bf16x2);
+    const bf16x2 e1 = __builtin_convertvector((f32x2){e[2] * mul, e[3] * mul}, bf16x2);
+    const bf16x2 o0 = __builtin_convertvector((f32x2){od[0] * mul, od[1] * mul}, bf16x2);
+    const bf16x2 o1 = __builtin_convertvector((f32x2){od[2] * mul, od[3] * mul}, bf16x2);
+    const auto r0 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, e0),
+                                                     __builtin_bit_cast(unsigned, o0), false, false);
+    const auto r1 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, e1),
+                                                     __builtin_bit_cast(unsigned, o1), false, false);
+    const u32x4 v = {(unsigned)r0[0], (unsigned)r1[0], (unsigned)r0[1], (unsigned)r1[1]};
+    if (ok) *reinterpret_cast<u32x4*>(row + 32 * p + 16 * (g >> 1) + 8 * (g & 1)) = v;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// dq: ring of 144 keys, K and V both in the chunk-plane layout
+// dq: ring of 144 keys, K and V both in the chunk-plane layout; 8 wavefronts,
+// one query head each
 // ---------------------------------------------------------------------------
 namespace dqring {
 
+constexpr int kThreads = 512;
 constexpr int kSlots = 9;
 constexpr int kRows = 16 * kSlots;
 constexpr int kPlane = kRows * 64;
@@ -82,30 +89,36 @@ constexpr int kBytes = 4 * kPlane;  // 36864 per operand
 
 __device__ __forceinline__ int mod9(int x) { x %= kSlots; return x < 0 ? x + kSlots : x; }
 
-// Load the 144 keys of a tile whose first key is kbase into both rings.
+// Load the 144 keys of a tile whose first key is kbase into both rings (32 rows per
+// pass of the 512 threads).
 __device__ __attribute__((noinline)) void fill(char* ks, char* vs, const bf16* __restrict__ k,
                                                const bf16* __restrict__ v, int kbase, int N, int hkv,
                                                int kvh) {
   const int t = threadIdx.x;
   const int r = t >> 4, u = t & 15;
   const int kblock0 = mod9(kbase >> 4);
-  u32x4 kr[kSlots], vr[kSlots];
+  constexpr int kPasses = (kRows + 31) / 32;
+  u32x4 kr[kPasses], vr[kPasses];
 #pragma unroll
-  for (int j = 0; j < kSlots; ++j) {
-    const int key = kbase + 16 * j + r;
+  for (int j = 0; j < kPasses; ++j) {
+    const int row = 32 * j + r;
+    const int key = kbase + row;
     kr[j] = (u32x4){0, 0, 0, 0};
     vr[j] = (u32x4){0, 0, 0, 0};
-    if (key >= 0 && key < N) {
+    if (row < kRows && key >= 0 && key < N) {
       const size_t off = ((size_t)key * hkv + kvh) * D + u * 8;
       kr[j] = *reinterpret_cast<const u32x4*>(k + off);
       vr[j] = *reinterpret_cast<const u32x4*>(v + off);
     }
   }
 #pragma unroll
-  for (int j = 0; j < kSlots; ++j) {
-    const int phys = 16 * mod9(kblock0 + j) + r;
-    put_k(ks, kPlane, phys, kbase + 16 * j + r, u, kr[j]);
-    put_k(vs, kPlane, phys, kbase + 16 * j + r, u, vr[j]);
+  for (int j = 0; j < kPasses; ++j) {
+    const int row = 32 * j + r;
+    if (row < kRows) {
+      const int phys = 16 * mod9(kblock0 + (row >> 4)) + (row & 15);
+      put_k(ks, kPlane, phys, kbase + row, u, kr[j]);
+      put_k(vs, kPlane, phys, kbase + row, u, vr[j]);
+    }
   }
 }
 
@@ -120,7 +133,7 @@ __device__ __forceinline__ int find_seq_c(const_ptr<int32_t> cu, int num_seqs, i
   return lo;
 }
 
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_ring_kernel(BackwardArgs a, int items_per_wg) {
+__global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(BackwardArgs a, int items_per_wg) {
   using namespace dqring;
   __shared__ __attribute__((aligned(16))) char smem[2 * kBytes];
   char* ks = smem;
@@ -133,7 +146,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ring_kernel(BackwardArgs a
   const int item_end = min(item + items_per_wg, total);
   if (item >= item_end) return;
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // head w of the octet
   const int i = lane & 15, g = lane >> 4;
   const int t = threadIdx.x;
   const int G = Hq / hkv;
@@ -150,26 +163,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ring_kernel(BackwardArgs a
   const int vrow = 8 * (g & 1) + (i >> 2);                  // key row of the transposed reads, pairs
   const int vrow8 = 8 * (g & 1) + 4 * (g >> 1) + (i >> 2);  // the single diagonal block
 
-  // Q and dO of one tile (lane (i, g): head-dim 32cc + 8g .. +8 of query q0 + i, heads
-  // 2w and 2w + 1 of the octet), with the rows' lse (log2 units) and delta.
-  bf16x8 qa[4], qb[4], da[4], db[4];
-  float la, lb, dla, dlb;
+  // Q and dO of one tile (lane (i, g): head-dim 32cc + 8g .. +8 of query q0 + i, head w
+  // of the octet) with the row's lse and delta.  Rows past the stream are loaded from
+  // the last token (their results are never stored), so the loads are unconditional
+  // and nothing waits for them before their first use.
+  bf16x8 qa[4], da[4];
+  float lr, dlr;
   auto load_rows = [&](int q0n, int octn) {
-    const int qi = q0n + i;
-    const bool ok = qi < N;
-    const size_t hr = (size_t)qi * Hq + octn * kHG + 2 * w;
+    const int qi = min(q0n + i, N - 1);
+    const size_t hr = (size_t)qi * Hq + octn * kHG + w;
     const size_t r0 = hr * D + 8 * g;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      qa[cc] = ok ? *reinterpret_cast<const bf16x8*>(qp + r0 + 32 * cc) : zero8();
-      qb[cc] = ok ? *reinterpret_cast<const bf16x8*>(qp + r0 + D + 32 * cc) : zero8();
-      da[cc] = ok ? *reinterpret_cast<const bf16x8*>(dop + r0 + 32 * cc) : zero8();
-      db[cc] = ok ? *reinterpret_cast<const bf16x8*>(dop + r0 + D + 32 * cc) : zero8();
+      qa[cc] = *reinterpret_cast<const bf16x8*>(qp + r0 + 32 * cc);
+      da[cc] = *reinterpret_cast<const bf16x8*>(dop + r0 + 32 * cc);
     }
-    la = ok ? a.lse[hr] * kLog2e : 0.f;
-    lb = ok ? a.lse[hr + 1] * kLog2e : 0.f;
-    dla = ok ? a.delta[hr] : 0.f;
-    dlb = ok ? a.delta[hr + 1] : 0.f;
+    lr = a.lse[hr];
+    dlr = a.delta[hr];
   };
 
   while (item < item_end) {
@@ -197,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ring_kernel(BackwardArgs a
       int sk[kSlots];
 #pragma unroll
       for (int j = 0; j < kSlots; ++j) sk[j] = 16 * 64 * slot(j);
-      const int h0 = oct * kHG + 2 * w;
+      const int h0 = oct * kHG + w;
 
       // ---- visible keys of each row: window and own-sequence start ----
       while (seq + 1 < S && cu[seq + 1] <= q0) ++seq;
@@ -209,15 +219,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ring_kernel(BackwardArgs a
       const int lo = lw > start ? (int)lw : start;
       const int rel_lo = lo - kbase;
       const unsigned span = (unsigned)(qi - kbase - rel_lo);
+      const float l2 = lr * kLog2e, dl = dlr;
 
       // ---- per 16-key block: S^T = K Q^T, dP^T = V dO^T, then dS^T in bf16 ----
-      bf16x8 sa[4], sb[4];
-      bf16x4 sa8, sb8;
+      bf16x8 sa[4];
+      bf16x4 sa8;
       {
         const int ko0 = pr0 * 64 + 16 * (g ^ kswz(16 * par + pr0)) - (i >= 8 ? 16 * 64 : 0);
         const int ko1 = pr1 * 64 + 16 * (g ^ kswz(16 * par + pr1)) - (i >= 8 ? 16 * 64 : 0);
         const int ko8 = p8 * 64 + 16 * (g ^ kswz(16 * par + p8));
-        f32x4 xa_prev, xb_prev;
+        f32x4 x_prev;
 #pragma unroll
         for (int bl = 0; bl < 9; ++bl) {
           int off;
@@ -227,45 +238,39 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ring_kernel(BackwardArgs a
           } else {
             off = sk[8] + ko8;
           }
-          f32x4 s0 = zero4, s1 = zero4, t0 = zero4, t1 = zero4;
+          f32x4 s0 = zero4, t0 = zero4;
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc) {
             const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + cc * kPlane + off);
             const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + cc * kPlane + off);
             s0 = mfma32(kf, qa[cc], s0);
-            s1 = mfma32(kf, qb[cc], s1);
             t0 = mfma32(vf, da[cc], t0);
-            t1 = mfma32(vf, db[cc], t1);
           }
-          f32x4 xa, xb;
+          f32x4 x;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int kr = bl < 8 ? 32 * (bl >> 1) + 8 * g + 4 * (bl & 1) + r
                                   : 128 + 8 * (g & 1) + 4 * (g >> 1) + r;
             const bool ok = (unsigned)(kr - rel_lo) <= span;
-            const float ea = fast_exp2(fmaf(s0[r], c, -la));
-            const float eb = fast_exp2(fmaf(s1[r], c, -lb));
-            xa[r] = (ok ? ea : 0.f) * (t0[r] - dla);
-            xb[r] = (ok ? eb : 0.f) * (t1[r] - dlb);
+            const float e = fast_exp2(fmaf(s0[r], c, -l2));
+            x[r] = (ok ? e : 0.f) * (t0[r] - dl);
           }
           if (bl == 8) {
-            sa8 = pack_quad(xa);
-            sb8 = pack_quad(xb);
+            sa8 = pack_quad(x);
           } else if (bl & 1) {
-            sa[bl >> 1] = pack_pair(xa_prev, xa);
-            sb[bl >> 1] = pack_pair(xb_prev, xb);
+            sa[bl >> 1] = pack_pair(x_prev, x);
           } else {
-            xa_prev = xa;
-            xb_prev = xb;
+            x_prev = x;
           }
         }
       }
 
-      // ---- prefetch for the next tile: its 16 newest K/V rows, its Q, dO, lse, delta ----
+      // ---- prefetch for the next tile: its 16 newest K/V rows (waves 0-3), its Q, dO,
+      // lse, delta ----
       const bool has_next = k + 1 < run_len;
       u32x4 pk = {0, 0, 0, 0}, pv = {0, 0, 0, 0};
       const int nkey = q0 + 16 + (t >> 4);
-      if (has_next && nkey < N) {
+      if (has_next && t < 256 && nkey < N) {
         const size_t off = ((size_t)nkey * hkv + kvh) * D + (t & 15) * 8;
         pk = *reinterpret_cast<const u32x4*>(kp + off);
         pv = *reinterpret_cast<const u32x4*>(vp + off);
@@ -273,15 +278,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ring_kernel(BackwardArgs a
       if (has_next) load_rows(q0 + kQT, oct);
 
       // ---- dQ^T = K^T dS^T: the diagonal block first (k = 16), then the four pairs ----
-      f32x4 o0[8], o1[8];
+      f32x4 o0[8];
       {
         const int b8 = sk[8] + tr_base(vrow8, 16 * par + vrow8, i);
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          const bf16x4 av = tr_read(ks, tr_at(b8, b, kPlane));
-          o0[b] = mfma16(av, sa8, zero4);
-          o1[b] = mfma16(av, sb8, zero4);
-        }
+        for (int b = 0; b < 8; ++b) o0[b] = mfma32_k16(tr_read(ks, tr_at(b8, b, kPlane)), sa8, zero4);
       }
       {
         // groups 0-1 read the pair's first block, 2-3 its second; key parity of each
@@ -297,7 +298,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ring_kernel(BackwardArgs a
             const bf16x4 hi4 = tr_read(ks, sbase + tr_at(bhi, b, kPlane));
             const bf16x8 av = (bf16x8){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
             o0[b] = mfma32(av, sa[p], o0[b]);
-            o1[b] = mfma32(av, sb[p], o1[b]);
           }
         }
       }
@@ -306,23 +306,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ring_kernel(BackwardArgs a
       // before the stores below are issued) ----
       if (has_next) {
         __syncthreads();
-        const int phys = 16 * kblock0 + (t >> 4);
-        put_k(ks, kPlane, phys, nkey, t & 15, pk);
-        put_k(vs, kPlane, phys, nkey, t & 15, pv);
+        if (t < 256) {
+          const int phys = 16 * kblock0 + (t >> 4);
+          put_k(ks, kPlane, phys, nkey, t & 15, pk);
+          put_k(vs, kPlane, phys, nkey, t & 15, pv);
+        }
         __syncthreads();
       }
       kblock0 = kblock0 == kSlots - 1 ? 0 : kblock0 + 1;
 
-      // ---- epilogue: dq rows of this tile ----
+      // ---- epilogue: the dq row of this tile ----
       __builtin_amdgcn_s_waitcnt(kVmcnt0);
       {
         const bool ok = qi < N;
-        bf16* out = static_cast<bf16*>(a.dq) + ((size_t)(ok ? qi : 0) * Hq + h0) * D;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          store_pair_tr(out, g, p, o0[2 * p], o0[2 * p + 1], a.scale, ok);
-          store_pair_tr(out + D, g, p, o1[2 * p], o1[2 * p + 1], a.scale, ok);
-        }
+        store_grad_row(static_cast<bf16*>(a.dq) + ((size_t)(ok ? qi : 0) * Hq + h0) * D, g, o0, a.scale, ok);
       }
     }
     item = run_end;
@@ -330,20 +327,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ring_kernel(BackwardArgs a
 }
 
 // ---------------------------------------------------------------------------
-// dk, dv: 16 keys per workgroup, query blocks of 16 tokens x 2 heads per step
+// dk, dv: 64 keys per workgroup (16 per wavefront), one shared query block of
+// 16 tokens x 2 heads per step
 // ---------------------------------------------------------------------------
 namespace kvtile {
 
 constexpr int kRows = 32;             // 16 tokens x 2 heads; row P = 16 * head_sel + token
 constexpr int kPlane = kRows * 64;    // 2048
 constexpr int kOpBytes = 4 * kPlane;  // 8192 per operand
-constexpr int kWaveBytes = 2 * kOpBytes + 2 * kRows * 4;  // Q, dO, lse, delta: 16640
+constexpr int kStage = 2 * kOpBytes + 2 * kRows * 4;  // Q, dO, lse, delta: 16640
+constexpr int kTiles = 4;             // 16-key tiles per workgroup, one per wavefront
 
 }  // namespace kvtile
 
-__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, int nkt) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, int ngrp) {
   using namespace kvtile;
-  __shared__ __attribute__((aligned(16))) char smem[4 * kWaveBytes];
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];  // double-buffered step
 
   // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous range
   // of key tiles so that the query blocks shared by neighbouring tiles are read
@@ -351,23 +350,36 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
   const int nwg = gridDim.x, bid = blockIdx.x;
   const int xcd = bid & 7, per = nwg >> 3, rem = nwg & 7;
   const int L = xcd * per + min(xcd, rem) + (bid >> 3);
-  const int kvh = L / nkt, kt = L - kvh * nkt;
+  const int kvh = L / ngrp, grp = L - kvh * ngrp;
 
   const int N = a.total_tokens, Hq = a.num_q_heads, hkv = a.num_kv_heads;
   const int G = Hq / hkv;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int i = lane & 15, g = lane >> 4;
-  char* qs = smem + w * kWaveBytes;
-  char* ds = qs + kOpBytes;
-  float* ls = reinterpret_cast<float*>(ds + kOpBytes);
-  float* dls = ls + kRows;
   const bf16* qp = static_cast<const bf16*>(a.q);
   const bf16* dop = static_cast<const bf16*>(a.dout);
   const float c = a.scale * kLog2e;
+  const const_ptr<int32_t> cu = as_const(a.cu_seqlens);
 
-  // K and V of the tile as B operands: lane (i, g) holds key k0 + i, head-dim 32cc + 8g ..
-  const int k0 = kt * 16;
+  // Last query that sees key jj: within the window and the key's own sequence (the
+  // largest s with cu[s] <= jj, so zero-length sequences are stepped over).
+  auto last_query = [&](int jj) {
+    int lo = 0, hi = a.num_seqs;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cu[mid] <= jj) lo = mid; else hi = mid;
+    }
+    const long lw = (long)jj + a.window - 1;
+    const long end = cu[lo + 1];
+    return (int)(lw < end - 1 ? lw : end - 1);
+  };
+
+  // This wavefront's keys, K and V as B operands: lane (i, g) holds key k0 + i,
+  // head-dim 32cc + 8g ..
+  const int kt0 = kTiles * grp;
+  const int k0 = 16 * (kt0 + w);
   const int j = k0 + i;
   const bool kvalid = j < N;
   bf16x8 kb[4], vb[4];
@@ -381,26 +393,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
       vb[cc] = kvalid ? *reinterpret_cast<const bf16x8*>(vp + r0 + 32 * cc) : zero8();
     }
   }
-  // Last query that sees key j: within the window and the key's own sequence (the
-  // largest s with cu[s] <= j, so zero-length sequences are stepped over).
-  int last = -1;
-  if (kvalid) {
-    int lo = 0, hi = a.num_seqs;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.cu_seqlens[mid] <= j) lo = mid; else hi = mid;
-    }
-    const int end = a.cu_seqlens[lo + 1];
-    const long lw = (long)j + a.window - 1;
-    last = (int)(lw < end - 1 ? lw : end - 1);
-  }
+  const int last = kvalid ? last_query(j) : -1;
   // query q sees key j iff (unsigned)(q - jm) <= span; invalid keys see nothing
   const int jm = kvalid ? j : 0x3fffffff;
   const unsigned span = kvalid ? (unsigned)(last - j) : 0u;
-  int qmax = last;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) qmax = max(qmax, __shfl_xor(qmax, o));
-  const int tb_lo = kt, tb_hi = __builtin_amdgcn_readfirstlane(qmax) >> 4;
+  // query blocks this wavefront works on (none if it has no valid key), and the
+  // workgroup's: last_query is nondecreasing in the key, so the workgroup's last
+  // valid key bounds them all
+  const int wlast = k0 < N ? last_query(min(k0 + 15, N - 1)) : -1;
+  const int tbw_lo = k0 >> 4, tbw_hi = wlast >> 4;
+  const int tb_lo = kt0;
+  const int tb_hi = last_query(min(16 * (kt0 + kTiles) - 1, N - 1)) >> 4;
+  const int nsteps = tb_hi - tb_lo + 1;
+  const int total = (G / 2) * nsteps;  // (head pair, query block) steps
 
   // Lane-constant LDS offsets: row reads (pair order) and transposed reads.
   const int pr0 = pair_row(i, 0), pr1 = pair_row(i, 1);
@@ -408,8 +413,46 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
   const int ro1 = pr1 * 64 + 16 * (g ^ kswz(pr1));
   const int tlo = tr_base(8 * g + (i >> 2), 8 * g + (i >> 2), i);
   const int thi = tr_base(8 * g + 4 + (i >> 2), 8 * g + 4 + (i >> 2), i);
-  // staging map: piece it (0..7) of lane l is row P = 16 (it >> 2) + 4 (it & 3) + (l >> 4), unit l & 15
-  const int su = lane & 15;
+
+  // Staging: thread t moves unit t & 15 of token row t >> 4 of both heads, Q and dO;
+  // threads 0-31 move the lse and delta of row P = t.  Two register sets: the loads
+  // of step s + 2 are issued at the start of step s, so they have two steps to land.
+  struct Stage {
+    u32x4 q[2], d[2];
+    float l, dl;
+  };
+  Stage sa, sb;
+  auto prefetch = [&](int step, Stage& st) {
+    const int hp = step / nsteps, tb = tb_lo + (step - hp * nsteps);
+    const int hbase = kvh * G + 2 * hp;
+    const int q = min(16 * tb + (t >> 4), N - 1);
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      const size_t off = ((size_t)q * Hq + hbase + hs) * D + 8 * (t & 15);
+      st.q[hs] = *reinterpret_cast<const u32x4*>(qp + off);
+      st.d[hs] = *reinterpret_cast<const u32x4*>(dop + off);
+    }
+    // every thread loads (threads 32.. duplicate 0..31) and nothing is computed on the
+    // values here: a branch or an early use would make the compiler wait for the load
+    const size_t r = (size_t)min(16 * tb + (t & 15), N - 1) * Hq + hbase + ((t >> 4) & 1);
+    st.l = a.lse[r];
+    st.dl = a.delta[r];
+  };
+  auto commit = [&](int buf, const Stage& st) {
+    char* qs = smem + buf * kStage;
+    char* ds = qs + kOpBytes;
+    float* ls = reinterpret_cast<float*>(ds + kOpBytes);
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      const int P = 16 * hs + (t >> 4);
+      put_k(qs, kPlane, P, P, t & 15, st.q[hs]);
+      put_k(ds, kPlane, P, P, t & 15, st.d[hs]);
+    }
+    if (t < kRows) {
+      ls[t] = st.l * kLog2e;
+      ls[kRows + t] = st.dl;
+    }
+  };
 
   f32x4 dk[8], dv[8];
 #pragma unroll
@@ -418,65 +461,35 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
     dv[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  const int npairs = G / 2;
-  for (int hp = w; hp < npairs; hp += 4) {
-    const int hbase = kvh * G + 2 * hp;
-    u32x4 pq[8], pd[8];
-    float pl = 0.f, pdl = 0.f;
-    auto prefetch = [&](int tb) {
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int tok = 4 * (it & 3) + (lane >> 4);
-        const int q = min(16 * tb + tok, N - 1);
-        const size_t off = ((size_t)q * Hq + hbase + (it >> 2)) * D + 8 * su;
-        pq[it] = *reinterpret_cast<const u32x4*>(qp + off);
-        pd[it] = *reinterpret_cast<const u32x4*>(dop + off);
-      }
-      if (lane < kRows) {
-        const int q = min(16 * tb + (lane & 15), N - 1);
-        const size_t r = (size_t)q * Hq + hbase + (lane >> 4);
-        pl = a.lse[r] * kLog2e;
-        pdl = a.delta[r];
-      }
-    };
-    prefetch(tb_lo);
-    for (int tb = tb_lo; tb <= tb_hi; ++tb) {
-      // ---- commit the staged block (the previous step's reads are complete: their
-      // values were consumed by the matrix products) ----
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int P = 16 * (it >> 2) + 4 * (it & 3) + (lane >> 4);
-        put_k(qs, kPlane, P, P, su, pq[it]);
-        put_k(ds, kPlane, P, P, su, pd[it]);
-      }
-      if (lane < kRows) {
-        ls[lane] = pl;
-        dls[lane] = pdl;
-      }
-      __builtin_amdgcn_wave_barrier();
-      if (tb < tb_hi) prefetch(tb + 1);
-
+  // One step: `cur` held this step's block (already in LDS buffer step & 1) and now
+  // takes step + 2; `nxt` holds step + 1, committed to the other buffer at the end.
+  auto do_step = [&](int step, Stage& cur, Stage& nxt) {
+    if (step + 2 < total) prefetch(step + 2, cur);
+    const int tb = tb_lo + step % nsteps;
+    if (tb >= tbw_lo && tb <= tbw_hi) {
+      const char* qs = smem + (step & 1) * kStage;
+      const char* ds = qs + kOpBytes;
+      const float* ls = reinterpret_cast<const float*>(ds + kOpBytes);
       // ---- S = Q K^T and dP = dO V^T for the two 16-row blocks of the pair ----
-      f32x4 s[2], t[2];
+      f32x4 s[2], tt[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         s[h] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        t[h] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        tt[h] = (f32x4){0.f, 0.f, 0.f, 0.f};
         const int ro = h ? ro1 : ro0;
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
           const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qs + cc * kPlane + ro);
           const bf16x8 df = *reinterpret_cast<const bf16x8*>(ds + cc * kPlane + ro);
           s[h] = mfma32(qf, kb[cc], s[h]);
-          t[h] = mfma32(df, vb[cc], t[h]);
+          tt[h] = mfma32(df, vb[cc], tt[h]);
         }
       }
       // lane (i, g) holds rows P = 8g + 4h + r: token 8 (g & 1) + 4h + r of head g >> 1
       const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls + 8 * g);
       const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + 8 * g + 4);
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(dls + 8 * g);
-      const f32x4 d1 = *reinterpret_cast<const f32x4*>(dls + 8 * g + 4);
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(ls + kRows + 8 * g);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(ls + kRows + 8 * g + 4);
       f32x4 p[2], x[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -486,7 +499,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
           const bool ok = (unsigned)(q - jm) <= span;
           const float e = fast_exp2(fmaf(s[h][r], c, -(h ? l1[r] : l0[r])));
           p[h][r] = ok ? e : 0.f;
-          x[h][r] = p[h][r] * (t[h][r] - (h ? d1[r] : d0[r]));
+          x[h][r] = p[h][r] * (tt[h][r] - (h ? d1[r] : d0[r]));
         }
       }
       const bf16x8 pp = pack_pair(p[0], p[1]);
@@ -503,37 +516,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
         dk[b] = mfma32((bf16x8){qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]}, xp, dk[b]);
       }
     }
+    // the other buffer was last read in the previous step, which every wavefront has
+    // finished (barrier below)
+    if (step + 1 < total) commit((step + 1) & 1, nxt);
+    __syncthreads();
+  };
+
+  prefetch(0, sa);
+  if (1 < total) prefetch(1, sb);
+  commit(0, sa);
+  __syncthreads();
+  for (int step = 0; step < total; step += 2) {
+    do_step(step, sa, sb);
+    if (step + 1 < total) do_step(step + 1, sb, sa);
   }
 
-  // ---- sum the four wavefronts' partial sums in a fixed order and store ----
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(smem + w * kWaveBytes);  // 64 registers x 64 lanes
-#pragma unroll
-  for (int b = 0; b < 8; ++b)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      red[(4 * b + r) * 64 + lane] = dk[b][r];
-      red[(32 + 4 * b + r) * 64 + lane] = dv[b][r];
-    }
-  __syncthreads();
-  // wavefront w adds registers 16w .. 16w + 15: dk blocks 0-3 / 4-7, dv blocks 0-3 / 4-7
-  f32x4 sum[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int reg = 16 * w + 4 * kk + r;
-      float acc = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww)
-        acc += reinterpret_cast<const float*>(smem + ww * kWaveBytes)[reg * 64 + lane];
-      sum[kk][r] = acc;
-    }
-  bf16* dst = static_cast<bf16*>(w < 2 ? a.dk : a.dv) + ((size_t)(kvalid ? j : 0) * hkv + kvh) * D;
-  const float mul = w < 2 ? a.scale : 1.f;
-  const int p0 = 2 * (w & 1);
-  store_pair_tr(dst, g, p0, sum[0], sum[1], mul, kvalid);
-  store_pair_tr(dst, g, p0 + 1, sum[2], sum[3], mul, kvalid);
+  const size_t krow = ((size_t)(kvalid ? j : 0) * hkv + kvh) * D;
+  store_grad_row(static_cast<bf16*>(a.dk) + krow, g, dk, a.scale, kvalid);
+  store_grad_row(static_cast<bf16*>(a.dv) + krow, g, dv, 1.f, kvalid);
 }
 
 }  // namespace
@@ -552,13 +552,17 @@ hipError_t launch_backward_mfma(const BackwardArgs& a, hipStream_t s) {
   int cus = 0;
   hipError_t e = device_cu_count(&cus);
   if (e != hipSuccess) return e;
-  const long slots = 2L * cus;
+  // one resident 8-wavefront workgroup per compute unit (register-bound), each
+  // walking a contiguous run of tiles
+  const long slots = kDqPerCu * cus;
   const long per = (total + slots - 1) / slots;
   const long grid = (total + per - 1) / per;
-  hipLaunchKernelGGL(bwd_dq_ring_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a, (int)per);
+  hipLaunchKernelGGL(bwd_dq_ring_kernel, dim3((unsigned)grid), dim3(dqring::kThreads), 0, s, a, (int)per);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kvtiles), dim3(kThreads), 0, s, a, (int)ntiles);
+  const long ngrp = (ntiles + kvtile::kTiles - 1) / kvtile::kTiles;
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(ngrp * a.num_kv_heads)), dim3(kThreads), 0, s, a,
+                     (int)ngrp);
   return hipGetLastError();
 }
 

@@ -270,7 +270,7 @@ void decode_kernel(DecodeArgs a) {
     for (int bb = 0; bb < 8; ++bb) {
       const bf16x4 av = column4(vrn, bb);
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) o[tt][bb] = mfma16(av, pack_quad(sn[tt]), o[tt][bb]);
+      for (int tt = 0; tt < NT; ++tt) o[tt][bb] = mfma32_k16(av, pack_quad(sn[tt]), o[tt][bb]);
     }
   }
   // ---- merge the four partials (they share the column maxima, so they add):

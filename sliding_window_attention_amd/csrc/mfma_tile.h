@@ -33,8 +33,14 @@ __device__ __forceinline__ int pair_row(int row, int s) { return 8 * (row >> 2) 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+// A k=16 product (four k-slots per lane group) issued as the k=32 instruction with
+// the other four k-slots zero in both operands.  Every accumulation chain then uses
+// a single MFMA shape: a 16x16x16 result taken as the accumulator of a 16x16x32
+// one wait state later has produced stale rows 2-3 on gfx950, and the compiler
+// does not pad that dependency.
+__device__ __forceinline__ f32x4 mfma32_k16(bf16x4 a, bf16x4 b, f32x4 c) {
+  const bf16 z = (bf16)0.f;
+  return mfma32((bf16x8){a[0], a[1], a[2], a[3], z, z, z, z}, (bf16x8){b[0], b[1], b[2], b[3], z, z, z, z}, c);
 }
 
 __device__ __forceinline__ bf16x8 zero8() {

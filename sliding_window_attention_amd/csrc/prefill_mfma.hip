@@ -264,8 +264,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
           const bf16x4 av = tr_read(vs, vb8 + 2 * (32 * (b >> 2) + 4 * (b & 3)));
-          o0[b] = mfma16(av, pa8, zero4);
-          o1[b] = mfma16(av, pb8, zero4);
+          o0[b] = mfma32_k16(av, pa8, zero4);
+          o1[b] = mfma32_k16(av, pb8, zero4);
         }
       }
 #pragma unroll
