@@ -24,6 +24,16 @@ the prose of that section and of the MiMo-V2 blog, section 2.2):
 Decode against an FP8 ring (swa_sink_decode_fp8kv) is the same decode on caches
 dequantised exactly (E4M3 code value times a per-tensor scale).
 
+RoPE around decode (swa_rope, swa_sink_decode_rope, swa_ring_append_rope): the
+rotary position embedding with a per-layer base (10,000 in SWA layers, 640,000 in
+GA layers, raised to 5,000,000 for the 256K stage: MiMo-V2-Flash Technical Report
+digest, section 3.1; the positions keep increasing as the window slides, ICML 2026
+keynote write-up, section 06).  The pages give neither the pairing nor the
+frequencies; the reading here is the common rotate-half form (element i pairs with
+i + D/2, inverse frequency base^(-2i/D), angle = position times frequency), and
+rotated vectors are rounded to the I/O type, as a separate rotation pass that
+stores its result would.
+
 Arithmetic is fp64 on the exact input values (bf16, fp32 and E4M3 convert to fp64
 exactly).  Rows are processed in blocks only to bound memory: every row is the
 definition above, computed independently, with no online rescaling and no
@@ -318,3 +328,83 @@ def hybrid_block(layers, window=128, scale=None):
             out.append(swa_sink_prefill(lay["q"], lay["k"], lay["v"], lay["sinks"],
                                         lay["cu_seqlens"], window, scale))
     return out
+
+
+def rope(x, positions, base):
+    """Rotary position embedding of x [R, H, D] (or [R, D]) with row r at integer
+    position positions[r], in fp64: for i < D/2, angle = positions[r] * base^(-2i/D),
+        y[i]       = x[i] cos(angle) - x[i + D/2] sin(angle)
+        y[i + D/2] = x[i + D/2] cos(angle) + x[i] sin(angle).
+    """
+    x = _as_f64(x)
+    d = x.shape[-1]
+    if d % 2:
+        raise ValueError("head_dim must be even")
+    half = d // 2
+    inv_freq = float(base) ** (-2.0 * np.arange(half) / d)                 # [D/2]
+    ang = np.asarray(positions, dtype=np.float64).reshape(-1)[:, None] * inv_freq[None, :]  # [R, D/2]
+    shape = (x.shape[0],) + (1,) * (x.ndim - 2) + (half,)
+    c, s_ = np.cos(ang).reshape(shape), np.sin(ang).reshape(shape)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s_, x2 * c + x1 * s_], axis=-1)
+
+
+def round_to(x, io_dtype):
+    """Round fp64 values to the I/O type ("bf16": round to nearest even through
+    torch's conversion; "f32": numpy's float32 cast; None: no rounding)."""
+    x = np.asarray(x, dtype=np.float64)
+    if io_dtype is None:
+        return x
+    if io_dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    import torch
+
+    return torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def swa_sink_decode_rope(q, k_new, v_new, k_cache, v_cache, ring_head, positions, sinks, rope_base,
+                         window=128, scale=None, io_dtype="bf16"):
+    """Decode / MTP verify with the rotary embedding applied to the query tokens and
+    the new keys first.  q [B, T, Hq, D] and k_new [B, T, Hkv, D] arrive unrotated;
+    new token t of sequence b sits at position positions[b] + t.  The ring holds
+    keys already rotated at their own positions.  Rotated q and k_new are rounded to
+    io_dtype, then this is swa_sink_decode."""
+    q, k_new = _as_f64(q), _as_f64(k_new)
+    bsz, t_new = q.shape[:2]
+    pos = np.asarray(positions, dtype=np.int64).reshape(bsz)[:, None] + np.arange(t_new)[None, :]
+    qr = round_to(rope(q.reshape((bsz * t_new,) + q.shape[2:]), pos.reshape(-1), rope_base), io_dtype)
+    kr = round_to(rope(k_new.reshape((bsz * t_new,) + k_new.shape[2:]), pos.reshape(-1), rope_base),
+                  io_dtype)
+    return swa_sink_decode(qr.reshape(q.shape), kr.reshape(k_new.shape), v_new, k_cache, v_cache,
+                           ring_head, sinks, window=window, scale=scale)
+
+
+def swa_ring_append_rope(k_new, v_new, n_accept, positions, k_cache, v_cache, ring_head, rope_base,
+                         io_dtype="bf16"):
+    """Commit the first n_accept[b] of the T new tokens of each sequence to its ring
+    (the accepted MTP tokens; rejected drafts never enter the cache).  Appending n
+    tokens evicts the n oldest: accepted token t goes to physical slot
+    (ring_head[b] + t) mod W, its key rotated at position positions[b] + t and
+    rounded to io_dtype, its value copied; the head then advances by n.  Returns
+    (k_cache, v_cache, ring_head) as new arrays."""
+    k_new, v_new = _as_f64(k_new), _as_f64(v_new)
+    kc, vc = _as_f64(k_cache).copy(), _as_f64(v_cache).copy()
+    bsz, t_new = k_new.shape[:2]
+    w = kc.shape[2]
+    heads = np.asarray(_as_f64(ring_head), dtype=np.int64).reshape(bsz) % w
+    n_acc = np.asarray(n_accept, dtype=np.int64).reshape(bsz)
+    pos = np.asarray(positions, dtype=np.int64).reshape(bsz)
+    new_heads = heads.copy()
+    for b in range(bsz):
+        n = int(n_acc[b])
+        if n < 0 or n > t_new:
+            raise ValueError("n_accept out of range")
+        if n == 0:
+            continue
+        kr = round_to(rope(k_new[b, :n], pos[b] + np.arange(n), rope_base), io_dtype)  # [n, Hkv, D]
+        for t in range(n):
+            slot = (heads[b] + t) % w
+            kc[b, :, slot, :] = kr[t]
+            vc[b, :, slot, :] = v_new[b, t]
+        new_heads[b] = (heads[b] + n) % w
+    return kc, vc, new_heads

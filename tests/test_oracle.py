@@ -513,3 +513,140 @@ def test_backward_shift_invariance_and_gqa():
         delta = (do[:, h] * o[:, h]).sum(axis=1)
         logit_grad_sum = (np.exp(s[h] - lse[:, h]) * delta).sum()
         assert abs(logit_grad_sum + ds[h]) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# RoPE around decode: rotation, decode with rotated inputs, ring append
+# (bases: Technical Report digest, section 3.1; rotate-half reading)
+# ---------------------------------------------------------------------------
+
+def test_rope_hand_values():
+    from tests.golden.load import load
+
+    fx = load("rope_hand.json")
+    for c in fx["cases"]:
+        y = orc.rope(np.array([c["x"]], dtype=np.float64), [c["pos"]], fx["base"])[0]
+        np.testing.assert_allclose(y, c["y"], rtol=0, atol=1e-15, err_msg=c["why"])
+
+
+def test_rope_equals_complex_rotation():
+    """Pairs (i, i + D/2) as complex numbers x_i + j x_{i+D/2}, multiplied by
+    exp(j * pos * base^(-2i/D)) with numpy's complex arithmetic."""
+    rng = np.random.default_rng(7)
+    for base in (10000.0, 640000.0, 5e6):
+        x = rng.standard_normal((6, 3, 16))
+        pos = np.array([0, 1, 7, 128, 4095, 262143])
+        z = x[..., :8] + 1j * x[..., 8:]
+        freq = base ** (-2.0 * np.arange(8) / 16)
+        z = z * np.exp(1j * pos[:, None, None] * freq[None, None, :])
+        np.testing.assert_allclose(orc.rope(x, pos, base), np.concatenate([z.real, z.imag], axis=-1),
+                                   rtol=0, atol=1e-12)
+
+
+def test_rope_invariants():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((5, 2, 32))
+    pos = np.array([0, 3, 99, 1000, 70000])
+    y = orc.rope(x, pos, 10000.0)
+    # position 0 is the identity; each pair keeps its length
+    np.testing.assert_array_equal(y[0], x[0])
+    np.testing.assert_allclose(y[..., :16] ** 2 + y[..., 16:] ** 2, x[..., :16] ** 2 + x[..., 16:] ** 2,
+                               rtol=1e-12)
+    # composition: rotating by a then by b is rotating by a + b
+    np.testing.assert_allclose(orc.rope(orc.rope(x, pos, 10000.0), pos + 5, 10000.0),
+                               orc.rope(x, 2 * pos + 5, 10000.0), atol=1e-9)
+    # relative positions: <rope(q, m), rope(k, n)> = <rope(q, m - n), k>
+    q, k = rng.standard_normal(32), rng.standard_normal(32)
+    for m, n in ((5, 2), (300, 299), (1000, 17)):
+        lhs = orc.rope(q[None], [m], 640000.0)[0] @ orc.rope(k[None], [n], 640000.0)[0]
+        rhs = orc.rope(q[None], [m - n], 640000.0)[0] @ k
+        assert abs(lhs - rhs) < 1e-10, (m, n, lhs, rhs)
+
+
+def _rope_decode_case(bsz, t_new, hq, hkv, d, w, seed, start):
+    """Raw (unrotated) keys of a sequence's last w tokens plus T new tokens, the ring
+    built by rotating each cached key at its own position."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((bsz, t_new, hq, d))
+    kn = rng.standard_normal((bsz, t_new, hkv, d))
+    vn = rng.standard_normal((bsz, t_new, hkv, d))
+    k_raw = rng.standard_normal((bsz, w, hkv, d))  # logical order, oldest first
+    v_ring = rng.standard_normal((bsz, hkv, w, d))
+    heads = rng.integers(0, w, size=bsz)
+    sinks = rng.standard_normal(hq)
+    return q, kn, vn, k_raw, v_ring, heads, sinks
+
+
+def _ring_from_raw(k_raw, heads, pos0, base, io_dtype):
+    bsz, w, hkv, d = k_raw.shape
+    kc = np.zeros((bsz, hkv, w, d))
+    for b in range(bsz):
+        rot = orc.round_to(orc.rope(k_raw[b], pos0[b] - w + np.arange(w), base), io_dtype)  # [w, hkv, d]
+        for l in range(w):
+            kc[b, :, (heads[b] + l) % w, :] = rot[l]
+    return kc
+
+
+def test_decode_rope_depends_on_relative_positions_only():
+    """Shifting every position (cached and new) leaves the decode unchanged: the
+    rotation of q and of the new keys agrees with the ring's."""
+    q, kn, vn, k_raw, v_ring, heads, sinks = _rope_decode_case(2, 3, 4, 2, 16, 8, 11, 0)
+    outs = []
+    for shift in (8, 1000, 123457):
+        pos0 = np.array([shift, shift + 40])
+        kc = _ring_from_raw(k_raw, heads, pos0, 10000.0, None)
+        o, lse = orc.swa_sink_decode_rope(q, kn, vn, kc, v_ring, heads, pos0, sinks, 10000.0, window=8,
+                                          io_dtype=None)
+        outs.append((o, lse))
+    for o, lse in outs[1:]:
+        np.testing.assert_allclose(o, outs[0][0], atol=1e-9)
+        np.testing.assert_allclose(lse, outs[0][1], atol=1e-9)
+
+
+def test_decode_rope_equals_prefill_on_rotated_stream():
+    """A ring whose keys were rotated at positions p-W..p-1, plus new tokens at p..p+T-1,
+    decodes like the windowed prefill of the whole rotated stream (sink included)."""
+    q, kn, vn, k_raw, v_ring, heads, sinks = _rope_decode_case(1, 2, 2, 1, 8, 6, 12, 0)
+    p = 50
+    kc = _ring_from_raw(k_raw, heads, np.array([p]), 10000.0, None)
+    o, lse = orc.swa_sink_decode_rope(q, kn, vn, kc, v_ring, heads, [p], sinks, 10000.0, window=6,
+                                      io_dtype=None)
+    w, t = 6, 2
+    pos = np.arange(p - w, p + t)
+    kstream = np.concatenate([k_raw[0], kn[0]], axis=0)                     # [w + t, hkv, d] raw
+    vlog = orc.ring_logical_order(v_ring[0], heads[0], w).transpose(1, 0, 2)
+    vstream = np.concatenate([vlog, vn[0]], axis=0)
+    qstream = np.zeros((w + t,) + q.shape[2:])
+    qstream[w:] = q[0]
+    qr, kr = orc.rope(qstream, pos, 10000.0), orc.rope(kstream, pos, 10000.0)
+    o2, l2 = brute.attention(qr.tolist(), kr.tolist(), vstream.tolist(), sinks.tolist(), [0, w + t], w)
+    np.testing.assert_allclose(o[0], np.asarray(o2)[w:], atol=1e-12)
+    np.testing.assert_allclose(lse[0], np.asarray(l2)[w:], atol=1e-12)
+
+
+def test_ring_append_matches_a_list_model():
+    """The ring after appending equals the last W tokens of (logical ring ++ accepted
+    tokens), tracked with a Python list: eviction order, slots, head and rejected drafts."""
+    rng = np.random.default_rng(13)
+    bsz, t_new, hkv, d, w = 4, 4, 2, 8, 6
+    kc = rng.standard_normal((bsz, hkv, w, d))
+    vc = rng.standard_normal((bsz, hkv, w, d))
+    heads = np.array([0, 5, 3, 2])
+    kn = rng.standard_normal((bsz, t_new, hkv, d))
+    vn = rng.standard_normal((bsz, t_new, hkv, d))
+    n_acc = np.array([0, 1, 4, 3])
+    pos = np.array([10, 0, 77, 123456])
+    k2, v2, h2 = orc.swa_ring_append_rope(kn, vn, n_acc, pos, kc, vc, heads, 10000.0, io_dtype=None)
+    for b in range(bsz):
+        klist = [kc[b, :, (heads[b] + l) % w, :] for l in range(w)]
+        vlist = [vc[b, :, (heads[b] + l) % w, :] for l in range(w)]
+        for t in range(n_acc[b]):
+            klist.append(orc.rope(kn[b, t][None], [pos[b] + t], 10000.0)[0])
+            vlist.append(vn[b, t])
+        klist, vlist = klist[-w:], vlist[-w:]
+        assert h2[b] == (heads[b] + n_acc[b]) % w
+        for l in range(w):
+            np.testing.assert_array_equal(k2[b, :, (h2[b] + l) % w, :], klist[l])
+            np.testing.assert_array_equal(v2[b, :, (h2[b] + l) % w, :], vlist[l])
+    # inputs are untouched (new arrays returned)
+    assert not np.shares_memory(k2, kc)
