@@ -57,7 +57,7 @@ typedef enum {
 
 typedef enum { SWA_DTYPE_F32 = 0, SWA_DTYPE_BF16 = 1 } swa_dtype;
 
-#define SWASINK_ABI_VERSION 3
+#define SWASINK_ABI_VERSION 4
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SWASINK_API __attribute__((visibility("default")))
@@ -180,6 +180,65 @@ SWASINK_API int swa_sink_prefill_backward(const void* q, const void* k, const vo
 
 /* Bytes of workspace swa_sink_prefill_backward needs (-1 for invalid sizes). */
 SWASINK_API int64_t swa_sink_prefill_backward_workspace(int32_t total_tokens, int32_t num_q_heads);
+
+/*
+ * Rotary position embedding (RoPE), in place.  Bases: 10,000 in SWA layers, 640,000
+ * in GA layers and 5,000,000 for GA after the 256K extension (technical report digest,
+ * section 3.1); positions keep increasing as the window slides (ICML keynote write-up,
+ * section 06).  Rotate-half pairing: for i < head_dim/2, angle = position *
+ * rope_base^(-2i/head_dim),
+ *   y[i] = x[i] cos - x[i + D/2] sin,   y[i + D/2] = x[i + D/2] cos + x[i] sin,
+ * the angle formed and reduced in fp64, the rotation in fp32, rounded to dtype.
+ *
+ *  x          [rows, heads, head_dim] dtype, rotated in place (e.g. the q or k of a
+ *             prefill: rows = tokens)
+ *  positions  [rows] int32 device array: position of each row (any int32 value)
+ *  rope_base  host fp32, finite and >= 0; 0 leaves x unchanged (nothing is launched)
+ * rows == 0 is accepted (x and positions may then be NULL).
+ */
+SWASINK_API int swa_rope(void* x, const int32_t* positions, int32_t rows, int32_t heads,
+                    int32_t head_dim, float rope_base, swa_dtype dtype, void* stream);
+
+/*
+ * swa_sink_decode with the rotary embedding applied inside the kernel: q and k_new
+ * arrive unrotated, new token t of sequence b sits at position positions[b] + t, and
+ * both are rotated (as swa_rope would, rounded to dtype) before attending.  The ring
+ * holds keys already rotated at their own positions (swa_ring_append_rope writes
+ * them so).  Every other argument and the outputs are those of swa_sink_decode.
+ *
+ *  positions  [batch] int32 device array: position of new token 0 of each sequence
+ *  rope_base  host fp32, finite and >= 0; 0 means no rotation (swa_sink_decode)
+ */
+SWASINK_API int swa_sink_decode_rope(const void* q, const void* k_new, const void* v_new,
+                    const void* k_cache, const void* v_cache, const int32_t* ring_head,
+                    const int32_t* positions, const float* sinks, int32_t batch, int32_t T,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                    float scale, float rope_base, swa_dtype dtype, void* out, float* lse,
+                    void* stream);
+
+/*
+ * Commit the accepted tokens of a decode / MTP-verify step to the ring (the drafts the
+ * verification rejected never enter it).  For each sequence b, with n = n_accept[b]
+ * clamped to [0, T] and h = ring_head[b] reduced modulo window: accepted token t < n
+ * is written to physical slot (h + t) mod window (evicting the n oldest), its key
+ * rotated at position positions[b] + t (as swa_rope, rounded to dtype) and its value
+ * copied; then ring_head[b] = (h + n) mod window.  Other slots are untouched.
+ *
+ *  k_new, v_new  [batch, T, num_kv_heads, head_dim] dtype: the step's new tokens,
+ *                keys unrotated
+ *  n_accept      [batch] int32 device array
+ *  positions     [batch] int32 device array (position of new token 0); may be NULL
+ *                when rope_base == 0 (keys copied as given)
+ *  k_cache, v_cache [batch, num_kv_heads, window, head_dim] dtype, updated in place
+ *  ring_head     [batch] int32 device array, updated in place
+ *  rope_base     host fp32, finite and >= 0; 0 copies the keys unrotated
+ * Requires 1 <= T < window.  batch == 0 is accepted (pointers may then be NULL).
+ * Calls that touch the same sequences must not overlap.
+ */
+SWASINK_API int swa_ring_append_rope(const void* k_new, const void* v_new, const int32_t* n_accept,
+                    const int32_t* positions, void* k_cache, void* v_cache, int32_t* ring_head,
+                    int32_t batch, int32_t T, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t window, float rope_base, swa_dtype dtype, void* stream);
 
 /* Message for the last non-OK return on the calling thread ("" if none). */
 SWASINK_API const char* swa_last_error(void);

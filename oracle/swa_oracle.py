@@ -385,8 +385,9 @@ def swa_ring_append_rope(k_new, v_new, n_accept, positions, k_cache, v_cache, ri
     (the accepted MTP tokens; rejected drafts never enter the cache).  Appending n
     tokens evicts the n oldest: accepted token t goes to physical slot
     (ring_head[b] + t) mod W, its key rotated at position positions[b] + t and
-    rounded to io_dtype, its value copied; the head then advances by n.  Returns
-    (k_cache, v_cache, ring_head) as new arrays."""
+    rounded to io_dtype, its value copied; the head then advances by n.  With
+    rope_base None the keys are copied unrotated.  Returns (k_cache, v_cache,
+    ring_head) as new arrays."""
     k_new, v_new = _as_f64(k_new), _as_f64(v_new)
     kc, vc = _as_f64(k_cache).copy(), _as_f64(v_cache).copy()
     bsz, t_new = k_new.shape[:2]
@@ -401,7 +402,10 @@ def swa_ring_append_rope(k_new, v_new, n_accept, positions, k_cache, v_cache, ri
             raise ValueError("n_accept out of range")
         if n == 0:
             continue
-        kr = round_to(rope(k_new[b, :n], pos[b] + np.arange(n), rope_base), io_dtype)  # [n, Hkv, D]
+        if rope_base is None:
+            kr = k_new[b, :n]
+        else:
+            kr = round_to(rope(k_new[b, :n], pos[b] + np.arange(n), rope_base), io_dtype)  # [n, Hkv, D]
         for t in range(n):
             slot = (heads[b] + t) % w
             kc[b, :, slot, :] = kr[t]

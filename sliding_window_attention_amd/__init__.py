@@ -40,7 +40,16 @@ _SIGNATURES = {
                                   _P, _P, _P, _P, _P, ctypes.c_int64, _P],
     "swa_sink_decode_fp8kv": [_P, _P, _P, _P, _P, _F, _F, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
                               _P, _P, _P],
+    "swa_rope": [_P, _P, _I, _I, _I, _F, _I, _P],
+    "swa_sink_decode_rope": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I,
+                             _P, _P, _P],
+    "swa_ring_append_rope": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P],
 }
+
+# Rotary bases the pages give (technical report digest, section 3.1).
+ROPE_BASE_SWA = 10000.0
+ROPE_BASE_GA = 640000.0
+ROPE_BASE_GA_256K = 5000000.0
 
 
 class SwaError(RuntimeError):
@@ -249,6 +258,84 @@ def swa_sink_decode_fp8kv(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, r
         _stream(q.device))
     _check(rc)
     return out, lse
+
+
+def swa_rope(x, positions, rope_base=ROPE_BASE_SWA):
+    """Rotary embedding of x [rows, heads, D] in place (row r at positions[r], int32).
+    Returns x."""
+    import torch
+
+    _dev(x, "x")
+    _dev(positions, "positions", torch.int32)
+    if x.dim() != 3 or positions.numel() != x.shape[0]:
+        raise ValueError("x must be [rows, heads, D] with one position per row")
+    rc = library().swa_rope(x.data_ptr(), positions.data_ptr(), x.shape[0], x.shape[1], x.shape[2],
+                            float(rope_base), _dtype_code(x), _stream(x.device))
+    _check(rc)
+    return x
+
+
+def swa_sink_decode_rope(q, k_new, v_new, k_cache, v_cache, ring_head, positions, sinks,
+                         rope_base=ROPE_BASE_SWA, scale=None, return_lse=True, out=None, lse=None):
+    """swa_sink_decode with q and k_new unrotated: new token t of sequence b is rotated
+    at positions[b] + t inside the kernel (positions [B] int32); the ring holds keys
+    rotated at their own positions."""
+    import torch
+
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
+                  (v_cache, "v_cache")):
+        _dev(t, nm, q.dtype)
+    _dev(ring_head, "ring_head", torch.int32)
+    _dev(positions, "positions", torch.int32)
+    _dev(sinks, "sinks", torch.float32)
+    if q.dim() != 4 or k_new.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q, k_new must be [B, T, H, D] and caches [B, Hkv, W, D]")
+    b, t, hq, d = q.shape
+    hkv, w = k_cache.shape[1], k_cache.shape[2]
+    if (k_new.shape != (b, t, hkv, d) or v_new.shape != k_new.shape or v_cache.shape != k_cache.shape
+            or k_cache.shape[0] != b or k_cache.shape[3] != d or ring_head.numel() != b
+            or positions.numel() != b or sinks.numel() != hq):
+        raise ValueError("inconsistent shapes")
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    if return_lse and lse is None:
+        lse = torch.empty((b, t, hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+    rc = library().swa_sink_decode_rope(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        ring_head.data_ptr(), positions.data_ptr(), sinks.data_ptr(), b, t, hq, hkv, d, w,
+        _scale(scale), float(rope_base), _dtype_code(q), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def swa_ring_append_rope(k_new, v_new, n_accept, positions, k_cache, v_cache, ring_head,
+                         rope_base=ROPE_BASE_SWA):
+    """Commit the first n_accept[b] new tokens of each sequence to its ring, keys rotated
+    at positions[b] + t; k_cache, v_cache and ring_head are updated in place."""
+    import torch
+
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, nm, k_new.dtype)
+    _dev(n_accept, "n_accept", torch.int32)
+    _dev(ring_head, "ring_head", torch.int32)
+    if positions is not None:
+        _dev(positions, "positions", torch.int32)
+    if k_new.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("k_new must be [B, T, Hkv, D] and caches [B, Hkv, W, D]")
+    b, t, hkv, d = k_new.shape
+    w = k_cache.shape[2]
+    if (v_new.shape != k_new.shape or v_cache.shape != k_cache.shape or k_cache.shape[0] != b
+            or k_cache.shape[1] != hkv or k_cache.shape[3] != d or n_accept.numel() != b
+            or ring_head.numel() != b or (positions is not None and positions.numel() != b)):
+        raise ValueError("inconsistent shapes")
+    rc = library().swa_ring_append_rope(
+        k_new.data_ptr(), v_new.data_ptr(), n_accept.data_ptr(),
+        positions.data_ptr() if positions is not None else None, k_cache.data_ptr(),
+        v_cache.data_ptr(), ring_head.data_ptr(), b, t, hkv, d, w, float(rope_base),
+        _dtype_code(k_new), _stream(k_new.device))
+    _check(rc)
 
 
 def swa_sink_prefill_backward(q, k, v, sinks, cu_seqlens, out, lse, dout, max_seqlen=None,

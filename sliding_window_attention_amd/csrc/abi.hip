@@ -115,13 +115,21 @@ int prefill_common(const void* q, const void* k, const void* v, const float* sin
   return hip_status(e, name);
 }
 
+int check_rope_base(float base, const char* name) {
+  if (!(isfinite(base) && base >= 0.f))
+    return fail(SWA_ERR_SHAPE, "%s: rope_base must be finite and >= 0 (got %g)", name, (double)base);
+  return 0;
+}
+
 int decode_common(const void* q, const void* k_new, const void* v_new, const void* k_cache,
                   const void* v_cache, bool fp8, float k_scale, float v_scale,
                   const int32_t* ring_head, const float* sinks, int32_t batch, int32_t T,
                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t window,
-                  float scale, int dtype, void* out, float* lse, void* stream, const char* name) {
+                  float scale, int dtype, void* out, float* lse, void* stream, const char* name,
+                  const int32_t* rope_pos = nullptr, float rope_base = 0.f) {
   int rc = check_dtype(dtype);
   if (rc) return rc;
+  if ((rc = check_rope_base(rope_base, name))) return rc;
   if (batch < 0) return fail(SWA_ERR_SHAPE, "%s: batch must be >= 0", name);
   if ((rc = check_heads(num_q_heads, num_kv_heads, head_dim))) return rc;
   if (window < 2) return fail(SWA_ERR_SHAPE, "%s: window must be >= 2 (got %d)", name, window);
@@ -137,6 +145,7 @@ int decode_common(const void* q, const void* k_new, const void* v_new, const voi
     return fail(SWA_ERR_NULL,
                 "%s: q, k_new, v_new, k_cache, v_cache, ring_head, sinks and out must be non-NULL",
                 name);
+  if (rope_base > 0.f && !rope_pos) return fail(SWA_ERR_NULL, "%s: positions must be non-NULL", name);
 
   swa::DecodeArgs a;
   a.q = q; a.k_new = k_new; a.v_new = v_new;
@@ -150,6 +159,10 @@ int decode_common(const void* q, const void* k_new, const void* v_new, const voi
   a.cache_fp8 = fp8;
   a.k_scale = fp8 ? k_scale : 1.f;
   a.v_scale = fp8 ? v_scale : 1.f;
+  if (rope_base > 0.f) {
+    a.rope_pos = rope_pos;
+    a.rope_log2_base = log2((double)rope_base);
+  }
   const bool bf = dtype == SWA_DTYPE_BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = swa::decode_mfma_supported(a, bf) ? swa::launch_decode_mfma(a, s)
@@ -205,6 +218,66 @@ int swa_sink_decode_fp8kv(const void* q, const void* k_new, const void* v_new,
   return decode_common(q, k_new, v_new, k_cache, v_cache, true, k_scale, v_scale, ring_head, sinks,
                        batch, T, num_q_heads, num_kv_heads, head_dim, window, scale, (int)dtype,
                        out, lse, stream, "swa_sink_decode_fp8kv");
+}
+
+int swa_sink_decode_rope(const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                         const void* v_cache, const int32_t* ring_head, const int32_t* positions,
+                         const float* sinks, int32_t batch, int32_t T, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t window, float scale,
+                         float rope_base, swa_dtype dtype, void* out, float* lse, void* stream) {
+  return decode_common(q, k_new, v_new, k_cache, v_cache, false, 1.f, 1.f, ring_head, sinks, batch,
+                       T, num_q_heads, num_kv_heads, head_dim, window, scale, (int)dtype, out, lse,
+                       stream, "swa_sink_decode_rope", positions, rope_base);
+}
+
+int swa_rope(void* x, const int32_t* positions, int32_t rows, int32_t heads, int32_t head_dim,
+             float rope_base, swa_dtype dtype, void* stream) {
+  const char* name = "swa_rope";
+  int rc = check_dtype((int)dtype);
+  if (rc) return rc;
+  if ((rc = check_rope_base(rope_base, name))) return rc;
+  if (rows < 0 || heads < 1) return fail(SWA_ERR_SHAPE, "%s: rows must be >= 0 and heads >= 1", name);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SWA_ERR_SHAPE, "%s: head_dim must be 64 or 128 (got %d)", name, head_dim);
+  if ((long long)rows * heads * head_dim > (1LL << 40)) return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
+  if (rows == 0 || rope_base == 0.f) return ok();
+  if (!x || !positions) return fail(SWA_ERR_NULL, "%s: x and positions must be non-NULL", name);
+  swa::RopeArgs a;
+  a.x = x; a.pos = positions; a.rows = rows; a.heads = heads; a.head_dim = head_dim;
+  a.log2_base = log2((double)rope_base);
+  return hip_status(swa::launch_rope(a, dtype == SWA_DTYPE_BF16, static_cast<hipStream_t>(stream)), name);
+}
+
+int swa_ring_append_rope(const void* k_new, const void* v_new, const int32_t* n_accept,
+                         const int32_t* positions, void* k_cache, void* v_cache, int32_t* ring_head,
+                         int32_t batch, int32_t T, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t window, float rope_base, swa_dtype dtype, void* stream) {
+  const char* name = "swa_ring_append_rope";
+  int rc = check_dtype((int)dtype);
+  if (rc) return rc;
+  if ((rc = check_rope_base(rope_base, name))) return rc;
+  if (batch < 0) return fail(SWA_ERR_SHAPE, "%s: batch must be >= 0", name);
+  if (num_kv_heads < 1) return fail(SWA_ERR_SHAPE, "%s: num_kv_heads must be >= 1", name);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SWA_ERR_SHAPE, "%s: head_dim must be 64 or 128 (got %d)", name, head_dim);
+  if (window < 2) return fail(SWA_ERR_SHAPE, "%s: window must be >= 2 (got %d)", name, window);
+  if (T < 1 || T >= window)
+    return fail(SWA_ERR_SHAPE, "%s: T must satisfy 1 <= T < window (got T=%d, window=%d)", name, T, window);
+  if ((long long)batch * num_kv_heads * window * head_dim > (1LL << 40))
+    return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
+  if (batch == 0) return ok();
+  if (!k_new || !v_new || !n_accept || !k_cache || !v_cache || !ring_head)
+    return fail(SWA_ERR_NULL, "%s: k_new, v_new, n_accept, k_cache, v_cache and ring_head must be non-NULL",
+                name);
+  if (rope_base > 0.f && !positions) return fail(SWA_ERR_NULL, "%s: positions must be non-NULL", name);
+  swa::AppendArgs a;
+  a.k_new = k_new; a.v_new = v_new; a.n_accept = n_accept;
+  a.rope_pos = rope_base > 0.f ? positions : nullptr;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.ring_head = ring_head;
+  a.batch = batch; a.t_new = T; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim; a.window = window;
+  a.log2_base = rope_base > 0.f ? log2((double)rope_base) : 0.0;
+  return hip_status(swa::launch_ring_append(a, dtype == SWA_DTYPE_BF16, static_cast<hipStream_t>(stream)),
+                    name);
 }
 
 int64_t swa_sink_prefill_backward_workspace(int32_t total_tokens, int32_t num_q_heads) {

@@ -68,6 +68,35 @@ struct DecodeArgs {
   bool cache_fp8 = false;  // k_cache / v_cache hold one-byte E4M3 codes
   float k_scale = 1.f;     // with cache_fp8: element value = code value * scale
   float v_scale = 1.f;
+  const int32_t* rope_pos = nullptr;  // [B] position of new token 0: rotate q and k_new
+  double rope_log2_base = 0.0;        // log2 of the rotary base (with rope_pos)
+};
+
+// Rotary embedding of x [rows, heads, D] in place, row r at position pos[r].
+struct RopeArgs {
+  void* x;
+  const int32_t* pos;
+  int32_t rows;
+  int32_t heads;
+  int32_t head_dim;
+  double log2_base;
+};
+
+// Commit accepted new tokens to a ring (keys rotated on the way in when rope is set).
+struct AppendArgs {
+  const void* k_new;        // [B, T, Hkv, D]
+  const void* v_new;        // [B, T, Hkv, D]
+  const int32_t* n_accept;  // [B], clamped to [0, T]
+  const int32_t* rope_pos;  // [B] position of new token 0, or nullptr (no rotation)
+  void* k_cache;            // [B, Hkv, W, D]
+  void* v_cache;            // [B, Hkv, W, D]
+  int32_t* ring_head;       // [B], advanced by the accepted count
+  int32_t batch;
+  int32_t t_new;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t window;
+  double log2_base;
 };
 
 // Arguments of the backward (gradients of O).  Pointers are device pointers.
@@ -125,6 +154,16 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(u32x2 w) {
 // One code as fp32.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
   return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+}
+
+// cos and sin of the rotary angle of pair i (of head_dim D) at an integer position:
+// angle = pos * base^(-2i/D), formed and reduced to [-pi, pi] in fp64 (positions go to
+// 2^31, where an angle formed in fp32 is off by whole radians), then evaluated in fp32.
+__device__ __forceinline__ void rope_cos_sin(int pos, int i, int D, double log2_base, float* c, float* s) {
+  const double f = exp2(-2.0 * (double)i / (double)D * log2_base);
+  const double ang = (double)pos * f;
+  const double r = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+  sincosf((float)r, s, c);
 }
 
 // s_waitcnt immediate for vmcnt(0) with the other counters left alone (gfx9

@@ -42,6 +42,7 @@ struct DecodeSmem {
     struct {
       char q[NT * 16][kRowPitch];  // query columns (dead once the scores are formed)
       char kn[16][kRowPitch];      // new-token K rows, zero past T
+      float cs[4 * 64][2];         // rotary cos / sin per (new token, pair), when rotating
     } in;
   } u;
   char vn[16][kRowPitch];  // new-token V rows, zero past T
@@ -86,7 +87,8 @@ __device__ __forceinline__ void add_partial(const char (*slot)[kColBytes], int i
 // registers, exactly); the K scale joins the ring logits' multiplier and the V scale
 // multiplies the ring weights as they are packed for P*V (the running sums stay
 // unscaled), so no cache element is ever rescaled.
-template <int NT, bool FP8>
+// ROPE: q and the new keys arrive unrotated and are rotated in LDS after staging.
+template <int NT, bool FP8, bool ROPE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) DecodeSmem<NT> sm;
@@ -164,6 +166,36 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) tcol[tt] = 2 * tt + (i >> 3);
   __syncthreads();
+  if constexpr (ROPE) {
+    // Rotary embedding of the staged query columns and new keys (they arrive
+    // unrotated; the ring's keys were rotated when they were appended): a cos/sin
+    // table per (token, pair), then one pass over (row, group of 8 pairs), rounding
+    // back to bf16 in place.
+    const int tid = threadIdx.x;
+    const int pos0 = as_const(a.rope_pos)[b];
+    for (int x = tid; x < T * 64; x += kThreads)
+      rope_cos_sin(pos0 + (x >> 6), x & 63, D, a.rope_log2_base, &sm.u.in.cs[x][0], &sm.u.in.cs[x][1]);
+    __syncthreads();
+    const int nq = T * kHG;  // query columns col = token * 8 + head
+    for (int x = tid; x < (nq + T) * 8; x += kThreads) {
+      const int r = x >> 3, gi = x & 7;
+      char* row = r < nq ? sm.u.in.q[r] : sm.u.in.kn[r - nq];
+      const int t = r < nq ? r >> 3 : r - nq;
+      bf16x8* lo = reinterpret_cast<bf16x8*>(row + 16 * gi);
+      bf16x8* hi = reinterpret_cast<bf16x8*>(row + 128 + 16 * gi);
+      const bf16x8 u = *lo, v = *hi;
+      bf16x8 yu, yv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float c = sm.u.in.cs[t * 64 + 8 * gi + e][0], sn = sm.u.in.cs[t * 64 + 8 * gi + e][1];
+        yu[e] = (bf16)((float)u[e] * c - (float)v[e] * sn);
+        yv[e] = (bf16)((float)v[e] * c + (float)u[e] * sn);
+      }
+      *lo = yu;
+      *hi = yv;
+    }
+    __syncthreads();
+  }
   // B operand (Q^T) of tile tt, head-dim chunk cc: column tt*16 + i, unit 4cc + g
   auto qop = [&](int tt, int cc) {
     return *reinterpret_cast<const bf16x8*>(&sm.u.in.q[tt * 16 + i][16 * (4 * cc + g)]);
@@ -324,12 +356,17 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
   const long blocks = (long)a.batch * (a.num_q_heads / kHG);
   if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
   const bool two = a.t_new > 2;
-  if (a.cache_fp8) {
-    if (two) hipLaunchKernelGGL((decode_kernel<2, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<1, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  if (a.rope_pos != nullptr) {  // rotation in the kernel (bf16 ring)
+    if (a.cache_fp8) return hipErrorInvalidValue;
+    if (two) hipLaunchKernelGGL((decode_kernel<2, false, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<1, false, true>), grid, block, 0, s, a);
+  } else if (a.cache_fp8) {
+    if (two) hipLaunchKernelGGL((decode_kernel<2, true, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<1, true, false>), grid, block, 0, s, a);
   } else {
-    if (two) hipLaunchKernelGGL((decode_kernel<2, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<1, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    if (two) hipLaunchKernelGGL((decode_kernel<2, false, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<1, false, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -69,9 +69,29 @@ struct DecodeKeys {
   int head;
   int new_stride;  // Hkv * D
   float k_scale, v_scale;
+  bool rope = false;  // rotate the new keys: token t at position rope_pos0 + t
+  int rope_pos0 = 0;
+  double rope_l2b = 0.0;
   __device__ int phys(int j) const { int p = head + j; return p - ((p >= W) ? W : 0); }
   __device__ void load_key(int j, int d, float* dst) const {
-    if (j >= W) { Elem<T>::load16(kn + (size_t)(j - W) * new_stride + d, dst); return; }
+    if (j >= W) {
+      const T* row = kn + (size_t)(j - W) * new_stride;
+      Elem<T>::load16(row + d, dst);
+      if (rope) {  // pair element i with i + D/2; rounded to the I/O type like a stored rotation
+        constexpr int H = D / 2;
+        const int dp = d < H ? d + H : d - H;
+        float part[Elem<T>::kVec];
+        Elem<T>::load16(row + dp, part);
+#pragma unroll
+        for (int e = 0; e < Elem<T>::kVec; ++e) {
+          float c, s;
+          rope_cos_sin(rope_pos0 + (j - W), (d % H) + e, D, rope_l2b, &c, &s);
+          const float y = d < H ? dst[e] * c - part[e] * s : dst[e] * c + part[e] * s;
+          dst[e] = (float)Elem<T>::store_cast(y);
+        }
+      }
+      return;
+    }
     const C* row = kc + (size_t)phys(j) * D + d;
     if constexpr (FP8) {
 #pragma unroll
@@ -91,13 +111,24 @@ struct DecodeKeys {
 // One wavefront computes one row against keys jlo..jhi (inclusive, jlo <= jhi).
 template <typename T, int D, class Keys>
 __device__ void attend_row(const T* __restrict__ qrow, const Keys& keys, int jlo, int jhi,
-                           float sink2, float c, T* __restrict__ orow, float* lse_out) {
+                           float sink2, float c, T* __restrict__ orow, float* lse_out,
+                           bool rope = false, int qpos = 0, double rope_l2b = 0.0) {
   using E = Elem<T>;
   constexpr int kPer = D / kWave;  // output elements per lane
   const int lane = threadIdx.x & (kWave - 1);
   float q[D];
 #pragma unroll
   for (int d = 0; d < D; d += E::kVec) E::load16(qrow + d, q + d);
+  if (rope) {  // rotary embedding of the query, rounded to the I/O type like a stored rotation
+#pragma unroll
+    for (int i = 0; i < D / 2; ++i) {
+      float cs, sn;
+      rope_cos_sin(qpos, i, D, rope_l2b, &cs, &sn);
+      const float u = q[i], v = q[i + D / 2];
+      q[i] = (float)E::store_cast(u * cs - v * sn);
+      q[i + D / 2] = (float)E::store_cast(v * cs + u * sn);
+    }
+  }
   float o[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) o[e] = 0.f;
@@ -185,11 +216,16 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void generic_decode_kernel(D
   keys.W = W;
   keys.head = head;
   keys.new_stride = hkv * D;
+  const bool rope = a.rope_pos != nullptr;
+  const int pos0 = rope ? a.rope_pos[b] : 0;
+  keys.rope = rope;
+  keys.rope_pos0 = pos0;
+  keys.rope_l2b = a.rope_log2_base;
   const T* qrow = static_cast<const T*>(a.q) + (size_t)row * D;
   T* orow = static_cast<T*>(a.out) + (size_t)row * D;
   // query t sits at virtual position W + t and sees W keys: t+1 .. W+t
   attend_row<T, D>(qrow, keys, t + 1, W + t, a.sinks[h] * kLog2e, a.scale * kLog2e, orow,
-                   a.lse ? a.lse + row : nullptr);
+                   a.lse ? a.lse + row : nullptr, rope, pos0 + t, a.rope_log2_base);
 }
 
 template <typename T, int D>

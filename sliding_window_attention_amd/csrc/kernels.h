@@ -26,6 +26,11 @@ hipError_t launch_backward(const BackwardArgs& a, bool bf16_io, hipStream_t s);
 bool backward_mfma_supported(const BackwardArgs& a, bool bf16_io);
 hipError_t launch_backward_mfma(const BackwardArgs& a, hipStream_t s);
 
+// Rotary embedding in place (bf16 / fp32, head_dim 64 / 128), and the ring append of
+// accepted tokens (keys rotated on the way in when a.rope_pos is set).
+hipError_t launch_rope(const RopeArgs& a, bool bf16_io, hipStream_t s);
+hipError_t launch_ring_append(const AppendArgs& a, bool bf16_io, hipStream_t s);
+
 // Compute units of the current device (cached per device).
 hipError_t device_cu_count(int* out);
 

@@ -129,6 +129,19 @@ def make_decode(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, dtype
             "ring_head": ring_head, "sinks": sinks}
 
 
+def make_decode_rope(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, dtype, seed,
+                     max_position=1 << 20):
+    """make_decode plus positions [B] int32 ~ U[window, max_position): the position of
+    each sequence's new token 0 (q and k_new are then read as unrotated; the ring's
+    values stand for keys rotated at their own positions).  Drawn after the decode
+    tensors from the same generator."""
+    x = make_decode(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, dtype, seed)
+    gen = torch.Generator().manual_seed(int(seed) + 1)
+    x["positions"] = torch.randint(window, max_position, (batch,), generator=gen,
+                                   dtype=torch.int64).to(torch.int32)
+    return x
+
+
 def _randn_device(shape, gen, device, dtype, chunk_rows=1 << 18):
     """N(0, 1) rounded to `dtype`, drawn on `device` a slab of rows at a time (so
     that no fp32 copy of a multi-GB tensor is ever held)."""

@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     assert set(names) == {"swa_sink_prefill", "ga_causal_prefill", "swa_sink_decode",
                           "swa_sink_decode_fp8kv", "swa_sink_prefill_backward",
-                          "swa_sink_prefill_backward_workspace", "swa_last_error", "swa_abi_version"}
+                          "swa_sink_prefill_backward_workspace", "swa_rope", "swa_sink_decode_rope",
+                          "swa_ring_append_rope", "swa_last_error", "swa_abi_version"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -228,3 +229,94 @@ def test_backward_rejects_bad_arguments(kw, code, needle):
 def test_backward_empty_stream_without_sinks_reads_nothing():
     assert _backward(n=0, max_seqlen=0, q=NULL, k=NULL, v=NULL, cu=NULL, out=NULL, lse=NULL, dout=NULL,
                      dq=NULL, dk=NULL, dv=NULL, sinks=NULL, dsinks=NULL, ws=NULL, ws_bytes=0) == OK
+
+
+# ---------------------------------------------------------------------------
+# rotary embedding around decode
+# ---------------------------------------------------------------------------
+
+def _rope(**kw):
+    a = dict(x=FAKE, pos=FAKE, rows=4, heads=2, d=128, base=10000.0, dtype=1)
+    a.update(kw)
+    return swa.library().swa_rope(a["x"], a["pos"], a["rows"], a["heads"], a["d"], a["base"], a["dtype"], NULL)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(base=-1.0), E_SHAPE, "rope_base"),
+    (dict(base=float("nan")), E_SHAPE, "rope_base"),
+    (dict(base=float("inf")), E_SHAPE, "rope_base"),
+    (dict(d=96), E_SHAPE, "head_dim"),
+    (dict(rows=-1), E_SHAPE, "rows"),
+    (dict(heads=0), E_SHAPE, "heads"),
+    (dict(x=NULL), E_NULL, "positions"),
+    (dict(pos=NULL), E_NULL, "positions"),
+    (dict(dtype=5), E_DTYPE, "dtype"),
+])
+def test_rope_rejects_bad_arguments(kw, code, needle):
+    assert _rope(**kw) == code
+    assert needle in _last()
+
+
+def test_rope_nothing_to_do_is_ok():
+    assert _rope(rows=0, x=NULL, pos=NULL) == OK
+    assert _rope(base=0.0, x=NULL, pos=NULL) == OK  # base 0: no rotation, nothing launched
+
+
+def _decode_rope(**kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, head=FAKE, pos=FAKE, sinks=FAKE, b=2, t=1, hq=8,
+             hkv=1, d=128, window=128, scale=0.0, base=10000.0, dtype=1, out=FAKE, lse=NULL)
+    a.update(kw)
+    return swa.library().swa_sink_decode_rope(
+        a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["head"], a["pos"], a["sinks"], a["b"], a["t"], a["hq"],
+        a["hkv"], a["d"], a["window"], a["scale"], a["base"], a["dtype"], a["out"], a["lse"], NULL)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(pos=NULL), E_NULL, "positions"),
+    (dict(base=-2.0), E_SHAPE, "rope_base"),
+    (dict(t=0), E_SHAPE, "T must"),
+    (dict(head=NULL), E_NULL, "ring_head"),
+    (dict(d=32), E_UNSUP, "head_dim"),
+])
+def test_decode_rope_rejects_bad_arguments(kw, code, needle):
+    assert _decode_rope(**kw) == code
+    assert needle in _last()
+
+
+def test_decode_rope_empty_batch_accepts_null_pointers():
+    assert _decode_rope(b=0, q=NULL, kn=NULL, vn=NULL, kc=NULL, vc=NULL, head=NULL, pos=NULL, sinks=NULL,
+                        out=NULL) == OK
+
+
+def _append(**kw):
+    a = dict(kn=FAKE, vn=FAKE, nacc=FAKE, pos=FAKE, kc=FAKE, vc=FAKE, head=FAKE, b=2, t=4, hkv=4, d=128,
+             window=128, base=10000.0, dtype=1)
+    a.update(kw)
+    return swa.library().swa_ring_append_rope(
+        a["kn"], a["vn"], a["nacc"], a["pos"], a["kc"], a["vc"], a["head"], a["b"], a["t"], a["hkv"], a["d"],
+        a["window"], a["base"], a["dtype"], NULL)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(t=0), E_SHAPE, "T must"),
+    (dict(t=128), E_SHAPE, "T must"),
+    (dict(window=1, t=1), E_SHAPE, "window"),
+    (dict(hkv=0), E_SHAPE, "num_kv_heads"),
+    (dict(d=80), E_SHAPE, "head_dim"),
+    (dict(b=-1), E_SHAPE, "batch"),
+    (dict(nacc=NULL), E_NULL, "n_accept"),
+    (dict(head=NULL), E_NULL, "ring_head"),
+    (dict(pos=NULL), E_NULL, "positions"),
+    (dict(base=float("nan")), E_SHAPE, "rope_base"),
+    (dict(dtype=9), E_DTYPE, "dtype"),
+])
+def test_ring_append_rejects_bad_arguments(kw, code, needle):
+    assert _append(**kw) == code
+    assert needle in _last()
+
+
+def test_ring_append_edge_cases_validate_without_launching():
+    assert _append(b=0, kn=NULL, vn=NULL, nacc=NULL, pos=NULL, kc=NULL, vc=NULL, head=NULL) == OK
+    # base 0 copies the keys unrotated, so positions may be NULL; every other pointer is still
+    # required (the call fails before any launch)
+    assert _append(pos=NULL, base=0.0, kc=NULL) == E_NULL and "k_cache" in _last()

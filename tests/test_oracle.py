@@ -650,3 +650,7 @@ def test_ring_append_matches_a_list_model():
             np.testing.assert_array_equal(v2[b, :, (h2[b] + l) % w, :], vlist[l])
     # inputs are untouched (new arrays returned)
     assert not np.shares_memory(k2, kc)
+    # without a base the keys are copied as given
+    k3, _, _ = orc.swa_ring_append_rope(kn, vn, n_acc, pos, kc, vc, heads, None)
+    b, t = 2, 3
+    np.testing.assert_array_equal(k3[b, :, (heads[b] + t) % w, :], kn[b, t])

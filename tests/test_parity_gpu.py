@@ -673,3 +673,180 @@ def test_backward_empty_stream_and_determinism():
 def test_backward_32k_layer():
     _say("backward of the 32K SWA-sink layer (32/4, D128, W128): every gradient element")
     _backward_case([32768], 32, 4, 128, "bf16", 128, True, seed=wl.WORKLOADS["swa_prefill_32k"].seed)
+
+
+# ---------------------------------------------------------------------------
+# rotary embedding around decode: in place, inside the decode, ring append
+# ---------------------------------------------------------------------------
+
+def _ulp(y, dtype):
+    """Spacing of the I/O type at |y| (bf16: 8 significant bits; fp32: 24)."""
+    bits = 8 if dtype == torch.bfloat16 else 24
+    a = np.maximum(np.abs(y), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - (bits - 1))
+
+
+def assert_rotated_close(got, x, ref, dtype, what):
+    """Rotated values against the fp64 oracle: within half a unit in the last place of
+    the I/O type (the oracle's rounding) plus the fp32 rotation error, bounded by
+    1e-5 (|x_i| + |x_pair|) for angles reduced in fp64.  For bf16 output, where the
+    fp32 rotation is far finer than the output spacing, at least 99.9% must also be
+    bit-identical to the oracle rounded to bf16 (fp32 output differs from a rounded
+    fp64 result in the last bit about half the time, so no such check there)."""
+    g = to_np(got).astype(np.float64)
+    xs = np.abs(np.asarray(x, dtype=np.float64))
+    half = xs.shape[-1] // 2
+    pair = np.concatenate([xs[..., half:], xs[..., :half]], axis=-1)
+    bound = 0.5 * _ulp(ref, dtype) + 1e-5 * (xs + pair)
+    err = np.abs(g - ref)
+    same = float(np.mean(g == orc.round_to(ref, "bf16" if dtype == torch.bfloat16 else "f32")))
+    msg = f"{what}: max err/bound {float((err / bound).max()):.3f}, identical {same:.5f}"
+    print(msg, flush=True)
+    assert np.isfinite(g).all() and np.all(err <= bound), msg
+    if dtype == torch.bfloat16:
+        assert same >= 0.999, msg
+
+
+@pytest.mark.parametrize("case", [(1000, 8, 128, "bf16", 10000.0), (513, 4, 64, "bf16", 640000.0),
+                                  (300, 2, 128, "f32", 5e6), (77, 32, 128, "bf16", 5e6)],
+                         ids=lambda c: f"{c[0]}x{c[1]}-D{c[2]}-{c[3]}-base{c[4]:g}")
+def test_rope_in_place(case):
+    rows, heads, d, dt, base = case
+    _say(f"rope in place {rows}x{heads} D{d} {dt} base {base:g}")
+    gen = torch.Generator().manual_seed(rows + heads)
+    x = torch.randn(rows, heads, d, generator=gen).to(wl._torch_dtype(dt))
+    pos = torch.randint(0, 1 << 20, (rows,), generator=gen, dtype=torch.int64)
+    pos[:4] = torch.tensor([0, 1, 2 ** 31 - 1, -12345])  # identity, first step, extremes
+    pos = pos.to(torch.int32)
+    xd = x.to(DEV)
+    swa.swa_rope(xd, pos.to(DEV), base)
+    torch.cuda.synchronize()
+    ref = orc.rope(x, pos.numpy(), base)
+    assert_rotated_close(xd, x.double().numpy(), ref, x.dtype, f"rope {case}")
+    assert torch.equal(xd[0].cpu(), x[0])  # position 0 is the identity, bit for bit
+
+
+def _run_decode_rope(x, base):
+    g = _gpu(x)
+    o, lse = swa.swa_sink_decode_rope(g["q"], g["k_new"], g["v_new"], g["k_cache"], g["v_cache"],
+                                      g["ring_head"], g["positions"], g["sinks"], base)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _oracle_decode_rope(x, window, base):
+    io = "bf16" if x["q"].dtype == torch.bfloat16 else "f32"
+    return orc.swa_sink_decode_rope(x["q"], x["k_new"], x["v_new"], x["k_cache"], x["v_cache"],
+                                    x["ring_head"].numpy(), x["positions"].numpy(), x["sinks"], base,
+                                    window, io_dtype=io)
+
+
+@pytest.mark.parametrize("t_new", [1, 2, 3, 4])
+def test_decode_rope_small(t_new):
+    _say(f"decode with RoPE B=16 T={t_new} 32/4 D128 bf16 (matrix cores), positions up to 2^31")
+    x = wl.make_decode_rope(16, t_new, 32, 4, 128, 128, "bf16", seed=3600 + t_new)
+    x["positions"][0] = 128
+    x["positions"][1] = 2 ** 31 - 8  # new tokens up to 2^31 - 5
+    x["ring_head"][2] = 127
+    for base in (10000.0, 5e6):
+        o, lse = _run_decode_rope(x, base)
+        o_ref, l_ref = _oracle_decode_rope(x, 128, base)
+        assert_close(torch.bfloat16, o, o_ref, lse, l_ref, f"decode rope T={t_new} base {base:g}")
+
+
+@pytest.mark.parametrize("case", [(6, 16, 2, 128, 128, "bf16", 3), (3, 8, 1, 64, 128, "bf16", 2),
+                                  (4, 8, 8, 128, 64, "bf16", 4), (5, 4, 1, 64, 128, "f32", 3),
+                                  (2, 8, 1, 128, 128, "bf16", 8)])
+def test_decode_rope_generic_shapes(case):
+    b, hq, hkv, d, w, dt, t_new = case
+    _say(f"decode with RoPE generic B={b} T={t_new} {hq}/{hkv} D{d} W{w} {dt}")
+    x = wl.make_decode_rope(b, t_new, hq, hkv, d, w, dt, seed=3700 + b * 7 + w)
+    o, lse = _run_decode_rope(x, 640000.0)
+    o_ref, l_ref = _oracle_decode_rope(x, w, 640000.0)
+    assert_close(x["q"].dtype, o, o_ref, lse, l_ref, f"decode rope generic {case}")
+
+
+def test_decode_rope_base_zero_is_plain_decode():
+    _say("decode with rope_base 0 equals swa_sink_decode bit for bit")
+    x = wl.make_decode_rope(8, 4, 32, 4, 128, 128, "bf16", seed=3800)
+    o, lse = _run_decode_rope(x, 0.0)
+    o2, l2 = _run_decode(x, 128)
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+@pytest.mark.parametrize("case", [(16, 4, 4, 128, 128, "bf16", 10000.0), (9, 3, 2, 64, 32, "f32", 640000.0),
+                                  (5, 2, 1, 128, 128, "bf16", 0.0)],
+                         ids=lambda c: f"B{c[0]}-T{c[1]}-kv{c[2]}-D{c[3]}-W{c[4]}-{c[5]}-base{c[6]:g}")
+def test_ring_append(case):
+    b, t_new, hkv, d, w, dt, base = case
+    _say(f"ring append B={b} T={t_new} kv {hkv} D{d} W{w} {dt} base {base:g}")
+    x = wl.make_decode_rope(b, t_new, hkv, hkv, d, w, dt, seed=3900 + b)
+    gen = torch.Generator().manual_seed(3901 + b)
+    n_acc = torch.randint(0, t_new + 1, (b,), generator=gen, dtype=torch.int64).to(torch.int32)
+    n_acc[0], n_acc[1] = t_new + 3, -2  # clamped to T and to 0
+    x["ring_head"][2] = w - 1           # writes wrap around the ring
+    x["ring_head"][3] = 3 * w + 1       # reduced modulo W
+    g = _gpu(x)
+    heads = g["ring_head"].clone()
+    swa.swa_ring_append_rope(g["k_new"], g["v_new"], n_acc.to(DEV), g["positions"], g["k_cache"],
+                             g["v_cache"], heads, base)
+    torch.cuda.synchronize()
+    io = "bf16" if dt == "bf16" else "f32"
+    kc, vc, h2 = orc.swa_ring_append_rope(x["k_new"], x["v_new"], np.clip(n_acc.numpy(), 0, t_new),
+                                          x["positions"].numpy(), x["k_cache"], x["v_cache"],
+                                          x["ring_head"].numpy(), base or None, io_dtype=io)
+    assert np.array_equal(heads.cpu().numpy(), h2)
+    assert np.array_equal(to_np(g["v_cache"]), vc)  # values copied bit for bit
+    got_k = to_np(g["k_cache"])
+    written = np.zeros(got_k.shape[:3], dtype=bool)  # [B, Hkv, W]
+    for bb in range(b):
+        n = int(np.clip(n_acc[bb], 0, t_new))
+        for t in range(n):
+            written[bb, :, (int(x["ring_head"][bb]) % w + t) % w] = True
+    assert np.array_equal(got_k[~written], to_np(x["k_cache"])[~written])  # untouched slots
+    if base == 0.0:
+        assert np.array_equal(got_k, kc)
+    else:
+        kraw = np.zeros_like(kc)
+        for bb in range(b):
+            n = int(np.clip(n_acc[bb], 0, t_new))
+            for t in range(n):
+                kraw[bb, :, (int(x["ring_head"][bb]) % w + t) % w] = x["k_new"][bb, t].double().numpy()
+        kref = orc.swa_ring_append_rope(x["k_new"], x["v_new"], np.clip(n_acc.numpy(), 0, t_new),
+                                        x["positions"].numpy(), x["k_cache"], x["v_cache"],
+                                        x["ring_head"].numpy(), base, io_dtype=None)[0]
+        assert_rotated_close(torch.from_numpy(got_k[written]), kraw[written], kref[written],
+                             x["k_new"].dtype, f"append keys {case}")
+
+
+def test_decode_and_append_steps_follow_the_oracle():
+    """Five MTP steps: verify T = 4 tokens against the ring (RoPE in the kernel), accept a
+    seeded 0..4 of them, commit those to the ring (keys rotated), advance the positions;
+    the GPU state and every step's outputs follow the oracle run on the same inputs."""
+    _say("decode + append: 5 MTP steps, B=8, 32/4 D128 bf16")
+    b, t_new, hq, hkv, d, w, base = 8, 4, 32, 4, 128, 128, 10000.0
+    x = wl.make_decode_rope(b, t_new, hq, hkv, d, w, "bf16", seed=4100)
+    gen = torch.Generator().manual_seed(4101)
+    g = _gpu(x)
+    kc, vc, heads = x["k_cache"].double().numpy(), x["v_cache"].double().numpy(), x["ring_head"].numpy()
+    pos = x["positions"].numpy().astype(np.int64)
+    for step in range(5):
+        q = torch.randn(b, t_new, hq, d, generator=gen).to(torch.bfloat16)
+        kn = torch.randn(b, t_new, hkv, d, generator=gen).to(torch.bfloat16)
+        vn = torch.randn(b, t_new, hkv, d, generator=gen).to(torch.bfloat16)
+        n_acc = torch.randint(0, t_new + 1, (b,), generator=gen, dtype=torch.int64).to(torch.int32)
+        pos_t = torch.from_numpy(pos.astype(np.int32))
+        o, lse = swa.swa_sink_decode_rope(q.to(DEV), kn.to(DEV), vn.to(DEV), g["k_cache"], g["v_cache"],
+                                          g["ring_head"], pos_t.to(DEV), g["sinks"], base)
+        swa.swa_ring_append_rope(kn.to(DEV), vn.to(DEV), n_acc.to(DEV), pos_t.to(DEV), g["k_cache"],
+                                 g["v_cache"], g["ring_head"], base)
+        torch.cuda.synchronize()
+        o_ref, l_ref = orc.swa_sink_decode_rope(q, kn, vn, kc, vc, heads, pos, x["sinks"], base, w)
+        assert_close(torch.bfloat16, o, o_ref, lse, l_ref, f"step {step}")
+        kc, vc, heads = orc.swa_ring_append_rope(kn, vn, n_acc.numpy(), pos, kc, vc, heads, base)
+        assert np.array_equal(g["ring_head"].cpu().numpy(), heads)
+        pos = pos + n_acc.numpy()
+        # the GPU ring carries its own rotated keys forward: compare them to the oracle's
+        diff = np.abs(to_np(g["k_cache"]) - kc)
+        assert diff.max() <= 2.0 ** -6 * max(1.0, float(np.abs(kc).max())), f"step {step} ring keys"
+        assert np.array_equal(to_np(g["v_cache"]), vc)
