@@ -154,6 +154,13 @@ void decode_kernel(DecodeArgs a) {
       st[NT] = *reinterpret_cast<const u32x4*>(kn + (size_t)row * hkv * D + 8 * uu);
       st[NT + 1] = *reinterpret_cast<const u32x4*>(vn + (size_t)row * hkv * D + 8 * uu);
     }
+    if constexpr (ROPE) {
+      // the rotary cos/sin table (token, pair) is formed while the staging loads are in
+      // flight (it depends on the position only)
+      const int pos0 = as_const(a.rope_pos)[b];
+      for (int x = tid; x < T * 64; x += kThreads)
+        rope_cos_sin(pos0 + (x >> 6), x & 63, D, a.rope_log2_base, &sm.u.in.cs[x][0], &sm.u.in.cs[x][1]);
+    }
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
       const int x = k * kThreads + tid;
@@ -168,14 +175,10 @@ void decode_kernel(DecodeArgs a) {
   __syncthreads();
   if constexpr (ROPE) {
     // Rotary embedding of the staged query columns and new keys (they arrive
-    // unrotated; the ring's keys were rotated when they were appended): a cos/sin
-    // table per (token, pair), then one pass over (row, group of 8 pairs), rounding
+    // unrotated; the ring's keys were rotated when they were appended): one pass over
+    // (row, group of 8 pairs) with the cos/sin table formed during staging, rounding
     // back to bf16 in place.
     const int tid = threadIdx.x;
-    const int pos0 = as_const(a.rope_pos)[b];
-    for (int x = tid; x < T * 64; x += kThreads)
-      rope_cos_sin(pos0 + (x >> 6), x & 63, D, a.rope_log2_base, &sm.u.in.cs[x][0], &sm.u.in.cs[x][1]);
-    __syncthreads();
     const int nq = T * kHG;  // query columns col = token * 8 + head
     for (int x = tid; x < (nq + T) * 8; x += kThreads) {
       const int r = x >> 3, gi = x & 7;

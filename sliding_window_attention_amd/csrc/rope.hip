@@ -52,10 +52,15 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a) {
 }
 
 // One workgroup per sequence: write the first n accepted tokens to physical slots
-// (head + t) mod W (the n oldest), then advance the head.  Every thread reads the head
-// before the barrier; one thread writes the new head after it.
+// (head + t) mod W (the n oldest), then advance the head.  The rotary cos/sin of each
+// (token, pair) is formed once in LDS and shared by the KV heads; keys and values move
+// in 16-byte pieces.  Every thread reads the head before the barriers; one thread
+// writes the new head after the last one.
+constexpr int kMaxT = 8;  // tokens per step with a shared angle table; larger T recomputes
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void ring_append_kernel(AppendArgs a) {
+  __shared__ float cs[kMaxT * (D / 2)][2];
+  constexpr int kVec = 16 / (int)sizeof(T);  // elements per 16-byte piece
   const int b = blockIdx.x;
   const int Tn = a.t_new, hkv = a.num_kv_heads, W = a.window;
   int n = a.n_accept[b];
@@ -64,34 +69,60 @@ __global__ __launch_bounds__(kThreads) void ring_append_kernel(AppendArgs a) {
   head += head < 0 ? W : 0;
   const bool rope = a.rope_pos != nullptr;
   const int pos0 = rope ? a.rope_pos[b] : 0;
+  const bool table = n <= kMaxT;
+  if (rope && table)
+    for (int x = threadIdx.x; x < n * (D / 2); x += kThreads)
+      rope_cos_sin(pos0 + x / (D / 2), x % (D / 2), D, a.log2_base, &cs[x][0], &cs[x][1]);
+  __syncthreads();
   const T* kn = static_cast<const T*>(a.k_new) + (size_t)b * Tn * hkv * D;
   const T* vn = static_cast<const T*>(a.v_new) + (size_t)b * Tn * hkv * D;
   T* kc = static_cast<T*>(a.k_cache) + (size_t)b * hkv * W * D;
   T* vc = static_cast<T*>(a.v_cache) + (size_t)b * hkv * W * D;
-  // keys: one item per (token, kv head, pair)
-  for (int x = threadIdx.x; x < n * hkv * (D / 2); x += kThreads) {
-    const int i = x % (D / 2);
-    const int r = x / (D / 2);  // token t = r / hkv, kv head r % hkv
-    const int t = r / hkv, g = r - t * hkv;
-    const T* src = kn + ((size_t)t * hkv + g) * D;
-    T* dst = kc + ((size_t)g * W + (head + t) % W) * D;
-    const float u = ldf(src + i), v = ldf(src + i + D / 2);
-    if (rope) {
-      float c, s;
-      rope_cos_sin(pos0 + t, i, D, a.log2_base, &c, &s);
-      dst[i] = cvt<T>(u * c - v * s);
-      dst[i + D / 2] = cvt<T>(v * c + u * s);
+  // keys: one item per (token, kv head, group of kVec pairs); values: per 16-byte piece
+  constexpr int kKGroups = D / 2 / kVec, kVPieces = D / kVec;
+  const int nk = n * hkv * kKGroups;
+  for (int x = threadIdx.x; x < nk + n * hkv * kVPieces; x += kThreads) {
+    if (x < nk) {
+      const int gi = x % kKGroups, r = x / kKGroups;  // r = token * hkv + kv head
+      const int t = r / hkv, g = r - t * hkv;
+      const T* src = kn + ((size_t)t * hkv + g) * D + gi * kVec;
+      T* dst = kc + ((size_t)g * W + (head + t) % W) * D + gi * kVec;
+      const u32x4 u4 = *reinterpret_cast<const u32x4*>(src);
+      const u32x4 v4 = *reinterpret_cast<const u32x4*>(src + D / 2);
+      if (!rope) {
+        *reinterpret_cast<u32x4*>(dst) = u4;
+        *reinterpret_cast<u32x4*>(dst + D / 2) = v4;
+        continue;
+      }
+      T u[kVec], v[kVec], yu[kVec], yv[kVec];
+      __builtin_memcpy(u, &u4, 16);
+      __builtin_memcpy(v, &v4, 16);
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        const int i = gi * kVec + e;
+        float c, s;
+        if (table) {
+          c = cs[t * (D / 2) + i][0];
+          s = cs[t * (D / 2) + i][1];
+        } else {
+          rope_cos_sin(pos0 + t, i, D, a.log2_base, &c, &s);
+        }
+        const float fu = ldf(&u[e]), fv = ldf(&v[e]);
+        yu[e] = cvt<T>(fu * c - fv * s);
+        yv[e] = cvt<T>(fv * c + fu * s);
+      }
+      u32x4 o1, o2;
+      __builtin_memcpy(&o1, yu, 16);
+      __builtin_memcpy(&o2, yv, 16);
+      *reinterpret_cast<u32x4*>(dst) = o1;
+      *reinterpret_cast<u32x4*>(dst + D / 2) = o2;
     } else {
-      dst[i] = src[i];
-      dst[i + D / 2] = src[i + D / 2];
+      const int y = x - nk;
+      const int pc = y % kVPieces, r = y / kVPieces;
+      const int t = r / hkv, g = r - t * hkv;
+      *reinterpret_cast<u32x4*>(vc + ((size_t)g * W + (head + t) % W) * D + pc * kVec) =
+          *reinterpret_cast<const u32x4*>(vn + ((size_t)t * hkv + g) * D + pc * kVec);
     }
-  }
-  // values: one item per (token, kv head, element)
-  for (int x = threadIdx.x; x < n * hkv * D; x += kThreads) {
-    const int e = x % D;
-    const int r = x / D;
-    const int t = r / hkv, g = r - t * hkv;
-    vc[((size_t)g * W + (head + t) % W) * D + e] = vn[((size_t)t * hkv + g) * D + e];
   }
   __syncthreads();
   if (threadIdx.x == 0) a.ring_head[b] = (head + n) % W;

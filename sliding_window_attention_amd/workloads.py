@@ -26,7 +26,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "prefill" | "decode" | "decode_fp8" | "hybrid" | "varlen"
+    kind: str  # "prefill" | "decode" | "decode_fp8" | "decode_rope" | "hybrid" | "varlen"
     dtype: str  # "f32" | "bf16"
     seq_len: int = 0  # total packed tokens for prefill kinds
     num_q_heads: int = 32
@@ -53,6 +53,10 @@ WORKLOADS = {
     # The same two decode workloads against an FP8 (E4M3) ring with per-tensor scales.
     "decode_fp8_t1": Workload("decode_fp8_t1", "decode_fp8", "bf16", batch=256, t_new=1, seed=3200),
     "decode_fp8_t4": Workload("decode_fp8_t4", "decode_fp8", "bf16", batch=256, t_new=4, seed=3300),
+    # The same two decode workloads with unrotated q / new keys and positions (RoPE in
+    # the kernel, SWA base 10,000), and the commit of the accepted tokens to the ring.
+    "decode_rope_t1": Workload("decode_rope_t1", "decode_rope", "bf16", batch=256, t_new=1, seed=3400),
+    "decode_rope_t4": Workload("decode_rope_t4", "decode_rope", "bf16", batch=256, t_new=4, seed=3500),
     # Hybrid block: 5 SWA-sink layers (seeds 4000..4004) + 1 GA layer (seed 4005).
     "hybrid_5to1_32k": Workload("hybrid_5to1_32k", "hybrid", "bf16", seq_len=32768, seed=4000),
     # Packed varlen prefill: 8 log-normal sequence lengths summing to 262144.
@@ -221,6 +225,9 @@ def make_workload(name: str, layer: int = 0):
     if w.kind == "decode_fp8":
         return make_decode_fp8(w.batch, w.t_new, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                w.window, w.dtype, w.seed)
+    if w.kind == "decode_rope":
+        return make_decode_rope(w.batch, w.t_new, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                w.window, w.dtype, w.seed)
     raise KeyError(name)
 
 
@@ -281,11 +288,22 @@ def decode_bytes(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, elem
     return kv + qo + lse
 
 
+def append_bytes(batch, n_accepted_total, num_kv_heads, head_dim, elem_bytes):
+    """Ring append: the accepted tokens' K and V read once and written once, plus the
+    accept counts, positions and heads (read, heads written)."""
+    return 4 * n_accepted_total * num_kv_heads * head_dim * elem_bytes + 4 * 4 * batch
+
+
+def rope_bytes(rows, heads, head_dim, elem_bytes):
+    """In-place rotation: every element read and written once, plus one int32 position per row."""
+    return 2 * rows * heads * head_dim * elem_bytes + 4 * rows
+
+
 def workload_work(name: str):
     """(flops, bytes) of one pass of a named workload as its kind defines it."""
     w = WORKLOADS[name]
     eb = 4 if w.dtype == "f32" else 2
-    if w.kind in ("decode", "decode_fp8"):
+    if w.kind in ("decode", "decode_fp8", "decode_rope"):
         return (decode_flops(w.batch, w.t_new, w.num_q_heads, w.head_dim, w.window),
                 decode_bytes(w.batch, w.t_new, w.num_q_heads, w.num_kv_heads, w.head_dim,
                              w.window, eb, cache_elem_bytes=1 if w.kind == "decode_fp8" else None))

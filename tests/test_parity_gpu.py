@@ -850,3 +850,33 @@ def test_decode_and_append_steps_follow_the_oracle():
         diff = np.abs(to_np(g["k_cache"]) - kc)
         assert diff.max() <= 2.0 ** -6 * max(1.0, float(np.abs(kc).max())), f"step {step} ring keys"
         assert np.array_equal(to_np(g["v_cache"]), vc)
+
+
+@pytest.mark.parametrize("name", ["decode_rope_t1", "decode_rope_t4"])
+def test_decode_rope_full(name):
+    _say(f"{name}: every element of the benchmarked decode with RoPE (B=256)")
+    x = wl.make_workload(name)
+    o, lse = _run_decode_rope(x, 10000.0)
+    o_ref, l_ref = _oracle_decode_rope(x, 128, 10000.0)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, name)
+
+
+def test_ring_append_full_batch():
+    _say("ring append after the T = 4 verify of the benchmarked workload (B=256), every slot")
+    x = wl.make_workload("decode_rope_t4")
+    gen = torch.Generator().manual_seed(3501)
+    n_acc = torch.randint(0, 5, (256,), generator=gen, dtype=torch.int64).to(torch.int32)
+    g = _gpu(x)
+    swa.swa_ring_append_rope(g["k_new"], g["v_new"], n_acc.to(DEV), g["positions"], g["k_cache"],
+                             g["v_cache"], g["ring_head"], 10000.0)
+    torch.cuda.synchronize()
+    kc, vc, h2 = orc.swa_ring_append_rope(x["k_new"], x["v_new"], n_acc.numpy(), x["positions"].numpy(),
+                                          x["k_cache"], x["v_cache"], x["ring_head"].numpy(), 10000.0)
+    assert np.array_equal(g["ring_head"].cpu().numpy(), h2)
+    assert np.array_equal(to_np(g["v_cache"]), vc)
+    got = to_np(g["k_cache"])
+    # rotated keys: the fp32 rotation may round to the neighbouring bf16 value of the
+    # oracle's in rare near-ties; everything else is bit-identical
+    diff = got != kc
+    assert float(diff.mean()) < 1e-4
+    assert np.all(np.abs(got - kc)[diff] <= 2.0 ** -7 * np.abs(kc)[diff] + 1e-30)
