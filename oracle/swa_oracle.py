@@ -34,6 +34,17 @@ i + D/2, inverse frequency base^(-2i/D), angle = position times frequency), and
 rotated vectors are rounded to the I/O type, as a separate rotation pass that
 stores its result would.
 
+Token-level sparse attention with a forced recent window (topk_select,
+sparse_decode): the HySparse2 selection of the MiMo-V3 / HySparse2 report (page on
+the MiMo-V3 news, HySparse2 sections): the full-attention layer's scores pick the top
+k tokens (1024 there) and the most recent 128 tokens are always kept, the sparse
+layers attending to that set over the shared KV cache.  Readings where the pages are
+silent: the scores arrive per (sequence, KV head) over the cached positions; the top
+k are taken among the tokens older than the recent window (larger score first, the
+lower position on equal scores) and returned in increasing position; the query (the
+newest token) attends to those plus the recent window, with the sink of the other
+layers when one is given.
+
 Arithmetic is fp64 on the exact input values (bf16, fp32 and E4M3 convert to fp64
 exactly).  Rows are processed in blocks only to bound memory: every row is the
 definition above, computed independently, with no online rescaling and no
@@ -412,3 +423,58 @@ def swa_ring_append_rope(k_new, v_new, n_accept, positions, k_cache, v_cache, ri
             vc[b, :, slot, :] = v_new[b, t]
         new_heads[b] = (heads[b] + n) % w
     return kc, vc, new_heads
+
+
+def topk_select(scores, lengths, k=1024, recent=128):
+    """Token selection for the sparse layers.  scores [B, Hkv, Lmax] (finite floats);
+    lengths [B]: sequence b holds positions 0 .. lengths[b]-1 (the newest, the query's,
+    last).  Candidates are the positions older than the recent window, j < lengths[b] -
+    recent; the min(k, #candidates) with the largest scores are chosen, equal scores
+    broken towards the lower position.  Returns (indices [B, Hkv, k] int64 in increasing
+    position, padded with -1; counts [B, Hkv] int64)."""
+    sc = _as_f64(scores)
+    bsz, hkv, _ = sc.shape
+    lens = np.asarray(lengths, dtype=np.int64).reshape(bsz)
+    idx = np.full((bsz, hkv, k), -1, dtype=np.int64)
+    cnt = np.zeros((bsz, hkv), dtype=np.int64)
+    for b in range(bsz):
+        ncand = max(0, int(lens[b]) - recent)
+        for h in range(hkv):
+            cand = np.arange(ncand)
+            order = np.lexsort((cand, -sc[b, h, :ncand]))  # score descending, then position
+            chosen = np.sort(cand[order[:k]])
+            idx[b, h, :len(chosen)] = chosen
+            cnt[b, h] = len(chosen)
+    return idx, cnt
+
+
+def sparse_decode(q, k_cache, v_cache, lengths, indices, counts, sinks, recent=128, scale=None):
+    """One query token per sequence (the newest, at position lengths[b]-1) over the
+    selected older positions indices[b, g, :counts[b, g]] of its KV head g plus the
+    recent window max(0, L-recent) .. L-1.  q [B, Hq, D]; caches [B, Hkv, Lmax, D]
+    (token t of sequence b at [b, :, t]); sinks [Hq] or None.  Every query head reads its
+    group's selection.  Returns (o [B, Hq, D], lse [B, Hq])."""
+    q, kc, vc = _as_f64(q), _as_f64(k_cache), _as_f64(v_cache)
+    bsz, hq, d = q.shape
+    hkv = kc.shape[1]
+    grp = hq // hkv
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lens = np.asarray(lengths, dtype=np.int64).reshape(bsz)
+    idx = np.asarray(indices, dtype=np.int64)
+    cnt = np.asarray(counts, dtype=np.int64)
+    o = np.zeros((bsz, hq, d))
+    lse = np.zeros((bsz, hq))
+    for b in range(bsz):
+        L = int(lens[b])
+        rec = np.arange(max(0, L - recent), L)
+        for h in range(hq):
+            g = h // grp
+            keys = np.concatenate([idx[b, g, :cnt[b, g]], rec])
+            a = sc * (kc[b, g, keys] @ q[b, h])
+            sink = NEG_INF if sinks is None else float(_as_f64(sinks)[h])
+            m = max(a.max(), sink)
+            e = np.exp(a - m)
+            z = e.sum() + (np.exp(sink - m) if sink != NEG_INF else 0.0)
+            o[b, h] = (e @ vc[b, g, keys]) / z
+            lse[b, h] = m + np.log(z)
+    return o, lse

@@ -654,3 +654,103 @@ def test_ring_append_matches_a_list_model():
     k3, _, _ = orc.swa_ring_append_rope(kn, vn, n_acc, pos, kc, vc, heads, None)
     b, t = 2, 3
     np.testing.assert_array_equal(k3[b, :, (heads[b] + t) % w, :], kn[b, t])
+
+
+# ---------------------------------------------------------------------------
+# Token-level sparse attention with a forced recent window (MiMo-V3 / HySparse2 page)
+# ---------------------------------------------------------------------------
+
+def _brute_topk(scores_row, n_cand, k):
+    """Python's sorted() on (score descending, position ascending), then increasing position."""
+    pairs = sorted(((-float(scores_row[j]), j) for j in range(n_cand)))
+    return sorted(j for _, j in pairs[:k])
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(0, 40), st.integers(0, 12), st.integers(1, 6), st.integers(0, 3))
+def test_topk_select_matches_brute_force(length, k, recent, levels):
+    rng = np.random.default_rng(length * 1000 + k * 10 + recent)
+    lmax = 48
+    # levels > 0: scores drawn from a few values, so equal scores are common
+    sc = rng.standard_normal((2, 3, lmax)) if levels == 0 else rng.integers(0, levels + 1, (2, 3, lmax)) * 0.5
+    lens = np.array([length, max(0, length - 7)])
+    idx, cnt = orc.topk_select(sc, lens, k=k, recent=recent)
+    for b in range(2):
+        for h in range(3):
+            want = _brute_topk(sc[b, h], max(0, int(lens[b]) - recent), k)
+            assert cnt[b, h] == len(want)
+            assert list(idx[b, h, :cnt[b, h]]) == want
+            assert np.all(idx[b, h, cnt[b, h]:] == -1)
+
+
+def _sparse_case(bsz, hq, hkv, d, lmax, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((bsz, hq, d))
+    kc = rng.standard_normal((bsz, hkv, lmax, d))
+    vc = rng.standard_normal((bsz, hkv, lmax, d))
+    sinks = rng.standard_normal(hq)
+    scores = rng.standard_normal((bsz, hkv, lmax))
+    return q, kc, vc, sinks, scores
+
+
+def _prefill_last_row(q, kc, vc, sinks, b, L, window):
+    """The oracle's windowed prefill of sequence b's first L tokens, newest row only
+    (q placed on the newest token, zeros elsewhere)."""
+    hq, d = q.shape[1], q.shape[2]
+    qs = np.zeros((L, hq, d))
+    qs[L - 1] = q[b]
+    ks = kc[b, :, :L].transpose(1, 0, 2)
+    vs = vc[b, :, :L].transpose(1, 0, 2)
+    o, lse = orc.swa_sink_prefill(qs, ks, vs, sinks, [0, L], window)
+    return o[L - 1], lse[L - 1]
+
+
+def test_sparse_decode_special_cases_reduce_to_dense_attention():
+    """k covering every older token: full causal attention (window = L); k = 0: the
+    128-window SWA of the same layer -- both through the pinned prefill oracle."""
+    q, kc, vc, sinks, scores = _sparse_case(3, 4, 2, 16, 60, 21)
+    lens = np.array([60, 9, 33])
+    recent = 8
+    idx, cnt = orc.topk_select(scores, lens, k=64, recent=recent)  # k >= every candidate count
+    o, lse = orc.sparse_decode(q, kc, vc, lens, idx, cnt, sinks, recent=recent)
+    idx0, cnt0 = orc.topk_select(scores, lens, k=0, recent=recent)
+    o0, lse0 = orc.sparse_decode(q, kc, vc, lens, idx0, cnt0, sinks, recent=recent)
+    for b in range(3):
+        L = int(lens[b])
+        of, lf = _prefill_last_row(q, kc, vc, sinks, b, L, L)
+        np.testing.assert_allclose(o[b], of, atol=1e-12)
+        np.testing.assert_allclose(lse[b], lf, atol=1e-12)
+        ow, lw = _prefill_last_row(q, kc, vc, sinks, b, L, recent)
+        np.testing.assert_allclose(o0[b], ow, atol=1e-12)
+        np.testing.assert_allclose(lse0[b], lw, atol=1e-12)
+
+
+def test_sparse_decode_matches_brute_force_and_ignores_index_order():
+    q, kc, vc, sinks, scores = _sparse_case(2, 4, 2, 8, 40, 22)
+    lens = np.array([40, 25])
+    recent, k = 5, 6
+    idx, cnt = orc.topk_select(scores, lens, k=k, recent=recent)
+    o, lse = orc.sparse_decode(q, kc, vc, lens, idx, cnt, sinks, recent=recent)
+    for b in range(2):
+        L = int(lens[b])
+        for g in range(2):
+            keys = list(idx[b, g, :cnt[b, g]]) + list(range(L - recent, L))
+            m = len(keys)
+            # the key list as a causal sequence whose last row is the query: brute force
+            qs = [[[0.0] * 8 for _ in range(4)] for _ in range(m)]
+            for h in range(2 * g, 2 * g + 2):
+                qs[m - 1][h] = list(q[b, h])
+            ks = [[list(kc[b, gg, j]) for gg in range(2)] for j in keys]
+            vs = [[list(vc[b, gg, j]) for gg in range(2)] for j in keys]
+            ob, lb = brute.attention(qs, ks, vs, list(sinks), [0, m], None)
+            for h in range(2 * g, 2 * g + 2):
+                np.testing.assert_allclose(o[b, h], ob[m - 1][h], atol=1e-12)
+                assert abs(lse[b, h] - lb[m - 1][h]) < 1e-12
+    # reversing each selection list changes nothing
+    rev = idx.copy()
+    for b in range(2):
+        for g in range(2):
+            rev[b, g, :cnt[b, g]] = idx[b, g, :cnt[b, g]][::-1]
+    o2, l2 = orc.sparse_decode(q, kc, vc, lens, rev, cnt, sinks, recent=recent)
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    np.testing.assert_allclose(l2, lse, atol=1e-12)
