@@ -57,7 +57,7 @@ typedef enum {
 
 typedef enum { SWA_DTYPE_F32 = 0, SWA_DTYPE_BF16 = 1 } swa_dtype;
 
-#define SWASINK_ABI_VERSION 4
+#define SWASINK_ABI_VERSION 5
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SWASINK_API __attribute__((visibility("default")))
@@ -239,6 +239,50 @@ SWASINK_API int swa_ring_append_rope(const void* k_new, const void* v_new, const
                     const int32_t* positions, void* k_cache, void* v_cache, int32_t* ring_head,
                     int32_t batch, int32_t T, int32_t num_kv_heads, int32_t head_dim,
                     int32_t window, float rope_base, swa_dtype dtype, void* stream);
+
+/*
+ * Token selection for sparse attention with a forced recent window (the HySparse2
+ * selection of the MiMo-V3 / HySparse2 report: top k tokens by the full-attention
+ * layer's scores, 1024 there, plus the most recent 128 always kept).  For each
+ * (sequence b, KV head g) row, the candidates are the positions older than the recent
+ * window, j < lengths[b] - recent; the min(k, #candidates) with the largest scores are
+ * chosen, equal scores going to the lower position, NaN ranking below every number.
+ * Exact and deterministic.
+ *
+ *  scores   [batch, num_kv_heads, max_len] fp32 (position j of sequence b at [b, g, j])
+ *  lengths  [batch] int32 device array, clamped to [0, max_len]
+ *  indices  [batch, num_kv_heads, k] int32: chosen positions in increasing order, -1 past
+ *           the count
+ *  counts   [batch, num_kv_heads] int32
+ * Requires k >= 0, recent >= 1, max_len >= 1.  batch == 0 is accepted (pointers may then
+ * be NULL).
+ */
+SWASINK_API int swa_topk_select(const float* scores, const int32_t* lengths, int32_t batch,
+                    int32_t num_kv_heads, int32_t max_len, int32_t k, int32_t recent,
+                    int32_t* indices, int32_t* counts, void* stream);
+
+/*
+ * Sparse decode: one query token per sequence -- the newest, at position
+ * lengths[b] - 1 -- attends its KV head's selected positions indices[b, g, :counts[b, g]]
+ * plus the recent window max(0, L - recent) .. L - 1, with the sink in the denominator
+ * when sinks is given (the operator of swa_sink_prefill on that key set).
+ *
+ *  q            [batch, num_q_heads, head_dim] dtype
+ *  k_cache, v_cache [batch, num_kv_heads, max_len, head_dim] dtype (the full-attention
+ *               layer's cache, shared with the sparse layers)
+ *  lengths      [batch] int32, clamped to [1, max_len]
+ *  indices, counts  as written by swa_topk_select (the listed positions must be distinct
+ *               and older than the recent window; out-of-range entries are clamped into the
+ *               sequence, never read out of bounds); counts clamped to [0, k]
+ *  sinks        [num_q_heads] fp32, or NULL (no sink)
+ *  out          [batch, num_q_heads, head_dim] dtype;  lse [batch, num_q_heads] fp32 or NULL
+ * Requires recent >= 1 and k + recent <= 8192.  batch == 0 is accepted.
+ */
+SWASINK_API int swa_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* lengths, const int32_t* indices, const int32_t* counts,
+                    const float* sinks, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t max_len, int32_t k, int32_t recent, float scale,
+                    swa_dtype dtype, void* out, float* lse, void* stream);
 
 /* Message for the last non-OK return on the calling thread ("" if none). */
 SWASINK_API const char* swa_last_error(void);

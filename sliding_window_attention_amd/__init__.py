@@ -44,7 +44,13 @@ _SIGNATURES = {
     "swa_sink_decode_rope": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I,
                              _P, _P, _P],
     "swa_ring_append_rope": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P],
+    "swa_topk_select": [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P],
+    "swa_sparse_decode": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P],
 }
+
+# HySparse2 selection sizes (MiMo-V3 / HySparse2 report): top 1024 plus the recent 128.
+SPARSE_TOPK = 1024
+SPARSE_RECENT = 128
 
 # Rotary bases the pages give (technical report digest, section 3.1).
 ROPE_BASE_SWA = 10000.0
@@ -336,6 +342,65 @@ def swa_ring_append_rope(k_new, v_new, n_accept, positions, k_cache, v_cache, ri
         v_cache.data_ptr(), ring_head.data_ptr(), b, t, hkv, d, w, float(rope_base),
         _dtype_code(k_new), _stream(k_new.device))
     _check(rc)
+
+
+def swa_topk_select(scores, lengths, k=SPARSE_TOPK, recent=SPARSE_RECENT, indices=None, counts=None):
+    """Top-k positions older than the recent window per (sequence, KV head) row of
+    scores [B, Hkv, Lmax] fp32 (lengths [B] int32).  Returns (indices [B, Hkv, k] int32
+    increasing, -1 padded; counts [B, Hkv] int32)."""
+    import torch
+
+    _dev(scores, "scores", torch.float32)
+    _dev(lengths, "lengths", torch.int32)
+    if scores.dim() != 3 or lengths.numel() != scores.shape[0]:
+        raise ValueError("scores must be [B, Hkv, Lmax] with one length per sequence")
+    b, hkv, lmax = scores.shape
+    if indices is None:
+        indices = torch.empty((b, hkv, k), dtype=torch.int32, device=scores.device)
+    if counts is None:
+        counts = torch.empty((b, hkv), dtype=torch.int32, device=scores.device)
+    _dev(indices, "indices", torch.int32)
+    _dev(counts, "counts", torch.int32)
+    rc = library().swa_topk_select(scores.data_ptr(), lengths.data_ptr(), b, hkv, lmax, k, recent,
+                                   indices.data_ptr(), counts.data_ptr(), _stream(scores.device))
+    _check(rc)
+    return indices, counts
+
+
+def swa_sparse_decode(q, k_cache, v_cache, lengths, indices, counts, sinks=None, recent=SPARSE_RECENT,
+                      scale=None, return_lse=True, out=None, lse=None):
+    """The newest token of each sequence (q [B, Hq, D]) over its selected positions plus
+    the recent window of a [B, Hkv, Lmax, D] cache."""
+    import torch
+
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, nm, q.dtype)
+    _dev(lengths, "lengths", torch.int32)
+    _dev(indices, "indices", torch.int32)
+    _dev(counts, "counts", torch.int32)
+    if sinks is not None:
+        _dev(sinks, "sinks", torch.float32)
+    if q.dim() != 3 or k_cache.dim() != 4 or indices.dim() != 3:
+        raise ValueError("q must be [B, Hq, D], caches [B, Hkv, Lmax, D], indices [B, Hkv, k]")
+    b, hq, d = q.shape
+    hkv, lmax = k_cache.shape[1], k_cache.shape[2]
+    k = indices.shape[2]
+    if (k_cache.shape != (b, hkv, lmax, d) or v_cache.shape != k_cache.shape or lengths.numel() != b
+            or indices.shape[:2] != (b, hkv) or counts.shape != (b, hkv)
+            or (sinks is not None and sinks.numel() != hq)):
+        raise ValueError("inconsistent shapes")
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    if return_lse and lse is None:
+        lse = torch.empty((b, hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+    rc = library().swa_sparse_decode(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lengths.data_ptr(), indices.data_ptr(),
+        counts.data_ptr(), sinks.data_ptr() if sinks is not None else None, b, hq, hkv, d, lmax, k, recent,
+        _scale(scale), _dtype_code(q), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        _stream(q.device))
+    _check(rc)
+    return out, lse
 
 
 def swa_sink_prefill_backward(q, k, v, sinks, cu_seqlens, out, lse, dout, max_seqlen=None,

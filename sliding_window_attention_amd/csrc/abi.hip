@@ -280,6 +280,49 @@ int swa_ring_append_rope(const void* k_new, const void* v_new, const int32_t* n_
                     name);
 }
 
+int swa_topk_select(const float* scores, const int32_t* lengths, int32_t batch, int32_t num_kv_heads,
+                    int32_t max_len, int32_t k, int32_t recent, int32_t* indices, int32_t* counts,
+                    void* stream) {
+  const char* name = "swa_topk_select";
+  if (batch < 0 || num_kv_heads < 1 || max_len < 1)
+    return fail(SWA_ERR_SHAPE, "%s: batch >= 0, num_kv_heads >= 1 and max_len >= 1 are required", name);
+  if (k < 0 || recent < 1) return fail(SWA_ERR_SHAPE, "%s: k must be >= 0 and recent >= 1", name);
+  if ((long long)batch * num_kv_heads * max_len > (1LL << 40))
+    return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
+  if (batch == 0) return ok();
+  if (!scores || !lengths || !counts || (k > 0 && !indices))
+    return fail(SWA_ERR_NULL, "%s: scores, lengths, indices and counts must be non-NULL", name);
+  swa::TopkArgs a;
+  a.scores = scores; a.lengths = lengths; a.indices = indices; a.counts = counts;
+  a.batch = batch; a.num_kv_heads = num_kv_heads; a.max_len = max_len; a.k = k; a.recent = recent;
+  return hip_status(swa::launch_topk_select(a, static_cast<hipStream_t>(stream)), name);
+}
+
+int swa_sparse_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* lengths,
+                      const int32_t* indices, const int32_t* counts, const float* sinks, int32_t batch,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_len,
+                      int32_t k, int32_t recent, float scale, swa_dtype dtype, void* out, float* lse,
+                      void* stream) {
+  const char* name = "swa_sparse_decode";
+  int rc = check_dtype((int)dtype);
+  if (rc) return rc;
+  if ((rc = check_heads(num_q_heads, num_kv_heads, head_dim))) return rc;
+  if (batch < 0 || max_len < 1) return fail(SWA_ERR_SHAPE, "%s: batch >= 0 and max_len >= 1 are required", name);
+  if (k < 0 || recent < 1 || (long long)k + recent > 8192)
+    return fail(SWA_ERR_SHAPE, "%s: k >= 0, recent >= 1 and k + recent <= 8192 are required", name);
+  if ((long long)batch * num_kv_heads * max_len * head_dim > (1LL << 40))
+    return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
+  if (batch == 0) return ok();
+  if (!q || !k_cache || !v_cache || !lengths || !counts || !out || (k > 0 && !indices))
+    return fail(SWA_ERR_NULL, "%s: q, k_cache, v_cache, lengths, indices, counts and out must be non-NULL", name);
+  swa::SparseArgs a;
+  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.lengths = lengths; a.indices = indices;
+  a.counts = counts; a.sinks = sinks; a.out = out; a.lse = lse;
+  a.batch = batch; a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
+  a.max_len = max_len; a.k = k; a.recent = recent; a.scale = resolve_scale(scale, head_dim);
+  return hip_status(swa::launch_sparse_decode(a, dtype == SWA_DTYPE_BF16, static_cast<hipStream_t>(stream)), name);
+}
+
 int64_t swa_sink_prefill_backward_workspace(int32_t total_tokens, int32_t num_q_heads) {
   return backward_workspace_bytes(total_tokens, num_q_heads);
 }

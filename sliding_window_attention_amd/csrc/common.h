@@ -99,6 +99,41 @@ struct AppendArgs {
   double log2_base;
 };
 
+// Token selection for the sparse layers: per (sequence, KV head) row of scores, the top
+// k positions older than the recent window.
+struct TopkArgs {
+  const float* scores;    // [B, Hkv, Lmax]
+  const int32_t* lengths;  // [B]
+  int32_t* indices;       // [B, Hkv, k] increasing, padded with -1
+  int32_t* counts;        // [B, Hkv]
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t max_len;
+  int32_t k;
+  int32_t recent;
+};
+
+// One query token per sequence over selected + recent keys of a [B, Hkv, Lmax, D] cache.
+struct SparseArgs {
+  const void* q;             // [B, Hq, D]
+  const void* k_cache;       // [B, Hkv, Lmax, D]
+  const void* v_cache;
+  const int32_t* lengths;    // [B]
+  const int32_t* indices;    // [B, Hkv, k]
+  const int32_t* counts;     // [B, Hkv]
+  const float* sinks;        // [Hq] or nullptr
+  void* out;                 // [B, Hq, D]
+  float* lse;                // [B, Hq] or nullptr
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_len;
+  int32_t k;
+  int32_t recent;
+  float scale;
+};
+
 // Arguments of the backward (gradients of O).  Pointers are device pointers.
 struct BackwardArgs {
   const void* q;             // [N, Hq, D]

@@ -108,6 +108,25 @@ struct DecodeKeys {
   }
 };
 
+// Keys of the sparse decode: list entry m < cnt is the selected position sel[m]
+// (clamped into the sequence), then the recent window L - nrec .. L - 1.
+template <typename T, int D>
+struct SparseKeys {
+  const T* kc;  // this (sequence, kv head)'s cache rows: [Lmax, D]
+  const T* vc;
+  const int32_t* sel;
+  int cnt, L, nrec;
+  __device__ int pos(int m) const {
+    if (m < cnt) {
+      const int j = sel[m];
+      return j < 0 ? 0 : (j >= L ? L - 1 : j);
+    }
+    return L - nrec + (m - cnt);
+  }
+  __device__ void load_key(int m, int d, float* dst) const { Elem<T>::load16(kc + (size_t)pos(m) * D + d, dst); }
+  __device__ float load_val(int m, int e) const { return Elem<T>::load1(vc + (size_t)pos(m) * D + e); }
+};
+
 // One wavefront computes one row against keys jlo..jhi (inclusive, jlo <= jhi).
 template <typename T, int D, class Keys>
 __device__ void attend_row(const T* __restrict__ qrow, const Keys& keys, int jlo, int jhi,
@@ -229,6 +248,41 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void generic_decode_kernel(D
 }
 
 template <typename T, int D>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void generic_sparse_kernel(SparseArgs a) {
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int hq = a.num_q_heads;
+  if (row >= a.batch * hq) return;
+  const int b = row / hq, h = row - b * hq;
+  const int hkv = a.num_kv_heads;
+  const int kvh = h / (hq / hkv);
+  int L = a.lengths[b];
+  L = L < 1 ? 1 : (L > a.max_len ? a.max_len : L);
+  int cnt = a.counts[b * hkv + kvh];
+  cnt = cnt < 0 ? 0 : (cnt > a.k ? a.k : cnt);
+  SparseKeys<T, D> keys;
+  keys.kc = static_cast<const T*>(a.k_cache) + ((size_t)b * hkv + kvh) * a.max_len * D;
+  keys.vc = static_cast<const T*>(a.v_cache) + ((size_t)b * hkv + kvh) * a.max_len * D;
+  keys.sel = a.indices + ((size_t)b * hkv + kvh) * a.k;
+  keys.cnt = cnt;
+  keys.L = L;
+  keys.nrec = a.recent < L ? a.recent : L;
+  const int M = cnt + keys.nrec;
+  const float sink2 = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
+  attend_row<T, D>(static_cast<const T*>(a.q) + (size_t)row * D, keys, 0, M - 1, sink2, a.scale * kLog2e,
+                   static_cast<T*>(a.out) + (size_t)row * D, a.lse ? a.lse + row : nullptr);
+}
+
+template <typename T, int D>
+hipError_t launch_sparse_t(const SparseArgs& a, hipStream_t s) {
+  const long rows = (long)a.batch * a.num_q_heads;
+  const long blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((generic_sparse_kernel<T, D>), dim3((unsigned)blocks), dim3(kRowsPerBlock * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
   const long rows = (long)a.total_tokens * a.num_q_heads;
   const long blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -257,6 +311,11 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_generic_prefill(const PrefillArgs& a, bool bf16_io, hipStream_t s) {
   if (bf16_io) return a.head_dim == 64 ? launch_prefill_t<bf16, 64>(a, s) : launch_prefill_t<bf16, 128>(a, s);
   return a.head_dim == 64 ? launch_prefill_t<float, 64>(a, s) : launch_prefill_t<float, 128>(a, s);
+}
+
+hipError_t launch_generic_sparse(const SparseArgs& a, bool bf16_io, hipStream_t s) {
+  if (bf16_io) return a.head_dim == 64 ? launch_sparse_t<bf16, 64>(a, s) : launch_sparse_t<bf16, 128>(a, s);
+  return a.head_dim == 64 ? launch_sparse_t<float, 64>(a, s) : launch_sparse_t<float, 128>(a, s);
 }
 
 hipError_t launch_generic_decode(const DecodeArgs& a, bool bf16_io, hipStream_t s) {

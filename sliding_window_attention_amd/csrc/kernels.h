@@ -9,6 +9,7 @@ namespace swa {
 // Shape-general vector-ALU kernels (fp32 or bf16 I/O, head_dim 64 or 128).
 hipError_t launch_generic_prefill(const PrefillArgs& a, bool bf16_io, hipStream_t s);
 hipError_t launch_generic_decode(const DecodeArgs& a, bool bf16_io, hipStream_t s);
+hipError_t launch_generic_sparse(const SparseArgs& a, bool bf16_io, hipStream_t s);
 
 // Matrix-core kernels: bf16 I/O, head_dim 128, query heads per KV head a multiple of 8.
 // Sliding window of at most 128 keys, whole window held in registers.
@@ -30,6 +31,11 @@ hipError_t launch_backward_mfma(const BackwardArgs& a, hipStream_t s);
 // accepted tokens (keys rotated on the way in when a.rope_pos is set).
 hipError_t launch_rope(const RopeArgs& a, bool bf16_io, hipStream_t s);
 hipError_t launch_ring_append(const AppendArgs& a, bool bf16_io, hipStream_t s);
+
+// Token-level top-k selection and the sparse decode over selected + recent keys.
+hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
+bool sparse_mfma_supported(const SparseArgs& a, bool bf16_io);
+hipError_t launch_sparse_decode(const SparseArgs& a, bool bf16_io, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 hipError_t device_cu_count(int* out);

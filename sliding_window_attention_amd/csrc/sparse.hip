@@ -1,0 +1,381 @@
+// Token-level sparse attention with a forced recent window (the HySparse2 selection of
+// the MiMo-V3 / HySparse2 report: the full-attention layer's scores pick the top k
+// tokens -- 1024 there -- and the most recent 128 tokens are always kept; the sparse
+// layers attend to that set over the shared KV cache).
+//
+//  * topk_select_kernel: one workgroup per (sequence, KV head) row of scores.  The
+//    candidates are the positions older than the recent window.  A radix select over
+//    an order-preserving 32-bit key finds the k-th largest score (four 8-bit histogram
+//    passes); one ordered pass then writes the chosen positions in increasing order:
+//    every score above the threshold, and the lowest positions among those equal to
+//    it, so the result is exact and deterministic (no floating point decides a rank).
+//  * sparse_decode_kernel: one workgroup per (sequence, head octet); the key list
+//    (selected positions, then the recent window) is staged in LDS, and the four
+//    wavefronts take 32-key chunks in turn: K rows gathered straight into MFMA A
+//    operands, S^T = K Q^T for the octet's 8 heads, an online softmax per head, V rows
+//    transposed in registers for O^T += V^T P^T.  The wavefronts' partial results are
+//    merged exactly through LDS, with the sink in the denominator.
+#include "common.h"
+#include "kernels.h"
+#include "mfma_tile.h"
+
+namespace swa {
+namespace {
+
+using namespace tile;
+
+// ---------------------------------------------------------------------------
+// top-k selection
+// ---------------------------------------------------------------------------
+
+constexpr int kSelThreads = 512;  // 8 wavefronts
+constexpr int kSelPer = 8;        // consecutive candidates per thread in the ordered pass
+
+// Larger float -> larger key; NaN below every number.  The scores are read as their
+// 32-bit patterns: the device code is built without NaN semantics, under which a test
+// on a float value (even through its bits) may be folded away.
+__device__ __forceinline__ uint32_t order_key(uint32_t u) {
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive prefix sum over the workgroup (one value per thread); `tmp` holds one slot
+// per wavefront.  Returns the inclusive sum; *total receives the workgroup's total.
+__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t x, uint32_t* tmp, uint32_t* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[w] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int v = 0; v < kSelThreads / 64; ++v) {
+    const uint32_t t = tmp[v];
+    before += v < w ? t : 0u;
+    all += t;
+  }
+  __syncthreads();  // tmp may be reused by the caller's next scan
+  *total = all;
+  return x + before;
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t tmp[kSelThreads / 64];
+  __shared__ uint32_t pick[2];
+  const int row = blockIdx.x;  // sequence * Hkv + KV head
+  const int b = row / a.num_kv_heads;
+  const int tid = threadIdx.x;
+  int L = a.lengths[b];
+  L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
+  const int ncand = L - a.recent > 0 ? L - a.recent : 0;
+  const int K = a.k;
+  const uint32_t* sc = reinterpret_cast<const uint32_t*>(a.scores) + (size_t)row * a.max_len;
+  int32_t* out = a.indices + (size_t)row * K;
+  if (ncand <= K || K == 0) {  // every candidate is chosen, or none is asked for
+    for (int x = tid; x < K; x += kSelThreads) out[x] = x < ncand ? x : -1;
+    if (tid == 0) a.counts[row] = ncand < K ? ncand : K;
+    return;
+  }
+
+  // ---- radix select of the K-th largest key, 8 bits per pass from the top ----
+  uint32_t prefix = 0, mask = 0;
+  int rem = K;  // how many of the keys matching `prefix` are still to be chosen
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int x = tid; x < 256; x += kSelThreads) hist[x] = 0;
+    __syncthreads();
+    for (int j = tid; j < ncand; j += kSelThreads) {
+      const uint32_t u = order_key(sc[j]);
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {  // one wavefront: lane l owns bins 4l .. 4l+3; suffix sums from the top bin
+      uint32_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = hist[4 * tid + e];
+      const uint32_t mine = h[0] + h[1] + h[2] + h[3];
+      uint32_t suf = mine;  // inclusive suffix over lanes >= tid
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_down(suf, o);
+        if (tid + o < 64) suf += y;
+      }
+      uint32_t acc = suf - mine;  // keys in bins above this lane's
+      if (acc < (uint32_t)rem && (uint32_t)rem <= suf) {
+        int d = 4 * tid + 3;
+        for (int e = 3; e >= 0; --e, --d) {
+          if (acc + h[e] >= (uint32_t)rem) break;
+          acc += h[e];
+        }
+        pick[0] = (uint32_t)d;
+        pick[1] = (uint32_t)rem - acc;
+      }
+    }
+    __syncthreads();
+    prefix |= pick[0] << shift;
+    mask |= 255u << shift;
+    rem = (int)pick[1];
+    __syncthreads();  // pick and hist are rewritten by the next pass
+  }
+  const uint32_t T = prefix;  // the K-th largest key; `rem` of the keys equal to it are taken
+
+  // ---- ordered pass: position of a chosen candidate j = (# above T before j) +
+  // min(# equal to T before j, rem) ----
+  uint32_t gt_run = 0, eq_run = 0;
+  for (int c0 = 0; c0 < ncand; c0 += kSelThreads * kSelPer) {
+    const int j0 = c0 + tid * kSelPer;
+    uint32_t key[kSelPer];
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e) {
+      const int j = j0 + e;
+      key[e] = j < ncand ? order_key(sc[j]) : 0u;
+      ngt += (j < ncand && key[e] > T) ? 1u : 0u;
+      neq += (j < ncand && key[e] == T) ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t incl = block_inclusive_scan((ngt << 16) | neq, tmp, &tot);
+    uint32_t gt_b = gt_run + ((incl >> 16) - ngt), eq_b = eq_run + ((incl & 0xffffu) - neq);
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e) {
+      const int j = j0 + e;
+      if (j >= ncand) break;
+      if (key[e] > T) {
+        out[gt_b + min(eq_b, (uint32_t)rem)] = j;
+        ++gt_b;
+      } else if (key[e] == T) {
+        if (eq_b < (uint32_t)rem) out[gt_b + eq_b] = j;
+        ++eq_b;
+      }
+    }
+    gt_run += tot >> 16;
+    eq_run += tot & 0xffffu;
+  }
+  if (tid == 0) a.counts[row] = K;
+}
+
+// ---------------------------------------------------------------------------
+// sparse decode (bf16, head_dim 128, heads per KV head a multiple of 8)
+// ---------------------------------------------------------------------------
+
+constexpr int kSpThreads = 256;
+constexpr int kHG = 8;                 // query heads per workgroup
+constexpr int kMaxList = 8192;         // selected + recent keys staged in LDS
+constexpr int kQPitch = 272;           // staged bf16 query row, padded
+constexpr int kOPitch = D + 4;         // fp32 partial row, padded
+
+struct SparseSmem {
+  int32_t keys[kMaxList];
+  char q[16][kQPitch];                 // 8 query heads; columns 8..15 zero
+  float m[4][16], l[4][16];
+  float o[3][16][kOPitch];             // partial O of wavefronts 1..3
+};
+
+__global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs a) {
+  __shared__ __attribute__((aligned(16))) SparseSmem sm;
+  const int noct = a.num_q_heads / kHG;
+  const int b = blockIdx.x / noct;
+  const int oct = blockIdx.x - b * noct;
+  const int h_base = oct * kHG;
+  const int hkv = a.num_kv_heads;
+  const int kvh = h_base / (a.num_q_heads / hkv);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 15, g = lane >> 4;
+
+  int L = as_const(a.lengths)[b];
+  L = L < 1 ? 1 : (L > a.max_len ? a.max_len : L);
+  int cnt = as_const(a.counts)[b * hkv + kvh];
+  cnt = cnt < 0 ? 0 : (cnt > a.k ? a.k : cnt);
+  const int nrec = a.recent < L ? a.recent : L;
+  const int M = cnt + nrec;  // keys of the list (<= kMaxList: checked on the host)
+
+  // ---- stage the key list and the 8 query rows ----
+  const int32_t* sel = a.indices + ((size_t)b * hkv + kvh) * a.k;
+  for (int m = tid; m < M; m += kSpThreads) {
+    int j;
+    if (m < cnt) {
+      j = sel[m];
+      j = j < 0 ? 0 : (j >= L ? L - 1 : j);  // keeps every access in bounds
+    } else {
+      j = L - nrec + (m - cnt);
+    }
+    sm.keys[m] = j;
+  }
+  {
+    const int r = tid >> 4, u = tid & 15;  // 16 rows x 16 units
+    u32x4 x = {0, 0, 0, 0};
+    if (r < kHG)
+      x = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(a.q) +
+                                           ((size_t)b * a.num_q_heads + h_base + r) * D + 8 * u);
+    *reinterpret_cast<u32x4*>(&sm.q[r][16 * u]) = x;
+  }
+  __syncthreads();
+
+  const bf16* kc = static_cast<const bf16*>(a.k_cache) + ((size_t)b * hkv + kvh) * a.max_len * D;
+  const bf16* vc = static_cast<const bf16*>(a.v_cache) + ((size_t)b * hkv + kvh) * a.max_len * D;
+  const float c = a.scale * kLog2e;
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  bf16x8 qop[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) qop[cc] = *reinterpret_cast<const bf16x8*>(&sm.q[i][16 * (4 * cc + g)]);
+
+  // operands of one 32-key chunk: K rows pair_row(i, s) (A operand, head-dim 32cc + 8g),
+  // V rows 8g + e (head-dim 8i .. 8i+7); keys past the list read the last key (their
+  // weight is zero)
+  const int nchunks = (M + 31) >> 5;
+  auto load_chunk = [&](int ch, bf16x8 (&kf)[2][4], bf16x8 (&vr)[8]) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int m = 32 * ch + pair_row(i, s);
+      const int j = sm.keys[m < M ? m : M - 1];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        kf[s][cc] = *reinterpret_cast<const bf16x8*>(kc + (size_t)j * D + 32 * cc + 8 * g);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int m = 32 * ch + 8 * g + e;
+      const int j = sm.keys[m < M ? m : M - 1];
+      vr[e] = *reinterpret_cast<const bf16x8*>(vc + (size_t)j * D + 8 * i);
+    }
+  };
+
+  float mcol = -INFINITY, lcol = 0.f;  // running max (log2 units) and sum of column i
+  f32x4 o[8];
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) o[bb] = zero4;
+  bf16x8 kf[2][4], vr[8], nkf[2][4], nvr[8];
+  if (w < nchunks) load_chunk(w, kf, vr);
+  for (int ch = w; ch < nchunks; ch += 4) {
+    const bool more = ch + 4 < nchunks;
+    if (more) load_chunk(ch + 4, nkf, nvr);
+    f32x4 s2[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      s2[s] = zero4;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) s2[s] = mfma32(kf[s][cc], qop[cc], s2[s]);
+    }
+    // lane (i, g) holds keys 8g + 4s + r of the chunk for column i
+    float mx = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = 32 * ch + 8 * g + 4 * s + r < M;
+        s2[s][r] = ok ? s2[s][r] * c : -INFINITY;
+        mx = fmaxf(mx, s2[s][r]);
+      }
+    const float mnew = fmaxf(mcol, quad_max(mx));  // finite: the chunk's first key is valid
+    const float alpha = fast_exp2(mcol - mnew);
+    float ps = 0.f;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s2[s][r] = fast_exp2(s2[s][r] - mnew);
+        ps += s2[s][r];
+      }
+    lcol = lcol * alpha + quad_sum(ps);
+    mcol = mnew;
+    const bf16x8 pp = pack_pair(s2[0], s2[1]);
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) {
+      o[bb] *= alpha;
+      o[bb] = mfma32(column8(vr, bb), pp, o[bb]);
+    }
+    if (more) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) kf[s][cc] = nkf[s][cc];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vr[e] = nvr[e];
+    }
+  }
+
+  // ---- exact merge of the four wavefronts' partials (lane (i, g): column i,
+  // head-dim 32g + 8r + bb in register r of block bb) ----
+  if (g == 0) {
+    sm.m[w][i] = mcol;
+    sm.l[w][i] = lcol;
+  }
+  if (w > 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* row = &sm.o[w - 1][i][32 * g + 8 * r];
+      *reinterpret_cast<f32x4*>(row) = (f32x4){o[0][r], o[1][r], o[2][r], o[3][r]};
+      *reinterpret_cast<f32x4*>(row + 4) = (f32x4){o[4][r], o[5][r], o[6][r], o[7][r]};
+    }
+  }
+  __syncthreads();
+  if (w != 0 || i >= kHG) return;
+  const int h = h_base + i;
+  const float sink2 = a.sinks ? as_const(a.sinks)[h] * kLog2e : -INFINITY;
+  float mt = sink2;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) mt = fmaxf(mt, sm.m[v][i]);
+  float z = a.sinks ? fast_exp2(sink2 - mt) : 0.f;
+  float sc[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    sc[v] = fast_exp2(sm.m[v][i] - mt);  // 0 for a wavefront that had no chunk
+    z += sm.l[v][i] * sc[v];
+  }
+  const float inv = 1.f / z;
+  bf16* out = static_cast<bf16*>(a.out) + ((size_t)b * a.num_q_heads + h) * D;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float acc[8];
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) acc[bb] = o[bb][r] * sc[0];
+#pragma unroll
+    for (int v = 1; v < 4; ++v) {
+      const float* row = &sm.o[v - 1][i][32 * g + 8 * r];
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(row);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(row + 4);
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        acc[bb] = fmaf(lo[bb], sc[v], acc[bb]);
+        acc[bb + 4] = fmaf(hi[bb], sc[v], acc[bb + 4]);
+      }
+    }
+    bf16x8 v8;
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) v8[bb] = (bf16)(acc[bb] * inv);
+    *reinterpret_cast<bf16x8*>(out + 32 * g + 8 * r) = v8;
+  }
+  if (a.lse != nullptr && g == 0) a.lse[(size_t)b * a.num_q_heads + h] = (mt + fast_log2(z)) * kLn2;
+}
+
+}  // namespace
+
+hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s) {
+  const long rows = (long)a.batch * a.num_kv_heads;
+  if (rows == 0) return hipSuccess;
+  if (rows > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+bool sparse_mfma_supported(const SparseArgs& a, bool bf16_io) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+  return bf16_io && a.head_dim == 128 && G % kHG == 0 && (long)a.k + a.recent <= kMaxList;
+}
+
+hipError_t launch_sparse_decode(const SparseArgs& a, bool bf16_io, hipStream_t s) {
+  if (!sparse_mfma_supported(a, bf16_io)) return launch_generic_sparse(a, bf16_io, s);
+  const long blocks = (long)a.batch * (a.num_q_heads / kHG);
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(sparse_decode_kernel, dim3((unsigned)blocks), dim3(kSpThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace swa

@@ -26,7 +26,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "prefill" | "decode" | "decode_fp8" | "decode_rope" | "hybrid" | "varlen"
+    kind: str  # "prefill" | "decode" | "decode_fp8" | "decode_rope" | "sparse" | "hybrid" | "varlen"
     dtype: str  # "f32" | "bf16"
     seq_len: int = 0  # total packed tokens for prefill kinds
     num_q_heads: int = 32
@@ -57,6 +57,11 @@ WORKLOADS = {
     # the kernel, SWA base 10,000), and the commit of the accepted tokens to the ring.
     "decode_rope_t1": Workload("decode_rope_t1", "decode_rope", "bf16", batch=256, t_new=1, seed=3400),
     "decode_rope_t4": Workload("decode_rope_t4", "decode_rope", "bf16", batch=256, t_new=4, seed=3500),
+    # Sparse decode (HySparse2 selection: top 1024 + the recent 128) for 64 sequences of
+    # 16K-32K cached tokens over a [64, 4, 32768, 128] cache; the scores stand for the
+    # full-attention layer's (no sink in the sparse layers).
+    "sparse_b64": Workload("sparse_b64", "sparse", "bf16", seq_len=32768, batch=64, t_new=1, seed=6000,
+                           extra={"topk": 1024, "recent": 128, "min_len": 16384}),
     # Hybrid block: 5 SWA-sink layers (seeds 4000..4004) + 1 GA layer (seed 4005).
     "hybrid_5to1_32k": Workload("hybrid_5to1_32k", "hybrid", "bf16", seq_len=32768, seed=4000),
     # Packed varlen prefill: 8 log-normal sequence lengths summing to 262144.
@@ -144,6 +149,60 @@ def make_decode_rope(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, 
     x["positions"] = torch.randint(window, max_position, (batch,), generator=gen,
                                    dtype=torch.int64).to(torch.int32)
     return x
+
+
+def make_sparse(batch, num_q_heads, num_kv_heads, head_dim, max_len, dtype, seed, min_len=1,
+                with_sinks=True):
+    """Sparse-decode inputs: q [B, Hq, D] (the newest token of each sequence), caches
+    [B, Hkv, Lmax, D], lengths [B] int32 ~ U[min_len, max_len], sinks [Hq] fp32 (or None)
+    and the full-attention layer's scores [B, Hkv, Lmax] fp32 ~ N(0, 1).  CPU tensors."""
+    gen = torch.Generator().manual_seed(int(seed))
+    td = _torch_dtype(dtype)
+    q = torch.randn(batch, num_q_heads, head_dim, generator=gen).to(td)
+    k_cache = torch.randn(batch, num_kv_heads, max_len, head_dim, generator=gen).to(td)
+    v_cache = torch.randn(batch, num_kv_heads, max_len, head_dim, generator=gen).to(td)
+    sinks = torch.randn(num_q_heads, generator=gen)
+    scores = torch.randn(batch, num_kv_heads, max_len, generator=gen)
+    lengths = torch.randint(min_len, max_len + 1, (batch,), generator=gen, dtype=torch.int64).to(torch.int32)
+    return {"q": q, "k_cache": k_cache, "v_cache": v_cache, "lengths": lengths,
+            "sinks": sinks if with_sinks else None, "scores": scores}
+
+
+def make_sparse_device(batch, num_q_heads, num_kv_heads, head_dim, max_len, seed, device, min_len=1):
+    """make_sparse for caches too large to draw on the host (bf16, no sinks): q, caches
+    and scores drawn on `device` by a seeded device generator, lengths on the host."""
+    gen = torch.Generator(device=device).manual_seed(int(seed))
+    hgen = torch.Generator().manual_seed(int(seed) + 1)
+    q = _randn_device((batch, num_q_heads, head_dim), gen, device, torch.bfloat16)
+    kc = _randn_device((batch * num_kv_heads * max_len, head_dim), gen, device, torch.bfloat16)
+    vc = _randn_device((batch * num_kv_heads * max_len, head_dim), gen, device, torch.bfloat16)
+    scores = torch.randn((batch, num_kv_heads, max_len), generator=gen, device=device)
+    lengths = torch.randint(min_len, max_len + 1, (batch,), generator=hgen, dtype=torch.int64).to(torch.int32)
+    return {"q": q, "k_cache": kc.view(batch, num_kv_heads, max_len, head_dim),
+            "v_cache": vc.view(batch, num_kv_heads, max_len, head_dim), "lengths": lengths,
+            "sinks": None, "scores": scores}
+
+
+def sparse_bytes(lengths, num_q_heads, num_kv_heads, head_dim, topk, recent, elem_bytes):
+    """Sparse decode: per (sequence, KV head) the selected and recent K and V rows read
+    once, the query read and the output written, the selection (indices, counts) and
+    the LSE."""
+    keys = sum(min(topk, max(0, int(n) - recent)) + min(recent, int(n)) for n in lengths)
+    b = len(lengths)
+    return (2 * keys * num_kv_heads * head_dim * elem_bytes + 2 * b * num_q_heads * head_dim * elem_bytes
+            + b * num_kv_heads * (topk + 1) * 4 + 4 * b * num_q_heads)
+
+
+def sparse_flops(lengths, num_q_heads, head_dim, topk, recent):
+    """4 D FLOPs per (query head, key) over the selected and recent keys."""
+    keys = sum(min(topk, max(0, int(n) - recent)) + min(recent, int(n)) for n in lengths)
+    return 4 * head_dim * num_q_heads * keys
+
+
+def topk_bytes(lengths, num_kv_heads, topk, recent):
+    """Selection: every candidate score read once, indices and counts written."""
+    cand = sum(max(0, int(n) - recent) for n in lengths)
+    return 4 * num_kv_heads * cand + len(lengths) * num_kv_heads * (topk + 1) * 4
 
 
 def _randn_device(shape, gen, device, dtype, chunk_rows=1 << 18):

@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
     assert set(names) == {"swa_sink_prefill", "ga_causal_prefill", "swa_sink_decode",
                           "swa_sink_decode_fp8kv", "swa_sink_prefill_backward",
                           "swa_sink_prefill_backward_workspace", "swa_rope", "swa_sink_decode_rope",
-                          "swa_ring_append_rope", "swa_last_error", "swa_abi_version"}
+                          "swa_ring_append_rope", "swa_topk_select", "swa_sparse_decode",
+                          "swa_last_error", "swa_abi_version"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -320,3 +321,64 @@ def test_ring_append_edge_cases_validate_without_launching():
     # base 0 copies the keys unrotated, so positions may be NULL; every other pointer is still
     # required (the call fails before any launch)
     assert _append(pos=NULL, base=0.0, kc=NULL) == E_NULL and "k_cache" in _last()
+
+
+# ---------------------------------------------------------------------------
+# token-level sparse attention
+# ---------------------------------------------------------------------------
+
+def _topk(**kw):
+    a = dict(sc=FAKE, lens=FAKE, b=2, hkv=4, lmax=4096, k=1024, recent=128, idx=FAKE, cnt=FAKE)
+    a.update(kw)
+    return swa.library().swa_topk_select(a["sc"], a["lens"], a["b"], a["hkv"], a["lmax"], a["k"], a["recent"],
+                                         a["idx"], a["cnt"], NULL)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(k=-1), E_SHAPE, "k must"),
+    (dict(recent=0), E_SHAPE, "recent"),
+    (dict(lmax=0), E_SHAPE, "max_len"),
+    (dict(hkv=0), E_SHAPE, "num_kv_heads"),
+    (dict(b=-3), E_SHAPE, "batch"),
+    (dict(sc=NULL), E_NULL, "scores"),
+    (dict(idx=NULL), E_NULL, "indices"),
+    (dict(cnt=NULL), E_NULL, "counts"),
+])
+def test_topk_rejects_bad_arguments(kw, code, needle):
+    assert _topk(**kw) == code
+    assert needle in _last()
+
+
+def test_topk_empty_and_k_zero_need_no_index_array():
+    assert _topk(b=0, sc=NULL, lens=NULL, idx=NULL, cnt=NULL) == OK
+    assert _topk(k=0, idx=NULL, sc=NULL) == E_NULL  # scores are still required
+
+
+def _sparse(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, idx=FAKE, cnt=FAKE, sinks=NULL, b=2, hq=32, hkv=4, d=128,
+             lmax=4096, k=1024, recent=128, scale=0.0, dtype=1, out=FAKE, lse=NULL)
+    a.update(kw)
+    return swa.library().swa_sparse_decode(
+        a["q"], a["kc"], a["vc"], a["lens"], a["idx"], a["cnt"], a["sinks"], a["b"], a["hq"], a["hkv"], a["d"],
+        a["lmax"], a["k"], a["recent"], a["scale"], a["dtype"], a["out"], a["lse"], NULL)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(recent=0), E_SHAPE, "recent"),
+    (dict(k=8000, recent=200), E_SHAPE, "8192"),
+    (dict(k=-5), E_SHAPE, "k >= 0"),
+    (dict(lmax=0), E_SHAPE, "max_len"),
+    (dict(hq=12, hkv=8), E_SHAPE, "multiple"),
+    (dict(d=32), E_UNSUP, "head_dim"),
+    (dict(q=NULL), E_NULL, "q, k_cache"),
+    (dict(idx=NULL), E_NULL, "indices"),
+    (dict(dtype=7), E_DTYPE, "dtype"),
+])
+def test_sparse_decode_rejects_bad_arguments(kw, code, needle):
+    assert _sparse(**kw) == code
+    assert needle in _last()
+
+
+def test_sparse_decode_empty_batch_and_optional_sinks():
+    assert _sparse(b=0, q=NULL, kc=NULL, vc=NULL, lens=NULL, idx=NULL, cnt=NULL, out=NULL) == OK
+    assert _sparse(sinks=NULL, out=NULL) == E_NULL and "out" in _last()

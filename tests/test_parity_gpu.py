@@ -880,3 +880,129 @@ def test_ring_append_full_batch():
     diff = got != kc
     assert float(diff.mean()) < 1e-4
     assert np.all(np.abs(got - kc)[diff] <= 2.0 ** -7 * np.abs(kc)[diff] + 1e-30)
+
+
+# ---------------------------------------------------------------------------
+# token-level sparse attention: selection (exact) and sparse decode
+# ---------------------------------------------------------------------------
+
+def _topk_gpu(scores, lengths, k, recent):
+    idx, cnt = swa.swa_topk_select(scores.to(DEV), lengths.to(DEV), k=k, recent=recent)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), cnt.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", [(6, 3, 5000, 1024, 128, "normal"), (5, 2, 3000, 300, 7, "ties"),
+                                  (4, 4, 9000, 64, 128, "few"), (3, 2, 700, 1024, 128, "short"),
+                                  (4, 2, 2000, 0, 128, "k0"), (3, 2, 4100, 500, 16, "special")],
+                         ids=lambda c: f"B{c[0]}-kv{c[1]}-L{c[2]}-k{c[3]}-r{c[4]}-{c[5]}")
+def test_topk_select_exact(case):
+    b, hkv, lmax, k, recent, kind = case
+    _say(f"top-k selection {case}")
+    gen = torch.Generator().manual_seed(lmax + k)
+    scores = torch.randn(b, hkv, lmax, generator=gen)
+    if kind == "ties":  # a handful of distinct values: most ranks are decided by position
+        scores = torch.randint(0, 4, (b, hkv, lmax), generator=gen).float() * 0.25
+    if kind == "few":  # values equal to the threshold straddle chunk boundaries
+        scores = torch.randint(0, 40, (b, hkv, lmax), generator=gen).float()
+    if kind == "special":  # NaN ranks below every number (numpy's sort puts it last too); +-inf; -0.0
+        scores[:, :, ::7] = float("nan")
+        scores[:, :, 3::11] = float("inf")
+        scores[:, :, 5::13] = float("-inf")
+        scores[:, :, 1::17] = -0.0  # (+0.0 is not mixed in: the kernel ranks it above -0.0)
+    lengths = torch.randint(1, lmax + 1, (b,), generator=gen, dtype=torch.int64).to(torch.int32)
+    lengths[0] = lmax
+    if kind == "short":
+        lengths[1] = recent      # no candidate
+        lengths[2] = recent + 5  # fewer candidates than k
+    idx, cnt = _topk_gpu(scores, lengths, k, recent)
+    ridx, rcnt = orc.topk_select(scores, lengths.numpy(), k=k, recent=recent)
+    assert np.array_equal(cnt, rcnt)
+    assert np.array_equal(idx, ridx)
+
+
+def _sparse_gpu(x, idx, cnt, recent):
+    g = {k_: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k_, v in x.items()}
+    o, lse = swa.swa_sparse_decode(g["q"], g["k_cache"], g["v_cache"], g["lengths"],
+                                   torch.as_tensor(idx, dtype=torch.int32).to(DEV),
+                                   torch.as_tensor(cnt, dtype=torch.int32).to(DEV), g["sinks"], recent=recent)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("case", [(8, 32, 4, 128, 6000, "bf16", 1024, 128, True),
+                                  (6, 16, 2, 128, 3000, "bf16", 300, 37, False),
+                                  (5, 8, 1, 128, 900, "bf16", 1024, 128, True),
+                                  (4, 8, 2, 64, 2000, "bf16", 200, 64, True),
+                                  (3, 4, 1, 128, 1500, "f32", 256, 128, True),
+                                  (4, 32, 4, 128, 2500, "bf16", 2000, 128, False)],
+                         ids=lambda c: f"B{c[0]}-{c[1]}/{c[2]}-D{c[3]}-L{c[4]}-{c[5]}-k{c[6]}-r{c[7]}-{'sink' if c[8] else 'nosink'}")
+def test_sparse_decode_against_oracle(case):
+    b, hq, hkv, d, lmax, dt, k, recent, sink = case
+    _say(f"sparse decode {case}")
+    x = wl.make_sparse(b, hq, hkv, d, lmax, dt, seed=6100 + lmax + k, with_sinks=sink)
+    x["lengths"][0] = lmax
+    x["lengths"][1] = min(lmax, recent // 2 + 1)  # shorter than the recent window
+    idx, cnt = _topk_gpu(x["scores"], x["lengths"], k, recent)
+    ridx, rcnt = orc.topk_select(x["scores"], x["lengths"].numpy(), k=k, recent=recent)
+    assert np.array_equal(idx, ridx) and np.array_equal(cnt, rcnt)
+    o, lse = _sparse_gpu(x, idx, cnt, recent)
+    o_ref, l_ref = orc.sparse_decode(x["q"], x["k_cache"], x["v_cache"], x["lengths"].numpy(), ridx, rcnt,
+                                     x["sinks"], recent=recent)
+    assert_close(x["q"].dtype, o, o_ref, lse, l_ref, f"sparse {case}")
+
+
+def test_sparse_decode_limits_match_dense_kernels():
+    """k = 0 with the 128-token recent window is the newest row of swa_sink_prefill with
+    window 128; a selection of every older token is the newest row of full causal
+    attention (swa_sink_prefill with the window at the sequence length)."""
+    _say("sparse decode limits vs the library's own dense prefill")
+    b, hq, hkv, d, lmax = 4, 32, 4, 128, 1000
+    x = wl.make_sparse(b, hq, hkv, d, lmax, "bf16", seed=6200, min_len=300)
+    for k, window_of in ((0, lambda n: 128), (1024, lambda n: n)):
+        idx, cnt = _topk_gpu(x["scores"], x["lengths"], k, 128)
+        o, lse = _sparse_gpu(x, idx, cnt, 128)
+        for bb in range(b):
+            n = int(x["lengths"][bb])
+            qs = torch.zeros(n, hq, d, dtype=torch.bfloat16)
+            qs[n - 1] = x["q"][bb]
+            ks = x["k_cache"][bb, :, :n].transpose(0, 1).contiguous()
+            vs = x["v_cache"][bb, :, :n].transpose(0, 1).contiguous()
+            od, ld = swa.swa_sink_prefill(qs.to(DEV), ks.to(DEV), vs.to(DEV), x["sinks"].to(DEV),
+                                          torch.tensor([0, n], dtype=torch.int32, device=DEV), n,
+                                          window=window_of(n))
+            torch.cuda.synchronize()
+            err = (o[bb].float() - od[n - 1].float()).abs().max().item()
+            lerr = (lse[bb] - ld[n - 1]).abs().max().item()
+            assert err <= 2e-2 and lerr <= 1e-3, (k, bb, err, lerr)
+
+
+def test_sparse_full_size_workload():
+    """The benchmarked workload (64 sequences of 16K-32K tokens, [64, 4, 32768, 128]
+    caches drawn on the GPU): every selection index exactly, every output row against the
+    oracle on the rows it gathers."""
+    w = wl.WORKLOADS["sparse_b64"]
+    k, recent = w.extra["topk"], w.extra["recent"]
+    _say("sparse_b64 full size: top-k exact, all 64 x 32 output rows")
+    x = wl.make_sparse_device(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.seq_len, w.seed, DEV,
+                              min_len=w.extra["min_len"])
+    idx, cnt = swa.swa_topk_select(x["scores"], x["lengths"].to(DEV), k=k, recent=recent)
+    o, lse = swa.swa_sparse_decode(x["q"], x["k_cache"], x["v_cache"], x["lengths"].to(DEV), idx, cnt, None,
+                                   recent=recent)
+    torch.cuda.synchronize()
+    ridx, rcnt = orc.topk_select(x["scores"].cpu(), x["lengths"].numpy(), k=k, recent=recent)
+    assert np.array_equal(idx.cpu().numpy(), ridx) and np.array_equal(cnt.cpu().numpy(), rcnt)
+    # the oracle on each sequence's gathered rows (selected + recent), read back from the GPU
+    hkv, d = w.num_kv_heads, w.head_dim
+    o_ref = np.zeros((w.batch, w.num_q_heads, d))
+    l_ref = np.zeros((w.batch, w.num_q_heads))
+    for bb in range(w.batch):
+        n = int(x["lengths"][bb])
+        keys = [np.concatenate([ridx[bb, g, :rcnt[bb, g]], np.arange(n - recent, n)]) for g in range(hkv)]
+        m = len(keys[0])
+        kg = torch.stack([x["k_cache"][bb, g, torch.as_tensor(keys[g], device=DEV)] for g in range(hkv)])
+        vg = torch.stack([x["v_cache"][bb, g, torch.as_tensor(keys[g], device=DEV)] for g in range(hkv)])
+        ob, lb = orc.sparse_decode(x["q"][bb:bb + 1].cpu(), kg[None].cpu(), vg[None].cpu(), [m],
+                                   np.full((1, hkv, 1), -1), np.zeros((1, hkv)), None, recent=m)
+        o_ref[bb], l_ref[bb] = ob[0], lb[0]
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, "sparse_b64")
