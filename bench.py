@@ -201,6 +201,78 @@ def _rope_inputs(dev):
     return {"q": x["q"], "positions": torch.arange(32768, dtype=torch.int32, device=dev)}
 
 
+def _sparse_inputs(dev):
+    """The sparse_b64 workload drawn on the GPU (64 sequences, [64, 4, 32768, 128] caches)
+    with its selection, indices and counts allocated."""
+    import torch
+
+    from sliding_window_attention_amd import workloads as wl
+
+    w = wl.WORKLOADS["sparse_b64"]
+    x = wl.make_sparse_device(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.seq_len, w.seed, dev,
+                              min_len=w.extra["min_len"])
+    x["lengths_host"] = x["lengths"]
+    x["lengths"] = x["lengths"].to(dev)
+    x["indices"] = torch.empty((w.batch, w.num_kv_heads, w.extra["topk"]), dtype=torch.int32, device=dev)
+    x["counts"] = torch.empty((w.batch, w.num_kv_heads), dtype=torch.int32, device=dev)
+    x["out"] = torch.empty_like(x["q"])
+    x["lse"] = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
+    return x
+
+
+def _topk_fn():
+    """Timed call of swa_topk_select on the sparse workload's scores."""
+    import ctypes
+
+    import torch
+
+    import sliding_window_attention_amd as swa
+
+    lib = swa.library()
+
+    def fn(x):
+        b, hkv, lmax = x["scores"].shape
+        rc = lib.swa_topk_select(x["scores"].data_ptr(), x["lengths"].data_ptr(), b, hkv, lmax,
+                                 x["indices"].shape[2], swa.SPARSE_RECENT, x["indices"].data_ptr(),
+                                 x["counts"].data_ptr(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(lib.swa_last_error().decode())
+    return fn
+
+
+def _sparse_fn():
+    """Timed call of swa_sparse_decode on the sparse workload (selection already made)."""
+    import ctypes
+
+    import torch
+
+    import sliding_window_attention_amd as swa
+
+    lib = swa.library()
+
+    def fn(x):
+        b, hq, d = x["q"].shape
+        hkv, lmax = x["k_cache"].shape[1], x["k_cache"].shape[2]
+        rc = lib.swa_sparse_decode(x["q"].data_ptr(), x["k_cache"].data_ptr(), x["v_cache"].data_ptr(),
+                                   x["lengths"].data_ptr(), x["indices"].data_ptr(), x["counts"].data_ptr(),
+                                   None, b, hq, hkv, d, lmax, x["indices"].shape[2], swa.SPARSE_RECENT, 0.0, 1,
+                                   x["out"].data_ptr(), x["lse"].data_ptr(),
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(lib.swa_last_error().decode())
+    return fn
+
+
+def _sparse_work(x):
+    from sliding_window_attention_amd import workloads as wl
+
+    w = wl.WORKLOADS["sparse_b64"]
+    lens = x["lengths_host"].tolist()
+    return (wl.topk_bytes(lens, w.num_kv_heads, w.extra["topk"], w.extra["recent"]),
+            wl.sparse_bytes(lens, w.num_q_heads, w.num_kv_heads, w.head_dim, w.extra["topk"], w.extra["recent"], 2),
+            wl.sparse_flops(lens, w.num_q_heads, w.head_dim, w.extra["topk"], w.extra["recent"]))
+
+
 def _append_inputs(dev):
     """Ring append after an MTP verify of the T = 4 decode workload: seeded accept counts
     ~ U{0..4} per sequence (keys rotated at base 10,000)."""
@@ -417,6 +489,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", choices=["prefill", "decode", "decode1", "decode_fp8", "decode_fp8_1",
                                        "decode_rope", "decode_rope_1", "append", "mtp_step", "rope",
+                                       "topk", "sparse",
                                        "ga", "varlen", "backward", "copy"],
                     default=None,
                     help="time a single workload (for profiling runs); prints no JSON line")
@@ -472,6 +545,16 @@ def main(argv=None):
         st = _stats(per)
         by = wl.append_bytes(256, int(x["n_accept"].sum()), 4, 128, 2)
         _log(f"{args.only} B=256 T=4: {st}  (append bytes {by})")
+        return 0
+    if args.only in ("topk", "sparse"):
+        x = _sparse_inputs(dev)
+        _topk_fn()(x)
+        fn = _topk_fn() if args.only == "topk" else _sparse_fn()
+        per, _ = _time_calls(fn, [x], max(steps, 100), warmup, per_call=False)
+        st = _stats(per)
+        tb, sb, sfl = _sparse_work(x)
+        by = tb if args.only == "topk" else sb
+        _log(f"{args.only} sparse_b64: {st}  {by / (st['mean_ms'] * 1e-3) / 1e9:.0f} GB/s ({by} bytes)")
         return 0
     if args.only == "rope":
         x = _rope_inputs(dev)
@@ -606,6 +689,20 @@ def run_extra(dev, steps, warmup):
                                  "accepted_tokens": int(x["n_accept"].sum()),
                                  "what": "swa_sink_decode_rope (T=4) + swa_ring_append_rope per step"}
     del x
+    _log("sparse attention: top-k selection and sparse decode, 64 sequences of 16K-32K tokens")
+    x = _sparse_inputs(dev)
+    tb, sb, sfl = _sparse_work(x)
+    per, _ = _time_calls(_topk_fn(), [x], max(100, steps), warmup, per_call=False)
+    st = _stats(per)
+    extra["topk_select_b64"] = {**st, "gbps": tb / (st["mean_ms"] * 1e-3) / 1e9, "bytes": tb}
+    per, _ = _time_calls(_sparse_fn(), [x], max(100, steps), warmup, per_call=False)
+    st = _stats(per)
+    extra["sparse_decode_b64"] = {**st, "gbps": sb / (st["mean_ms"] * 1e-3) / 1e9,
+                                  "hbm_frac": sb / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": sb,
+                                  "tflops": sfl / (st["mean_ms"] * 1e-3) / 1e12}
+    del x
+    torch.cuda.empty_cache()
+
     _log("rope in place, Q of the 32K layer")
     x = _rope_inputs(dev)
     per, _ = _time_calls(_rope_fn(), [x], steps, warmup, per_call=False)

@@ -5,8 +5,12 @@
 //
 //  * topk_select_kernel: one workgroup per (sequence, KV head) row of scores.  The
 //    candidates are the positions older than the recent window.  A radix select over
-//    an order-preserving 32-bit key finds the k-th largest score (four 8-bit histogram
-//    passes); one ordered pass then writes the chosen positions in increasing order:
+//    an order-preserving 32-bit key finds the k-th largest score (histogram passes over
+//    digits of 12, 10 and 10 bits -- the first digit takes mantissa bits too, so scores
+//    of one binade do not pile onto a few bins; the first pass reads the row with
+//    16-byte loads and keeps the keys in LDS for the others when the row has at most
+//    32768 candidates); one ordered pass then
+//    writes the chosen positions in increasing order:
 //    every score above the threshold, and the lowest positions among those equal to
 //    it, so the result is exact and deterministic (no floating point decides a rank).
 //  * sparse_decode_kernel: one workgroup per (sequence, head octet); the key list
@@ -28,7 +32,7 @@ using namespace tile;
 // top-k selection
 // ---------------------------------------------------------------------------
 
-constexpr int kSelThreads = 512;  // 8 wavefronts
+constexpr int kSelThreads = 1024;  // 16 wavefronts
 constexpr int kSelPer = 8;        // consecutive candidates per thread in the ordered pass
 
 // Larger float -> larger key; NaN below every number.  The scores are read as their
@@ -62,8 +66,13 @@ __device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t x, uint32_t* t
   return x + before;
 }
 
+constexpr int kKeyCache = 32768;  // candidates whose keys are kept in LDS (128 KB)
+constexpr int kBins0 = 4096;       // first digit: bits 31..20 (sign, exponent, 3 mantissa bits)
+constexpr int kBins = 1024;        // next digits: bits 19..10 and 9..0
+
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t cache[kKeyCache];  // the row's keys when it fits, else unused
+  __shared__ uint32_t hist[kBins0];
   __shared__ uint32_t tmp[kSelThreads / 64];
   __shared__ uint32_t pick[2];
   const int row = blockIdx.x;  // sequence * Hkv + KV head
@@ -80,36 +89,89 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
     if (tid == 0) a.counts[row] = ncand < K ? ncand : K;
     return;
   }
+  const bool cached = ncand <= kKeyCache;
+  // key of candidate j: from the LDS cache (filled during the first pass) or from memory
+  auto key_at = [&](int j) -> uint32_t { return cached ? cache[j] : order_key(sc[j]); };
 
-  // ---- radix select of the K-th largest key, 8 bits per pass from the top ----
+  // ---- radix select of the K-th largest key: digits of 12, 10 and 10 bits ----
   uint32_t prefix = 0, mask = 0;
   int rem = K;  // how many of the keys matching `prefix` are still to be chosen
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int x = tid; x < 256; x += kSelThreads) hist[x] = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 0 ? kBins0 : kBins;
+    const uint32_t dmask = (uint32_t)nb - 1u;
+    for (int x = tid; x < nb; x += kSelThreads) hist[x] = 0;
     __syncthreads();
-    for (int j = tid; j < ncand; j += kSelThreads) {
-      const uint32_t u = order_key(sc[j]);
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    if (pass == 0) {
+      // 4 candidates per 16-byte load, 4 loads in flight per thread; scalar head/tail
+      // where the row is not 16-byte aligned
+      const int head = (int)((4 - (((uintptr_t)sc >> 2) & 3)) & 3);
+      const int h = head < ncand ? head : ncand;
+      for (int j = tid; j < h; j += kSelThreads) {
+        const uint32_t u = order_key(sc[j]);
+        if (cached) cache[j] = u;
+        atomicAdd(&hist[u >> 20], 1u);
+      }
+      const int nvec = (ncand - h) >> 2;
+      const u32x4* v4 = reinterpret_cast<const u32x4*>(sc + h);
+      for (int x0 = 0; x0 < nvec; x0 += 4 * kSelThreads) {
+        u32x4 ld[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int x = x0 + e * kSelThreads + tid;
+          ld[e] = x < nvec ? v4[x] : (u32x4){0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int x = x0 + e * kSelThreads + tid;
+          if (x < nvec) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const uint32_t u = order_key(ld[e][c]);
+              if (cached) cache[h + 4 * x + c] = u;
+              atomicAdd(&hist[u >> 20], 1u);
+            }
+          }
+        }
+      }
+      for (int j = h + 4 * nvec + tid; j < ncand; j += kSelThreads) {
+        const uint32_t u = order_key(sc[j]);
+        if (cached) cache[j] = u;
+        atomicAdd(&hist[u >> 20], 1u);
+      }
+    } else {
+      for (int j0 = 0; j0 < ncand; j0 += 4 * kSelThreads) {
+        uint32_t u[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = j0 + e * kSelThreads + tid;
+          u[e] = j < ncand ? key_at(j) : 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = j0 + e * kSelThreads + tid;
+          if (j < ncand && (u[e] & mask) == prefix) atomicAdd(&hist[(u[e] >> shift) & dmask], 1u);
+        }
+      }
     }
     __syncthreads();
-    if (tid < 64) {  // one wavefront: lane l owns bins 4l .. 4l+3; suffix sums from the top bin
-      uint32_t h[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) h[e] = hist[4 * tid + e];
-      const uint32_t mine = h[0] + h[1] + h[2] + h[3];
-      uint32_t suf = mine;  // inclusive suffix over lanes >= tid
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_down(suf, o);
-        if (tid + o < 64) suf += y;
-      }
-      uint32_t acc = suf - mine;  // keys in bins above this lane's
-      if (acc < (uint32_t)rem && (uint32_t)rem <= suf) {
-        int d = 4 * tid + 3;
-        for (int e = 3; e >= 0; --e, --d) {
-          if (acc + h[e] >= (uint32_t)rem) break;
-          acc += h[e];
+    // the digit holding the rem-th largest matching key: thread t owns the `per` bins
+    // just below the top t * per (descending), an inclusive scan over threads counts
+    // the keys at or above each thread's lowest bin
+    {
+      const int per = nb / kSelThreads;  // 8 or 2
+      const int top = nb - 1 - tid * per;
+      uint32_t mine = 0;
+      for (int e = 0; e < per; ++e) mine += hist[top - e];
+      uint32_t tot;
+      const uint32_t incl = block_inclusive_scan(mine, tmp, &tot);
+      uint32_t acc = incl - mine;  // keys in bins above this thread's
+      if (acc < (uint32_t)rem && (uint32_t)rem <= incl) {
+        int d = top;
+        for (int e = 0; e < per; ++e, --d) {
+          const uint32_t hv = hist[d];
+          if (acc + hv >= (uint32_t)rem) break;
+          acc += hv;
         }
         pick[0] = (uint32_t)d;
         pick[1] = (uint32_t)rem - acc;
@@ -117,7 +179,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
     }
     __syncthreads();
     prefix |= pick[0] << shift;
-    mask |= 255u << shift;
+    mask |= dmask << shift;
     rem = (int)pick[1];
     __syncthreads();  // pick and hist are rewritten by the next pass
   }
@@ -133,7 +195,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
 #pragma unroll
     for (int e = 0; e < kSelPer; ++e) {
       const int j = j0 + e;
-      key[e] = j < ncand ? order_key(sc[j]) : 0u;
+      key[e] = j < ncand ? key_at(j) : 0u;
       ngt += (j < ncand && key[e] > T) ? 1u : 0u;
       neq += (j < ncand && key[e] == T) ? 1u : 0u;
     }
