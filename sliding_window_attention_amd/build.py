@@ -30,8 +30,10 @@ HIPCC_FLAGS = [
     # packed fp32 arithmetic is kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # device code never relies on NaN semantics (masking uses -inf, which stays
-    # honoured); without NaN handling, max/min need no canonicalising moves
-    "-Xarch_device", "-fno-honor-nans", "-Xarch_device", "-mno-amdgpu-ieee",
+    # honoured); without NaN handling, max/min need no canonicalising moves.  The
+    # IEEE mode stays at its default: a kernel compiled with another mode than the
+    # device library cannot inline the library's work-item and math functions.
+    "-Xarch_device", "-fno-honor-nans",
     "-I", os.path.join(HERE, "..", "include"),
 ]
 

@@ -41,11 +41,11 @@ struct DecodeSmem {
     char o[2][NT * 16][kColBytes];  // two partial-output slots for the pairwise merge
     struct {
       char q[NT * 16][kRowPitch];  // query columns (dead once the scores are formed)
-      char kn[16][kRowPitch];      // new-token K rows, zero past T
+      char kn[16][kRowPitch];      // new-token K rows (rows past T repeat row T-1)
       float cs[4 * 64][2];         // rotary cos / sin per (new token, pair), when rotating
     } in;
   } u;
-  char vn[16][kRowPitch];  // new-token V rows, zero past T
+  char vn[16][kRowPitch];  // new-token V rows (rows past T repeat row T-1)
 };
 
 // Partial O^T of lane (i, g), column tt*16 + i, head-dim 32g + 8r + b, to/from LDS.
@@ -118,44 +118,44 @@ void decode_kernel(DecodeArgs a) {
   const bf16* kn = static_cast<const bf16*>(a.k_new) + ((size_t)b * T * hkv + kvh) * D;
   const bf16* vn = static_cast<const bf16*>(a.v_new) + ((size_t)b * T * hkv + kvh) * D;
 
-  // ---- loads: ring K (A operand) and ring V rows into registers; Q columns and
-  // the new tokens' K/V staged once in LDS for the four wavefronts ----
+  // ---- loads, issued in the order their data is needed: the query columns and the
+  // new tokens' K/V (staged once in LDS for the four wavefronts), then ring K (A
+  // operands), then ring V rows, which arrive while the scores are formed.  Every load
+  // is unconditional and reads a valid row, so no wait is tied to a lane condition:
+  // query columns past the T tokens repeat token T-1 (their results are never stored),
+  // new-token rows past T repeat row T-1 (weight 0), and the oldest ring slot, which no
+  // query sees, is replaced by logical slot 1 (weight 0 as well) and is never read. ----
+  const int tid = threadIdx.x;
+  // sink of this lane's head (query column i: head i & 7), loaded ahead of the bulk
+  const float sink2 = a.sinks[h_base + (i & 7)] * kLog2e;
+  const int nrow = min(tid >> 4, T - 1), nuu = tid & 15;  // new token of this thread
+  u32x4 st[NT + 2];
+#pragma unroll
+  for (int k = 0; k < NT; ++k) {  // Q column col = x >> 4: token col >> 3, head col & 7
+    const int x = k * kThreads + tid;
+    const int col = x >> 4, uu = x & 15, t = min(col >> 3, T - 1);
+    st[k] = *reinterpret_cast<const u32x4*>(qp + (((size_t)b * T + t) * Hq + h_base + (col & 7)) * D + 8 * uu);
+  }
+  st[NT] = *reinterpret_cast<const u32x4*>(kn + (size_t)nrow * hkv * D + 8 * nuu);
+  st[NT + 1] = *reinterpret_cast<const u32x4*>(vn + (size_t)nrow * hkv * D + 8 * nuu);
   bf16x8 kf[2][4];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int kr = 32 * w + pair_row(i, s);
-    const int phys = (head + kr) & (kW - 1);
+    const int phys = (head + (kr != 0 ? kr : 1)) & (kW - 1);
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-      kf[s][cc] = kr != 0 ? ring8(kc, phys, 32 * cc + 8 * g) : zero8();
+    for (int cc = 0; cc < 4; ++cc) kf[s][cc] = ring8(kc, phys, 32 * cc + 8 * g);
   }
   bf16x8 vr[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int kr = 32 * w + 8 * g + e;
-    const int phys = (head + kr) & (kW - 1);
-    vr[e] = kr != 0 ? ring8(vc, phys, 8 * i) : zero8();
+    const int phys = (head + (kr != 0 ? kr : 1)) & (kW - 1);
+    vr[e] = ring8(vc, phys, 8 * i);
   }
   {
-    const int tid = threadIdx.x;
-    u32x4 st[NT + 2];
-#pragma unroll
-    for (int k = 0; k < NT; ++k) {  // Q column col = x >> 4: token col >> 3, head col & 7
-      const int x = k * kThreads + tid;
-      const int col = x >> 4, uu = x & 15, t = col >> 3;
-      st[k] = (u32x4){0, 0, 0, 0};
-      if (t < T)
-        st[k] = *reinterpret_cast<const u32x4*>(qp + (((size_t)b * T + t) * Hq + h_base + (col & 7)) * D + 8 * uu);
-    }
-    const int row = tid >> 4, uu = tid & 15;  // new token `row`
-    st[NT] = (u32x4){0, 0, 0, 0};
-    st[NT + 1] = (u32x4){0, 0, 0, 0};
-    if (row < T) {
-      st[NT] = *reinterpret_cast<const u32x4*>(kn + (size_t)row * hkv * D + 8 * uu);
-      st[NT + 1] = *reinterpret_cast<const u32x4*>(vn + (size_t)row * hkv * D + 8 * uu);
-    }
     if constexpr (ROPE) {
-      // the rotary cos/sin table (token, pair) is formed while the staging loads are in
+      // the rotary cos/sin table (token, pair) is formed while the loads are in
       // flight (it depends on the position only)
       const int pos0 = as_const(a.rope_pos)[b];
       for (int x = tid; x < T * 64; x += kThreads)
@@ -166,8 +166,8 @@ void decode_kernel(DecodeArgs a) {
       const int x = k * kThreads + tid;
       *reinterpret_cast<u32x4*>(&sm.u.in.q[x >> 4][16 * (x & 15)]) = st[k];
     }
-    *reinterpret_cast<u32x4*>(&sm.u.in.kn[row][16 * uu]) = st[NT];
-    *reinterpret_cast<u32x4*>(&sm.vn[row][16 * uu]) = st[NT + 1];
+    *reinterpret_cast<u32x4*>(&sm.u.in.kn[tid >> 4][16 * nuu]) = st[NT];
+    *reinterpret_cast<u32x4*>(&sm.vn[tid >> 4][16 * nuu]) = st[NT + 1];
   }
   int tcol[NT];
 #pragma unroll
@@ -178,7 +178,6 @@ void decode_kernel(DecodeArgs a) {
     // unrotated; the ring's keys were rotated when they were appended): one pass over
     // (row, group of 8 pairs) with the cos/sin table formed during staging, rounding
     // back to bf16 in place.
-    const int tid = threadIdx.x;
     const int nq = T * kHG;  // query columns col = token * 8 + head
     for (int x = tid; x < (nq + T) * 8; x += kThreads) {
       const int r = x >> 3, gi = x & 7;
@@ -259,7 +258,6 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
     const int col = tt * 16 + i;
-    const float sink2 = a.sinks[h_base + (i & 7)] * kLog2e;
     mcol[tt] = fmaxf(fmaxf(fmaxf(sm.m[0][col], sm.m[1][col]), fmaxf(sm.m[2][col], sm.m[3][col])), sink2);
     float ps = 0.f;
 #pragma unroll
@@ -328,7 +326,7 @@ void decode_kernel(DecodeArgs a) {
     if (t >= T) continue;
     const int h = h_base + (i & 7);
     const float z = sm.l[0][col] + sm.l[1][col] + sm.l[2][col] + sm.l[3][col] +
-                    fast_exp2(a.sinks[h] * kLog2e - mcol[tt]);
+                    fast_exp2(sink2 - mcol[tt]);
     const float inv = __builtin_amdgcn_rcpf(z);
     const size_t row_idx = ((size_t)b * T + t) * Hq + h;
 #pragma unroll
