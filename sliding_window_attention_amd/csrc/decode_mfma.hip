@@ -33,12 +33,20 @@ constexpr int kColBytes = 528;  // fp32 partial row (512 B) padded against bank 
 
 constexpr int kRowPitch = 272;  // staged bf16 row (256 B) padded: 16 rows hit 16 bank quads
 
+// Partial-output slots of the merge: one per wavefront for a single query tile (one
+// barrier), two for two tiles (a pairwise step first), which keeps the workgroup
+// within a quarter of the LDS either way.
+template <int NT>
+constexpr int kMergeSlots = NT == 1 ? 4 : 2;
+
 template <int NT>
 struct DecodeSmem {
   float m[4][NT * 16];
   float l[4][NT * 16];
+  float mc[NT * 16];  // column maximum (sink included), log2 units
+  float zs[NT * 16];  // the sink's term of the column's denominator
   union {
-    char o[2][NT * 16][kColBytes];  // two partial-output slots for the pairwise merge
+    char o[kMergeSlots<NT>][NT * 16][kColBytes];  // partial outputs, fp32
     struct {
       char q[NT * 16][kRowPitch];  // query columns (dead once the scores are formed)
       char kn[16][kRowPitch];      // new-token K rows (rows past T repeat row T-1)
@@ -276,6 +284,10 @@ void decode_kernel(DecodeArgs a) {
     }
     ps = quad_sum(ps);
     if (g == 0) sm.l[w][col] = ps;
+    if (w == 0 && g == 0) {
+      sm.mc[col] = mcol[tt];
+      sm.zs[col] = fast_exp2(sink2 - mcol[tt]);
+    }
   }
 
   // ---- partial O^T = V^T P^T ----
@@ -306,42 +318,52 @@ void decode_kernel(DecodeArgs a) {
       for (int tt = 0; tt < NT; ++tt) o[tt][bb] = mfma32_k16(av, pack_quad(sn[tt]), o[tt][bb]);
     }
   }
-  // ---- merge the four partials (they share the column maxima, so they add):
-  // wavefronts 2, 3 hand theirs to 0, 1; then 1 hands its sum to 0 ----
-  if (w >= 2) put_partial<NT>(sm.u.o[w - 2], i, g, o);
-  __syncthreads();
-  if (w < 2) add_partial<NT>(sm.u.o[w], i, g, o);
-  __syncthreads();
-  if (w == 1) put_partial<NT>(sm.u.o[0], i, g, o);
-  __syncthreads();
-  if (w != 0) return;
-  add_partial<NT>(sm.u.o[0], i, g, o);
-
-  // ---- normalise and store: lane (i, g) owns head-dim 32g .. 32g+31 of column tt*16 + i ----
-  bf16* out = static_cast<bf16*>(a.out);
-#pragma unroll
-  for (int tt = 0; tt < NT; ++tt) {
-    const int col = tt * 16 + i;
-    const int t = tcol[tt];
-    if (t >= T) continue;
-    const int h = h_base + (i & 7);
-    const float z = sm.l[0][col] + sm.l[1][col] + sm.l[2][col] + sm.l[3][col] +
-                    fast_exp2(sink2 - mcol[tt]);
-    const float inv = __builtin_amdgcn_rcpf(z);
-    const size_t row_idx = ((size_t)b * T + t) * Hq + h;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      bf16x8 v8;
-#pragma unroll
-      for (int bb = 0; bb < 8; bb += 2) {
-        const bf16x2 x = __builtin_convertvector((f32x2){o[tt][bb][r] * inv, o[tt][bb + 1][r] * inv}, bf16x2);
-        v8[bb] = x[0];
-        v8[bb + 1] = x[1];
-      }
-      *reinterpret_cast<bf16x8*>(out + row_idx * D + 32 * g + 8 * r) = v8;
+  // ---- merge the four partials (they share the column maxima, so they add) ----
+  if constexpr (kMergeSlots<NT> == 4) {
+    put_partial<NT>(sm.u.o[w], i, g, o);
+  } else {  // wavefronts 2, 3 hand theirs to 0, 1, which write back the pair sums
+    if (w >= 2) put_partial<NT>(sm.u.o[w - 2], i, g, o);
+    __syncthreads();
+    if (w < 2) {
+      add_partial<NT>(sm.u.o[w], i, g, o);
+      put_partial<NT>(sm.u.o[w], i, g, o);
     }
-    if (a.lse != nullptr && g == 0) a.lse[row_idx] = (mcol[tt] + fast_log2(z)) * kLn2;
   }
+  __syncthreads();
+
+  // ---- normalise and store, all threads: thread tid owns kPer consecutive head-dim
+  // elements of one query column (qc = token * 8 + head), a 16- or 32-byte
+  // piece of its output row; the 16 or 8 threads of a column cover the row ----
+  constexpr int kPer = NT * 16 * D / kThreads;  // 8 or 16
+  const int qc = tid / (D / kPer);
+  const int d0 = (tid % (D / kPer)) * kPer;
+  const int t = qc >> 3;
+  if (t >= T) return;
+  float acc[kPer];
+#pragma unroll
+  for (int q4 = 0; q4 < kPer / 4; ++q4) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(&sm.u.o[0][qc][4 * (d0 + 4 * q4)]);
+#pragma unroll
+    for (int sl = 1; sl < kMergeSlots<NT>; ++sl) v += *reinterpret_cast<const f32x4*>(&sm.u.o[sl][qc][4 * (d0 + 4 * q4)]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[4 * q4 + e] = v[e];
+  }
+  const float z = sm.l[0][qc] + sm.l[1][qc] + sm.l[2][qc] + sm.l[3][qc] + sm.zs[qc];
+  const float inv = __builtin_amdgcn_rcpf(z);
+  const size_t row_idx = ((size_t)b * T + t) * Hq + h_base + (qc & 7);
+  bf16* out = static_cast<bf16*>(a.out) + row_idx * D + d0;
+#pragma unroll
+  for (int q8 = 0; q8 < kPer / 8; ++q8) {
+    bf16x8 v8;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 x = __builtin_convertvector((f32x2){acc[8 * q8 + e] * inv, acc[8 * q8 + e + 1] * inv}, bf16x2);
+      v8[e] = x[0];
+      v8[e + 1] = x[1];
+    }
+    *reinterpret_cast<bf16x8*>(out + 8 * q8) = v8;
+  }
+  if (a.lse != nullptr && d0 == 0) a.lse[row_idx] = (sm.mc[qc] + fast_log2(z)) * kLn2;
 }
 
 }  // namespace
