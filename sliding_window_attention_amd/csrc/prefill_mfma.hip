@@ -12,7 +12,9 @@
 // blocks of 16 keys) is scored in registers and the softmax is exact in one pass
 // (no online rescaling), the sink entering as the initial maximum candidate and
 // as exp(sink - m) in the denominator.  Workgroups are persistent and keep the
-// band in an LDS ring across consecutive tiles.
+// band in an LDS ring across consecutive tiles, walking their run of tiles upwards
+// or (odd runs) downwards, so that neighbouring runs read the rows they share at the
+// same time on the same XCD.
 #include "common.h"
 #include "kernels.h"
 #include "mfma_tile.h"
@@ -84,9 +86,19 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
   const int N = a.total_tokens, Hq = a.num_q_heads, hkv = a.num_kv_heads;
   const int ntiles = (N + kQT - 1) / kQT;
   const int total = ntiles * (Hq / kHG);
-  int item = blockIdx.x * items_per_wg;
-  const int item_end = min(item + items_per_wg, total);
-  if (item >= item_end) return;
+  // Runs of neighbouring workgroups share the K/V rows of the window that straddles
+  // their boundary.  Workgroups are dealt to the 8 XCDs round-robin; the logical run
+  // index gives each XCD a contiguous range of runs, and odd runs walk their tiles
+  // downwards, so that the two runs of every boundary read its shared rows at the same
+  // time (both at their start, or both at their end) through one L2.
+  const int nwg = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, perx = nwg >> 3, remx = nwg & 7;
+  const int run = xcd * perx + min(xcd, remx) + (bid >> 3);
+  const bool down = run & 1;
+  const int item_lo = run * items_per_wg;
+  const int item_hi = min(item_lo + items_per_wg, total);
+  if (item_lo >= item_hi) return;
+  int item = down ? item_hi - 1 : item_lo;  // next unprocessed item
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 15, g = lane >> 4;
@@ -123,29 +135,29 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
   // Outer loop: runs of consecutive tiles of one head octet (the ring is filled
   // once per run).  Inner loop: one tile per iteration, the ring advancing by
   // one 16-key block.
-  while (item < item_end) {
+  while (down ? item >= item_lo : item < item_hi) {
     item = __builtin_amdgcn_readfirstlane(item);
     const int oct = item / ntiles;
-    int tile = item - oct * ntiles;
-    const int run_end = min(item_end, (oct + 1) * ntiles);
-    int seq = find_seq(cu, S, tile * kQT);  // sequence of the tile's first query
+    const int tile0 = item - oct * ntiles;  // first tile of this run
+    const int run_len = __builtin_amdgcn_readfirstlane(
+        down ? item - max(item_lo, oct * ntiles) + 1 : min(item_hi, (oct + 1) * ntiles) - item);
+    const int dir = down ? -1 : 1;
+    int seq = find_seq(cu, S, tile0 * kQT);  // sequence of the tile's first query
     const int kvh = (oct * kHG) / G;
     __syncthreads();  // the previous run is done with the ring
-    fill(ks, vs, kp, vp, tile * kQT - 128, N, hkv, kvh);
-    load_q_tile(tile * kQT, oct);
+    fill(ks, vs, kp, vp, tile0 * kQT - 128, N, hkv, kvh);
+    load_q_tile(tile0 * kQT, oct);
     // Drain the run prologue's loads so that, at the loop head, no vector load
     // is outstanding on any path: each iteration waits for its prefetches
     // before it issues its stores.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    const int run_len = __builtin_amdgcn_readfirstlane(run_end - item);
-    const int tile0 = tile;
     // ring slot of the tile's oldest block: (kbase / 16) mod 9 with kbase = 16 tile
-    // - 128, i.e. (tile + 1) mod 9; it advances by one slot per tile
+    // - 128, i.e. (tile + 1) mod 9; it moves by one slot per tile, with the walk
     int kblock0 = __builtin_amdgcn_readfirstlane((tile0 + 1) % kSlots);
     for (int k = 0; k < run_len; ++k) {
-      tile = tile0 + k;
+      const int tile = tile0 + dir * k;
       const int q0 = tile * kQT;
       const int kbase = q0 - 128;  // ring block j holds keys kbase + 16j ..
       const int par = tile & 1;    // (kbase / 16) & 1
@@ -157,7 +169,11 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
       const int h0 = oct * kHG + 2 * w;
 
       // ---- first visible key of each row: window and own-sequence start ----
-      while (seq + 1 < S && cu[seq + 1] <= q0) ++seq;
+      if (down) {
+        while (seq > 0 && cu[seq] > q0) --seq;
+      } else {
+        while (seq + 1 < S && cu[seq + 1] <= q0) ++seq;
+      }
       const int qi = q0 + i;
       int start = cu[seq];
       for (int s2 = seq + 1; s2 < S && cu[s2] < q0 + kQT; ++s2)  // boundaries inside the tile
@@ -202,16 +218,17 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
         }
       }
 
-      // ---- prefetch for the next tile: its 16 newest K/V rows and its Q ----
+      // ---- prefetch for the next tile: the 16 K/V rows it adds to the ring (its newest
+      // block walking up, its oldest walking down) and its Q ----
       const bool has_next = k + 1 < run_len;
       u32x4 pk = {0, 0, 0, 0}, pv = {0, 0, 0, 0};
-      const int nkey = q0 + 16 + (t >> 4);
-      if (has_next && nkey < N) {
+      const int nkey = (down ? q0 - 144 : q0 + 16) + (t >> 4);
+      if (has_next && nkey >= 0 && nkey < N) {
         const size_t off = ((size_t)nkey * hkv + kvh) * D + (t & 15) * 8;
         pk = *reinterpret_cast<const u32x4*>(kp + off);
         pv = *reinterpret_cast<const u32x4*>(vp + off);
       }
-      if (has_next) load_q_tile(q0 + kQT, oct);
+      if (has_next) load_q_tile(q0 + dir * kQT, oct);
 
       // ---- mask, row max ----
       float mx0 = -INFINITY, mx1 = -INFINITY;
@@ -290,13 +307,13 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
       // completion counter, so a store issued ahead of a load's wait would make
       // that wait cover the store too. ----
       if (has_next) {
-        __syncthreads();  // every wavefront is done with the oldest ring block
-        const int phys = 16 * kblock0 + (t >> 4);  // the next tile's newest block
+        __syncthreads();  // every wavefront is done with the block being replaced
+        const int phys = 16 * slot(down ? 8 : 0) + (t >> 4);  // the block the next tile replaces
         put_k(ks, kKPlane, phys, nkey, t & 15, pk);
         put_v(vs, phys, t & 15, pv);
         __syncthreads();
       }
-      kblock0 = kblock0 == kSlots - 1 ? 0 : kblock0 + 1;
+      kblock0 = down ? (kblock0 == 0 ? kSlots - 1 : kblock0 - 1) : (kblock0 == kSlots - 1 ? 0 : kblock0 + 1);
 
       // ---- epilogue: O and LSE of this tile ----
       // vmcnt(0) on every path (on the common one the ring update has already
@@ -315,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
         }
       }
     }
-    item = run_end;  // next run
+    item += dir * run_len;  // next run
   }
 }
 
