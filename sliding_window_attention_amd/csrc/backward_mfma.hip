@@ -142,9 +142,17 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
   const int N = a.total_tokens, Hq = a.num_q_heads, hkv = a.num_kv_heads;
   const int ntiles = (N + kQT - 1) / kQT;
   const int total = ntiles * (Hq / kHG);
-  int item = blockIdx.x * items_per_wg;
-  const int item_end = min(item + items_per_wg, total);
-  if (item >= item_end) return;
+  // Runs as in the forward ring kernel: each XCD takes a contiguous range of runs and
+  // odd runs walk their tiles downwards, so that neighbouring runs read the K/V rows
+  // they share at the same time through one L2.
+  const int nwg = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, perx = nwg >> 3, remx = nwg & 7;
+  const int run = xcd * perx + min(xcd, remx) + (bid >> 3);
+  const bool down = run & 1;
+  const int item_lo = run * items_per_wg;
+  const int item_hi = min(item_lo + items_per_wg, total);
+  if (item_lo >= item_hi) return;
+  int item = down ? item_hi - 1 : item_lo;  // next unprocessed item
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // head w of the octet
   const int i = lane & 15, g = lane >> 4;
@@ -182,24 +190,25 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
     dlr = a.delta[hr];
   };
 
-  while (item < item_end) {
+  while (down ? item >= item_lo : item < item_hi) {
     item = __builtin_amdgcn_readfirstlane(item);
     const int oct = item / ntiles;
-    int tile = item - oct * ntiles;
-    const int run_end = min(item_end, (oct + 1) * ntiles);
-    int seq = find_seq_c(cu, S, tile * kQT);
+    const int tile0 = item - oct * ntiles;  // first tile of this run
+    const int run_len = __builtin_amdgcn_readfirstlane(
+        down ? item - max(item_lo, oct * ntiles) + 1 : min(item_hi, (oct + 1) * ntiles) - item);
+    const int dir = down ? -1 : 1;
+    int seq = find_seq_c(cu, S, tile0 * kQT);
     const int kvh = (oct * kHG) / G;
     __syncthreads();  // the previous run is done with the ring
-    fill(ks, vs, kp, vp, tile * kQT - 128, N, hkv, kvh);
-    load_rows(tile * kQT, oct);
+    fill(ks, vs, kp, vp, tile0 * kQT - 128, N, hkv, kvh);
+    load_rows(tile0 * kQT, oct);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    const int run_len = __builtin_amdgcn_readfirstlane(run_end - item);
-    const int tile0 = tile;
+    // ring slot of the tile's oldest block, (tile + 1) mod 9, moving with the walk
     int kblock0 = __builtin_amdgcn_readfirstlane((tile0 + 1) % kSlots);
     for (int k = 0; k < run_len; ++k) {
-      tile = tile0 + k;
+      const int tile = tile0 + dir * k;
       const int q0 = tile * kQT;
       const int kbase = q0 - 128;
       const int par = tile & 1;
@@ -210,7 +219,11 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
       const int h0 = oct * kHG + w;
 
       // ---- visible keys of each row: window and own-sequence start ----
-      while (seq + 1 < S && cu[seq + 1] <= q0) ++seq;
+      if (down) {
+        while (seq > 0 && cu[seq] > q0) --seq;
+      } else {
+        while (seq + 1 < S && cu[seq + 1] <= q0) ++seq;
+      }
       const int qi = q0 + i;
       int start = cu[seq];
       for (int s2 = seq + 1; s2 < S && cu[s2] < q0 + kQT; ++s2)
@@ -265,17 +278,17 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
         }
       }
 
-      // ---- prefetch for the next tile: its 16 newest K/V rows (waves 0-3), its Q, dO,
-      // lse, delta ----
+      // ---- prefetch for the next tile: the 16 K/V rows it adds to the ring (waves 0-3;
+      // its newest block walking up, its oldest walking down), its Q, dO, lse, delta ----
       const bool has_next = k + 1 < run_len;
       u32x4 pk = {0, 0, 0, 0}, pv = {0, 0, 0, 0};
-      const int nkey = q0 + 16 + (t >> 4);
-      if (has_next && t < 256 && nkey < N) {
+      const int nkey = (down ? q0 - 144 : q0 + 16) + (t >> 4);
+      if (has_next && t < 256 && nkey >= 0 && nkey < N) {
         const size_t off = ((size_t)nkey * hkv + kvh) * D + (t & 15) * 8;
         pk = *reinterpret_cast<const u32x4*>(kp + off);
         pv = *reinterpret_cast<const u32x4*>(vp + off);
       }
-      if (has_next) load_rows(q0 + kQT, oct);
+      if (has_next) load_rows(q0 + dir * kQT, oct);
 
       // ---- dQ^T = K^T dS^T: the diagonal block first (k = 16), then the four pairs ----
       f32x4 o0[8];
@@ -307,13 +320,13 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
       if (has_next) {
         __syncthreads();
         if (t < 256) {
-          const int phys = 16 * kblock0 + (t >> 4);
+          const int phys = 16 * slot(down ? 8 : 0) + (t >> 4);  // the block the next tile replaces
           put_k(ks, kPlane, phys, nkey, t & 15, pk);
           put_k(vs, kPlane, phys, nkey, t & 15, pv);
         }
         __syncthreads();
       }
-      kblock0 = kblock0 == kSlots - 1 ? 0 : kblock0 + 1;
+      kblock0 = down ? (kblock0 == 0 ? kSlots - 1 : kblock0 - 1) : (kblock0 == kSlots - 1 ? 0 : kblock0 + 1);
 
       // ---- epilogue: the dq row of this tile ----
       __builtin_amdgcn_s_waitcnt(kVmcnt0);
@@ -322,7 +335,7 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
         store_grad_row(static_cast<bf16*>(a.dq) + ((size_t)(ok ? qi : 0) * Hq + h0) * D, g, o0, a.scale, ok);
       }
     }
-    item = run_end;
+    item += dir * run_len;  // next run
   }
 }
 
