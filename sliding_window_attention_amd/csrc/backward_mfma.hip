@@ -419,6 +419,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
   const int tb_hi = last_query(min(16 * (kt0 + kTiles) - 1, N - 1)) >> 4;
   const int nsteps = tb_hi - tb_lo + 1;
   const int total = (G / 2) * nsteps;  // (head pair, query block) steps
+  // Query block of a step: within each head pair's sweep, step m takes the block tb with
+  // tb = m (mod nsteps).  Neighbouring workgroups share most of their blocks and start
+  // together on one XCD; with this order they read each shared block at the same step.
+  auto step_block = [&](int m) {
+    int r = (m - tb_lo) % nsteps;
+    r += r < 0 ? nsteps : 0;
+    return tb_lo + r;
+  };
 
   // Lane-constant LDS offsets: row reads (pair order) and transposed reads.
   const int pr0 = pair_row(i, 0), pr1 = pair_row(i, 1);
@@ -436,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
   };
   Stage sa, sb;
   auto prefetch = [&](int step, Stage& st) {
-    const int hp = step / nsteps, tb = tb_lo + (step - hp * nsteps);
+    const int hp = step / nsteps, tb = step_block(step - hp * nsteps);
     const int hbase = kvh * G + 2 * hp;
     const int q = min(16 * tb + (t >> 4), N - 1);
 #pragma unroll
@@ -478,7 +486,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
   // takes step + 2; `nxt` holds step + 1, committed to the other buffer at the end.
   auto do_step = [&](int step, Stage& cur, Stage& nxt) {
     if (step + 2 < total) prefetch(step + 2, cur);
-    const int tb = tb_lo + step % nsteps;
+    const int tb = step_block(step % nsteps);
     if (tb >= tbw_lo && tb <= tbw_hi) {
       const char* qs = smem + (step & 1) * kStage;
       const char* ds = qs + kOpBytes;
