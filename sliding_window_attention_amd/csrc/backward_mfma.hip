@@ -15,8 +15,8 @@
 //    sits in an LDS ring that advances by 16 keys per tile.  S^T = K Q^T and dP^T = V dO^T come out with
 //    queries in columns, so dS^T feeds dQ^T = K^T dS^T straight from registers.
 //  * bwd_dkdv_kernel: the transpose -- a workgroup owns 64 keys of one KV head (16
-//    per wavefront) and walks the (head pair, query block) steps that see them, one
-//    LDS-staged block of 16 tokens x 2 heads per step shared by the four wavefronts.
+//    per wavefront) and walks the (head quad, query block) steps that see them, one
+//    LDS-staged block of 16 tokens x 4 heads per step shared by the four wavefronts.
 //    S = Q K^T and dP = dO V^T come out with queries in rows, so P and dS feed
 //    dV^T = dO^T P and dK^T = Q^T dS from registers; each wavefront sums over all
 //    heads of the group itself.
@@ -341,14 +341,15 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
 
 // ---------------------------------------------------------------------------
 // dk, dv: 64 keys per workgroup (16 per wavefront), one shared query block of
-// 16 tokens x 2 heads per step
+// 16 tokens x 4 heads per step
 // ---------------------------------------------------------------------------
 namespace kvtile {
 
-constexpr int kRows = 32;             // 16 tokens x 2 heads; row P = 16 * head_sel + token
-constexpr int kPlane = kRows * 64;    // 2048
-constexpr int kOpBytes = 4 * kPlane;  // 8192 per operand
-constexpr int kStage = 2 * kOpBytes + 2 * kRows * 4;  // Q, dO, lse, delta: 16640
+constexpr int kHeads = 4;             // query heads per step
+constexpr int kRows = 16 * kHeads;    // 16 tokens x 4 heads; row P = 16 * head_sel + token
+constexpr int kPlane = kRows * 64;    // 4096
+constexpr int kOpBytes = 4 * kPlane;  // 16384 per operand
+constexpr int kStage = 2 * kOpBytes + 2 * kRows * 4;  // Q, dO, lse, delta: 33280
 constexpr int kTiles = 4;             // 16-key tiles per workgroup, one per wavefront
 
 }  // namespace kvtile
@@ -418,8 +419,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
   const int tb_lo = kt0;
   const int tb_hi = last_query(min(16 * (kt0 + kTiles) - 1, N - 1)) >> 4;
   const int nsteps = tb_hi - tb_lo + 1;
-  const int total = (G / 2) * nsteps;  // (head pair, query block) steps
-  // Query block of a step: within each head pair's sweep, step m takes the block tb with
+  const int total = (G / kHeads) * nsteps;  // (head quad, query block) steps
+  // Query block of a step: within each head quad's sweep, step m takes the block tb with
   // tb = m (mod nsteps).  Neighbouring workgroups share most of their blocks and start
   // together on one XCD; with this order they read each shared block at the same step.
   auto step_block = [&](int m) {
@@ -435,27 +436,27 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
   const int tlo = tr_base(8 * g + (i >> 2), 8 * g + (i >> 2), i);
   const int thi = tr_base(8 * g + 4 + (i >> 2), 8 * g + 4 + (i >> 2), i);
 
-  // Staging: thread t moves unit t & 15 of token row t >> 4 of both heads, Q and dO;
-  // threads 0-31 move the lse and delta of row P = t.  Two register sets: the loads
-  // of step s + 2 are issued at the start of step s, so they have two steps to land.
+  // Staging: thread t moves unit t & 15 of token row t >> 4 of the four heads, Q and
+  // dO; threads 0-63 move the lse and delta of row P = t.  One register set: the loads
+  // of step s + 1 are issued at the start of step s.
   struct Stage {
-    u32x4 q[2], d[2];
+    u32x4 q[kHeads], d[kHeads];
     float l, dl;
   };
-  Stage sa, sb;
+  Stage sa;
   auto prefetch = [&](int step, Stage& st) {
     const int hp = step / nsteps, tb = step_block(step - hp * nsteps);
-    const int hbase = kvh * G + 2 * hp;
+    const int hbase = kvh * G + kHeads * hp;
     const int q = min(16 * tb + (t >> 4), N - 1);
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs) {
+    for (int hs = 0; hs < kHeads; ++hs) {
       const size_t off = ((size_t)q * Hq + hbase + hs) * D + 8 * (t & 15);
       st.q[hs] = *reinterpret_cast<const u32x4*>(qp + off);
       st.d[hs] = *reinterpret_cast<const u32x4*>(dop + off);
     }
     // every thread loads (threads 32.. duplicate 0..31) and nothing is computed on the
     // values here: a branch or an early use would make the compiler wait for the load
-    const size_t r = (size_t)min(16 * tb + (t & 15), N - 1) * Hq + hbase + ((t >> 4) & 1);
+    const size_t r = (size_t)min(16 * tb + (t & 15), N - 1) * Hq + hbase + ((t >> 4) & (kHeads - 1));
     st.l = a.lse[r];
     st.dl = a.delta[r];
   };
@@ -464,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
     char* ds = qs + kOpBytes;
     float* ls = reinterpret_cast<float*>(ds + kOpBytes);
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs) {
+    for (int hs = 0; hs < kHeads; ++hs) {
       const int P = 16 * hs + (t >> 4);
       put_k(qs, kPlane, P, P, t & 15, st.q[hs]);
       put_k(ds, kPlane, P, P, t & 15, st.d[hs]);
@@ -482,75 +483,82 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
     dv[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  // One step: `cur` held this step's block (already in LDS buffer step & 1) and now
-  // takes step + 2; `nxt` holds step + 1, committed to the other buffer at the end.
-  auto do_step = [&](int step, Stage& cur, Stage& nxt) {
-    if (step + 2 < total) prefetch(step + 2, cur);
+  // One step: its block is already in LDS buffer step & 1; the next step's loads are
+  // issued first and committed to the other buffer at the end.
+  auto do_step = [&](int step) {
+    if (step + 1 < total) prefetch(step + 1, sa);
     const int tb = step_block(step % nsteps);
     if (tb >= tbw_lo && tb <= tbw_hi) {
       const char* qs = smem + (step & 1) * kStage;
       const char* ds = qs + kOpBytes;
       const float* ls = reinterpret_cast<const float*>(ds + kOpBytes);
-      // ---- S = Q K^T and dP = dO V^T for the two 16-row blocks of the pair ----
-      f32x4 s[2], tt[2];
+      // ---- S = Q K^T and dP = dO V^T for two pairs of 16-row blocks (rows 32 pi ..) ----
+      f32x4 s[2][2], tt[2][2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        s[h] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        tt[h] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        const int ro = h ? ro1 : ro0;
+      for (int pi = 0; pi < 2; ++pi)
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qs + cc * kPlane + ro);
-          const bf16x8 df = *reinterpret_cast<const bf16x8*>(ds + cc * kPlane + ro);
-          s[h] = mfma32(qf, kb[cc], s[h]);
-          tt[h] = mfma32(df, vb[cc], tt[h]);
+        for (int h = 0; h < 2; ++h) {
+          s[pi][h] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          tt[pi][h] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          const int ro = (h ? ro1 : ro0) + 32 * 64 * pi;
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qs + cc * kPlane + ro);
+            const bf16x8 df = *reinterpret_cast<const bf16x8*>(ds + cc * kPlane + ro);
+            s[pi][h] = mfma32(qf, kb[cc], s[pi][h]);
+            tt[pi][h] = mfma32(df, vb[cc], tt[pi][h]);
+          }
         }
-      }
-      // lane (i, g) holds rows P = 8g + 4h + r: token 8 (g & 1) + 4h + r of head g >> 1
-      const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls + 8 * g);
-      const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + 8 * g + 4);
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(ls + kRows + 8 * g);
-      const f32x4 d1 = *reinterpret_cast<const f32x4*>(ls + kRows + 8 * g + 4);
-      f32x4 p[2], x[2];
+      // lane (i, g) holds rows P = 32 pi + 8g + 4h + r: token 8 (g & 1) + 4h + r
+      bf16x8 pp[2], xp[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int pi = 0; pi < 2; ++pi) {
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls + 32 * pi + 8 * g);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + 32 * pi + 8 * g + 4);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(ls + kRows + 32 * pi + 8 * g);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(ls + kRows + 32 * pi + 8 * g + 4);
+        f32x4 p[2], x[2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = 16 * tb + 8 * (g & 1) + 4 * h + r;
-          const bool ok = (unsigned)(q - jm) <= span;
-          const float e = fast_exp2(fmaf(s[h][r], c, -(h ? l1[r] : l0[r])));
-          p[h][r] = ok ? e : 0.f;
-          x[h][r] = p[h][r] * (tt[h][r] - (h ? d1[r] : d0[r]));
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int q = 16 * tb + 8 * (g & 1) + 4 * h + r;
+            const bool ok = (unsigned)(q - jm) <= span;
+            const float e = fast_exp2(fmaf(s[pi][h][r], c, -(h ? l1[r] : l0[r])));
+            p[h][r] = ok ? e : 0.f;
+            x[h][r] = p[h][r] * (tt[pi][h][r] - (h ? d1[r] : d0[r]));
+          }
         }
+        pp[pi] = pack_pair(p[0], p[1]);
+        xp[pi] = pack_pair(x[0], x[1]);
       }
-      const bf16x8 pp = pack_pair(p[0], p[1]);
-      const bf16x8 xp = pack_pair(x[0], x[1]);
 
-      // ---- dV^T += dO^T P and dK^T += Q^T dS over the pair's 32 rows ----
+      // ---- dV^T += dO^T P and dK^T += Q^T dS over the step's 64 rows ----
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const bf16x4 dlo = tr_read(ds, tr_at(tlo, b, kPlane));
-        const bf16x4 dhi = tr_read(ds, tr_at(thi, b, kPlane));
-        const bf16x4 qlo = tr_read(qs, tr_at(tlo, b, kPlane));
-        const bf16x4 qhi = tr_read(qs, tr_at(thi, b, kPlane));
-        dv[b] = mfma32((bf16x8){dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]}, pp, dv[b]);
-        dk[b] = mfma32((bf16x8){qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]}, xp, dk[b]);
+      for (int pi = 0; pi < 2; ++pi) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const int lo = tr_at(tlo, b, kPlane) + 32 * 64 * pi;
+          const int hi = tr_at(thi, b, kPlane) + 32 * 64 * pi;
+          const bf16x4 dlo = tr_read(ds, lo);
+          const bf16x4 dhi = tr_read(ds, hi);
+          const bf16x4 qlo = tr_read(qs, lo);
+          const bf16x4 qhi = tr_read(qs, hi);
+          dv[b] = mfma32((bf16x8){dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]}, pp[pi], dv[b]);
+          dk[b] = mfma32((bf16x8){qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]}, xp[pi], dk[b]);
+        }
       }
     }
     // the other buffer was last read in the previous step, which every wavefront has
     // finished (barrier below)
-    if (step + 1 < total) commit((step + 1) & 1, nxt);
+    if (step + 1 < total) commit((step + 1) & 1, sa);
     __syncthreads();
   };
 
   prefetch(0, sa);
-  if (1 < total) prefetch(1, sb);
   commit(0, sa);
   __syncthreads();
-  for (int step = 0; step < total; step += 2) {
-    do_step(step, sa, sb);
-    if (step + 1 < total) do_step(step + 1, sb, sa);
-  }
+  for (int step = 0; step < total; ++step) do_step(step);
 
   const size_t krow = ((size_t)(kvalid ? j : 0) * hkv + kvh) * D;
   store_grad_row(static_cast<bf16*>(a.dk) + krow, g, dk, a.scale, kvalid);
