@@ -133,6 +133,35 @@ def _prefill_fn(window, ga=False):
     return fn
 
 
+def _prefill_fp8_fn(window):
+    """Timed call of swa_sink_prefill_fp8kv (E4M3 K/V), arguments marshalled once per input set."""
+    import ctypes
+
+    import torch
+
+    import sliding_window_attention_amd as swa
+
+    lib = swa.library()
+    cache = {}
+
+    def fn(x):
+        key = id(x)
+        if key not in cache:
+            swa.swa_sink_prefill_fp8kv(x["q"], x["k"], x["v"], x["k_scale"], x["v_scale"], x["sinks"],
+                                       x["cu_seqlens"], x["max_seqlen"], window=window, out=x["out"],
+                                       lse=x["lse"])
+            n, hq, d = x["q"].shape
+            stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            cache[key] = (x["q"].data_ptr(), x["k"].data_ptr(), x["v"].data_ptr(), ctypes.c_float(x["k_scale"]),
+                          ctypes.c_float(x["v_scale"]), x["sinks"].data_ptr(), x["cu_seqlens"].data_ptr(),
+                          x["cu_seqlens"].numel() - 1, n, int(x["max_seqlen"]), hq, x["k"].shape[1], d,
+                          window, 0.0, 1, x["out"].data_ptr(), x["lse"].data_ptr(), stream)
+        rc = lib.swa_sink_prefill_fp8kv(*cache[key])
+        if rc != 0:
+            raise RuntimeError(lib.swa_last_error().decode())
+    return fn
+
+
 def _decode_fn():
     """Timed call of swa_sink_decode, arguments marshalled once per input set."""
     import ctypes
@@ -487,7 +516,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="time only the primary workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["prefill", "decode", "decode1", "decode_fp8", "decode_fp8_1",
+    ap.add_argument("--only", choices=["prefill", "prefill_fp8", "decode", "decode1", "decode_fp8", "decode_fp8_1",
                                        "decode_rope", "decode_rope_1", "append", "mtp_step", "rope",
                                        "topk", "sparse",
                                        "ga", "varlen", "backward", "copy"],
@@ -564,7 +593,8 @@ def main(argv=None):
         _log(f"rope q 32K: {st}  {by / (st['mean_ms'] * 1e-3) / 1e9:.0f} GB/s")
         return 0
     if args.only is not None:
-        name = {"prefill": PRIMARY, "decode": "decode_t4", "decode1": "decode_t1",
+        name = {"prefill": PRIMARY, "prefill_fp8": "swa_prefill_fp8kv_32k", "decode": "decode_t4",
+                "decode1": "decode_t1",
                 "decode_fp8": "decode_fp8_t4", "decode_fp8_1": "decode_fp8_t1",
                 "decode_rope": "decode_rope_t4", "decode_rope_1": "decode_rope_t1",
                 "ga": "hybrid_5to1_32k", "varlen": "varlen_262k"}[args.only]
@@ -573,6 +603,8 @@ def main(argv=None):
         x = _with_outputs(_to(wl.make_workload(name, layer), dev), "decode" if dec else "p")
         if args.only.startswith("decode_fp8"):
             fn = _decode_fp8_fn()
+        elif args.only == "prefill_fp8":
+            fn = _prefill_fp8_fn(128)
         elif args.only.startswith("decode_rope"):
             fn = _decode_rope_fn()
         else:
@@ -658,6 +690,18 @@ def run_extra(dev, steps, warmup):
     per, _ = _time_calls(lambda _: b.copy_(a), [None], 20, 3)
     extra["copy_ceiling_gbps"] = 2 * a.numel() * 2 / (min(per) * 1e-3) / 1e9
     del a, b
+
+    _log("swa_prefill_fp8kv_32k")
+    x = _with_outputs(_to(wl.make_workload("swa_prefill_fp8kv_32k"), dev), "prefill")
+    sets = _clone_sets(x, 4)
+    per, _ = _time_calls(_prefill_fp8_fn(128), sets, steps, warmup, per_call=False)
+    fl, by = wl.workload_work("swa_prefill_fp8kv_32k")
+    st = _stats(per)
+    extra["swa_prefill_fp8kv_32k"] = {**st, "gbps": by / (st["mean_ms"] * 1e-3) / 1e9,
+                                      "hbm_frac": by / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                      "tflops": fl / (st["mean_ms"] * 1e-3) / 1e12, "bytes": by}
+    del sets, x
+    torch.cuda.empty_cache()
 
     for name in ("decode_t1", "decode_t4", "decode_fp8_t1", "decode_fp8_t4", "decode_rope_t1",
                  "decode_rope_t4"):

@@ -57,7 +57,7 @@ typedef enum {
 
 typedef enum { SWA_DTYPE_F32 = 0, SWA_DTYPE_BF16 = 1 } swa_dtype;
 
-#define SWASINK_ABI_VERSION 5
+#define SWASINK_ABI_VERSION 6
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SWASINK_API __attribute__((visibility("default")))
@@ -99,6 +99,26 @@ SWASINK_API int ga_causal_prefill(const void* q, const void* k, const void* v, c
                       int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen,
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale,
                       swa_dtype dtype, void* out, float* lse, void* stream);
+
+/*
+ * swa_sink_prefill (or, with NULL sinks and an unbounded window, the GA layer) with K
+ * and V as one-byte E4M3 codes: the FP8 (E4M3) KV format of the MiMo-V2 blog, section
+ * 6, with the same bit layout and per-tensor scales as swa_sink_decode_fp8kv.  The
+ * value of a key / value element is its code's value times k_scale / v_scale.  Q, sinks,
+ * out and lse keep their types; every other argument, the masking and the outputs are
+ * those of swa_sink_prefill.
+ *
+ *  k, v             [total_tokens, num_kv_heads, head_dim] uint8 E4M3 codes
+ *  k_scale, v_scale host fp32, finite and > 0 (SWA_ERR_SHAPE otherwise)
+ *  sinks            [num_q_heads] fp32, or NULL for no sink (GA: window = INT32_MAX)
+ * The K/V bytes halve against bf16; at window 128 they are 1/9 of the prefill's bytes.
+ */
+SWASINK_API int swa_sink_prefill_fp8kv(const void* q, const uint8_t* k, const uint8_t* v, float k_scale,
+                           float v_scale, const float* sinks, const int32_t* cu_seqlens,
+                           int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t window, float scale, swa_dtype dtype, void* out, float* lse,
+                           void* stream);
 
 /*
  * Decode / MTP verify against a window-slot ring buffer per (sequence, KV head).

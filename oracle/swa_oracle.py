@@ -323,6 +323,21 @@ def swa_sink_decode_fp8kv(q, k_new, v_new, k_codes, v_codes, k_scale, v_scale, r
     return swa_sink_decode(q, k_new, v_new, kc, vc, ring_head, sinks, window=window, scale=scale)
 
 
+def swa_sink_prefill_fp8kv(q, k_codes, v_codes, k_scale, v_scale, sinks, cu_seqlens, window=128,
+                           scale=None, block=128):
+    """Prefill whose K and V are stored as E4M3 codes (the same FP8 KV format and
+    per-tensor scales as swa_sink_decode_fp8kv): key / value element = the code's E4M3
+    value times k_scale / v_scale.  sinks=None means no sink and window=None an
+    unbounded window (the GA layer).  Everything else is the prefill operator on the
+    dequantised K and V.
+    """
+    k = e4m3_to_float(k_codes) * float(k_scale)
+    v = e4m3_to_float(v_codes) * float(v_scale)
+    if window is None and sinks is None:
+        return ga_causal_prefill(q, k, v, cu_seqlens, scale, block)
+    return _prefill(q, k, v, sinks, cu_seqlens, None if window is None else int(window), scale, block)
+
+
 def hybrid_block(layers, window=128, scale=None):
     """Five SWA-with-sink layers then one GA layer, each on its own inputs.
 

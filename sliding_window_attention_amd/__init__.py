@@ -40,6 +40,8 @@ _SIGNATURES = {
                                   _P, _P, _P, _P, _P, ctypes.c_int64, _P],
     "swa_sink_decode_fp8kv": [_P, _P, _P, _P, _P, _F, _F, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
                               _P, _P, _P],
+    "swa_sink_prefill_fp8kv": [_P, _P, _P, _F, _F, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P,
+                               _P],
     "swa_rope": [_P, _P, _I, _I, _I, _F, _I, _P],
     "swa_sink_decode_rope": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I,
                              _P, _P, _P],
@@ -167,6 +169,40 @@ def swa_sink_prefill(q, k, v, sinks, cu_seqlens, max_seqlen=None, window=128, sc
         cu_seqlens.numel() - 1, n, ms, hq, k.shape[1], d, int(window), _scale(scale),
         _dtype_code(q), out.data_ptr(), lse.data_ptr() if lse is not None else None,
         _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def swa_sink_prefill_fp8kv(q, k, v, k_scale, v_scale, sinks, cu_seqlens, max_seqlen=None, window=128,
+                           scale=None, return_lse=True, out=None, lse=None):
+    """swa_sink_prefill with k/v [N, Hkv, D] uint8 E4M3 codes, element value = code value *
+    k_scale (K) or v_scale (V) (python floats).  sinks may be None (no sink); with
+    window=None the window is unbounded (the GA layer)."""
+    import torch
+
+    _dev(q, "q")
+    _dev(k, "k", torch.uint8)
+    _dev(v, "v", torch.uint8)
+    if sinks is not None:
+        _dev(sinks, "sinks", torch.float32)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("q must be [N, Hq, D] and k, v [N, Hkv, D]")
+    n, hq, d = q.shape
+    if k.shape[0] != n or k.shape[2] != d or (sinks is not None and sinks.numel() != hq):
+        raise ValueError("inconsistent shapes")
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    if return_lse and lse is None:
+        lse = torch.empty((n, hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+    ms = n if max_seqlen is None else int(max_seqlen)
+    win = 0x7FFFFFFF if window is None else int(window)
+    rc = library().swa_sink_prefill_fp8kv(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), float(k_scale), float(v_scale),
+        sinks.data_ptr() if sinks is not None else None, cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+        n, ms, hq, k.shape[1], d, win, _scale(scale), _dtype_code(q), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, _stream(q.device))
     _check(rc)
     return out, lse
 

@@ -77,9 +77,11 @@ int prefill_common(const void* q, const void* k, const void* v, const float* sin
                    bool need_sinks, const int32_t* cu_seqlens, int32_t num_seqs,
                    int32_t total_tokens, int32_t max_seqlen, int32_t hq, int32_t hkv, int32_t d,
                    int32_t window, float scale, int dtype, void* out, float* lse, void* stream,
-                   const char* name) {
+                   const char* name, bool fp8 = false, float k_scale = 1.f, float v_scale = 1.f) {
   int rc = check_dtype(dtype);
   if (rc) return rc;
+  if (fp8 && !(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f))
+    return fail(SWA_ERR_SHAPE, "%s: k_scale and v_scale must be finite and > 0", name);
   if (total_tokens < 0) return fail(SWA_ERR_SHAPE, "%s: total_tokens must be >= 0", name);
   if (num_seqs < 1) return fail(SWA_ERR_SHAPE, "%s: num_seqs must be >= 1", name);
   if (num_seqs > total_tokens && total_tokens > 0)
@@ -106,6 +108,9 @@ int prefill_common(const void* q, const void* k, const void* v, const float* sin
   a.num_q_heads = hq; a.num_kv_heads = hkv; a.head_dim = d;
   a.window = window;
   a.scale = resolve_scale(scale, d);
+  a.kv_fp8 = fp8;
+  a.k_scale = fp8 ? k_scale : 1.f;
+  a.v_scale = fp8 ? v_scale : 1.f;
   const bool bf = dtype == SWA_DTYPE_BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -197,6 +202,17 @@ int ga_causal_prefill(const void* q, const void* k, const void* v, const int32_t
   return prefill_common(q, k, v, nullptr, false, cu_seqlens, num_seqs, total_tokens, max_seqlen,
                         num_q_heads, num_kv_heads, head_dim, 0x7fffffff, scale, (int)dtype, out,
                         lse, stream, "ga_causal_prefill");
+}
+
+int swa_sink_prefill_fp8kv(const void* q, const uint8_t* k, const uint8_t* v, float k_scale,
+                           float v_scale, const float* sinks, const int32_t* cu_seqlens,
+                           int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t window, float scale, swa_dtype dtype, void* out, float* lse,
+                           void* stream) {
+  return prefill_common(q, k, v, sinks, false, cu_seqlens, num_seqs, total_tokens, max_seqlen,
+                        num_q_heads, num_kv_heads, head_dim, window, scale, (int)dtype, out, lse,
+                        stream, "swa_sink_prefill_fp8kv", true, k_scale, v_scale);
 }
 
 int swa_sink_decode(const void* q, const void* k_new, const void* v_new, const void* k_cache,

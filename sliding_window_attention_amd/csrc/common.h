@@ -45,6 +45,9 @@ struct PrefillArgs {
   int32_t head_dim;
   int32_t window;           // keys i-window+1 .. i; INT32_MAX for unbounded
   float scale;              // logit scale (already resolved, > 0)
+  bool kv_fp8 = false;      // k / v hold one-byte E4M3 codes
+  float k_scale = 1.f;      // with kv_fp8: element value = code value * scale
+  float v_scale = 1.f;
 };
 
 // Parameters of one decode / MTP-verify call against a ring buffer.

@@ -14,6 +14,8 @@
 // by more than kSlack (log2 units); otherwise the exponent keeps the older, smaller
 // reference and the weights may exceed 1 by at most 2^kSlack, which fp32 sums and
 // bf16 weights hold without loss of relative precision.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "mfma_tile.h"
@@ -34,6 +36,14 @@ constexpr int kVBuf = kStage * kVPitch;  // 33792
 constexpr int kBuf = kKBuf + kVBuf;
 constexpr float kSlack = 8.f;
 
+// Staged K/V as loaded: 16 bytes of bf16, or (FP8) 8 bytes of E4M3 codes widened to
+// bf16 (exactly) only when committed to LDS, so that no conversion waits on a load.
+template <bool FP8>
+using GaRaw = typename std::conditional<FP8, u32x2, u32x4>::type;
+
+// FP8: K and V arrive as E4M3 codes; the K scale joins the logit multiplier and the V
+// scale the output's 1/l.
+template <bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void ga_chunk_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kBuf];
@@ -51,10 +61,11 @@ void ga_chunk_kernel(PrefillArgs a) {
   const int h0 = oct * kHG + 2 * (w & 3);
   const int qw = q0 + 16 * (w >> 2);  // first query of this wavefront's tiles
   const int qi = qw + i;
-  const bf16* kp = static_cast<const bf16*>(a.k);
-  const bf16* vp = static_cast<const bf16*>(a.v);
+  using KvT = typename std::conditional<FP8, uint8_t, bf16>::type;
+  const KvT* kp = static_cast<const KvT*>(a.k);
+  const KvT* vp = static_cast<const KvT*>(a.v);
   const bf16* qp = static_cast<const bf16*>(a.q);
-  const float c = a.scale * kLog2e;
+  const float c = a.scale * kLog2e * (FP8 ? a.k_scale : 1.f);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // ---- first visible key of each row, of this wavefront and of the workgroup ----
@@ -85,9 +96,9 @@ void ga_chunk_kernel(PrefillArgs a) {
   // srow + 32 j (j < 4), srow = t >> 4, of K (pf[j]) and of V (pf[4 + j]) ----
   const int srow = t >> 4, su = t & 15;
   const size_t key_stride = (size_t)hkv * D;  // elements from one key's row to the next
-  const uint32_t goff0 = (uint32_t)((((size_t)srow * hkv + kvh) * D + su * 8) * sizeof(bf16));
+  const uint32_t goff0 = (uint32_t)((((size_t)srow * hkv + kvh) * D + su * 8) * sizeof(KvT));
   const size_t gstep = 32 * key_stride;  // elements from row r to row r + 32
-  u32x4 pf[8];
+  GaRaw<FP8> pf[8];
   bool edge = false;  // (uniform) the staged keys reach outside [0, N)
   bool ok[4] = {true, true, true, true};  // row srow + 32 j of the stage exists
   auto prefetch = [&](int kb) {
@@ -98,8 +109,8 @@ void ga_chunk_kernel(PrefillArgs a) {
       for (int j = 0; j < 4; ++j) {
         const char* kbase = reinterpret_cast<const char*>(kp + (size_t)kb * key_stride + j * gstep);
         const char* vbase = reinterpret_cast<const char*>(vp + (size_t)kb * key_stride + j * gstep);
-        pf[j] = *reinterpret_cast<const u32x4*>(kbase + goff0);
-        pf[4 + j] = *reinterpret_cast<const u32x4*>(vbase + goff0);
+        pf[j] = *reinterpret_cast<const GaRaw<FP8>*>(kbase + goff0);
+        pf[4 + j] = *reinterpret_cast<const GaRaw<FP8>*>(vbase + goff0);
       }
     } else {
       // rows outside the stream load a clamped row (no masked loads, which would
@@ -109,8 +120,8 @@ void ga_chunk_kernel(PrefillArgs a) {
         const int r = kb + srow + 32 * j;
         ok[j] = r >= 0 && r < N;
         const size_t e = ((size_t)min(max(r, 0), N - 1) * hkv + kvh) * D + su * 8;
-        pf[j] = *reinterpret_cast<const u32x4*>(kp + e);
-        pf[4 + j] = *reinterpret_cast<const u32x4*>(vp + e);
+        pf[j] = *reinterpret_cast<const GaRaw<FP8>*>(kp + e);
+        pf[4 + j] = *reinterpret_cast<const GaRaw<FP8>*>(vp + e);
       }
     }
   };
@@ -123,14 +134,22 @@ void ga_chunk_kernel(PrefillArgs a) {
     if (edge) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (!ok[j]) { pf[j] = (u32x4){0, 0, 0, 0}; pf[4 + j] = (u32x4){0, 0, 0, 0}; }
+        if (!ok[j]) { pf[j] = GaRaw<FP8>{}; pf[4 + j] = GaRaw<FP8>{}; }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<u32x4*>(buf + ks_off + 32 * 64 * j) = pf[j];
+      u32x4 kx, vx;
+      if constexpr (FP8) {
+        kx = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(pf[j]));
+        vx = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(pf[4 + j]));
+      } else {
+        kx = pf[j];
+        vx = pf[4 + j];
+      }
+      *reinterpret_cast<u32x4*>(buf + ks_off + 32 * 64 * j) = kx;
       char* v = buf + vs_off + 32 * kVPitch * j;
-      *reinterpret_cast<u32x2*>(v) = (u32x2){pf[4 + j][0], pf[4 + j][1]};
-      *reinterpret_cast<u32x2*>(v + 8) = (u32x2){pf[4 + j][2], pf[4 + j][3]};
+      *reinterpret_cast<u32x2*>(v) = (u32x2){vx[0], vx[1]};
+      *reinterpret_cast<u32x2*>(v + 8) = (u32x2){vx[2], vx[3]};
     }
   };
 
@@ -279,8 +298,9 @@ void ga_chunk_kernel(PrefillArgs a) {
   l1 = quad_sum(l1);
   if (qi < N) {
     bf16* out = static_cast<bf16*>(a.out) + ((size_t)qi * Hq + h0) * D;
-    store_row_tr(out, g, o0, __builtin_amdgcn_rcpf(l0));
-    store_row_tr(out + D, g, o1, __builtin_amdgcn_rcpf(l1));
+    const float vmul = FP8 ? a.v_scale : 1.f;
+    store_row_tr(out, g, o0, __builtin_amdgcn_rcpf(l0) * vmul);
+    store_row_tr(out + D, g, o1, __builtin_amdgcn_rcpf(l1) * vmul);
     if (a.lse != nullptr && g == 0) {
       float* l = a.lse + (size_t)qi * Hq + h0;
       l[0] = (m0 + fast_log2(l0)) * kLn2;
@@ -300,7 +320,10 @@ hipError_t launch_online_mfma(const PrefillArgs& a, hipStream_t s) {
   const long ntiles = (a.total_tokens + kQT - 1) / kQT;
   const long total = ntiles * (a.num_q_heads / kHG);
   if (total > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(ga_chunk_kernel, dim3((unsigned)total), dim3(kThreads), 0, s, a);
+  if (a.kv_fp8)
+    hipLaunchKernelGGL(ga_chunk_kernel<true>, dim3((unsigned)total), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(ga_chunk_kernel<false>, dim3((unsigned)total), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

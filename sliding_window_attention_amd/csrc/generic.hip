@@ -40,18 +40,29 @@ template <> struct Elem<bf16> {
 // Key sources hand attend_row fp32 values: load_key(j, d, dst) fills dst with
 // Elem<T>::kVec head-dim elements d.. of key j, load_val(j, e) is element e of value j.
 
-// Keys of one prefill row: positions jlo..jhi of the packed stream, KV head kvh.
-template <typename T, int D>
+// Keys of one prefill row: positions jlo..jhi of the packed stream, KV head kvh.  FP8:
+// K and V hold E4M3 codes whose values are scaled by k_scale / v_scale.
+template <typename T, int D, bool FP8>
 struct PrefillKeys {
-  const T* k;
-  const T* v;
+  using C = typename std::conditional<FP8, uint8_t, T>::type;
+  const C* k;
+  const C* v;
   int row_stride;  // Hkv * D
   int kvh;
+  float k_scale, v_scale;
   __device__ void load_key(int j, int d, float* dst) const {
-    Elem<T>::load16(k + (size_t)j * row_stride + kvh * D + d, dst);
+    const C* row = k + (size_t)j * row_stride + kvh * D + d;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int e = 0; e < Elem<T>::kVec; ++e) dst[e] = e4m3_to_f32(row[e]) * k_scale;
+    } else {
+      Elem<T>::load16(row, dst);
+    }
   }
   __device__ float load_val(int j, int e) const {
-    return Elem<T>::load1(v + (size_t)j * row_stride + kvh * D + e);
+    const C* p = v + (size_t)j * row_stride + kvh * D + e;
+    if constexpr (FP8) return e4m3_to_f32(*p) * v_scale;
+    else return Elem<T>::load1(p);
   }
 };
 
@@ -190,7 +201,7 @@ __device__ void attend_row(const T* __restrict__ qrow, const Keys& keys, int jlo
 
 constexpr int kRowsPerBlock = 4;
 
-template <typename T, int D>
+template <typename T, int D, bool FP8>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void generic_prefill_kernel(PrefillArgs a) {
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   const int hq = a.num_q_heads;
@@ -200,8 +211,9 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void generic_prefill_kernel(
   const int kvh = h / (hq / a.num_kv_heads);
   const int start = seq_start_of(a.cu_seqlens, a.num_seqs, n);
   const int lo = (a.window >= n - start + 1) ? start : n - a.window + 1;
-  PrefillKeys<T, D> keys{static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                         a.num_kv_heads * D, kvh};
+  using C = typename PrefillKeys<T, D, FP8>::C;
+  PrefillKeys<T, D, FP8> keys{static_cast<const C*>(a.k), static_cast<const C*>(a.v),
+                              a.num_kv_heads * D, kvh, a.k_scale, a.v_scale};
   const float sink2 = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
   const T* qrow = static_cast<const T*>(a.q) + (size_t)row * D;
   T* orow = static_cast<T*>(a.out) + (size_t)row * D;
@@ -287,8 +299,12 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
   const long rows = (long)a.total_tokens * a.num_q_heads;
   const long blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((generic_prefill_kernel<T, D>), dim3((unsigned)blocks),
-                     dim3(kRowsPerBlock * kWave), 0, s, a);
+  if (a.kv_fp8)
+    hipLaunchKernelGGL((generic_prefill_kernel<T, D, true>), dim3((unsigned)blocks),
+                       dim3(kRowsPerBlock * kWave), 0, s, a);
+  else
+    hipLaunchKernelGGL((generic_prefill_kernel<T, D, false>), dim3((unsigned)blocks),
+                       dim3(kRowsPerBlock * kWave), 0, s, a);
   return hipGetLastError();
 }
 

@@ -15,6 +15,8 @@
 // band in an LDS ring across consecutive tiles, walking their run of tiles upwards
 // or (odd runs) downwards, so that neighbouring runs read the rows they share at the
 // same time on the same XCD.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "mfma_tile.h"
@@ -38,29 +40,46 @@ constexpr int kVBytes = kRows * kVPitch;     // 38016
 
 __device__ __forceinline__ int mod9(int x) { x %= kSlots; return x < 0 ? x + kSlots : x; }
 
+// Eight K/V elements starting at element `elem`, as loaded: bf16 in 16 bytes, or (FP8)
+// eight E4M3 codes in 8 bytes, widened to bf16 only when written to the ring (widen),
+// so that no conversion waits on a load where it is issued.
+template <bool FP8>
+using KvRaw = typename std::conditional<FP8, u32x2, u32x4>::type;
+template <bool FP8>
+__device__ __forceinline__ KvRaw<FP8> load_kv(const void* base, size_t elem) {
+  if constexpr (FP8) return *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(base) + elem);
+  else return *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(base) + elem);
+}
+template <bool FP8>
+__device__ __forceinline__ u32x4 widen(KvRaw<FP8> x) {
+  if constexpr (FP8) return __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(x));  // exact
+  else return x;
+}
+
 // Load all 144 rows of a tile whose first key is kbase into the ring.
-__device__ __attribute__((noinline)) void fill(char* ks, char* vs, const bf16* __restrict__ k,
-                                     const bf16* __restrict__ v, int kbase, int N, int hkv, int kvh) {
+template <bool FP8>
+__device__ __attribute__((noinline)) void fill(char* ks, char* vs, const void* __restrict__ k,
+                                     const void* __restrict__ v, int kbase, int N, int hkv, int kvh) {
   const int t = threadIdx.x;
   const int r = t >> 4, u = t & 15;
   const int kblock0 = mod9(kbase >> 4);
-  u32x4 kr[kSlots], vr[kSlots];
+  KvRaw<FP8> kr[kSlots], vr[kSlots];
 #pragma unroll
   for (int j = 0; j < kSlots; ++j) {
     const int key = kbase + 16 * j + r;
-    kr[j] = (u32x4){0, 0, 0, 0};
-    vr[j] = (u32x4){0, 0, 0, 0};
+    kr[j] = KvRaw<FP8>{};
+    vr[j] = KvRaw<FP8>{};
     if (key >= 0 && key < N) {
       const size_t off = ((size_t)key * hkv + kvh) * D + u * 8;
-      kr[j] = *reinterpret_cast<const u32x4*>(k + off);
-      vr[j] = *reinterpret_cast<const u32x4*>(v + off);
+      kr[j] = load_kv<FP8>(k, off);
+      vr[j] = load_kv<FP8>(v, off);
     }
   }
 #pragma unroll
   for (int j = 0; j < kSlots; ++j) {
     const int phys = 16 * mod9(kblock0 + j) + r;
-    put_k(ks, kKPlane, phys, kbase + 16 * j + r, u, kr[j]);
-    put_v(vs, phys, u, vr[j]);
+    put_k(ks, kKPlane, phys, kbase + 16 * j + r, u, widen<FP8>(kr[j]));
+    put_v(vs, phys, u, widen<FP8>(vr[j]));
   }
 }
 
@@ -77,6 +96,9 @@ __device__ __forceinline__ int find_seq(const_ptr<int32_t> cu, int num_seqs, int
   return lo;
 }
 
+// FP8: K and V arrive as E4M3 codes and are widened to bf16 (exactly) on their way into
+// the ring; the K scale joins the logit multiplier and the V scale the output's 1/Z.
+template <bool FP8>
 __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, int items_per_wg) {
   using namespace ring;
   __shared__ __attribute__((aligned(16))) char smem[kKBytes + kVBytes];
@@ -107,10 +129,11 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
   const int S = a.num_seqs;
   const const_ptr<int32_t> cu = as_const(a.cu_seqlens);
   const const_ptr<float> sinks = as_const(a.sinks);
-  const bf16* kp = static_cast<const bf16*>(a.k);
-  const bf16* vp = static_cast<const bf16*>(a.v);
+  const void* kp = a.k;
+  const void* vp = a.v;
   const bf16* qp = static_cast<const bf16*>(a.q);
-  const float c = a.scale * kLog2e;
+  const float c = a.scale * kLog2e * (FP8 ? a.k_scale : 1.f);
+  const float vmul = FP8 ? a.v_scale : 1.f;
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // Lane-constant parts of the LDS addresses.
@@ -145,7 +168,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
     int seq = find_seq(cu, S, tile0 * kQT);  // sequence of the tile's first query
     const int kvh = (oct * kHG) / G;
     __syncthreads();  // the previous run is done with the ring
-    fill(ks, vs, kp, vp, tile0 * kQT - 128, N, hkv, kvh);
+    fill<FP8>(ks, vs, kp, vp, tile0 * kQT - 128, N, hkv, kvh);
     load_q_tile(tile0 * kQT, oct);
     // Drain the run prologue's loads so that, at the loop head, no vector load
     // is outstanding on any path: each iteration waits for its prefetches
@@ -221,12 +244,12 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
       // ---- prefetch for the next tile: the 16 K/V rows it adds to the ring (its newest
       // block walking up, its oldest walking down) and its Q ----
       const bool has_next = k + 1 < run_len;
-      u32x4 pk = {0, 0, 0, 0}, pv = {0, 0, 0, 0};
+      KvRaw<FP8> pk{}, pv{};
       const int nkey = (down ? q0 - 144 : q0 + 16) + (t >> 4);
       if (has_next && nkey >= 0 && nkey < N) {
         const size_t off = ((size_t)nkey * hkv + kvh) * D + (t & 15) * 8;
-        pk = *reinterpret_cast<const u32x4*>(kp + off);
-        pv = *reinterpret_cast<const u32x4*>(vp + off);
+        pk = load_kv<FP8>(kp, off);
+        pv = load_kv<FP8>(vp, off);
       }
       if (has_next) load_q_tile(q0 + dir * kQT, oct);
 
@@ -309,8 +332,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
       if (has_next) {
         __syncthreads();  // every wavefront is done with the block being replaced
         const int phys = 16 * slot(down ? 8 : 0) + (t >> 4);  // the block the next tile replaces
-        put_k(ks, kKPlane, phys, nkey, t & 15, pk);
-        put_v(vs, phys, t & 15, pv);
+        put_k(ks, kKPlane, phys, nkey, t & 15, widen<FP8>(pk));
+        put_v(vs, phys, t & 15, widen<FP8>(pv));
         __syncthreads();
       }
       kblock0 = down ? (kblock0 == 0 ? kSlots - 1 : kblock0 - 1) : (kblock0 == kSlots - 1 ? 0 : kblock0 + 1);
@@ -323,8 +346,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_ring_kernel(PrefillArgs a, in
       __builtin_amdgcn_s_waitcnt(kVmcnt0);
       if (qi < N) {
         bf16* out = static_cast<bf16*>(a.out) + ((size_t)qi * Hq + h0) * D;
-        store_row_tr(out, g, o0, __builtin_amdgcn_rcpf(z0));
-        store_row_tr(out + D, g, o1, __builtin_amdgcn_rcpf(z1));
+        store_row_tr(out, g, o0, __builtin_amdgcn_rcpf(z0) * vmul);
+        store_row_tr(out + D, g, o1, __builtin_amdgcn_rcpf(z1) * vmul);
         if (a.lse != nullptr && g == 0) {
           float* l = a.lse + (size_t)qi * Hq + h0;
           l[0] = (m0 + fast_log2(z0)) * kLn2;
@@ -356,7 +379,10 @@ hipError_t launch_swa_window_mfma(const PrefillArgs& a, hipStream_t s) {
   const long slots = 2L * cus;
   const long per = (total + slots - 1) / slots;
   const long grid = (total + per - 1) / per;
-  hipLaunchKernelGGL(swa_ring_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a, (int)per);
+  if (a.kv_fp8)
+    hipLaunchKernelGGL(swa_ring_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, a, (int)per);
+  else
+    hipLaunchKernelGGL(swa_ring_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, a, (int)per);
   return hipGetLastError();
 }
 

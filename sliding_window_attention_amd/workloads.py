@@ -26,7 +26,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "prefill" | "decode" | "decode_fp8" | "decode_rope" | "sparse" | "hybrid" | "varlen"
+    kind: str  # "prefill" | "prefill_fp8" | "decode" | "decode_fp8" | "decode_rope" | "sparse" | "hybrid" | "varlen"
     dtype: str  # "f32" | "bf16"
     seq_len: int = 0  # total packed tokens for prefill kinds
     num_q_heads: int = 32
@@ -46,6 +46,9 @@ WORKLOADS = {
                           num_kv_heads=1, head_dim=64, seed=1000),
     # One SWA layer prefill at 32K tokens, 32 q / 4 kv heads, head_dim 128.
     "swa_prefill_32k": Workload("swa_prefill_32k", "prefill", "bf16", seq_len=32768, seed=2000),
+    # The same layer with K and V as E4M3 codes (per-tensor scales).
+    "swa_prefill_fp8kv_32k": Workload("swa_prefill_fp8kv_32k", "prefill_fp8", "bf16", seq_len=32768,
+                                      seed=2100),
     # Batched ring-buffer decode, one query token per sequence.
     "decode_t1": Workload("decode_t1", "decode", "bf16", batch=256, t_new=1, seed=3000),
     # MTP verify: 1 + 3 draft tokens per sequence, causal among themselves.
@@ -255,6 +258,18 @@ def e4m3_codes(shape, gen, exp_center=10.0, exp_spread=2.0):
     return ((sgn << 7) | (e.to(torch.int64) << 3) | m).to(torch.uint8)
 
 
+def make_prefill_fp8(seq_lens, num_q_heads, num_kv_heads, head_dim, dtype, seed, with_sinks=True):
+    """make_prefill with K and V as E4M3 codes [N, Hkv, D] uint8 and per-tensor scales
+    k_scale = 1/32, v_scale = 1/64 (values of about N(0, 1))."""
+    x = make_prefill(seq_lens, num_q_heads, num_kv_heads, head_dim, dtype, seed, with_sinks)
+    gen = torch.Generator().manual_seed(int(seed) + 17)
+    shape = tuple(x["k"].shape)
+    x["k"] = e4m3_codes(shape, gen)
+    x["v"] = e4m3_codes(shape, gen)
+    x["k_scale"], x["v_scale"] = 1.0 / 32, 1.0 / 64
+    return x
+
+
 def make_decode_fp8(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, dtype, seed):
     """make_decode with the caches as E4M3 codes [B, Hkv, W, D] uint8 and per-tensor
     scales: k_scale = 1/32 and v_scale = 1/64 bring the values to about N(0, 1)."""
@@ -272,6 +287,8 @@ def make_workload(name: str, layer: int = 0):
     w = WORKLOADS[name]
     if w.kind == "prefill":
         return make_prefill([w.seq_len], w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype, w.seed)
+    if w.kind == "prefill_fp8":
+        return make_prefill_fp8([w.seq_len], w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype, w.seed)
     if w.kind == "hybrid":
         return make_prefill([w.seq_len], w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype,
                             w.seed + layer, with_sinks=layer < 5)
@@ -309,9 +326,12 @@ def prefill_flops(lengths, num_q_heads, head_dim, window) -> int:
     return 4 * head_dim * num_q_heads * sum(pairs(n, window) for n in lengths)
 
 
-def prefill_bytes(total_tokens, num_q_heads, num_kv_heads, head_dim, elem_bytes, with_lse=True):
-    """Q, K, V read once, O written once, LSE (fp32) written once."""
-    per_tok = (2 * num_q_heads + 2 * num_kv_heads) * head_dim * elem_bytes
+def prefill_bytes(total_tokens, num_q_heads, num_kv_heads, head_dim, elem_bytes, with_lse=True,
+                  kv_elem_bytes=None):
+    """Q, K, V read once, O written once, LSE (fp32) written once.  kv_elem_bytes: K/V
+    element size when it differs from the rest (1 for E4M3 codes)."""
+    kb = elem_bytes if kv_elem_bytes is None else kv_elem_bytes
+    per_tok = 2 * num_q_heads * head_dim * elem_bytes + 2 * num_kv_heads * head_dim * kb
     if with_lse:
         per_tok += 4 * num_q_heads
     return total_tokens * per_tok
@@ -371,7 +391,8 @@ def workload_work(name: str):
     else:
         lens = [w.seq_len]
     fl = prefill_flops(lens, w.num_q_heads, w.head_dim, w.window)
-    by = prefill_bytes(sum(lens), w.num_q_heads, w.num_kv_heads, w.head_dim, eb)
+    by = prefill_bytes(sum(lens), w.num_q_heads, w.num_kv_heads, w.head_dim, eb,
+                       kv_elem_bytes=1 if w.kind == "prefill_fp8" else None)
     if w.kind == "hybrid":
         ga = prefill_flops(lens, w.num_q_heads, w.head_dim, None)
         return 5 * fl + ga, 6 * by

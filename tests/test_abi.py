@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    assert set(names) == {"swa_sink_prefill", "ga_causal_prefill", "swa_sink_decode",
+    assert set(names) == {"swa_sink_prefill", "ga_causal_prefill", "swa_sink_prefill_fp8kv", "swa_sink_decode",
                           "swa_sink_decode_fp8kv", "swa_sink_prefill_backward",
                           "swa_sink_prefill_backward_workspace", "swa_rope", "swa_sink_decode_rope",
                           "swa_ring_append_rope", "swa_topk_select", "swa_sparse_decode",
@@ -144,6 +144,48 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError, match="GPU tensor"):
         swa.swa_sink_prefill(q, q[:, :1].contiguous(), q[:, :1].contiguous(), torch.zeros(8),
                              torch.tensor([0, 4], dtype=torch.int32))
+
+
+def _prefill_fp8(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=0.5, vs=0.25, sinks=FAKE, cu=FAKE, num_seqs=1, n=16,
+             max_seqlen=16, hq=8, hkv=1, d=128, window=128, scale=0.0, dtype=1, out=FAKE, lse=NULL,
+             stream=NULL)
+    a.update(kw)
+    return swa.library().swa_sink_prefill_fp8kv(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["sinks"],
+                                                a["cu"], a["num_seqs"], a["n"], a["max_seqlen"], a["hq"],
+                                                a["hkv"], a["d"], a["window"], a["scale"], a["dtype"],
+                                                a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(ks=0.0), E_SHAPE, "k_scale"),
+    (dict(vs=-2.0), E_SHAPE, "v_scale"),
+    (dict(ks=float("nan")), E_SHAPE, "finite"),
+    (dict(vs=float("inf")), E_SHAPE, "finite"),
+    (dict(window=0), E_SHAPE, "window"),
+    (dict(k=NULL), E_NULL, "non-NULL"),
+    (dict(cu=NULL), E_NULL, "non-NULL"),
+    (dict(hq=6, hkv=4), E_SHAPE, "multiple"),
+    (dict(d=96), E_UNSUP, "head_dim"),
+    (dict(dtype=5), E_DTYPE, "dtype"),
+])
+def test_prefill_fp8kv_rejects_bad_arguments(kw, code, needle):
+    assert _prefill_fp8(**kw) == code
+    assert needle in _last()
+
+
+def test_prefill_fp8kv_empty_stream_accepts_null_pointers():
+    assert _prefill_fp8(n=0, q=NULL, k=NULL, v=NULL, sinks=NULL, cu=NULL, out=NULL) == OK
+    assert _prefill_fp8(n=0, vs=0.0) == E_SHAPE  # the scales are still checked
+
+
+def test_binding_prefill_fp8_refuses_non_byte_kv():
+    import torch
+
+    q = torch.zeros(4, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, TypeError)):
+        swa.swa_sink_prefill_fp8kv(q, torch.zeros(4, 1, 128), torch.zeros(4, 1, 128), 1.0, 1.0,
+                                   torch.zeros(8), torch.tensor([0, 4], dtype=torch.int32))
 
 
 def _decode_fp8(**kw):

@@ -389,6 +389,56 @@ def test_fp8kv_scales_act_on_the_ring_only():
     np.testing.assert_allclose(k2[1], base[1], rtol=0, atol=1e-12)
 
 
+def _codes(rng, shape, lo=1, hi=13):
+    """Random finite E4M3 codes with exponent fields in [lo, hi] (hand-built, not from the oracle)."""
+    e = rng.integers(lo, hi + 1, shape)
+    m = rng.integers(0, 8, shape)
+    sgn = rng.integers(0, 2, shape)
+    return ((sgn << 7) | (e << 3) | m).astype(np.uint8), sgn, e, m
+
+
+@pytest.mark.parametrize("window,with_sinks", [(3, True), (5, False), (None, True), (None, False)])
+def test_fp8kv_prefill_brute_force(window, with_sinks):
+    """The FP8 prefill on codes equals brute-force enumeration over values decoded by hand
+    from the bit fields ((-1)^s (1 + m/8) 2^(e-7), the E4M3 normal numbers) times the scales."""
+    rng = np.random.default_rng(11)
+    lens, hq, hkv, d = [5, 7], 4, 2, 6
+    n = sum(lens)
+    cu = np.array([0, 5, 12])
+    q = rng.standard_normal((n, hq, d))
+    kc, ks_, ke, km = _codes(rng, (n, hkv, d))
+    vc, vs_, ve, vm = _codes(rng, (n, hkv, d))
+    k_scale, v_scale = 0.375, 1.5
+    kv = np.where(ks_ == 1, -1.0, 1.0) * (1 + km / 8.0) * 2.0 ** (ke - 7) * k_scale
+    vv = np.where(vs_ == 1, -1.0, 1.0) * (1 + vm / 8.0) * 2.0 ** (ve - 7) * v_scale
+    sinks = rng.standard_normal(hq) if with_sinks else None
+    o, lse = orc.swa_sink_prefill_fp8kv(q, kc, vc, k_scale, v_scale, sinks, cu, window=window, block=4)
+    ob, lb = brute.attention(q.tolist(), kv.tolist(), vv.tolist(),
+                             None if sinks is None else sinks.tolist(), cu.tolist(), window)
+    np.testing.assert_allclose(o, np.array(ob), atol=1e-12, rtol=1e-12)
+    np.testing.assert_allclose(lse, np.array(lb), atol=1e-12, rtol=1e-12)
+
+
+def test_fp8kv_prefill_scales_are_exponent_shifts():
+    """Doubling v_scale equals raising every V code's exponent by one; k_scale = 2 with every K
+    exponent lowered by one leaves the result unchanged (K and V scales are not swapped)."""
+    rng = np.random.default_rng(12)
+    n, hq, hkv, d = 9, 4, 1, 8
+    cu = np.array([0, 9])
+    q = rng.standard_normal((n, hq, d))
+    codes, sgn, e, m = _codes(rng, (n, hkv, d), 2, 12)
+    lower = ((sgn << 7) | ((e - 1) << 3) | m).astype(np.uint8)
+    higher = ((sgn << 7) | ((e + 1) << 3) | m).astype(np.uint8)
+    sinks = rng.standard_normal(hq)
+    base = orc.swa_sink_prefill_fp8kv(q, codes, codes, 1.0, 1.0, sinks, cu, window=4)
+    v2 = orc.swa_sink_prefill_fp8kv(q, codes, codes, 1.0, 2.0, sinks, cu, window=4)
+    vh = orc.swa_sink_prefill_fp8kv(q, codes, higher, 1.0, 1.0, sinks, cu, window=4)
+    k2 = orc.swa_sink_prefill_fp8kv(q, lower, codes, 2.0, 1.0, sinks, cu, window=4)
+    np.testing.assert_allclose(v2[0], vh[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(k2[0], base[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(k2[1], base[1], rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # backward (gradients of O)
 # ---------------------------------------------------------------------------

@@ -562,6 +562,78 @@ def test_decode_fp8_max_batch_sampled():
 
 
 # ---------------------------------------------------------------------------
+# prefill with FP8 (E4M3) K and V
+# ---------------------------------------------------------------------------
+
+def _run_prefill_fp8(x, window, k_scale=None, v_scale=None):
+    g = _gpu(x)
+    o, lse = swa.swa_sink_prefill_fp8kv(
+        g["q"], g["k"], g["v"], x["k_scale"] if k_scale is None else k_scale,
+        x["v_scale"] if v_scale is None else v_scale, g["sinks"], g["cu_seqlens"], x["max_seqlen"],
+        window=window)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _oracle_prefill_fp8(x, window):
+    return orc.swa_sink_prefill_fp8kv(x["q"], x["k"].numpy(), x["v"].numpy(), x["k_scale"], x["v_scale"],
+                                      x["sinks"], x["cu_seqlens"].numpy(), window=window)
+
+
+PREFILL_FP8_CASES = [
+    # (lengths, Hq, Hkv, D, dtype, window (None: unbounded), sinks)
+    ([700], 32, 4, 128, "bf16", 128, True),                 # window kernel, ragged tail
+    ([130, 1, 17, 300, 5], 16, 2, 128, "bf16", 100, True),  # boundaries inside tiles, G = 8
+    ([7], 32, 4, 128, "bf16", 128, True),                   # fewer tokens than one tile
+    ([520, 45], 32, 4, 128, "bf16", 200, True),             # online kernel, window + sink
+    ([600, 33], 16, 2, 128, "bf16", None, False),           # GA kernel
+    ([300, 77], 8, 2, 128, "bf16", 128, True),              # generic kernel (G = 4)
+    ([250], 8, 1, 64, "bf16", None, False),                 # generic kernel, D = 64, GA
+    ([200, 3], 4, 2, 128, "f32", 50, True),                 # generic fp32
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_FP8_CASES,
+                         ids=lambda c: f"{c[0]}-{c[1]}/{c[2]}-D{c[3]}-{c[4]}-W{c[5]}-{'sink' if c[6] else 'nosink'}")
+def test_prefill_fp8kv_small(case):
+    lens, hq, hkv, d, dt, window, with_sinks = case
+    _say(f"FP8 K/V prefill lens={lens} heads={hq}/{hkv} D={d} {dt} W={window} sinks={with_sinks}")
+    x = wl.make_prefill_fp8(lens, hq, hkv, d, dt, seed=2300 + sum(lens) + hq, with_sinks=with_sinks)
+    o, lse = _run_prefill_fp8(x, window)
+    o_ref, l_ref = _oracle_prefill_fp8(x, window)
+    assert_close(x["q"].dtype, o, o_ref, lse, l_ref, f"fp8 prefill {case}")
+
+
+@pytest.mark.parametrize("window", [128, 100, None])
+def test_prefill_fp8kv_unit_scales_equal_bf16_prefill(window):
+    """Every E4M3 value is a bf16 value and the kernels widen codes exactly, so with unit scales
+    the FP8 prefill is bitwise the bf16 prefill on the decoded K/V (decoded by torch's
+    float8_e4m3fn): window kernel, and with no window and no sink the GA kernel."""
+    _say(f"FP8 K/V prefill, unit scales, against the bf16 prefill (W={window})")
+    lens = [900, 140, 3]
+    x = wl.make_prefill_fp8(lens, 32, 4, 128, "bf16", seed=2400, with_sinks=window is not None)
+    o8, l8 = _run_prefill_fp8(x, window, 1.0, 1.0)
+    g = _gpu(x)
+    kd = g["k"].view(torch.float8_e4m3fn).to(torch.bfloat16)
+    vd = g["v"].view(torch.float8_e4m3fn).to(torch.bfloat16)
+    if window is None:
+        ob, lb = swa.ga_causal_prefill(g["q"], kd, vd, g["cu_seqlens"], x["max_seqlen"])
+    else:
+        ob, lb = swa.swa_sink_prefill(g["q"], kd, vd, g["sinks"], g["cu_seqlens"], x["max_seqlen"],
+                                      window=window)
+    torch.cuda.synchronize()
+    assert torch.equal(o8, ob) and torch.equal(l8, lb)
+
+
+def test_prefill_fp8kv_32k_full():
+    _say("swa_prefill_fp8kv_32k: 32768 tokens, 32/4, D128, W128, E4M3 K/V, every element")
+    x = wl.make_workload("swa_prefill_fp8kv_32k")
+    o, lse = _run_prefill_fp8(x, 128)
+    o_ref, l_ref = _oracle_prefill_fp8(x, 128)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, "swa_prefill_fp8kv_32k")
+
+
+# ---------------------------------------------------------------------------
 # backward (gradients of O)
 # ---------------------------------------------------------------------------
 
