@@ -22,7 +22,8 @@ the prose of that section and of the MiMo-V2 blog, section 2.2):
   GQA: query head h reads KV head h // (Hq // Hkv).
 
 Decode against an FP8 ring (swa_sink_decode_fp8kv) is the same decode on caches
-dequantised exactly (E4M3 code value times a per-tensor scale).
+dequantised exactly (E4M3 code value times a per-tensor scale); the prefill with FP8
+K/V (swa_sink_prefill_fp8kv) is likewise the prefill on dequantised K and V.
 
 RoPE around decode (swa_rope, swa_sink_decode_rope, swa_ring_append_rope): the
 rotary position embedding with a per-layer base (10,000 in SWA layers, 640,000 in
