@@ -220,6 +220,38 @@ def _decode_rope_fn():
     return fn
 
 
+def _decode_rope_fp8_fn():
+    """Timed call of swa_sink_decode_rope_fp8kv (SWA base 10,000), arguments marshalled once
+    per input set."""
+    import ctypes
+
+    import torch
+
+    import sliding_window_attention_amd as swa
+
+    lib = swa.library()
+    cache = {}
+
+    def fn(x):
+        key = id(x)
+        if key not in cache:
+            swa.swa_sink_decode_rope_fp8kv(x["q"], x["k_new"], x["v_new"], x["k_cache"], x["v_cache"],
+                                           x["k_scale"], x["v_scale"], x["ring_head"], x["positions"],
+                                           x["sinks"], swa.ROPE_BASE_SWA, out=x["out"], lse=x["lse"])
+            b, t, hq, d = x["q"].shape
+            hkv, w = x["k_cache"].shape[1], x["k_cache"].shape[2]
+            cache[key] = (x["q"].data_ptr(), x["k_new"].data_ptr(), x["v_new"].data_ptr(),
+                          x["k_cache"].data_ptr(), x["v_cache"].data_ptr(), float(x["k_scale"]),
+                          float(x["v_scale"]), x["ring_head"].data_ptr(), x["positions"].data_ptr(),
+                          x["sinks"].data_ptr(), b, t, hq, hkv, d, w, 0.0, swa.ROPE_BASE_SWA, 1,
+                          x["out"].data_ptr(), x["lse"].data_ptr(),
+                          ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        rc = lib.swa_sink_decode_rope_fp8kv(*cache[key])
+        if rc != 0:
+            raise RuntimeError(lib.swa_last_error().decode())
+    return fn
+
+
 def _rope_inputs(dev):
     """The 32K layer's Q (seeded like the prefill workload) and positions 0..32767."""
     import torch
@@ -302,23 +334,25 @@ def _sparse_work(x):
             wl.sparse_flops(lens, w.num_q_heads, w.head_dim, w.extra["topk"], w.extra["recent"]))
 
 
-def _append_inputs(dev):
-    """Ring append after an MTP verify of the T = 4 decode workload: seeded accept counts
-    ~ U{0..4} per sequence (keys rotated at base 10,000)."""
+def _append_inputs(dev, fp8=False):
+    """Ring append after an MTP verify of the T = 4 decode workload (bf16 ring, or the FP8
+    ring of the same shape): seeded accept counts ~ U{0..4} per sequence (keys rotated at
+    base 10,000)."""
     import torch
 
     from sliding_window_attention_amd import workloads as wl
 
-    x = _to(wl.make_workload("decode_rope_t4"), dev)
+    x = _to(wl.make_workload("decode_rope_fp8_t4" if fp8 else "decode_rope_t4"), dev)
     gen = torch.Generator().manual_seed(3501)
     x["n_accept"] = torch.randint(0, 5, (x["q"].shape[0],), generator=gen,
                                   dtype=torch.int64).to(torch.int32).to(dev)
     return x
 
 
-def _append_fn():
-    """Timed call of swa_ring_append_rope; each call commits the same accept counts again
-    (the ring keeps rolling: the same work every call)."""
+def _append_fn(fp8=False):
+    """Timed call of swa_ring_append_rope (or swa_ring_append_fp8kv into an FP8 ring); each
+    call commits the same accept counts again (the ring keeps rolling: the same work every
+    call)."""
     import ctypes
 
     import torch
@@ -332,11 +366,18 @@ def _append_fn():
         key = id(x)
         if key not in cache:
             b, t, hkv, d = x["k_new"].shape
-            cache[key] = (x["k_new"].data_ptr(), x["v_new"].data_ptr(), x["n_accept"].data_ptr(),
-                          x["positions"].data_ptr(), x["k_cache"].data_ptr(), x["v_cache"].data_ptr(),
-                          x["ring_head"].data_ptr(), b, t, hkv, d, x["k_cache"].shape[2],
-                          swa.ROPE_BASE_SWA, 1, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-        rc = lib.swa_ring_append_rope(*cache[key])
+            st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            if fp8:
+                cache[key] = (x["k_new"].data_ptr(), x["v_new"].data_ptr(), x["n_accept"].data_ptr(),
+                              x["positions"].data_ptr(), x["k_cache"].data_ptr(), x["v_cache"].data_ptr(),
+                              float(x["k_scale"]), float(x["v_scale"]), x["ring_head"].data_ptr(), b, t, hkv,
+                              d, x["k_cache"].shape[2], swa.ROPE_BASE_SWA, 1, st)
+            else:
+                cache[key] = (x["k_new"].data_ptr(), x["v_new"].data_ptr(), x["n_accept"].data_ptr(),
+                              x["positions"].data_ptr(), x["k_cache"].data_ptr(), x["v_cache"].data_ptr(),
+                              x["ring_head"].data_ptr(), b, t, hkv, d, x["k_cache"].shape[2],
+                              swa.ROPE_BASE_SWA, 1, st)
+        rc = (lib.swa_ring_append_fp8kv if fp8 else lib.swa_ring_append_rope)(*cache[key])
         if rc != 0:
             raise RuntimeError(lib.swa_last_error().decode())
     return fn
@@ -517,7 +558,8 @@ def main(argv=None):
     ap.add_argument("--no-extra", action="store_true", help="time only the primary workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", choices=["prefill", "prefill_fp8", "decode", "decode1", "decode_fp8", "decode_fp8_1",
-                                       "decode_rope", "decode_rope_1", "append", "mtp_step", "rope",
+                                       "decode_rope", "decode_rope_1", "decode_rope_fp8", "append",
+                                       "append_fp8", "mtp_step", "mtp_step_fp8", "rope",
                                        "topk", "sparse",
                                        "ga", "varlen", "backward", "copy"],
                     default=None,
@@ -557,22 +599,23 @@ def main(argv=None):
         _log(f"backward 32K: {st}  {fl / (st['mean_ms'] * 1e-3) / 1e12:.1f} TFLOP/s  "
              f"{by / (st['mean_ms'] * 1e-3) / 1e9:.0f} GB/s")
         return 0
-    if args.only in ("append", "mtp_step"):
+    if args.only in ("append", "mtp_step", "append_fp8", "mtp_step_fp8"):
         # append alone is launch-bound from this loop (a ~4 us kernel); in a decode loop it
         # is queued behind the verify kernel, which "mtp_step" times
-        x = _with_outputs(_append_inputs(dev), "decode")
-        app_fn = _append_fn()
-        if args.only == "append":
+        fp8 = args.only.endswith("fp8")
+        x = _with_outputs(_append_inputs(dev, fp8), "decode")
+        app_fn = _append_fn(fp8)
+        if args.only.startswith("append"):
             fn = app_fn
         else:
-            dec_fn = _decode_rope_fn()
+            dec_fn = _decode_rope_fp8_fn() if fp8 else _decode_rope_fn()
 
             def fn(x_):
                 dec_fn(x_)
                 app_fn(x_)
         per, _ = _time_calls(fn, [x], max(steps, 200), warmup, per_call=False)
         st = _stats(per)
-        by = wl.append_bytes(256, int(x["n_accept"].sum()), 4, 128, 2)
+        by = wl.append_bytes(256, int(x["n_accept"].sum()), 4, 128, 2, cache_elem_bytes=1 if fp8 else None)
         _log(f"{args.only} B=256 T=4: {st}  (append bytes {by})")
         return 0
     if args.only in ("topk", "sparse"):
@@ -597,12 +640,15 @@ def main(argv=None):
                 "decode1": "decode_t1",
                 "decode_fp8": "decode_fp8_t4", "decode_fp8_1": "decode_fp8_t1",
                 "decode_rope": "decode_rope_t4", "decode_rope_1": "decode_rope_t1",
+                "decode_rope_fp8": "decode_rope_fp8_t4",
                 "ga": "hybrid_5to1_32k", "varlen": "varlen_262k"}[args.only]
         layer = 5 if args.only == "ga" else 0
         dec = args.only.startswith("decode")
         x = _with_outputs(_to(wl.make_workload(name, layer), dev), "decode" if dec else "p")
         if args.only.startswith("decode_fp8"):
             fn = _decode_fp8_fn()
+        elif args.only == "decode_rope_fp8":
+            fn = _decode_rope_fp8_fn()
         elif args.only == "prefill_fp8":
             fn = _prefill_fp8_fn(128)
         elif args.only.startswith("decode_rope"):
@@ -704,11 +750,12 @@ def run_extra(dev, steps, warmup):
     torch.cuda.empty_cache()
 
     for name in ("decode_t1", "decode_t4", "decode_fp8_t1", "decode_fp8_t4", "decode_rope_t1",
-                 "decode_rope_t4"):
+                 "decode_rope_t4", "decode_rope_fp8_t4"):
         _log(f"{name}")
         x = _with_outputs(_to(wl.make_workload(name), dev), "decode")
         sets = _clone_sets(x, 32)  # 32 x 38-86 MB: more than the Infinity Cache
-        fn = _decode_fp8_fn() if "fp8" in name else (_decode_rope_fn() if "rope" in name else _decode_fn())
+        fn = {"decode_fp8": _decode_fp8_fn, "decode_rope": _decode_rope_fn,
+              "decode_rope_fp8": _decode_rope_fp8_fn}.get(wl.WORKLOADS[name].kind, _decode_fn)()
         per, _ = _time_calls(fn, sets, max(200, steps), warmup, per_call=False)
         fl, by = wl.workload_work(name)
         st = _stats(per)
@@ -718,21 +765,27 @@ def run_extra(dev, steps, warmup):
         del sets, x
         torch.cuda.empty_cache()
 
-    _log("MTP step: verify T = 4 with RoPE, then commit the accepted tokens (B = 256)")
-    x = _with_outputs(_append_inputs(dev), "decode")
-    dec_fn, app_fn = _decode_rope_fn(), _append_fn()
+    for fp8 in (False, True):
+        ring = "an FP8" if fp8 else "a bf16"
+        _log(f"MTP step: verify T = 4 with RoPE against {ring} ring, then commit the accepted tokens (B = 256)")
+        x = _with_outputs(_append_inputs(dev, fp8), "decode")
+        dec_fn = _decode_rope_fp8_fn() if fp8 else _decode_rope_fn()
+        app_fn = _append_fn(fp8)
 
-    def step(x_):
-        dec_fn(x_)
-        app_fn(x_)
-    per, _ = _time_calls(step, [x], max(200, steps), warmup, per_call=False)
-    st = _stats(per)
-    fl, by_dec = wl.workload_work("decode_rope_t4")
-    by = by_dec + wl.append_bytes(256, int(x["n_accept"].sum()), 4, 128, 2)
-    extra["mtp_step_rope_t4"] = {**st, "gbps": by / (st["mean_ms"] * 1e-3) / 1e9, "bytes": by,
-                                 "accepted_tokens": int(x["n_accept"].sum()),
-                                 "what": "swa_sink_decode_rope (T=4) + swa_ring_append_rope per step"}
-    del x
+        def step(x_):
+            dec_fn(x_)
+            app_fn(x_)
+        per, _ = _time_calls(step, [x], max(200, steps), warmup, per_call=False)
+        st = _stats(per)
+        fl, by_dec = wl.workload_work("decode_rope_fp8_t4" if fp8 else "decode_rope_t4")
+        by = by_dec + wl.append_bytes(256, int(x["n_accept"].sum()), 4, 128, 2,
+                                      cache_elem_bytes=1 if fp8 else None)
+        what = ("swa_sink_decode_rope_fp8kv (T=4) + swa_ring_append_fp8kv per step" if fp8
+                else "swa_sink_decode_rope (T=4) + swa_ring_append_rope per step")
+        extra["mtp_step_rope_fp8_t4" if fp8 else "mtp_step_rope_t4"] = {
+            **st, "gbps": by / (st["mean_ms"] * 1e-3) / 1e9, "bytes": by,
+            "accepted_tokens": int(x["n_accept"].sum()), "what": what}
+        del x
     _log("sparse attention: top-k selection and sparse decode, 64 sequences of 16K-32K tokens")
     x = _sparse_inputs(dev)
     tb, sb, sfl = _sparse_work(x)

@@ -57,7 +57,7 @@ typedef enum {
 
 typedef enum { SWA_DTYPE_F32 = 0, SWA_DTYPE_BF16 = 1 } swa_dtype;
 
-#define SWASINK_ABI_VERSION 6
+#define SWASINK_ABI_VERSION 7
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SWASINK_API __attribute__((visibility("default")))
@@ -237,6 +237,23 @@ SWASINK_API int swa_sink_decode_rope(const void* q, const void* k_new, const voi
                     void* stream);
 
 /*
+ * swa_sink_decode_rope against an FP8 ring: q and k_new arrive unrotated and are
+ * rotated in the kernel as in swa_sink_decode_rope; the caches hold E4M3 codes with
+ * per-tensor scales as in swa_sink_decode_fp8kv (keys rotated at their own positions
+ * before they were encoded: swa_ring_append_fp8kv writes them so).
+ *
+ *  k_cache, v_cache [batch, num_kv_heads, window, head_dim] uint8 E4M3 codes, read only
+ *  k_scale, v_scale host fp32, finite and > 0 (SWA_ERR_SHAPE otherwise)
+ *  positions, rope_base as for swa_sink_decode_rope (rope_base 0: swa_sink_decode_fp8kv)
+ */
+SWASINK_API int swa_sink_decode_rope_fp8kv(const void* q, const void* k_new, const void* v_new,
+                    const uint8_t* k_cache, const uint8_t* v_cache, float k_scale, float v_scale,
+                    const int32_t* ring_head, const int32_t* positions, const float* sinks,
+                    int32_t batch, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t window, float scale, float rope_base,
+                    swa_dtype dtype, void* out, float* lse, void* stream);
+
+/*
  * Commit the accepted tokens of a decode / MTP-verify step to the ring (the drafts the
  * verification rejected never enter it).  For each sequence b, with n = n_accept[b]
  * clamped to [0, T] and h = ring_head[b] reduced modulo window: accepted token t < n
@@ -259,6 +276,27 @@ SWASINK_API int swa_ring_append_rope(const void* k_new, const void* v_new, const
                     const int32_t* positions, void* k_cache, void* v_cache, int32_t* ring_head,
                     int32_t batch, int32_t T, int32_t num_kv_heads, int32_t head_dim,
                     int32_t window, float rope_base, swa_dtype dtype, void* stream);
+
+/*
+ * swa_ring_append_rope into an FP8 ring (the E4M3 caches swa_sink_decode_fp8kv
+ * reads): the same slots, head update, clamping and rotation, but each committed
+ * element x -- the rotated key rounded to dtype, or the value as given -- is stored as
+ * the E4M3 code of x / k_scale (keys) or x / v_scale (values): the exact quotient
+ * rounded once to the nearest E4M3 value, ties to the even mantissa, finite
+ * magnitudes beyond 448 saturating to 448 (codes 0x7E / 0xFE), zero keeping its sign,
+ * and an x that is not finite stored as the NaN code of its sign (0x7F / 0xFF).
+ * Rotating a non-finite key gives an unspecified code.
+ *
+ *  k_cache, v_cache [batch, num_kv_heads, window, head_dim] uint8 E4M3 codes, updated
+ *                   in place
+ *  k_scale, v_scale host fp32, finite and > 0 (SWA_ERR_SHAPE otherwise)
+ * Everything else is as for swa_ring_append_rope.
+ */
+SWASINK_API int swa_ring_append_fp8kv(const void* k_new, const void* v_new, const int32_t* n_accept,
+                    const int32_t* positions, uint8_t* k_cache, uint8_t* v_cache, float k_scale,
+                    float v_scale, int32_t* ring_head, int32_t batch, int32_t T,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t window, float rope_base,
+                    swa_dtype dtype, void* stream);
 
 /*
  * Token selection for sparse attention with a forced recent window (the HySparse2

@@ -23,7 +23,12 @@ the prose of that section and of the MiMo-V2 blog, section 2.2):
 
 Decode against an FP8 ring (swa_sink_decode_fp8kv) is the same decode on caches
 dequantised exactly (E4M3 code value times a per-tensor scale); the prefill with FP8
-K/V (swa_sink_prefill_fp8kv) is likewise the prefill on dequantised K and V.
+K/V (swa_sink_prefill_fp8kv) is likewise the prefill on dequantised K and V, and
+the decode with RoPE against an FP8 ring (swa_sink_decode_rope_fp8kv) the decode with
+RoPE on dequantised caches.  The append into an FP8 ring (swa_ring_append_fp8kv) stores E4M3 codes of element / scale,
+rounded once to the nearest E4M3 value with ties to the even mantissa, saturating at
+448 (e4m3_encode: the pages name the format, not the rounding, so this is the
+plainest reading of a rounding conversion).
 
 RoPE around decode (swa_rope, swa_sink_decode_rope, swa_ring_append_rope): the
 rotary position embedding with a per-layer base (10,000 in SWA layers, 640,000 in
@@ -310,6 +315,40 @@ def e4m3_to_float(codes) -> np.ndarray:
     return np.where((e == 15) & (m == 7), np.nan, sign * mag)
 
 
+def e4m3_encode(x, scale=1.0) -> np.ndarray:
+    """E4M3 codes (uint8) of x / scale, with scale an fp32 value.
+
+    Rounding follows the usual reading of a rounding conversion: the exact quotient
+    goes to the nearest E4M3 value; on a tie, to the neighbour whose code has mantissa
+    LSB 0 (round half to even).  Finite magnitudes beyond the largest finite value 448
+    saturate to it, the sign of zero is kept, and an x that is not finite becomes the
+    NaN code S.1111.111 with x's sign.  The quotient is formed in fp64: x here has at
+    most 24 significant bits and so has the scale, so a quotient that is not exactly
+    halfway between two E4M3 values differs from every such point by far more than
+    fp64's rounding, and the nearest value found from the fp64 quotient is the one of
+    the exact quotient.  The nearest value is looked up in the table of all E4M3
+    values (e4m3_to_float of codes 0..126).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    s = float(np.float32(scale))
+    if not (np.isfinite(s) and s > 0):
+        raise ValueError("scale must be finite and > 0")
+    table = e4m3_to_float(np.arange(127))           # 0, 2^-9, ..., 448, increasing
+    sign = np.signbit(x)
+    with np.errstate(invalid="ignore", over="ignore"):
+        a = np.abs(x) / s
+    finite = np.isfinite(a)
+    a = np.where(finite, np.minimum(a, table[-1]), 0.0)
+    hi = np.clip(np.searchsorted(table, a, side="left"), 1, 126)    # table[hi-1] < a <= table[hi]
+    lo = hi - 1
+    d_lo, d_hi = a - table[lo], table[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == 0.0, 0, code)
+    code = np.where(finite, code, 0x7F)
+    return (code | np.where(sign, 0x80, 0)).astype(np.uint8)
+
+
 def swa_sink_decode_fp8kv(q, k_new, v_new, k_codes, v_codes, k_scale, v_scale, ring_head, sinks,
                           window=128, scale=None):
     """Decode / MTP verify against a ring whose K and V are stored as E4M3 codes.
@@ -406,6 +445,17 @@ def swa_sink_decode_rope(q, k_new, v_new, k_cache, v_cache, ring_head, positions
                            ring_head, sinks, window=window, scale=scale)
 
 
+def swa_sink_decode_rope_fp8kv(q, k_new, v_new, k_codes, v_codes, k_scale, v_scale, ring_head, positions,
+                               sinks, rope_base, window=128, scale=None, io_dtype="bf16"):
+    """swa_sink_decode_rope against an FP8 ring: the caches dequantised exactly (E4M3
+    code value times the per-tensor scale), then the decode with q and the new keys
+    rotated at their positions and rounded to io_dtype."""
+    kc = e4m3_to_float(k_codes) * float(k_scale)
+    vc = e4m3_to_float(v_codes) * float(v_scale)
+    return swa_sink_decode_rope(q, k_new, v_new, kc, vc, ring_head, positions, sinks, rope_base,
+                                window=window, scale=scale, io_dtype=io_dtype)
+
+
 def swa_ring_append_rope(k_new, v_new, n_accept, positions, k_cache, v_cache, ring_head, rope_base,
                          io_dtype="bf16"):
     """Commit the first n_accept[b] of the T new tokens of each sequence to its ring
@@ -437,6 +487,42 @@ def swa_ring_append_rope(k_new, v_new, n_accept, positions, k_cache, v_cache, ri
             slot = (heads[b] + t) % w
             kc[b, :, slot, :] = kr[t]
             vc[b, :, slot, :] = v_new[b, t]
+        new_heads[b] = (heads[b] + n) % w
+    return kc, vc, new_heads
+
+
+def swa_ring_append_fp8kv(k_new, v_new, n_accept, positions, k_codes, v_codes, ring_head, rope_base,
+                          k_scale, v_scale, io_dtype="bf16"):
+    """swa_ring_append_rope into an FP8 ring: each committed element -- the key rotated
+    at its position and rounded to io_dtype, or the value as given -- enters the ring as
+    its E4M3 code of element / k_scale (keys) or element / v_scale (values)
+    (e4m3_encode).  k_codes / v_codes [B, Hkv, W, D] uint8; returns (k_codes, v_codes,
+    ring_head) as new arrays."""
+    k_new, v_new = _as_f64(k_new), _as_f64(v_new)
+    kc = np.asarray(k_codes, dtype=np.uint8).copy()
+    vc = np.asarray(v_codes, dtype=np.uint8).copy()
+    bsz, t_new = k_new.shape[:2]
+    w = kc.shape[2]
+    heads = np.asarray(ring_head, dtype=np.int64).reshape(bsz) % w
+    n_acc = np.asarray(n_accept, dtype=np.int64).reshape(bsz)
+    pos = None if rope_base is None else np.asarray(positions, dtype=np.int64).reshape(bsz)
+    new_heads = heads.copy()
+    for b in range(bsz):
+        n = int(n_acc[b])
+        if n < 0 or n > t_new:
+            raise ValueError("n_accept out of range")
+        if n == 0:
+            continue
+        if rope_base is None:
+            kr = k_new[b, :n]
+        else:
+            kr = round_to(rope(k_new[b, :n], pos[b] + np.arange(n), rope_base), io_dtype)
+        kq = e4m3_encode(kr, k_scale)
+        vq = e4m3_encode(v_new[b, :n], v_scale)
+        for t in range(n):
+            slot = (heads[b] + t) % w
+            kc[b, :, slot, :] = kq[t]
+            vc[b, :, slot, :] = vq[t]
         new_heads[b] = (heads[b] + n) % w
     return kc, vc, new_heads
 

@@ -45,7 +45,10 @@ _SIGNATURES = {
     "swa_rope": [_P, _P, _I, _I, _I, _F, _I, _P],
     "swa_sink_decode_rope": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I,
                              _P, _P, _P],
+    "swa_sink_decode_rope_fp8kv": [_P, _P, _P, _P, _P, _F, _F, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F,
+                                   _F, _I, _P, _P, _P],
     "swa_ring_append_rope": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P],
+    "swa_ring_append_fp8kv": [_P, _P, _P, _P, _P, _P, _F, _F, _P, _I, _I, _I, _I, _I, _F, _I, _P],
     "swa_topk_select": [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P],
     "swa_sparse_decode": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P],
 }
@@ -352,14 +355,50 @@ def swa_sink_decode_rope(q, k_new, v_new, k_cache, v_cache, ring_head, positions
     return out, lse
 
 
-def swa_ring_append_rope(k_new, v_new, n_accept, positions, k_cache, v_cache, ring_head,
-                         rope_base=ROPE_BASE_SWA):
-    """Commit the first n_accept[b] new tokens of each sequence to its ring, keys rotated
-    at positions[b] + t; k_cache, v_cache and ring_head are updated in place."""
+def swa_sink_decode_rope_fp8kv(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, ring_head, positions,
+                               sinks, rope_base=ROPE_BASE_SWA, scale=None, return_lse=True, out=None,
+                               lse=None):
+    """swa_sink_decode_rope against an FP8 ring: q and k_new unrotated (rotated in the
+    kernel at positions[b] + t); k_cache/v_cache [B, Hkv, W, D] uint8 E4M3 codes with
+    per-tensor scales, keys rotated at their own positions before encoding."""
     import torch
 
-    for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
-        _dev(t, nm, k_new.dtype)
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+        _dev(t, nm, q.dtype)
+    _dev(k_cache, "k_cache", torch.uint8)
+    _dev(v_cache, "v_cache", torch.uint8)
+    _dev(ring_head, "ring_head", torch.int32)
+    _dev(positions, "positions", torch.int32)
+    _dev(sinks, "sinks", torch.float32)
+    if q.dim() != 4 or k_new.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q, k_new must be [B, T, H, D] and caches [B, Hkv, W, D]")
+    b, t, hq, d = q.shape
+    hkv, w = k_cache.shape[1], k_cache.shape[2]
+    if (k_new.shape != (b, t, hkv, d) or v_new.shape != k_new.shape or v_cache.shape != k_cache.shape
+            or k_cache.shape[0] != b or k_cache.shape[3] != d or ring_head.numel() != b
+            or positions.numel() != b or sinks.numel() != hq):
+        raise ValueError("inconsistent shapes")
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    if return_lse and lse is None:
+        lse = torch.empty((b, t, hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+    rc = library().swa_sink_decode_rope_fp8kv(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        float(k_scale), float(v_scale), ring_head.data_ptr(), positions.data_ptr(), sinks.data_ptr(),
+        b, t, hq, hkv, d, w, _scale(scale), float(rope_base), _dtype_code(q), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def _append_shapes(k_new, v_new, n_accept, positions, k_cache, v_cache, ring_head, cache_dtype):
+    import torch
+
+    _dev(k_new, "k_new")
+    _dev(v_new, "v_new", k_new.dtype)
+    _dev(k_cache, "k_cache", cache_dtype)
+    _dev(v_cache, "v_cache", cache_dtype)
     _dev(n_accept, "n_accept", torch.int32)
     _dev(ring_head, "ring_head", torch.int32)
     if positions is not None:
@@ -372,11 +411,36 @@ def swa_ring_append_rope(k_new, v_new, n_accept, positions, k_cache, v_cache, ri
             or k_cache.shape[1] != hkv or k_cache.shape[3] != d or n_accept.numel() != b
             or ring_head.numel() != b or (positions is not None and positions.numel() != b)):
         raise ValueError("inconsistent shapes")
+    return b, t, hkv, d, w
+
+
+def swa_ring_append_rope(k_new, v_new, n_accept, positions, k_cache, v_cache, ring_head,
+                         rope_base=ROPE_BASE_SWA):
+    """Commit the first n_accept[b] new tokens of each sequence to its ring, keys rotated
+    at positions[b] + t; k_cache, v_cache and ring_head are updated in place."""
+    b, t, hkv, d, w = _append_shapes(k_new, v_new, n_accept, positions, k_cache, v_cache, ring_head,
+                                     k_new.dtype)
     rc = library().swa_ring_append_rope(
         k_new.data_ptr(), v_new.data_ptr(), n_accept.data_ptr(),
         positions.data_ptr() if positions is not None else None, k_cache.data_ptr(),
         v_cache.data_ptr(), ring_head.data_ptr(), b, t, hkv, d, w, float(rope_base),
         _dtype_code(k_new), _stream(k_new.device))
+    _check(rc)
+
+
+def swa_ring_append_fp8kv(k_new, v_new, n_accept, positions, k_cache, v_cache, k_scale, v_scale,
+                          ring_head, rope_base=ROPE_BASE_SWA):
+    """swa_ring_append_rope into an FP8 ring: k_cache/v_cache [B, Hkv, W, D] uint8 receive
+    the E4M3 codes of (rotated) key / k_scale and value / v_scale; updated in place."""
+    import torch
+
+    b, t, hkv, d, w = _append_shapes(k_new, v_new, n_accept, positions, k_cache, v_cache, ring_head,
+                                     torch.uint8)
+    rc = library().swa_ring_append_fp8kv(
+        k_new.data_ptr(), v_new.data_ptr(), n_accept.data_ptr(),
+        positions.data_ptr() if positions is not None else None, k_cache.data_ptr(),
+        v_cache.data_ptr(), float(k_scale), float(v_scale), ring_head.data_ptr(), b, t, hkv, d, w,
+        float(rope_base), _dtype_code(k_new), _stream(k_new.device))
     _check(rc)
 
 

@@ -181,6 +181,41 @@ int64_t backward_workspace_bytes(int32_t total_tokens, int32_t num_q_heads) {
   return ((2 * rows * (int64_t)sizeof(float)) + 255) / 256 * 256;  // delta and sink terms
 }
 
+int ring_append_common(const void* k_new, const void* v_new, const int32_t* n_accept,
+                       const int32_t* positions, void* k_cache, void* v_cache, int32_t* ring_head,
+                       int32_t batch, int32_t T, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t window, float rope_base, swa_dtype dtype, void* stream, const char* name,
+                       bool fp8 = false, float k_scale = 1.f, float v_scale = 1.f) {
+  int rc = check_dtype((int)dtype);
+  if (rc) return rc;
+  if ((rc = check_rope_base(rope_base, name))) return rc;
+  if (fp8 && !(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f))
+    return fail(SWA_ERR_SHAPE, "%s: k_scale and v_scale must be finite and > 0", name);
+  if (batch < 0) return fail(SWA_ERR_SHAPE, "%s: batch must be >= 0", name);
+  if (num_kv_heads < 1) return fail(SWA_ERR_SHAPE, "%s: num_kv_heads must be >= 1", name);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SWA_ERR_SHAPE, "%s: head_dim must be 64 or 128 (got %d)", name, head_dim);
+  if (window < 2) return fail(SWA_ERR_SHAPE, "%s: window must be >= 2 (got %d)", name, window);
+  if (T < 1 || T >= window)
+    return fail(SWA_ERR_SHAPE, "%s: T must satisfy 1 <= T < window (got T=%d, window=%d)", name, T, window);
+  if ((long long)batch * num_kv_heads * window * head_dim > (1LL << 40))
+    return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
+  if (batch == 0) return ok();
+  if (!k_new || !v_new || !n_accept || !k_cache || !v_cache || !ring_head)
+    return fail(SWA_ERR_NULL, "%s: k_new, v_new, n_accept, k_cache, v_cache and ring_head must be non-NULL",
+                name);
+  if (rope_base > 0.f && !positions) return fail(SWA_ERR_NULL, "%s: positions must be non-NULL", name);
+  swa::AppendArgs a;
+  a.k_new = k_new; a.v_new = v_new; a.n_accept = n_accept;
+  a.rope_pos = rope_base > 0.f ? positions : nullptr;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.ring_head = ring_head;
+  a.batch = batch; a.t_new = T; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim; a.window = window;
+  a.log2_base = rope_base > 0.f ? log2((double)rope_base) : 0.0;
+  a.kv_fp8 = fp8; a.k_scale = k_scale; a.v_scale = v_scale;
+  return hip_status(swa::launch_ring_append(a, dtype == SWA_DTYPE_BF16, static_cast<hipStream_t>(stream)),
+                    name);
+}
+
 }  // namespace
 
 extern "C" {
@@ -246,6 +281,17 @@ int swa_sink_decode_rope(const void* q, const void* k_new, const void* v_new, co
                        stream, "swa_sink_decode_rope", positions, rope_base);
 }
 
+int swa_sink_decode_rope_fp8kv(const void* q, const void* k_new, const void* v_new,
+                               const uint8_t* k_cache, const uint8_t* v_cache, float k_scale,
+                               float v_scale, const int32_t* ring_head, const int32_t* positions,
+                               const float* sinks, int32_t batch, int32_t T, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t window, float scale,
+                               float rope_base, swa_dtype dtype, void* out, float* lse, void* stream) {
+  return decode_common(q, k_new, v_new, k_cache, v_cache, true, k_scale, v_scale, ring_head, sinks,
+                       batch, T, num_q_heads, num_kv_heads, head_dim, window, scale, (int)dtype,
+                       out, lse, stream, "swa_sink_decode_rope_fp8kv", positions, rope_base);
+}
+
 int swa_rope(void* x, const int32_t* positions, int32_t rows, int32_t heads, int32_t head_dim,
              float rope_base, swa_dtype dtype, void* stream) {
   const char* name = "swa_rope";
@@ -268,32 +314,19 @@ int swa_ring_append_rope(const void* k_new, const void* v_new, const int32_t* n_
                          const int32_t* positions, void* k_cache, void* v_cache, int32_t* ring_head,
                          int32_t batch, int32_t T, int32_t num_kv_heads, int32_t head_dim,
                          int32_t window, float rope_base, swa_dtype dtype, void* stream) {
-  const char* name = "swa_ring_append_rope";
-  int rc = check_dtype((int)dtype);
-  if (rc) return rc;
-  if ((rc = check_rope_base(rope_base, name))) return rc;
-  if (batch < 0) return fail(SWA_ERR_SHAPE, "%s: batch must be >= 0", name);
-  if (num_kv_heads < 1) return fail(SWA_ERR_SHAPE, "%s: num_kv_heads must be >= 1", name);
-  if (head_dim != 64 && head_dim != 128)
-    return fail(SWA_ERR_SHAPE, "%s: head_dim must be 64 or 128 (got %d)", name, head_dim);
-  if (window < 2) return fail(SWA_ERR_SHAPE, "%s: window must be >= 2 (got %d)", name, window);
-  if (T < 1 || T >= window)
-    return fail(SWA_ERR_SHAPE, "%s: T must satisfy 1 <= T < window (got T=%d, window=%d)", name, T, window);
-  if ((long long)batch * num_kv_heads * window * head_dim > (1LL << 40))
-    return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
-  if (batch == 0) return ok();
-  if (!k_new || !v_new || !n_accept || !k_cache || !v_cache || !ring_head)
-    return fail(SWA_ERR_NULL, "%s: k_new, v_new, n_accept, k_cache, v_cache and ring_head must be non-NULL",
-                name);
-  if (rope_base > 0.f && !positions) return fail(SWA_ERR_NULL, "%s: positions must be non-NULL", name);
-  swa::AppendArgs a;
-  a.k_new = k_new; a.v_new = v_new; a.n_accept = n_accept;
-  a.rope_pos = rope_base > 0.f ? positions : nullptr;
-  a.k_cache = k_cache; a.v_cache = v_cache; a.ring_head = ring_head;
-  a.batch = batch; a.t_new = T; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim; a.window = window;
-  a.log2_base = rope_base > 0.f ? log2((double)rope_base) : 0.0;
-  return hip_status(swa::launch_ring_append(a, dtype == SWA_DTYPE_BF16, static_cast<hipStream_t>(stream)),
-                    name);
+  return ring_append_common(k_new, v_new, n_accept, positions, k_cache, v_cache, ring_head, batch, T,
+                            num_kv_heads, head_dim, window, rope_base, dtype, stream,
+                            "swa_ring_append_rope");
+}
+
+int swa_ring_append_fp8kv(const void* k_new, const void* v_new, const int32_t* n_accept,
+                          const int32_t* positions, uint8_t* k_cache, uint8_t* v_cache, float k_scale,
+                          float v_scale, int32_t* ring_head, int32_t batch, int32_t T,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t window, float rope_base,
+                          swa_dtype dtype, void* stream) {
+  return ring_append_common(k_new, v_new, n_accept, positions, k_cache, v_cache, ring_head, batch, T,
+                            num_kv_heads, head_dim, window, rope_base, dtype, stream,
+                            "swa_ring_append_fp8kv", true, k_scale, v_scale);
 }
 
 int swa_topk_select(const float* scores, const int32_t* lengths, int32_t batch, int32_t num_kv_heads,

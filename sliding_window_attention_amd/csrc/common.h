@@ -100,6 +100,8 @@ struct AppendArgs {
   int32_t head_dim;
   int32_t window;
   double log2_base;
+  bool kv_fp8 = false;      // caches hold E4M3 codes of value / scale
+  float k_scale = 1.f, v_scale = 1.f;
 };
 
 // Token selection for the sparse layers: per (sequence, KV head) row of scores, the top

@@ -380,10 +380,14 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
   if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
   const bool two = a.t_new > 2;
   const dim3 grid((unsigned)blocks), block(kThreads);
-  if (a.rope_pos != nullptr) {  // rotation in the kernel (bf16 ring)
-    if (a.cache_fp8) return hipErrorInvalidValue;
-    if (two) hipLaunchKernelGGL((decode_kernel<2, false, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<1, false, true>), grid, block, 0, s, a);
+  if (a.rope_pos != nullptr) {  // rotation in the kernel
+    if (a.cache_fp8) {
+      if (two) hipLaunchKernelGGL((decode_kernel<2, true, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((decode_kernel<1, true, true>), grid, block, 0, s, a);
+    } else {
+      if (two) hipLaunchKernelGGL((decode_kernel<2, false, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((decode_kernel<1, false, true>), grid, block, 0, s, a);
+    }
   } else if (a.cache_fp8) {
     if (two) hipLaunchKernelGGL((decode_kernel<2, true, false>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((decode_kernel<1, true, false>), grid, block, 0, s, a);

@@ -1,6 +1,7 @@
 // Rotary position embedding around decode: an in-place rotation of [rows, heads, D]
 // tensors (queries and keys of a prefill), and the commit of accepted new tokens to a
-// ring with their keys rotated on the way in.
+// ring with their keys rotated on the way in; the ring holds the I/O type or, for the
+// FP8 (E4M3) KV cache, one-byte codes with a per-tensor scale.
 //
 // Bases: 10,000 in SWA layers and 640,000 (5,000,000 after the 256K extension) in GA
 // layers (MiMo-V2-Flash Technical Report digest, section 3.1); positions keep
@@ -51,29 +52,120 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a) {
   }
 }
 
+// E4M3 code (sign bit 7, exponent bits 6..3 with bias 7, mantissa bits 2..0, subnormals
+// m/8 * 2^-6, S.1111.111 = NaN, largest finite 448) of y / scale: the quotient rounded
+// once to the nearest E4M3 value, ties to the even mantissa; finite magnitudes past 448
+// saturate to 448, and a y that is not finite gives the NaN code with y's sign.  The
+// quotient is formed in fp64: y and scale carry at most 24 significant bits, so a
+// quotient that is not itself halfway between two E4M3 values stays about 2^-30
+// (relative) away from such a point and its fp64 rounding cannot land on one.  Every
+// case is computed and the code selected, with no branches.
+template <typename T>
+__device__ __forceinline__ uint32_t e4m3_encode(T y, double scale) {
+  uint32_t sign, nonfinite;
+  if constexpr (sizeof(T) == 2) {
+    const uint16_t b = __builtin_bit_cast(uint16_t, y);
+    sign = (b >> 8) & 0x80u;
+    nonfinite = (b & 0x7F80u) == 0x7F80u;
+  } else {
+    const uint32_t b = __builtin_bit_cast(uint32_t, y);
+    sign = (b >> 24) & 0x80u;
+    nonfinite = (b & 0x7F800000u) == 0x7F800000u;
+  }
+  const double q = __builtin_fabs((double)(float)y / scale);
+  const uint64_t a = __builtin_bit_cast(uint64_t, q);
+  const int e = (int)(a >> 52) - 1023;
+  const uint64_t mant = a & ((1ull << 52) - 1);
+  // mantissa rounded to 3 bits (0..8); 8 carries into the exponent field
+  const int r = (int)((mant + ((1ull << 48) - 1) + ((mant >> 49) & 1)) >> 49);
+  const uint32_t normal = (uint32_t)(((e + 7) << 3) + r);
+  const uint32_t sub = (uint32_t)__builtin_rint(q * 512.0);  // k * 2^-9, k = 0..8
+  uint32_t code = e < -6 ? sub : normal;
+  code = q >= 448.0 ? 0x7Eu : code;
+  code = nonfinite ? 0x7Fu : code;
+  return sign | code;
+}
+
+// N values of the I/O type from 8, 16 or 32 aligned bytes.
+template <typename T, int N>
+__device__ __forceinline__ void load_n(const T* p, T (&y)[N]) {
+  constexpr int kBytes = N * (int)sizeof(T);
+  static_assert(kBytes == 8 || kBytes == 16 || kBytes == 32, "8, 16 or 32 bytes");
+  if constexpr (kBytes == 8) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    __builtin_memcpy(y, &w, 8);
+  } else {
+    u32x4 w[kBytes / 16];
+#pragma unroll
+    for (int k = 0; k < kBytes / 16; ++k) w[k] = reinterpret_cast<const u32x4*>(p)[k];
+    __builtin_memcpy(y, w, kBytes);
+  }
+}
+
+// N E4M3 codes of y / scale stored at dst (4 or 8 aligned bytes).
+template <typename T, int N>
+__device__ __forceinline__ void store_codes(uint8_t* dst, const T (&y)[N], double scale) {
+  static_assert(N == 4 || N == 8, "4 or 8 codes");
+  uint64_t w = 0;
+#pragma unroll
+  for (int e = 0; e < N; ++e) w |= (uint64_t)e4m3_encode(y[e], scale) << (8 * e);
+  if constexpr (N == 8) *reinterpret_cast<uint64_t*>(dst) = w;
+  else *reinterpret_cast<uint32_t*>(dst) = (uint32_t)w;
+}
+
+// The accepted count and the ring head of sequence b, and the rotary cos/sin table of
+// its (token, pair)s in LDS when the tokens fit it (every thread reads the head before
+// the barrier that ends this).
+constexpr int kMaxT = 8;  // tokens per step with a shared angle table; larger T recomputes
+template <int D>
+__device__ __forceinline__ void append_setup(const AppendArgs& a, int b, float (*cs)[2], int& n, int& head) {
+  const int Tn = a.t_new, W = a.window;
+  n = a.n_accept[b];
+  n = n < 0 ? 0 : (n > Tn ? Tn : n);
+  head = a.ring_head[b] % W;
+  head += head < 0 ? W : 0;
+  if (a.rope_pos != nullptr && n <= kMaxT) {
+    const int pos0 = a.rope_pos[b];
+    for (int x = threadIdx.x; x < n * (D / 2); x += blockDim.x)
+      rope_cos_sin(pos0 + x / (D / 2), x % (D / 2), D, a.log2_base, &cs[x][0], &cs[x][1]);
+  }
+  __syncthreads();
+}
+
+// Rotate N pairs (u[e], v[e]) = (x[i], x[i + D/2]), i = i0 + e, of new token t in place,
+// rounding to the I/O type.
+template <typename T, int D, int N>
+__device__ __forceinline__ void rotate_pairs(const AppendArgs& a, int b, int n, int t, int i0,
+                                             const float (*cs)[2], T (&u)[N], T (&v)[N]) {
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const int i = i0 + e;
+    float c, s;
+    if (n <= kMaxT) {
+      c = cs[t * (D / 2) + i][0];
+      s = cs[t * (D / 2) + i][1];
+    } else {
+      rope_cos_sin(a.rope_pos[b] + t, i, D, a.log2_base, &c, &s);
+    }
+    const float fu = ldf(&u[e]), fv = ldf(&v[e]);
+    u[e] = cvt<T>(fu * c - fv * s);
+    v[e] = cvt<T>(fv * c + fu * s);
+  }
+}
+
 // One workgroup per sequence: write the first n accepted tokens to physical slots
 // (head + t) mod W (the n oldest), then advance the head.  The rotary cos/sin of each
 // (token, pair) is formed once in LDS and shared by the KV heads; keys and values move
-// in 16-byte pieces.  Every thread reads the head before the barriers; one thread
-// writes the new head after the last one.
-constexpr int kMaxT = 8;  // tokens per step with a shared angle table; larger T recomputes
+// in 16-byte pieces.  One thread writes the new head after the last barrier.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void ring_append_kernel(AppendArgs a) {
   __shared__ float cs[kMaxT * (D / 2)][2];
   constexpr int kVec = 16 / (int)sizeof(T);  // elements per 16-byte piece
   const int b = blockIdx.x;
+  int n, head;
+  append_setup<D>(a, b, cs, n, head);
   const int Tn = a.t_new, hkv = a.num_kv_heads, W = a.window;
-  int n = a.n_accept[b];
-  n = n < 0 ? 0 : (n > Tn ? Tn : n);
-  int head = a.ring_head[b] % W;
-  head += head < 0 ? W : 0;
   const bool rope = a.rope_pos != nullptr;
-  const int pos0 = rope ? a.rope_pos[b] : 0;
-  const bool table = n <= kMaxT;
-  if (rope && table)
-    for (int x = threadIdx.x; x < n * (D / 2); x += kThreads)
-      rope_cos_sin(pos0 + x / (D / 2), x % (D / 2), D, a.log2_base, &cs[x][0], &cs[x][1]);
-  __syncthreads();
   const T* kn = static_cast<const T*>(a.k_new) + (size_t)b * Tn * hkv * D;
   const T* vn = static_cast<const T*>(a.v_new) + (size_t)b * Tn * hkv * D;
   T* kc = static_cast<T*>(a.k_cache) + (size_t)b * hkv * W * D;
@@ -87,33 +179,13 @@ __global__ __launch_bounds__(kThreads) void ring_append_kernel(AppendArgs a) {
       const int t = r / hkv, g = r - t * hkv;
       const T* src = kn + ((size_t)t * hkv + g) * D + gi * kVec;
       T* dst = kc + ((size_t)g * W + (head + t) % W) * D + gi * kVec;
-      const u32x4 u4 = *reinterpret_cast<const u32x4*>(src);
-      const u32x4 v4 = *reinterpret_cast<const u32x4*>(src + D / 2);
-      if (!rope) {
-        *reinterpret_cast<u32x4*>(dst) = u4;
-        *reinterpret_cast<u32x4*>(dst + D / 2) = v4;
-        continue;
-      }
-      T u[kVec], v[kVec], yu[kVec], yv[kVec];
-      __builtin_memcpy(u, &u4, 16);
-      __builtin_memcpy(v, &v4, 16);
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) {
-        const int i = gi * kVec + e;
-        float c, s;
-        if (table) {
-          c = cs[t * (D / 2) + i][0];
-          s = cs[t * (D / 2) + i][1];
-        } else {
-          rope_cos_sin(pos0 + t, i, D, a.log2_base, &c, &s);
-        }
-        const float fu = ldf(&u[e]), fv = ldf(&v[e]);
-        yu[e] = cvt<T>(fu * c - fv * s);
-        yv[e] = cvt<T>(fv * c + fu * s);
-      }
+      T u[kVec], v[kVec];
+      load_n(src, u);
+      load_n(src + D / 2, v);
+      if (rope) rotate_pairs<T, D>(a, b, n, t, gi * kVec, cs, u, v);
       u32x4 o1, o2;
-      __builtin_memcpy(&o1, yu, 16);
-      __builtin_memcpy(&o2, yv, 16);
+      __builtin_memcpy(&o1, u, 16);
+      __builtin_memcpy(&o2, v, 16);
       *reinterpret_cast<u32x4*>(dst) = o1;
       *reinterpret_cast<u32x4*>(dst + D / 2) = o2;
     } else {
@@ -122,6 +194,51 @@ __global__ __launch_bounds__(kThreads) void ring_append_kernel(AppendArgs a) {
       const int t = r / hkv, g = r - t * hkv;
       *reinterpret_cast<u32x4*>(vc + ((size_t)g * W + (head + t) % W) * D + pc * kVec) =
           *reinterpret_cast<const u32x4*>(vn + ((size_t)t * hkv + g) * D + pc * kVec);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.ring_head[b] = (head + n) % W;
+}
+
+// The same commit into an FP8 ring: every element is encoded (e4m3_encode), so the work
+// is arithmetic rather than data movement and is spread thinner -- 512 threads per
+// sequence, each item 8 codes: 4 pairs of a key (two 4-byte stores) or 8 elements of a
+// value (one 8-byte store).
+constexpr int kThreadsFp8 = 512;
+template <typename T, int D>
+__global__ __launch_bounds__(kThreadsFp8) void ring_append_fp8_kernel(AppendArgs a) {
+  __shared__ float cs[kMaxT * (D / 2)][2];
+  const int b = blockIdx.x;
+  int n, head;
+  append_setup<D>(a, b, cs, n, head);
+  const int Tn = a.t_new, hkv = a.num_kv_heads, W = a.window;
+  const bool rope = a.rope_pos != nullptr;
+  const double ks = a.k_scale, vs = a.v_scale;
+  const T* kn = static_cast<const T*>(a.k_new) + (size_t)b * Tn * hkv * D;
+  const T* vn = static_cast<const T*>(a.v_new) + (size_t)b * Tn * hkv * D;
+  uint8_t* kc = static_cast<uint8_t*>(a.k_cache) + (size_t)b * hkv * W * D;
+  uint8_t* vc = static_cast<uint8_t*>(a.v_cache) + (size_t)b * hkv * W * D;
+  constexpr int kKUnits = D / 2 / 4, kVUnits = D / 8;
+  const int nk = n * hkv * kKUnits;
+  for (int x = threadIdx.x; x < nk + n * hkv * kVUnits; x += kThreadsFp8) {
+    if (x < nk) {
+      const int gi = x % kKUnits, r = x / kKUnits;  // r = token * hkv + kv head
+      const int t = r / hkv, g = r - t * hkv;
+      const T* src = kn + ((size_t)t * hkv + g) * D + gi * 4;
+      uint8_t* dst = kc + ((size_t)g * W + (head + t) % W) * D + gi * 4;
+      T u[4], v[4];
+      load_n(src, u);
+      load_n(src + D / 2, v);
+      if (rope) rotate_pairs<T, D>(a, b, n, t, gi * 4, cs, u, v);
+      store_codes(dst, u, ks);
+      store_codes(dst + D / 2, v, ks);
+    } else {
+      const int y = x - nk;
+      const int pc = y % kVUnits, r = y / kVUnits;
+      const int t = r / hkv, g = r - t * hkv;
+      T v[8];
+      load_n(vn + ((size_t)t * hkv + g) * D + pc * 8, v);
+      store_codes(vc + ((size_t)g * W + (head + t) % W) * D + pc * 8, v, vs);
     }
   }
   __syncthreads();
@@ -141,7 +258,10 @@ hipError_t rope_t(const RopeArgs& a, hipStream_t s) {
 template <typename T, int D>
 hipError_t append_t(const AppendArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL((ring_append_kernel<T, D>), dim3((unsigned)a.batch), dim3(kThreads), 0, s, a);
+  if (a.kv_fp8)
+    hipLaunchKernelGGL((ring_append_fp8_kernel<T, D>), dim3((unsigned)a.batch), dim3(kThreadsFp8), 0, s, a);
+  else
+    hipLaunchKernelGGL((ring_append_kernel<T, D>), dim3((unsigned)a.batch), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -60,6 +60,9 @@ WORKLOADS = {
     # the kernel, SWA base 10,000), and the commit of the accepted tokens to the ring.
     "decode_rope_t1": Workload("decode_rope_t1", "decode_rope", "bf16", batch=256, t_new=1, seed=3400),
     "decode_rope_t4": Workload("decode_rope_t4", "decode_rope", "bf16", batch=256, t_new=4, seed=3500),
+    # The MTP verify with RoPE in the kernel against an FP8 ring, and its commit.
+    "decode_rope_fp8_t4": Workload("decode_rope_fp8_t4", "decode_rope_fp8", "bf16", batch=256, t_new=4,
+                                   seed=3550),
     # Sparse decode (HySparse2 selection: top 1024 + the recent 128) for 64 sequences of
     # 16K-32K cached tokens over a [64, 4, 32768, 128] cache; the scores stand for the
     # full-attention layer's (no sink in the sparse layers).
@@ -282,6 +285,16 @@ def make_decode_fp8(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, d
     return x
 
 
+def make_decode_rope_fp8(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, dtype, seed):
+    """make_decode_rope with the caches as E4M3 codes (make_decode_fp8's codes and
+    scales, drawn from the same seeds)."""
+    x = make_decode_rope(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, dtype, seed)
+    y = make_decode_fp8(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, dtype, seed)
+    for k in ("k_cache", "v_cache", "k_scale", "v_scale"):
+        x[k] = y[k]
+    return x
+
+
 def make_workload(name: str, layer: int = 0):
     """Inputs of a named workload (for 'hybrid_5to1_32k', layer 0..4 are SWA, 5 is GA)."""
     w = WORKLOADS[name]
@@ -304,6 +317,9 @@ def make_workload(name: str, layer: int = 0):
     if w.kind == "decode_rope":
         return make_decode_rope(w.batch, w.t_new, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                 w.window, w.dtype, w.seed)
+    if w.kind == "decode_rope_fp8":
+        return make_decode_rope_fp8(w.batch, w.t_new, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                    w.window, w.dtype, w.seed)
     raise KeyError(name)
 
 
@@ -367,10 +383,12 @@ def decode_bytes(batch, t_new, num_q_heads, num_kv_heads, head_dim, window, elem
     return kv + qo + lse
 
 
-def append_bytes(batch, n_accepted_total, num_kv_heads, head_dim, elem_bytes):
-    """Ring append: the accepted tokens' K and V read once and written once, plus the
-    accept counts, positions and heads (read, heads written)."""
-    return 4 * n_accepted_total * num_kv_heads * head_dim * elem_bytes + 4 * 4 * batch
+def append_bytes(batch, n_accepted_total, num_kv_heads, head_dim, elem_bytes, cache_elem_bytes=None):
+    """Ring append: the accepted tokens' K and V read once and written once (in the
+    ring's element size: 1 for an FP8 ring), plus the accept counts, positions and heads
+    (read, heads written)."""
+    cb = elem_bytes if cache_elem_bytes is None else cache_elem_bytes
+    return 2 * n_accepted_total * num_kv_heads * head_dim * (elem_bytes + cb) + 4 * 4 * batch
 
 
 def rope_bytes(rows, heads, head_dim, elem_bytes):
@@ -382,10 +400,10 @@ def workload_work(name: str):
     """(flops, bytes) of one pass of a named workload as its kind defines it."""
     w = WORKLOADS[name]
     eb = 4 if w.dtype == "f32" else 2
-    if w.kind in ("decode", "decode_fp8", "decode_rope"):
+    if w.kind in ("decode", "decode_fp8", "decode_rope", "decode_rope_fp8"):
         return (decode_flops(w.batch, w.t_new, w.num_q_heads, w.head_dim, w.window),
                 decode_bytes(w.batch, w.t_new, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                             w.window, eb, cache_elem_bytes=1 if w.kind == "decode_fp8" else None))
+                             w.window, eb, cache_elem_bytes=1 if "fp8" in w.kind else None))
     if w.kind == "varlen":
         lens = lognormal_lengths(w.seq_len, w.num_seqs, w.seed)
     else:

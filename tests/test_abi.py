@@ -28,6 +28,7 @@ def test_header_declares_the_entry_points():
                           "swa_sink_decode_fp8kv", "swa_sink_prefill_backward",
                           "swa_sink_prefill_backward_workspace", "swa_rope", "swa_sink_decode_rope",
                           "swa_ring_append_rope", "swa_topk_select", "swa_sparse_decode",
+                          "swa_sink_decode_rope_fp8kv", "swa_ring_append_fp8kv",
                           "swa_last_error", "swa_abi_version"}
 
 
@@ -363,6 +364,81 @@ def test_ring_append_edge_cases_validate_without_launching():
     # base 0 copies the keys unrotated, so positions may be NULL; every other pointer is still
     # required (the call fails before any launch)
     assert _append(pos=NULL, base=0.0, kc=NULL) == E_NULL and "k_cache" in _last()
+
+
+def _append_fp8(**kw):
+    a = dict(kn=FAKE, vn=FAKE, nacc=FAKE, pos=FAKE, kc=FAKE, vc=FAKE, ks=0.5, vs=0.25, head=FAKE, b=2, t=4,
+             hkv=4, d=128, window=128, base=10000.0, dtype=1)
+    a.update(kw)
+    return swa.library().swa_ring_append_fp8kv(
+        a["kn"], a["vn"], a["nacc"], a["pos"], a["kc"], a["vc"], a["ks"], a["vs"], a["head"], a["b"], a["t"],
+        a["hkv"], a["d"], a["window"], a["base"], a["dtype"], NULL)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(ks=0.0), E_SHAPE, "k_scale"),
+    (dict(vs=-0.5), E_SHAPE, "v_scale"),
+    (dict(ks=float("inf")), E_SHAPE, "finite"),
+    (dict(vs=float("nan")), E_SHAPE, "finite"),
+    (dict(t=0), E_SHAPE, "T must"),
+    (dict(d=80), E_SHAPE, "head_dim"),
+    (dict(kc=NULL), E_NULL, "k_cache"),
+    (dict(pos=NULL), E_NULL, "positions"),
+    (dict(dtype=9), E_DTYPE, "dtype"),
+])
+def test_ring_append_fp8kv_rejects_bad_arguments(kw, code, needle):
+    assert _append_fp8(**kw) == code
+    assert needle in _last()
+    if code in (E_SHAPE, E_NULL):
+        assert "swa_ring_append_fp8kv" in _last()
+
+
+def test_ring_append_fp8kv_edge_cases_validate_without_launching():
+    assert _append_fp8(b=0, kn=NULL, vn=NULL, nacc=NULL, pos=NULL, kc=NULL, vc=NULL, head=NULL) == OK
+    assert _append_fp8(b=0, ks=-1.0) == E_SHAPE  # the scales are still checked
+    assert _append_fp8(pos=NULL, base=0.0, vc=NULL) == E_NULL and "v_cache" in _last()
+
+
+def _decode_rope_fp8(**kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, ks=0.5, vs=0.25, head=FAKE, pos=FAKE, sinks=FAKE,
+             b=2, t=1, hq=8, hkv=1, d=128, window=128, scale=0.0, base=10000.0, dtype=1, out=FAKE, lse=NULL)
+    a.update(kw)
+    return swa.library().swa_sink_decode_rope_fp8kv(
+        a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["ks"], a["vs"], a["head"], a["pos"], a["sinks"], a["b"],
+        a["t"], a["hq"], a["hkv"], a["d"], a["window"], a["scale"], a["base"], a["dtype"], a["out"], a["lse"],
+        NULL)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(ks=0.0), E_SHAPE, "k_scale"),
+    (dict(vs=float("inf")), E_SHAPE, "finite"),
+    (dict(pos=NULL), E_NULL, "positions"),
+    (dict(base=-2.0), E_SHAPE, "rope_base"),
+    (dict(t=128), E_SHAPE, "T must"),
+    (dict(sinks=NULL), E_NULL, "sinks"),
+    (dict(d=32), E_UNSUP, "head_dim"),
+])
+def test_decode_rope_fp8kv_rejects_bad_arguments(kw, code, needle):
+    assert _decode_rope_fp8(**kw) == code
+    assert needle in _last()
+
+
+def test_decode_rope_fp8kv_empty_batch_accepts_null_pointers():
+    assert _decode_rope_fp8(b=0, q=NULL, kn=NULL, vn=NULL, kc=NULL, vc=NULL, head=NULL, pos=NULL, sinks=NULL,
+                            out=NULL) == OK
+
+
+def test_binding_fp8_append_refuses_non_byte_caches():
+    import torch
+
+    kn = torch.zeros(1, 1, 1, 128, dtype=torch.bfloat16)
+    ring = torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, TypeError)):
+        swa.swa_ring_append_fp8kv(kn, kn, torch.ones(1, dtype=torch.int32), None, ring, ring, 1.0, 1.0,
+                                  torch.zeros(1, dtype=torch.int32), rope_base=0.0)
+    with pytest.raises((ValueError, TypeError)):
+        swa.swa_sink_decode_rope_fp8kv(kn, kn, kn, ring, ring, 1.0, 1.0, torch.zeros(1, dtype=torch.int32),
+                                       torch.zeros(1, dtype=torch.int32), torch.zeros(1))
 
 
 # ---------------------------------------------------------------------------

@@ -440,6 +440,111 @@ def test_fp8kv_prefill_scales_are_exponent_shifts():
 
 
 # ---------------------------------------------------------------------------
+# E4M3 encoding (the append into an FP8 ring)
+# ---------------------------------------------------------------------------
+
+def test_e4m3_encode_round_trips_every_finite_code():
+    """Every finite code's value (the pinned decoder) encodes back to that code, -0 included."""
+    codes = np.arange(256, dtype=np.uint8)
+    fin = codes[(codes & 0x7F) != 0x7F]
+    assert np.array_equal(orc.e4m3_encode(orc.e4m3_to_float(fin)), fin)
+
+
+def test_e4m3_encode_matches_library_cast():
+    """fp32 values spread over the E4M3 range and beyond its subnormals, against torch's
+    float8_e4m3fn cast (round to nearest even).  That cast turns magnitudes from 464 on into
+    NaN rather than saturating, so the comparison stays below 464; power-of-two scales keep the
+    quotient exact in fp32, which is what the cast receives."""
+    g = torch.Generator().manual_seed(31)
+    x = torch.randn(200000, generator=g) * torch.exp2(torch.randint(-16, 9, (200000,), generator=g).float())
+    for s in (1.0, 1.0 / 32, 4.0):
+        q = x / s
+        keep = q.abs() < 464
+        ref = q[keep].to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        got = orc.e4m3_encode(x[keep].double().numpy(), s)
+        assert np.array_equal(got, ref), s
+
+
+def test_e4m3_encode_is_the_nearest_value_in_exact_arithmetic():
+    """With a scale that is no power of two, each code is the nearest E4M3 value to x / scale
+    found by exact rational search over the hand-decoded value set (ties to the even code),
+    saturating at 448; quotients sitting exactly on ties are included."""
+    from fractions import Fraction
+
+    s32 = float(np.float32(0.0173))
+    vals = [Fraction(m, 8) * Fraction(2) ** -6 for m in range(8)]          # codes 0..7
+    vals += [(1 + Fraction(m, 8)) * Fraction(2) ** (e - 7) for e in range(1, 16) for m in range(8)
+             if not (e == 15 and m == 7)]                                  # codes 8..126
+    rng = np.random.default_rng(32)
+    xs = list((rng.standard_normal(1500) * np.exp2(rng.integers(-14, 4, 1500))).astype(np.float32))
+    # exact ties: halfway points times the scale, where that product is an fp32 value
+    for c in rng.integers(0, 126, 400):
+        t = (vals[c] + vals[c + 1]) / 2 * Fraction(s32)
+        if float(np.float32(float(t))) == t:
+            xs.append(np.float32(float(t)))
+    xs += [np.float32(449 * s32), np.float32(-1e3)]
+    got = orc.e4m3_encode(np.array(xs, dtype=np.float64), s32)
+    for x, c in zip(xs, got):
+        q = abs(Fraction(float(x))) / Fraction(s32)
+        q = min(q, vals[-1])
+        best = min(range(127), key=lambda k: (abs(q - vals[k]), k % 2))
+        want = best | (0x80 if x < 0 else 0)
+        assert int(c) == want, (float(x), hex(int(c)), hex(want))
+
+
+def test_e4m3_encode_hand_values():
+    from tests.golden.load import load, value
+
+    for case in load("e4m3_encode_hand.json")["cases"]:
+        x = float(case["x"]) if case["x"] in ("inf", "-inf", "nan", "-0") else value(case["x"])
+        code = orc.e4m3_encode(np.array([x]), value(case["scale"]))[0]
+        assert int(code) == int(case["code"], 16), case
+
+
+def test_fp8_ring_append_matches_a_list_model():
+    """The FP8 append places the same slots as the list model of the ring (last W of ring ++
+    accepted tokens); keys and values that are E4M3 values times the scales come back as their
+    codes unchanged, and rotated keys decode to within half an E4M3 step of the rotation."""
+    rng = np.random.default_rng(33)
+    bsz, t_new, hkv, d, w = 4, 4, 2, 8, 6
+    k_scale, v_scale = 1.0 / 32, 0.25
+    kc0 = _codes(rng, (bsz, hkv, w, d))[0]
+    vc0 = _codes(rng, (bsz, hkv, w, d))[0]
+    kcodes, ks_, ke, km = _codes(rng, (bsz, t_new, hkv, d))
+    vcodes, vs_, ve, vm = _codes(rng, (bsz, t_new, hkv, d))
+    kn = np.where(ks_ == 1, -1.0, 1.0) * (1 + km / 8.0) * 2.0 ** (ke - 7) * k_scale
+    vn = np.where(vs_ == 1, -1.0, 1.0) * (1 + vm / 8.0) * 2.0 ** (ve - 7) * v_scale
+    heads = np.array([0, 5, 3, 2])
+    n_acc = np.array([0, 1, 4, 3])
+    pos = np.array([10, 0, 77, 123456])
+    k2, v2, h2 = orc.swa_ring_append_fp8kv(kn, vn, n_acc, pos, kc0, vc0, heads, None, k_scale, v_scale)
+    k3, v3, h3 = orc.swa_ring_append_fp8kv(kn, vn, n_acc, pos, kc0, vc0, heads, 10000.0, k_scale, v_scale,
+                                           io_dtype=None)
+    assert np.array_equal(h2, h3) and np.array_equal(v2, v3)
+    for b in range(bsz):
+        klist = [kc0[b, :, (heads[b] + l) % w, :] for l in range(w)]
+        vlist = [vc0[b, :, (heads[b] + l) % w, :] for l in range(w)]
+        rlist = [None] * w
+        for t in range(n_acc[b]):
+            klist.append(kcodes[b, t])
+            vlist.append(vcodes[b, t])
+            rlist.append(orc.rope(kn[b, t][None], [pos[b] + t], 10000.0)[0])
+        klist, vlist, rlist = klist[-w:], vlist[-w:], rlist[-w:]
+        assert h2[b] == (heads[b] + n_acc[b]) % w
+        for l in range(w):
+            slot = (h2[b] + l) % w
+            np.testing.assert_array_equal(k2[b, :, slot, :], klist[l])
+            np.testing.assert_array_equal(v2[b, :, slot, :], vlist[l])
+            if rlist[l] is None:
+                np.testing.assert_array_equal(k3[b, :, slot, :], klist[l])
+            else:
+                dec = orc.e4m3_to_float(k3[b, :, slot, :]) * k_scale
+                ref = rlist[l]
+                assert np.all(np.abs(dec - ref) <= 2.0 ** -4 * np.abs(ref) + 2.0 ** -10 * k_scale)
+    assert not np.shares_memory(k2, kc0)
+
+
+# ---------------------------------------------------------------------------
 # backward (gradients of O)
 # ---------------------------------------------------------------------------
 

@@ -955,6 +955,180 @@ def test_ring_append_full_batch():
 
 
 # ---------------------------------------------------------------------------
+# FP8 ring with RoPE: decode (rotation in the kernel) and the append that encodes
+# ---------------------------------------------------------------------------
+
+def _run_decode_rope_fp8(x, base):
+    g = _gpu(x)
+    o, lse = swa.swa_sink_decode_rope_fp8kv(g["q"], g["k_new"], g["v_new"], g["k_cache"], g["v_cache"],
+                                            x["k_scale"], x["v_scale"], g["ring_head"], g["positions"],
+                                            g["sinks"], base)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _oracle_decode_rope_fp8(x, window, base):
+    io = "bf16" if x["q"].dtype == torch.bfloat16 else "f32"
+    return orc.swa_sink_decode_rope_fp8kv(x["q"], x["k_new"], x["v_new"], x["k_cache"].numpy(),
+                                          x["v_cache"].numpy(), x["k_scale"], x["v_scale"],
+                                          x["ring_head"].numpy(), x["positions"].numpy(), x["sinks"], base,
+                                          window, io_dtype=io)
+
+
+@pytest.mark.parametrize("t_new", [1, 2, 3, 4])
+def test_decode_rope_fp8(t_new):
+    _say(f"FP8 ring decode with RoPE B=16 T={t_new} 32/4 D128 bf16 (matrix cores)")
+    x = wl.make_decode_rope_fp8(16, t_new, 32, 4, 128, 128, "bf16", seed=3620 + t_new)
+    x["positions"][0] = 128
+    x["positions"][1] = 2 ** 31 - 8
+    x["ring_head"][2] = 127
+    for base in (10000.0, 5e6):
+        o, lse = _run_decode_rope_fp8(x, base)
+        o_ref, l_ref = _oracle_decode_rope_fp8(x, 128, base)
+        assert_close(torch.bfloat16, o, o_ref, lse, l_ref, f"FP8 decode rope T={t_new} base {base:g}")
+
+
+@pytest.mark.parametrize("case", [(3, 8, 1, 64, 128, "bf16", 2), (5, 4, 1, 64, 128, "f32", 3),
+                                  (4, 8, 8, 128, 64, "bf16", 4)])
+def test_decode_rope_fp8_generic_shapes(case):
+    b, hq, hkv, d, w, dt, t_new = case
+    _say(f"FP8 ring decode with RoPE generic B={b} T={t_new} {hq}/{hkv} D{d} W{w} {dt}")
+    x = wl.make_decode_rope_fp8(b, t_new, hq, hkv, d, w, dt, seed=3640 + b * 7 + w)
+    o, lse = _run_decode_rope_fp8(x, 640000.0)
+    o_ref, l_ref = _oracle_decode_rope_fp8(x, w, 640000.0)
+    assert_close(x["q"].dtype, o, o_ref, lse, l_ref, f"FP8 decode rope generic {case}")
+
+
+def test_decode_rope_fp8_base_zero_is_fp8_decode():
+    _say("FP8 ring decode with rope_base 0 equals swa_sink_decode_fp8kv bit for bit")
+    x = wl.make_decode_rope_fp8(8, 4, 32, 4, 128, 128, "bf16", seed=3660)
+    o, lse = _run_decode_rope_fp8(x, 0.0)
+    o2, l2 = _run_decode_fp8(x)
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+def _codes_close(got, ref, what, min_same=0.999):
+    """E4M3 codes that come from rotated keys: the fp32 rotation may round to the
+    neighbouring I/O value of the oracle's, which moves a code by at most one step when the
+    quotient sits near a rounding point.  At least min_same must be identical; every other
+    code must decode to a neighbour (same sign, magnitudes one step apart)."""
+    got = np.asarray(got, dtype=np.int64)
+    ref = np.asarray(ref, dtype=np.int64)
+    same = got == ref
+    frac = float(same.mean()) if same.size else 1.0
+    diff = ~same
+    adjacent = ((got & 0x80) == (ref & 0x80)) & (np.abs((got & 0x7F) - (ref & 0x7F)) == 1)
+    msg = f"{what}: identical {frac:.6f}, non-adjacent {int((diff & ~adjacent).sum())}"
+    print(msg, flush=True)
+    assert frac >= min_same and not np.any(diff & ~adjacent), msg
+
+
+def _written(ring_head, n_acc, b, t_new, w, shape):
+    m = np.zeros(shape[:3], dtype=bool)  # [B, Hkv, W]
+    for bb in range(b):
+        n = int(np.clip(n_acc[bb], 0, t_new))
+        for t in range(n):
+            m[bb, :, (int(ring_head[bb]) % w + t) % w] = True
+    return m
+
+
+@pytest.mark.parametrize("case", [(16, 4, 4, 128, 128, "bf16", 0.0, 1 / 32, 1 / 64),
+                                  (16, 4, 4, 128, 128, "bf16", 10000.0, 0.0173, 0.0311),
+                                  (9, 3, 2, 64, 32, "f32", 640000.0, 0.0173, 0.0311),
+                                  (7, 2, 1, 128, 128, "f32", 0.0, 0.0173, 0.0311)],
+                         ids=lambda c: f"B{c[0]}-T{c[1]}-kv{c[2]}-D{c[3]}-W{c[4]}-{c[5]}-base{c[6]:g}-s{c[7]:g}")
+def test_ring_append_fp8kv(case):
+    """Codes written to an FP8 ring: bit-exact against the oracle's encoding where the keys
+    are copied (base 0; specials, saturation and subnormals planted; with power-of-two scales
+    bf16 quotients sit exactly halfway between E4M3 values about once in sixteen, with other
+    scales they round), values always bit-exact, rotated keys identical up to one-step
+    neighbours; untouched slots and the heads exact."""
+    b, t_new, hkv, d, w, dt, base, ks, vs = case
+    _say(f"FP8 ring append B={b} T={t_new} kv {hkv} D{d} W{w} {dt} base {base:g} scales {ks:g}/{vs:g}")
+    x = wl.make_decode_rope_fp8(b, t_new, hkv, hkv, d, w, dt, seed=3680 + b)
+    gen = torch.Generator().manual_seed(3681 + b)
+    n_acc = torch.randint(0, t_new + 1, (b,), generator=gen, dtype=torch.int64).to(torch.int32)
+    n_acc[0], n_acc[1], n_acc[4] = t_new + 3, -2, t_new  # clamped to T and to 0
+    x["ring_head"][2] = w - 1
+    x["ring_head"][3] = 3 * w + 1
+    if base == 0.0:
+        s32 = float(np.float32(ks))
+        specials = [float("nan"), float("inf"), -float("inf"), -0.0, 1e30, -1e30, 449 * s32, 1e-30,
+                    2.0 ** -10 * s32, 3 * 2.0 ** -10 * s32, 17 / 16 * s32, 19 / 16 * s32]
+        sp = torch.tensor(specials, dtype=torch.float64).to(x["k_new"].dtype)
+        x["k_new"][4, 0, 0, :len(specials)] = sp
+        x["v_new"][4, 0, 0, :len(specials)] = torch.tensor(specials, dtype=torch.float64).to(x["k_new"].dtype)
+        x["v_new"][4, 0, 0, :len(specials)] *= float(np.float32(vs)) / s32
+    g = _gpu(x)
+    heads = g["ring_head"].clone()
+    swa.swa_ring_append_fp8kv(g["k_new"], g["v_new"], n_acc.to(DEV), g["positions"], g["k_cache"],
+                              g["v_cache"], ks, vs, heads, base)
+    torch.cuda.synchronize()
+    io = "bf16" if dt == "bf16" else "f32"
+    kc, vc, h2 = orc.swa_ring_append_fp8kv(x["k_new"], x["v_new"], np.clip(n_acc.numpy(), 0, t_new),
+                                           x["positions"].numpy(), x["k_cache"].numpy(), x["v_cache"].numpy(),
+                                           x["ring_head"].numpy(), base or None, ks, vs, io_dtype=io)
+    assert np.array_equal(heads.cpu().numpy(), h2)
+    got_k, got_v = g["k_cache"].cpu().numpy(), g["v_cache"].cpu().numpy()
+    assert np.array_equal(got_v, vc)
+    written = _written(x["ring_head"].numpy(), n_acc.numpy(), b, t_new, w, got_k.shape)
+    assert np.array_equal(got_k[~written], x["k_cache"].numpy()[~written])
+    if base == 0.0:
+        assert np.array_equal(got_k, kc)
+    else:
+        _codes_close(got_k[written], kc[written], f"FP8 append keys {case}")
+
+
+def test_fp8_mtp_steps_follow_the_oracle():
+    """Five MTP steps against an FP8 ring: verify T = 4 tokens (RoPE in the kernel), commit a
+    seeded 0..4 of them (keys rotated, both encoded), advance the positions; each step's
+    outputs and the ring follow the oracle run on the same inputs."""
+    _say("FP8 decode + append: 5 MTP steps, B=8, 32/4 D128 bf16")
+    b, t_new, hq, hkv, d, w, base = 8, 4, 32, 4, 128, 128, 10000.0
+    x = wl.make_decode_rope_fp8(b, t_new, hq, hkv, d, w, "bf16", seed=4150)
+    ks, vs = x["k_scale"], x["v_scale"]
+    gen = torch.Generator().manual_seed(4151)
+    g = _gpu(x)
+    kc, vc, heads = x["k_cache"].numpy(), x["v_cache"].numpy(), x["ring_head"].numpy()
+    pos = x["positions"].numpy().astype(np.int64)
+    for step in range(5):
+        q = torch.randn(b, t_new, hq, d, generator=gen).to(torch.bfloat16)
+        kn = torch.randn(b, t_new, hkv, d, generator=gen).to(torch.bfloat16)
+        vn = torch.randn(b, t_new, hkv, d, generator=gen).to(torch.bfloat16)
+        n_acc = torch.randint(0, t_new + 1, (b,), generator=gen, dtype=torch.int64).to(torch.int32)
+        pos_t = torch.from_numpy(pos.astype(np.int32))
+        o, lse = swa.swa_sink_decode_rope_fp8kv(q.to(DEV), kn.to(DEV), vn.to(DEV), g["k_cache"], g["v_cache"],
+                                                ks, vs, g["ring_head"], pos_t.to(DEV), g["sinks"], base)
+        swa.swa_ring_append_fp8kv(kn.to(DEV), vn.to(DEV), n_acc.to(DEV), pos_t.to(DEV), g["k_cache"],
+                                  g["v_cache"], ks, vs, g["ring_head"], base)
+        torch.cuda.synchronize()
+        o_ref, l_ref = orc.swa_sink_decode_rope_fp8kv(q, kn, vn, kc, vc, ks, vs, heads, pos, x["sinks"], base, w)
+        assert_close(torch.bfloat16, o, o_ref, lse, l_ref, f"FP8 step {step}")
+        kc, vc, heads = orc.swa_ring_append_fp8kv(kn, vn, n_acc.numpy(), pos, kc, vc, heads, base, ks, vs)
+        assert np.array_equal(g["ring_head"].cpu().numpy(), heads)
+        assert np.array_equal(g["v_cache"].cpu().numpy(), vc)
+        _codes_close(g["k_cache"].cpu().numpy(), kc, f"FP8 step {step} ring keys", min_same=0.9999)
+        pos = pos + n_acc.numpy()
+
+
+def test_ring_append_fp8kv_full_batch():
+    _say("FP8 ring append after the T = 4 verify (B=256), every slot")
+    x = wl.make_workload("decode_rope_fp8_t4")
+    gen = torch.Generator().manual_seed(3501)
+    n_acc = torch.randint(0, 5, (256,), generator=gen, dtype=torch.int64).to(torch.int32)
+    g = _gpu(x)
+    swa.swa_ring_append_fp8kv(g["k_new"], g["v_new"], n_acc.to(DEV), g["positions"], g["k_cache"],
+                              g["v_cache"], x["k_scale"], x["v_scale"], g["ring_head"], 10000.0)
+    torch.cuda.synchronize()
+    kc, vc, h2 = orc.swa_ring_append_fp8kv(x["k_new"], x["v_new"], n_acc.numpy(), x["positions"].numpy(),
+                                           x["k_cache"].numpy(), x["v_cache"].numpy(), x["ring_head"].numpy(),
+                                           10000.0, x["k_scale"], x["v_scale"])
+    assert np.array_equal(g["ring_head"].cpu().numpy(), h2)
+    assert np.array_equal(g["v_cache"].cpu().numpy(), vc)
+    _codes_close(g["k_cache"].cpu().numpy(), kc, "FP8 append B=256 keys", min_same=0.9999)
+
+
+# ---------------------------------------------------------------------------
 # token-level sparse attention: selection (exact) and sparse decode
 # ---------------------------------------------------------------------------
 
