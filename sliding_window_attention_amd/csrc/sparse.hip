@@ -33,7 +33,6 @@ using namespace tile;
 // ---------------------------------------------------------------------------
 
 constexpr int kSelThreads = 1024;  // 16 wavefronts
-constexpr int kSelPer = 8;        // consecutive candidates per thread in the ordered pass
 
 // Larger float -> larger key; NaN below every number.  The scores are read as their
 // 32-bit patterns: the device code is built without NaN semantics, under which a test
@@ -69,15 +68,86 @@ __device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t x, uint32_t* t
 constexpr int kKeyCache = 32768;  // candidates whose keys are kept in LDS (128 KB)
 constexpr int kBins0 = 4096;       // first digit: bits 31..20 (sign, exponent, 3 mantissa bits)
 constexpr int kBins = 1024;        // next digits: bits 19..10 and 9..0
+constexpr int kList = kBins0 - kBins;  // keys of the threshold's first-digit bin kept after pass 0
+
+// The digit holding the rem-th largest of the keys counted in hist[0, nb): thread t owns
+// the nb / 1024 bins just below the top t * per (descending), and an inclusive scan over
+// threads counts the keys at or above each thread's lowest bin; exactly one thread holds
+// the rem-th.  After the closing barrier pick[0] is the digit and pick[1] how many keys
+// with that digit are still to be taken.
+__device__ __forceinline__ void pick_digit(const uint32_t* hist, int nb, int rem, uint32_t* tmp,
+                                           uint32_t* pick) {
+  const int per = nb / kSelThreads;  // 4 or 1
+  const int top = nb - 1 - (int)threadIdx.x * per;
+  uint32_t mine = 0;
+  for (int e = 0; e < per; ++e) mine += hist[top - e];
+  uint32_t tot;
+  const uint32_t incl = block_inclusive_scan(mine, tmp, &tot);
+  uint32_t acc = incl - mine;  // keys in bins above this thread's
+  if (acc < (uint32_t)rem && (uint32_t)rem <= incl) {
+    int d = top;
+    for (int e = 0; e < per; ++e, --d) {
+      const uint32_t hv = hist[d];
+      if (acc + hv >= (uint32_t)rem) break;
+      acc += hv;
+    }
+    pick[0] = (uint32_t)d;
+    pick[1] = (uint32_t)rem - acc;
+  }
+  __syncthreads();
+}
+
+// The ordered pass: candidate j is chosen when its key is above the threshold T, or equal
+// to it and among the first `rem` such positions; its output slot is (# above T before j)
+// + min(# equal to T before j, rem).  Each thread takes P consecutive candidates per chunk
+// of 1024 * P (keys past ncand are read but never counted).
+template <int P, typename KeysAt>
+__device__ __forceinline__ void write_ordered(KeysAt keys_at, int ncand, uint32_t T, uint32_t rem, int32_t* out,
+                                              uint32_t* tmp) {
+  uint32_t gt_run = 0, eq_run = 0;
+  for (int c0 = 0; c0 < ncand; c0 += kSelThreads * P) {
+    const int j0 = c0 + (int)threadIdx.x * P;
+    uint32_t key[P];
+    keys_at(j0, key);
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      const bool ok = j0 + e < ncand;
+      ngt += (ok && key[e] > T) ? 1u : 0u;
+      neq += (ok && key[e] == T) ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t incl = block_inclusive_scan((ngt << 16) | neq, tmp, &tot);
+    if (ngt + neq != 0) {
+      uint32_t gt_b = gt_run + ((incl >> 16) - ngt), eq_b = eq_run + ((incl & 0xffffu) - neq);
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        const int j = j0 + e;
+        if (j < ncand && key[e] >= T) {
+          if (key[e] > T) {
+            out[gt_b + min(eq_b, rem)] = j;
+            ++gt_b;
+          } else {
+            if (eq_b < rem) out[gt_b + eq_b] = j;
+            ++eq_b;
+          }
+        }
+      }
+    }
+    gt_run += tot >> 16;
+    eq_run += tot & 0xffffu;
+  }
+}
 
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
-  __shared__ uint32_t cache[kKeyCache];  // the row's keys when it fits, else unused
-  __shared__ uint32_t hist[kBins0];
+  __shared__ __attribute__((aligned(16))) uint32_t cache[kKeyCache];  // the row's keys when it fits
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins0];  // histograms; then also the key list
   __shared__ uint32_t tmp[kSelThreads / 64];
   __shared__ uint32_t pick[2];
+  __shared__ uint32_t nlist;
   const int row = blockIdx.x;  // sequence * Hkv + KV head
   const int b = row / a.num_kv_heads;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   int L = a.lengths[b];
   L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
   const int ncand = L - a.recent > 0 ? L - a.recent : 0;
@@ -89,63 +159,23 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
     if (tid == 0) a.counts[row] = ncand < K ? ncand : K;
     return;
   }
-  const bool cached = ncand <= kKeyCache;
-  // key of candidate j: from the LDS cache (filled during the first pass) or from memory
-  auto key_at = [&](int j) -> uint32_t { return cached ? cache[j] : order_key(sc[j]); };
 
-  // ---- radix select of the K-th largest key: digits of 12, 10 and 10 bits ----
-  uint32_t prefix = 0, mask = 0;
-  int rem = K;  // how many of the keys matching `prefix` are still to be chosen
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
-    const int nb = pass == 0 ? kBins0 : kBins;
-    const uint32_t dmask = (uint32_t)nb - 1u;
-    for (int x = tid; x < nb; x += kSelThreads) hist[x] = 0;
-    __syncthreads();
-    if (pass == 0) {
-      // 4 candidates per 16-byte load, 4 loads in flight per thread; scalar head/tail
-      // where the row is not 16-byte aligned
-      const int head = (int)((4 - (((uintptr_t)sc >> 2) & 3)) & 3);
-      const int h = head < ncand ? head : ncand;
-      for (int j = tid; j < h; j += kSelThreads) {
-        const uint32_t u = order_key(sc[j]);
-        if (cached) cache[j] = u;
-        atomicAdd(&hist[u >> 20], 1u);
-      }
-      const int nvec = (ncand - h) >> 2;
-      const u32x4* v4 = reinterpret_cast<const u32x4*>(sc + h);
-      for (int x0 = 0; x0 < nvec; x0 += 4 * kSelThreads) {
-        u32x4 ld[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int x = x0 + e * kSelThreads + tid;
-          ld[e] = x < nvec ? v4[x] : (u32x4){0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int x = x0 + e * kSelThreads + tid;
-          if (x < nvec) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const uint32_t u = order_key(ld[e][c]);
-              if (cached) cache[h + 4 * x + c] = u;
-              atomicAdd(&hist[u >> 20], 1u);
-            }
-          }
-        }
-      }
-      for (int j = h + 4 * nvec + tid; j < ncand; j += kSelThreads) {
-        const uint32_t u = order_key(sc[j]);
-        if (cached) cache[j] = u;
-        atomicAdd(&hist[u >> 20], 1u);
-      }
-    } else {
+  if (ncand > kKeyCache) {
+    // ---- long rows: three histogram passes straight from memory, then the ordered pass ----
+    uint32_t prefix = 0, mask = 0;
+    int rem = K;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
+      const int nb = pass == 0 ? kBins0 : kBins;
+      const uint32_t dmask = (uint32_t)nb - 1u;
+      for (int x = tid; x < nb; x += kSelThreads) hist[x] = 0;
+      __syncthreads();
       for (int j0 = 0; j0 < ncand; j0 += 4 * kSelThreads) {
         uint32_t u[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = j0 + e * kSelThreads + tid;
-          u[e] = j < ncand ? key_at(j) : 0u;
+          u[e] = j < ncand ? order_key(sc[j]) : 0u;
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -153,69 +183,173 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
           if (j < ncand && (u[e] & mask) == prefix) atomicAdd(&hist[(u[e] >> shift) & dmask], 1u);
         }
       }
+      __syncthreads();
+      pick_digit(hist, nb, rem, tmp, pick);
+      prefix |= pick[0] << shift;
+      mask |= dmask << shift;
+      rem = (int)pick[1];
+      __syncthreads();  // pick and hist are rewritten by the next pass
     }
-    __syncthreads();
-    // the digit holding the rem-th largest matching key: thread t owns the `per` bins
-    // just below the top t * per (descending), an inclusive scan over threads counts
-    // the keys at or above each thread's lowest bin
-    {
-      const int per = nb / kSelThreads;  // 8 or 2
-      const int top = nb - 1 - tid * per;
-      uint32_t mine = 0;
-      for (int e = 0; e < per; ++e) mine += hist[top - e];
-      uint32_t tot;
-      const uint32_t incl = block_inclusive_scan(mine, tmp, &tot);
-      uint32_t acc = incl - mine;  // keys in bins above this thread's
-      if (acc < (uint32_t)rem && (uint32_t)rem <= incl) {
-        int d = top;
-        for (int e = 0; e < per; ++e, --d) {
-          const uint32_t hv = hist[d];
-          if (acc + hv >= (uint32_t)rem) break;
-          acc += hv;
+    write_ordered<8>([&](int j0, uint32_t (&k)[8]) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) k[e] = j0 + e < ncand ? order_key(sc[j0 + e]) : 0u;
+    }, ncand, prefix, (uint32_t)rem, out, tmp);
+    if (tid == 0) a.counts[row] = K;
+    return;
+  }
+
+  // ---- pass 0: read the row once (16-byte loads, four in flight per thread), keep its
+  // keys in LDS and histogram their first digit ----
+  for (int x = tid; x < kBins0; x += kSelThreads) hist[x] = 0;
+  __syncthreads();
+  {
+    const int head = (int)((4 - (((uintptr_t)sc >> 2) & 3)) & 3);  // scalar head where the row is unaligned
+    const int h = head < ncand ? head : ncand;
+    for (int j = tid; j < h; j += kSelThreads) {
+      const uint32_t u = order_key(sc[j]);
+      cache[j] = u;
+      atomicAdd(&hist[u >> 20], 1u);
+    }
+    const int nvec = (ncand - h) >> 2;
+    const u32x4* v4 = reinterpret_cast<const u32x4*>(sc + h);
+    for (int x0 = 0; x0 < nvec; x0 += 4 * kSelThreads) {
+      u32x4 ld[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int x = x0 + e * kSelThreads + tid;
+        ld[e] = v4[x < nvec ? x : 0];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int x = x0 + e * kSelThreads + tid;
+        if (x < nvec) {
+          u32x4 k4;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) k4[c] = order_key(ld[e][c]);
+          if (h == 0) {
+            reinterpret_cast<u32x4*>(cache)[x] = k4;
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) cache[h + 4 * x + c] = k4[c];
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c) atomicAdd(&hist[k4[c] >> 20], 1u);
         }
-        pick[0] = (uint32_t)d;
-        pick[1] = (uint32_t)rem - acc;
+      }
+    }
+    for (int j = h + 4 * nvec + tid; j < ncand; j += kSelThreads) {
+      const uint32_t u = order_key(sc[j]);
+      cache[j] = u;
+      atomicAdd(&hist[u >> 20], 1u);
+    }
+    // keys past the row up to a multiple of 32 read as 0 (the NaN key) in the later scans
+    for (int j = ncand + tid; j < ((ncand + 31) & ~31); j += kSelThreads) cache[j] = 0u;
+  }
+  __syncthreads();
+  pick_digit(hist, kBins0, K, tmp, pick);
+  const uint32_t d0 = pick[0];
+  int rem = (int)pick[1];
+  uint32_t T = d0 << 20;
+  const int nv = (ncand + 3) >> 2;
+  const u32x4* cache4 = reinterpret_cast<const u32x4*>(cache);
+  uint32_t* list = hist + kBins;
+  if (d0 != 0) {  // (first digit 0 holds only the NaN key 0: then T = 0 exactly)
+    __syncthreads();  // pick and hist are rewritten below
+    // ---- pass 1: histogram the second digit of the keys in bin d0 and collect those
+    // keys (wavefront ballots reserve their slots) ----
+    for (int x = tid; x < kBins; x += kSelThreads) hist[x] = 0;
+    if (tid == 0) nlist = 0;
+    __syncthreads();
+    for (int x0 = 0; x0 < nv; x0 += kSelThreads) {
+      const int x = x0 + tid;
+      const u32x4 k4 = cache4[x < nv ? x : 0];
+      bool m[4];
+      uint64_t bal[4];
+      uint32_t total = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        m[c] = x < nv && (k4[c] >> 20) == d0;
+        bal[c] = __ballot(m[c]);
+        total += (uint32_t)__popcll(bal[c]);
+        if (m[c]) atomicAdd(&hist[(k4[c] >> 10) & (kBins - 1)], 1u);
+      }
+      if (total != 0) {  // uniform over the wavefront
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&nlist, total);
+        base = __shfl(base, 0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[c] >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal[c], 0u));
+          if (m[c] && base + below < (uint32_t)kList) list[base + below] = k4[c];
+          base += (uint32_t)__popcll(bal[c]);
+        }
       }
     }
     __syncthreads();
-    prefix |= pick[0] << shift;
-    mask |= dmask << shift;
+    pick_digit(hist, kBins, rem, tmp, pick);
+    const uint32_t d1 = pick[0];
     rem = (int)pick[1];
-    __syncthreads();  // pick and hist are rewritten by the next pass
-  }
-  const uint32_t T = prefix;  // the K-th largest key; `rem` of the keys equal to it are taken
-
-  // ---- ordered pass: position of a chosen candidate j = (# above T before j) +
-  // min(# equal to T before j, rem) ----
-  uint32_t gt_run = 0, eq_run = 0;
-  for (int c0 = 0; c0 < ncand; c0 += kSelThreads * kSelPer) {
-    const int j0 = c0 + tid * kSelPer;
-    uint32_t key[kSelPer];
-    uint32_t ngt = 0, neq = 0;
+    const uint32_t n = nlist;
+    __syncthreads();
+    // ---- pass 2: the third digit, over the collected keys (or the whole row when the bin
+    // held more than the list) ----
+    for (int x = tid; x < kBins; x += kSelThreads) hist[x] = 0;
+    __syncthreads();
+    if (n <= (uint32_t)kList) {
+      for (int x = tid; x < (int)n; x += kSelThreads) {
+        const uint32_t u = list[x];
+        if (((u >> 10) & (kBins - 1)) == d1) atomicAdd(&hist[u & (kBins - 1)], 1u);
+      }
+    } else {
+      const uint32_t want = (d0 << 10) | d1;
+      for (int x = tid; x < nv; x += kSelThreads) {
+        const u32x4 k4 = cache4[x];
 #pragma unroll
-    for (int e = 0; e < kSelPer; ++e) {
-      const int j = j0 + e;
-      key[e] = j < ncand ? key_at(j) : 0u;
-      ngt += (j < ncand && key[e] > T) ? 1u : 0u;
-      neq += (j < ncand && key[e] == T) ? 1u : 0u;
+        for (int c = 0; c < 4; ++c)
+          if ((k4[c] >> 10) == want) atomicAdd(&hist[k4[c] & (kBins - 1)], 1u);
+      }
     }
+    __syncthreads();
+    pick_digit(hist, kBins, rem, tmp, pick);
+    T = (d0 << 20) | (d1 << 10) | pick[0];
+    rem = (int)pick[1];
+  }
+
+  // ---- ordered pass over the cached keys: 32 consecutive candidates per thread, one
+  // chunk.  A mask marks the keys at or above T (the padding past ncand is masked off);
+  // the chosen ones, a few per thread, are then visited in increasing position ----
+  {
+    const int j0 = tid * 32;
+    uint32_t gem = 0, ngt = 0;
+    if (j0 < ncand) {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const u32x4 k4 = cache4[(j0 >> 2) + v];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          gem |= (k4[c] >= T ? 1u : 0u) << (4 * v + c);
+          ngt += k4[c] > T ? 1u : 0u;  // the zero padding is never above T
+        }
+      }
+      if (ncand - j0 < 32) gem &= (1u << (ncand - j0)) - 1u;
+    }
+    const uint32_t neq = (uint32_t)__builtin_popcount(gem) - ngt;
     uint32_t tot;
     const uint32_t incl = block_inclusive_scan((ngt << 16) | neq, tmp, &tot);
-    uint32_t gt_b = gt_run + ((incl >> 16) - ngt), eq_b = eq_run + ((incl & 0xffffu) - neq);
-#pragma unroll
-    for (int e = 0; e < kSelPer; ++e) {
+    uint32_t gt_b = (incl >> 16) - ngt, eq_b = (incl & 0xffffu) - neq;
+    while (gem != 0) {
+      const int e = __builtin_ctz(gem);
+      gem &= gem - 1u;
       const int j = j0 + e;
-      if (j >= ncand) break;
-      if (key[e] > T) {
+      if (cache[j] > T) {
         out[gt_b + min(eq_b, (uint32_t)rem)] = j;
         ++gt_b;
-      } else if (key[e] == T) {
+      } else {
         if (eq_b < (uint32_t)rem) out[gt_b + eq_b] = j;
         ++eq_b;
       }
     }
-    gt_run += tot >> 16;
-    eq_run += tot & 0xffffu;
   }
   if (tid == 0) a.counts[row] = K;
 }

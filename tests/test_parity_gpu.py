@@ -1140,7 +1140,8 @@ def _topk_gpu(scores, lengths, k, recent):
 
 @pytest.mark.parametrize("case", [(6, 3, 5000, 1024, 128, "normal"), (5, 2, 3000, 300, 7, "ties"),
                                   (4, 4, 9000, 64, 128, "few"), (3, 2, 700, 1024, 128, "short"),
-                                  (4, 2, 2000, 0, 128, "k0"), (3, 2, 4100, 500, 16, "special")],
+                                  (4, 2, 2000, 0, 128, "k0"), (3, 2, 4100, 500, 16, "special"),
+                                  (3, 2, 9000, 1024, 128, "two"), (2, 2, 40000, 1024, 128, "normal")],
                          ids=lambda c: f"B{c[0]}-kv{c[1]}-L{c[2]}-k{c[3]}-r{c[4]}-{c[5]}")
 def test_topk_select_exact(case):
     b, hkv, lmax, k, recent, kind = case
@@ -1149,6 +1150,8 @@ def test_topk_select_exact(case):
     scores = torch.randn(b, hkv, lmax, generator=gen)
     if kind == "ties":  # a handful of distinct values: most ranks are decided by position
         scores = torch.randint(0, 4, (b, hkv, lmax), generator=gen).float() * 0.25
+    if kind == "two":  # two values: the threshold's first-digit bin holds thousands of keys
+        scores = torch.randint(0, 2, (b, hkv, lmax), generator=gen).float() * 0.5
     if kind == "few":  # values equal to the threshold straddle chunk boundaries
         scores = torch.randint(0, 40, (b, hkv, lmax), generator=gen).float()
     if kind == "special":  # NaN ranks below every number (numpy's sort puts it last too); +-inf; -0.0
