@@ -14,7 +14,7 @@
 // and dv per key row, one wavefront per row; (4) dsink per head by a two-pass
 // fixed-order reduction (deterministic: no atomics anywhere).  For bf16, head_dim
 // 128, windows up to 128 and groups of 8k heads, the matrix-core kernels replace
-// (2) and (3).
+// (1), (2) and (3): their dq kernel forms delta and the sink terms of the rows it owns.
 #include "common.h"
 #include "kernels.h"
 
@@ -218,8 +218,17 @@ __global__ __launch_bounds__(kSinkThreads) void bwd_sink_chunk_kernel(BackwardAr
   if (h >= a.num_q_heads) return;
   const long n0 = (long)blockIdx.x * kSinkChunk;
   const long n1 = min(n0 + kSinkChunk, (long)a.total_tokens);
+  // every load issued before the first add (rows past the stream read its last row and
+  // count as 0), then the sum in row order
+  float v[kSinkChunk];
+#pragma unroll
+  for (int k = 0; k < kSinkChunk; ++k) {
+    const long n = n0 + k < n1 ? n0 + k : n1 - 1;
+    v[k] = a.sink_term[n * a.num_q_heads + h];
+  }
   float acc = 0.f;
-  for (long n = n0; n < n1; ++n) acc += a.sink_term[n * a.num_q_heads + h];
+#pragma unroll
+  for (int k = 0; k < kSinkChunk; ++k) acc += n0 + k < n1 ? v[k] : 0.f;
   a.sink_term[n0 * a.num_q_heads + h] = acc;
 }
 __global__ __launch_bounds__(kSinkThreads) void bwd_dsink_kernel(BackwardArgs a) {
@@ -227,6 +236,7 @@ __global__ __launch_bounds__(kSinkThreads) void bwd_dsink_kernel(BackwardArgs a)
   const int h = blockIdx.x;
   const long nchunks = ((long)a.total_tokens + kSinkChunk - 1) / kSinkChunk;
   float acc = 0.f;
+#pragma unroll 8
   for (long c = threadIdx.x; c < nchunks; c += kSinkThreads)
     acc += a.sink_term[c * kSinkChunk * a.num_q_heads + h];
   part[threadIdx.x] = acc;
@@ -250,16 +260,19 @@ hipError_t launch_t(const BackwardArgs& a, bool kMfma, hipStream_t s) {
   if (qblocks > 0x7fffffffL || kblocks > 0x7fffffffL || nchunks > 0x7fffffffL || hgroups > 0xffff)
     return hipErrorInvalidConfiguration;
   if (qrows > 0) {  // an empty stream only writes zero sink gradients
-    hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)pblocks), dim3(kPrepThreads), 0, s, a);
-    if (a.dsinks != nullptr)
-      hipLaunchKernelGGL(bwd_sink_chunk_kernel, dim3((unsigned)nchunks, (unsigned)hgroups), dim3(kSinkThreads),
-                         0, s, a);
     if (kMfma) {
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
+      // the matrix-core dq kernel forms delta and the sink terms itself (it reads dO
+      // and, for this, O), before the dk/dv kernel reads them
       const hipError_t m = launch_backward_mfma(a, s);
       if (m != hipSuccess) return m;
+      if (a.dsinks != nullptr)
+        hipLaunchKernelGGL(bwd_sink_chunk_kernel, dim3((unsigned)nchunks, (unsigned)hgroups),
+                           dim3(kSinkThreads), 0, s, a);
     } else {
+      hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)pblocks), dim3(kPrepThreads), 0, s, a);
+      if (a.dsinks != nullptr)
+        hipLaunchKernelGGL(bwd_sink_chunk_kernel, dim3((unsigned)nchunks, (unsigned)hgroups),
+                           dim3(kSinkThreads), 0, s, a);
       hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((unsigned)qblocks), dim3(kRows * kWave), 0, s, a);
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3((unsigned)kblocks), dim3(kRows * kWave), 0, s, a);
     }

@@ -13,7 +13,9 @@
 //  * bwd_dq_ring_kernel: the forward's decomposition -- a workgroup owns 16 query
 //    tokens x 8 heads sharing one KV head (one head per wavefront), the 144-key band
 //    sits in an LDS ring that advances by 16 keys per tile.  S^T = K Q^T and dP^T = V dO^T come out with
-//    queries in columns, so dS^T feeds dQ^T = K^T dS^T straight from registers.
+//    queries in columns, so dS^T feeds dQ^T = K^T dS^T straight from registers.  It
+//    also forms delta = dO . O of its rows (reading O beside dO) and writes it, with
+//    the sink's term, for the dk/dv kernel and the sink gradient.
 //  * bwd_dkdv_kernel: the transpose -- a workgroup owns 64 keys of one KV head (16
 //    per wavefront) and walks the (head quad, query block) steps that see them, one
 //    LDS-staged block of 16 tokens x 4 heads per step shared by the four wavefronts.
@@ -164,6 +166,7 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
   const bf16* vp = static_cast<const bf16*>(a.v);
   const bf16* qp = static_cast<const bf16*>(a.q);
   const bf16* dop = static_cast<const bf16*>(a.dout);
+  const bf16* op = static_cast<const bf16*>(a.out);
   const float c = a.scale * kLog2e;
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
@@ -171,12 +174,12 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
   const int vrow = 8 * (g & 1) + (i >> 2);                  // key row of the transposed reads, pairs
   const int vrow8 = 8 * (g & 1) + 4 * (g >> 1) + (i >> 2);  // the single diagonal block
 
-  // Q and dO of one tile (lane (i, g): head-dim 32cc + 8g .. +8 of query q0 + i, head w
-  // of the octet) with the row's lse and delta.  Rows past the stream are loaded from
-  // the last token (their results are never stored), so the loads are unconditional
-  // and nothing waits for them before their first use.
-  bf16x8 qa[4], da[4];
-  float lr, dlr;
+  // Q, dO and O of one tile (lane (i, g): head-dim 32cc + 8g .. +8 of query q0 + i,
+  // head w of the octet) with the row's lse.  Rows past the stream are loaded from the
+  // last token (their results are never stored), so the loads are unconditional and
+  // nothing waits for them before their first use.
+  bf16x8 qa[4], da[4], oa[4];
+  float lr;
   auto load_rows = [&](int q0n, int octn) {
     const int qi = min(q0n + i, N - 1);
     const size_t hr = (size_t)qi * Hq + octn * kHG + w;
@@ -185,9 +188,9 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
     for (int cc = 0; cc < 4; ++cc) {
       qa[cc] = *reinterpret_cast<const bf16x8*>(qp + r0 + 32 * cc);
       da[cc] = *reinterpret_cast<const bf16x8*>(dop + r0 + 32 * cc);
+      oa[cc] = *reinterpret_cast<const bf16x8*>(op + r0 + 32 * cc);
     }
     lr = a.lse[hr];
-    dlr = a.delta[hr];
   };
 
   while (down ? item >= item_lo : item < item_hi) {
@@ -232,7 +235,21 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
       const int lo = lw > start ? (int)lw : start;
       const int rel_lo = lo - kbase;
       const unsigned span = (unsigned)(qi - kbase - rel_lo);
-      const float l2 = lr * kLog2e, dl = dlr;
+      const float l2 = lr * kLog2e;
+      // delta = dO . O of the lane's row: 32 elements per lane, then the row's 4 lanes;
+      // written once (with the sink's term) for the dk/dv kernel and the sink gradient
+      float dl = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dl = fmaf((float)oa[cc][e], (float)da[cc][e], dl);
+      dl += __shfl_xor(dl, 16);
+      dl += __shfl_xor(dl, 32);
+      if (g == 0 && qi < N) {
+        const size_t hr = (size_t)qi * Hq + h0;
+        a.delta[hr] = dl;
+        if (a.sinks) a.sink_term[hr] = expf(a.sinks[h0] - lr) * dl;
+      }
 
       // ---- per 16-key block: S^T = K Q^T, dP^T = V dO^T, then dS^T in bf16 ----
       bf16x8 sa[4];
