@@ -290,12 +290,16 @@ def _topk_fn():
     import sliding_window_attention_amd as swa
 
     lib = swa.library()
+    cache = {}
 
     def fn(x):
-        b, hkv, lmax = x["scores"].shape
-        rc = lib.swa_topk_select(x["scores"].data_ptr(), x["lengths"].data_ptr(), b, hkv, lmax,
-                                 x["indices"].shape[2], swa.SPARSE_RECENT, x["indices"].data_ptr(),
-                                 x["counts"].data_ptr(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        key = id(x)
+        if key not in cache:
+            b, hkv, lmax = x["scores"].shape
+            cache[key] = (x["scores"].data_ptr(), x["lengths"].data_ptr(), b, hkv, lmax, x["indices"].shape[2],
+                          swa.SPARSE_RECENT, x["indices"].data_ptr(), x["counts"].data_ptr(),
+                          ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        rc = lib.swa_topk_select(*cache[key])
         if rc != 0:
             raise RuntimeError(lib.swa_last_error().decode())
     return fn
@@ -310,15 +314,19 @@ def _sparse_fn():
     import sliding_window_attention_amd as swa
 
     lib = swa.library()
+    cache = {}
 
     def fn(x):
-        b, hq, d = x["q"].shape
-        hkv, lmax = x["k_cache"].shape[1], x["k_cache"].shape[2]
-        rc = lib.swa_sparse_decode(x["q"].data_ptr(), x["k_cache"].data_ptr(), x["v_cache"].data_ptr(),
-                                   x["lengths"].data_ptr(), x["indices"].data_ptr(), x["counts"].data_ptr(),
-                                   None, b, hq, hkv, d, lmax, x["indices"].shape[2], swa.SPARSE_RECENT, 0.0, 1,
-                                   x["out"].data_ptr(), x["lse"].data_ptr(),
-                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        key = id(x)
+        if key not in cache:
+            b, hq, d = x["q"].shape
+            hkv, lmax = x["k_cache"].shape[1], x["k_cache"].shape[2]
+            cache[key] = (x["q"].data_ptr(), x["k_cache"].data_ptr(), x["v_cache"].data_ptr(),
+                          x["lengths"].data_ptr(), x["indices"].data_ptr(), x["counts"].data_ptr(),
+                          None, b, hq, hkv, d, lmax, x["indices"].shape[2], swa.SPARSE_RECENT, 0.0, 1,
+                          x["out"].data_ptr(), x["lse"].data_ptr(),
+                          ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        rc = lib.swa_sparse_decode(*cache[key])
         if rc != 0:
             raise RuntimeError(lib.swa_last_error().decode())
     return fn

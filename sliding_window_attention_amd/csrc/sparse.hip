@@ -69,6 +69,7 @@ constexpr int kKeyCache = 32768;  // candidates whose keys are kept in LDS (128 
 constexpr int kBins0 = 4096;       // first digit: bits 31..20 (sign, exponent, 3 mantissa bits)
 constexpr int kBins = 1024;        // next digits: bits 19..10 and 9..0
 constexpr int kList = kBins0 - kBins;  // keys of the threshold's first-digit bin kept after pass 0
+constexpr int kPerWave = kList / (kSelThreads / 64);  // the part of the list each wavefront fills
 
 // The digit holding the rem-th largest of the keys counted in hist[0, nb): thread t owns
 // the nb / 1024 bins just below the top t * per (descending), and an inclusive scan over
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[kBins0];  // histograms; then also the key list
   __shared__ uint32_t tmp[kSelThreads / 64];
   __shared__ uint32_t pick[2];
-  __shared__ uint32_t nlist;
+  __shared__ uint32_t wcount[kSelThreads / 64];  // keys of the threshold's bin found per wavefront
   const int row = blockIdx.x;  // sequence * Hkv + KV head
   const int b = row / a.num_kv_heads;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -256,50 +257,47 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   if (d0 != 0) {  // (first digit 0 holds only the NaN key 0: then T = 0 exactly)
     __syncthreads();  // pick and hist are rewritten below
     // ---- pass 1: histogram the second digit of the keys in bin d0 and collect those
-    // keys (wavefront ballots reserve their slots) ----
+    // keys, each wavefront into its own part of the list (no shared counter) ----
     for (int x = tid; x < kBins; x += kSelThreads) hist[x] = 0;
-    if (tid == 0) nlist = 0;
     __syncthreads();
+    const int wv = tid >> 6;
+    uint32_t wn = 0;  // keys this wavefront has found (uniform over the wavefront)
     for (int x0 = 0; x0 < nv; x0 += kSelThreads) {
       const int x = x0 + tid;
       const u32x4 k4 = cache4[x < nv ? x : 0];
-      bool m[4];
-      uint64_t bal[4];
-      uint32_t total = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        m[c] = x < nv && (k4[c] >> 20) == d0;
-        bal[c] = __ballot(m[c]);
-        total += (uint32_t)__popcll(bal[c]);
-        if (m[c]) atomicAdd(&hist[(k4[c] >> 10) & (kBins - 1)], 1u);
-      }
-      if (total != 0) {  // uniform over the wavefront
-        uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&nlist, total);
-        base = __shfl(base, 0);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[c] >> 32),
-                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal[c], 0u));
-          if (m[c] && base + below < (uint32_t)kList) list[base + below] = k4[c];
-          base += (uint32_t)__popcll(bal[c]);
+        const bool m = x < nv && (k4[c] >> 20) == d0;
+        const uint64_t bal = __ballot(m);
+        if (m) {
+          atomicAdd(&hist[(k4[c] >> 10) & (kBins - 1)], 1u);
+          const uint32_t slot = wn + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+          if (slot < (uint32_t)kPerWave) list[wv * kPerWave + slot] = k4[c];
         }
+        wn += (uint32_t)__popcll(bal);
       }
     }
+    if (lane == 0) wcount[wv] = wn;
     __syncthreads();
     pick_digit(hist, kBins, rem, tmp, pick);
     const uint32_t d1 = pick[0];
     rem = (int)pick[1];
-    const uint32_t n = nlist;
+    bool fits = true;
+#pragma unroll
+    for (int v = 0; v < kSelThreads / 64; ++v) fits = fits && wcount[v] <= (uint32_t)kPerWave;
     __syncthreads();
-    // ---- pass 2: the third digit, over the collected keys (or the whole row when the bin
-    // held more than the list) ----
+    // ---- pass 2: the third digit, over the collected keys (or the whole row when a
+    // wavefront found more than its part of the list holds) ----
     for (int x = tid; x < kBins; x += kSelThreads) hist[x] = 0;
     __syncthreads();
-    if (n <= (uint32_t)kList) {
-      for (int x = tid; x < (int)n; x += kSelThreads) {
-        const uint32_t u = list[x];
-        if (((u >> 10) & (kBins - 1)) == d1) atomicAdd(&hist[u & (kBins - 1)], 1u);
+    if (fits) {
+      for (int e = tid; e < kList; e += kSelThreads) {
+        const int v = e / kPerWave, idx = e - v * kPerWave;
+        if ((uint32_t)idx < wcount[v]) {
+          const uint32_t u = list[e];
+          if (((u >> 10) & (kBins - 1)) == d1) atomicAdd(&hist[u & (kBins - 1)], 1u);
+        }
       }
     } else {
       const uint32_t want = (d0 << 10) | d1;
