@@ -847,7 +847,8 @@ def test_decode_rope_base_zero_is_plain_decode():
 
 
 @pytest.mark.parametrize("case", [(16, 4, 4, 128, 128, "bf16", 10000.0), (9, 3, 2, 64, 32, "f32", 640000.0),
-                                  (5, 2, 1, 128, 128, "bf16", 0.0)],
+                                  (5, 2, 1, 128, 128, "bf16", 0.0),
+                                  (6, 12, 2, 128, 128, "bf16", 10000.0)],  # T > 8: angles per element
                          ids=lambda c: f"B{c[0]}-T{c[1]}-kv{c[2]}-D{c[3]}-W{c[4]}-{c[5]}-base{c[6]:g}")
 def test_ring_append(case):
     b, t_new, hkv, d, w, dt, base = case
@@ -1035,7 +1036,8 @@ def _written(ring_head, n_acc, b, t_new, w, shape):
 @pytest.mark.parametrize("case", [(16, 4, 4, 128, 128, "bf16", 0.0, 1 / 32, 1 / 64),
                                   (16, 4, 4, 128, 128, "bf16", 10000.0, 0.0173, 0.0311),
                                   (9, 3, 2, 64, 32, "f32", 640000.0, 0.0173, 0.0311),
-                                  (7, 2, 1, 128, 128, "f32", 0.0, 0.0173, 0.0311)],
+                                  (7, 2, 1, 128, 128, "f32", 0.0, 0.0173, 0.0311),
+                                  (6, 12, 2, 128, 128, "bf16", 10000.0, 0.0173, 0.0311)],
                          ids=lambda c: f"B{c[0]}-T{c[1]}-kv{c[2]}-D{c[3]}-W{c[4]}-{c[5]}-base{c[6]:g}-s{c[7]:g}")
 def test_ring_append_fp8kv(case):
     """Codes written to an FP8 ring: bit-exact against the oracle's encoding where the keys
