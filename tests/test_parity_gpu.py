@@ -1143,7 +1143,8 @@ def _topk_gpu(scores, lengths, k, recent):
 @pytest.mark.parametrize("case", [(6, 3, 5000, 1024, 128, "normal"), (5, 2, 3000, 300, 7, "ties"),
                                   (4, 4, 9000, 64, 128, "few"), (3, 2, 700, 1024, 128, "short"),
                                   (4, 2, 2000, 0, 128, "k0"), (3, 2, 4100, 500, 16, "special"),
-                                  (3, 2, 9000, 1024, 128, "two"), (2, 2, 40000, 1024, 128, "normal")],
+                                  (3, 2, 9000, 1024, 128, "two"), (2, 2, 40000, 1024, 128, "normal"),
+                                  (4, 3, 3001, 256, 64, "normal")],  # rows at every 4-byte alignment
                          ids=lambda c: f"B{c[0]}-kv{c[1]}-L{c[2]}-k{c[3]}-r{c[4]}-{c[5]}")
 def test_topk_select_exact(case):
     b, hkv, lmax, k, recent, kind = case
