@@ -237,7 +237,9 @@ SWASINK_API int swa_sink_decode_rope(const void* q, const void* k_new, const voi
                     void* stream);
 
 /*
- * swa_sink_decode_rope against an FP8 ring: q and k_new arrive unrotated and are
+ * swa_sink_decode_rope against an FP8 ring (RoPE: technical report digest, section
+ * 3.1; FP8 (E4M3) KV cache: MiMo-V2 blog, section 6, and the MiMo-V3 / HySparse2
+ * report): q and k_new arrive unrotated and are
  * rotated in the kernel as in swa_sink_decode_rope; the caches hold E4M3 codes with
  * per-tensor scales as in swa_sink_decode_fp8kv (keys rotated at their own positions
  * before they were encoded: swa_ring_append_fp8kv writes them so).
@@ -279,7 +281,10 @@ SWASINK_API int swa_ring_append_rope(const void* k_new, const void* v_new, const
 
 /*
  * swa_ring_append_rope into an FP8 ring (the E4M3 caches swa_sink_decode_fp8kv
- * reads): the same slots, head update, clamping and rotation, but each committed
+ * reads: the FP8 (E4M3) format of the MiMo-V2 blog, section 6, for the KV cache whose
+ * FP8 sizes the MiMo-V3 / HySparse2 report quotes; the pages give no rounding, so the
+ * one below is the usual one of a rounding conversion, with saturation as FP8 caches
+ * are commonly filled): the same slots, head update, clamping and rotation, but each committed
  * element x -- the rotated key rounded to dtype, or the value as given -- is stored as
  * the E4M3 code of x / k_scale (keys) or x / v_scale (values): the exact quotient
  * rounded once to the nearest E4M3 value, ties to the even mantissa, finite
