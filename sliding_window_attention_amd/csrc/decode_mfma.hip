@@ -95,7 +95,7 @@ __device__ __forceinline__ void add_partial(const char (*slot)[kColBytes], int i
 // registers, exactly); the K scale joins the ring logits' multiplier and the V scale
 // multiplies the ring weights as they are packed for P*V (the running sums stay
 // unscaled), so no cache element is ever rescaled.
-// ROPE: q and the new keys arrive unrotated and are rotated in LDS after staging.
+// ROPE: q and the new keys arrive unrotated and are rotated in registers as they are staged.
 template <int NT, bool FP8, bool ROPE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void decode_kernel(DecodeArgs a) {
@@ -164,10 +164,36 @@ void decode_kernel(DecodeArgs a) {
   {
     if constexpr (ROPE) {
       // the rotary cos/sin table (token, pair) is formed while the loads are in
-      // flight (it depends on the position only)
+      // flight (it depends on the position only); then each staged 8-element piece of
+      // a query column or new-key row is rotated in registers before it is written:
+      // element i pairs with i + 64, i.e. piece uu with piece uu ^ 8 of the same row,
+      // which sits in the lane 8 away within the 16-lane row (a DPP row rotation by 8)
       const int pos0 = as_const(a.rope_pos)[b];
       for (int x = tid; x < T * 64; x += kThreads)
         rope_cos_sin(pos0 + (x >> 6), x & 63, D, a.rope_log2_base, &sm.u.in.cs[x][0], &sm.u.in.cs[x][1]);
+      __syncthreads();  // the table is complete
+      const bool first = (tid & 8) == 0;  // this lane holds x[i], the partner x[i + 64]
+      auto rotate = [&](u32x4 v4, int t) -> u32x4 {
+        u32x4 p4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          p4[j] = (uint32_t)__builtin_amdgcn_mov_dpp((int)v4[j], 0x128, 0xf, 0xf, false);  // row_ror:8
+        const bf16x8 me = __builtin_bit_cast(bf16x8, v4), pa = __builtin_bit_cast(bf16x8, p4);
+        bf16x8 y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float c = sm.u.in.cs[t * 64 + 8 * (tid & 7) + e][0];
+          const float sn = sm.u.in.cs[t * 64 + 8 * (tid & 7) + e][1];
+          y[e] = first ? (bf16)((float)me[e] * c - (float)pa[e] * sn) : (bf16)((float)me[e] * c + (float)pa[e] * sn);
+        }
+        return __builtin_bit_cast(u32x4, y);
+      };
+#pragma unroll
+      for (int k = 0; k < NT; ++k) {
+        const int col = (k * kThreads + tid) >> 4;
+        st[k] = rotate(st[k], min(col >> 3, T - 1));
+      }
+      st[NT] = rotate(st[NT], nrow);
     }
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
@@ -181,31 +207,6 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) tcol[tt] = 2 * tt + (i >> 3);
   __syncthreads();
-  if constexpr (ROPE) {
-    // Rotary embedding of the staged query columns and new keys (they arrive
-    // unrotated; the ring's keys were rotated when they were appended): one pass over
-    // (row, group of 8 pairs) with the cos/sin table formed during staging, rounding
-    // back to bf16 in place.
-    const int nq = T * kHG;  // query columns col = token * 8 + head
-    for (int x = tid; x < (nq + T) * 8; x += kThreads) {
-      const int r = x >> 3, gi = x & 7;
-      char* row = r < nq ? sm.u.in.q[r] : sm.u.in.kn[r - nq];
-      const int t = r < nq ? r >> 3 : r - nq;
-      bf16x8* lo = reinterpret_cast<bf16x8*>(row + 16 * gi);
-      bf16x8* hi = reinterpret_cast<bf16x8*>(row + 128 + 16 * gi);
-      const bf16x8 u = *lo, v = *hi;
-      bf16x8 yu, yv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float c = sm.u.in.cs[t * 64 + 8 * gi + e][0], sn = sm.u.in.cs[t * 64 + 8 * gi + e][1];
-        yu[e] = (bf16)((float)u[e] * c - (float)v[e] * sn);
-        yv[e] = (bf16)((float)v[e] * c + (float)u[e] * sn);
-      }
-      *lo = yu;
-      *hi = yv;
-    }
-    __syncthreads();
-  }
   // B operand (Q^T) of tile tt, head-dim chunk cc: column tt*16 + i, unit 4cc + g
   auto qop = [&](int tt, int cc) {
     return *reinterpret_cast<const bf16x8*>(&sm.u.in.q[tt * 16 + i][16 * (4 * cc + g)]);
