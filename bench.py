@@ -252,26 +252,29 @@ def _decode_rope_fp8_fn():
     return fn
 
 
-def _rope_inputs(dev):
-    """The 32K layer's Q (seeded like the prefill workload) and positions 0..32767."""
+def _rope_inputs(dev, nsets=1):
+    """The 32K layer's Q (seeded like the prefill workload) and positions 0..32767, as
+    `nsets` distinct copies of Q (268 MB each) sharing the positions."""
     import torch
 
     from sliding_window_attention_amd import workloads as wl
 
     x = _to(wl.make_workload(PRIMARY), dev)
-    return {"q": x["q"], "positions": torch.arange(32768, dtype=torch.int32, device=dev)}
+    pos = torch.arange(32768, dtype=torch.int32, device=dev)
+    return [{"q": x["q"] if i == 0 else x["q"].clone(), "positions": pos} for i in range(nsets)]
 
 
-def _sparse_inputs(dev):
+def _sparse_inputs(dev, set_index=0):
     """The sparse_b64 workload drawn on the GPU (64 sequences, [64, 4, 32768, 128] caches)
-    with its selection, indices and counts allocated."""
+    with its selection, indices and counts allocated.  set_index > 0 draws another set of
+    the same shape (seed offset), for rotation past the Infinity Cache."""
     import torch
 
     from sliding_window_attention_amd import workloads as wl
 
     w = wl.WORKLOADS["sparse_b64"]
-    x = wl.make_sparse_device(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.seq_len, w.seed, dev,
-                              min_len=w.extra["min_len"])
+    x = wl.make_sparse_device(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.seq_len,
+                              w.seed + 7919 * set_index, dev, min_len=w.extra["min_len"])
     x["lengths_host"] = x["lengths"]
     x["lengths"] = x["lengths"].to(dev)
     x["indices"] = torch.empty((w.batch, w.num_kv_heads, w.extra["topk"]), dtype=torch.int32, device=dev)
@@ -355,6 +358,45 @@ def _append_inputs(dev, fp8=False):
     x["n_accept"] = torch.randint(0, 5, (x["q"].shape[0],), generator=gen,
                                   dtype=torch.int64).to(torch.int32).to(dev)
     return x
+
+
+MTP_SETS = 8     # 8 x ~88 MB (decode T = 4 inputs + ring) per MTP-step rotation
+SPARSE_SETS = 4  # 4 x 153 MB of gathered K/V rows (each set has its own 4 GB caches)
+TOPK_SETS = 16   # 16 x 24.5 MB of candidate scores
+
+
+def _mtp_sets(dev, fp8):
+    """Distinct copies of the MTP-step inputs (each with its own ring, ring heads and
+    outputs), rotated so that no step finds its ring in the Infinity Cache."""
+    x = _with_outputs(_append_inputs(dev, fp8), "decode")
+    sets = [x]
+    for _ in range(MTP_SETS - 1):
+        sets.append({k: (v.clone() if hasattr(v, "clone") else v) for k, v in x.items()})
+    return sets
+
+
+def _sparse_sets(dev, what):
+    """Input sets for the sparse legs: the selection rotates over TOPK_SETS copies of the
+    scores (sharing one workload's caches), the sparse decode over SPARSE_SETS workloads
+    drawn with different seeds, each selected once beforehand."""
+    import torch
+
+    if what == "topk":
+        x = _sparse_inputs(dev)
+        sets = [x]
+        for _ in range(TOPK_SETS - 1):
+            y = dict(x)
+            y["scores"] = x["scores"].clone()
+            y["indices"] = torch.empty_like(x["indices"])
+            y["counts"] = torch.empty_like(x["counts"])
+            sets.append(y)
+        return sets
+    sets = []
+    for i in range(SPARSE_SETS):
+        x = _sparse_inputs(dev, i)
+        _topk_fn()(x)
+        sets.append(x)
+    return sets
 
 
 def _append_fn(fp8=False):
@@ -555,7 +597,7 @@ def cpu_baseline(sample_tokens=32768):
     flops = wl.prefill_flops([sample_tokens], 32, 128, 128)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{sample_tokens} of 32768 tokens of the layer (all 32 heads), fp64 numpy, {dt:.2f} s",
-            "seconds": dt}
+            "seconds": dt, "blas_threads": int(threads), "affinity_cores": len(os.sched_getaffinity(0))}
 
 
 def main(argv=None):
@@ -600,7 +642,7 @@ def main(argv=None):
         return 0
     if args.only == "backward":
         x = _backward_inputs(dev)
-        per, _ = _time_calls(_backward_fn(), [x], max(3, steps), warmup, per_call=False)
+        per, _ = _time_calls(_backward_fn(), [x], max(20, steps), max(3, warmup), per_call=False)
         st = _stats(per)
         fl = wl.backward_flops([32768], 32, 128, 128)
         by = wl.backward_bytes(32768, 32, 4, 128, 2)
@@ -611,7 +653,8 @@ def main(argv=None):
         # append alone is launch-bound from this loop (a ~4 us kernel); in a decode loop it
         # is queued behind the verify kernel, which "mtp_step" times
         fp8 = args.only.endswith("fp8")
-        x = _with_outputs(_append_inputs(dev, fp8), "decode")
+        xs = _mtp_sets(dev, fp8)
+        x = xs[0]
         app_fn = _append_fn(fp8)
         if args.only.startswith("append"):
             fn = app_fn
@@ -621,24 +664,22 @@ def main(argv=None):
             def fn(x_):
                 dec_fn(x_)
                 app_fn(x_)
-        per, _ = _time_calls(fn, [x], max(steps, 200), warmup, per_call=False)
+        per, _ = _time_calls(fn, xs, max(steps, 200), warmup, per_call=False)
         st = _stats(per)
         by = wl.append_bytes(256, int(x["n_accept"].sum()), 4, 128, 2, cache_elem_bytes=1 if fp8 else None)
         _log(f"{args.only} B=256 T=4: {st}  (append bytes {by})")
         return 0
     if args.only in ("topk", "sparse"):
-        x = _sparse_inputs(dev)
-        _topk_fn()(x)
+        xs = _sparse_sets(dev, args.only)
         fn = _topk_fn() if args.only == "topk" else _sparse_fn()
-        per, _ = _time_calls(fn, [x], max(steps, 100), warmup, per_call=False)
+        per, _ = _time_calls(fn, xs, max(steps, 100), warmup, per_call=False)
         st = _stats(per)
-        tb, sb, sfl = _sparse_work(x)
+        tb, sb, sfl = _sparse_work(xs[0])
         by = tb if args.only == "topk" else sb
         _log(f"{args.only} sparse_b64: {st}  {by / (st['mean_ms'] * 1e-3) / 1e9:.0f} GB/s ({by} bytes)")
         return 0
     if args.only == "rope":
-        x = _rope_inputs(dev)
-        per, _ = _time_calls(_rope_fn(), [x], steps, warmup, per_call=False)
+        per, _ = _time_calls(_rope_fn(), _rope_inputs(dev, 4), steps, warmup, per_call=False)
         st = _stats(per)
         by = wl.rope_bytes(32768, 32, 128, 2)
         _log(f"rope q 32K: {st}  {by / (st['mean_ms'] * 1e-3) / 1e9:.0f} GB/s")
@@ -664,6 +705,8 @@ def main(argv=None):
         else:
             fn = _decode_fn() if dec else _prefill_fn(128, ga=args.only == "ga")
         nsets = 32 if dec else (1 if args.only in ("varlen", "ga") else 4)
+        if args.only in ("varlen", "ga"):
+            steps, warmup = max(steps, 20), max(warmup, 3)
         per, _ = _time_calls(fn, _clone_sets(x, nsets), steps, warmup, per_call=not dec)
         fl, by = wl.workload_work(name)
         if args.only == "ga":
@@ -776,14 +819,15 @@ def run_extra(dev, steps, warmup):
     for fp8 in (False, True):
         ring = "an FP8" if fp8 else "a bf16"
         _log(f"MTP step: verify T = 4 with RoPE against {ring} ring, then commit the accepted tokens (B = 256)")
-        x = _with_outputs(_append_inputs(dev, fp8), "decode")
+        xs = _mtp_sets(dev, fp8)
+        x = xs[0]
         dec_fn = _decode_rope_fp8_fn() if fp8 else _decode_rope_fn()
         app_fn = _append_fn(fp8)
 
         def step(x_):
             dec_fn(x_)
             app_fn(x_)
-        per, _ = _time_calls(step, [x], max(200, steps), warmup, per_call=False)
+        per, _ = _time_calls(step, xs, max(200, steps), warmup, per_call=False)
         st = _stats(per)
         fl, by_dec = wl.workload_work("decode_rope_fp8_t4" if fp8 else "decode_rope_t4")
         by = by_dec + wl.append_bytes(256, int(x["n_accept"].sum()), 4, 128, 2,
@@ -792,30 +836,35 @@ def run_extra(dev, steps, warmup):
                 else "swa_sink_decode_rope (T=4) + swa_ring_append_rope per step")
         extra["mtp_step_rope_fp8_t4" if fp8 else "mtp_step_rope_t4"] = {
             **st, "gbps": by / (st["mean_ms"] * 1e-3) / 1e9, "bytes": by,
-            "accepted_tokens": int(x["n_accept"].sum()), "what": what}
-        del x
+            "accepted_tokens": int(x["n_accept"].sum()), "what": what, "sets": len(xs)}
+        del x, xs
+        torch.cuda.empty_cache()
     _log("sparse attention: top-k selection and sparse decode, 64 sequences of 16K-32K tokens")
-    x = _sparse_inputs(dev)
-    tb, sb, sfl = _sparse_work(x)
-    per, _ = _time_calls(_topk_fn(), [x], max(100, steps), warmup, per_call=False)
+    xs = _sparse_sets(dev, "topk")
+    tb, sb, sfl = _sparse_work(xs[0])
+    per, _ = _time_calls(_topk_fn(), xs, max(100, steps), warmup, per_call=False)
     st = _stats(per)
-    extra["topk_select_b64"] = {**st, "gbps": tb / (st["mean_ms"] * 1e-3) / 1e9, "bytes": tb}
-    per, _ = _time_calls(_sparse_fn(), [x], max(100, steps), warmup, per_call=False)
+    extra["topk_select_b64"] = {**st, "gbps": tb / (st["mean_ms"] * 1e-3) / 1e9, "bytes": tb, "sets": len(xs)}
+    del xs
+    torch.cuda.empty_cache()
+    xs = _sparse_sets(dev, "sparse")
+    per, _ = _time_calls(_sparse_fn(), xs, max(100, steps), warmup, per_call=False)
     st = _stats(per)
     extra["sparse_decode_b64"] = {**st, "gbps": sb / (st["mean_ms"] * 1e-3) / 1e9,
                                   "hbm_frac": sb / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": sb,
-                                  "tflops": sfl / (st["mean_ms"] * 1e-3) / 1e12}
-    del x
+                                  "tflops": sfl / (st["mean_ms"] * 1e-3) / 1e12, "sets": len(xs)}
+    del xs
     torch.cuda.empty_cache()
 
     _log("rope in place, Q of the 32K layer")
-    x = _rope_inputs(dev)
-    per, _ = _time_calls(_rope_fn(), [x], steps, warmup, per_call=False)
+    xs = _rope_inputs(dev, 4)
+    per, _ = _time_calls(_rope_fn(), xs, steps, warmup, per_call=False)
     st = _stats(per)
     by = wl.rope_bytes(32768, 32, 128, 2)
     extra["rope_q_32k"] = {**st, "gbps": by / (st["mean_ms"] * 1e-3) / 1e9,
-                           "hbm_frac": by / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": by}
-    del x
+                           "hbm_frac": by / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": by,
+                           "sets": len(xs)}
+    del xs
     torch.cuda.empty_cache()
 
     _log("hybrid_5to1_32k (5 SWA + 1 GA layers)")
@@ -823,8 +872,8 @@ def run_extra(dev, steps, warmup):
     for layer in range(6):
         layers.append(_with_outputs(_to(wl.make_workload("hybrid_5to1_32k", layer), dev), "prefill"))
     swa_fn, ga_fn = _prefill_fn(128), _prefill_fn(None, ga=True)
-    ga_steps = 3
-    per_ga, _ = _time_calls(ga_fn, [layers[5]], ga_steps, 1)
+    ga_steps, ga_warmup = 20, 3
+    per_ga, _ = _time_calls(ga_fn, [layers[5]], ga_steps, ga_warmup)
     fl_swa = wl.prefill_flops([32768], 32, 128, 128)
     fl_ga = wl.prefill_flops([32768], 32, 128, None)
     by = wl.prefill_bytes(32768, 32, 4, 128, 2)
@@ -836,8 +885,8 @@ def run_extra(dev, steps, warmup):
         for li in range(5):
             swa_fn(layers[li])
         ga_fn(layers[5])
-    per_blk, _ = _time_calls(block, [None], ga_steps, 1)
-    per_swa, _ = _time_calls(swa_fn, layers[:5], 20, 2)
+    per_blk, _ = _time_calls(block, [None], ga_steps, ga_warmup)
+    per_swa, _ = _time_calls(swa_fn, layers[:5], 20, 3)
     st_blk = _stats(per_blk)
     extra["hybrid_block"] = {**st_blk, "tflops": (5 * fl_swa + fl_ga) / (st_blk["mean_ms"] * 1e-3) / 1e12,
                              "swa_layer_mean_ms": _stats(per_swa)["mean_ms"],
@@ -847,7 +896,7 @@ def run_extra(dev, steps, warmup):
 
     _log("backward of the 32K layer")
     x = _backward_inputs(dev)
-    per, _ = _time_calls(_backward_fn(), [x], 5, 1, per_call=False)
+    per, _ = _time_calls(_backward_fn(), [x], 20, 3, per_call=False)
     st = _stats(per)
     fl = wl.backward_flops([32768], 32, 128, 128)
     by = wl.backward_bytes(32768, 32, 4, 128, 2)
@@ -858,7 +907,7 @@ def run_extra(dev, steps, warmup):
 
     _log("varlen_262k")
     x = _with_outputs(_to(wl.make_workload("varlen_262k"), dev), "prefill")
-    per, _ = _time_calls(_prefill_fn(128), [x], 10, 2)
+    per, _ = _time_calls(_prefill_fn(128), [x], 20, 3)
     fl, by = wl.workload_work("varlen_262k")
     st = _stats(per)
     extra["varlen_262k"] = {**st, "tflops": fl / (st["mean_ms"] * 1e-3) / 1e12,

@@ -1,9 +1,13 @@
 """fp64 numpy oracle for SWA-with-sink, global causal attention and ring-buffer decode.
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
-cpu_baseline leg of bench.py, never by the library.  Parity is pinned by
-tests/test_oracle.py and tests/test_golden.py (closed forms, library routines,
-brute force, hand-worked fixtures); no function here is "parity unpinned".
+cpu_baseline leg of bench.py, never by the library.  Every public function is pinned
+by tests/test_oracle.py or tests/test_golden.py against something other than itself
+(closed forms, library routines, brute force, hand-worked fixtures, invariants),
+including the row-sampled evaluation (prefill_sample_rows: against the full oracle on
+every row of multi-sequence streams with empty sequences, and brute force) and the
+FP8 decode with RoPE (brute-force ring enumeration over hand-decoded codes with
+distinct K and V scales, and exponent-shift identities of the two scales).
 
 The operator (MiMo-V2-Flash Technical Report digest, section 2.2.2; the formula
 block there lost its symbols in extraction, so the reading below is rebuilt from
@@ -376,24 +380,6 @@ def swa_sink_prefill_fp8kv(q, k_codes, v_codes, k_scale, v_scale, sinks, cu_seql
     if window is None and sinks is None:
         return ga_causal_prefill(q, k, v, cu_seqlens, scale, block)
     return _prefill(q, k, v, sinks, cu_seqlens, None if window is None else int(window), scale, block)
-
-
-def hybrid_block(layers, window=128, scale=None):
-    """Five SWA-with-sink layers then one GA layer, each on its own inputs.
-
-    `layers` is a list of dicts with q, k, v, cu_seqlens and (SWA only) sinks; the
-    last entry is the GA layer.  There is no data flow between layers: only the
-    attention operators are evaluated (technical report digest, section 2.2.1:
-    5 SWA layers per GA layer).  Returns a list of (o, lse).
-    """
-    out = []
-    for li, lay in enumerate(layers):
-        if li == len(layers) - 1:
-            out.append(ga_causal_prefill(lay["q"], lay["k"], lay["v"], lay["cu_seqlens"], scale))
-        else:
-            out.append(swa_sink_prefill(lay["q"], lay["k"], lay["v"], lay["sinks"],
-                                        lay["cu_seqlens"], window, scale))
-    return out
 
 
 def rope(x, positions, base):

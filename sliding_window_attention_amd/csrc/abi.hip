@@ -84,9 +84,6 @@ int prefill_common(const void* q, const void* k, const void* v, const float* sin
     return fail(SWA_ERR_SHAPE, "%s: k_scale and v_scale must be finite and > 0", name);
   if (total_tokens < 0) return fail(SWA_ERR_SHAPE, "%s: total_tokens must be >= 0", name);
   if (num_seqs < 1) return fail(SWA_ERR_SHAPE, "%s: num_seqs must be >= 1", name);
-  if (num_seqs > total_tokens && total_tokens > 0)
-    return fail(SWA_ERR_SHAPE, "%s: num_seqs (%d) exceeds total_tokens (%d)", name, num_seqs,
-                total_tokens);
   if (total_tokens > 0 && (max_seqlen < 1 || max_seqlen > total_tokens))
     return fail(SWA_ERR_SHAPE, "%s: max_seqlen must be in [1, total_tokens]", name);
   if ((rc = check_heads(hq, hkv, d))) return rc;
@@ -388,9 +385,6 @@ int swa_sink_prefill_backward(const void* q, const void* k, const void* v, const
   if (rc) return rc;
   if (total_tokens < 0) return fail(SWA_ERR_SHAPE, "%s: total_tokens must be >= 0", name);
   if (num_seqs < 1) return fail(SWA_ERR_SHAPE, "%s: num_seqs must be >= 1", name);
-  if (num_seqs > total_tokens && total_tokens > 0)
-    return fail(SWA_ERR_SHAPE, "%s: num_seqs (%d) exceeds total_tokens (%d)", name, num_seqs,
-                total_tokens);
   if (total_tokens > 0 && (max_seqlen < 1 || max_seqlen > total_tokens))
     return fail(SWA_ERR_SHAPE, "%s: max_seqlen must be in [1, total_tokens]", name);
   if ((rc = check_heads(num_q_heads, num_kv_heads, head_dim))) return rc;

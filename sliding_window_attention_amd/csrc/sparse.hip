@@ -34,11 +34,14 @@ using namespace tile;
 
 constexpr int kSelThreads = 1024;  // 16 wavefronts
 
-// Larger float -> larger key; NaN below every number.  The scores are read as their
-// 32-bit patterns: the device code is built without NaN semantics, under which a test
-// on a float value (even through its bits) may be folded away.
+// Larger float -> larger key; equal floats -> equal keys (-0 takes the key of +0, so
+// the two zeros tie and the lower position wins between them); NaN below every number.
+// The scores are read as their 32-bit patterns: the device code is built without NaN
+// semantics, under which a test on a float value (even through its bits) may be folded
+// away.
 __device__ __forceinline__ uint32_t order_key(uint32_t u) {
   if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return 0u;
+  u = u == 0x80000000u ? 0u : u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

@@ -909,3 +909,112 @@ def test_sparse_decode_matches_brute_force_and_ignores_index_order():
     o2, l2 = orc.sparse_decode(q, kc, vc, lens, rev, cnt, sinks, recent=recent)
     np.testing.assert_allclose(o2, o, atol=1e-12)
     np.testing.assert_allclose(l2, lse, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# the row-sampled evaluation used at sizes where the full fp64 output is too large
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("window,with_sinks", [(3, True), (16, True), (None, False), (None, True)])
+def test_prefill_sample_rows_equals_full_oracle_on_every_row(window, with_sinks):
+    """prefill_sample_rows at every (token, head) pair of a multi-sequence stream with
+    zero-length sequences (before the first, between and after the others) equals the full
+    swa_sink_prefill / ga_causal_prefill: each sequence's first and last token, the rows
+    inside its first window and the rows past it all take their own sequence's keys."""
+    lens = [0, 5, 0, 0, 23, 1, 0, 40, 2, 0]
+    q, k, v, sinks, cu = _inputs(lens, 4, 2, 8, seed=31)
+    sinks = sinks if with_sinks else None
+    if window is None and sinks is None:
+        o, lse = orc.ga_causal_prefill(q, k, v, cu)
+    elif window is None:
+        o, lse = orc._prefill(q, k, v, sinks, cu, None, None, 128)
+    else:
+        o, lse = orc.swa_sink_prefill(q, k, v, sinks, cu, window)
+    n, hq = q.shape[:2]
+    rows = np.array([(t, h) for t in range(n) for h in range(hq)])
+    os_, ls_ = orc.prefill_sample_rows(q, k, v, sinks, cu, rows, window=window)
+    np.testing.assert_allclose(os_, o[rows[:, 0], rows[:, 1]], atol=1e-13, rtol=0)
+    np.testing.assert_allclose(ls_, lse[rows[:, 0], rows[:, 1]], atol=1e-13, rtol=0)
+    # and against brute-force enumeration for the first tokens of each non-empty sequence
+    ob, lb = brute.attention(q.tolist(), k.tolist(), v.tolist(), None if sinks is None else sinks.tolist(),
+                             cu.tolist(), window)
+    firsts = [(int(cu[s]), h) for s in range(len(lens)) if lens[s] for h in range(hq)]
+    fo, fl = orc.prefill_sample_rows(q, k, v, sinks, cu, np.array(firsts), window=window)
+    for r, (t, h) in enumerate(firsts):
+        np.testing.assert_allclose(fo[r], ob[t][h], atol=1e-13)
+        assert abs(fl[r] - lb[t][h]) < 1e-13
+
+
+def test_prefill_sample_rows_first_token_sees_only_itself():
+    """Row 0 of every sequence attends to its own key alone: o = sigmoid(a - sink) v, the
+    closed form of the first row, whatever the previous sequence holds."""
+    lens = [7, 0, 9, 4]
+    q, k, v, sinks, cu = _inputs(lens, 2, 1, 6, seed=32)
+    d = q.shape[2]
+    for s in (0, 2, 3):
+        t = int(cu[s])
+        for h in range(2):
+            o, lse = orc.prefill_sample_rows(q, k, v, sinks, cu, np.array([[t, h]]), window=128)
+            a = (q[t, h] @ k[t, 0]) / math.sqrt(d)
+            w_ = 1.0 / (1.0 + math.exp(sinks[h] - a))
+            np.testing.assert_allclose(o[0], w_ * v[t, 0], atol=1e-14)
+            assert abs(lse[0] - np.logaddexp(a, sinks[h])) < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# decode with RoPE against an FP8 ring
+# ---------------------------------------------------------------------------
+
+def test_decode_rope_fp8kv_brute_force_with_distinct_scales():
+    """swa_sink_decode_rope_fp8kv equals brute-force ring enumeration (oracle.brute.decode) over
+    cache values decoded by hand from the E4M3 bit fields times k_scale (keys) and v_scale
+    (values), with q and the new keys rotated at positions p .. p+T-1 (the pinned rope)."""
+    rng = np.random.default_rng(33)
+    b, t, hq, hkv, d, w = 2, 3, 4, 2, 8, 7
+    q = rng.standard_normal((b, t, hq, d))
+    kn = rng.standard_normal((b, t, hkv, d))
+    vn = rng.standard_normal((b, t, hkv, d))
+    kc, ks_, ke, km = _codes(rng, (b, hkv, w, d), 3, 10)
+    vc, vs_, ve, vm = _codes(rng, (b, hkv, w, d), 3, 10)
+    k_scale, v_scale = 0.0625 * 3, 0.3
+    kval = np.where(ks_ == 1, -1.0, 1.0) * (1 + km / 8.0) * 2.0 ** (ke - 7) * k_scale
+    vval = np.where(vs_ == 1, -1.0, 1.0) * (1 + vm / 8.0) * 2.0 ** (ve - 7) * v_scale
+    heads = np.array([2, 6])
+    pos = np.array([40, 1234])
+    sinks = rng.standard_normal(hq)
+    base = 10000.0
+    o, lse = orc.swa_sink_decode_rope_fp8kv(q, kn, vn, kc, vc, k_scale, v_scale, heads, pos, sinks, base,
+                                            window=w, io_dtype=None)
+    qr = np.stack([orc.rope(q[bi], pos[bi] + np.arange(t), base) for bi in range(b)])
+    kr = np.stack([orc.rope(kn[bi], pos[bi] + np.arange(t), base) for bi in range(b)])
+    ob, lb = brute.decode(qr.tolist(), kr.tolist(), vn.tolist(), kval.tolist(), vval.tolist(),
+                          heads.tolist(), sinks.tolist(), w)
+    np.testing.assert_allclose(o, np.array(ob), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse, np.array(lb), atol=1e-12, rtol=0)
+
+
+def test_decode_rope_fp8kv_scales_are_exponent_shifts():
+    """Doubling v_scale equals raising every V code's exponent by one; k_scale = 2 with every K
+    exponent lowered by one leaves the result unchanged; so the two scales are neither swapped
+    nor applied to the new tokens (which keep their own values)."""
+    rng = np.random.default_rng(34)
+    b, t, hq, hkv, d, w = 2, 2, 4, 1, 8, 6
+    q = rng.standard_normal((b, t, hq, d))
+    kn = rng.standard_normal((b, t, hkv, d))
+    vn = rng.standard_normal((b, t, hkv, d))
+    codes, sgn, e, m = _codes(rng, (b, hkv, w, d), 2, 12)
+    lower = ((sgn << 7) | ((e - 1) << 3) | m).astype(np.uint8)
+    higher = ((sgn << 7) | ((e + 1) << 3) | m).astype(np.uint8)
+    heads, pos, sinks = np.array([0, 3]), np.array([7, 99]), rng.standard_normal(hq)
+
+    def run(kc, vc, ksc, vsc):
+        return orc.swa_sink_decode_rope_fp8kv(q, kn, vn, kc, vc, ksc, vsc, heads, pos, sinks, 640000.0,
+                                              window=w, io_dtype=None)
+    base = run(codes, codes, 1.0, 1.0)
+    v2, vh = run(codes, codes, 1.0, 2.0), run(codes, higher, 1.0, 1.0)
+    k2 = run(lower, codes, 2.0, 1.0)
+    np.testing.assert_allclose(v2[0], vh[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(v2[1], vh[1], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(k2[0], base[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(k2[1], base[1], rtol=0, atol=1e-12)
+    assert np.abs(v2[0] - base[0]).max() > 1e-3  # the V scale does act on the ring values

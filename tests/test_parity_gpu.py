@@ -15,7 +15,7 @@ import sliding_window_attention_amd as swa
 from oracle import swa_oracle as orc
 from sliding_window_attention_amd import workloads as wl
 from tests.golden.load import array, load
-from tests.parity import assert_close, to_np
+from tests.parity import TOL, assert_close, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -273,6 +273,28 @@ def test_prefill_zero_length_sequences(case):
     assert_close(x["q"].dtype, o, o_ref, lse, l_ref, "zero-length sequences GA")
 
 
+@pytest.mark.parametrize("lens", [[0, 0, 1], [0, 0, 0, 2, 0, 0, 3, 0, 0, 0]], ids=["0-0-1", "trailing-empty"])
+def test_more_sequences_than_tokens(lens):
+    """Packed batches with more (mostly empty) sequences than tokens, e.g. cu_seqlens =
+    [0, 0, 0, 1]: every prefill path, the FP8-K/V prefill and the backward."""
+    _say(f"prefill with more sequences than tokens: {lens}")
+    for hq, hkv, w in ((32, 4, 128), (32, 4, 200), (8, 2, 128)):
+        x = wl.make_prefill(lens, hq, hkv, 128, "bf16", seed=950 + w + hq + len(lens))
+        assert x["cu_seqlens"].numel() - 1 > x["q"].shape[0]
+        o, lse = _run_prefill(x, w)
+        o_ref, l_ref = _oracle_prefill(x, w)
+        assert_close(torch.bfloat16, o, o_ref, lse, l_ref, f"{lens} {hq}/{hkv} W{w}")
+        o, lse = _run_prefill(x, None, ga=True)
+        o_ref, l_ref = _oracle_prefill(x, None, ga=True)
+        assert_close(torch.bfloat16, o, o_ref, lse, l_ref, f"{lens} {hq}/{hkv} GA")
+    f = wl.make_prefill_fp8(lens, 32, 4, 128, "bf16", seed=960 + len(lens))
+    o, lse = _run_prefill_fp8(f, 128)
+    o_ref, l_ref = _oracle_prefill_fp8(f, 128)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, f"{lens} FP8 K/V")
+    for hq, hkv in ((32, 4), (8, 2)):  # matrix-core and vector backward paths
+        _backward_case(lens, hq, hkv, 128, "bf16", 128, True, seed=970 + hq + len(lens))
+
+
 def test_empty_stream_and_batch():
     _say("empty prefill stream and empty decode batch")
     x = wl.make_prefill([0, 0], 32, 4, 128, "bf16", seed=1)
@@ -362,13 +384,81 @@ def test_hybrid_block_full_size():
             _check_rows(x, o, lse, rows, None if ga else 128, f"hybrid layer {layer}")
 
 
-def test_varlen_262k_sampled():
-    _say("varlen_262k: 8 log-normal sequences, 262144 tokens, sampled rows")
+class _Err:
+    """Errors of one operator call accumulated over pieces of its output: max-abs of O and
+    LSE over all pieces, rel-L2 of O over the whole output."""
+
+    def __init__(self):
+        self.max_abs, self.num, self.den, self.lse, self.finite = 0.0, 0.0, 0.0, 0.0, True
+
+    def add(self, o_gpu, o_ref, l_gpu, l_ref):
+        og, lg = to_np(o_gpu), to_np(l_gpu)
+        diff = og - o_ref
+        self.max_abs = max(self.max_abs, float(np.abs(diff).max(initial=0.0)))
+        self.num += float((diff * diff).sum())
+        self.den += float((o_ref * o_ref).sum())
+        self.lse = max(self.lse, float(np.abs(lg - l_ref).max(initial=0.0)))
+        self.finite &= bool(np.isfinite(og).all() and np.isfinite(lg).all())
+
+    def check(self, what):
+        tol = TOL[torch.bfloat16]
+        e = {"max_abs": self.max_abs, "rel_l2": (self.num / max(self.den, 1e-300)) ** 0.5, "finite": self.finite,
+             "lse_max_abs": self.lse}
+        msg = f"{what}: {e} vs {tol}"
+        print(msg, flush=True)
+        assert self.finite and e["max_abs"] <= tol["max_abs"] and e["rel_l2"] <= tol["rel_l2"], msg
+        assert e["lse_max_abs"] <= tol["lse"], msg
+
+
+def test_ga_layer_32k_every_row_of_one_head_per_kv_head():
+    """The 32K GA layer of the 5:1 block: every query row of four query heads, one per KV head
+    (heads 3, 14, 17 and 28), so every tile and workgroup of the launch is compared; the four
+    single-head oracle runs go to threads (numpy releases the GIL in its kernels)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    _say("hybrid_5to1_32k GA layer: every row of heads 3, 14, 17, 28 against the oracle")
+    x = wl.make_workload("hybrid_5to1_32k", 5)
+    o, lse = _run_prefill(x, None, ga=True)
+    heads = [3, 14, 17, 28]
+    g = x["q"].shape[1] // x["k"].shape[1]
+    cu = x["cu_seqlens"].numpy()
+
+    def one(h):
+        kvh = h // g
+        return orc.ga_causal_prefill(x["q"][:, h:h + 1].contiguous(), x["k"][:, kvh:kvh + 1].contiguous(),
+                                     x["v"][:, kvh:kvh + 1].contiguous(), cu)
+
+    with ThreadPoolExecutor(len(heads)) as ex:
+        refs = list(ex.map(one, heads))
+    err = _Err()
+    for h, (o_ref, l_ref) in zip(heads, refs):
+        err.add(o[:, h], o_ref[:, 0], lse[:, h], l_ref[:, 0])
+    err.check("GA 32K, 4 heads every row")
+
+
+def test_varlen_262k_full():
+    """The 262,144-token varlen workload: every element against the oracle, one sequence at a
+    time (sequences are independent: no attention crosses a boundary), so the fp64 copies
+    stay bounded by the longest sequence."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    _say("varlen_262k: 8 log-normal sequences, 262144 tokens, every element")
     x = wl.make_workload("varlen_262k")
     o, lse = _run_prefill(x, 128)
-    rows = _sample_rows(x, 512, seed=5)
-    _check_rows(x, o, lse, rows, 128, "varlen_262k")
-    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    cu = x["cu_seqlens"].tolist()
+
+    def one(s):
+        c0, c1 = cu[s], cu[s + 1]
+        return orc.swa_sink_prefill(x["q"][c0:c1], x["k"][c0:c1], x["v"][c0:c1], x["sinks"],
+                                    np.array([0, c1 - c0]), 128)
+
+    err = _Err()
+    order = sorted(range(len(cu) - 1), key=lambda s: cu[s] - cu[s + 1])  # longest first
+    with ThreadPoolExecutor(2) as ex:
+        for s, (o_ref, l_ref) in zip(order, ex.map(one, order)):
+            err.add(o[cu[s]:cu[s + 1]], o_ref, lse[cu[s]:cu[s + 1]], l_ref)
+            del o_ref, l_ref
+    err.check("varlen_262k every element")
 
 
 # ---------------------------------------------------------------------------
@@ -1144,7 +1234,8 @@ def _topk_gpu(scores, lengths, k, recent):
                                   (4, 4, 9000, 64, 128, "few"), (3, 2, 700, 1024, 128, "short"),
                                   (4, 2, 2000, 0, 128, "k0"), (3, 2, 4100, 500, 16, "special"),
                                   (3, 2, 9000, 1024, 128, "two"), (2, 2, 40000, 1024, 128, "normal"),
-                                  (4, 3, 3001, 256, 64, "normal")],  # rows at every 4-byte alignment
+                                  (4, 3, 3001, 256, 64, "normal"),  # rows at every 4-byte alignment
+                                  (4, 2, 3000, 1024, 128, "zeros"), (3, 2, 2500, 700, 33, "zeros")],
                          ids=lambda c: f"B{c[0]}-kv{c[1]}-L{c[2]}-k{c[3]}-r{c[4]}-{c[5]}")
 def test_topk_select_exact(case):
     b, hkv, lmax, k, recent, kind = case
@@ -1157,11 +1248,15 @@ def test_topk_select_exact(case):
         scores = torch.randint(0, 2, (b, hkv, lmax), generator=gen).float() * 0.5
     if kind == "few":  # values equal to the threshold straddle chunk boundaries
         scores = torch.randint(0, 40, (b, hkv, lmax), generator=gen).float()
-    if kind == "special":  # NaN ranks below every number (numpy's sort puts it last too); +-inf; -0.0
+    if kind == "special":  # NaN ranks below every number (numpy's sort puts it last too); +-inf; +-0.0
         scores[:, :, ::7] = float("nan")
         scores[:, :, 3::11] = float("inf")
         scores[:, :, 5::13] = float("-inf")
-        scores[:, :, 1::17] = -0.0  # (+0.0 is not mixed in: the kernel ranks it above -0.0)
+        scores[:, :, 1::17] = -0.0
+        scores[:, :, 2::19] = 0.0   # the two zeros are equal scores: the lower position wins
+    if kind == "zeros":  # mostly signed zeros: the threshold lands on zero, ties across both signs
+        scores = torch.randn(b, hkv, lmax, generator=gen).clamp(min=0.0)
+        scores = torch.where(torch.rand(b, hkv, lmax, generator=gen) < 0.5, scores, -scores)
     lengths = torch.randint(1, lmax + 1, (b,), generator=gen, dtype=torch.int64).to(torch.int32)
     lengths[0] = lmax
     if kind == "short":
