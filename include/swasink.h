@@ -57,7 +57,7 @@ typedef enum {
 
 typedef enum { SWA_DTYPE_F32 = 0, SWA_DTYPE_BF16 = 1 } swa_dtype;
 
-#define SWASINK_ABI_VERSION 7
+#define SWASINK_ABI_VERSION 8
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SWASINK_API __attribute__((visibility("default")))
@@ -200,6 +200,27 @@ SWASINK_API int swa_sink_prefill_backward(const void* q, const void* k, const vo
 
 /* Bytes of workspace swa_sink_prefill_backward needs (-1 for invalid sizes). */
 SWASINK_API int64_t swa_sink_prefill_backward_workspace(int32_t total_tokens, int32_t num_q_heads);
+
+/*
+ * swa_sink_prefill_backward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight training loops, harnesses that forbid hipMalloc): the same
+ * kernels and results, with the workspace taken from a scratch array the library owns
+ * (16 MiB per GPU, a static device array, held until the process ends) instead of an
+ * argument.  It calls no allocating routine.  Arguments, layouts, outputs and errors are
+ * those of swa_sink_prefill_backward without workspace and workspace_bytes; in
+ * addition, total_tokens * num_q_heads must not exceed 2,097,152 (the array holds the
+ * 2 x total_tokens x num_q_heads fp32 delta and sink terms), else SWA_ERR_UNSUPPORTED.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents
+ * (nothing in it must start at zero): calls that overlap on one GPU -- on different
+ * streams, or from different threads -- race and give unspecified gradients.  Calls
+ * ordered on one stream are safe.
+ */
+SWASINK_API int swa_sink_prefill_backward_noalloc(const void* q, const void* k, const void* v,
+                    const float* sinks, const int32_t* cu_seqlens, int32_t num_seqs,
+                    int32_t total_tokens, int32_t max_seqlen, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t window, float scale,
+                    swa_dtype dtype, const void* out, const float* lse, const void* dout,
+                    void* dq, void* dk, void* dv, float* dsinks, void* stream);
 
 /*
  * Rotary position embedding (RoPE), in place.  Bases: 10,000 in SWA layers, 640,000

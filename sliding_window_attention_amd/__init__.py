@@ -38,6 +38,8 @@ _SIGNATURES = {
     "swa_sink_decode": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P],
     "swa_sink_prefill_backward": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P,
                                   _P, _P, _P, _P, _P, ctypes.c_int64, _P],
+    "swa_sink_prefill_backward_noalloc": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P,
+                                          _P, _P, _P, _P, _P, _P],
     "swa_sink_decode_fp8kv": [_P, _P, _P, _P, _P, _F, _F, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
                               _P, _P, _P],
     "swa_sink_prefill_fp8kv": [_P, _P, _P, _F, _F, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P,
@@ -504,12 +506,15 @@ def swa_sparse_decode(q, k_cache, v_cache, lengths, indices, counts, sinks=None,
 
 
 def swa_sink_prefill_backward(q, k, v, sinks, cu_seqlens, out, lse, dout, max_seqlen=None,
-                              window=128, scale=None):
+                              window=128, scale=None, library_scratch=False, grads=None):
     """Gradients of swa_sink_prefill's output O: (dq, dk, dv, dsinks) for dout = dL/dO.
 
     q/out/dout [N, Hq, D], k/v [N, Hkv, D] in one dtype, lse [N, Hq] fp32 from the
     forward, sinks [Hq] fp32 or None (no sink; dsinks is then None).  The workspace
-    the library needs is allocated here with torch.
+    the library needs is allocated here with torch; with library_scratch=True the call
+    goes to swa_sink_prefill_backward_noalloc, which uses the library's own scratch
+    array instead.  grads = (dq, dk, dv, dsinks) receives the gradients in caller
+    buffers (then nothing at all is allocated here with library_scratch=True).
     """
     import torch
 
@@ -526,13 +531,32 @@ def swa_sink_prefill_backward(q, k, v, sinks, cu_seqlens, out, lse, dout, max_se
             sinks is not None and sinks.numel() != hq):
         raise ValueError("inconsistent shapes")
     lib = library()
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dsinks = None if sinks is None else torch.empty(hq, dtype=torch.float32, device=q.device)
+    else:
+        dq, dk, dv, dsinks = grads
+        for t, ref, nm in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+            _dev(t, nm, ref.dtype)
+            if t.shape != ref.shape:
+                raise ValueError(f"{nm} must have the shape of {nm[1:]}")
+        if (dsinks is None) != (sinks is None) or (dsinks is not None and dsinks.numel() != hq):
+            raise ValueError("dsinks must be given exactly when sinks is, with one value per head")
+        if dsinks is not None:
+            _dev(dsinks, "dsinks", torch.float32)
+    ms = n if max_seqlen is None else int(max_seqlen)
+    if library_scratch:
+        rc = lib.swa_sink_prefill_backward_noalloc(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), None if sinks is None else sinks.data_ptr(),
+            cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, n, ms, hq, k.shape[1], d, int(window),
+            _scale(scale), _dtype_code(q), out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), None if dsinks is None else dsinks.data_ptr(), _stream(q.device))
+        _check(rc)
+        return dq, dk, dv, dsinks
     need = int(lib.swa_sink_prefill_backward_workspace(n, hq))
     if need < 0:
         raise ValueError("invalid sizes")
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dsinks = None if sinks is None else torch.empty(hq, dtype=torch.float32, device=q.device)
-    ms = n if max_seqlen is None else int(max_seqlen)
     rc = lib.swa_sink_prefill_backward(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), None if sinks is None else sinks.data_ptr(),
         cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, n, ms, hq, k.shape[1], d, int(window),

@@ -10,6 +10,16 @@
 #include "../../include/swasink.h"
 #include "kernels.h"
 
+// Scratch array of swa_sink_prefill_backward_noalloc, owned by the library: the
+// backward's per-row delta and sink terms (2 x total_tokens x num_q_heads fp32) for
+// callers that cannot allocate.  Each GPU the library runs on holds its own copy until
+// the process ends.  In host code `scratch` only names a host-side stand-in; its device
+// address is looked up once per device (hipGetSymbolAddress with that device current)
+// and only that address is passed to kernels.  Nothing in it must start at zero: every
+// element a call reads was written earlier in the same call.
+constexpr int64_t kNoAllocScratchBytes = 16ll << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 namespace swa {
 
 hipError_t device_cu_count(int* out) {
@@ -213,6 +223,78 @@ int ring_append_common(const void* k_new, const void* v_new, const int32_t* n_ac
                     name);
 }
 
+// Device address of this device's copy of `scratch` (see the top of this file).
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch array (resolved on the first call per device).
+int scratch_address(void** out, const char* name) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, name);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SWA_ERR_UNSUPPORTED, "%s: device ordinal %d beyond the %d this library tracks", name, dev,
+                kMaxDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, name);
+    if (p == nullptr) return fail(SWA_ERR_HIP, "%s: no device address for the scratch array", name);
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return SWA_OK;
+}
+
+int backward_common(const void* q, const void* k, const void* v, const float* sinks,
+                    const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t window, float scale,
+                    swa_dtype dtype, const void* out, const float* lse, const void* dout, void* dq, void* dk,
+                    void* dv, float* dsinks, void* workspace, int64_t workspace_bytes, bool library_scratch,
+                    void* stream, const char* name) {
+  int rc = check_dtype((int)dtype);
+  if (rc) return rc;
+  if (total_tokens < 0) return fail(SWA_ERR_SHAPE, "%s: total_tokens must be >= 0", name);
+  if (num_seqs < 1) return fail(SWA_ERR_SHAPE, "%s: num_seqs must be >= 1", name);
+  if (total_tokens > 0 && (max_seqlen < 1 || max_seqlen > total_tokens))
+    return fail(SWA_ERR_SHAPE, "%s: max_seqlen must be in [1, total_tokens]", name);
+  if ((rc = check_heads(num_q_heads, num_kv_heads, head_dim))) return rc;
+  if (window < 1) return fail(SWA_ERR_SHAPE, "%s: window must be >= 1 (got %d)", name, window);
+  if ((long long)total_tokens * num_q_heads * head_dim > (1LL << 40))
+    return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
+  if ((sinks == nullptr) != (dsinks == nullptr))
+    return fail(SWA_ERR_NULL, "%s: sinks and dsinks must both be given or both be NULL", name);
+  if (total_tokens == 0 && dsinks == nullptr) return ok();  // nothing to read or write
+  if (total_tokens > 0 && (!q || !k || !v || !cu_seqlens || !out || !lse || !dout || !dq || !dk || !dv))
+    return fail(SWA_ERR_NULL, "%s: q, k, v, cu_seqlens, out, lse, dout, dq, dk and dv must be non-NULL",
+                name);
+  const int64_t need = backward_workspace_bytes(total_tokens, num_q_heads);
+  if (library_scratch) {
+    if (need > kNoAllocScratchBytes)
+      return fail(SWA_ERR_UNSUPPORTED,
+                  "%s: needs %lld bytes of scratch, the library's array holds %lld "
+                  "(total_tokens * num_q_heads <= %lld)",
+                  name, (long long)need, (long long)kNoAllocScratchBytes,
+                  (long long)(kNoAllocScratchBytes / (2 * (int64_t)sizeof(float))));
+    if ((rc = scratch_address(&workspace, name))) return rc;
+  } else if (total_tokens > 0 && (workspace == nullptr || workspace_bytes < need)) {
+    return fail(SWA_ERR_SHAPE, "%s: workspace of %lld bytes needed (got %lld)", name, (long long)need,
+                (long long)workspace_bytes);
+  }
+  swa::BackwardArgs a;
+  a.q = q; a.k = k; a.v = v; a.sinks = sinks; a.cu_seqlens = cu_seqlens;
+  a.out = out; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dsinks = dsinks;
+  a.delta = static_cast<float*>(workspace);
+  a.sink_term = a.delta + (size_t)total_tokens * num_q_heads;
+  a.num_seqs = num_seqs; a.total_tokens = total_tokens;
+  a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
+  a.window = window;
+  a.scale = resolve_scale(scale, head_dim);
+  const hipError_t e = swa::launch_backward(a, dtype == SWA_DTYPE_BF16, static_cast<hipStream_t>(stream));
+  return hip_status(e, name);
+}
+
 }  // namespace
 
 extern "C" {
@@ -380,39 +462,20 @@ int swa_sink_prefill_backward(const void* q, const void* k, const void* v, const
                               const void* out, const float* lse, const void* dout, void* dq,
                               void* dk, void* dv, float* dsinks, void* workspace,
                               int64_t workspace_bytes, void* stream) {
-  const char* name = "swa_sink_prefill_backward";
-  int rc = check_dtype((int)dtype);
-  if (rc) return rc;
-  if (total_tokens < 0) return fail(SWA_ERR_SHAPE, "%s: total_tokens must be >= 0", name);
-  if (num_seqs < 1) return fail(SWA_ERR_SHAPE, "%s: num_seqs must be >= 1", name);
-  if (total_tokens > 0 && (max_seqlen < 1 || max_seqlen > total_tokens))
-    return fail(SWA_ERR_SHAPE, "%s: max_seqlen must be in [1, total_tokens]", name);
-  if ((rc = check_heads(num_q_heads, num_kv_heads, head_dim))) return rc;
-  if (window < 1) return fail(SWA_ERR_SHAPE, "%s: window must be >= 1 (got %d)", name, window);
-  if ((long long)total_tokens * num_q_heads * head_dim > (1LL << 40))
-    return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
-  if ((sinks == nullptr) != (dsinks == nullptr))
-    return fail(SWA_ERR_NULL, "%s: sinks and dsinks must both be given or both be NULL", name);
-  if (total_tokens == 0 && dsinks == nullptr) return ok();  // nothing to read or write
-  if (total_tokens > 0 && (!q || !k || !v || !cu_seqlens || !out || !lse || !dout || !dq || !dk || !dv))
-    return fail(SWA_ERR_NULL, "%s: q, k, v, cu_seqlens, out, lse, dout, dq, dk and dv must be non-NULL",
-                name);
-  const int64_t need = backward_workspace_bytes(total_tokens, num_q_heads);
-  if (total_tokens > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(SWA_ERR_SHAPE, "%s: workspace of %lld bytes needed (got %lld)", name, (long long)need,
-                (long long)workspace_bytes);
-  swa::BackwardArgs a;
-  a.q = q; a.k = k; a.v = v; a.sinks = sinks; a.cu_seqlens = cu_seqlens;
-  a.out = out; a.lse = lse; a.dout = dout;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.dsinks = dsinks;
-  a.delta = static_cast<float*>(workspace);
-  a.sink_term = a.delta + (size_t)total_tokens * num_q_heads;
-  a.num_seqs = num_seqs; a.total_tokens = total_tokens;
-  a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
-  a.window = window;
-  a.scale = resolve_scale(scale, head_dim);
-  const hipError_t e = swa::launch_backward(a, dtype == SWA_DTYPE_BF16, static_cast<hipStream_t>(stream));
-  return hip_status(e, name);
+  return backward_common(q, k, v, sinks, cu_seqlens, num_seqs, total_tokens, max_seqlen, num_q_heads,
+                         num_kv_heads, head_dim, window, scale, dtype, out, lse, dout, dq, dk, dv, dsinks,
+                         workspace, workspace_bytes, false, stream, "swa_sink_prefill_backward");
+}
+
+int swa_sink_prefill_backward_noalloc(const void* q, const void* k, const void* v, const float* sinks,
+                                      const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                                      int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t window, float scale, swa_dtype dtype,
+                                      const void* out, const float* lse, const void* dout, void* dq,
+                                      void* dk, void* dv, float* dsinks, void* stream) {
+  return backward_common(q, k, v, sinks, cu_seqlens, num_seqs, total_tokens, max_seqlen, num_q_heads,
+                         num_kv_heads, head_dim, window, scale, dtype, out, lse, dout, dq, dk, dv, dsinks,
+                         nullptr, 0, true, stream, "swa_sink_prefill_backward_noalloc");
 }
 
 const char* swa_last_error(void) { return g_last_error; }

@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     assert set(names) == {"swa_sink_prefill", "ga_causal_prefill", "swa_sink_prefill_fp8kv", "swa_sink_decode",
                           "swa_sink_decode_fp8kv", "swa_sink_prefill_backward",
-                          "swa_sink_prefill_backward_workspace", "swa_rope", "swa_sink_decode_rope",
+                          "swa_sink_prefill_backward_workspace", "swa_sink_prefill_backward_noalloc",
+                          "swa_rope", "swa_sink_decode_rope",
                           "swa_ring_append_rope", "swa_topk_select", "swa_sparse_decode",
                           "swa_sink_decode_rope_fp8kv", "swa_ring_append_fp8kv",
                           "swa_last_error", "swa_abi_version"}
@@ -276,6 +277,30 @@ def test_backward_workspace_size():
 ])
 def test_backward_rejects_bad_arguments(kw, code, needle):
     assert _backward(**kw) == code
+    assert needle in _last()
+
+
+def _backward_noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sinks=FAKE, cu=FAKE, num_seqs=1, n=16, max_seqlen=16, hq=8,
+             hkv=1, d=128, window=128, scale=0.0, dtype=1, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE,
+             dk=FAKE, dv=FAKE, dsinks=FAKE, stream=NULL)
+    a.update(kw)
+    return swa.library().swa_sink_prefill_backward_noalloc(
+        a["q"], a["k"], a["v"], a["sinks"], a["cu"], a["num_seqs"], a["n"], a["max_seqlen"], a["hq"],
+        a["hkv"], a["d"], a["window"], a["scale"], a["dtype"], a["out"], a["lse"], a["dout"], a["dq"],
+        a["dk"], a["dv"], a["dsinks"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(n=65537, max_seqlen=65537, hq=32, hkv=4), E_UNSUP, "16777216"),  # 2 x 65537 x 32 fp32 > 16 MiB
+    (dict(n=1 << 20, max_seqlen=1 << 20, hq=8, hkv=1), E_UNSUP, "2097152"),
+    (dict(lse=NULL), E_NULL, "lse"),
+    (dict(dsinks=NULL), E_NULL, "both"),
+    (dict(window=0), E_SHAPE, "window"),
+    (dict(num_seqs=0), E_SHAPE, "num_seqs"),
+])
+def test_backward_noalloc_rejects_bad_arguments_and_sizes_beyond_its_scratch(kw, code, needle):
+    assert _backward_noalloc(**kw) == code
     assert needle in _last()
 
 
