@@ -74,7 +74,9 @@ class SwaError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, _LIB_NAME)
+    """The in-tree libswasink.so, or the build named by SWASINK_LIBRARY (used to run the
+    ABI checks against a host-sanitizer build of the same sources)."""
+    return os.environ.get("SWASINK_LIBRARY") or os.path.join(_HERE, _LIB_NAME)
 
 
 def library() -> ctypes.CDLL:
