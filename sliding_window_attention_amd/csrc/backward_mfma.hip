@@ -511,6 +511,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
       const float* ls = reinterpret_cast<const float*>(ds + kOpBytes);
       // ---- S = Q K^T and dP = dO V^T for two pairs of 16-row blocks (rows 32 pi ..) ----
       f32x4 s[2][2], tt[2][2];
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int pi = 0; pi < 2; ++pi)
 #pragma unroll
@@ -526,6 +527,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
             tt[pi][h] = mfma32(df, vb[cc], tt[pi][h]);
           }
         }
+      __builtin_amdgcn_s_setprio(0);
       // lane (i, g) holds rows P = 32 pi + 8g + 4h + r: token 8 (g & 1) + 4h + r
       bf16x8 pp[2], xp[2];
 #pragma unroll
@@ -551,6 +553,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
       }
 
       // ---- dV^T += dO^T P and dK^T += Q^T dS over the step's 64 rows ----
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int pi = 0; pi < 2; ++pi) {
 #pragma unroll
@@ -566,6 +569,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // the other buffer was last read in the previous step, which every wavefront has
     // finished (barrier below)
     if (step + 1 < total) commit((step + 1) & 1, sa);

@@ -13,7 +13,11 @@
 // lazily: O and the running sum are rescaled only when some row's maximum grows
 // by more than kSlack (log2 units); otherwise the exponent keeps the older, smaller
 // reference and the weights may exceed 1 by at most 2^kSlack, which fp32 sums and
-// bf16 weights hold without loss of relative precision.
+// bf16 weights hold without loss of relative precision.  Once every row has a
+// finite reference, a chunk is exponentiated against it without forming maxima:
+// the weights are non-negative, so a lane's partial sum of at most 2^kSlack bounds
+// each of its weights by the same; a larger sum (rare once the maxima settle) sends
+// the chunk through the full path with its scores formed again.
 #include <type_traits>
 
 #include "common.h"
@@ -35,6 +39,8 @@ constexpr int kKBuf = 4 * kKPlane;       // 32768
 constexpr int kVBuf = kStage * kVPitch;  // 33792
 constexpr int kBuf = kKBuf + kVBuf;
 constexpr float kSlack = 8.f;
+constexpr float kSlackPow = 256.f;  // 2^kSlack
+constexpr float kArgCap = 64.f;     // exp2 arguments capped: weights stay finite
 
 // Staged K/V as loaded: 16 bytes of bf16, or (FP8) 8 bytes of E4M3 codes widened to
 // bf16 (exactly) only when committed to LDS, so that no conversion waits on a load.
@@ -167,6 +173,7 @@ void ga_chunk_kernel(PrefillArgs a) {
   // this lane's share of the running sums (the 4 lanes of a row are added at the end)
   float l0 = (a.sinks && g == 0) ? 1.f : 0.f, l1 = l0;
   f32x4 o0[8], o1[8];
+  bool ready = false;  // (uniform) every row of the wavefront has a finite reference maximum
 #pragma unroll
   for (int b = 0; b < 8; ++b) { o0[b] = zero4; o1[b] = zero4; }
 
@@ -190,84 +197,111 @@ void ga_chunk_kernel(PrefillArgs a) {
     // every query): nothing to do
     const bool skip = kb + kChunk - 1 < lo_w_min || kb > qw + 15;
     if (!skip) {
-      // ---- S^T = K Q^T over 4 blocks of 16 keys (2 pairs) ----
+      // ---- S^T = K Q^T over 4 blocks of 16 keys (2 pairs), masked where a row's
+      // window or the causal edge cuts the chunk ----
       f32x4 s0[4], s1[4];
-      // Raised issue priority over the MFMA runs: the two waves sharing a SIMD then
-      // tend to alternate matrix work with the other's softmax instead of colliding.
-      __builtin_amdgcn_s_setprio(1);
+      auto scores = [&]() {
+        // Raised issue priority over the MFMA runs: the two waves sharing a SIMD then
+        // tend to alternate matrix work with the other's softmax instead of colliding.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int bl = 0; bl < 4; ++bl) {
-        const int off = 32 * 64 * (bl >> 1) + ((bl & 1) ? ko1 : ko0);
-        bf16x8 kf = *reinterpret_cast<const bf16x8*>(buf + off);
-        s0[bl] = mfma32(kf, qa[0], zero4);
-        s1[bl] = mfma32(kf, qb[0], zero4);
+        for (int bl = 0; bl < 4; ++bl) {
+          const int off = 32 * 64 * (bl >> 1) + ((bl & 1) ? ko1 : ko0);
+          bf16x8 kf = *reinterpret_cast<const bf16x8*>(buf + off);
+          s0[bl] = mfma32(kf, qa[0], zero4);
+          s1[bl] = mfma32(kf, qb[0], zero4);
 #pragma unroll
-        for (int cc = 1; cc < 4; ++cc) {
-          kf = *reinterpret_cast<const bf16x8*>(buf + cc * kKPlane + off);
-          s0[bl] = mfma32(kf, qa[cc], s0[bl]);
-          s1[bl] = mfma32(kf, qb[cc], s1[bl]);
+          for (int cc = 1; cc < 4; ++cc) {
+            kf = *reinterpret_cast<const bf16x8*>(buf + cc * kKPlane + off);
+            s0[bl] = mfma32(kf, qa[cc], s0[bl]);
+            s1[bl] = mfma32(kf, qb[cc], s1[bl]);
+          }
         }
-      }
-      __builtin_amdgcn_s_setprio(0);
-      // ---- mask (only chunks not fully visible to every row) and chunk maxima ----
-      const bool full = kb >= lo_w_max && kb + kChunk - 1 <= qw;
-      if (!full) {
-        const unsigned span = (unsigned)(qi - lo);
+        __builtin_amdgcn_s_setprio(0);
+        const bool full = kb >= lo_w_max && kb + kChunk - 1 <= qw;
+        if (!full) {
+          const unsigned span = (unsigned)(qi - lo);
+#pragma unroll
+          for (int bl = 0; bl < 4; ++bl)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int key = kb + 32 * (bl >> 1) + 8 * g + 4 * (bl & 1) + r;
+              const bool ok = (unsigned)(key - lo) <= span;
+              s0[bl][r] = ok ? s0[bl][r] : -INFINITY;
+              s1[bl][r] = ok ? s1[bl][r] : -INFINITY;
+            }
+        }
+      };
+      scores();
+      // ---- exponentiate against the reference maxima and sum.  Once every row of the
+      // wavefront has a finite reference, the chunk is exponentiated directly (the
+      // argument clamped so that no weight is infinite): if no lane's partial sum of a
+      // head exceeds 2^kSlack, no weight does, which is exactly the bound the lazy
+      // rescale keeps, and the weights equal those of the full path below.  Otherwise
+      // the raw scores are formed again and the full path runs: per-lane maxima, the
+      // rescale where a row's maximum outgrew its reference, the exponentials. ----
+      float ps0 = 0.f, ps1 = 0.f;
+      bool need_max = !ready;
+      if (!need_max) {
 #pragma unroll
         for (int bl = 0; bl < 4; ++bl)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int key = kb + 32 * (bl >> 1) + 8 * g + 4 * (bl & 1) + r;
-            const bool ok = (unsigned)(key - lo) <= span;
-            s0[bl][r] = ok ? s0[bl][r] : -INFINITY;
-            s1[bl][r] = ok ? s1[bl][r] : -INFINITY;
+            s0[bl][r] = fast_exp2(fminf(fmaf(s0[bl][r], c, -m0), kArgCap));
+            s1[bl][r] = fast_exp2(fminf(fmaf(s1[bl][r], c, -m1), kArgCap));
+            ps0 += s0[bl][r];
+            ps1 += s1[bl][r];
           }
+        need_max = __builtin_amdgcn_ballot_w64(fmaxf(ps0, ps1) > kSlackPow) != 0;
+        if (need_max) scores();
       }
-      float mx0 = -INFINITY, mx1 = -INFINITY;
+      if (need_max) {
+        float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
-      for (int bl = 0; bl < 4; ++bl) {
-        mx0 = fmaxf(mx0, fmaxf(fmaxf(s0[bl][0], s0[bl][1]), fmaxf(s0[bl][2], s0[bl][3])));
-        mx1 = fmaxf(mx1, fmaxf(fmaxf(s1[bl][0], s1[bl][1]), fmaxf(s1[bl][2], s1[bl][3])));
-      }
-      mx0 *= c;  // this lane's maxima: a row's maximum exceeds a bound iff one of
-      mx1 *= c;  // its 4 lanes does, so the row maximum is needed only to rescale
-      // ---- lazy rescale: only when some row's maximum outgrows its reference ----
-      if (__builtin_amdgcn_ballot_w64(mx0 > m0 + kSlack) != 0) {
-        const float mn = fmaxf(m0, quad_max(mx0));
-        const float al = (m0 == -INFINITY) ? 0.f : fast_exp2(m0 - mn);
-        l0 *= al;
+        for (int bl = 0; bl < 4; ++bl) {
+          mx0 = fmaxf(mx0, fmaxf(fmaxf(s0[bl][0], s0[bl][1]), fmaxf(s0[bl][2], s0[bl][3])));
+          mx1 = fmaxf(mx1, fmaxf(fmaxf(s1[bl][0], s1[bl][1]), fmaxf(s1[bl][2], s1[bl][3])));
+        }
+        mx0 *= c;  // this lane's maxima: a row's maximum exceeds a bound iff one of
+        mx1 *= c;  // its 4 lanes does, so the row maximum is needed only to rescale
+        if (__builtin_amdgcn_ballot_w64(mx0 > m0 + kSlack) != 0) {
+          const float mn = fmaxf(m0, quad_max(mx0));
+          const float al = (m0 == -INFINITY) ? 0.f : fast_exp2(m0 - mn);
+          l0 *= al;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) o0[b] *= al;
-        m0 = mn;
-      }
-      if (__builtin_amdgcn_ballot_w64(mx1 > m1 + kSlack) != 0) {
-        const float mn = fmaxf(m1, quad_max(mx1));
-        const float al = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - mn);
-        l1 *= al;
+          for (int b = 0; b < 8; ++b) o0[b] *= al;
+          m0 = mn;
+        }
+        if (__builtin_amdgcn_ballot_w64(mx1 > m1 + kSlack) != 0) {
+          const float mn = fmaxf(m1, quad_max(mx1));
+          const float al = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - mn);
+          l1 *= al;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) o1[b] *= al;
-        m1 = mn;
+          for (int b = 0; b < 8; ++b) o1[b] *= al;
+          m1 = mn;
+        }
+        // rows that have seen no visible key yet keep reference -inf: exponentiate
+        // against 0 so masked scores give exactly 0
+        const float e0 = (m0 == -INFINITY) ? 0.f : m0;
+        const float e1 = (m1 == -INFINITY) ? 0.f : m1;
+        ps0 = 0.f;
+        ps1 = 0.f;
+#pragma unroll
+        for (int bl = 0; bl < 4; ++bl)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            s0[bl][r] = fast_exp2(fmaf(s0[bl][r], c, -e0));
+            s1[bl][r] = fast_exp2(fmaf(s1[bl][r], c, -e1));
+            ps0 += s0[bl][r];
+            ps1 += s1[bl][r];
+          }
+        ready = __builtin_amdgcn_ballot_w64(m0 == -INFINITY || m1 == -INFINITY) == 0;
       }
-      // rows that have seen no visible key yet keep reference -inf: exponentiate
-      // against 0 so masked scores give exactly 0
-      const float e0 = (m0 == -INFINITY) ? 0.f : m0;
-      const float e1 = (m1 == -INFINITY) ? 0.f : m1;
-      // ---- exponentiate, sum, pack P ----
       bf16x8 pa[2], pb[2];
-      float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-      for (int bl = 0; bl < 4; ++bl) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          s0[bl][r] = fast_exp2(fmaf(s0[bl][r], c, -e0));
-          s1[bl][r] = fast_exp2(fmaf(s1[bl][r], c, -e1));
-          ps0 += s0[bl][r];
-          ps1 += s1[bl][r];
-        }
-        if (bl & 1) {
-          pa[bl >> 1] = pack_pair(s0[bl - 1], s0[bl]);
-          pb[bl >> 1] = pack_pair(s1[bl - 1], s1[bl]);
-        }
+      for (int p = 0; p < 2; ++p) {
+        pa[p] = pack_pair(s0[2 * p], s0[2 * p + 1]);
+        pb[p] = pack_pair(s1[2 * p], s1[2 * p + 1]);
       }
       l0 += ps0;
       l1 += ps1;
