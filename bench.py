@@ -550,28 +550,34 @@ def _stats(ms):
     return {"mean_ms": sum(s) / len(s), "median_ms": s[len(s) // 2], "min_ms": s[0]}
 
 
-def kernel_source_digest() -> str:
-    """Hash of the HIP sources; traffic counters are only reported for the kernel
-    version they were taken on."""
+# Sources each profiled kernel is built from: counters taken on a kernel stay valid
+# while these files are unchanged.
+KERNEL_SOURCES = {
+    "swa_ring_kernel": ("prefill_mfma.hip", "mfma_tile.h", "common.h", "kernels.h"),
+}
+
+
+def kernel_source_digest(kernel: str = "swa_ring_kernel") -> str:
+    """Hash of the HIP sources a kernel is built from; traffic counters are only
+    reported for the kernel version they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sliding_window_attention_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + fh.read())
+    for f in sorted(KERNEL_SOURCES[kernel]):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
 def _traffic(kernel: str, algorithmic_bytes: float):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel sources."""
+    taken on the kernel's current sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f).get(kernel)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_digest") != kernel_source_digest():
+    if not rec or rec.get("source_digest") != kernel_source_digest(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 

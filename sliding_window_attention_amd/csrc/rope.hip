@@ -10,6 +10,8 @@
 // i pairs with i + D/2 at angle pos * base^(-2i/D):
 //   y[i] = x[i] cos - x[i + D/2] sin,   y[i + D/2] = x[i + D/2] cos + x[i] sin,
 // computed in fp32 and rounded to the I/O type.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -17,12 +19,16 @@ namespace swa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPairs = 8;  // pairs per work item of the in-place rotation
+constexpr int kPairs = 8;      // pairs per work item of the in-place rotation
+constexpr int kHeadBatch = 8;  // heads whose loads are in flight together
 
 template <typename T> __device__ __forceinline__ float ldf(const T* p) { return (float)*p; }
 template <typename T> __device__ __forceinline__ T cvt(float x) { return (T)x; }
 
 // Work item (row, group of kPairs pairs): the angles are shared by the row's heads.
+// The heads are taken kHeadBatch at a time, all loads of a batch issued before its
+// first store, so each thread keeps 2 x kHeadBatch 16-byte loads in flight instead of
+// one round trip per head.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a) {
   constexpr int kGroups = D / 2 / kPairs;
@@ -35,19 +41,59 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a) {
 #pragma unroll
   for (int e = 0; e < kPairs; ++e) rope_cos_sin(pos, i0 + e, D, a.log2_base, &c[e], &s[e]);
   T* base = static_cast<T*>(a.x) + (size_t)row * a.heads * D + i0;
-  for (int h = 0; h < a.heads; ++h) {
-    T* x1 = base + (size_t)h * D;
-    T* x2 = x1 + D / 2;
-    float u[kPairs], v[kPairs];
+  using Vec = typename std::conditional<sizeof(T) == 2, u32x4, f32x4>::type;  // kPairs * 2 bytes for bf16
+  constexpr int kVecs = kPairs * (int)sizeof(T) / 16;                         // 16-byte pieces per half
+  auto rotate = [&](const Vec (&xv)[kVecs], const Vec (&yv)[kVecs], Vec (&xo)[kVecs], Vec (&yo)[kVecs]) {
+    T u[kPairs], v[kPairs], uo[kPairs], vo[kPairs];
+    __builtin_memcpy(u, xv, sizeof(u));
+    __builtin_memcpy(v, yv, sizeof(v));
 #pragma unroll
     for (int e = 0; e < kPairs; ++e) {
-      u[e] = ldf(x1 + e);
-      v[e] = ldf(x2 + e);
+      const float fu = (float)u[e], fv = (float)v[e];
+      uo[e] = cvt<T>(fu * c[e] - fv * s[e]);
+      vo[e] = cvt<T>(fv * c[e] + fu * s[e]);
     }
+    __builtin_memcpy(xo, uo, sizeof(uo));
+    __builtin_memcpy(yo, vo, sizeof(vo));
+  };
+  int h = 0;
+  for (; h + kHeadBatch <= a.heads; h += kHeadBatch) {
+    Vec xv[kHeadBatch][kVecs], yv[kHeadBatch][kVecs];
 #pragma unroll
-    for (int e = 0; e < kPairs; ++e) {
-      x1[e] = cvt<T>(u[e] * c[e] - v[e] * s[e]);
-      x2[e] = cvt<T>(v[e] * c[e] + u[e] * s[e]);
+    for (int j = 0; j < kHeadBatch; ++j) {
+      const T* x1 = base + (size_t)(h + j) * D;
+#pragma unroll
+      for (int q = 0; q < kVecs; ++q) {
+        xv[j][q] = *reinterpret_cast<const Vec*>(x1 + q * (16 / sizeof(T)));
+        yv[j][q] = *reinterpret_cast<const Vec*>(x1 + D / 2 + q * (16 / sizeof(T)));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the batch's loads stay ahead of its stores
+#pragma unroll
+    for (int j = 0; j < kHeadBatch; ++j) {
+      Vec xo[kVecs], yo[kVecs];
+      rotate(xv[j], yv[j], xo, yo);
+      T* x1 = base + (size_t)(h + j) * D;
+#pragma unroll
+      for (int q = 0; q < kVecs; ++q) {
+        *reinterpret_cast<Vec*>(x1 + q * (16 / sizeof(T))) = xo[q];
+        *reinterpret_cast<Vec*>(x1 + D / 2 + q * (16 / sizeof(T))) = yo[q];
+      }
+    }
+  }
+  for (; h < a.heads; ++h) {  // the heads past the last whole batch
+    T* x1 = base + (size_t)h * D;
+    Vec xv[kVecs], yv[kVecs], xo[kVecs], yo[kVecs];
+#pragma unroll
+    for (int q = 0; q < kVecs; ++q) {
+      xv[q] = *reinterpret_cast<const Vec*>(x1 + q * (16 / sizeof(T)));
+      yv[q] = *reinterpret_cast<const Vec*>(x1 + D / 2 + q * (16 / sizeof(T)));
+    }
+    rotate(xv, yv, xo, yo);
+#pragma unroll
+    for (int q = 0; q < kVecs; ++q) {
+      *reinterpret_cast<Vec*>(x1 + q * (16 / sizeof(T))) = xo[q];
+      *reinterpret_cast<Vec*>(x1 + D / 2 + q * (16 / sizeof(T))) = yo[q];
     }
   }
 }
