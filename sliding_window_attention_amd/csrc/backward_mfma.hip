@@ -445,6 +445,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
     r += r < 0 ? nsteps : 0;
     return tb_lo + r;
   };
+  // the block of local step 0; later steps advance it by one, wrapping within
+  // [tb_lo, tb_lo + nsteps) (no division per step)
+  const int tb_first = __builtin_amdgcn_readfirstlane(step_block(0));
+  const int tb_wrap = tb_lo + nsteps;
 
   // Lane-constant LDS offsets: row reads (pair order) and transposed reads.
   const int pr0 = pair_row(i, 0), pr1 = pair_row(i, 1);
@@ -461,8 +465,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
     float l, dl;
   };
   Stage sa;
-  auto prefetch = [&](int step, Stage& st) {
-    const int hp = step / nsteps, tb = step_block(step - hp * nsteps);
+  // position of the prefetched step: head quad hp_n, query block tb_n
+  int hp_n = 0, tb_n = tb_first, m_n = 0;
+  auto advance = [&](int& hp, int& tb, int& m) {
+    ++m;
+    ++tb;
+    if (tb == tb_wrap) tb = tb_lo;
+    if (m == nsteps) { m = 0; ++hp; tb = tb_first; }
+  };
+  auto prefetch = [&](Stage& st) {
+    const int hp = hp_n, tb = tb_n;
     const int hbase = kvh * G + kHeads * hp;
     const int q = min(16 * tb + (t >> 4), N - 1);
 #pragma unroll
@@ -502,9 +514,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
 
   // One step: its block is already in LDS buffer step & 1; the next step's loads are
   // issued first and committed to the other buffer at the end.
+  int hp_c = 0, tb_c = tb_first, m_c = 0;  // position of the current step
   auto do_step = [&](int step) {
-    if (step + 1 < total) prefetch(step + 1, sa);
-    const int tb = step_block(step % nsteps);
+    if (step + 1 < total) {
+      advance(hp_n, tb_n, m_n);
+      prefetch(sa);
+    }
+    const int tb = tb_c;
     if (tb >= tbw_lo && tb <= tbw_hi) {
       const char* qs = smem + (step & 1) * kStage;
       const char* ds = qs + kOpBytes;
@@ -574,9 +590,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
     // finished (barrier below)
     if (step + 1 < total) commit((step + 1) & 1, sa);
     __syncthreads();
+    advance(hp_c, tb_c, m_c);
   };
 
-  prefetch(0, sa);
+  prefetch(sa);
   commit(0, sa);
   __syncthreads();
   for (int step = 0; step < total; ++step) do_step(step);
