@@ -118,10 +118,13 @@ void decode_kernel(DecodeArgs a) {
   using CacheT = typename std::conditional<FP8, uint8_t, bf16>::type;
   const CacheT* kc = static_cast<const CacheT*>(a.k_cache) + ((size_t)b * hkv + kvh) * kW * D;
   const CacheT* vc = static_cast<const CacheT*>(a.v_cache) + ((size_t)b * hkv + kvh) * kW * D;
-  // ring operand of 8 elements starting at element e0 of row `phys`
+  // ring operand of 8 elements starting at element e0 of row `phys`.  A decode step reads each ring row once; the
+  // layer's next step comes only after every other layer's cache has streamed through, so the bf16 loads carry the
+  // non-temporal hint and leave the caches to the rows that are re-read within the step (measured faster at every
+  // decode shape; the fp8 loads are 8-byte and were not).
   auto ring8 = [&](const CacheT* base, int phys, int e0) -> bf16x8 {
     if constexpr (FP8) return e4m3x8_to_bf16x8(*reinterpret_cast<const u32x2*>(base + (size_t)phys * D + e0));
-    else return *reinterpret_cast<const bf16x8*>(base + (size_t)phys * D + e0);
+    else return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)phys * D + e0)));
   };
   const bf16* kn = static_cast<const bf16*>(a.k_new) + ((size_t)b * T * hkv + kvh) * D;
   const bf16* vn = static_cast<const bf16*>(a.v_new) + ((size_t)b * T * hkv + kvh) * D;
@@ -362,7 +365,8 @@ void decode_kernel(DecodeArgs a) {
       v8[e] = x[0];
       v8[e + 1] = x[1];
     }
-    *reinterpret_cast<bf16x8*>(out + 8 * q8) = v8;
+    // whole 16-byte runs written once and read by the next kernel long after: streamed past the caches
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v8), reinterpret_cast<u32x4*>(out + 8 * q8));
   }
   if (a.lse != nullptr && d0 == 0) a.lse[row_idx] = (sm.mc[qc] + fast_log2(z)) * kLn2;
 }

@@ -431,15 +431,17 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
     for (int s = 0; s < 2; ++s) {
       const int m = 32 * ch + pair_row(i, s);
       const int j = sm.keys[m < M ? m : M - 1];
+      // each selected row is gathered once per step and not again until the layer's next step: non-temporal
+      // loads, as for the dense decode's ring (measured faster)
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc)
-        kf[s][cc] = *reinterpret_cast<const bf16x8*>(kc + (size_t)j * D + 32 * cc + 8 * g);
+        kf[s][cc] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc + (size_t)j * D + 32 * cc + 8 * g)));
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int m = 32 * ch + 8 * g + e;
       const int j = sm.keys[m < M ? m : M - 1];
-      vr[e] = *reinterpret_cast<const bf16x8*>(vc + (size_t)j * D + 8 * i);
+      vr[e] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc + (size_t)j * D + 8 * i)));
     }
   };
 
