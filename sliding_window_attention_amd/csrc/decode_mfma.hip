@@ -335,20 +335,23 @@ void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // ---- normalise and store, all threads: thread tid owns kPer consecutive head-dim
-  // elements of one query column (qc = token * 8 + head), a 16- or 32-byte
-  // piece of its output row; the 16 or 8 threads of a column cover the row ----
+  // ---- normalise and store, all threads: thread tid owns kPer head-dim elements of one
+  // query column (qc = token * 8 + head) as kPer / 8 runs of 8, run q8 starting at
+  // d0 + 8 * kCol * q8, so that each store instruction's kCol threads of a column write
+  // one contiguous stretch of the output row (whole 128-byte lines per instruction) ----
   constexpr int kPer = NT * 16 * D / kThreads;  // 8 or 16
-  const int qc = tid / (D / kPer);
-  const int d0 = (tid % (D / kPer)) * kPer;
+  constexpr int kCol = D / kPer;                 // threads per output row
+  const int qc = tid / kCol;
+  const int d0 = (tid % kCol) * 8;
   const int t = qc >> 3;
   if (t >= T) return;
   float acc[kPer];
 #pragma unroll
   for (int q4 = 0; q4 < kPer / 4; ++q4) {
-    f32x4 v = *reinterpret_cast<const f32x4*>(&sm.u.o[0][qc][4 * (d0 + 4 * q4)]);
+    const int e0 = d0 + (q4 >> 1) * 8 * kCol + 4 * (q4 & 1);
+    f32x4 v = *reinterpret_cast<const f32x4*>(&sm.u.o[0][qc][4 * e0]);
 #pragma unroll
-    for (int sl = 1; sl < kMergeSlots<NT>; ++sl) v += *reinterpret_cast<const f32x4*>(&sm.u.o[sl][qc][4 * (d0 + 4 * q4)]);
+    for (int sl = 1; sl < kMergeSlots<NT>; ++sl) v += *reinterpret_cast<const f32x4*>(&sm.u.o[sl][qc][4 * e0]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[4 * q4 + e] = v[e];
   }
@@ -365,8 +368,10 @@ void decode_kernel(DecodeArgs a) {
       v8[e] = x[0];
       v8[e + 1] = x[1];
     }
-    // whole 16-byte runs written once and read by the next kernel long after: streamed past the caches
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v8), reinterpret_cast<u32x4*>(out + 8 * q8));
+    // written once and read by the next kernel long after: streamed past the caches.  With these stores a
+    // line that one instruction covers only in part reaches HBM as separate partial writes (half lines
+    // per instruction measured 1.6x the output's bytes), hence the run layout above.
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v8), reinterpret_cast<u32x4*>(out + 8 * kCol * q8));
   }
   if (a.lse != nullptr && d0 == 0) a.lse[row_idx] = (sm.mc[qc] + fast_log2(z)) * kLn2;
 }
