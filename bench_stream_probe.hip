@@ -3,10 +3,13 @@
 // per (sequence, KV head), 64 MiB in all), read once by kernels that do nothing with the
 // data but fold it into 16 bytes per thread, in several workgroup shapes: one
 // workgroup per ring with 128 / 256 / 512 threads, a ring split over 2 / 4 / 8
-// workgroups, and one wavefront per ring streaming it in chunks.  32 input sets (2 GiB)
-// are rotated so that no launch finds its data in the 256 MB Infinity Cache.
+// workgroups, and one wavefront per ring streaming it in chunks; the one-workgroup and
+// split shapes also with the loads marked non-temporal (as the decode's bf16 ring loads
+// are).  32 input sets (2 GiB) are rotated so that no launch finds its data in the
+// 256 MB Infinity Cache.
 //
-//   hipcc --offload-arch=gfx950 -O3 -o /tmp/bench_stream_probe bench_stream_probe.hip
+//   hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops \
+//     -o /tmp/bench_stream_probe bench_stream_probe.hip
 //   /tmp/bench_stream_probe
 //
 // Prints the average time per launch (HIP events over 400 launches) and GB/s.
@@ -19,7 +22,18 @@
 constexpr int kRings = 1024;         // 256 x 4
 constexpr int kUnits = 2048;         // 16-byte units per ring per tensor (32 KB)
 
-template <int THREADS, int SPLIT>
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const uint4* p) {
+  if constexpr (NT) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  } else {
+    return *p;
+  }
+}
+
+template <int THREADS, int SPLIT, bool NT = false>
 __global__ __launch_bounds__(THREADS) void stream_k(const uint4* __restrict__ K, const uint4* __restrict__ V,
                                                      uint4* __restrict__ out) {
   constexpr int PER = kUnits / SPLIT / THREADS;  // units per thread per tensor
@@ -28,9 +42,9 @@ __global__ __launch_bounds__(THREADS) void stream_k(const uint4* __restrict__ K,
   const uint4* vb = V + (size_t)ring * kUnits + part * (kUnits / SPLIT);
   uint4 r[2 * PER];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) r[j] = kb[j * THREADS + threadIdx.x];
+  for (int j = 0; j < PER; ++j) r[j] = load16<NT>(kb + j * THREADS + threadIdx.x);
 #pragma unroll
-  for (int j = 0; j < PER; ++j) r[PER + j] = vb[j * THREADS + threadIdx.x];
+  for (int j = 0; j < PER; ++j) r[PER + j] = load16<NT>(vb + j * THREADS + threadIdx.x);
   uint4 acc = r[0];
 #pragma unroll
   for (int j = 1; j < 2 * PER; ++j) { acc.x ^= r[j].x; acc.y += r[j].y; acc.z ^= r[j].z; acc.w += r[j].w; }
@@ -103,6 +117,13 @@ int main() {
   }
   RUN(256, 1) RUN(512, 1) RUN(128, 1) RUN(256, 2) RUN(128, 2) RUN(64, 4) RUN(128, 4) RUN(256, 4)
   RUN(64, 8) RUN(256, 8) RUN(64, 2)
+#define RUNNT(T, S)                                                                                     \
+  {                                                                                                     \
+    float us = time_it([&](int s) { stream_k<T, S, true><<<kRings * S, T>>>(K[s], V[s], out); }, iters); \
+    printf("stream-nt threads=%4d split=%d  wgs=%5d  bytes/wg=%6d  %7.2f us  %6.0f GB/s\n", T, S,        \
+           kRings * S, 65536 / S, us, bytes / us / 1e3);                                                \
+  }
+  RUNNT(256, 1) RUNNT(128, 1) RUNNT(128, 2) RUNNT(64, 2) RUNNT(64, 4)
 #define RUNW(C)                                                                                   \
   {                                                                                               \
     float us = time_it([&](int s) { stream_wave<C><<<kRings, 64>>>(K[s], V[s], out); }, iters);    \
