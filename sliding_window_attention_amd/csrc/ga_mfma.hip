@@ -40,7 +40,6 @@ constexpr int kVBuf = kStage * kVPitch;  // 33792
 constexpr int kBuf = kKBuf + kVBuf;
 constexpr float kSlack = 8.f;
 constexpr float kSlackPow = 256.f;  // 2^kSlack
-constexpr float kArgCap = 64.f;     // exp2 arguments capped: weights stay finite
 
 // Staged K/V as loaded: 16 bytes of bf16, or (FP8) 8 bytes of E4M3 codes widened to
 // bf16 (exactly) only when committed to LDS, so that no conversion waits on a load.
@@ -234,12 +233,14 @@ void ga_chunk_kernel(PrefillArgs a) {
       };
       scores();
       // ---- exponentiate against the reference maxima and sum.  Once every row of the
-      // wavefront has a finite reference, the chunk is exponentiated directly (the
-      // argument clamped so that no weight is infinite): if no lane's partial sum of a
-      // head exceeds 2^kSlack, no weight does, which is exactly the bound the lazy
-      // rescale keeps, and the weights equal those of the full path below.  Otherwise
-      // the raw scores are formed again and the full path runs: per-lane maxima, the
-      // rescale where a row's maximum outgrew its reference, the exponentials. ----
+      // wavefront has a finite reference, the chunk is exponentiated directly: if no
+      // lane's partial sum of a head exceeds 2^kSlack, no weight does, which is exactly
+      // the bound the lazy rescale keeps, and the weights equal those of the full path
+      // below.  A weight that overflows is +inf (the arguments are finite or -inf, the
+      // weights non-negative, so no NaN arises) and its sum fails the same test.
+      // Otherwise the raw scores are formed again and the full path runs: per-lane
+      // maxima, the rescale where a row's maximum outgrew its reference, the
+      // exponentials. ----
       float ps0 = 0.f, ps1 = 0.f;
       bool need_max = !ready;
       if (!need_max) {
@@ -247,8 +248,8 @@ void ga_chunk_kernel(PrefillArgs a) {
         for (int bl = 0; bl < 4; ++bl)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            s0[bl][r] = fast_exp2(fminf(fmaf(s0[bl][r], c, -m0), kArgCap));
-            s1[bl][r] = fast_exp2(fminf(fmaf(s1[bl][r], c, -m1), kArgCap));
+            s0[bl][r] = fast_exp2(fmaf(s0[bl][r], c, -m0));
+            s1[bl][r] = fast_exp2(fmaf(s1[bl][r], c, -m1));
             ps0 += s0[bl][r];
             ps1 += s1[bl][r];
           }
