@@ -199,7 +199,8 @@ void ga_chunk_kernel(PrefillArgs a) {
       // ---- S^T = K Q^T over 4 blocks of 16 keys (2 pairs), masked where a row's
       // window or the causal edge cuts the chunk ----
       f32x4 s0[4], s1[4];
-      auto scores = [&]() {
+      const bool full = kb >= lo_w_max && kb + kChunk - 1 <= qw;  // (uniform) no row is cut
+      auto products = [&]() {
         // Raised issue priority over the MFMA runs: the two waves sharing a SIMD then
         // tend to alternate matrix work with the other's softmax instead of colliding.
         __builtin_amdgcn_s_setprio(1);
@@ -217,21 +218,23 @@ void ga_chunk_kernel(PrefillArgs a) {
           }
         }
         __builtin_amdgcn_s_setprio(0);
-        const bool full = kb >= lo_w_max && kb + kChunk - 1 <= qw;
-        if (!full) {
-          const unsigned span = (unsigned)(qi - lo);
-#pragma unroll
-          for (int bl = 0; bl < 4; ++bl)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = kb + 32 * (bl >> 1) + 8 * g + 4 * (bl & 1) + r;
-              const bool ok = (unsigned)(key - lo) <= span;
-              s0[bl][r] = ok ? s0[bl][r] : -INFINITY;
-              s1[bl][r] = ok ? s1[bl][r] : -INFINITY;
-            }
-        }
       };
-      scores();
+      auto mask = [&]() {
+        const unsigned span = (unsigned)(qi - lo);
+#pragma unroll
+        for (int bl = 0; bl < 4; ++bl)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kb + 32 * (bl >> 1) + 8 * g + 4 * (bl & 1) + r;
+            const bool ok = (unsigned)(key - lo) <= span;
+            s0[bl][r] = ok ? s0[bl][r] : -INFINITY;
+            s1[bl][r] = ok ? s1[bl][r] : -INFINITY;
+          }
+      };
+      auto scores = [&]() {
+        products();
+        if (!full) mask();
+      };
       // ---- exponentiate against the reference maxima and sum.  Once every row of the
       // wavefront has a finite reference, the chunk is exponentiated directly: if no
       // lane's partial sum of a head exceeds 2^kSlack, no weight does, which is exactly
@@ -240,10 +243,11 @@ void ga_chunk_kernel(PrefillArgs a) {
       // weights non-negative, so no NaN arises) and its sum fails the same test.
       // Otherwise the raw scores are formed again and the full path runs: per-lane
       // maxima, the rescale where a row's maximum outgrew its reference, the
+      // exponentials.  The common case (references ready, no row cut by the chunk) is
+      // tested before the products, so that no mask branch splits them from the
       // exponentials. ----
       float ps0 = 0.f, ps1 = 0.f;
-      bool need_max = !ready;
-      if (!need_max) {
+      auto fast = [&]() {
 #pragma unroll
         for (int bl = 0; bl < 4; ++bl)
 #pragma unroll
@@ -253,8 +257,20 @@ void ga_chunk_kernel(PrefillArgs a) {
             ps0 += s0[bl][r];
             ps1 += s1[bl][r];
           }
+      };
+      bool need_max = !ready;
+      if (ready && full) {
+        products();
+        fast();
         need_max = __builtin_amdgcn_ballot_w64(fmaxf(ps0, ps1) > kSlackPow) != 0;
-        if (need_max) scores();
+        if (need_max) products();
+      } else {
+        scores();
+        if (!need_max) {
+          fast();
+          need_max = __builtin_amdgcn_ballot_w64(fmaxf(ps0, ps1) > kSlackPow) != 0;
+          if (need_max) scores();
+        }
       }
       if (need_max) {
         float mx0 = -INFINITY, mx1 = -INFINITY;
