@@ -906,8 +906,10 @@ def run_extra(dev, steps, warmup):
     st = _stats(per)
     fl = wl.backward_flops([32768], 32, 128, 128)
     by = wl.backward_bytes(32768, 32, 4, 128, 2)
+    by_out = wl.backward_bytes(32768, 32, 4, 128, 2, with_out=True)  # with the forward output read too
     extra["backward_32k"] = {**st, "tflops": fl / (st["mean_ms"] * 1e-3) / 1e12,
-                             "gbps": by / (st["mean_ms"] * 1e-3) / 1e9, "flops": fl, "bytes": by}
+                             "gbps": by / (st["mean_ms"] * 1e-3) / 1e9, "flops": fl, "bytes": by,
+                             "bytes_with_out": by_out}
     del x
     torch.cuda.empty_cache()
 

@@ -171,16 +171,20 @@ SWASINK_API int swa_sink_decode_fp8kv(const void* q, const void* k_new, const vo
  * dL/dv and dL/dsinks, where the sink is the learnable per-head scalar of the
  * technical report digest, section 2.2.2 (the ICML keynote's Q&A, section 06, names
  * its training stability as critical).  With p_ij the forward weights and
- * p_s(i) = exp(sink - lse_i) the sink's: delta_i = dout_i . out_i,
+ * p_s(i) = exp(sink - lse_i) the sink's: delta_i = dout_i . O_i,
  * da_ij = p_ij (dout_i . v_j - delta_i), dq_i = scale sum_j da_ij k_j,
  * dk_j = scale sum_i da_ij q_i, dv_j = sum_i p_ij dout_i (dk, dv summed over the
  * query heads of each KV head), dsink_h = -sum_i p_s(i) delta_i.  The LSE output is
- * not differentiated.
+ * not differentiated.  Since O_i = sum_j p_ij v_j (the sink carries no value),
+ * delta_i = sum_j p_ij (dout_i . v_j): the matrix-core path (bf16, head_dim 128,
+ * query heads per KV head a multiple of 8, window <= 128) forms it that way from the
+ * weights it recomputes and does not read `out`; the other shapes take it from `out`.
  *
  *  q, k, v, sinks, cu_seqlens, num_seqs, total_tokens, max_seqlen, heads, head_dim,
  *  window, scale, dtype: as swa_sink_prefill; sinks may be NULL (no sink, e.g. a GA
  *  layer with window >= the longest sequence), and then dsinks must be NULL too.
- *  out   [total_tokens, num_q_heads, head_dim] dtype: the forward output
+ *  out   [total_tokens, num_q_heads, head_dim] dtype: the forward output (required;
+ *        read only where delta is taken from it, see above)
  *  lse   [total_tokens, num_q_heads] fp32: the forward log-sum-exp (required)
  *  dout  like out
  *  dq    like q;  dk, dv like k, v;  dsinks [num_q_heads] fp32 (written, not added to)

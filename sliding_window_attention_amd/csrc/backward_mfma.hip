@@ -14,8 +14,10 @@
 //    tokens x 8 heads sharing one KV head (one head per wavefront), the 144-key band
 //    sits in an LDS ring that advances by 16 keys per tile.  S^T = K Q^T and dP^T = V dO^T come out with
 //    queries in columns, so dS^T feeds dQ^T = K^T dS^T straight from registers.  It
-//    also forms delta = dO . O of its rows (reading O beside dO) and writes it, with
-//    the sink's term, for the dk/dv kernel and the sink gradient.
+//    also forms delta of its rows as sum_j p_ij dP_ij over the row's keys, which is
+//    dO . O for the exact O (O = sum_j p_ij v_j: the sink carries no value), so O is
+//    not read; delta is written, with the sink's term, for the dk/dv kernel and the
+//    sink gradient.
 //  * bwd_dkdv_kernel: the transpose -- a workgroup owns 64 keys of one KV head (16
 //    per wavefront) and walks the (head quad, query block) steps that see them, one
 //    LDS-staged block of 16 tokens x 4 heads per step shared by the four wavefronts.
@@ -166,7 +168,6 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
   const bf16* vp = static_cast<const bf16*>(a.v);
   const bf16* qp = static_cast<const bf16*>(a.q);
   const bf16* dop = static_cast<const bf16*>(a.dout);
-  const bf16* op = static_cast<const bf16*>(a.out);
   const float c = a.scale * kLog2e;
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
@@ -174,11 +175,11 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
   const int vrow = 8 * (g & 1) + (i >> 2);                  // key row of the transposed reads, pairs
   const int vrow8 = 8 * (g & 1) + 4 * (g >> 1) + (i >> 2);  // the single diagonal block
 
-  // Q, dO and O of one tile (lane (i, g): head-dim 32cc + 8g .. +8 of query q0 + i,
+  // Q and dO of one tile (lane (i, g): head-dim 32cc + 8g .. +8 of query q0 + i,
   // head w of the octet) with the row's lse.  Rows past the stream are loaded from the
   // last token (their results are never stored), so the loads are unconditional and
   // nothing waits for them before their first use.
-  bf16x8 qa[4], da[4], oa[4];
+  bf16x8 qa[4], da[4];
   float lr;
   auto load_rows = [&](int q0n, int octn) {
     const int qi = min(q0n + i, N - 1);
@@ -188,7 +189,6 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
     for (int cc = 0; cc < 4; ++cc) {
       qa[cc] = *reinterpret_cast<const bf16x8*>(qp + r0 + 32 * cc);
       da[cc] = *reinterpret_cast<const bf16x8*>(dop + r0 + 32 * cc);
-      oa[cc] = *reinterpret_cast<const bf16x8*>(op + r0 + 32 * cc);
     }
     lr = a.lse[hr];
   };
@@ -236,13 +236,47 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
       const int rel_lo = lo - kbase;
       const unsigned span = (unsigned)(qi - kbase - rel_lo);
       const float l2 = lr * kLog2e;
-      // delta = dO . O of the lane's row: 32 elements per lane, then the row's 4 lanes;
-      // written once (with the sink's term) for the dk/dv kernel and the sink gradient
+      const int ko0 = pr0 * 64 + 16 * (g ^ kswz(16 * par + pr0)) - (i >= 8 ? 16 * 64 : 0);
+      const int ko1 = pr1 * 64 + 16 * (g ^ kswz(16 * par + pr1)) - (i >= 8 ? 16 * 64 : 0);
+      const int ko8 = p8 * 64 + 16 * (g ^ kswz(16 * par + p8));
+      auto block_off = [&](int bl) {
+        if (bl < 8) {
+          const int p = bl >> 1;
+          return (i >= 8 ? sk[2 * p + 1] : sk[2 * p]) + ((bl & 1) ? ko1 : ko0);
+        }
+        return sk[8] + ko8;
+      };
+      // S^T = K Q^T and dP^T = V dO^T of block bl, the weights p formed in place of S
+      auto products = [&](int bl, f32x4& s0, f32x4& t0) {
+        const int off = block_off(bl);
+        s0 = zero4;
+        t0 = zero4;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + cc * kPlane + off);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + cc * kPlane + off);
+          s0 = mfma32(kf, qa[cc], s0);
+          t0 = mfma32(vf, da[cc], t0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kr = bl < 8 ? 32 * (bl >> 1) + 8 * g + 4 * (bl & 1) + r
+                                : 128 + 8 * (g & 1) + 4 * (g >> 1) + r;
+          const bool ok = (unsigned)(kr - rel_lo) <= span;
+          const float e = fast_exp2(fmaf(s0[r], c, -l2));
+          s0[r] = ok ? e : 0.f;
+        }
+      };
+      // ---- p and dP of every block, delta = sum_j p_j dP_j over the row's keys (equal
+      // to dO . O: the sink carries no value), then dS^T = p (dP - delta) in bf16 ----
+      f32x4 ps[9], ts[9];
+#pragma unroll
+      for (int bl = 0; bl < 9; ++bl) products(bl, ps[bl], ts[bl]);
       float dl = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
+      for (int bl = 0; bl < 9; ++bl)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dl = fmaf((float)oa[cc][e], (float)da[cc][e], dl);
+        for (int r = 0; r < 4; ++r) dl = fmaf(ps[bl][r], ts[bl][r], dl);
       dl += __shfl_xor(dl, 16);
       dl += __shfl_xor(dl, 32);
       if (g == 0 && qi < N) {
@@ -250,41 +284,15 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
         a.delta[hr] = dl;
         if (a.sinks) a.sink_term[hr] = expf(a.sinks[h0] - lr) * dl;
       }
-
-      // ---- per 16-key block: S^T = K Q^T, dP^T = V dO^T, then dS^T in bf16 ----
       bf16x8 sa[4];
       bf16x4 sa8;
       {
-        const int ko0 = pr0 * 64 + 16 * (g ^ kswz(16 * par + pr0)) - (i >= 8 ? 16 * 64 : 0);
-        const int ko1 = pr1 * 64 + 16 * (g ^ kswz(16 * par + pr1)) - (i >= 8 ? 16 * 64 : 0);
-        const int ko8 = p8 * 64 + 16 * (g ^ kswz(16 * par + p8));
         f32x4 x_prev;
 #pragma unroll
         for (int bl = 0; bl < 9; ++bl) {
-          int off;
-          if (bl < 8) {
-            const int p = bl >> 1;
-            off = (i >= 8 ? sk[2 * p + 1] : sk[2 * p]) + ((bl & 1) ? ko1 : ko0);
-          } else {
-            off = sk[8] + ko8;
-          }
-          f32x4 s0 = zero4, t0 = zero4;
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + cc * kPlane + off);
-            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + cc * kPlane + off);
-            s0 = mfma32(kf, qa[cc], s0);
-            t0 = mfma32(vf, da[cc], t0);
-          }
           f32x4 x;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int kr = bl < 8 ? 32 * (bl >> 1) + 8 * g + 4 * (bl & 1) + r
-                                  : 128 + 8 * (g & 1) + 4 * (g >> 1) + r;
-            const bool ok = (unsigned)(kr - rel_lo) <= span;
-            const float e = fast_exp2(fmaf(s0[r], c, -l2));
-            x[r] = (ok ? e : 0.f) * (t0[r] - dl);
-          }
+          for (int r = 0; r < 4; ++r) x[r] = ps[bl][r] * (ts[bl][r] - dl);
           if (bl == 8) {
             sa8 = pack_quad(x);
           } else if (bl & 1) {
@@ -296,7 +304,7 @@ __global__ __launch_bounds__(dqring::kThreads, 2) void bwd_dq_ring_kernel(Backwa
       }
 
       // ---- prefetch for the next tile: the 16 K/V rows it adds to the ring (waves 0-3;
-      // its newest block walking up, its oldest walking down), its Q, dO, lse, delta ----
+      // its newest block walking up, its oldest walking down), its Q, dO and lse ----
       const bool has_next = k + 1 < run_len;
       u32x4 pk = {0, 0, 0, 0}, pv = {0, 0, 0, 0};
       const int nkey = (down ? q0 - 144 : q0 + 16) + (t >> 4);

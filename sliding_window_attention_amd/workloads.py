@@ -359,11 +359,13 @@ def backward_flops(lengths, num_q_heads, head_dim, window) -> int:
     return 10 * head_dim * num_q_heads * sum(pairs(l, window) for l in lengths)
 
 
-def backward_bytes(total_tokens, num_q_heads, num_kv_heads, head_dim, elem_bytes):
-    """q, out, dout, dq ([N, Hq, D]); k, v, dk, dv ([N, Hkv, D]); the fp32 LSE: each
-    read or written once."""
-    return (4 * total_tokens * num_q_heads * head_dim * elem_bytes
-            + 4 * total_tokens * num_kv_heads * head_dim * elem_bytes + 4 * total_tokens * num_q_heads)
+def backward_bytes(total_tokens, num_q_heads, num_kv_heads, head_dim, elem_bytes, with_out=False):
+    """q, dout, dq ([N, Hq, D]); k, v, dk, dv ([N, Hkv, D]); the fp32 LSE: each read or
+    written once.  The forward output `out` is counted only with with_out: the matrix-core
+    backward forms delta_i = dout_i . O_i as sum_j p_ij (dout_i . v_j) from the weights it
+    recomputes and does not read it."""
+    nq = (4 if with_out else 3) * total_tokens * num_q_heads * head_dim * elem_bytes
+    return nq + 4 * total_tokens * num_kv_heads * head_dim * elem_bytes + 4 * total_tokens * num_q_heads
 
 
 def decode_flops(batch, t_new, num_q_heads, head_dim, window) -> int:
