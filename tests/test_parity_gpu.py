@@ -733,8 +733,9 @@ INT_MAX = 2 ** 31 - 1
 def assert_grads_close(dtype, got, ref, what):
     """Gradient bar derived from the arithmetic: fp32 accumulation on exact inputs, outputs
     rounded to the I/O type (bf16: 2^-9 relative), and delta = dO . O taken on the forward output
-    as stored (bf16-rounded), so bf16 errors are a few 2^-9 of the largest gradient: max-abs
-    <= 1e-2 * max(1, max |ref|) and rel-L2 <= 1e-2; fp32: 1e-4 and 1e-5."""
+    as stored (bf16-rounded; the matrix-core path forms delta from its recomputed weights
+    instead, which only brings it closer to the oracle's), so bf16 errors are a few 2^-9 of the
+    largest gradient: max-abs <= 1e-2 * max(1, max |ref|) and rel-L2 <= 1e-2; fp32: 1e-4 and 1e-5."""
     g = to_np(got).astype(np.float64)
     r = np.asarray(ref, dtype=np.float64)
     assert g.shape == r.shape, (what, g.shape, r.shape)
@@ -776,9 +777,11 @@ def _backward_case(lens, hq, hkv, d, dt, window, sink=True, seed=0):
     assert_grads_close(td, dk, rk, f"dk {tag}")
     assert_grads_close(td, dv, rv, f"dv {tag}")
     if sink:
-        # dsink_h = -sum_i p_s(i) delta_i with delta_i = dO_i . O_i taken on O as stored: rounding
-        # each O element (2^-9 relative in bf16, 2^-24 in fp32) moves dsink_h by at most
-        # u * sum_i p_s(i) sum_d |dO_id O_id|; the bar is twice that plus fp32 accumulation slack
+        # dsink_h = -sum_i p_s(i) delta_i with delta_i = dO_i . O_i taken on O as stored (the
+        # vector path; the matrix-core path forms delta from its recomputed weights, nearer the
+        # oracle's): rounding each O element (2^-9 relative in bf16, 2^-24 in fp32) moves dsink_h
+        # by at most u * sum_i p_s(i) sum_d |dO_id O_id|; the bar is twice that plus fp32
+        # accumulation slack
         u = 2.0 ** -9 if td == torch.bfloat16 else 2.0 ** -24
         p_s = np.exp(x["sinks"].double().numpy()[None, :] - l_ref)          # [N, Hq]
         mag = (np.abs(dout.double().numpy()) * np.abs(o_ref)).sum(axis=2)   # [N, Hq]
