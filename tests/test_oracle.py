@@ -670,6 +670,30 @@ def test_backward_shift_invariance_and_gqa():
         assert abs(logit_grad_sum + ds[h]) < 1e-12
 
 
+def test_backward_delta_equals_weighted_value_products():
+    """delta_i = dO_i . O_i equals sum_j p_ij (dO_i . v_j) with p_ij = exp(a_ij - lse_i) the key
+    weights and lse the forward's (sink included): O_i = sum_j p_ij v_j because the sink carries
+    no value.  The matrix-core backward forms delta this way; checked on the forward oracle's O
+    and LSE, with key positions and masks brute-forced from the definition."""
+    rng = np.random.default_rng(11)
+    n, hq, hkv, d, w = 23, 4, 2, 8, 6
+    cu = np.array([0, 9, 9, 23])
+    q, k, v = (rng.standard_normal((n, h, d)) for h in (hq, hkv, hkv))
+    s = rng.standard_normal(hq) * 3
+    do = rng.standard_normal((n, hq, d))
+    o, lse = orc.swa_sink_prefill(q, k, v, s, cu, w)
+    scale = 1.0 / math.sqrt(d)
+    g = hq // hkv
+    for i in range(n):
+        seq = int(np.searchsorted(cu, i, side="right")) - 1
+        keys = range(max(int(cu[seq]), i - w + 1), i + 1)
+        for h in range(hq):
+            p = np.array([math.exp(scale * float(q[i, h] @ k[j, h // g]) - lse[i, h]) for j in keys])
+            dp = np.array([float(do[i, h] @ v[j, h // g]) for j in keys])
+            assert abs(float(p @ dp) - float(do[i, h] @ o[i, h])) < 1e-12
+            assert abs(p.sum() + math.exp(s[h] - lse[i, h]) - 1.0) < 1e-12
+
+
 # ---------------------------------------------------------------------------
 # RoPE around decode: rotation, decode with rotated inputs, ring append
 # (bases: Technical Report digest, section 3.1; rotate-half reading)
