@@ -840,6 +840,61 @@ def test_backward_32k_layer():
     _backward_case([32768], 32, 4, 128, "bf16", 128, True, seed=wl.WORKLOADS["swa_prefill_32k"].seed)
 
 
+def test_backward_max_size_sampled():
+    """Backward of a 2^21 + 37-token stream in 2 sequences (q, dout, dq byte offsets past
+    2^33), on sampled outputs: dq of (token, head) rows and dk, dv of (key, KV head) rows,
+    each from the oracle's backward of the tokens around it -- dq_t depends only on row t's
+    window, dk_j and dv_j only on queries j .. j + 127 of j's sequence, whose windows lie in
+    the window before j -- so each small problem gives exactly the values of the full one.
+    The GPU backward takes its out and lse from the library's forward (its inputs, as in the
+    bench); every expected value comes from the oracle on the seeded q, k, v and dout.  The
+    sink gradient sums over every token and is checked at full size by the 32K test."""
+    import bisect
+
+    n1, n = 1_300_001, (1 << 21) + 37
+    _say(f"backward {n} tokens in 2 sequences, 32/4 D128 W128: byte offsets past 2^33")
+    x = wl.make_prefill_device([n1, n - n1], 32, 4, 128, seed=6400, device=DEV)
+    gen = torch.Generator(device=DEV).manual_seed(6401)
+    dout = wl._randn_device(x["q"].shape, gen, DEV, torch.bfloat16)
+    sinks, cu_d = x["sinks"].to(DEV), x["cu_seqlens"].to(DEV)
+    out, lse = swa.swa_sink_prefill(x["q"], x["k"], x["v"], sinks, cu_d, x["max_seqlen"], window=128)
+    dq, dk, dv, _ = swa.swa_sink_prefill_backward(x["q"], x["k"], x["v"], sinks, cu_d, out, lse, dout,
+                                                  x["max_seqlen"], window=128)
+    torch.cuda.synchronize()
+    del out, lse
+    cu = x["cu_seqlens"].tolist()
+    per_tok = 32 * 128
+    special = [0, 1, 127, 128, (1 << 31) // per_tok, (1 << 32) // per_tok - 1, (1 << 32) // per_tok,
+               n1 - 1, n1, n1 + 1, n1 + 128, n - 1]
+    rng = np.random.default_rng(6400)
+    toks = special + [int(t) for t in rng.integers(0, n, 12)]
+
+    def local(a, b):  # oracle backward of tokens a .. b (one sequence)
+        sl = slice(a, b + 1)
+        return orc.swa_sink_prefill_backward(x["q"][sl].cpu(), x["k"][sl].cpu(), x["v"][sl].cpu(),
+                                             x["sinks"], np.array([0, b - a + 1]), dout[sl].cpu(), window=128)
+
+    got_q, ref_q, got_kv, ref_k, ref_v = [], [], [], [], []
+    for t in toks:
+        s0 = cu[bisect.bisect_right(cu, t) - 1]
+        s1 = cu[bisect.bisect_right(cu, t)]
+        a = max(s0, t - 127)
+        rq, _, _, _ = local(a, t)                      # row t's window is whole
+        got_q.append(to_np(dq[t]))
+        ref_q.append(rq[t - a])
+        b = min(s1 - 1, t + 127)
+        _, rk, rv, _ = local(a, b)                     # every query that sees key t
+        got_kv.append((to_np(dk[t]), to_np(dv[t])))
+        ref_k.append(rk[t - a])
+        ref_v.append(rv[t - a])
+    tag = f"{n} tokens, {len(toks)} sampled tokens"
+    assert_grads_close(torch.bfloat16, torch.tensor(np.array(got_q)), np.array(ref_q), f"dq {tag}")
+    assert_grads_close(torch.bfloat16, torch.tensor(np.array([g[0] for g in got_kv])), np.array(ref_k), f"dk {tag}")
+    assert_grads_close(torch.bfloat16, torch.tensor(np.array([g[1] for g in got_kv])), np.array(ref_v), f"dv {tag}")
+    del x, dout, dq, dk, dv
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------------------
 # rotary embedding around decode: in place, inside the decode, ring append
 # ---------------------------------------------------------------------------
