@@ -57,7 +57,7 @@ typedef enum {
 
 typedef enum { SWA_DTYPE_F32 = 0, SWA_DTYPE_BF16 = 1 } swa_dtype;
 
-#define SWASINK_ABI_VERSION 8
+#define SWASINK_ABI_VERSION 9
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SWASINK_API __attribute__((visibility("default")))
@@ -303,6 +303,44 @@ SWASINK_API int swa_ring_append_rope(const void* k_new, const void* v_new, const
                     const int32_t* positions, void* k_cache, void* v_cache, int32_t* ring_head,
                     int32_t batch, int32_t T, int32_t num_kv_heads, int32_t head_dim,
                     int32_t window, float rope_base, swa_dtype dtype, void* stream);
+
+/*
+ * One MTP step in one call (MTP verification: technical report digest, section 2.3;
+ * RoPE: section 3.1): the previous step's accepted tokens are committed to the ring,
+ * then the T new tokens are verified against the ring so updated.  The results -- out,
+ * lse, the caches and the new head -- are those of swa_ring_append_rope(prev_k, prev_v,
+ * prev_accept, prev_positions, k_cache, v_cache, head, prev_T) followed by
+ * swa_sink_decode_rope(q, k_new, v_new, k_cache, v_cache, head, positions), where head
+ * starts as a copy of ring_head, with one difference: ring_head is only read, and the
+ * head after the commit is written to ring_head_out (so the next step passes
+ * ring_head_out as its ring_head and this step's k_new / v_new / positions as its
+ * prev_k / prev_v / prev_positions).
+ *
+ *  prev_k, prev_v   [batch, prev_T, num_kv_heads, head_dim] dtype: the previous step's
+ *                   new tokens, keys unrotated
+ *  prev_accept      [batch] int32 device array: tokens of the previous step to commit,
+ *                   clamped to [0, prev_T] (0 for the first step of a sequence)
+ *  prev_positions   [batch] int32 device array: position of the previous step's token
+ *                   0; may be NULL when rope_base == 0
+ *  prev_T           1 <= prev_T < window
+ *  k_cache, v_cache [batch, num_kv_heads, window, head_dim] dtype, updated in place
+ *  ring_head        [batch] int32 device array, read only
+ *  ring_head_out    [batch] int32 device array, written; must not be ring_head
+ * Every other argument is as for swa_sink_decode_rope.  With bf16, head_dim 128,
+ * window 128, num_q_heads / num_kv_heads a multiple of 8, T <= 4, prev_T <= 4 and
+ * rope_base > 0 the step is one kernel launch (the verify reads the committed tokens'
+ * rows from prev_k / prev_v); otherwise it runs as the copy of the head and the two
+ * calls above, in order on the stream.  prev_k / prev_v must not overlap the caches.
+ * batch == 0 is accepted once the sizes validate (pointers may then be NULL).  Calls
+ * that touch the same sequences must not overlap.
+ */
+SWASINK_API int swa_sink_decode_rope_commit(const void* q, const void* k_new, const void* v_new,
+                    const int32_t* positions, const void* prev_k, const void* prev_v,
+                    const int32_t* prev_accept, const int32_t* prev_positions, int32_t prev_T,
+                    void* k_cache, void* v_cache, const int32_t* ring_head, int32_t* ring_head_out,
+                    const float* sinks, int32_t batch, int32_t T, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t window, float scale,
+                    float rope_base, swa_dtype dtype, void* out, float* lse, void* stream);
 
 /*
  * swa_ring_append_rope into an FP8 ring (the E4M3 caches swa_sink_decode_fp8kv

@@ -34,7 +34,8 @@ rounded once to the nearest E4M3 value with ties to the even mantissa, saturatin
 448 (e4m3_encode: the pages name the format, not the rounding, so this is the
 plainest reading of a rounding conversion).
 
-RoPE around decode (swa_rope, swa_sink_decode_rope, swa_ring_append_rope): the
+RoPE around decode (swa_rope, swa_sink_decode_rope, swa_ring_append_rope, and the MTP
+step swa_sink_decode_rope_commit, which is the append followed by the decode): the
 rotary position embedding with a per-layer base (10,000 in SWA layers, 640,000 in
 GA layers, raised to 5,000,000 for the 256K stage: MiMo-V2-Flash Technical Report
 digest, section 3.1; the positions keep increasing as the window slides, ICML 2026
@@ -475,6 +476,24 @@ def swa_ring_append_rope(k_new, v_new, n_accept, positions, k_cache, v_cache, ri
             vc[b, :, slot, :] = v_new[b, t]
         new_heads[b] = (heads[b] + n) % w
     return kc, vc, new_heads
+
+
+def swa_sink_decode_rope_commit(q, k_new, v_new, positions, prev_k, prev_v, prev_accept, prev_positions,
+                                k_cache, v_cache, ring_head, sinks, rope_base, window=128, scale=None,
+                                io_dtype="bf16"):
+    """One MTP step (technical report digest, section 2.3): the previous step's accepted
+    tokens enter the ring, then the step's T tokens are verified against the ring so
+    updated.  The commit is swa_ring_append_rope of the first prev_accept[b] (clamped to
+    [0, prev_T]) of prev_k / prev_v at prev_positions[b] + t; the verify is
+    swa_sink_decode_rope of q / k_new / v_new at positions[b] + t.  Returns (out, lse,
+    k_cache, v_cache, ring_head) with the caches and head after the commit."""
+    prev_k = _as_f64(prev_k)
+    n = np.clip(np.asarray(prev_accept, dtype=np.int64).reshape(-1), 0, prev_k.shape[1])
+    kc, vc, heads = swa_ring_append_rope(prev_k, prev_v, n, prev_positions, k_cache, v_cache, ring_head,
+                                         rope_base, io_dtype=io_dtype)
+    out, lse = swa_sink_decode_rope(q, k_new, v_new, kc, vc, heads, positions, sinks, rope_base,
+                                    window=window, scale=scale, io_dtype=io_dtype)
+    return out, lse, kc, vc, heads
 
 
 def swa_ring_append_fp8kv(k_new, v_new, n_accept, positions, k_codes, v_codes, ring_head, rope_base,

@@ -49,6 +49,8 @@ _SIGNATURES = {
                              _P, _P, _P],
     "swa_sink_decode_rope_fp8kv": [_P, _P, _P, _P, _P, _F, _F, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F,
                                    _F, _I, _P, _P, _P],
+    "swa_sink_decode_rope_commit": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                    _I, _I, _F, _F, _I, _P, _P, _P],
     "swa_ring_append_rope": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P],
     "swa_ring_append_fp8kv": [_P, _P, _P, _P, _P, _P, _F, _F, _P, _I, _I, _I, _I, _I, _F, _I, _P],
     "swa_topk_select": [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P],
@@ -354,6 +356,48 @@ def swa_sink_decode_rope(q, k_new, v_new, k_cache, v_cache, ring_head, positions
         q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         ring_head.data_ptr(), positions.data_ptr(), sinks.data_ptr(), b, t, hq, hkv, d, w,
         _scale(scale), float(rope_base), _dtype_code(q), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def swa_sink_decode_rope_commit(q, k_new, v_new, positions, prev_k, prev_v, prev_accept, prev_positions,
+                                k_cache, v_cache, ring_head, ring_head_out, sinks, rope_base=ROPE_BASE_SWA,
+                                scale=None, return_lse=True, out=None, lse=None):
+    """One MTP step: commit the previous step's first prev_accept[b] tokens (prev_k, prev_v
+    [B, prev_T, Hkv, D], keys unrotated, token 0 at prev_positions[b]) to the ring, then
+    verify the T new tokens against it as swa_sink_decode_rope does.  The caches are
+    updated in place; ring_head is read and the new head written to ring_head_out."""
+    import torch
+
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (prev_k, "prev_k"), (prev_v, "prev_v"),
+                  (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, nm, q.dtype)
+    for t, nm in ((ring_head, "ring_head"), (ring_head_out, "ring_head_out"), (positions, "positions"),
+                  (prev_accept, "prev_accept"), (prev_positions, "prev_positions")):
+        _dev(t, nm, torch.int32)
+    _dev(sinks, "sinks", torch.float32)
+    if q.dim() != 4 or k_new.dim() != 4 or prev_k.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q, k_new, prev_k must be [B, T, H, D] and caches [B, Hkv, W, D]")
+    b, t, hq, d = q.shape
+    hkv, w = k_cache.shape[1], k_cache.shape[2]
+    pt = prev_k.shape[1]
+    if (k_new.shape != (b, t, hkv, d) or v_new.shape != k_new.shape or prev_k.shape != (b, pt, hkv, d)
+            or prev_v.shape != prev_k.shape or v_cache.shape != k_cache.shape or k_cache.shape[0] != b
+            or k_cache.shape[3] != d or ring_head.numel() != b or ring_head_out.numel() != b
+            or positions.numel() != b or prev_accept.numel() != b or prev_positions.numel() != b
+            or sinks.numel() != hq):
+        raise ValueError("inconsistent shapes")
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    if return_lse and lse is None:
+        lse = torch.empty((b, t, hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+    rc = library().swa_sink_decode_rope_commit(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), positions.data_ptr(), prev_k.data_ptr(),
+        prev_v.data_ptr(), prev_accept.data_ptr(), prev_positions.data_ptr(), pt, k_cache.data_ptr(),
+        v_cache.data_ptr(), ring_head.data_ptr(), ring_head_out.data_ptr(), sinks.data_ptr(), b, t, hq,
+        hkv, d, w, _scale(scale), float(rope_base), _dtype_code(q), out.data_ptr(),
         lse.data_ptr() if lse is not None else None, _stream(q.device))
     _check(rc)
     return out, lse

@@ -133,12 +133,29 @@ int check_rope_base(float base, const char* name) {
   return 0;
 }
 
+// The previous MTP step's tokens that a decode commits to the ring before it verifies.
+struct CommitIn {
+  const void* prev_k;
+  const void* prev_v;
+  const int32_t* prev_accept;
+  const int32_t* prev_pos;
+  int32_t prev_t;
+  int32_t* ring_head_out;
+};
+
+int ring_append_common(const void* k_new, const void* v_new, const int32_t* n_accept,
+                       const int32_t* positions, void* k_cache, void* v_cache, int32_t* ring_head,
+                       int32_t batch, int32_t T, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t window, float rope_base, swa_dtype dtype, void* stream, const char* name,
+                       bool fp8 = false, float k_scale = 1.f, float v_scale = 1.f);
+
 int decode_common(const void* q, const void* k_new, const void* v_new, const void* k_cache,
                   const void* v_cache, bool fp8, float k_scale, float v_scale,
                   const int32_t* ring_head, const float* sinks, int32_t batch, int32_t T,
                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t window,
                   float scale, int dtype, void* out, float* lse, void* stream, const char* name,
-                  const int32_t* rope_pos = nullptr, float rope_base = 0.f) {
+                  const int32_t* rope_pos = nullptr, float rope_base = 0.f,
+                  const CommitIn* commit = nullptr) {
   int rc = check_dtype(dtype);
   if (rc) return rc;
   if ((rc = check_rope_base(rope_base, name))) return rc;
@@ -152,12 +169,23 @@ int decode_common(const void* q, const void* k_new, const void* v_new, const voi
     return fail(SWA_ERR_SHAPE, "%s: k_scale and v_scale must be finite and > 0", name);
   if ((long long)batch * num_kv_heads * window * head_dim > (1LL << 40))
     return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
+  if (commit && (commit->prev_t < 1 || commit->prev_t >= window))
+    return fail(SWA_ERR_SHAPE, "%s: prev_T must satisfy 1 <= prev_T < window (got prev_T=%d, window=%d)",
+                name, commit->prev_t, window);
   if (batch == 0) return ok();  // nothing is read or written: pointers may be NULL
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !ring_head || !sinks || !out)
     return fail(SWA_ERR_NULL,
                 "%s: q, k_new, v_new, k_cache, v_cache, ring_head, sinks and out must be non-NULL",
                 name);
   if (rope_base > 0.f && !rope_pos) return fail(SWA_ERR_NULL, "%s: positions must be non-NULL", name);
+  if (commit) {
+    if (!commit->prev_k || !commit->prev_v || !commit->prev_accept || !commit->ring_head_out)
+      return fail(SWA_ERR_NULL, "%s: prev_k, prev_v, prev_accept and ring_head_out must be non-NULL", name);
+    if (rope_base > 0.f && !commit->prev_pos)
+      return fail(SWA_ERR_NULL, "%s: prev_positions must be non-NULL", name);
+    if (commit->ring_head_out == ring_head)
+      return fail(SWA_ERR_SHAPE, "%s: ring_head_out must not be ring_head", name);
+  }
 
   swa::DecodeArgs a;
   a.q = q; a.k_new = k_new; a.v_new = v_new;
@@ -177,6 +205,26 @@ int decode_common(const void* q, const void* k_new, const void* v_new, const voi
   }
   const bool bf = dtype == SWA_DTYPE_BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (commit) {
+    a.prev_k = commit->prev_k; a.prev_v = commit->prev_v;
+    a.prev_accept = commit->prev_accept; a.prev_pos = commit->prev_pos;
+    a.prev_t = commit->prev_t; a.ring_head_out = commit->ring_head_out;
+    if (swa::decode_mfma_supported(a, bf)) return hip_status(swa::launch_decode_mfma(a, s), name);
+    // any other shape: the same step in three launches -- the head copied to ring_head_out,
+    // the append advancing that copy, the decode against the updated ring
+    a.prev_k = a.prev_v = nullptr;
+    a.prev_accept = a.prev_pos = nullptr;
+    a.prev_t = 0; a.ring_head_out = nullptr;
+    hipError_t e = hipMemcpyAsync(commit->ring_head_out, ring_head, (size_t)batch * sizeof(int32_t),
+                                  hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_status(e, name);
+    int rc2 = ring_append_common(commit->prev_k, commit->prev_v, commit->prev_accept, commit->prev_pos,
+                                 const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                                 commit->ring_head_out, batch, commit->prev_t, num_kv_heads, head_dim,
+                                 window, rope_base, (swa_dtype)dtype, stream, name);
+    if (rc2) return rc2;
+    a.ring_head = commit->ring_head_out;
+  }
   hipError_t e = swa::decode_mfma_supported(a, bf) ? swa::launch_decode_mfma(a, s)
                                                    : swa::launch_generic_decode(a, bf, s);
   return hip_status(e, name);
@@ -192,7 +240,7 @@ int ring_append_common(const void* k_new, const void* v_new, const int32_t* n_ac
                        const int32_t* positions, void* k_cache, void* v_cache, int32_t* ring_head,
                        int32_t batch, int32_t T, int32_t num_kv_heads, int32_t head_dim,
                        int32_t window, float rope_base, swa_dtype dtype, void* stream, const char* name,
-                       bool fp8 = false, float k_scale = 1.f, float v_scale = 1.f) {
+                       bool fp8, float k_scale, float v_scale) {
   int rc = check_dtype((int)dtype);
   if (rc) return rc;
   if ((rc = check_rope_base(rope_base, name))) return rc;
@@ -358,6 +406,20 @@ int swa_sink_decode_rope(const void* q, const void* k_new, const void* v_new, co
   return decode_common(q, k_new, v_new, k_cache, v_cache, false, 1.f, 1.f, ring_head, sinks, batch,
                        T, num_q_heads, num_kv_heads, head_dim, window, scale, (int)dtype, out, lse,
                        stream, "swa_sink_decode_rope", positions, rope_base);
+}
+
+int swa_sink_decode_rope_commit(const void* q, const void* k_new, const void* v_new,
+                                const int32_t* positions, const void* prev_k, const void* prev_v,
+                                const int32_t* prev_accept, const int32_t* prev_positions,
+                                int32_t prev_T, void* k_cache, void* v_cache,
+                                const int32_t* ring_head, int32_t* ring_head_out, const float* sinks,
+                                int32_t batch, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t window, float scale, float rope_base,
+                                swa_dtype dtype, void* out, float* lse, void* stream) {
+  const CommitIn c{prev_k, prev_v, prev_accept, prev_positions, prev_T, ring_head_out};
+  return decode_common(q, k_new, v_new, k_cache, v_cache, false, 1.f, 1.f, ring_head, sinks, batch,
+                       T, num_q_heads, num_kv_heads, head_dim, window, scale, (int)dtype, out, lse,
+                       stream, "swa_sink_decode_rope_commit", positions, rope_base, &c);
 }
 
 int swa_sink_decode_rope_fp8kv(const void* q, const void* k_new, const void* v_new,

@@ -73,6 +73,14 @@ struct DecodeArgs {
   float v_scale = 1.f;
   const int32_t* rope_pos = nullptr;  // [B] position of new token 0: rotate q and k_new
   double rope_log2_base = 0.0;        // log2 of the rotary base (with rope_pos)
+  // one-launch MTP step (with rope_pos): the previous step's accepted tokens, committed to
+  // the ring before the verify; the ring is then written and ring_head is only read
+  const void* prev_k = nullptr;         // [B, prev_t, Hkv, D], keys unrotated
+  const void* prev_v = nullptr;         // [B, prev_t, Hkv, D]
+  const int32_t* prev_accept = nullptr;  // [B] tokens of the previous step to commit
+  const int32_t* prev_pos = nullptr;     // [B] position of the previous step's token 0
+  int32_t prev_t = 0;
+  int32_t* ring_head_out = nullptr;     // [B] head after the commit
 };
 
 // Rotary embedding of x [rows, heads, D] in place, row r at position pos[r].
@@ -204,6 +212,15 @@ __device__ __forceinline__ void rope_cos_sin(int pos, int i, int D, double log2_
   const double ang = (double)pos * f;
   const double r = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
   sincosf((float)r, s, c);
+}
+
+// One rotary pair (x, y) = (element i, element i + D/2) in fp32: (x cos - y sin,
+// y cos + x sin), each product rounded before the sum, with no fused multiply-add
+// whatever the call site, so every kernel that rotates a value produces the same bits.
+__device__ __forceinline__ void rope_pair(float x, float y, float c, float s, float& lo, float& hi) {
+#pragma clang fp contract(off)
+  lo = x * c - y * s;
+  hi = y * c + x * s;
 }
 
 // s_waitcnt immediate for vmcnt(0) with the other counters left alone (gfx9

@@ -50,7 +50,7 @@ struct DecodeSmem {
     struct {
       char q[NT * 16][kRowPitch];  // query columns (dead once the scores are formed)
       char kn[16][kRowPitch];      // new-token K rows (rows past T repeat row T-1)
-      float cs[4 * 64][2];         // rotary cos / sin per (new token, pair), when rotating
+      float cs[8 * 64][2];         // rotary cos / sin per (token, pair), when rotating
     } in;
   } u;
   char vn[16][kRowPitch];  // new-token V rows (rows past T repeat row T-1)
@@ -96,9 +96,18 @@ __device__ __forceinline__ void add_partial(const char (*slot)[kColBytes], int i
 // multiplies the ring weights as they are packed for P*V (the running sums stay
 // unscaled), so no cache element is ever rescaled.
 // ROPE: q and the new keys arrive unrotated and are rotated in registers as they are staged.
-template <int NT, bool FP8, bool ROPE>
+// COMMIT (with ROPE, bf16 ring): one launch per MTP step -- the previous step's first
+// prev_accept[b] tokens are committed to the ring (keys rotated at their positions, as the
+// ring append does) and the drafts are verified against the ring after that commit.  The
+// committed tokens are staged with the new ones (rows 4 .. 7 of the staging, free since
+// T <= 4) and rotated there; the first octet of each KV head stores them to the ring from
+// the staging registers, and the verify takes their rows from the staging, never from the
+// ring slots being rewritten.  ring_head is read and the new head written to
+// ring_head_out, so that every workgroup of a sequence sees the head before the commit.
+template <int NT, bool FP8, bool ROPE, bool COMMIT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void decode_kernel(DecodeArgs a) {
+  static_assert(!COMMIT || (ROPE && !FP8), "the one-launch step rotates keys into a bf16 ring");
   __shared__ __attribute__((aligned(16))) DecodeSmem<NT> sm;
   const int noct = a.num_q_heads / kHG;
   const int b = blockIdx.x / noct;
@@ -113,6 +122,15 @@ void decode_kernel(DecodeArgs a) {
   const int i = lane & 15, g = lane >> 4;
   int head = as_const(a.ring_head)[b] % kW;  // scalar load: addresses wait on nothing else
   head += head < 0 ? kW : 0;
+  // COMMIT: the verify sees the ring after the commit, whose newest ncommit logical slots
+  // hold the previous step's first ncommit tokens
+  int ncommit = 0;
+  if constexpr (COMMIT) {
+    ncommit = as_const(a.prev_accept)[b];
+    ncommit = ncommit < 0 ? 0 : (ncommit > a.prev_t ? a.prev_t : ncommit);
+    head = (head + ncommit) & (kW - 1);
+    if (h_base == 0 && threadIdx.x == 0) a.ring_head_out[b] = head;
+  }
 
   const bf16* qp = static_cast<const bf16*>(a.q);
   using CacheT = typename std::conditional<FP8, uint8_t, bf16>::type;
@@ -122,9 +140,14 @@ void decode_kernel(DecodeArgs a) {
   // layer's next step comes only after every other layer's cache has streamed through, so the bf16 loads carry the
   // non-temporal hint and leave the caches to the rows that are re-read within the step (measured faster at every
   // decode shape; the fp8 loads are 8-byte and were not).
-  auto ring8 = [&](const CacheT* base, int phys, int e0) -> bf16x8 {
-    if constexpr (FP8) return e4m3x8_to_bf16x8(*reinterpret_cast<const u32x2*>(base + (size_t)phys * D + e0));
-    else return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)phys * D + e0)));
+  auto ring8 = [&](const CacheT* row, int e0) -> bf16x8 {
+    if constexpr (FP8) return e4m3x8_to_bf16x8(*reinterpret_cast<const u32x2*>(row + e0));
+    else return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + e0)));
+  };
+  // the ring row of logical slot kr (the oldest, which no query sees, replaced by slot 1)
+  auto slot_row = [&](const CacheT* ring, int kr) -> const CacheT* {
+    const int k2 = kr != 0 ? kr : 1;
+    return ring + (size_t)((head + k2) & (kW - 1)) * D;
   };
   const bf16* kn = static_cast<const bf16*>(a.k_new) + ((size_t)b * T * hkv + kvh) * D;
   const bf16* vn = static_cast<const bf16*>(a.v_new) + ((size_t)b * T * hkv + kvh) * D;
@@ -140,6 +163,20 @@ void decode_kernel(DecodeArgs a) {
   // sink of this lane's head (query column i: head i & 7), loaded ahead of the bulk
   const float sink2 = a.sinks[h_base + (i & 7)] * kLog2e;
   const int nrow = min(tid >> 4, T - 1), nuu = tid & 15;  // new token of this thread
+  // COMMIT: staging rows 4 .. 4 + ncommit - 1 (past the T <= 4 new tokens, whose logits
+  // and weights they do not touch) carry the committed tokens, read from the previous
+  // step's K / V; ctok is this thread's committed token, or -1
+  const bf16* ksrc = kn + (size_t)nrow * hkv * D;
+  const bf16* vsrc = vn + (size_t)nrow * hkv * D;
+  int ctok = -1;
+  if constexpr (COMMIT) {
+    if ((tid >> 4) >= 4 && (tid >> 4) < 4 + ncommit) {
+      ctok = (tid >> 4) - 4;
+      const size_t off = (((size_t)b * a.prev_t + ctok) * hkv + kvh) * D;
+      ksrc = static_cast<const bf16*>(a.prev_k) + off;
+      vsrc = static_cast<const bf16*>(a.prev_v) + off;
+    }
+  }
   u32x4 st[NT + 2];
 #pragma unroll
   for (int k = 0; k < NT; ++k) {  // Q column col = x >> 4: token col >> 3, head col & 7
@@ -147,23 +184,18 @@ void decode_kernel(DecodeArgs a) {
     const int col = x >> 4, uu = x & 15, t = min(col >> 3, T - 1);
     st[k] = *reinterpret_cast<const u32x4*>(qp + (((size_t)b * T + t) * Hq + h_base + (col & 7)) * D + 8 * uu);
   }
-  st[NT] = *reinterpret_cast<const u32x4*>(kn + (size_t)nrow * hkv * D + 8 * nuu);
-  st[NT + 1] = *reinterpret_cast<const u32x4*>(vn + (size_t)nrow * hkv * D + 8 * nuu);
+  st[NT] = *reinterpret_cast<const u32x4*>(ksrc + 8 * nuu);
+  st[NT + 1] = *reinterpret_cast<const u32x4*>(vsrc + 8 * nuu);
   bf16x8 kf[2][4];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int kr = 32 * w + pair_row(i, s);
-    const int phys = (head + (kr != 0 ? kr : 1)) & (kW - 1);
+    const CacheT* row = slot_row(kc, 32 * w + pair_row(i, s));
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) kf[s][cc] = ring8(kc, phys, 32 * cc + 8 * g);
+    for (int cc = 0; cc < 4; ++cc) kf[s][cc] = ring8(row, 32 * cc + 8 * g);
   }
   bf16x8 vr[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int kr = 32 * w + 8 * g + e;
-    const int phys = (head + (kr != 0 ? kr : 1)) & (kW - 1);
-    vr[e] = ring8(vc, phys, 8 * i);
-  }
+  for (int e = 0; e < 8; ++e) vr[e] = ring8(slot_row(vc, 32 * w + 8 * g + e), 8 * i);
   {
     if constexpr (ROPE) {
       // the rotary cos/sin table (token, pair) is formed while the loads are in
@@ -171,9 +203,14 @@ void decode_kernel(DecodeArgs a) {
       // a query column or new-key row is rotated in registers before it is written:
       // element i pairs with i + 64, i.e. piece uu with piece uu ^ 8 of the same row,
       // which sits in the lane 8 away within the 16-lane row (a DPP row rotation by 8)
+      // (COMMIT: rows T .. T + ncommit - 1 of the table belong to the committed tokens)
       const int pos0 = as_const(a.rope_pos)[b];
-      for (int x = tid; x < T * 64; x += kThreads)
-        rope_cos_sin(pos0 + (x >> 6), x & 63, D, a.rope_log2_base, &sm.u.in.cs[x][0], &sm.u.in.cs[x][1]);
+      const int ppos0 = COMMIT ? as_const(a.prev_pos)[b] : 0;
+      for (int x = tid; x < (T + ncommit) * 64; x += kThreads) {
+        const int tok = x >> 6;
+        rope_cos_sin(tok < T ? pos0 + tok : ppos0 + (tok - T), x & 63, D, a.rope_log2_base, &sm.u.in.cs[x][0],
+                     &sm.u.in.cs[x][1]);
+      }
       __syncthreads();  // the table is complete
       const bool first = (tid & 8) == 0;  // this lane holds x[i], the partner x[i + 64]
       auto rotate = [&](u32x4 v4, int t) -> u32x4 {
@@ -187,7 +224,11 @@ void decode_kernel(DecodeArgs a) {
         for (int e = 0; e < 8; ++e) {
           const float c = sm.u.in.cs[t * 64 + 8 * (tid & 7) + e][0];
           const float sn = sm.u.in.cs[t * 64 + 8 * (tid & 7) + e][1];
-          y[e] = first ? (bf16)((float)me[e] * c - (float)pa[e] * sn) : (bf16)((float)me[e] * c + (float)pa[e] * sn);
+          // this lane holds x[i] (first) or x[i + 64] of pair i: the pair's lo or hi
+          float lo, hi;
+          if (first) rope_pair((float)me[e], (float)pa[e], c, sn, lo, hi);
+          else rope_pair((float)pa[e], (float)me[e], c, sn, lo, hi);
+          y[e] = (bf16)(first ? lo : hi);
         }
         return __builtin_bit_cast(u32x4, y);
       };
@@ -196,7 +237,16 @@ void decode_kernel(DecodeArgs a) {
         const int col = (k * kThreads + tid) >> 4;
         st[k] = rotate(st[k], min(col >> 3, T - 1));
       }
-      st[NT] = rotate(st[NT], nrow);
+      st[NT] = rotate(st[NT], ctok >= 0 ? T + ctok : nrow);
+      if constexpr (COMMIT) {
+        // the first octet of the KV head commits the staged tokens: token ctok to logical
+        // slot kW - ncommit + ctok of the ring after the commit, the key as just rotated
+        if (ctok >= 0 && h_base == kvh * (Hq / hkv)) {
+          const size_t dst = (size_t)((head + kW - ncommit + ctok) & (kW - 1)) * D + 8 * nuu;
+          *reinterpret_cast<u32x4*>(const_cast<CacheT*>(kc) + dst) = st[NT];
+          *reinterpret_cast<u32x4*>(const_cast<CacheT*>(vc) + dst) = st[NT + 1];
+        }
+      }
     }
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
@@ -218,6 +268,22 @@ void decode_kernel(DecodeArgs a) {
   const float c = a.scale * kLog2e;       // new tokens' logits to log2 units
   const float cr = FP8 ? c * a.k_scale : c;  // the ring's
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  if constexpr (COMMIT) {
+    // wavefront 3's slots kW - ncommit .. kW - 1 are the committed tokens: their keys (as
+    // rotated in staging) replace the ring rows loaded for them, which the commit rewrites
+    if (w == 3 && ncommit > 0) {
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        const int tc = 96 + pair_row(i, ss) - (kW - ncommit);
+        if (tc >= 0) {
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc)
+            kf[ss][cc] = *reinterpret_cast<const bf16x8*>(&sm.u.in.kn[4 + tc][16 * (4 * cc + g)]);
+        }
+      }
+    }
+  }
 
   // ---- scores ----
   f32x4 s[NT][2], sn[NT];
@@ -291,6 +357,16 @@ void decode_kernel(DecodeArgs a) {
     if (w == 0 && g == 0) {
       sm.mc[col] = mcol[tt];
       sm.zs[col] = fast_exp2(sink2 - mcol[tt]);
+    }
+  }
+
+  if constexpr (COMMIT) {  // likewise the committed values, from their staging rows
+    if (w == 3 && ncommit > 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tc = 96 + 8 * g + e - (kW - ncommit);
+        if (tc >= 0) vr[e] = *reinterpret_cast<const bf16x8*>(&sm.vn[4 + tc][16 * i]);
+      }
     }
   }
 
@@ -381,6 +457,10 @@ void decode_kernel(DecodeArgs a) {
 bool decode_mfma_supported(const DecodeArgs& a, bool bf16_io) {
   // (an FP8 ring takes the same path: only the cache element type differs)
   const int G = a.num_q_heads / a.num_kv_heads;
+  // the one-launch MTP step: rotation, a bf16 ring, and at most 4 committed tokens (wavefront
+  // 3's newest slots)
+  if (a.prev_accept != nullptr && (a.rope_pos == nullptr || a.cache_fp8 || a.prev_t < 1 || a.prev_t > 4))
+    return false;
   return bf16_io && a.head_dim == 128 && G % kHG == 0 && a.window == kW && a.t_new >= 1 &&
          a.t_new <= 4;
 }
@@ -390,7 +470,10 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
   if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
   const bool two = a.t_new > 2;
   const dim3 grid((unsigned)blocks), block(kThreads);
-  if (a.rope_pos != nullptr) {  // rotation in the kernel
+  if (a.prev_accept != nullptr) {  // one-launch MTP step (rotation, bf16 ring)
+    if (two) hipLaunchKernelGGL((decode_kernel<2, false, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<1, false, true, true>), grid, block, 0, s, a);
+  } else if (a.rope_pos != nullptr) {  // rotation in the kernel
     if (a.cache_fp8) {
       if (two) hipLaunchKernelGGL((decode_kernel<2, true, true>), grid, block, 0, s, a);
       else hipLaunchKernelGGL((decode_kernel<1, true, true>), grid, block, 0, s, a);

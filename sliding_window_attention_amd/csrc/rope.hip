@@ -49,9 +49,10 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a) {
     __builtin_memcpy(v, yv, sizeof(v));
 #pragma unroll
     for (int e = 0; e < kPairs; ++e) {
-      const float fu = (float)u[e], fv = (float)v[e];
-      uo[e] = cvt<T>(fu * c[e] - fv * s[e]);
-      vo[e] = cvt<T>(fv * c[e] + fu * s[e]);
+      float lo, hi;
+      rope_pair((float)u[e], (float)v[e], c[e], s[e], lo, hi);
+      uo[e] = cvt<T>(lo);
+      vo[e] = cvt<T>(hi);
     }
     __builtin_memcpy(xo, uo, sizeof(uo));
     __builtin_memcpy(yo, vo, sizeof(vo));
@@ -193,9 +194,10 @@ __device__ __forceinline__ void rotate_pairs(const AppendArgs& a, int b, int n, 
     } else {
       rope_cos_sin(a.rope_pos[b] + t, i, D, a.log2_base, &c, &s);
     }
-    const float fu = ldf(&u[e]), fv = ldf(&v[e]);
-    u[e] = cvt<T>(fu * c - fv * s);
-    v[e] = cvt<T>(fv * c + fu * s);
+    float lo, hi;
+    rope_pair(ldf(&u[e]), ldf(&v[e]), c, s, lo, hi);
+    u[e] = cvt<T>(lo);
+    v[e] = cvt<T>(hi);
   }
 }
 

@@ -393,6 +393,14 @@ def append_bytes(batch, n_accepted_total, num_kv_heads, head_dim, elem_bytes, ca
     return 2 * n_accepted_total * num_kv_heads * head_dim * (elem_bytes + cb) + 4 * 4 * batch
 
 
+def mtp_commit_bytes(batch, n_accepted_total, num_kv_heads, head_dim, elem_bytes):
+    """What the one-launch MTP step adds to the verify's bytes: the committed tokens' K and
+    V written to the ring (the verify reads their rows from the previous step's K / V in
+    place of the ring slots they fill, so its reads are the verify's), plus the accept
+    counts, previous positions and heads (two heads: read and written)."""
+    return 2 * n_accepted_total * num_kv_heads * head_dim * elem_bytes + 4 * 4 * batch
+
+
 def rope_bytes(rows, heads, head_dim, elem_bytes):
     """In-place rotation: every element read and written once, plus one int32 position per row."""
     return 2 * rows * heads * head_dim * elem_bytes + 4 * rows

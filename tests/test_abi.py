@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
                           "swa_sink_prefill_backward_workspace", "swa_sink_prefill_backward_noalloc",
                           "swa_rope", "swa_sink_decode_rope",
                           "swa_ring_append_rope", "swa_topk_select", "swa_sparse_decode",
-                          "swa_sink_decode_rope_fp8kv", "swa_ring_append_fp8kv",
+                          "swa_sink_decode_rope_fp8kv", "swa_ring_append_fp8kv", "swa_sink_decode_rope_commit",
                           "swa_last_error", "swa_abi_version"}
 
 
@@ -129,6 +129,46 @@ def test_ga_rejects_bad_arguments():
 def test_decode_rejects_bad_arguments(kw, code, needle):
     assert _decode(**kw) == code
     assert needle in _last()
+
+
+FAKE2 = ctypes.c_void_p(0x2000)
+
+
+def _commit(**kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, pos=FAKE, pk=FAKE, pv=FAKE, acc=FAKE, ppos=FAKE, pt=4, kc=FAKE,
+             vc=FAKE, head=FAKE, head_out=FAKE2, sinks=FAKE, b=4, t=4, hq=8, hkv=1, d=128, window=128,
+             scale=0.0, base=10000.0, dtype=1, out=FAKE, lse=NULL, stream=NULL)
+    a.update(kw)
+    return swa.library().swa_sink_decode_rope_commit(
+        a["q"], a["kn"], a["vn"], a["pos"], a["pk"], a["pv"], a["acc"], a["ppos"], a["pt"], a["kc"], a["vc"],
+        a["head"], a["head_out"], a["sinks"], a["b"], a["t"], a["hq"], a["hkv"], a["d"], a["window"],
+        a["scale"], a["base"], a["dtype"], a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(pt=0), E_SHAPE, "prev_T"),
+    (dict(pt=128), E_SHAPE, "prev_T"),
+    (dict(pt=0, b=0), E_SHAPE, "prev_T"),  # sizes validate before the empty batch returns
+    (dict(t=0), E_SHAPE, "T must"),
+    (dict(head_out=FAKE), E_SHAPE, "must not be ring_head"),
+    (dict(head_out=NULL), E_NULL, "ring_head_out"),
+    (dict(pk=NULL), E_NULL, "prev_k"),
+    (dict(acc=NULL), E_NULL, "prev_accept"),
+    (dict(ppos=NULL), E_NULL, "prev_positions"),
+    (dict(pos=NULL), E_NULL, "positions"),
+    (dict(base=-1.0), E_SHAPE, "rope_base"),
+    (dict(dtype=3), E_DTYPE, "dtype"),
+])
+def test_decode_rope_commit_rejects_bad_arguments(kw, code, needle):
+    assert _commit(**kw) == code
+    assert needle in _last()
+
+
+def test_decode_rope_commit_empty_batch_and_no_rotation():
+    assert _commit(b=0, q=NULL, kn=NULL, vn=NULL, pos=NULL, pk=NULL, pv=NULL, acc=NULL, ppos=NULL, kc=NULL,
+                   vc=NULL, head=NULL, head_out=NULL, sinks=NULL, out=NULL) == OK
+    # without rotation the positions are not needed, but prev_accept still is
+    assert _commit(base=0.0, ppos=NULL, acc=NULL) == E_NULL and "prev_accept" in _last()
 
 
 def test_decode_empty_batch_is_ok():

@@ -835,6 +835,52 @@ def test_ring_append_matches_a_list_model():
     np.testing.assert_array_equal(k3[b, :, (heads[b] + t) % w, :], kn[b, t])
 
 
+def test_mtp_steps_equal_attention_over_the_accepted_stream():
+    """A run of MTP steps (commit the previous step's accepted tokens, verify the new
+    ones) sees exactly the stream of accepted tokens: each step's outputs equal brute
+    force windowed attention with sink over (history ++ every accepted token ++ the
+    step's T tokens), all rotated at their positions.  Covers accept counts 0, partial
+    and all (and a count above prev_T, clamped), and the head carried between steps."""
+    rng = np.random.default_rng(21)
+    w, d, hq, hkv, t_new, base = 6, 8, 4, 2, 3, 10000.0
+    q0, kn0, vn0, k_raw, v_ring, heads, sinks = _rope_decode_case(1, t_new, hq, hkv, d, w, 22, 0)
+    p = 40  # history at positions p-w .. p-1
+    kc = _ring_from_raw(k_raw, heads, np.array([p]), base, None)
+    vc = v_ring.copy()
+    hist_k = [k_raw[0, l] for l in range(w)]
+    hist_v = [v_ring[0, :, (heads[0] + l) % w, :] for l in range(w)]
+    prev_k, prev_v = kn0, vn0
+    # the first step commits nothing (its "previous" tokens are arbitrary)
+    accepts = [0, 2, 3, 1, 7, 0, 3]
+    head = heads.copy()
+    pos, prev_pos = p, p
+    for step, acc in enumerate(accepts):
+        n = min(acc, t_new)
+        if step > 0:
+            hist_k += [prev_k[0, t] for t in range(n)]
+            hist_v += [prev_v[0, t] for t in range(n)]
+            pos = prev_pos + n
+        q = rng.standard_normal((1, t_new, hq, d))
+        kn = rng.standard_normal((1, t_new, hkv, d))
+        vn = rng.standard_normal((1, t_new, hkv, d))
+        o, lse, kc, vc, head = orc.swa_sink_decode_rope_commit(
+            q, kn, vn, [pos], prev_k, prev_v, [acc if step > 0 else 0], [prev_pos], kc, vc, head, sinks,
+            base, window=w, io_dtype=None)
+        ks = np.stack(hist_k + [kn[0, t] for t in range(t_new)])            # [L, hkv, d] raw
+        vs = np.stack(hist_v + [vn[0, t] for t in range(t_new)])
+        L = ks.shape[0]
+        spos = pos - (L - t_new) + np.arange(L)
+        assert spos[0] == p - w  # the stream is contiguous from the history's first position
+        qs = np.zeros((L, hq, d))
+        qs[L - t_new:] = q[0]
+        qr, kr = orc.rope(qs, spos, base), orc.rope(ks, spos, base)
+        o2, l2 = brute.attention(qr.tolist(), kr.tolist(), vs.tolist(), sinks.tolist(), [0, L], w)
+        np.testing.assert_allclose(o[0], np.asarray(o2)[L - t_new:], atol=1e-12)
+        np.testing.assert_allclose(lse[0], np.asarray(l2)[L - t_new:], atol=1e-12)
+        assert head[0] == (heads[0] + len(hist_k) - w) % w
+        prev_k, prev_v, prev_pos = kn, vn, pos
+
+
 # ---------------------------------------------------------------------------
 # Token-level sparse attention with a forced recent window (MiMo-V3 / HySparse2 page)
 # ---------------------------------------------------------------------------

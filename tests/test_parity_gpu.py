@@ -1104,6 +1104,175 @@ def test_ring_append_full_batch():
 
 
 # ---------------------------------------------------------------------------
+# one-launch MTP step: commit the previous step's accepted tokens, then verify
+# ---------------------------------------------------------------------------
+
+def _commit_case(b, t_new, prev_t, hq, hkv, d, w, dt, seed):
+    """Decode-with-RoPE inputs plus a previous step: prev_k / prev_v [B, prev_T, Hkv, D]
+    (keys unrotated), accept counts ~ U{0..prev_T} and the previous step's positions
+    (new token 0 of this step minus the accepted count)."""
+    x = wl.make_decode_rope(b, t_new, hq, hkv, d, w, dt, seed=seed)
+    gen = torch.Generator().manual_seed(seed + 7)
+    td = x["q"].dtype
+    x["prev_k"] = torch.randn(b, prev_t, hkv, d, generator=gen).to(td)
+    x["prev_v"] = torch.randn(b, prev_t, hkv, d, generator=gen).to(td)
+    x["prev_accept"] = torch.randint(0, prev_t + 1, (b,), generator=gen, dtype=torch.int64).to(torch.int32)
+    x["prev_positions"] = x["positions"] - x["prev_accept"]
+    return x
+
+
+def _run_commit(g, base, ring_head_out=None):
+    head_out = torch.empty_like(g["ring_head"]) if ring_head_out is None else ring_head_out
+    o, lse = swa.swa_sink_decode_rope_commit(g["q"], g["k_new"], g["v_new"], g["positions"], g["prev_k"],
+                                             g["prev_v"], g["prev_accept"], g["prev_positions"], g["k_cache"],
+                                             g["v_cache"], g["ring_head"], head_out, g["sinks"], base)
+    torch.cuda.synchronize()
+    return o, lse, head_out
+
+
+def _run_append_then_decode(g, base):
+    """The same step as two calls: swa_ring_append_rope on a copy of the head, then
+    swa_sink_decode_rope against the updated ring."""
+    head = g["ring_head"].clone()
+    swa.swa_ring_append_rope(g["prev_k"], g["prev_v"], g["prev_accept"], g["prev_positions"], g["k_cache"],
+                             g["v_cache"], head, base)
+    o, lse = swa.swa_sink_decode_rope(g["q"], g["k_new"], g["v_new"], g["k_cache"], g["v_cache"], head,
+                                      g["positions"], g["sinks"], base)
+    torch.cuda.synchronize()
+    return o, lse, head
+
+
+def _oracle_commit(x, base, io):
+    t = x["prev_k"].shape[1]
+    return orc.swa_sink_decode_rope_commit(x["q"], x["k_new"], x["v_new"], x["positions"].numpy(), x["prev_k"],
+                                           x["prev_v"], np.clip(x["prev_accept"].numpy(), 0, t),
+                                           x["prev_positions"].numpy(), x["k_cache"], x["v_cache"],
+                                           x["ring_head"].numpy(), x["sinks"], base,
+                                           window=x["k_cache"].shape[2], io_dtype=io)
+
+
+COMMIT_FUSED_CASES = [(16, 4, 4), (16, 1, 1), (16, 3, 2), (16, 2, 3), (16, 1, 4), (16, 4, 1)]
+
+
+@pytest.mark.parametrize("case", COMMIT_FUSED_CASES, ids=lambda c: f"B{c[0]}-T{c[1]}-prevT{c[2]}")
+def test_mtp_commit_equals_append_then_decode(case):
+    """The one-launch step gives the bits of swa_ring_append_rope + swa_sink_decode_rope:
+    outputs, lse, every ring slot and the new head (accept counts 0, prev_T, and out of
+    range on both sides; heads 127, negative and beyond the window)."""
+    b, t_new, prev_t = case
+    _say(f"MTP step in one launch vs append + decode: B={b} T={t_new} prev_T={prev_t} 32/4 D128 bf16")
+    x = _commit_case(b, t_new, prev_t, 32, 4, 128, 128, "bf16", seed=4300 + 10 * t_new + prev_t)
+    x["prev_accept"][0], x["prev_accept"][1] = 0, prev_t
+    x["prev_accept"][2], x["prev_accept"][3] = prev_t + 3, -2   # clamped to prev_T and to 0
+    x["ring_head"][4], x["ring_head"][5], x["ring_head"][6] = 127, -5, 3 * 128 + 1
+    x["positions"][7], x["prev_positions"][7] = 2 ** 31 - 8, 2 ** 31 - 8 - prev_t
+    g1, g2 = _gpu(x), _gpu(x)
+    head0 = g1["ring_head"].clone()
+    o1, l1, h1 = _run_commit(g1, 10000.0)
+    o2, l2, h2 = _run_append_then_decode(g2, 10000.0)
+    assert torch.equal(g1["ring_head"], head0)  # read only
+    assert torch.equal(h1, h2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(g1["k_cache"], g2["k_cache"]) and torch.equal(g1["v_cache"], g2["v_cache"])
+
+
+def test_mtp_commit_follows_the_oracle():
+    _say("MTP step in one launch vs the oracle: B=16 T=4 prev_T=4 32/4 D128 bf16")
+    x = _commit_case(16, 4, 4, 32, 4, 128, 128, "bf16", seed=4400)
+    g = _gpu(x)
+    o, lse, h = _run_commit(g, 10000.0)
+    o_ref, l_ref, kc, vc, h_ref = _oracle_commit(x, 10000.0, "bf16")
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, "mtp commit")
+    assert np.array_equal(h.cpu().numpy(), h_ref)
+    assert np.array_equal(to_np(g["v_cache"]), vc)
+    got = to_np(g["k_cache"])
+    diff = got != kc  # rotated keys: rare neighbouring-bf16 near-ties, as the append's
+    assert float(diff.mean()) < 1e-3
+    assert np.all(np.abs(got - kc)[diff] <= 2.0 ** -7 * np.abs(kc)[diff] + 1e-30)
+
+
+def test_mtp_commit_steps_ping_pong_heads():
+    """Six steps, each passing the last one's new tokens as prev and its head_out as the
+    head (two head buffers in turn); every step matches the two-call sequence bit for
+    bit and the ring state follows it."""
+    _say("MTP steps in one launch, heads ping-ponged: B=8 T=4 32/4 D128 bf16")
+    b, t_new, hq, hkv, d, w, base = 8, 4, 32, 4, 128, 128, 10000.0
+    x = _commit_case(b, t_new, t_new, hq, hkv, d, w, "bf16", seed=4500)
+    x["prev_accept"].zero_()  # the first step commits nothing
+    gen = torch.Generator().manual_seed(4501)
+    g1, g2 = _gpu(x), _gpu(x)
+    heads = [g1["ring_head"], torch.empty_like(g1["ring_head"])]
+    head2 = g2["ring_head"].clone()
+    for step in range(6):
+        q = torch.randn(b, t_new, hq, d, generator=gen).to(torch.bfloat16).to(DEV)
+        kn = torch.randn(b, t_new, hkv, d, generator=gen).to(torch.bfloat16).to(DEV)
+        vn = torch.randn(b, t_new, hkv, d, generator=gen).to(torch.bfloat16).to(DEV)
+        pos = (g1["prev_positions"] + g1["prev_accept"].clamp(0, t_new)).to(torch.int32)
+        for g in (g1, g2):
+            g["q"], g["k_new"], g["v_new"], g["positions"] = q, kn, vn, pos
+        g1["ring_head"] = heads[step % 2]
+        o1, l1, _ = _run_commit(g1, base, ring_head_out=heads[(step + 1) % 2])
+        g2["ring_head"] = head2
+        o2, l2, head2 = _run_append_then_decode(g2, base)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"step {step}"
+        assert torch.equal(heads[(step + 1) % 2], head2), f"step {step}"
+        assert torch.equal(g1["k_cache"], g2["k_cache"]) and torch.equal(g1["v_cache"], g2["v_cache"])
+        n_acc = torch.randint(0, t_new + 1, (b,), generator=gen, dtype=torch.int64).to(torch.int32).to(DEV)
+        for g in (g1, g2):
+            g["prev_k"], g["prev_v"], g["prev_accept"], g["prev_positions"] = kn, vn, n_acc, pos
+
+
+@pytest.mark.parametrize("case", [(6, 3, 8, 16, 2, 128, 128, "bf16"), (5, 2, 3, 4, 1, 64, 128, "f32"),
+                                  (4, 4, 4, 8, 8, 128, 64, "bf16"), (3, 1, 2, 8, 1, 64, 128, "bf16")],
+                         ids=lambda c: f"B{c[0]}-T{c[1]}-prevT{c[2]}-{c[3]}/{c[4]}-D{c[5]}-W{c[6]}-{c[7]}")
+def test_mtp_commit_other_shapes(case):
+    """Shapes outside the one-launch kernel (prev_T > 4, fp32, D 64, other windows) run
+    as the head copy and the two calls: the same bits as those calls, and the oracle."""
+    b, t_new, prev_t, hq, hkv, d, w, dt = case
+    _say(f"MTP step, other shapes: {case}")
+    x = _commit_case(b, t_new, prev_t, hq, hkv, d, w, dt, seed=4600 + b)
+    x["prev_accept"][0] = prev_t
+    g1, g2 = _gpu(x), _gpu(x)
+    o1, l1, h1 = _run_commit(g1, 640000.0)
+    o2, l2, h2 = _run_append_then_decode(g2, 640000.0)
+    assert torch.equal(h1, h2) and torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(g1["k_cache"], g2["k_cache"]) and torch.equal(g1["v_cache"], g2["v_cache"])
+    io = "bf16" if dt == "bf16" else "f32"
+    o_ref, l_ref, _, vc, h_ref = _oracle_commit(x, 640000.0, io)
+    assert_close(x["q"].dtype, o1, o_ref, l1, l_ref, f"mtp commit {case}")
+    assert np.array_equal(h1.cpu().numpy(), h_ref)
+    assert np.array_equal(to_np(g1["v_cache"]), vc)
+    # without rotation: the step is the plain append (keys copied) and the plain decode
+    g3, g4 = _gpu(x), _gpu(x)
+    o3, l3, h3 = _run_commit(g3, 0.0)
+    o4, l4, h4 = _run_append_then_decode(g4, 0.0)
+    assert torch.equal(h3, h4) and torch.equal(o3, o4) and torch.equal(l3, l4)
+    assert torch.equal(g3["k_cache"], g4["k_cache"])
+
+
+def test_mtp_commit_full():
+    """The benchmarked step (B = 256, T = 4, prev_T = 4, accept counts ~ U{0..4}): every
+    output element against the oracle, the head and every ring slot."""
+    _say("MTP step in one launch, full: B=256 T=4 prev_T=4 32/4 D128 bf16")
+    x = wl.make_workload("decode_rope_t4")
+    gen = torch.Generator().manual_seed(4701)
+    x["prev_k"] = torch.randn(256, 4, 4, 128, generator=gen).to(torch.bfloat16)
+    x["prev_v"] = torch.randn(256, 4, 4, 128, generator=gen).to(torch.bfloat16)
+    x["prev_accept"] = torch.randint(0, 5, (256,), generator=gen, dtype=torch.int64).to(torch.int32)
+    x["prev_positions"] = x["positions"] - x["prev_accept"]
+    g = _gpu(x)
+    o, lse, h = _run_commit(g, 10000.0)
+    o_ref, l_ref, kc, vc, h_ref = _oracle_commit(x, 10000.0, "bf16")
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, "mtp commit full")
+    assert np.array_equal(h.cpu().numpy(), h_ref)
+    assert np.array_equal(to_np(g["v_cache"]), vc)
+    got = to_np(g["k_cache"])
+    diff = got != kc
+    assert float(diff.mean()) < 1e-4
+    assert np.all(np.abs(got - kc)[diff] <= 2.0 ** -7 * np.abs(kc)[diff] + 1e-30)
+
+
+# ---------------------------------------------------------------------------
 # FP8 ring with RoPE: decode (rotation in the kernel) and the append that encodes
 # ---------------------------------------------------------------------------
 
