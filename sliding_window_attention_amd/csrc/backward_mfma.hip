@@ -381,7 +381,10 @@ constexpr int kTiles = 4;             // 16-key tiles per workgroup, one per wav
 
 __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, int ngrp) {
   using namespace kvtile;
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];  // double-buffered step
+  // double-buffered step, as two arrays so that the compiler can tell the buffer being
+  // read from the one the next step's loads are filling
+  __shared__ __attribute__((aligned(16))) char smem0[kStage];
+  __shared__ __attribute__((aligned(16))) char smem1[kStage];
 
   // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous range
   // of key tiles so that the query blocks shared by neighbouring tiles are read
@@ -465,54 +468,39 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
   const int tlo = tr_base(8 * g + (i >> 2), 8 * g + (i >> 2), i);
   const int thi = tr_base(8 * g + 4 + (i >> 2), 8 * g + 4 + (i >> 2), i);
 
-  // Staging: thread t moves unit t & 15 of token row t >> 4 of the four heads, Q and
-  // dO; threads 0-63 move the lse and delta of row P = t.  One register set: the loads
-  // of step s + 1 are issued at the start of step s.
-  struct Stage {
-    u32x4 q[kHeads], d[kHeads];
-    float l, dl;
-  };
-  Stage sa;
-  // position of the prefetched step: head quad hp_n, query block tb_n
-  int hp_n = 0, tb_n = tb_first, m_n = 0;
+  // Staging: the step's Q and dO rows go from global memory straight into LDS (16 bytes
+  // per lane, 1 KB per instruction), each lane reading the unit that belongs at its slot of
+  // the swizzled chunk-plane layout: wavefront w fills plane w of both operands, row groups
+  // rg = 0..3 (head rg, tokens 0..15): lane L holds row P = 16 rg + L / 4, slot L & 3, i.e.
+  // unit 4w + ((L & 3) ^ kswz(P)).  Wavefronts 0 and 1 bring the rows' lse and delta (4 bytes
+  // per lane).  No registers hold the block; each wavefront waits for its own loads before
+  // the barrier that ends the step.
+  int hp_n = 0, tb_n = tb_first, m_n = 0;  // position of the step being loaded
   auto advance = [&](int& hp, int& tb, int& m) {
     ++m;
     ++tb;
     if (tb == tb_wrap) tb = tb_lo;
     if (m == nsteps) { m = 0; ++hp; tb = tb_first; }
   };
-  auto prefetch = [&](Stage& st) {
-    const int hp = hp_n, tb = tb_n;
-    const int hbase = kvh * G + kHeads * hp;
-    const int q = min(16 * tb + (t >> 4), N - 1);
+  using lds_ptr = __attribute__((address_space(3))) void*;
+  const int srow = lane >> 2, sslot = lane & 3;
+  auto issue = [&](char* buf) {
+    const int hbase = kvh * G + kHeads * hp_n;
+    const int q = min(16 * tb_n + srow, N - 1);
 #pragma unroll
-    for (int hs = 0; hs < kHeads; ++hs) {
-      const size_t off = ((size_t)q * Hq + hbase + hs) * D + 8 * (t & 15);
-      st.q[hs] = *reinterpret_cast<const u32x4*>(qp + off);
-      st.d[hs] = *reinterpret_cast<const u32x4*>(dop + off);
+    for (int rg = 0; rg < kHeads; ++rg) {
+      const int u = 4 * w + (sslot ^ kswz(16 * rg + srow));
+      const size_t off = ((size_t)q * Hq + hbase + rg) * D + 8 * u;
+      const int dst = w * kPlane + rg * 1024;
+      __builtin_amdgcn_global_load_lds(qp + off, (lds_ptr)(buf + dst), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(dop + off, (lds_ptr)(buf + kOpBytes + dst), 16, 0, 0);
     }
-    // every thread loads (threads 32.. duplicate 0..31) and nothing is computed on the
-    // values here: a branch or an early use would make the compiler wait for the load
-    const size_t r = (size_t)min(16 * tb + (t & 15), N - 1) * Hq + hbase + ((t >> 4) & (kHeads - 1));
-    st.l = a.lse[r];
-    st.dl = a.delta[r];
-  };
-  auto commit = [&](int buf, const Stage& st) {
-    char* qs = smem + buf * kStage;
-    char* ds = qs + kOpBytes;
-    float* ls = reinterpret_cast<float*>(ds + kOpBytes);
-#pragma unroll
-    for (int hs = 0; hs < kHeads; ++hs) {
-      const int P = 16 * hs + (t >> 4);
-      put_k(qs, kPlane, P, P, t & 15, st.q[hs]);
-      put_k(ds, kPlane, P, P, t & 15, st.d[hs]);
-    }
-    if (t < kRows) {
-      ls[t] = st.l * kLog2e;
-      ls[kRows + t] = st.dl;
+    if (w < 2) {  // lse (wavefront 0) or delta (1) of row P = lane: token P & 15, head P >> 4
+      const size_t r = (size_t)min(16 * tb_n + (lane & 15), N - 1) * Hq + hbase + (lane >> 4);
+      const float* src = w == 0 ? a.lse : a.delta;
+      __builtin_amdgcn_global_load_lds(src + r, (lds_ptr)(buf + 2 * kOpBytes + w * kRows * 4), 4, 0, 0);
     }
   };
-
   f32x4 dk[8], dv[8];
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
@@ -520,17 +508,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
     dv[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  // One step: its block is already in LDS buffer step & 1; the next step's loads are
-  // issued first and committed to the other buffer at the end.
+  // One step: its block is already in LDS buffer cur; the next step's loads into the
+  // other buffer are issued first and waited for at the end.
   int hp_c = 0, tb_c = tb_first, m_c = 0;  // position of the current step
-  auto do_step = [&](int step) {
+  auto do_step = [&](int step, const char* cur, char* nxt) {
     if (step + 1 < total) {
       advance(hp_n, tb_n, m_n);
-      prefetch(sa);
+      issue(nxt);
     }
     const int tb = tb_c;
     if (tb >= tbw_lo && tb <= tbw_hi) {
-      const char* qs = smem + (step & 1) * kStage;
+      const char* qs = cur;
       const char* ds = qs + kOpBytes;
       const float* ls = reinterpret_cast<const float*>(ds + kOpBytes);
       // ---- S = Q K^T and dP = dO V^T for two pairs of 16-row blocks (rows 32 pi ..) ----
@@ -556,8 +544,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
       bf16x8 pp[2], xp[2];
 #pragma unroll
       for (int pi = 0; pi < 2; ++pi) {
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls + 32 * pi + 8 * g);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + 32 * pi + 8 * g + 4);
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls + 32 * pi + 8 * g) * kLog2e;
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + 32 * pi + 8 * g + 4) * kLog2e;
         const f32x4 d0 = *reinterpret_cast<const f32x4*>(ls + kRows + 32 * pi + 8 * g);
         const f32x4 d1 = *reinterpret_cast<const f32x4*>(ls + kRows + 32 * pi + 8 * g + 4);
         f32x4 p[2], x[2];
@@ -594,17 +582,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
       }
     }
     __builtin_amdgcn_s_setprio(0);
-    // the other buffer was last read in the previous step, which every wavefront has
-    // finished (barrier below)
-    if (step + 1 < total) commit((step + 1) & 1, sa);
+    // the buffer being filled was last read in the previous step, which every wavefront
+    // had finished at the barrier that ended it; this one publishes the new block
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
     advance(hp_c, tb_c, m_c);
   };
 
-  prefetch(sa);
-  commit(0, sa);
+  issue(smem0);
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
-  for (int step = 0; step < total; ++step) do_step(step);
+  for (int step = 0; step < total; step += 2) {
+    do_step(step, smem0, smem1);
+    if (step + 1 < total) do_step(step + 1, smem1, smem0);
+  }
 
   const size_t krow = ((size_t)(kvalid ? j : 0) * hkv + kvh) * D;
   store_grad_row(static_cast<bf16*>(a.dk) + krow, g, dk, a.scale, kvalid);
