@@ -482,7 +482,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
     if (tb == tb_wrap) tb = tb_lo;
     if (m == nsteps) { m = 0; ++hp; tb = tb_first; }
   };
-  using lds_ptr = __attribute__((address_space(3))) void*;
   const int srow = lane >> 2, sslot = lane & 3;
   auto issue = [&](char* buf) {
     const int hbase = kvh * G + kHeads * hp_n;
@@ -492,13 +491,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BackwardArgs a, i
       const int u = 4 * w + (sslot ^ kswz(16 * rg + srow));
       const size_t off = ((size_t)q * Hq + hbase + rg) * D + 8 * u;
       const int dst = w * kPlane + rg * 1024;
-      __builtin_amdgcn_global_load_lds(qp + off, (lds_ptr)(buf + dst), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(dop + off, (lds_ptr)(buf + kOpBytes + dst), 16, 0, 0);
+      load_lds16(qp + off, buf + dst);
+      load_lds16(dop + off, buf + kOpBytes + dst);
     }
     if (w < 2) {  // lse (wavefront 0) or delta (1) of row P = lane: token P & 15, head P >> 4
       const size_t r = (size_t)min(16 * tb_n + (lane & 15), N - 1) * Hq + hbase + (lane >> 4);
       const float* src = w == 0 ? a.lse : a.delta;
-      __builtin_amdgcn_global_load_lds(src + r, (lds_ptr)(buf + 2 * kOpBytes + w * kRows * 4), 4, 0, 0);
+      load_lds4(src + r, buf + 2 * kOpBytes + w * kRows * 4);
     }
   };
   f32x4 dk[8], dv[8];

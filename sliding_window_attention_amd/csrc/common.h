@@ -223,6 +223,16 @@ __device__ __forceinline__ void rope_pair(float x, float y, float c, float s, fl
   hi = y * c + x * s;
 }
 
+// Global-to-LDS loads: lane L's 16 (or 4) bytes from src land at lds + 16 L (4 L), the
+// LDS base being uniform across the wavefront.  Completion is counted by vmcnt; a wait
+// for vmcnt(0) and a barrier publish the block to the workgroup.
+__device__ __forceinline__ void load_lds16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
 // s_waitcnt immediate for vmcnt(0) with the other counters left alone (gfx9
 // encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kVmcnt0 = 0x0F70;
