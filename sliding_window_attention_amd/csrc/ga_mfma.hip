@@ -97,49 +97,64 @@ void ga_chunk_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- stage staging: thread t moves the 16-byte unit su = t & 15 of key rows
-  // srow + 32 j (j < 4), srow = t >> 4, of K (pf[j]) and of V (pf[4 + j]) ----
+  // ---- stage staging.  K: wavefront w moves plane w & 3 of the stage rows
+  // r = 64 (w >> 2) + 16 j + lane / 4 (j < 4), lane L taking the unit that belongs at slot
+  // L & 3 of its row (unit 4 (w & 3) + ((L & 3) ^ kswz(r))), so that each store covers 1 KB
+  // of one plane and every 16 lanes write 256 contiguous bytes (rows of one unit index
+  // across the four planes would share their banks: plane bases are 8 KB apart).  V:
+  // thread t moves the unit su = t & 15 of rows srow + 32 j, srow = t >> 4. ----
   const int srow = t >> 4, su = t & 15;
   const size_t key_stride = (size_t)hkv * D;  // elements from one key's row to the next
-  const uint32_t goff0 = (uint32_t)((((size_t)srow * hkv + kvh) * D + su * 8) * sizeof(KvT));
+  const int kcc = w & 3;
+  auto krow = [&](int j) { return 64 * (w >> 2) + 16 * j + (lane >> 2); };
+  auto kunit = [&](int j) { return 4 * kcc + ((lane & 3) ^ kswz(krow(j))); };
+  uint32_t koff[4];  // byte offsets of the thread's K units from the stage's first key row
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    koff[j] = (uint32_t)((((size_t)krow(j) * hkv + kvh) * D + kunit(j) * 8) * sizeof(KvT));
+  const uint32_t voff0 = (uint32_t)((((size_t)srow * hkv + kvh) * D + su * 8) * sizeof(KvT));
   const size_t gstep = 32 * key_stride;  // elements from row r to row r + 32
   GaRaw<FP8> pf[8];
   bool edge = false;  // (uniform) the staged keys reach outside [0, N)
-  bool ok[4] = {true, true, true, true};  // row srow + 32 j of the stage exists
+  bool okk[4] = {true, true, true, true};  // K row krow(j) of the stage exists
+  bool okv[4] = {true, true, true, true};  // V row srow + 32 j of the stage exists
   auto prefetch = [&](int kb) {
     edge = !(kb >= 0 && kb + kStage <= N);
     if (!edge) {
       // whole stage inside the token stream: a uniform base and lane-constant offsets
+      const char* kbase = reinterpret_cast<const char*>(kp + (size_t)kb * key_stride);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const char* kbase = reinterpret_cast<const char*>(kp + (size_t)kb * key_stride + j * gstep);
         const char* vbase = reinterpret_cast<const char*>(vp + (size_t)kb * key_stride + j * gstep);
-        pf[j] = *reinterpret_cast<const GaRaw<FP8>*>(kbase + goff0);
-        pf[4 + j] = *reinterpret_cast<const GaRaw<FP8>*>(vbase + goff0);
+        pf[j] = *reinterpret_cast<const GaRaw<FP8>*>(kbase + koff[j]);
+        pf[4 + j] = *reinterpret_cast<const GaRaw<FP8>*>(vbase + voff0);
       }
     } else {
       // rows outside the stream load a clamped row (no masked loads, which would
       // force early waits) and are zeroed when committed
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = kb + srow + 32 * j;
-        ok[j] = r >= 0 && r < N;
-        const size_t e = ((size_t)min(max(r, 0), N - 1) * hkv + kvh) * D + su * 8;
-        pf[j] = *reinterpret_cast<const GaRaw<FP8>*>(kp + e);
-        pf[4 + j] = *reinterpret_cast<const GaRaw<FP8>*>(vp + e);
+        const int rk = kb + krow(j), rv = kb + srow + 32 * j;
+        okk[j] = rk >= 0 && rk < N;
+        okv[j] = rv >= 0 && rv < N;
+        pf[j] = *reinterpret_cast<const GaRaw<FP8>*>(kp + ((size_t)min(max(rk, 0), N - 1) * hkv + kvh) * D +
+                                                     kunit(j) * 8);
+        pf[4 + j] = *reinterpret_cast<const GaRaw<FP8>*>(vp + ((size_t)min(max(rv, 0), N - 1) * hkv + kvh) * D +
+                                                         su * 8);
       }
     }
   };
   // LDS byte offsets of the thread's units (put_k / put_v layouts).  Stage bases are
-  // multiples of 32, so a key's swizzle equals that of its row in the stage, and
-  // rows srow + 32 j share it.
-  const int ks_off = (su >> 2) * kKPlane + srow * 64 + 16 * ((su & 3) ^ kswz(srow));
+  // multiples of 32, so a key's swizzle equals that of its row in the stage.
+  const int ks_off = kcc * kKPlane + 64 * 64 * (w >> 2) + 16 * lane;  // + 1024 j
   const int vs_off = kKBuf + srow * kVPitch + 16 * su;
   auto commit = [&](char* buf) {
     if (edge) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (!ok[j]) { pf[j] = GaRaw<FP8>{}; pf[4 + j] = GaRaw<FP8>{}; }
+      for (int j = 0; j < 4; ++j) {
+        if (!okk[j]) pf[j] = GaRaw<FP8>{};
+        if (!okv[j]) pf[4 + j] = GaRaw<FP8>{};
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -151,7 +166,7 @@ void ga_chunk_kernel(PrefillArgs a) {
         kx = pf[j];
         vx = pf[4 + j];
       }
-      *reinterpret_cast<u32x4*>(buf + ks_off + 32 * 64 * j) = kx;
+      *reinterpret_cast<u32x4*>(buf + ks_off + 1024 * j) = kx;
       char* v = buf + vs_off + 32 * kVPitch * j;
       *reinterpret_cast<u32x2*>(v) = (u32x2){vx[0], vx[1]};
       *reinterpret_cast<u32x2*>(v + 8) = (u32x2){vx[2], vx[3]};
