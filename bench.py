@@ -433,11 +433,12 @@ def _append_fn(fp8=False):
     return fn
 
 
-def _commit_fn():
-    """Timed call of swa_sink_decode_rope_commit: the step's verify (T = 4) and the commit of
-    the previous step's accepted tokens in one launch.  The set's own new tokens stand for
-    the previous step's (prev_T = 4, its accept counts, its positions); the head is read
-    from ring_head and written to ring_head_out, so every call does the same work."""
+def _commit_fn(fp8=False):
+    """Timed call of swa_sink_decode_rope_commit (or its FP8-ring form): the step's verify
+    (T = 4) and the commit of the previous step's accepted tokens in one launch.  The set's
+    own new tokens stand for the previous step's (prev_T = 4, its accept counts, its
+    positions); the head is read from ring_head and written to ring_head_out, so every call
+    does the same work."""
     import ctypes
 
     import torch
@@ -453,14 +454,15 @@ def _commit_fn():
             x["ring_head_out"] = torch.empty_like(x["ring_head"])
             b, t, hq, d = x["q"].shape
             hkv, w = x["k_cache"].shape[1], x["k_cache"].shape[2]
+            scales = (float(x["k_scale"]), float(x["v_scale"])) if fp8 else ()
             cache[key] = (x["q"].data_ptr(), x["k_new"].data_ptr(), x["v_new"].data_ptr(),
                           x["positions"].data_ptr(), x["k_new"].data_ptr(), x["v_new"].data_ptr(),
                           x["n_accept"].data_ptr(), x["positions"].data_ptr(), t, x["k_cache"].data_ptr(),
-                          x["v_cache"].data_ptr(), x["ring_head"].data_ptr(), x["ring_head_out"].data_ptr(),
-                          x["sinks"].data_ptr(), b, t, hq, hkv, d, w, 0.0, swa.ROPE_BASE_SWA, 1,
-                          x["out"].data_ptr(), x["lse"].data_ptr(),
+                          x["v_cache"].data_ptr(), *scales, x["ring_head"].data_ptr(),
+                          x["ring_head_out"].data_ptr(), x["sinks"].data_ptr(), b, t, hq, hkv, d, w, 0.0,
+                          swa.ROPE_BASE_SWA, 1, x["out"].data_ptr(), x["lse"].data_ptr(),
                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-        rc = lib.swa_sink_decode_rope_commit(*cache[key])
+        rc = (lib.swa_sink_decode_rope_commit_fp8kv if fp8 else lib.swa_sink_decode_rope_commit)(*cache[key])
         if rc != 0:
             raise RuntimeError(lib.swa_last_error().decode())
     return fn
@@ -648,7 +650,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", choices=["prefill", "prefill_fp8", "decode", "decode1", "decode_fp8", "decode_fp8_1",
                                        "decode_rope", "decode_rope_1", "decode_rope_fp8", "append",
-                                       "append_fp8", "mtp_step", "mtp_step_fp8", "mtp_fused", "rope",
+                                       "append_fp8", "mtp_step", "mtp_step_fp8", "mtp_fused", "mtp_fused_fp8", "rope",
                                        "topk", "sparse",
                                        "ga", "varlen", "backward", "copy"],
                     default=None,
@@ -688,13 +690,14 @@ def main(argv=None):
         _log(f"backward 32K: {st}  {fl / (st['mean_ms'] * 1e-3) / 1e12:.1f} TFLOP/s  "
              f"{by / (st['mean_ms'] * 1e-3) / 1e9:.0f} GB/s")
         return 0
-    if args.only == "mtp_fused":
-        xs = _mtp_sets(dev, False)
-        per, _ = _time_calls(_commit_fn(), xs, max(steps, 200), warmup, per_call=False)
+    if args.only in ("mtp_fused", "mtp_fused_fp8"):
+        fp8 = args.only.endswith("fp8")
+        xs = _mtp_sets(dev, fp8)
+        per, _ = _time_calls(_commit_fn(fp8), xs, max(steps, 200), warmup, per_call=False)
         st = _stats(per)
-        by = (wl.workload_work("decode_rope_t4")[1]
-              + wl.mtp_commit_bytes(256, int(xs[0]["n_accept"].sum()), 4, 128, 2))
-        _log(f"mtp_fused B=256 T=4: {st}  {by / (st['mean_ms'] * 1e-3) / 1e9:.0f} GB/s ({by} bytes)")
+        by = (wl.workload_work("decode_rope_fp8_t4" if fp8 else "decode_rope_t4")[1]
+              + wl.mtp_commit_bytes(256, int(xs[0]["n_accept"].sum()), 4, 128, 1 if fp8 else 2))
+        _log(f"{args.only} B=256 T=4: {st}  {by / (st['mean_ms'] * 1e-3) / 1e9:.0f} GB/s ({by} bytes)")
         return 0
     if args.only in ("append", "mtp_step", "append_fp8", "mtp_step_fp8"):
         # append alone is launch-bound from this loop (a ~4 us kernel); in a decode loop it
@@ -886,19 +889,24 @@ def run_extra(dev, steps, warmup):
             "accepted_tokens": int(x["n_accept"].sum()), "what": what, "sets": len(xs)}
         del x, xs
         torch.cuda.empty_cache()
-    _log("MTP step in one launch: commit the previous step's accepted tokens, verify T = 4 (B = 256)")
-    xs = _mtp_sets(dev, False)
-    per, _ = _time_calls(_commit_fn(), xs, max(200, steps), warmup, per_call=False)
-    st = _stats(per)
-    n_acc = int(xs[0]["n_accept"].sum())
-    by = wl.workload_work("decode_rope_t4")[1] + wl.mtp_commit_bytes(256, n_acc, 4, 128, 2)
-    extra["mtp_step_fused_rope_t4"] = {
-        **st, "gbps": by / (st["mean_ms"] * 1e-3) / 1e9,
-        "hbm_frac": by / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": by,
-        "accepted_tokens": n_acc, "sets": len(xs),
-        "what": "swa_sink_decode_rope_commit (commit prev_T = 4 accepted, verify T = 4) per step"}
-    del xs
-    torch.cuda.empty_cache()
+    for fp8 in (False, True):
+        ring = "an FP8" if fp8 else "a bf16"
+        _log(f"MTP step in one launch against {ring} ring: commit the previous step's accepted tokens, "
+             "verify T = 4 (B = 256)")
+        xs = _mtp_sets(dev, fp8)
+        per, _ = _time_calls(_commit_fn(fp8), xs, max(200, steps), warmup, per_call=False)
+        st = _stats(per)
+        n_acc = int(xs[0]["n_accept"].sum())
+        by = (wl.workload_work("decode_rope_fp8_t4" if fp8 else "decode_rope_t4")[1]
+              + wl.mtp_commit_bytes(256, n_acc, 4, 128, 1 if fp8 else 2))
+        name = "swa_sink_decode_rope_commit_fp8kv" if fp8 else "swa_sink_decode_rope_commit"
+        extra["mtp_step_fused_rope_fp8_t4" if fp8 else "mtp_step_fused_rope_t4"] = {
+            **st, "gbps": by / (st["mean_ms"] * 1e-3) / 1e9,
+            "hbm_frac": by / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": by,
+            "accepted_tokens": n_acc, "sets": len(xs),
+            "what": f"{name} (commit prev_T = 4 accepted, verify T = 4) per step"}
+        del xs
+        torch.cuda.empty_cache()
     _log("sparse attention: top-k selection and sparse decode, 64 sequences of 16K-32K tokens")
     xs = _sparse_sets(dev, "topk")
     tb, sb, sfl = _sparse_work(xs[0])

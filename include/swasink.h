@@ -57,7 +57,7 @@ typedef enum {
 
 typedef enum { SWA_DTYPE_F32 = 0, SWA_DTYPE_BF16 = 1 } swa_dtype;
 
-#define SWASINK_ABI_VERSION 9
+#define SWASINK_ABI_VERSION 10
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SWASINK_API __attribute__((visibility("default")))
@@ -341,6 +341,28 @@ SWASINK_API int swa_sink_decode_rope_commit(const void* q, const void* k_new, co
                     const float* sinks, int32_t batch, int32_t T, int32_t num_q_heads,
                     int32_t num_kv_heads, int32_t head_dim, int32_t window, float scale,
                     float rope_base, swa_dtype dtype, void* out, float* lse, void* stream);
+
+/*
+ * swa_sink_decode_rope_commit against an FP8 ring: the results are those of
+ * swa_ring_append_fp8kv(prev_k, prev_v, prev_accept, prev_positions, k_cache, v_cache,
+ * k_scale, v_scale, head, prev_T) followed by swa_sink_decode_rope_fp8kv(q, k_new, v_new,
+ * k_cache, v_cache, k_scale, v_scale, head, positions), head starting as a copy of
+ * ring_head and the advanced head written to ring_head_out (ring_head is only read).
+ *
+ *  k_cache, v_cache [batch, num_kv_heads, window, head_dim] uint8 E4M3 codes, updated in
+ *                   place (the committed tokens' codes as swa_ring_append_fp8kv writes them)
+ *  k_scale, v_scale host fp32, finite and > 0 (SWA_ERR_SHAPE otherwise)
+ * Every other argument, the one-launch shapes and the three-launch fallback are as for
+ * swa_sink_decode_rope_commit.
+ */
+SWASINK_API int swa_sink_decode_rope_commit_fp8kv(const void* q, const void* k_new, const void* v_new,
+                    const int32_t* positions, const void* prev_k, const void* prev_v,
+                    const int32_t* prev_accept, const int32_t* prev_positions, int32_t prev_T,
+                    uint8_t* k_cache, uint8_t* v_cache, float k_scale, float v_scale,
+                    const int32_t* ring_head, int32_t* ring_head_out, const float* sinks,
+                    int32_t batch, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t window, float scale, float rope_base,
+                    swa_dtype dtype, void* out, float* lse, void* stream);
 
 /*
  * swa_ring_append_rope into an FP8 ring (the E4M3 caches swa_sink_decode_fp8kv

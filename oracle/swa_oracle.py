@@ -35,7 +35,8 @@ rounded once to the nearest E4M3 value with ties to the even mantissa, saturatin
 plainest reading of a rounding conversion).
 
 RoPE around decode (swa_rope, swa_sink_decode_rope, swa_ring_append_rope, and the MTP
-step swa_sink_decode_rope_commit, which is the append followed by the decode): the
+step swa_sink_decode_rope_commit, which is the append followed by the decode, with
+swa_sink_decode_rope_commit_fp8kv its FP8-ring form): the
 rotary position embedding with a per-layer base (10,000 in SWA layers, 640,000 in
 GA layers, raised to 5,000,000 for the 256K stage: MiMo-V2-Flash Technical Report
 digest, section 3.1; the positions keep increasing as the window slides, ICML 2026
@@ -530,6 +531,21 @@ def swa_ring_append_fp8kv(k_new, v_new, n_accept, positions, k_codes, v_codes, r
             vc[b, :, slot, :] = vq[t]
         new_heads[b] = (heads[b] + n) % w
     return kc, vc, new_heads
+
+
+def swa_sink_decode_rope_commit_fp8kv(q, k_new, v_new, positions, prev_k, prev_v, prev_accept, prev_positions,
+                                      k_codes, v_codes, k_scale, v_scale, ring_head, sinks, rope_base, window=128,
+                                      scale=None, io_dtype="bf16"):
+    """swa_sink_decode_rope_commit against an FP8 ring: swa_ring_append_fp8kv of the first
+    prev_accept[b] (clamped to [0, prev_T]) previous tokens, then swa_sink_decode_rope_fp8kv
+    of the new ones on the ring so updated.  Returns (out, lse, k_codes, v_codes, ring_head)."""
+    prev_k = _as_f64(prev_k)
+    n = np.clip(np.asarray(prev_accept, dtype=np.int64).reshape(-1), 0, prev_k.shape[1])
+    kc, vc, heads = swa_ring_append_fp8kv(prev_k, prev_v, n, prev_positions, k_codes, v_codes, ring_head,
+                                          rope_base, k_scale, v_scale, io_dtype=io_dtype)
+    out, lse = swa_sink_decode_rope_fp8kv(q, k_new, v_new, kc, vc, k_scale, v_scale, heads, positions, sinks,
+                                          rope_base, window=window, scale=scale, io_dtype=io_dtype)
+    return out, lse, kc, vc, heads
 
 
 def topk_select(scores, lengths, k=1024, recent=128):

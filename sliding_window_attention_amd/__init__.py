@@ -51,6 +51,8 @@ _SIGNATURES = {
                                    _F, _I, _P, _P, _P],
     "swa_sink_decode_rope_commit": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                     _I, _I, _F, _F, _I, _P, _P, _P],
+    "swa_sink_decode_rope_commit_fp8kv": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _F, _F, _P, _P, _P, _I,
+                                          _I, _I, _I, _I, _I, _F, _F, _I, _P, _P, _P],
     "swa_ring_append_rope": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P],
     "swa_ring_append_fp8kv": [_P, _P, _P, _P, _P, _P, _F, _F, _P, _I, _I, _I, _I, _I, _F, _I, _P],
     "swa_topk_select": [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P],
@@ -398,6 +400,48 @@ def swa_sink_decode_rope_commit(q, k_new, v_new, positions, prev_k, prev_v, prev
         prev_v.data_ptr(), prev_accept.data_ptr(), prev_positions.data_ptr(), pt, k_cache.data_ptr(),
         v_cache.data_ptr(), ring_head.data_ptr(), ring_head_out.data_ptr(), sinks.data_ptr(), b, t, hq,
         hkv, d, w, _scale(scale), float(rope_base), _dtype_code(q), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def swa_sink_decode_rope_commit_fp8kv(q, k_new, v_new, positions, prev_k, prev_v, prev_accept, prev_positions,
+                                      k_cache, v_cache, k_scale, v_scale, ring_head, ring_head_out, sinks,
+                                      rope_base=ROPE_BASE_SWA, scale=None, return_lse=True, out=None, lse=None):
+    """swa_sink_decode_rope_commit against an FP8 ring: k_cache/v_cache [B, Hkv, W, D] uint8
+    E4M3 codes with per-tensor scales; the committed tokens enter the ring encoded as
+    swa_ring_append_fp8kv encodes them."""
+    import torch
+
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (prev_k, "prev_k"), (prev_v, "prev_v")):
+        _dev(t, nm, q.dtype)
+    for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, nm, torch.uint8)
+    for t, nm in ((ring_head, "ring_head"), (ring_head_out, "ring_head_out"), (positions, "positions"),
+                  (prev_accept, "prev_accept"), (prev_positions, "prev_positions")):
+        _dev(t, nm, torch.int32)
+    _dev(sinks, "sinks", torch.float32)
+    if q.dim() != 4 or k_new.dim() != 4 or prev_k.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q, k_new, prev_k must be [B, T, H, D] and caches [B, Hkv, W, D]")
+    b, t, hq, d = q.shape
+    hkv, w = k_cache.shape[1], k_cache.shape[2]
+    pt = prev_k.shape[1]
+    if (k_new.shape != (b, t, hkv, d) or v_new.shape != k_new.shape or prev_k.shape != (b, pt, hkv, d)
+            or prev_v.shape != prev_k.shape or v_cache.shape != k_cache.shape or k_cache.shape[0] != b
+            or k_cache.shape[3] != d or ring_head.numel() != b or ring_head_out.numel() != b
+            or positions.numel() != b or prev_accept.numel() != b or prev_positions.numel() != b
+            or sinks.numel() != hq):
+        raise ValueError("inconsistent shapes")
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    if return_lse and lse is None:
+        lse = torch.empty((b, t, hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+    rc = library().swa_sink_decode_rope_commit_fp8kv(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), positions.data_ptr(), prev_k.data_ptr(),
+        prev_v.data_ptr(), prev_accept.data_ptr(), prev_positions.data_ptr(), pt, k_cache.data_ptr(),
+        v_cache.data_ptr(), float(k_scale), float(v_scale), ring_head.data_ptr(), ring_head_out.data_ptr(),
+        sinks.data_ptr(), b, t, hq, hkv, d, w, _scale(scale), float(rope_base), _dtype_code(q), out.data_ptr(),
         lse.data_ptr() if lse is not None else None, _stream(q.device))
     _check(rc)
     return out, lse

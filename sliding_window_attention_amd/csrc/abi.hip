@@ -221,7 +221,7 @@ int decode_common(const void* q, const void* k_new, const void* v_new, const voi
     int rc2 = ring_append_common(commit->prev_k, commit->prev_v, commit->prev_accept, commit->prev_pos,
                                  const_cast<void*>(k_cache), const_cast<void*>(v_cache),
                                  commit->ring_head_out, batch, commit->prev_t, num_kv_heads, head_dim,
-                                 window, rope_base, (swa_dtype)dtype, stream, name);
+                                 window, rope_base, (swa_dtype)dtype, stream, name, fp8, k_scale, v_scale);
     if (rc2) return rc2;
     a.ring_head = commit->ring_head_out;
   }
@@ -420,6 +420,21 @@ int swa_sink_decode_rope_commit(const void* q, const void* k_new, const void* v_
   return decode_common(q, k_new, v_new, k_cache, v_cache, false, 1.f, 1.f, ring_head, sinks, batch,
                        T, num_q_heads, num_kv_heads, head_dim, window, scale, (int)dtype, out, lse,
                        stream, "swa_sink_decode_rope_commit", positions, rope_base, &c);
+}
+
+int swa_sink_decode_rope_commit_fp8kv(const void* q, const void* k_new, const void* v_new,
+                                      const int32_t* positions, const void* prev_k, const void* prev_v,
+                                      const int32_t* prev_accept, const int32_t* prev_positions,
+                                      int32_t prev_T, uint8_t* k_cache, uint8_t* v_cache, float k_scale,
+                                      float v_scale, const int32_t* ring_head, int32_t* ring_head_out,
+                                      const float* sinks, int32_t batch, int32_t T, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t window, float scale,
+                                      float rope_base, swa_dtype dtype, void* out, float* lse,
+                                      void* stream) {
+  const CommitIn c{prev_k, prev_v, prev_accept, prev_positions, prev_T, ring_head_out};
+  return decode_common(q, k_new, v_new, k_cache, v_cache, true, k_scale, v_scale, ring_head, sinks, batch,
+                       T, num_q_heads, num_kv_heads, head_dim, window, scale, (int)dtype, out, lse,
+                       stream, "swa_sink_decode_rope_commit_fp8kv", positions, rope_base, &c);
 }
 
 int swa_sink_decode_rope_fp8kv(const void* q, const void* k_new, const void* v_new,

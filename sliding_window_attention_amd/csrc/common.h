@@ -204,6 +204,40 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
   return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
 }
 
+// E4M3 code (sign bit 7, exponent bits 6..3 with bias 7, mantissa bits 2..0, subnormals
+// m/8 * 2^-6, S.1111.111 = NaN, largest finite 448) of y / scale: the quotient rounded
+// once to the nearest E4M3 value, ties to the even mantissa; finite magnitudes past 448
+// saturate to 448, and a y that is not finite gives the NaN code with y's sign.  The
+// quotient is formed in fp64: y and scale carry at most 24 significant bits, so a
+// quotient that is not itself halfway between two E4M3 values stays about 2^-30
+// (relative) away from such a point and its fp64 rounding cannot land on one.  Every
+// case is computed and the code selected, with no branches.
+template <typename T>
+__device__ __forceinline__ uint32_t e4m3_encode(T y, double scale) {
+  uint32_t sign, nonfinite;
+  if constexpr (sizeof(T) == 2) {
+    const uint16_t b = __builtin_bit_cast(uint16_t, y);
+    sign = (b >> 8) & 0x80u;
+    nonfinite = (b & 0x7F80u) == 0x7F80u;
+  } else {
+    const uint32_t b = __builtin_bit_cast(uint32_t, y);
+    sign = (b >> 24) & 0x80u;
+    nonfinite = (b & 0x7F800000u) == 0x7F800000u;
+  }
+  const double q = __builtin_fabs((double)(float)y / scale);
+  const uint64_t a = __builtin_bit_cast(uint64_t, q);
+  const int e = (int)(a >> 52) - 1023;
+  const uint64_t mant = a & ((1ull << 52) - 1);
+  // mantissa rounded to 3 bits (0..8); 8 carries into the exponent field
+  const int r = (int)((mant + ((1ull << 48) - 1) + ((mant >> 49) & 1)) >> 49);
+  const uint32_t normal = (uint32_t)(((e + 7) << 3) + r);
+  const uint32_t sub = (uint32_t)__builtin_rint(q * 512.0);  // k * 2^-9, k = 0..8
+  uint32_t code = e < -6 ? sub : normal;
+  code = q >= 448.0 ? 0x7Eu : code;
+  code = nonfinite ? 0x7Fu : code;
+  return sign | code;
+}
+
 // cos and sin of the rotary angle of pair i (of head_dim D) at an integer position:
 // angle = pos * base^(-2i/D), formed and reduced to [-pi, pi] in fp64 (positions go to
 // 2^31, where an angle formed in fp32 is off by whole radians), then evaluated in fp32.

@@ -96,7 +96,7 @@ __device__ __forceinline__ void add_partial(const char (*slot)[kColBytes], int i
 // multiplies the ring weights as they are packed for P*V (the running sums stay
 // unscaled), so no cache element is ever rescaled.
 // ROPE: q and the new keys arrive unrotated and are rotated in registers as they are staged.
-// COMMIT (with ROPE, bf16 ring): one launch per MTP step -- the previous step's first
+// COMMIT (with ROPE): one launch per MTP step -- the previous step's first
 // prev_accept[b] tokens are committed to the ring (keys rotated at their positions, as the
 // ring append does) and the drafts are verified against the ring after that commit.  The
 // committed tokens are staged with the new ones (rows 4 .. 7 of the staging, free since
@@ -107,7 +107,7 @@ __device__ __forceinline__ void add_partial(const char (*slot)[kColBytes], int i
 template <int NT, bool FP8, bool ROPE, bool COMMIT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void decode_kernel(DecodeArgs a) {
-  static_assert(!COMMIT || (ROPE && !FP8), "the one-launch step rotates keys into a bf16 ring");
+  static_assert(!COMMIT || ROPE, "the one-launch step rotates the committed keys");
   __shared__ __attribute__((aligned(16))) DecodeSmem<NT> sm;
   const int noct = a.num_q_heads / kHG;
   const int b = blockIdx.x / noct;
@@ -240,9 +240,30 @@ void decode_kernel(DecodeArgs a) {
       st[NT] = rotate(st[NT], ctok >= 0 ? T + ctok : nrow);
       if constexpr (COMMIT) {
         // the first octet of the KV head commits the staged tokens: token ctok to logical
-        // slot kW - ncommit + ctok of the ring after the commit, the key as just rotated
-        if (ctok >= 0 && h_base == kvh * (Hq / hkv)) {
-          const size_t dst = (size_t)((head + kW - ncommit + ctok) & (kW - 1)) * D + 8 * nuu;
+        // slot kW - ncommit + ctok of the ring after the commit, the key as just rotated.
+        // FP8: the ring takes the E4M3 codes of key / k_scale and value / v_scale (as the
+        // FP8 ring append encodes them), and the staged rows become the codes' values,
+        // which is what the verify reads for every other ring slot.
+        const bool writer = ctok >= 0 && h_base == kvh * (Hq / hkv);
+        const size_t dst = (size_t)((head + kW - ncommit + ctok) & (kW - 1)) * D + 8 * nuu;
+        if constexpr (FP8) {
+          if (ctok >= 0) {
+            const bf16x8 kx = __builtin_bit_cast(bf16x8, st[NT]), vx = __builtin_bit_cast(bf16x8, st[NT + 1]);
+            const double ks = a.k_scale, vs = a.v_scale;
+            uint64_t kw = 0, vw = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              kw |= (uint64_t)e4m3_encode(kx[e], ks) << (8 * e);
+              vw |= (uint64_t)e4m3_encode(vx[e], vs) << (8 * e);
+            }
+            if (writer) {
+              *reinterpret_cast<uint64_t*>(const_cast<CacheT*>(kc) + dst) = kw;
+              *reinterpret_cast<uint64_t*>(const_cast<CacheT*>(vc) + dst) = vw;
+            }
+            st[NT] = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(__builtin_bit_cast(u32x2, kw)));
+            st[NT + 1] = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(__builtin_bit_cast(u32x2, vw)));
+          }
+        } else if (writer) {
           *reinterpret_cast<u32x4*>(const_cast<CacheT*>(kc) + dst) = st[NT];
           *reinterpret_cast<u32x4*>(const_cast<CacheT*>(vc) + dst) = st[NT + 1];
         }
@@ -457,10 +478,9 @@ void decode_kernel(DecodeArgs a) {
 bool decode_mfma_supported(const DecodeArgs& a, bool bf16_io) {
   // (an FP8 ring takes the same path: only the cache element type differs)
   const int G = a.num_q_heads / a.num_kv_heads;
-  // the one-launch MTP step: rotation, a bf16 ring, and at most 4 committed tokens (wavefront
-  // 3's newest slots)
-  if (a.prev_accept != nullptr && (a.rope_pos == nullptr || a.cache_fp8 || a.prev_t < 1 || a.prev_t > 4))
-    return false;
+  // the one-launch MTP step: rotation and at most 4 committed tokens (wavefront 3's newest
+  // slots)
+  if (a.prev_accept != nullptr && (a.rope_pos == nullptr || a.prev_t < 1 || a.prev_t > 4)) return false;
   return bf16_io && a.head_dim == 128 && G % kHG == 0 && a.window == kW && a.t_new >= 1 &&
          a.t_new <= 4;
 }
@@ -470,9 +490,14 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
   if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
   const bool two = a.t_new > 2;
   const dim3 grid((unsigned)blocks), block(kThreads);
-  if (a.prev_accept != nullptr) {  // one-launch MTP step (rotation, bf16 ring)
-    if (two) hipLaunchKernelGGL((decode_kernel<2, false, true, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<1, false, true, true>), grid, block, 0, s, a);
+  if (a.prev_accept != nullptr) {  // one-launch MTP step (rotation)
+    if (a.cache_fp8) {
+      if (two) hipLaunchKernelGGL((decode_kernel<2, true, true, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((decode_kernel<1, true, true, true>), grid, block, 0, s, a);
+    } else {
+      if (two) hipLaunchKernelGGL((decode_kernel<2, false, true, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((decode_kernel<1, false, true, true>), grid, block, 0, s, a);
+    }
   } else if (a.rope_pos != nullptr) {  // rotation in the kernel
     if (a.cache_fp8) {
       if (two) hipLaunchKernelGGL((decode_kernel<2, true, true>), grid, block, 0, s, a);

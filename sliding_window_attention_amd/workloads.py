@@ -395,9 +395,10 @@ def append_bytes(batch, n_accepted_total, num_kv_heads, head_dim, elem_bytes, ca
 
 def mtp_commit_bytes(batch, n_accepted_total, num_kv_heads, head_dim, elem_bytes):
     """What the one-launch MTP step adds to the verify's bytes: the committed tokens' K and
-    V written to the ring (the verify reads their rows from the previous step's K / V in
-    place of the ring slots they fill, so its reads are the verify's), plus the accept
-    counts, previous positions and heads (two heads: read and written)."""
+    V written to the ring in its element size (elem_bytes: 2 for bf16, 1 for E4M3), the
+    previous step's rows they come from standing in for the ring slots they fill (so the
+    reads are the verify's), plus the accept counts, previous positions and heads (two
+    heads: read and written)."""
     return 2 * n_accepted_total * num_kv_heads * head_dim * elem_bytes + 4 * 4 * batch
 
 

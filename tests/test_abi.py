@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
                           "swa_sink_prefill_backward_workspace", "swa_sink_prefill_backward_noalloc",
                           "swa_rope", "swa_sink_decode_rope",
                           "swa_ring_append_rope", "swa_topk_select", "swa_sparse_decode",
-                          "swa_sink_decode_rope_fp8kv", "swa_ring_append_fp8kv", "swa_sink_decode_rope_commit",
+                          "swa_sink_decode_rope_fp8kv", "swa_ring_append_fp8kv", "swa_sink_decode_rope_commit", "swa_sink_decode_rope_commit_fp8kv",
                           "swa_last_error", "swa_abi_version"}
 
 
@@ -162,6 +162,17 @@ def _commit(**kw):
 def test_decode_rope_commit_rejects_bad_arguments(kw, code, needle):
     assert _commit(**kw) == code
     assert needle in _last()
+
+
+def test_decode_rope_commit_fp8kv_rejects_bad_scales():
+    lib = swa.library()
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 0.0, 0.5, FAKE, FAKE2, FAKE, 4, 4, 8, 1,
+            128, 128, 0.0, 10000.0, 1, FAKE, NULL, NULL]
+    assert lib.swa_sink_decode_rope_commit_fp8kv(*args) == E_SHAPE and "k_scale" in _last()
+    args[11], args[12] = 0.5, float("nan")
+    assert lib.swa_sink_decode_rope_commit_fp8kv(*args) == E_SHAPE and "finite" in _last()
+    args[12], args[8] = 0.5, 0
+    assert lib.swa_sink_decode_rope_commit_fp8kv(*args) == E_SHAPE and "prev_T" in _last()
 
 
 def test_decode_rope_commit_empty_batch_and_no_rotation():

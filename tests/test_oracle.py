@@ -881,6 +881,51 @@ def test_mtp_steps_equal_attention_over_the_accepted_stream():
         prev_k, prev_v, prev_pos = kn, vn, pos
 
 
+def test_fp8_mtp_steps_equal_attention_over_the_accepted_stream():
+    """FP8 ring: each MTP step's outputs equal brute-force windowed attention with sink over
+    the accepted stream, where the ring's keys and values are their E4M3 code values times
+    the scales (distinct K and V scales), a committed key is rotated at its position before
+    it is encoded, and the step's drafts enter unquantised."""
+    rng = np.random.default_rng(31)
+    w, d, hq, hkv, t_new, base, ks, vs = 6, 8, 4, 2, 3, 10000.0, 0.1875, 0.3
+    kcode = rng.integers(1, 0x70, size=(1, hkv, w, d)).astype(np.uint8) | (rng.integers(0, 2, (1, hkv, w, d)) << 7).astype(np.uint8)
+    vcode = rng.integers(1, 0x70, size=(1, hkv, w, d)).astype(np.uint8) | (rng.integers(0, 2, (1, hkv, w, d)) << 7).astype(np.uint8)
+    heads = np.array([4])
+    sinks = rng.standard_normal(hq)
+    # the stream as the reference sees it: keys already rotated (ring) or raw (to rotate)
+    hist_k = [orc.e4m3_to_float(kcode[0, :, (heads[0] + l) % w, :]) * ks for l in range(w)]
+    hist_v = [orc.e4m3_to_float(vcode[0, :, (heads[0] + l) % w, :]) * vs for l in range(w)]
+    p = 90
+    prev_k = rng.standard_normal((1, t_new, hkv, d))
+    prev_v = rng.standard_normal((1, t_new, hkv, d))
+    kc, vc, head = kcode, vcode, heads
+    pos, prev_pos = p, p
+    for step, acc in enumerate([0, 3, 1, 2, 0, 3]):
+        n = min(acc, t_new)
+        if step > 0:
+            for t in range(n):
+                kr = orc.rope(prev_k[0, t][None], [prev_pos + t], base)[0]
+                hist_k.append(orc.e4m3_to_float(orc.e4m3_encode(kr, ks)) * ks)
+                hist_v.append(orc.e4m3_to_float(orc.e4m3_encode(prev_v[0, t], vs)) * vs)
+            pos = prev_pos + n
+        q = rng.standard_normal((1, t_new, hq, d))
+        kn = rng.standard_normal((1, t_new, hkv, d))
+        vn = rng.standard_normal((1, t_new, hkv, d))
+        o, lse, kc, vc, head = orc.swa_sink_decode_rope_commit_fp8kv(
+            q, kn, vn, [pos], prev_k, prev_v, [acc if step > 0 else 0], [prev_pos], kc, vc, ks, vs, head, sinks,
+            base, window=w, io_dtype=None)
+        newk = orc.rope(kn[0], pos + np.arange(t_new), base)
+        ks_ = np.concatenate([np.stack(hist_k), newk])
+        vs_ = np.concatenate([np.stack(hist_v), vn[0]])
+        L = ks_.shape[0]
+        qs = np.zeros((L, hq, d))
+        qs[L - t_new:] = orc.rope(q[0], pos + np.arange(t_new), base)
+        o2, l2 = brute.attention(qs.tolist(), ks_.tolist(), vs_.tolist(), sinks.tolist(), [0, L], w)
+        np.testing.assert_allclose(o[0], np.asarray(o2)[L - t_new:], atol=1e-12)
+        np.testing.assert_allclose(lse[0], np.asarray(l2)[L - t_new:], atol=1e-12)
+        prev_k, prev_v, prev_pos = kn, vn, pos
+
+
 # ---------------------------------------------------------------------------
 # Token-level sparse attention with a forced recent window (MiMo-V3 / HySparse2 page)
 # ---------------------------------------------------------------------------

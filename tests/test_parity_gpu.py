@@ -1272,6 +1272,109 @@ def test_mtp_commit_full():
     assert np.all(np.abs(got - kc)[diff] <= 2.0 ** -7 * np.abs(kc)[diff] + 1e-30)
 
 
+def _commit_case_fp8(b, t_new, prev_t, hq, hkv, d, w, dt, seed, scales=None):
+    x = _commit_case(b, t_new, prev_t, hq, hkv, d, w, dt, seed)
+    y = wl.make_decode_rope_fp8(b, t_new, hq, hkv, d, w, dt, seed=seed)
+    for k in ("k_cache", "v_cache", "k_scale", "v_scale"):
+        x[k] = y[k]
+    if scales is not None:
+        x["k_scale"], x["v_scale"] = scales
+    return x
+
+
+def _run_commit_fp8(g, x, base, ring_head_out=None):
+    head_out = torch.empty_like(g["ring_head"]) if ring_head_out is None else ring_head_out
+    o, lse = swa.swa_sink_decode_rope_commit_fp8kv(g["q"], g["k_new"], g["v_new"], g["positions"], g["prev_k"],
+                                                   g["prev_v"], g["prev_accept"], g["prev_positions"],
+                                                   g["k_cache"], g["v_cache"], x["k_scale"], x["v_scale"],
+                                                   g["ring_head"], head_out, g["sinks"], base)
+    torch.cuda.synchronize()
+    return o, lse, head_out
+
+
+def _run_append_then_decode_fp8(g, x, base):
+    head = g["ring_head"].clone()
+    swa.swa_ring_append_fp8kv(g["prev_k"], g["prev_v"], g["prev_accept"], g["prev_positions"], g["k_cache"],
+                              g["v_cache"], x["k_scale"], x["v_scale"], head, base)
+    o, lse = swa.swa_sink_decode_rope_fp8kv(g["q"], g["k_new"], g["v_new"], g["k_cache"], g["v_cache"],
+                                            x["k_scale"], x["v_scale"], head, g["positions"], g["sinks"], base)
+    torch.cuda.synchronize()
+    return o, lse, head
+
+
+@pytest.mark.parametrize("case", [(16, 4, 4, None), (16, 1, 1, None), (16, 3, 2, (0.0173, 0.0311)),
+                                  (16, 2, 3, None), (16, 1, 4, (0.0173, 0.0311)), (16, 4, 1, None)],
+                         ids=lambda c: f"B{c[0]}-T{c[1]}-prevT{c[2]}-{'s' if c[3] else 'p2'}")
+def test_mtp_commit_fp8_equals_append_then_decode(case):
+    """FP8 ring: the one-launch step gives the bits of swa_ring_append_fp8kv +
+    swa_sink_decode_rope_fp8kv (outputs, lse, every code of both rings, the head), with
+    power-of-two scales (exact E4M3 ties) and others."""
+    b, t_new, prev_t, scales = case
+    _say(f"FP8 MTP step in one launch vs append + decode: B={b} T={t_new} prev_T={prev_t} scales {scales}")
+    x = _commit_case_fp8(b, t_new, prev_t, 32, 4, 128, 128, "bf16", seed=4800 + 10 * t_new + prev_t,
+                         scales=scales)
+    x["prev_accept"][0], x["prev_accept"][1] = 0, prev_t
+    x["prev_accept"][2], x["prev_accept"][3] = prev_t + 3, -2
+    x["ring_head"][4], x["ring_head"][5], x["ring_head"][6] = 127, -5, 3 * 128 + 1
+    g1, g2 = _gpu(x), _gpu(x)
+    head0 = g1["ring_head"].clone()
+    o1, l1, h1 = _run_commit_fp8(g1, x, 10000.0)
+    o2, l2, h2 = _run_append_then_decode_fp8(g2, x, 10000.0)
+    assert torch.equal(g1["ring_head"], head0)
+    assert torch.equal(h1, h2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(g1["k_cache"], g2["k_cache"]) and torch.equal(g1["v_cache"], g2["v_cache"])
+
+
+@pytest.mark.parametrize("case", [(6, 3, 8, 16, 2, 128, 128, "bf16"), (5, 2, 3, 4, 1, 64, 128, "f32"),
+                                  (4, 4, 4, 8, 8, 128, 64, "bf16")],
+                         ids=lambda c: f"B{c[0]}-T{c[1]}-prevT{c[2]}-{c[3]}/{c[4]}-D{c[5]}-W{c[6]}-{c[7]}")
+def test_mtp_commit_fp8_other_shapes(case):
+    """FP8 ring, shapes outside the one-launch kernel: the same bits as the two calls, and
+    the oracle (rotated keys' codes up to one-step neighbours)."""
+    b, t_new, prev_t, hq, hkv, d, w, dt = case
+    _say(f"FP8 MTP step, other shapes: {case}")
+    x = _commit_case_fp8(b, t_new, prev_t, hq, hkv, d, w, dt, seed=4900 + b)
+    x["prev_accept"][0] = prev_t
+    g1, g2 = _gpu(x), _gpu(x)
+    o1, l1, h1 = _run_commit_fp8(g1, x, 640000.0)
+    o2, l2, h2 = _run_append_then_decode_fp8(g2, x, 640000.0)
+    assert torch.equal(h1, h2) and torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(g1["k_cache"], g2["k_cache"]) and torch.equal(g1["v_cache"], g2["v_cache"])
+    io = "bf16" if dt == "bf16" else "f32"
+    o_ref, l_ref, kc, vc, h_ref = orc.swa_sink_decode_rope_commit_fp8kv(
+        x["q"], x["k_new"], x["v_new"], x["positions"].numpy(), x["prev_k"], x["prev_v"],
+        np.clip(x["prev_accept"].numpy(), 0, prev_t), x["prev_positions"].numpy(), x["k_cache"].numpy(),
+        x["v_cache"].numpy(), x["k_scale"], x["v_scale"], x["ring_head"].numpy(), x["sinks"], 640000.0,
+        window=w, io_dtype=io)
+    assert_close(x["q"].dtype, o1, o_ref, l1, l_ref, f"FP8 mtp commit {case}")
+    assert np.array_equal(h1.cpu().numpy(), h_ref)
+    assert np.array_equal(g1["v_cache"].cpu().numpy(), vc)
+    _codes_close(g1["k_cache"].cpu().numpy(), kc, f"FP8 mtp commit keys {case}")
+
+
+def test_mtp_commit_fp8_full():
+    """The FP8-ring step at the benchmarked size (B = 256, T = 4, prev_T = 4, accept counts
+    ~ U{0..4}): every output element against the oracle, the head, every code."""
+    _say("FP8 MTP step in one launch, full: B=256 T=4 prev_T=4 32/4 D128 bf16")
+    x = wl.make_workload("decode_rope_fp8_t4")
+    gen = torch.Generator().manual_seed(4951)
+    x["prev_k"] = torch.randn(256, 4, 4, 128, generator=gen).to(torch.bfloat16)
+    x["prev_v"] = torch.randn(256, 4, 4, 128, generator=gen).to(torch.bfloat16)
+    x["prev_accept"] = torch.randint(0, 5, (256,), generator=gen, dtype=torch.int64).to(torch.int32)
+    x["prev_positions"] = x["positions"] - x["prev_accept"]
+    g = _gpu(x)
+    o, lse, h = _run_commit_fp8(g, x, 10000.0)
+    o_ref, l_ref, kc, vc, h_ref = orc.swa_sink_decode_rope_commit_fp8kv(
+        x["q"], x["k_new"], x["v_new"], x["positions"].numpy(), x["prev_k"], x["prev_v"],
+        x["prev_accept"].numpy(), x["prev_positions"].numpy(), x["k_cache"].numpy(), x["v_cache"].numpy(),
+        x["k_scale"], x["v_scale"], x["ring_head"].numpy(), x["sinks"], 10000.0)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, "FP8 mtp commit full")
+    assert np.array_equal(h.cpu().numpy(), h_ref)
+    assert np.array_equal(g["v_cache"].cpu().numpy(), vc)
+    _codes_close(g["k_cache"].cpu().numpy(), kc, "FP8 mtp commit full keys", min_same=0.9999)
+
+
 # ---------------------------------------------------------------------------
 # FP8 ring with RoPE: decode (rotation in the kernel) and the append that encodes
 # ---------------------------------------------------------------------------
