@@ -267,6 +267,15 @@ __device__ __forceinline__ void load_lds4(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
 }
 
+// The element of a rotary pair that a lane holds, from its own value x and its partner's p:
+// x c - p s if it holds the pair's first element, else x c + p s -- rope_pair's roundings
+// (each product rounded, then the sum), selected without a branch.
+__device__ __forceinline__ float rope_own(float x, float p, float c, float s, bool first) {
+#pragma clang fp contract(off)
+  const float a = x * c, b = p * s;
+  return a + (first ? -b : b);
+}
+
 // s_waitcnt immediate for vmcnt(0) with the other counters left alone (gfx9
 // encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kVmcnt0 = 0x0F70;

@@ -224,11 +224,17 @@ void decode_kernel(DecodeArgs a) {
         for (int e = 0; e < 8; ++e) {
           const float c = sm.u.in.cs[t * 64 + 8 * (tid & 7) + e][0];
           const float sn = sm.u.in.cs[t * 64 + 8 * (tid & 7) + e][1];
-          // this lane holds x[i] (first) or x[i + 64] of pair i: the pair's lo or hi
-          float lo, hi;
-          if (first) rope_pair((float)me[e], (float)pa[e], c, sn, lo, hi);
-          else rope_pair((float)pa[e], (float)me[e], c, sn, lo, hi);
-          y[e] = (bf16)(first ? lo : hi);
+          // this lane holds x[i] (first) or x[i + 64] of pair i: the pair's lo or hi.  The
+          // one-launch step keeps the branch per lane, which holds its registers under the
+          // budget (the select form spills there); both round the same products.
+          if constexpr (COMMIT) {
+            float lo, hi;
+            if (first) rope_pair((float)me[e], (float)pa[e], c, sn, lo, hi);
+            else rope_pair((float)pa[e], (float)me[e], c, sn, lo, hi);
+            y[e] = (bf16)(first ? lo : hi);
+          } else {
+            y[e] = (bf16)rope_own((float)me[e], (float)pa[e], c, sn, first);
+          }
         }
         return __builtin_bit_cast(u32x4, y);
       };

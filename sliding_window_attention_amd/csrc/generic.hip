@@ -97,10 +97,7 @@ struct DecodeKeys {
         for (int e = 0; e < Elem<T>::kVec; ++e) {
           float c, s;
           rope_cos_sin(rope_pos0 + (j - W), (d % H) + e, D, rope_l2b, &c, &s);
-          float lo, hi;
-          if (d < H) rope_pair(dst[e], part[e], c, s, lo, hi);
-          else rope_pair(part[e], dst[e], c, s, lo, hi);
-          dst[e] = (float)Elem<T>::store_cast(d < H ? lo : hi);
+          dst[e] = (float)Elem<T>::store_cast(rope_own(dst[e], part[e], c, s, d < H));
         }
       }
       return;
