@@ -50,7 +50,8 @@ Token-level sparse attention with a forced recent window (topk_select,
 sparse_decode): the HySparse2 selection of the MiMo-V3 / HySparse2 report (page on
 the MiMo-V3 news, HySparse2 sections): the full-attention layer's scores pick the top
 k tokens (1024 there) and the most recent 128 tokens are always kept, the sparse
-layers attending to that set over the shared KV cache.  Readings where the pages are
+layers attending to that set over the shared KV cache (sparse_decode_mtp: the newest
+T tokens as queries, each with its own recent window).  Readings where the pages are
 silent: the scores arrive per (sequence, KV head) over the cached positions; the top
 k are taken among the tokens older than the recent window (larger score first, the
 lower position on equal scores) and returned in increasing position; the query (the
@@ -546,6 +547,42 @@ def swa_sink_decode_rope_commit_fp8kv(q, k_new, v_new, positions, prev_k, prev_v
     out, lse = swa_sink_decode_rope_fp8kv(q, k_new, v_new, kc, vc, k_scale, v_scale, heads, positions, sinks,
                                           rope_base, window=window, scale=scale, io_dtype=io_dtype)
     return out, lse, kc, vc, heads
+
+
+def sparse_decode_mtp(q, k_cache, v_cache, lengths, indices, counts, sinks, recent=128, scale=None):
+    """MTP verify in a sparse layer: the newest T tokens of each sequence (positions
+    p_t = L-T+t, t < T, all in the cache) are queries.  Query t attends the selected
+    positions older than its own recent window, indices[b, g, :counts[b, g]] below
+    p_t-recent+1, plus that window max(0, p_t-recent+1) .. p_t -- with T = 1 this is
+    sparse_decode.  q [B, T, Hq, D]; caches [B, Hkv, Lmax, D]; sinks [Hq] or None.
+    Returns (o [B, T, Hq, D], lse [B, T, Hq])."""
+    q, kc, vc = _as_f64(q), _as_f64(k_cache), _as_f64(v_cache)
+    bsz, t_new, hq, d = q.shape
+    hkv = kc.shape[1]
+    grp = hq // hkv
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lens = np.asarray(lengths, dtype=np.int64).reshape(bsz)
+    idx = np.asarray(indices, dtype=np.int64)
+    cnt = np.asarray(counts, dtype=np.int64)
+    o = np.zeros((bsz, t_new, hq, d))
+    lse = np.zeros((bsz, t_new, hq))
+    for b in range(bsz):
+        L = int(lens[b])
+        for t in range(t_new):
+            p = L - t_new + t
+            lo = max(0, p - recent + 1)
+            for h in range(hq):
+                g = h // grp
+                sel = idx[b, g, :cnt[b, g]]
+                keys = np.concatenate([sel[sel < lo], np.arange(lo, p + 1)])
+                a = sc * (kc[b, g, keys] @ q[b, t, h])
+                sink = NEG_INF if sinks is None else float(_as_f64(sinks)[h])
+                m = max(a.max(), sink)
+                e = np.exp(a - m)
+                z = e.sum() + (np.exp(sink - m) if sink != NEG_INF else 0.0)
+                o[b, t, h] = (e @ vc[b, g, keys]) / z
+                lse[b, t, h] = m + np.log(z)
+    return o, lse
 
 
 def topk_select(scores, lengths, k=1024, recent=128):

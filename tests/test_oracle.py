@@ -1026,6 +1026,85 @@ def test_sparse_decode_matches_brute_force_and_ignores_index_order():
     np.testing.assert_allclose(l2, lse, atol=1e-12)
 
 
+def _prefill_rows(q_t, kc, vc, sinks, b, L, window):
+    """The oracle's windowed prefill of sequence b's first L tokens, rows L-T .. L-1
+    (q_t [T, Hq, D] placed on the newest T tokens, zeros elsewhere)."""
+    t_new, hq, d = q_t.shape
+    qs = np.zeros((L, hq, d))
+    qs[L - t_new:] = q_t
+    ks = kc[b, :, :L].transpose(1, 0, 2)
+    vs = vc[b, :, :L].transpose(1, 0, 2)
+    o, lse = orc.swa_sink_prefill(qs, ks, vs, sinks, [0, L], window)
+    return o[L - t_new:], lse[L - t_new:]
+
+
+def test_sparse_mtp_special_cases_reduce_to_dense_attention():
+    """T verified tokens in a sparse layer: T = 1 is sparse_decode; every older token
+    selected gives full causal attention for each of the T rows, none selected the
+    recent-window SWA (each row with its own window) -- through the pinned prefill oracle."""
+    rng = np.random.default_rng(23)
+    _, kc, vc, sinks, scores = _sparse_case(3, 4, 2, 16, 60, 24)
+    lens = np.array([60, 10, 33])
+    recent = 8
+    for t_new in (1, 2, 3):
+        q = rng.standard_normal((3, t_new, 4, 16))
+        idx, cnt = orc.topk_select(scores, lens, k=64, recent=recent)
+        o, lse = orc.sparse_decode_mtp(q, kc, vc, lens, idx, cnt, sinks, recent=recent)
+        idx0, cnt0 = orc.topk_select(scores, lens, k=0, recent=recent)
+        o0, lse0 = orc.sparse_decode_mtp(q, kc, vc, lens, idx0, cnt0, sinks, recent=recent)
+        if t_new == 1:
+            o1, l1 = orc.sparse_decode(q[:, 0], kc, vc, lens, idx, cnt, sinks, recent=recent)
+            np.testing.assert_allclose(o[:, 0], o1, atol=1e-12)
+            np.testing.assert_allclose(lse[:, 0], l1, atol=1e-12)
+        for b in range(3):
+            L = int(lens[b])
+            of, lf = _prefill_rows(q[b], kc, vc, sinks, b, L, L)
+            np.testing.assert_allclose(o[b], of, atol=1e-12)
+            np.testing.assert_allclose(lse[b], lf, atol=1e-12)
+            ow, lw = _prefill_rows(q[b], kc, vc, sinks, b, L, recent)
+            np.testing.assert_allclose(o0[b], ow, atol=1e-12)
+            np.testing.assert_allclose(lse0[b], lw, atol=1e-12)
+
+
+def test_sparse_mtp_matches_brute_force_with_the_windows_overlapping_the_selection():
+    """Brute force over explicit key lists: query t sees the selected positions below its
+    own window and the window itself, each once, including a selection that reaches into
+    the older drafts' windows (positions just below the newest token's window)."""
+    rng = np.random.default_rng(25)
+    hq, hkv, d, lmax, recent, t_new = 4, 2, 8, 40, 5, 3
+    _, kc, vc, sinks, _ = _sparse_case(2, hq, hkv, d, lmax, 26)
+    q = rng.standard_normal((2, t_new, hq, d))
+    lens = np.array([40, 9])
+    idx = np.full((2, hkv, 6), -1, dtype=np.int64)
+    cnt = np.zeros((2, hkv), dtype=np.int64)
+    for b in range(2):
+        L = int(lens[b])
+        for g in range(hkv):  # the newest candidates (just below the newest window) always chosen
+            cand = np.arange(L - recent)
+            pick = np.sort(np.concatenate([cand[-2:], rng.choice(cand[:-2], size=min(4, len(cand) - 2), replace=False)]))
+            idx[b, g, :len(pick)] = pick
+            cnt[b, g] = len(pick)
+    o, lse = orc.sparse_decode_mtp(q, kc, vc, lens, idx, cnt, sinks, recent=recent)
+    for b in range(2):
+        L = int(lens[b])
+        for t in range(t_new):
+            p = L - t_new + t
+            for g in range(hkv):
+                win = list(range(max(0, p - recent + 1), p + 1))
+                keys = [j for j in idx[b, g, :cnt[b, g]] if j not in win] + win
+                assert len(set(keys)) == len(keys)
+                m = len(keys)
+                qs = [[[0.0] * d for _ in range(hq)] for _ in range(m)]
+                for h in range(2 * g, 2 * g + 2):
+                    qs[m - 1][h] = list(q[b, t, h])
+                ks = [[list(kc[b, gg, j]) for gg in range(hkv)] for j in keys]
+                vs = [[list(vc[b, gg, j]) for gg in range(hkv)] for j in keys]
+                ob, lb = brute.attention(qs, ks, vs, list(sinks), [0, m], None)
+                for h in range(2 * g, 2 * g + 2):
+                    np.testing.assert_allclose(o[b, t, h], ob[m - 1][h], atol=1e-12)
+                    assert abs(lse[b, t, h] - lb[m - 1][h]) < 1e-12
+
+
 # ---------------------------------------------------------------------------
 # the row-sampled evaluation used at sizes where the full fp64 output is too large
 # ---------------------------------------------------------------------------
