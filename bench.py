@@ -335,6 +335,48 @@ def _sparse_fn():
     return fn
 
 
+def _sparse_mtp_fn():
+    """Timed call of swa_sparse_decode_mtp (T = 2) on the sparse workload: the newest two
+    tokens of each sequence as queries, the selection already made."""
+    import ctypes
+
+    import torch
+
+    import sliding_window_attention_amd as swa
+
+    lib = swa.library()
+    cache = {}
+
+    def fn(x):
+        key = id(x)
+        if key not in cache:
+            if "q2" not in x:
+                b, hq, d = x["q"].shape
+                x["q2"] = torch.randn((b, 2, hq, d), generator=torch.Generator(device=x["q"].device).manual_seed(17),
+                                      device=x["q"].device).to(x["q"].dtype)
+                x["out2"] = torch.empty_like(x["q2"])
+                x["lse2"] = torch.empty((b, 2, hq), dtype=torch.float32, device=x["q"].device)
+            b, t, hq, d = x["q2"].shape
+            hkv, lmax = x["k_cache"].shape[1], x["k_cache"].shape[2]
+            cache[key] = (x["q2"].data_ptr(), x["k_cache"].data_ptr(), x["v_cache"].data_ptr(),
+                          x["lengths"].data_ptr(), x["indices"].data_ptr(), x["counts"].data_ptr(),
+                          None, b, t, hq, hkv, d, lmax, x["indices"].shape[2], swa.SPARSE_RECENT, 0.0, 1,
+                          x["out2"].data_ptr(), x["lse2"].data_ptr(),
+                          ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        rc = lib.swa_sparse_decode_mtp(*cache[key])
+        if rc != 0:
+            raise RuntimeError(lib.swa_last_error().decode())
+    return fn
+
+
+def _sparse_mtp_work(x):
+    from sliding_window_attention_amd import workloads as wl
+
+    w = wl.WORKLOADS["sparse_b64"]
+    return wl.sparse_mtp_work(x["lengths_host"].tolist(), x["indices"].cpu().numpy(), x["counts"].cpu().numpy(),
+                              w.num_q_heads, w.num_kv_heads, w.head_dim, w.extra["recent"], 2, 2)
+
+
 def _sparse_work(x):
     from sliding_window_attention_amd import workloads as wl
 
@@ -651,7 +693,7 @@ def main(argv=None):
     ap.add_argument("--only", choices=["prefill", "prefill_fp8", "decode", "decode1", "decode_fp8", "decode_fp8_1",
                                        "decode_rope", "decode_rope_1", "decode_rope_fp8", "append",
                                        "append_fp8", "mtp_step", "mtp_step_fp8", "mtp_fused", "mtp_fused_fp8", "rope",
-                                       "topk", "sparse",
+                                       "topk", "sparse", "sparse_mtp",
                                        "ga", "varlen", "backward", "copy"],
                     default=None,
                     help="time a single workload (for profiling runs); prints no JSON line")
@@ -718,6 +760,14 @@ def main(argv=None):
         st = _stats(per)
         by = wl.append_bytes(256, int(x["n_accept"].sum()), 4, 128, 2, cache_elem_bytes=1 if fp8 else None)
         _log(f"{args.only} B=256 T=4: {st}  (append bytes {by})")
+        return 0
+    if args.only == "sparse_mtp":
+        xs = _sparse_sets(dev, "sparse")
+        fn = _sparse_mtp_fn()
+        per, _ = _time_calls(fn, xs, max(steps, 100), warmup, per_call=False)
+        st = _stats(per)
+        fl, by = _sparse_mtp_work(xs[0])
+        _log(f"sparse_mtp T=2 sparse_b64: {st}  {by / (st['mean_ms'] * 1e-3) / 1e9:.0f} GB/s ({by} bytes)")
         return 0
     if args.only in ("topk", "sparse"):
         xs = _sparse_sets(dev, args.only)
@@ -921,6 +971,14 @@ def run_extra(dev, steps, warmup):
     extra["sparse_decode_b64"] = {**st, "gbps": sb / (st["mean_ms"] * 1e-3) / 1e9,
                                   "hbm_frac": sb / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": sb,
                                   "tflops": sfl / (st["mean_ms"] * 1e-3) / 1e12, "sets": len(xs)}
+    _log("sparse MTP verify: the newest two tokens of the same 64 sequences")
+    per, _ = _time_calls(_sparse_mtp_fn(), xs, max(100, steps), warmup, per_call=False)
+    st = _stats(per)
+    mfl, mby = _sparse_mtp_work(xs[0])
+    extra["sparse_decode_mtp_t2_b64"] = {**st, "gbps": mby / (st["mean_ms"] * 1e-3) / 1e9,
+                                         "hbm_frac": mby / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                         "bytes": mby, "tflops": mfl / (st["mean_ms"] * 1e-3) / 1e12,
+                                         "sets": len(xs)}
     del xs
     torch.cuda.empty_cache()
 

@@ -57,7 +57,7 @@ typedef enum {
 
 typedef enum { SWA_DTYPE_F32 = 0, SWA_DTYPE_BF16 = 1 } swa_dtype;
 
-#define SWASINK_ABI_VERSION 10
+#define SWASINK_ABI_VERSION 11
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SWASINK_API __attribute__((visibility("default")))
@@ -431,6 +431,30 @@ SWASINK_API int swa_sparse_decode(const void* q, const void* k_cache, const void
                     const float* sinks, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                     int32_t head_dim, int32_t max_len, int32_t k, int32_t recent, float scale,
                     swa_dtype dtype, void* out, float* lse, void* stream);
+
+/*
+ * MTP verify in a sparse layer: the newest T tokens of each sequence are the queries
+ * (positions p_t = L - T + t, t < T, with L = lengths[b]; their K/V already in the
+ * caches).  Query t attends its own most recent window max(0, p_t - recent + 1) .. p_t
+ * and the selected positions (indices[b, g, :counts[b, g]]) below that window: a
+ * selected position inside the window is counted once, as part of it (reading of the
+ * HySparse2 selection for drafts; with T = 1 this is swa_sparse_decode).  The selection
+ * must be increasing, as swa_topk_select writes it.
+ *
+ *  q     [batch, T, num_q_heads, head_dim] dtype
+ *  out   [batch, T, num_q_heads, head_dim] dtype
+ *  lse   [batch, T, num_q_heads] fp32, or NULL
+ *  T     1 <= T <= max_len; k + recent + T - 1 <= 8192
+ * Lengths below T are taken as T.  Every other argument is as for swa_sparse_decode; the
+ * matrix-core kernel takes T <= 2 (bf16, head_dim 128, groups of 8k heads), other shapes
+ * the vector kernel.
+ */
+SWASINK_API int swa_sparse_decode_mtp(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* lengths, const int32_t* indices, const int32_t* counts,
+                    const float* sinks, int32_t batch, int32_t T, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t max_len, int32_t k,
+                    int32_t recent, float scale, swa_dtype dtype, void* out, float* lse,
+                    void* stream);
 
 /* Message for the last non-OK return on the calling thread ("" if none). */
 SWASINK_API const char* swa_last_error(void);

@@ -503,18 +503,20 @@ int swa_topk_select(const float* scores, const int32_t* lengths, int32_t batch, 
   return hip_status(swa::launch_topk_select(a, static_cast<hipStream_t>(stream)), name);
 }
 
-int swa_sparse_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* lengths,
-                      const int32_t* indices, const int32_t* counts, const float* sinks, int32_t batch,
-                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_len,
-                      int32_t k, int32_t recent, float scale, swa_dtype dtype, void* out, float* lse,
-                      void* stream) {
-  const char* name = "swa_sparse_decode";
+// (internal: the single-token and the MTP entry points below)
+static int sparse_common(const void* q, const void* k_cache, const void* v_cache, const int32_t* lengths,
+                  const int32_t* indices, const int32_t* counts, const float* sinks, int32_t batch, int32_t T,
+                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_len, int32_t k,
+                  int32_t recent, float scale, swa_dtype dtype, void* out, float* lse, void* stream,
+                  const char* name) {
   int rc = check_dtype((int)dtype);
   if (rc) return rc;
   if ((rc = check_heads(num_q_heads, num_kv_heads, head_dim))) return rc;
   if (batch < 0 || max_len < 1) return fail(SWA_ERR_SHAPE, "%s: batch >= 0 and max_len >= 1 are required", name);
-  if (k < 0 || recent < 1 || (long long)k + recent > 8192)
-    return fail(SWA_ERR_SHAPE, "%s: k >= 0, recent >= 1 and k + recent <= 8192 are required", name);
+  if (T < 1 || T > max_len)
+    return fail(SWA_ERR_SHAPE, "%s: T must satisfy 1 <= T <= max_len (got T=%d, max_len=%d)", name, T, max_len);
+  if (k < 0 || recent < 1 || (long long)k + recent + T - 1 > 8192)
+    return fail(SWA_ERR_SHAPE, "%s: k >= 0, recent >= 1 and k + recent + T - 1 <= 8192 are required", name);
   if ((long long)batch * num_kv_heads * max_len * head_dim > (1LL << 40))
     return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
   if (batch == 0) return ok();
@@ -523,9 +525,27 @@ int swa_sparse_decode(const void* q, const void* k_cache, const void* v_cache, c
   swa::SparseArgs a;
   a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.lengths = lengths; a.indices = indices;
   a.counts = counts; a.sinks = sinks; a.out = out; a.lse = lse;
-  a.batch = batch; a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
-  a.max_len = max_len; a.k = k; a.recent = recent; a.scale = resolve_scale(scale, head_dim);
+  a.batch = batch; a.t_new = T; a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim; a.max_len = max_len; a.k = k; a.recent = recent; a.scale = resolve_scale(scale, head_dim);
   return hip_status(swa::launch_sparse_decode(a, dtype == SWA_DTYPE_BF16, static_cast<hipStream_t>(stream)), name);
+}
+
+int swa_sparse_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* lengths,
+                      const int32_t* indices, const int32_t* counts, const float* sinks, int32_t batch,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_len,
+                      int32_t k, int32_t recent, float scale, swa_dtype dtype, void* out, float* lse,
+                      void* stream) {
+  return sparse_common(q, k_cache, v_cache, lengths, indices, counts, sinks, batch, 1, num_q_heads, num_kv_heads,
+                       head_dim, max_len, k, recent, scale, dtype, out, lse, stream, "swa_sparse_decode");
+}
+
+int swa_sparse_decode_mtp(const void* q, const void* k_cache, const void* v_cache, const int32_t* lengths,
+                          const int32_t* indices, const int32_t* counts, const float* sinks, int32_t batch,
+                          int32_t T, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_len,
+                          int32_t k, int32_t recent, float scale, swa_dtype dtype, void* out, float* lse,
+                          void* stream) {
+  return sparse_common(q, k_cache, v_cache, lengths, indices, counts, sinks, batch, T, num_q_heads, num_kv_heads,
+                       head_dim, max_len, k, recent, scale, dtype, out, lse, stream, "swa_sparse_decode_mtp");
 }
 
 int64_t swa_sink_prefill_backward_workspace(int32_t total_tokens, int32_t num_q_heads) {

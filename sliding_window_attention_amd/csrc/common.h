@@ -128,16 +128,17 @@ struct TopkArgs {
 
 // One query token per sequence over selected + recent keys of a [B, Hkv, Lmax, D] cache.
 struct SparseArgs {
-  const void* q;             // [B, Hq, D]
+  const void* q;             // [B, T, Hq, D] (T = t_new)
   const void* k_cache;       // [B, Hkv, Lmax, D]
   const void* v_cache;
   const int32_t* lengths;    // [B]
   const int32_t* indices;    // [B, Hkv, k]
   const int32_t* counts;     // [B, Hkv]
   const float* sinks;        // [Hq] or nullptr
-  void* out;                 // [B, Hq, D]
-  float* lse;                // [B, Hq] or nullptr
+  void* out;                 // [B, T, Hq, D]
+  float* lse;                // [B, T, Hq] or nullptr
   int32_t batch;
+  int32_t t_new = 1;         // queries per sequence: its newest T tokens (MTP verify)
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t head_dim;

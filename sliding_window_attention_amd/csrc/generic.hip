@@ -125,13 +125,16 @@ struct SparseKeys {
   const T* kc;  // this (sequence, kv head)'s cache rows: [Lmax, D]
   const T* vc;
   const int32_t* sel;
-  int cnt, L, nrec;
+  int cnt;   // selected positions seen by the row
+  int L;     // the sequence's length (selected positions are clamped into it)
+  int end;   // the row's position + 1: its window is end - nrec .. end - 1
+  int nrec;
   __device__ int pos(int m) const {
     if (m < cnt) {
       const int j = sel[m];
       return j < 0 ? 0 : (j >= L ? L - 1 : j);
     }
-    return L - nrec + (m - cnt);
+    return end - nrec + (m - cnt);
   }
   __device__ void load_key(int m, int d, float* dst) const { Elem<T>::load16(kc + (size_t)pos(m) * D + d, dst); }
   __device__ float load_val(int m, int e) const { return Elem<T>::load1(vc + (size_t)pos(m) * D + e); }
@@ -260,24 +263,32 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void generic_decode_kernel(D
 
 template <typename T, int D>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void generic_sparse_kernel(SparseArgs a) {
+  // row = (sequence b, query token t, head h); token t sits at position L - T + t and sees
+  // the selected positions below its own window and the window itself
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  const int hq = a.num_q_heads;
-  if (row >= a.batch * hq) return;
-  const int b = row / hq, h = row - b * hq;
+  const int hq = a.num_q_heads, Tn = a.t_new;
+  if (row >= a.batch * Tn * hq) return;
+  const int h = row % hq;
+  const int bt = row / hq;
+  const int t = bt % Tn, b = bt / Tn;
   const int hkv = a.num_kv_heads;
   const int kvh = h / (hq / hkv);
   int L = a.lengths[b];
-  L = L < 1 ? 1 : (L > a.max_len ? a.max_len : L);
+  L = L < Tn ? Tn : (L > a.max_len ? a.max_len : L);
   int cnt = a.counts[b * hkv + kvh];
   cnt = cnt < 0 ? 0 : (cnt > a.k ? a.k : cnt);
   SparseKeys<T, D> keys;
   keys.kc = static_cast<const T*>(a.k_cache) + ((size_t)b * hkv + kvh) * a.max_len * D;
   keys.vc = static_cast<const T*>(a.v_cache) + ((size_t)b * hkv + kvh) * a.max_len * D;
   keys.sel = a.indices + ((size_t)b * hkv + kvh) * a.k;
-  keys.cnt = cnt;
   keys.L = L;
-  keys.nrec = a.recent < L ? a.recent : L;
-  const int M = cnt + keys.nrec;
+  const int p = L - Tn + t;
+  keys.end = p + 1;
+  keys.nrec = a.recent < p + 1 ? a.recent : p + 1;
+  // the selection is increasing: only its last Tn - 1 - t entries can reach into the window
+  keys.cnt = cnt;
+  for (int z = 0; z < Tn - 1 - t && keys.cnt > 0 && keys.pos(keys.cnt - 1) >= p + 1 - keys.nrec; ++z) --keys.cnt;
+  const int M = keys.cnt + keys.nrec;
   const float sink2 = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
   attend_row<T, D>(static_cast<const T*>(a.q) + (size_t)row * D, keys, 0, M - 1, sink2, a.scale * kLog2e,
                    static_cast<T*>(a.out) + (size_t)row * D, a.lse ? a.lse + row : nullptr);
@@ -285,7 +296,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void generic_sparse_kernel(S
 
 template <typename T, int D>
 hipError_t launch_sparse_t(const SparseArgs& a, hipStream_t s) {
-  const long rows = (long)a.batch * a.num_q_heads;
+  const long rows = (long)a.batch * a.t_new * a.num_q_heads;
   const long blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;

@@ -372,6 +372,12 @@ struct SparseSmem {
   float o[3][16][kOPitch];             // partial O of wavefronts 1..3
 };
 
+// T queries per sequence (1, or 2 for an MTP verify): the 16 query columns are token
+// c >> 3, head c & 7 (T = 1: columns 8..15 zero).  Query t (position p_t = L - T + t) sees
+// the selected positions below its own recent window and the window
+// max(0, p_t - recent + 1) .. p_t; the staged list holds the selection and the union of
+// the T windows, and each column masks the rest.
+template <int T>
 __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs a) {
   __shared__ __attribute__((aligned(16))) SparseSmem sm;
   const int noct = a.num_q_heads / kHG;
@@ -386,10 +392,11 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
   const int i = lane & 15, g = lane >> 4;
 
   int L = as_const(a.lengths)[b];
-  L = L < 1 ? 1 : (L > a.max_len ? a.max_len : L);
+  L = L < T ? T : (L > a.max_len ? a.max_len : L);  // the T queries are the newest tokens
   int cnt = as_const(a.counts)[b * hkv + kvh];
   cnt = cnt < 0 ? 0 : (cnt > a.k ? a.k : cnt);
-  const int nrec = a.recent < L ? a.recent : L;
+  const int rs = max(0, L - a.recent - (T - 1));  // first position of the windows' union
+  const int nrec = L - rs;
   const int M = cnt + nrec;  // keys of the list (<= kMaxList: checked on the host)
 
   // ---- stage the key list and the 8 query rows ----
@@ -405,14 +412,30 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
     sm.keys[m] = j;
   }
   {
-    const int r = tid >> 4, u = tid & 15;  // 16 rows x 16 units
+    const int r = tid >> 4, u = tid & 15;  // 16 rows x 16 units: token r >> 3, head r & 7
     u32x4 x = {0, 0, 0, 0};
-    if (r < kHG)
-      x = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(a.q) +
-                                           ((size_t)b * a.num_q_heads + h_base + r) * D + 8 * u);
+    if ((r >> 3) < T)
+      x = *reinterpret_cast<const u32x4*>(
+          static_cast<const bf16*>(a.q) + (((size_t)b * T + (r >> 3)) * a.num_q_heads + h_base + (r & 7)) * D + 8 * u);
     *reinterpret_cast<u32x4*>(&sm.q[r][16 * u]) = x;
   }
   __syncthreads();
+  // this lane's column i: token tq, its window's first position wlo, and cut, the
+  // selected keys below that window (the selection is increasing, and only its last
+  // T - 1 - tq entries can reach into the window)
+  const int tq = i >> 3;
+  const int pq = L - T + tq;
+  const int wlo = pq - a.recent + 1;
+  int cut = cnt;
+  if constexpr (T > 1) {
+    for (int z = 0; z < T - 1 - tq && cut > 0 && sm.keys[cut - 1] >= wlo; ++z) --cut;
+  }
+  // key m of the list is seen by this lane's column
+  auto visible = [&](int m) {
+    if (m < cnt) return m < cut;
+    const int pos = rs + (m - cnt);
+    return pos >= wlo && pos <= pq;
+  };
 
   const bf16* kc = static_cast<const bf16*>(a.k_cache) + ((size_t)b * hkv + kvh) * a.max_len * D;
   const bf16* vc = static_cast<const bf16*>(a.v_cache) + ((size_t)b * hkv + kvh) * a.max_len * D;
@@ -467,18 +490,23 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool ok = 32 * ch + 8 * g + 4 * s + r < M;
+        const int m = 32 * ch + 8 * g + 4 * s + r;
+        bool ok = m < M;
+        if constexpr (T > 1) ok = ok && visible(m);
         s2[s][r] = ok ? s2[s][r] * c : -INFINITY;
         mx = fmaxf(mx, s2[s][r]);
       }
-    const float mnew = fmaxf(mcol, quad_max(mx));  // finite: the chunk's first key is valid
-    const float alpha = fast_exp2(mcol - mnew);
+    // T = 1: finite, the chunk's first key is valid; T > 1: a column may have seen no key
+    // yet (its reference is then 0 and every weight 0)
+    const float mnew = fmaxf(mcol, quad_max(mx));
+    const float mref = (T > 1 && mnew == -INFINITY) ? 0.f : mnew;
+    const float alpha = fast_exp2(mcol - mref);
     float ps = 0.f;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s2[s][r] = fast_exp2(s2[s][r] - mnew);
+        s2[s][r] = fast_exp2(s2[s][r] - mref);
         ps += s2[s][r];
       }
     lcol = lcol * alpha + quad_sum(ps);
@@ -514,8 +542,9 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
     }
   }
   __syncthreads();
-  if (w != 0 || i >= kHG) return;
-  const int h = h_base + i;
+  if (w != 0 || i >= kHG * T) return;
+  const int h = h_base + (i & 7);
+  const size_t orow = ((size_t)b * T + tq) * a.num_q_heads + h;
   const float sink2 = a.sinks ? as_const(a.sinks)[h] * kLog2e : -INFINITY;
   float mt = sink2;
 #pragma unroll
@@ -528,7 +557,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
     z += sm.l[v][i] * sc[v];
   }
   const float inv = 1.f / z;
-  bf16* out = static_cast<bf16*>(a.out) + ((size_t)b * a.num_q_heads + h) * D;
+  bf16* out = static_cast<bf16*>(a.out) + orow * D;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     float acc[8];
@@ -550,7 +579,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
     for (int bb = 0; bb < 8; ++bb) v8[bb] = (bf16)(acc[bb] * inv);
     *reinterpret_cast<bf16x8*>(out + 32 * g + 8 * r) = v8;
   }
-  if (a.lse != nullptr && g == 0) a.lse[(size_t)b * a.num_q_heads + h] = (mt + fast_log2(z)) * kLn2;
+  if (a.lse != nullptr && g == 0) a.lse[orow] = (mt + fast_log2(z)) * kLn2;
 }
 
 }  // namespace
@@ -565,7 +594,8 @@ hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s) {
 
 bool sparse_mfma_supported(const SparseArgs& a, bool bf16_io) {
   const int G = a.num_q_heads / a.num_kv_heads;
-  return bf16_io && a.head_dim == 128 && G % kHG == 0 && (long)a.k + a.recent <= kMaxList;
+  return bf16_io && a.head_dim == 128 && G % kHG == 0 && a.t_new >= 1 && a.t_new <= 2 &&
+         (long)a.k + a.recent + a.t_new - 1 <= kMaxList;
 }
 
 hipError_t launch_sparse_decode(const SparseArgs& a, bool bf16_io, hipStream_t s) {
@@ -573,7 +603,8 @@ hipError_t launch_sparse_decode(const SparseArgs& a, bool bf16_io, hipStream_t s
   const long blocks = (long)a.batch * (a.num_q_heads / kHG);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(sparse_decode_kernel, dim3((unsigned)blocks), dim3(kSpThreads), 0, s, a);
+  if (a.t_new == 2) hipLaunchKernelGGL(sparse_decode_kernel<2>, dim3((unsigned)blocks), dim3(kSpThreads), 0, s, a);
+  else hipLaunchKernelGGL(sparse_decode_kernel<1>, dim3((unsigned)blocks), dim3(kSpThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -199,6 +199,32 @@ def sparse_bytes(lengths, num_q_heads, num_kv_heads, head_dim, topk, recent, ele
             + b * num_kv_heads * (topk + 1) * 4 + 4 * b * num_q_heads)
 
 
+def sparse_mtp_work(lengths, indices, counts, num_q_heads, num_kv_heads, head_dim, recent, t_new, elem_bytes):
+    """(flops, bytes) of the sparse MTP verify of the newest t_new tokens: 4 D FLOPs per
+    (query head, visible key) -- query t sees the selected positions below its window and
+    the window -- and per (sequence, KV head) the selection plus the windows' union read
+    once as K and V rows, the queries read, the outputs and LSE written, the selection."""
+    import numpy as np
+
+    idx = np.asarray(indices)
+    cnt = np.asarray(counts)
+    grp = num_q_heads // num_kv_heads
+    visible = rows = 0
+    for b, n in enumerate(lengths):
+        n = max(int(n), t_new)
+        for g in range(num_kv_heads):
+            sel = idx[b, g, :cnt[b, g]]
+            rows += len(sel) + min(recent + t_new - 1, n)
+            for t in range(t_new):
+                p = n - t_new + t
+                lo = max(0, p - recent + 1)
+                visible += grp * (int((sel < lo).sum()) + p - lo + 1)
+    bsz = len(lengths)
+    by = (2 * rows * head_dim * elem_bytes + 2 * bsz * t_new * num_q_heads * head_dim * elem_bytes
+          + 4 * int(cnt.size) + 4 * int(cnt.sum()) + 4 * bsz * t_new * num_q_heads)
+    return 4 * head_dim * visible, by
+
+
 def sparse_flops(lengths, num_q_heads, head_dim, topk, recent):
     """4 D FLOPs per (query head, key) over the selected and recent keys."""
     keys = sum(min(topk, max(0, int(n) - recent)) + min(recent, int(n)) for n in lengths)

@@ -1654,6 +1654,74 @@ def test_sparse_decode_limits_match_dense_kernels():
             assert err <= 2e-2 and lerr <= 1e-3, (k, bb, err, lerr)
 
 
+@pytest.mark.parametrize("case", [(8, 32, 4, 128, 6000, "bf16", 1024, 128, True, 2),
+                                  (6, 16, 2, 128, 3000, "bf16", 300, 37, False, 2),
+                                  (5, 8, 1, 128, 900, "bf16", 1024, 128, True, 1),
+                                  (4, 32, 4, 128, 2500, "bf16", 2000, 128, True, 3),
+                                  (4, 8, 2, 64, 2000, "bf16", 200, 64, True, 2),
+                                  (3, 4, 1, 128, 1500, "f32", 256, 128, True, 2)],
+                         ids=lambda c: f"B{c[0]}-{c[1]}/{c[2]}-D{c[3]}-L{c[4]}-{c[5]}-k{c[6]}-r{c[7]}-"
+                                       f"{'sink' if c[8] else 'nosink'}-T{c[9]}")
+def test_sparse_mtp_against_oracle(case):
+    """MTP verify in the sparse layer: the newest T tokens, each with its own recent window
+    and the selection below it; the newest candidate (just below the newest token's window)
+    forced into the selection, so it falls inside the older drafts' windows; a sequence
+    shorter than the window and one of exactly T tokens."""
+    b, hq, hkv, d, lmax, dt, k, recent, sink, t_new = case
+    _say(f"sparse MTP verify {case}")
+    x = wl.make_sparse(b, hq, hkv, d, lmax, dt, seed=6300 + lmax + k, with_sinks=sink)
+    gen = torch.Generator().manual_seed(6301 + lmax)
+    x["q"] = torch.randn(b, t_new, hq, d, generator=gen).to(x["q"].dtype)
+    x["lengths"][0] = lmax
+    x["lengths"][1] = min(lmax, recent // 2 + 1)
+    x["lengths"][2] = t_new
+    x["scores"][0, :, lmax - recent - 1] = 1e4  # selected, and inside the older drafts' windows
+    if b > 3 and int(x["lengths"][3]) > recent + 1:
+        x["scores"][3, :, int(x["lengths"][3]) - recent - 1] = 1e4
+    idx, cnt = _topk_gpu(x["scores"], x["lengths"], k, recent)
+    ridx, rcnt = orc.topk_select(x["scores"], x["lengths"].numpy(), k=k, recent=recent)
+    assert np.array_equal(idx, ridx) and np.array_equal(cnt, rcnt)
+    g = {k_: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k_, v in x.items()}
+    o, lse = swa.swa_sparse_decode_mtp(g["q"], g["k_cache"], g["v_cache"], g["lengths"],
+                                       torch.as_tensor(idx, dtype=torch.int32).to(DEV),
+                                       torch.as_tensor(cnt, dtype=torch.int32).to(DEV), g["sinks"], recent=recent)
+    torch.cuda.synchronize()
+    o_ref, l_ref = orc.sparse_decode_mtp(x["q"], x["k_cache"], x["v_cache"], x["lengths"].numpy(), ridx, rcnt,
+                                         x["sinks"], recent=recent)
+    assert_close(x["q"].dtype, o, o_ref, lse, l_ref, f"sparse MTP {case}")
+    if t_new == 1:  # the same kernel as the single-token entry point
+        o1, l1 = _sparse_gpu({**x, "q": x["q"][:, 0].contiguous()}, idx, cnt, recent)
+        assert torch.equal(o1, o[:, 0]) and torch.equal(l1, lse[:, 0])
+
+
+def test_sparse_mtp_limits_match_dense_kernels():
+    """k = 0 gives each of the T rows the windowed prefill's row (window 128); every older
+    token selected gives full causal attention -- against the library's own dense prefill."""
+    _say("sparse MTP verify limits vs the library's dense prefill, T = 2")
+    b, hq, hkv, d, lmax, t_new = 4, 32, 4, 128, 1000, 2
+    x = wl.make_sparse(b, hq, hkv, d, lmax, "bf16", seed=6400, min_len=300)
+    x["q"] = torch.randn(b, t_new, hq, d, generator=torch.Generator().manual_seed(6401)).to(torch.bfloat16)
+    for k, window_of in ((0, lambda n: 128), (1024, lambda n: n)):
+        idx, cnt = _topk_gpu(x["scores"], x["lengths"], k, 128)
+        o, lse = swa.swa_sparse_decode_mtp(x["q"].to(DEV), x["k_cache"].to(DEV), x["v_cache"].to(DEV),
+                                           x["lengths"].to(DEV), torch.as_tensor(idx, dtype=torch.int32).to(DEV),
+                                           torch.as_tensor(cnt, dtype=torch.int32).to(DEV), x["sinks"].to(DEV))
+        torch.cuda.synchronize()
+        for bb in range(b):
+            n = int(x["lengths"][bb])
+            qs = torch.zeros(n, hq, d, dtype=torch.bfloat16)
+            qs[n - t_new:] = x["q"][bb]
+            ks = x["k_cache"][bb, :, :n].transpose(0, 1).contiguous()
+            vs = x["v_cache"][bb, :, :n].transpose(0, 1).contiguous()
+            od, ld = swa.swa_sink_prefill(qs.to(DEV), ks.to(DEV), vs.to(DEV), x["sinks"].to(DEV),
+                                          torch.tensor([0, n], dtype=torch.int32, device=DEV), n,
+                                          window=window_of(n))
+            torch.cuda.synchronize()
+            err = (o[bb].float() - od[n - t_new:].float()).abs().max().item()
+            lerr = (lse[bb] - ld[n - t_new:]).abs().max().item()
+            assert err <= 2e-2 and lerr <= 1e-3, (k, bb, err, lerr)
+
+
 def test_sparse_full_size_workload():
     """The benchmarked workload (64 sequences of 16K-32K tokens, [64, 4, 32768, 128]
     caches drawn on the GPU): every selection index exactly, every output row against the
