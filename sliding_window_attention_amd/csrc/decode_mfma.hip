@@ -14,7 +14,9 @@
 // partial outputs then simply add.  The ring is read straight from HBM into MFMA
 // operand registers (V rows 16 lanes per 256-byte row, fully coalesced, and
 // transposed in registers); the query columns and the new tokens' K/V, shared by
-// the four wavefronts, are staged once in LDS.
+// the four wavefronts, are staged once in LDS.  Template switches: an FP8 (E4M3) ring,
+// the rotary embedding applied in the kernel, and the one-launch MTP step that first
+// commits the previous step's accepted tokens to the ring (see decode_kernel).
 #include <type_traits>
 
 #include "common.h"
@@ -49,11 +51,12 @@ struct DecodeSmem {
     char o[kMergeSlots<NT>][NT * 16][kColBytes];  // partial outputs, fp32
     struct {
       char q[NT * 16][kRowPitch];  // query columns (dead once the scores are formed)
-      char kn[16][kRowPitch];      // new-token K rows (rows past T repeat row T-1)
+      char kn[16][kRowPitch];      // new-token K rows (rows past T repeat row T-1; in the one-launch
+                                   // MTP step rows 4 .. 7 hold the committed tokens)
       float cs[8 * 64][2];         // rotary cos / sin per (token, pair), when rotating
     } in;
   } u;
-  char vn[16][kRowPitch];  // new-token V rows (rows past T repeat row T-1)
+  char vn[16][kRowPitch];  // new-token V rows (as kn)
 };
 
 // Partial O^T of lane (i, g), column tt*16 + i, head-dim 32g + 8r + b, to/from LDS.
