@@ -118,8 +118,8 @@ struct DecodeKeys {
   }
 };
 
-// Keys of the sparse decode: list entry m < cnt is the selected position sel[m]
-// (clamped into the sequence), then the recent window L - nrec .. L - 1.
+// Keys of one sparse-decode row: list entry m < cnt is the selected position sel[m]
+// (clamped into the sequence), then the row's recent window end - nrec .. end - 1.
 template <typename T, int D>
 struct SparseKeys {
   const T* kc;  // this (sequence, kv head)'s cache rows: [Lmax, D]

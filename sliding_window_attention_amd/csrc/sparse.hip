@@ -18,7 +18,9 @@
 //    wavefronts take 32-key chunks in turn: K rows gathered straight into MFMA A
 //    operands, S^T = K Q^T for the octet's 8 heads, an online softmax per head, V rows
 //    transposed in registers for O^T += V^T P^T.  The wavefronts' partial results are
-//    merged exactly through LDS, with the sink in the denominator.
+//    merged exactly through LDS, with the sink in the denominator.  MTP verify (T = 2):
+//    the second token's heads take the query columns the single token leaves empty, and
+//    each column masks the keys its token does not see.
 #include "common.h"
 #include "kernels.h"
 #include "mfma_tile.h"
