@@ -51,7 +51,8 @@ sparse_decode): the HySparse2 selection of the MiMo-V3 / HySparse2 report (page 
 the MiMo-V3 news, HySparse2 sections): the full-attention layer's scores pick the top
 k tokens (1024 there) and the most recent 128 tokens are always kept, the sparse
 layers attending to that set over the shared KV cache (sparse_decode_mtp: the newest
-T tokens as queries, each with its own recent window).  Readings where the pages are
+T tokens as queries, each with its own recent window; sparse_decode_mtp_fp8kv: over a
+cache of E4M3 codes).  Readings where the pages are
 silent: the scores arrive per (sequence, KV head) over the cached positions; the top
 k are taken among the tokens older than the recent window (larger score first, the
 lower position on equal scores) and returned in increasing position; the query (the
@@ -583,6 +584,16 @@ def sparse_decode_mtp(q, k_cache, v_cache, lengths, indices, counts, sinks, rece
                 o[b, t, h] = (e @ vc[b, g, keys]) / z
                 lse[b, t, h] = m + np.log(z)
     return o, lse
+
+
+def sparse_decode_mtp_fp8kv(q, k_codes, v_codes, k_scale, v_scale, lengths, indices, counts, sinks, recent=128,
+                            scale=None):
+    """sparse_decode_mtp over a cache of E4M3 codes with per-tensor scales: the caches
+    dequantised exactly (code value times k_scale / v_scale).  k_codes / v_codes
+    [B, Hkv, Lmax, D] uint8; T = 1 is the single-token sparse decode."""
+    kc = e4m3_to_float(k_codes) * float(k_scale)
+    vc = e4m3_to_float(v_codes) * float(v_scale)
+    return sparse_decode_mtp(q, kc, vc, lengths, indices, counts, sinks, recent=recent, scale=scale)
 
 
 def topk_select(scores, lengths, k=1024, recent=128):

@@ -1105,6 +1105,52 @@ def test_sparse_mtp_matches_brute_force_with_the_windows_overlapping_the_selecti
                     assert abs(lse[b, t, h] - lb[m - 1][h]) < 1e-12
 
 
+def test_sparse_mtp_fp8kv_brute_force_with_distinct_scales():
+    """FP8 cache: brute force over explicit key lists whose K and V values are decoded by
+    hand from the E4M3 bit fields (sign, 4 exponent bits with bias 7, 3 mantissa bits,
+    subnormals) times distinct scales, T = 2, the selection reaching into the older
+    draft's window."""
+    rng = np.random.default_rng(27)
+    hq, hkv, d, lmax, recent, t_new, ks, vs = 4, 2, 8, 30, 5, 2, 0.1875, 0.3
+    kcode = _codes(rng, (2, hkv, lmax, d), lo=0)[0]
+    vcode = _codes(rng, (2, hkv, lmax, d), lo=0)[0]
+    sinks = rng.standard_normal(hq)
+    q = rng.standard_normal((2, t_new, hq, d))
+    lens = np.array([30, 12])
+    idx = np.full((2, hkv, 4), -1, dtype=np.int64)
+    cnt = np.zeros((2, hkv), dtype=np.int64)
+    for b in range(2):
+        L = int(lens[b])
+        for g in range(hkv):
+            pick = np.sort(np.concatenate([[L - recent - 1], rng.choice(L - recent - 1, size=3, replace=False)]))
+            idx[b, g, :4] = pick
+            cnt[b, g] = 4
+
+    def hand(c):
+        s_, e, m = (c >> 7) & 1, (c >> 3) & 15, c & 7
+        v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        return -v if s_ else v
+
+    o, lse = orc.sparse_decode_mtp_fp8kv(q, kcode, vcode, ks, vs, lens, idx, cnt, sinks, recent=recent)
+    for b in range(2):
+        L = int(lens[b])
+        for t in range(t_new):
+            p = L - t_new + t
+            for g in range(hkv):
+                win = list(range(max(0, p - recent + 1), p + 1))
+                keys = [int(j) for j in idx[b, g, :cnt[b, g]] if j not in win] + win
+                m = len(keys)
+                qs = [[[0.0] * d for _ in range(hq)] for _ in range(m)]
+                for h in range(2 * g, 2 * g + 2):
+                    qs[m - 1][h] = list(q[b, t, h])
+                kk = [[[hand(int(c)) * ks for c in kcode[b, gg, j]] for gg in range(hkv)] for j in keys]
+                vv = [[[hand(int(c)) * vs for c in vcode[b, gg, j]] for gg in range(hkv)] for j in keys]
+                ob, lb = brute.attention(qs, kk, vv, list(sinks), [0, m], None)
+                for h in range(2 * g, 2 * g + 2):
+                    np.testing.assert_allclose(o[b, t, h], ob[m - 1][h], atol=1e-12)
+                    assert abs(lse[b, t, h] - lb[m - 1][h]) < 1e-12
+
+
 # ---------------------------------------------------------------------------
 # the row-sampled evaluation used at sizes where the full fp64 output is too large
 # ---------------------------------------------------------------------------
