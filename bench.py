@@ -369,12 +369,68 @@ def _sparse_mtp_fn():
     return fn
 
 
-def _sparse_mtp_work(x):
+def _sparse_fp8_fn(t_new):
+    """Timed call of swa_sparse_decode_fp8kv (the newest t_new tokens as queries) on the
+    sparse workload with its caches as E4M3 codes, the selection already made."""
+    import ctypes
+
+    import torch
+
+    import sliding_window_attention_amd as swa
+
+    lib = swa.library()
+    cache = {}
+
+    def fn(x):
+        key = id(x)
+        if key not in cache:
+            qk, ok, lk = f"q{t_new}", f"out{t_new}", f"lse{t_new}"
+            if qk not in x:
+                b, hq, d = x["q"].shape
+                x[qk] = torch.randn((b, t_new, hq, d), generator=torch.Generator(device=x["q"].device).manual_seed(17),
+                                    device=x["q"].device).to(x["q"].dtype)
+                x[ok] = torch.empty_like(x[qk])
+                x[lk] = torch.empty((b, t_new, hq), dtype=torch.float32, device=x["q"].device)
+            b, t, hq, d = x[qk].shape
+            hkv, lmax = x["k_codes"].shape[1], x["k_codes"].shape[2]
+            cache[key] = (x[qk].data_ptr(), x["k_codes"].data_ptr(), x["v_codes"].data_ptr(), ctypes.c_float(1 / 32),
+                          ctypes.c_float(1 / 64), x["lengths"].data_ptr(), x["indices"].data_ptr(),
+                          x["counts"].data_ptr(), None, b, t, hq, hkv, d, lmax, x["indices"].shape[2],
+                          swa.SPARSE_RECENT, 0.0, 1, x[ok].data_ptr(), x[lk].data_ptr(),
+                          ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        rc = lib.swa_sparse_decode_fp8kv(*cache[key])
+        if rc != 0:
+            raise RuntimeError(lib.swa_last_error().decode())
+    return fn
+
+
+def _with_fp8_caches(xs):
+    """Replace each sparse set's bf16 caches by E4M3 codes of the same shape, drawn on the
+    GPU per sequence (scales 1/32 and 1/64: values of about N(0, 1))."""
+    import torch
+
+    from sliding_window_attention_amd import workloads as wl
+
+    for i, x in enumerate(xs):
+        shape = tuple(x["k_cache"].shape)
+        dev = x["k_cache"].device
+        del x["k_cache"], x["v_cache"]
+        gen = torch.Generator(device=dev).manual_seed(9001 + i)
+        x["k_codes"] = torch.empty(shape, dtype=torch.uint8, device=dev)
+        x["v_codes"] = torch.empty(shape, dtype=torch.uint8, device=dev)
+        for b in range(shape[0]):
+            x["k_codes"][b] = wl.e4m3_codes(shape[1:], gen)
+            x["v_codes"][b] = wl.e4m3_codes(shape[1:], gen)
+    torch.cuda.empty_cache()
+    return xs
+
+
+def _sparse_mtp_work(x, t_new=2, kv_elem_bytes=2):
     from sliding_window_attention_amd import workloads as wl
 
     w = wl.WORKLOADS["sparse_b64"]
     return wl.sparse_mtp_work(x["lengths_host"].tolist(), x["indices"].cpu().numpy(), x["counts"].cpu().numpy(),
-                              w.num_q_heads, w.num_kv_heads, w.head_dim, w.extra["recent"], 2, 2)
+                              w.num_q_heads, w.num_kv_heads, w.head_dim, w.extra["recent"], t_new, 2, kv_elem_bytes)
 
 
 def _sparse_work(x):
@@ -693,7 +749,7 @@ def main(argv=None):
     ap.add_argument("--only", choices=["prefill", "prefill_fp8", "decode", "decode1", "decode_fp8", "decode_fp8_1",
                                        "decode_rope", "decode_rope_1", "decode_rope_fp8", "append",
                                        "append_fp8", "mtp_step", "mtp_step_fp8", "mtp_fused", "mtp_fused_fp8", "rope",
-                                       "topk", "sparse", "sparse_mtp",
+                                       "topk", "sparse", "sparse_mtp", "sparse_fp8", "sparse_mtp_fp8",
                                        "ga", "varlen", "backward", "copy"],
                     default=None,
                     help="time a single workload (for profiling runs); prints no JSON line")
@@ -760,6 +816,14 @@ def main(argv=None):
         st = _stats(per)
         by = wl.append_bytes(256, int(x["n_accept"].sum()), 4, 128, 2, cache_elem_bytes=1 if fp8 else None)
         _log(f"{args.only} B=256 T=4: {st}  (append bytes {by})")
+        return 0
+    if args.only in ("sparse_fp8", "sparse_mtp_fp8"):
+        t_new = 1 if args.only == "sparse_fp8" else 2
+        xs = _with_fp8_caches(_sparse_sets(dev, "sparse"))
+        per, _ = _time_calls(_sparse_fp8_fn(t_new), xs, max(steps, 100), warmup, per_call=False)
+        st = _stats(per)
+        fl, by = _sparse_mtp_work(xs[0], t_new, 1)
+        _log(f"{args.only} T={t_new} sparse_b64: {st}  {by / (st['mean_ms'] * 1e-3) / 1e9:.0f} GB/s ({by} bytes)")
         return 0
     if args.only == "sparse_mtp":
         xs = _sparse_sets(dev, "sparse")
@@ -979,6 +1043,15 @@ def run_extra(dev, steps, warmup):
                                          "hbm_frac": mby / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                          "bytes": mby, "tflops": mfl / (st["mean_ms"] * 1e-3) / 1e12,
                                          "sets": len(xs)}
+    _log("sparse decode and MTP verify over an FP8 cache (E4M3 codes) of the same shape")
+    xs = _with_fp8_caches(xs)
+    for t_new, name in ((1, "sparse_decode_fp8_b64"), (2, "sparse_decode_mtp_fp8_t2_b64")):
+        per, _ = _time_calls(_sparse_fp8_fn(t_new), xs, max(100, steps), warmup, per_call=False)
+        st = _stats(per)
+        ffl, fby = _sparse_mtp_work(xs[0], t_new, 1)
+        extra[name] = {**st, "gbps": fby / (st["mean_ms"] * 1e-3) / 1e9,
+                       "hbm_frac": fby / (st["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": fby,
+                       "tflops": ffl / (st["mean_ms"] * 1e-3) / 1e12, "sets": len(xs)}
     del xs
     torch.cuda.empty_cache()
 

@@ -57,7 +57,7 @@ typedef enum {
 
 typedef enum { SWA_DTYPE_F32 = 0, SWA_DTYPE_BF16 = 1 } swa_dtype;
 
-#define SWASINK_ABI_VERSION 11
+#define SWASINK_ABI_VERSION 12
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SWASINK_API __attribute__((visibility("default")))
@@ -454,6 +454,25 @@ SWASINK_API int swa_sparse_decode_mtp(const void* q, const void* k_cache, const 
                     const float* sinks, int32_t batch, int32_t T, int32_t num_q_heads,
                     int32_t num_kv_heads, int32_t head_dim, int32_t max_len, int32_t k,
                     int32_t recent, float scale, swa_dtype dtype, void* out, float* lse,
+                    void* stream);
+
+/*
+ * swa_sparse_decode_mtp over an FP8 cache: k_cache and v_cache hold E4M3 codes, element
+ * value = code value * k_scale (K) or v_scale (V), as the FP8 ring of swa_sink_decode_fp8kv
+ * (MiMo-V2-Flash report, FP8 KV cache; HySparse2 selection over it).  The codes are decoded
+ * exactly and scaled in fp32, so the result is swa_sparse_decode_mtp's on the dequantised
+ * cache up to fp32 rounding.
+ *
+ *  k_cache, v_cache [batch, num_kv_heads, max_len, head_dim] uint8 E4M3 codes
+ *  k_scale, v_scale finite, > 0
+ * Every other argument is as for swa_sparse_decode_mtp (T = 1 is the single-token step;
+ * the matrix-core kernel takes the same shapes).
+ */
+SWASINK_API int swa_sparse_decode_fp8kv(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                    float k_scale, float v_scale, const int32_t* lengths, const int32_t* indices,
+                    const int32_t* counts, const float* sinks, int32_t batch, int32_t T,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_len,
+                    int32_t k, int32_t recent, float scale, swa_dtype dtype, void* out, float* lse,
                     void* stream);
 
 /* Message for the last non-OK return on the calling thread ("" if none). */

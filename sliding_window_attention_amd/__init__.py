@@ -58,6 +58,8 @@ _SIGNATURES = {
     "swa_topk_select": [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P],
     "swa_sparse_decode": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P],
     "swa_sparse_decode_mtp": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P],
+    "swa_sparse_decode_fp8kv": [_P, _P, _P, _F, _F, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P,
+                                _P, _P],
 }
 
 # HySparse2 selection sizes (MiMo-V3 / HySparse2 report): top 1024 plus the recent 128.
@@ -627,6 +629,44 @@ def swa_sparse_decode_mtp(q, k_cache, v_cache, lengths, indices, counts, sinks=N
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lengths.data_ptr(), indices.data_ptr(),
         counts.data_ptr(), sinks.data_ptr() if sinks is not None else None, b, t, hq, hkv, d, lmax, k, recent,
         _scale(scale), _dtype_code(q), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def swa_sparse_decode_fp8kv(q, k_cache, v_cache, k_scale, v_scale, lengths, indices, counts, sinks=None,
+                            recent=SPARSE_RECENT, scale=None, return_lse=True, out=None, lse=None):
+    """swa_sparse_decode_mtp over an FP8 cache: k_cache/v_cache [B, Hkv, Lmax, D] uint8 E4M3
+    codes, element value = code value * k_scale (K) or v_scale (V) (python floats);
+    q [B, T, Hq, D] (T = 1: the single-token step)."""
+    import torch
+
+    _dev(q, "q")
+    _dev(k_cache, "k_cache", torch.uint8)
+    _dev(v_cache, "v_cache", torch.uint8)
+    _dev(lengths, "lengths", torch.int32)
+    _dev(indices, "indices", torch.int32)
+    _dev(counts, "counts", torch.int32)
+    if sinks is not None:
+        _dev(sinks, "sinks", torch.float32)
+    if q.dim() != 4 or k_cache.dim() != 4 or indices.dim() != 3:
+        raise ValueError("q must be [B, T, Hq, D], caches [B, Hkv, Lmax, D], indices [B, Hkv, k]")
+    b, t, hq, d = q.shape
+    hkv, lmax = k_cache.shape[1], k_cache.shape[2]
+    k = indices.shape[2]
+    if (k_cache.shape != (b, hkv, lmax, d) or v_cache.shape != k_cache.shape or lengths.numel() != b
+            or indices.shape[:2] != (b, hkv) or counts.shape != (b, hkv)
+            or (sinks is not None and sinks.numel() != hq)):
+        raise ValueError("inconsistent shapes")
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    if return_lse and lse is None:
+        lse = torch.empty((b, t, hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _dev(lse, "lse", torch.float32)
+    rc = library().swa_sparse_decode_fp8kv(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), float(k_scale), float(v_scale), lengths.data_ptr(),
+        indices.data_ptr(), counts.data_ptr(), sinks.data_ptr() if sinks is not None else None, b, t, hq, hkv, d,
+        lmax, k, recent, _scale(scale), _dtype_code(q), out.data_ptr(), lse.data_ptr() if lse is not None else None,
         _stream(q.device))
     _check(rc)
     return out, lse

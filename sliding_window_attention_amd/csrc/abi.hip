@@ -508,10 +508,12 @@ static int sparse_common(const void* q, const void* k_cache, const void* v_cache
                   const int32_t* indices, const int32_t* counts, const float* sinks, int32_t batch, int32_t T,
                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_len, int32_t k,
                   int32_t recent, float scale, swa_dtype dtype, void* out, float* lse, void* stream,
-                  const char* name) {
+                  const char* name, bool fp8 = false, float k_scale = 1.f, float v_scale = 1.f) {
   int rc = check_dtype((int)dtype);
   if (rc) return rc;
   if ((rc = check_heads(num_q_heads, num_kv_heads, head_dim))) return rc;
+  if (fp8 && !(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f))
+    return fail(SWA_ERR_SHAPE, "%s: k_scale and v_scale must be finite and > 0", name);
   if (batch < 0 || max_len < 1) return fail(SWA_ERR_SHAPE, "%s: batch >= 0 and max_len >= 1 are required", name);
   if (T < 1 || T > max_len)
     return fail(SWA_ERR_SHAPE, "%s: T must satisfy 1 <= T <= max_len (got T=%d, max_len=%d)", name, T, max_len);
@@ -527,6 +529,7 @@ static int sparse_common(const void* q, const void* k_cache, const void* v_cache
   a.counts = counts; a.sinks = sinks; a.out = out; a.lse = lse;
   a.batch = batch; a.t_new = T; a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim; a.max_len = max_len; a.k = k; a.recent = recent; a.scale = resolve_scale(scale, head_dim);
+  a.kv_fp8 = fp8; a.k_scale = fp8 ? k_scale : 1.f; a.v_scale = fp8 ? v_scale : 1.f;
   return hip_status(swa::launch_sparse_decode(a, dtype == SWA_DTYPE_BF16, static_cast<hipStream_t>(stream)), name);
 }
 
@@ -537,6 +540,16 @@ int swa_sparse_decode(const void* q, const void* k_cache, const void* v_cache, c
                       void* stream) {
   return sparse_common(q, k_cache, v_cache, lengths, indices, counts, sinks, batch, 1, num_q_heads, num_kv_heads,
                        head_dim, max_len, k, recent, scale, dtype, out, lse, stream, "swa_sparse_decode");
+}
+
+int swa_sparse_decode_fp8kv(const void* q, const uint8_t* k_cache, const uint8_t* v_cache, float k_scale,
+                            float v_scale, const int32_t* lengths, const int32_t* indices, const int32_t* counts,
+                            const float* sinks, int32_t batch, int32_t T, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t max_len, int32_t k, int32_t recent,
+                            float scale, swa_dtype dtype, void* out, float* lse, void* stream) {
+  return sparse_common(q, k_cache, v_cache, lengths, indices, counts, sinks, batch, T, num_q_heads, num_kv_heads,
+                       head_dim, max_len, k, recent, scale, dtype, out, lse, stream, "swa_sparse_decode_fp8kv", true,
+                       k_scale, v_scale);
 }
 
 int swa_sparse_decode_mtp(const void* q, const void* k_cache, const void* v_cache, const int32_t* lengths,

@@ -146,6 +146,8 @@ struct SparseArgs {
   int32_t k;
   int32_t recent;
   float scale;
+  bool kv_fp8 = false;       // caches hold E4M3 codes; values = code value x k_scale / v_scale
+  float k_scale = 1.f, v_scale = 1.f;
 };
 
 // Arguments of the backward (gradients of O).  Pointers are device pointers.

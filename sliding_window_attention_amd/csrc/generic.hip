@@ -120,10 +120,12 @@ struct DecodeKeys {
 
 // Keys of one sparse-decode row: list entry m < cnt is the selected position sel[m]
 // (clamped into the sequence), then the row's recent window end - nrec .. end - 1.
-template <typename T, int D>
+template <typename T, int D, bool FP8>
 struct SparseKeys {
-  const T* kc;  // this (sequence, kv head)'s cache rows: [Lmax, D]
-  const T* vc;
+  using C = typename std::conditional<FP8, uint8_t, T>::type;  // FP8: E4M3 codes
+  const C* kc;  // this (sequence, kv head)'s cache rows: [Lmax, D]
+  const C* vc;
+  float k_scale, v_scale;
   const int32_t* sel;
   int cnt;   // selected positions seen by the row
   int L;     // the sequence's length (selected positions are clamped into it)
@@ -136,8 +138,20 @@ struct SparseKeys {
     }
     return end - nrec + (m - cnt);
   }
-  __device__ void load_key(int m, int d, float* dst) const { Elem<T>::load16(kc + (size_t)pos(m) * D + d, dst); }
-  __device__ float load_val(int m, int e) const { return Elem<T>::load1(vc + (size_t)pos(m) * D + e); }
+  __device__ void load_key(int m, int d, float* dst) const {
+    const C* row = kc + (size_t)pos(m) * D + d;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int e = 0; e < Elem<T>::kVec; ++e) dst[e] = e4m3_to_f32(row[e]) * k_scale;
+    } else {
+      Elem<T>::load16(row, dst);
+    }
+  }
+  __device__ float load_val(int m, int e) const {
+    const C* p = vc + (size_t)pos(m) * D + e;
+    if constexpr (FP8) return e4m3_to_f32(*p) * v_scale;
+    else return Elem<T>::load1(p);
+  }
 };
 
 // One wavefront computes one row against keys jlo..jhi (inclusive, jlo <= jhi).
@@ -261,7 +275,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void generic_decode_kernel(D
                    a.lse ? a.lse + row : nullptr, rope, pos0 + t, a.rope_log2_base);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool FP8>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void generic_sparse_kernel(SparseArgs a) {
   // row = (sequence b, query token t, head h); token t sits at position L - T + t and sees
   // the selected positions below its own window and the window itself
@@ -277,9 +291,12 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void generic_sparse_kernel(S
   L = L < Tn ? Tn : (L > a.max_len ? a.max_len : L);
   int cnt = a.counts[b * hkv + kvh];
   cnt = cnt < 0 ? 0 : (cnt > a.k ? a.k : cnt);
-  SparseKeys<T, D> keys;
-  keys.kc = static_cast<const T*>(a.k_cache) + ((size_t)b * hkv + kvh) * a.max_len * D;
-  keys.vc = static_cast<const T*>(a.v_cache) + ((size_t)b * hkv + kvh) * a.max_len * D;
+  using Keys = SparseKeys<T, D, FP8>;
+  Keys keys;
+  keys.kc = static_cast<const typename Keys::C*>(a.k_cache) + ((size_t)b * hkv + kvh) * a.max_len * D;
+  keys.vc = static_cast<const typename Keys::C*>(a.v_cache) + ((size_t)b * hkv + kvh) * a.max_len * D;
+  keys.k_scale = a.k_scale;
+  keys.v_scale = a.v_scale;
   keys.sel = a.indices + ((size_t)b * hkv + kvh) * a.k;
   keys.L = L;
   const int p = L - Tn + t;
@@ -300,7 +317,11 @@ hipError_t launch_sparse_t(const SparseArgs& a, hipStream_t s) {
   const long blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((generic_sparse_kernel<T, D>), dim3((unsigned)blocks), dim3(kRowsPerBlock * kWave), 0, s, a);
+  if (a.kv_fp8)
+    hipLaunchKernelGGL((generic_sparse_kernel<T, D, true>), dim3((unsigned)blocks), dim3(kRowsPerBlock * kWave), 0, s, a);
+  else
+    hipLaunchKernelGGL((generic_sparse_kernel<T, D, false>), dim3((unsigned)blocks), dim3(kRowsPerBlock * kWave), 0,
+                       s, a);
   return hipGetLastError();
 }
 

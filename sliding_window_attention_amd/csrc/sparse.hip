@@ -21,6 +21,8 @@
 //    merged exactly through LDS, with the sink in the denominator.  MTP verify (T = 2):
 //    the second token's heads take the query columns the single token leaves empty, and
 //    each column masks the keys its token does not see.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "mfma_tile.h"
@@ -379,7 +381,10 @@ struct SparseSmem {
 // the selected positions below its own recent window and the window
 // max(0, p_t - recent + 1) .. p_t; the staged list holds the selection and the union of
 // the T windows, and each column masks the rest.
-template <int T>
+// FP8: the caches hold E4M3 codes, gathered 8 bytes per operand and kept as codes until
+// they are used (so the next chunk's loads are never waited for early); the K scale joins
+// the logit multiplier and the V scale the output's 1 / z.
+template <int T, bool FP8>
 __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs a) {
   __shared__ __attribute__((aligned(16))) SparseSmem sm;
   const int noct = a.num_q_heads / kHG;
@@ -439,9 +444,21 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
     return pos >= wlo && pos <= pq;
   };
 
-  const bf16* kc = static_cast<const bf16*>(a.k_cache) + ((size_t)b * hkv + kvh) * a.max_len * D;
-  const bf16* vc = static_cast<const bf16*>(a.v_cache) + ((size_t)b * hkv + kvh) * a.max_len * D;
-  const float c = a.scale * kLog2e;
+  using CacheT = typename std::conditional<FP8, uint8_t, bf16>::type;
+  using Raw = typename std::conditional<FP8, u32x2, bf16x8>::type;  // one operand as gathered
+  const CacheT* kc = static_cast<const CacheT*>(a.k_cache) + ((size_t)b * hkv + kvh) * a.max_len * D;
+  const CacheT* vc = static_cast<const CacheT*>(a.v_cache) + ((size_t)b * hkv + kvh) * a.max_len * D;
+  auto op = [](Raw r) -> bf16x8 {
+    if constexpr (FP8) return e4m3x8_to_bf16x8(r);
+    else return r;
+  };
+  auto gather = [](const CacheT* p) -> Raw {
+    // each selected row is gathered once per step and not again until the layer's next
+    // step: non-temporal loads, as for the dense decode's ring (measured faster for bf16)
+    if constexpr (FP8) return *reinterpret_cast<const u32x2*>(p);
+    else return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+  };
+  const float c = a.scale * kLog2e * (FP8 ? a.k_scale : 1.f);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   bf16x8 qop[4];
 #pragma unroll
@@ -451,22 +468,19 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
   // V rows 8g + e (head-dim 8i .. 8i+7); keys past the list read the last key (their
   // weight is zero)
   const int nchunks = (M + 31) >> 5;
-  auto load_chunk = [&](int ch, bf16x8 (&kf)[2][4], bf16x8 (&vr)[8]) {
+  auto load_chunk = [&](int ch, Raw (&kf)[2][4], Raw (&vr)[8]) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int m = 32 * ch + pair_row(i, s);
       const int j = sm.keys[m < M ? m : M - 1];
-      // each selected row is gathered once per step and not again until the layer's next step: non-temporal
-      // loads, as for the dense decode's ring (measured faster)
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-        kf[s][cc] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc + (size_t)j * D + 32 * cc + 8 * g)));
+      for (int cc = 0; cc < 4; ++cc) kf[s][cc] = gather(kc + (size_t)j * D + 32 * cc + 8 * g);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int m = 32 * ch + 8 * g + e;
       const int j = sm.keys[m < M ? m : M - 1];
-      vr[e] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc + (size_t)j * D + 8 * i)));
+      vr[e] = gather(vc + (size_t)j * D + 8 * i);
     }
   };
 
@@ -474,7 +488,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
   f32x4 o[8];
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) o[bb] = zero4;
-  bf16x8 kf[2][4], vr[8], nkf[2][4], nvr[8];
+  Raw kf[2][4], vr[8], nkf[2][4], nvr[8];
   if (w < nchunks) load_chunk(w, kf, vr);
   for (int ch = w; ch < nchunks; ch += 4) {
     const bool more = ch + 4 < nchunks;
@@ -484,7 +498,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
     for (int s = 0; s < 2; ++s) {
       s2[s] = zero4;
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) s2[s] = mfma32(kf[s][cc], qop[cc], s2[s]);
+      for (int cc = 0; cc < 4; ++cc) s2[s] = mfma32(op(kf[s][cc]), qop[cc], s2[s]);
     }
     // lane (i, g) holds keys 8g + 4s + r of the chunk for column i
     float mx = -INFINITY;
@@ -514,10 +528,13 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
     lcol = lcol * alpha + quad_sum(ps);
     mcol = mnew;
     const bf16x8 pp = pack_pair(s2[0], s2[1]);
+    bf16x8 vb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vb[e] = op(vr[e]);
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb) {
       o[bb] *= alpha;
-      o[bb] = mfma32(column8(vr, bb), pp, o[bb]);
+      o[bb] = mfma32(column8(vb, bb), pp, o[bb]);
     }
     if (more) {
 #pragma unroll
@@ -558,7 +575,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
     sc[v] = fast_exp2(sm.m[v][i] - mt);  // 0 for a wavefront that had no chunk
     z += sm.l[v][i] * sc[v];
   }
-  const float inv = 1.f / z;
+  const float inv = (FP8 ? a.v_scale : 1.f) / z;
   bf16* out = static_cast<bf16*>(a.out) + orow * D;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -605,8 +622,14 @@ hipError_t launch_sparse_decode(const SparseArgs& a, bool bf16_io, hipStream_t s
   const long blocks = (long)a.batch * (a.num_q_heads / kHG);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  if (a.t_new == 2) hipLaunchKernelGGL(sparse_decode_kernel<2>, dim3((unsigned)blocks), dim3(kSpThreads), 0, s, a);
-  else hipLaunchKernelGGL(sparse_decode_kernel<1>, dim3((unsigned)blocks), dim3(kSpThreads), 0, s, a);
+  const dim3 grid((unsigned)blocks), block(kSpThreads);
+  if (a.kv_fp8) {
+    if (a.t_new == 2) hipLaunchKernelGGL((sparse_decode_kernel<2, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((sparse_decode_kernel<1, true>), grid, block, 0, s, a);
+  } else {
+    if (a.t_new == 2) hipLaunchKernelGGL((sparse_decode_kernel<2, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((sparse_decode_kernel<1, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

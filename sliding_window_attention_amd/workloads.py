@@ -174,6 +174,19 @@ def make_sparse(batch, num_q_heads, num_kv_heads, head_dim, max_len, dtype, seed
             "sinks": sinks if with_sinks else None, "scores": scores}
 
 
+def make_sparse_fp8(batch, num_q_heads, num_kv_heads, head_dim, max_len, dtype, seed, min_len=1,
+                    with_sinks=True):
+    """make_sparse with the caches as E4M3 codes [B, Hkv, Lmax, D] uint8 and per-tensor
+    scales k_scale = 1/32, v_scale = 1/64 (values of about N(0, 1))."""
+    x = make_sparse(batch, num_q_heads, num_kv_heads, head_dim, max_len, dtype, seed, min_len, with_sinks)
+    gen = torch.Generator().manual_seed(int(seed) + 17)
+    shape = tuple(x["k_cache"].shape)
+    x["k_cache"] = e4m3_codes(shape, gen)
+    x["v_cache"] = e4m3_codes(shape, gen)
+    x["k_scale"], x["v_scale"] = 1.0 / 32, 1.0 / 64
+    return x
+
+
 def make_sparse_device(batch, num_q_heads, num_kv_heads, head_dim, max_len, seed, device, min_len=1):
     """make_sparse for caches too large to draw on the host (bf16, no sinks): q, caches
     and scores drawn on `device` by a seeded device generator, lengths on the host."""
@@ -189,21 +202,25 @@ def make_sparse_device(batch, num_q_heads, num_kv_heads, head_dim, max_len, seed
             "sinks": None, "scores": scores}
 
 
-def sparse_bytes(lengths, num_q_heads, num_kv_heads, head_dim, topk, recent, elem_bytes):
+def sparse_bytes(lengths, num_q_heads, num_kv_heads, head_dim, topk, recent, elem_bytes, kv_elem_bytes=None):
     """Sparse decode: per (sequence, KV head) the selected and recent K and V rows read
     once, the query read and the output written, the selection (indices, counts) and
-    the LSE."""
+    the LSE.  kv_elem_bytes: bytes per cache element (1 for E4M3 codes; default
+    elem_bytes)."""
     keys = sum(min(topk, max(0, int(n) - recent)) + min(recent, int(n)) for n in lengths)
     b = len(lengths)
-    return (2 * keys * num_kv_heads * head_dim * elem_bytes + 2 * b * num_q_heads * head_dim * elem_bytes
+    kvb = elem_bytes if kv_elem_bytes is None else kv_elem_bytes
+    return (2 * keys * num_kv_heads * head_dim * kvb + 2 * b * num_q_heads * head_dim * elem_bytes
             + b * num_kv_heads * (topk + 1) * 4 + 4 * b * num_q_heads)
 
 
-def sparse_mtp_work(lengths, indices, counts, num_q_heads, num_kv_heads, head_dim, recent, t_new, elem_bytes):
+def sparse_mtp_work(lengths, indices, counts, num_q_heads, num_kv_heads, head_dim, recent, t_new, elem_bytes,
+                    kv_elem_bytes=None):
     """(flops, bytes) of the sparse MTP verify of the newest t_new tokens: 4 D FLOPs per
     (query head, visible key) -- query t sees the selected positions below its window and
     the window -- and per (sequence, KV head) the selection plus the windows' union read
-    once as K and V rows, the queries read, the outputs and LSE written, the selection."""
+    once as K and V rows, the queries read, the outputs and LSE written, the selection.
+    kv_elem_bytes: bytes per cache element (1 for E4M3 codes; default elem_bytes)."""
     import numpy as np
 
     idx = np.asarray(indices)
@@ -220,7 +237,8 @@ def sparse_mtp_work(lengths, indices, counts, num_q_heads, num_kv_heads, head_di
                 lo = max(0, p - recent + 1)
                 visible += grp * (int((sel < lo).sum()) + p - lo + 1)
     bsz = len(lengths)
-    by = (2 * rows * head_dim * elem_bytes + 2 * bsz * t_new * num_q_heads * head_dim * elem_bytes
+    kvb = elem_bytes if kv_elem_bytes is None else kv_elem_bytes
+    by = (2 * rows * head_dim * kvb + 2 * bsz * t_new * num_q_heads * head_dim * elem_bytes
           + 4 * int(cnt.size) + 4 * int(cnt.sum()) + 4 * bsz * t_new * num_q_heads)
     return 4 * head_dim * visible, by
 
@@ -280,10 +298,12 @@ def make_decode_device(batch, t_new, num_q_heads, num_kv_heads, head_dim, window
 def e4m3_codes(shape, gen, exp_center=10.0, exp_spread=2.0):
     """One-byte E4M3 codes shaped like a quantised N(0, s) tensor: random sign,
     exponent field ~ round(N(exp_center, exp_spread)) clipped to 1..14 (normal
-    numbers, never the NaN pattern), uniform mantissa.  uint8, on the host."""
-    e = torch.clamp(torch.round(exp_center + exp_spread * torch.randn(shape, generator=gen)), 1, 14)
-    m = torch.randint(0, 8, shape, generator=gen)
-    sgn = torch.randint(0, 2, shape, generator=gen)
+    numbers, never the NaN pattern), uniform mantissa.  uint8, on the generator's
+    device."""
+    dev = gen.device
+    e = torch.clamp(torch.round(exp_center + exp_spread * torch.randn(shape, generator=gen, device=dev)), 1, 14)
+    m = torch.randint(0, 8, shape, generator=gen, device=dev)
+    sgn = torch.randint(0, 2, shape, generator=gen, device=dev)
     return ((sgn << 7) | (e.to(torch.int64) << 3) | m).to(torch.uint8)
 
 

@@ -29,6 +29,7 @@ def test_header_declares_the_entry_points():
                           "swa_sink_prefill_backward_workspace", "swa_sink_prefill_backward_noalloc",
                           "swa_rope", "swa_sink_decode_rope",
                           "swa_ring_append_rope", "swa_topk_select", "swa_sparse_decode", "swa_sparse_decode_mtp",
+                          "swa_sparse_decode_fp8kv",
                           "swa_sink_decode_rope_fp8kv", "swa_ring_append_fp8kv", "swa_sink_decode_rope_commit", "swa_sink_decode_rope_commit_fp8kv",
                           "swa_last_error", "swa_abi_version"}
 
@@ -593,6 +594,22 @@ def test_sparse_decode_mtp_rejects_bad_arguments():
     assert lib.swa_sparse_decode_mtp(*args) == E_SHAPE and "k + recent + T - 1" in _last()
     args[14], args[7] = 128, 0  # empty batch: sizes still validated, nothing launched
     assert lib.swa_sparse_decode_mtp(*args) == OK
+
+
+def test_sparse_decode_fp8kv_rejects_bad_arguments():
+    lib = swa.library()
+    # every call below fails validation (or has an empty batch): nothing is launched
+    args = [FAKE, FAKE, FAKE, 0.0, 0.5, FAKE, FAKE, FAKE, NULL, 2, 1, 8, 1, 128, 4096, 1024, 128, 0.0, 1, FAKE,
+            NULL, NULL]
+    assert lib.swa_sparse_decode_fp8kv(*args) == E_SHAPE and "k_scale" in _last()
+    args[3], args[4] = 0.5, float("inf")
+    assert lib.swa_sparse_decode_fp8kv(*args) == E_SHAPE and "finite" in _last()
+    args[4], args[10] = 0.5, 0
+    assert lib.swa_sparse_decode_fp8kv(*args) == E_SHAPE and "T must" in _last()
+    args[10], args[16] = 2, 0
+    assert lib.swa_sparse_decode_fp8kv(*args) == E_SHAPE and "recent" in _last()
+    args[16], args[9] = 128, 0
+    assert lib.swa_sparse_decode_fp8kv(*args) == OK
 
 
 def test_sparse_decode_empty_batch_and_optional_sinks():

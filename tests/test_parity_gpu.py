@@ -1722,6 +1722,74 @@ def test_sparse_mtp_limits_match_dense_kernels():
             assert err <= 2e-2 and lerr <= 1e-3, (k, bb, err, lerr)
 
 
+@pytest.mark.parametrize("case", [(8, 32, 4, 128, 6000, "bf16", 1024, 128, True, 1),
+                                  (6, 16, 2, 128, 3000, "bf16", 300, 37, False, 2),
+                                  (5, 8, 1, 128, 900, "bf16", 1024, 128, True, 2),
+                                  (4, 32, 4, 128, 2500, "bf16", 2000, 128, True, 3),
+                                  (4, 8, 2, 64, 2000, "bf16", 200, 64, True, 1),
+                                  (3, 4, 1, 128, 1500, "f32", 256, 128, True, 2)],
+                         ids=lambda c: f"B{c[0]}-{c[1]}/{c[2]}-D{c[3]}-L{c[4]}-{c[5]}-k{c[6]}-r{c[7]}-"
+                                       f"{'sink' if c[8] else 'nosink'}-T{c[9]}")
+def test_sparse_fp8_against_oracle(case):
+    """The sparse decode and MTP verify over an FP8 cache (E4M3 codes, per-tensor scales):
+    the matrix-core kernel (bf16, head_dim 128, T <= 2) and the vector kernel, the selection
+    reaching into the older drafts' windows, a sequence shorter than the window and one of
+    exactly T tokens."""
+    b, hq, hkv, d, lmax, dt, k, recent, sink, t_new = case
+    _say(f"sparse FP8 {case}")
+    x = wl.make_sparse_fp8(b, hq, hkv, d, lmax, dt, seed=6500 + lmax + k, with_sinks=sink)
+    gen = torch.Generator().manual_seed(6501 + lmax)
+    x["q"] = torch.randn(b, t_new, hq, d, generator=gen).to(x["q"].dtype)
+    x["lengths"][0] = lmax
+    x["lengths"][1] = min(lmax, recent // 2 + 1)
+    x["lengths"][2] = t_new
+    x["scores"][0, :, lmax - recent - 1] = 1e4
+    idx, cnt = _topk_gpu(x["scores"], x["lengths"], k, recent)
+    ridx, rcnt = orc.topk_select(x["scores"], x["lengths"].numpy(), k=k, recent=recent)
+    assert np.array_equal(idx, ridx) and np.array_equal(cnt, rcnt)
+    g = {k_: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k_, v in x.items()}
+    o, lse = swa.swa_sparse_decode_fp8kv(g["q"], g["k_cache"], g["v_cache"], x["k_scale"], x["v_scale"],
+                                         g["lengths"], torch.as_tensor(idx, dtype=torch.int32).to(DEV),
+                                         torch.as_tensor(cnt, dtype=torch.int32).to(DEV), g["sinks"],
+                                         recent=recent)
+    torch.cuda.synchronize()
+    o_ref, l_ref = orc.sparse_decode_mtp_fp8kv(x["q"], x["k_cache"].numpy(), x["v_cache"].numpy(), x["k_scale"],
+                                               x["v_scale"], x["lengths"].numpy(), ridx, rcnt, x["sinks"],
+                                               recent=recent)
+    assert_close(x["q"].dtype, o, o_ref, lse, l_ref, f"sparse FP8 {case}")
+
+
+def test_sparse_fp8_every_finite_code():
+    """Every finite E4M3 code (both signs, zeros and subnormals included) appears in each
+    (sequence, kv head)'s recent window, which every query row reads, in the matrix-core
+    kernel, T = 2."""
+    _say("sparse FP8 every finite code")
+    b, hq, hkv, d, lmax, k, recent = 4, 32, 4, 128, 2000, 512, 128
+    x = wl.make_sparse_fp8(b, hq, hkv, d, lmax, "bf16", seed=6600, min_len=lmax)
+    finite = torch.tensor([c for c in range(256) if c & 0x7F != 0x7F], dtype=torch.uint8).repeat(64)
+    gen = torch.Generator().manual_seed(6601)
+    for key in ("k_cache", "v_cache"):
+        for bb in range(b):
+            for gg in range(hkv):
+                win = x[key][bb, gg, lmax - recent:].reshape(-1)
+                win[:finite.numel()] = finite[torch.randperm(finite.numel(), generator=gen)]
+                x[key][bb, gg, lmax - recent:] = win.view(recent, d)
+    x["q"] = torch.randn(b, 2, hq, d, generator=gen).to(torch.bfloat16)
+    idx, cnt = _topk_gpu(x["scores"], x["lengths"], k, recent)
+    ridx, rcnt = orc.topk_select(x["scores"], x["lengths"].numpy(), k=k, recent=recent)
+    assert np.array_equal(idx, ridx) and np.array_equal(cnt, rcnt)
+    g = {k_: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k_, v in x.items()}
+    o, lse = swa.swa_sparse_decode_fp8kv(g["q"], g["k_cache"], g["v_cache"], x["k_scale"], x["v_scale"],
+                                         g["lengths"], torch.as_tensor(idx, dtype=torch.int32).to(DEV),
+                                         torch.as_tensor(cnt, dtype=torch.int32).to(DEV), g["sinks"],
+                                         recent=recent)
+    torch.cuda.synchronize()
+    o_ref, l_ref = orc.sparse_decode_mtp_fp8kv(x["q"], x["k_cache"].numpy(), x["v_cache"].numpy(), x["k_scale"],
+                                               x["v_scale"], x["lengths"].numpy(), ridx, rcnt, x["sinks"],
+                                               recent=recent)
+    assert_close(torch.bfloat16, o, o_ref, lse, l_ref, "sparse FP8 every code")
+
+
 def test_sparse_full_size_workload():
     """The benchmarked workload (64 sequences of 16K-32K tokens, [64, 4, 32768, 128]
     caches drawn on the GPU): every selection index exactly, every output row against the
