@@ -20,6 +20,11 @@
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers, row-major and contiguous, owned by
  *    the caller.  The library allocates nothing and keeps no state across calls.
+ *  - The tensors read or written with 16-byte vector accesses (q, k, v, k_new, v_new,
+ *    the caches, prev_k, prev_v, out, dout, dq, dk, dv, the backward workspace and
+ *    swa_rope's x) must be 16-byte aligned, as every torch or hipMalloc allocation is;
+ *    a misaligned one is refused with SWA_ERR_UNSUPPORTED.  Index, length, score and
+ *    fp32 per-row arrays need only their element alignment.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
  *    call only enqueues work on `stream` and returns without synchronising.
  *  - Arguments are validated on the host before anything is launched.  On error

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <initializer_list>
 
 #include "../../include/swasink.h"
 #include "kernels.h"
@@ -79,6 +80,14 @@ int check_heads(int32_t hq, int32_t hkv, int32_t d) {
   return SWA_OK;
 }
 
+// The kernels read and write the tensors with 16-byte vector accesses.
+int check_aligned(const char* name, const char* what, std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) & 15u)
+      return fail(SWA_ERR_UNSUPPORTED, "%s: %s must be 16-byte aligned", name, what);
+  return SWA_OK;
+}
+
 float resolve_scale(float scale, int32_t d) {
   return (scale > 0.f && isfinite(scale)) ? scale : 1.0f / sqrtf((float)d);
 }
@@ -104,6 +113,7 @@ int prefill_common(const void* q, const void* k, const void* v, const float* sin
   if (!q || !k || !v || !cu_seqlens || !out || (need_sinks && !sinks))
     return fail(SWA_ERR_NULL, "%s: q, k, v, %scu_seqlens and out must be non-NULL", name,
                 need_sinks ? "sinks, " : "");
+  if ((rc = check_aligned(name, "q, k, v and out", {q, k, v, out}))) return rc;
 
   swa::PrefillArgs a;
   a.q = q; a.k = k; a.v = v;
@@ -185,7 +195,10 @@ int decode_common(const void* q, const void* k_new, const void* v_new, const voi
       return fail(SWA_ERR_NULL, "%s: prev_positions must be non-NULL", name);
     if (commit->ring_head_out == ring_head)
       return fail(SWA_ERR_SHAPE, "%s: ring_head_out must not be ring_head", name);
+    if ((rc = check_aligned(name, "prev_k and prev_v", {commit->prev_k, commit->prev_v}))) return rc;
   }
+  if ((rc = check_aligned(name, "q, k_new, v_new, k_cache, v_cache and out", {q, k_new, v_new, k_cache, v_cache, out})))
+    return rc;
 
   swa::DecodeArgs a;
   a.q = q; a.k_new = k_new; a.v_new = v_new;
@@ -260,6 +273,7 @@ int ring_append_common(const void* k_new, const void* v_new, const int32_t* n_ac
     return fail(SWA_ERR_NULL, "%s: k_new, v_new, n_accept, k_cache, v_cache and ring_head must be non-NULL",
                 name);
   if (rope_base > 0.f && !positions) return fail(SWA_ERR_NULL, "%s: positions must be non-NULL", name);
+  if ((rc = check_aligned(name, "k_new, v_new, k_cache and v_cache", {k_new, v_new, k_cache, v_cache}))) return rc;
   swa::AppendArgs a;
   a.k_new = k_new; a.v_new = v_new; a.n_accept = n_accept;
   a.rope_pos = rope_base > 0.f ? positions : nullptr;
@@ -316,6 +330,9 @@ int backward_common(const void* q, const void* k, const void* v, const float* si
   if (total_tokens > 0 && (!q || !k || !v || !cu_seqlens || !out || !lse || !dout || !dq || !dk || !dv))
     return fail(SWA_ERR_NULL, "%s: q, k, v, cu_seqlens, out, lse, dout, dq, dk and dv must be non-NULL",
                 name);
+  if ((rc = check_aligned(name, "q, k, v, out, dout, dq, dk, dv and workspace",
+                          {q, k, v, out, dout, dq, dk, dv, library_scratch ? nullptr : workspace})))
+    return rc;
   const int64_t need = backward_workspace_bytes(total_tokens, num_q_heads);
   if (library_scratch) {
     if (need > kNoAllocScratchBytes)
@@ -460,6 +477,7 @@ int swa_rope(void* x, const int32_t* positions, int32_t rows, int32_t heads, int
   if ((long long)rows * heads * head_dim > (1LL << 40)) return fail(SWA_ERR_UNSUPPORTED, "%s: problem too large", name);
   if (rows == 0 || rope_base == 0.f) return ok();
   if (!x || !positions) return fail(SWA_ERR_NULL, "%s: x and positions must be non-NULL", name);
+  if ((rc = check_aligned(name, "x", {x}))) return rc;
   swa::RopeArgs a;
   a.x = x; a.pos = positions; a.rows = rows; a.heads = heads; a.head_dim = head_dim;
   a.log2_base = log2((double)rope_base);
@@ -524,6 +542,7 @@ static int sparse_common(const void* q, const void* k_cache, const void* v_cache
   if (batch == 0) return ok();
   if (!q || !k_cache || !v_cache || !lengths || !counts || !out || (k > 0 && !indices))
     return fail(SWA_ERR_NULL, "%s: q, k_cache, v_cache, lengths, indices, counts and out must be non-NULL", name);
+  if ((rc = check_aligned(name, "q, k_cache, v_cache and out", {q, k_cache, v_cache, out}))) return rc;
   swa::SparseArgs a;
   a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.lengths = lengths; a.indices = indices;
   a.counts = counts; a.sinks = sinks; a.out = out; a.lse = lse;

@@ -14,8 +14,9 @@
 //    every score above the threshold, and the lowest positions among those equal to
 //    it, so the result is exact and deterministic (no floating point decides a rank).
 //  * sparse_decode_kernel: one workgroup per (sequence, head octet); the key list
-//    (selected positions, then the recent window) is staged in LDS, and the four
-//    wavefronts take 32-key chunks in turn: K rows gathered straight into MFMA A
+//    (selected positions, then the recent window) is staged in LDS, and the wavefronts
+//    (4, or 8 for an FP8 cache on a grid of at most one workgroup per CU) take 32-key
+//    chunks in turn: K rows gathered straight into MFMA A
 //    operands, S^T = K Q^T for the octet's 8 heads, an online softmax per head, V rows
 //    transposed in registers for O^T += V^T P^T.  The wavefronts' partial results are
 //    merged exactly through LDS, with the sink in the denominator.  MTP verify (T = 2):
@@ -363,17 +364,17 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
 // sparse decode (bf16, head_dim 128, heads per KV head a multiple of 8)
 // ---------------------------------------------------------------------------
 
-constexpr int kSpThreads = 256;
 constexpr int kHG = 8;                 // query heads per workgroup
 constexpr int kMaxList = 8192;         // selected + recent keys staged in LDS
 constexpr int kQPitch = 272;           // staged bf16 query row, padded
 constexpr int kOPitch = D + 4;         // fp32 partial row, padded
 
+template <int NW>
 struct SparseSmem {
   int32_t keys[kMaxList];
   char q[16][kQPitch];                 // 8 query heads; columns 8..15 zero
-  float m[4][16], l[4][16];
-  float o[3][16][kOPitch];             // partial O of wavefronts 1..3
+  float m[NW][16], l[NW][16];
+  float o[NW - 1][16][kOPitch];        // partial O of wavefronts 1 .. NW-1
 };
 
 // T queries per sequence (1, or 2 for an MTP verify): the 16 query columns are token
@@ -384,9 +385,13 @@ struct SparseSmem {
 // FP8: the caches hold E4M3 codes, gathered 8 bytes per operand and kept as codes until
 // they are used (so the next chunk's loads are never waited for early); the K scale joins
 // the logit multiplier and the V scale the output's 1 / z.
-template <int T, bool FP8>
-__global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs a) {
-  __shared__ __attribute__((aligned(16))) SparseSmem sm;
+// NW wavefronts take the chunks in turn, each with one chunk in use and the next in
+// flight.  With one workgroup per CU, the FP8 gather (one 128-byte row per key and
+// operand) runs 8 wavefronts to keep twice the rows in flight; bf16 rows move twice the
+// bytes per load and measured no faster with 8.
+template <int T, bool FP8, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void sparse_decode_kernel(SparseArgs a) {
+  __shared__ __attribute__((aligned(16))) SparseSmem<NW> sm;
   const int noct = a.num_q_heads / kHG;
   const int b = blockIdx.x / noct;
   const int oct = blockIdx.x - b * noct;
@@ -408,7 +413,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
 
   // ---- stage the key list and the 8 query rows ----
   const int32_t* sel = a.indices + ((size_t)b * hkv + kvh) * a.k;
-  for (int m = tid; m < M; m += kSpThreads) {
+  for (int m = tid; m < M; m += NW * 64) {
     int j;
     if (m < cnt) {
       j = sel[m];
@@ -418,7 +423,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
     }
     sm.keys[m] = j;
   }
-  {
+  if (tid < 256) {
     const int r = tid >> 4, u = tid & 15;  // 16 rows x 16 units: token r >> 3, head r & 7
     u32x4 x = {0, 0, 0, 0};
     if ((r >> 3) < T)
@@ -460,11 +465,18 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
   };
   const float c = a.scale * kLog2e * (FP8 ? a.k_scale : 1.f);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  // K operand of chunk cc: the 8 head-dim elements of unit kunit(cc) (8 elements per
+  // unit): unit 4 cc + g, the chunk's 32 dims in order; for FP8 codes unit
+  // 2 g + 8 (cc >> 1) + (cc & 1), so that chunks 2h and 2h + 1 of a lane are adjacent
+  // codes and one 16-byte load brings both, the four lanes of a row covering 64
+  // contiguous bytes.  The query operands take the same units; the contraction runs over
+  // all 128 dims either way.
+  auto kunit = [&](int cc) { return FP8 ? 2 * g + 8 * (cc >> 1) + (cc & 1) : 4 * cc + g; };
   bf16x8 qop[4];
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) qop[cc] = *reinterpret_cast<const bf16x8*>(&sm.q[i][16 * (4 * cc + g)]);
+  for (int cc = 0; cc < 4; ++cc) qop[cc] = *reinterpret_cast<const bf16x8*>(&sm.q[i][16 * kunit(cc)]);
 
-  // operands of one 32-key chunk: K rows pair_row(i, s) (A operand, head-dim 32cc + 8g),
+  // operands of one 32-key chunk: K rows pair_row(i, s) (A operand, head-dim unit kunit(cc)),
   // V rows 8g + e (head-dim 8i .. 8i+7); keys past the list read the last key (their
   // weight is zero)
   const int nchunks = (M + 31) >> 5;
@@ -473,8 +485,17 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
     for (int s = 0; s < 2; ++s) {
       const int m = 32 * ch + pair_row(i, s);
       const int j = sm.keys[m < M ? m : M - 1];
+      if constexpr (FP8) {
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) kf[s][cc] = gather(kc + (size_t)j * D + 32 * cc + 8 * g);
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 c16 = *reinterpret_cast<const u32x4*>(kc + (size_t)j * D + 64 * h + 16 * g);
+          kf[s][2 * h] = (u32x2){c16[0], c16[1]};
+          kf[s][2 * h + 1] = (u32x2){c16[2], c16[3]};
+        }
+      } else {
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) kf[s][cc] = gather(kc + (size_t)j * D + 32 * cc + 8 * g);
+      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -490,9 +511,9 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
   for (int bb = 0; bb < 8; ++bb) o[bb] = zero4;
   Raw kf[2][4], vr[8], nkf[2][4], nvr[8];
   if (w < nchunks) load_chunk(w, kf, vr);
-  for (int ch = w; ch < nchunks; ch += 4) {
-    const bool more = ch + 4 < nchunks;
-    if (more) load_chunk(ch + 4, nkf, nvr);
+  for (int ch = w; ch < nchunks; ch += NW) {
+    const bool more = ch + NW < nchunks;
+    if (more) load_chunk(ch + NW, nkf, nvr);
     f32x4 s2[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -546,7 +567,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
     }
   }
 
-  // ---- exact merge of the four wavefronts' partials (lane (i, g): column i,
+  // ---- exact merge of the wavefronts' partials (lane (i, g): column i,
   // head-dim 32g + 8r + bb in register r of block bb) ----
   if (g == 0) {
     sm.m[w][i] = mcol;
@@ -567,11 +588,11 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
   const float sink2 = a.sinks ? as_const(a.sinks)[h] * kLog2e : -INFINITY;
   float mt = sink2;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) mt = fmaxf(mt, sm.m[v][i]);
+  for (int v = 0; v < NW; ++v) mt = fmaxf(mt, sm.m[v][i]);
   float z = a.sinks ? fast_exp2(sink2 - mt) : 0.f;
-  float sc[4];
+  float sc[NW];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
+  for (int v = 0; v < NW; ++v) {
     sc[v] = fast_exp2(sm.m[v][i] - mt);  // 0 for a wavefront that had no chunk
     z += sm.l[v][i] * sc[v];
   }
@@ -583,7 +604,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void sparse_decode_kernel(SparseArgs
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb) acc[bb] = o[bb][r] * sc[0];
 #pragma unroll
-    for (int v = 1; v < 4; ++v) {
+    for (int v = 1; v < NW; ++v) {
       const float* row = &sm.o[v - 1][i][32 * g + 8 * r];
       const f32x4 lo = *reinterpret_cast<const f32x4*>(row);
       const f32x4 hi = *reinterpret_cast<const f32x4*>(row + 4);
@@ -617,20 +638,26 @@ bool sparse_mfma_supported(const SparseArgs& a, bool bf16_io) {
          (long)a.k + a.recent + a.t_new - 1 <= kMaxList;
 }
 
+constexpr long kSparseWideGrid = 256;  // workgroups up to which each has a CU of its own
+
+template <bool FP8, int NW>
+hipError_t launch_sparse_nw(const SparseArgs& a, unsigned blocks, hipStream_t s) {
+  const dim3 grid(blocks), block(NW * 64);
+  if (a.t_new == 2) hipLaunchKernelGGL((sparse_decode_kernel<2, FP8, NW>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((sparse_decode_kernel<1, FP8, NW>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_sparse_decode(const SparseArgs& a, bool bf16_io, hipStream_t s) {
   if (!sparse_mfma_supported(a, bf16_io)) return launch_generic_sparse(a, bf16_io, s);
   const long blocks = (long)a.batch * (a.num_q_heads / kHG);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)blocks), block(kSpThreads);
-  if (a.kv_fp8) {
-    if (a.t_new == 2) hipLaunchKernelGGL((sparse_decode_kernel<2, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((sparse_decode_kernel<1, true>), grid, block, 0, s, a);
-  } else {
-    if (a.t_new == 2) hipLaunchKernelGGL((sparse_decode_kernel<2, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((sparse_decode_kernel<1, false>), grid, block, 0, s, a);
-  }
-  return hipGetLastError();
+  if (!a.kv_fp8) return launch_sparse_nw<false, 4>(a, (unsigned)blocks, s);
+  // FP8 with up to one workgroup per CU: 8 wavefronts each; beyond that 4, two
+  // workgroups sharing a CU
+  if (blocks <= kSparseWideGrid) return launch_sparse_nw<true, 8>(a, (unsigned)blocks, s);
+  return launch_sparse_nw<true, 4>(a, (unsigned)blocks, s);
 }
 
 }  // namespace swa

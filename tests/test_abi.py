@@ -615,3 +615,27 @@ def test_sparse_decode_fp8kv_rejects_bad_arguments():
 def test_sparse_decode_empty_batch_and_optional_sinks():
     assert _sparse(b=0, q=NULL, kc=NULL, vc=NULL, lens=NULL, idx=NULL, cnt=NULL, out=NULL) == OK
     assert _sparse(sinks=NULL, out=NULL) == E_NULL and "out" in _last()
+
+
+MIS = ctypes.c_void_p(0x1008)  # 8-byte aligned, not 16
+
+
+def _gpu_visible():
+    import torch
+
+    return torch.cuda.device_count() > 0
+
+
+@pytest.mark.parametrize("call", [
+    lambda: _prefill(k=MIS), lambda: _prefill(out=MIS), lambda: _decode(vc=MIS), lambda: _decode(kn=MIS),
+    lambda: _commit(pk=MIS), lambda: _commit(q=MIS), lambda: _prefill_fp8(v=MIS), lambda: _decode_fp8(out=MIS),
+    lambda: _backward(dq=MIS), lambda: _backward(ws=MIS), lambda: _rope(x=MIS), lambda: _append(kc=MIS),
+    lambda: _append_fp8(vn=MIS), lambda: _decode_rope_fp8(kc=MIS), lambda: _decode_rope(q=MIS),
+    lambda: _sparse(vc=MIS), lambda: _sparse(q=MIS),
+], ids=lambda f: "")
+def test_misaligned_tensor_pointers_are_refused(call):
+    # every argument but one pointer is valid: the alignment check is the last before a
+    # launch, so on a machine with a GPU a missing check would launch on fake pointers
+    if _gpu_visible():
+        pytest.skip("runs where no GPU is visible")
+    assert call() == E_UNSUP and "16-byte aligned" in _last()

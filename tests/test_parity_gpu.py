@@ -1612,7 +1612,8 @@ def _sparse_gpu(x, idx, cnt, recent):
                                   (5, 8, 1, 128, 900, "bf16", 1024, 128, True),
                                   (4, 8, 2, 64, 2000, "bf16", 200, 64, True),
                                   (3, 4, 1, 128, 1500, "f32", 256, 128, True),
-                                  (4, 32, 4, 128, 2500, "bf16", 2000, 128, False)],
+                                  (4, 32, 4, 128, 2500, "bf16", 2000, 128, False),
+                                  (70, 32, 4, 128, 800, "bf16", 300, 128, True)],  # > 256 workgroups
                          ids=lambda c: f"B{c[0]}-{c[1]}/{c[2]}-D{c[3]}-L{c[4]}-{c[5]}-k{c[6]}-r{c[7]}-{'sink' if c[8] else 'nosink'}")
 def test_sparse_decode_against_oracle(case):
     b, hq, hkv, d, lmax, dt, k, recent, sink = case
@@ -1659,7 +1660,8 @@ def test_sparse_decode_limits_match_dense_kernels():
                                   (5, 8, 1, 128, 900, "bf16", 1024, 128, True, 1),
                                   (4, 32, 4, 128, 2500, "bf16", 2000, 128, True, 3),
                                   (4, 8, 2, 64, 2000, "bf16", 200, 64, True, 2),
-                                  (3, 4, 1, 128, 1500, "f32", 256, 128, True, 2)],
+                                  (3, 4, 1, 128, 1500, "f32", 256, 128, True, 2),
+                                  (72, 32, 4, 128, 700, "bf16", 256, 64, True, 2)],  # > 256 workgroups
                          ids=lambda c: f"B{c[0]}-{c[1]}/{c[2]}-D{c[3]}-L{c[4]}-{c[5]}-k{c[6]}-r{c[7]}-"
                                        f"{'sink' if c[8] else 'nosink'}-T{c[9]}")
 def test_sparse_mtp_against_oracle(case):
@@ -1727,7 +1729,9 @@ def test_sparse_mtp_limits_match_dense_kernels():
                                   (5, 8, 1, 128, 900, "bf16", 1024, 128, True, 2),
                                   (4, 32, 4, 128, 2500, "bf16", 2000, 128, True, 3),
                                   (4, 8, 2, 64, 2000, "bf16", 200, 64, True, 1),
-                                  (3, 4, 1, 128, 1500, "f32", 256, 128, True, 2)],
+                                  (3, 4, 1, 128, 1500, "f32", 256, 128, True, 2),
+                                  (72, 32, 4, 128, 700, "bf16", 256, 64, True, 1),  # > 256 workgroups
+                                  (66, 32, 4, 128, 900, "bf16", 512, 128, False, 2)],
                          ids=lambda c: f"B{c[0]}-{c[1]}/{c[2]}-D{c[3]}-L{c[4]}-{c[5]}-k{c[6]}-r{c[7]}-"
                                        f"{'sink' if c[8] else 'nosink'}-T{c[9]}")
 def test_sparse_fp8_against_oracle(case):
