@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) where no GPU is visible, so that a plain
-    # `pytest` run on a CPU-only machine stays green; `-m gpu` on the GPU machine runs them.
+    # `pytest` run on a CPU-only machine stays green; `-m gpu` on an MI355X runs them.
     try:
         import torch
 
