@@ -5,8 +5,12 @@
 // workgroup per ring with 128 / 256 / 512 threads, a ring split over 2 / 4 / 8
 // workgroups, and one wavefront per ring streaming it in chunks; the one-workgroup and
 // split shapes also with the loads marked non-temporal (as the decode's bf16 ring loads
-// are).  32 input sets (2 GiB) are rotated so that no launch finds its data in the
-// 256 MB Infinity Cache.
+// are).  The FP8 ring's shape (16 KB of K codes + 16 KB of V codes per ring, 32 MiB in
+// all) is read by one 256-thread workgroup per ring, with 16-byte loads and with the V
+// codes as 8-byte loads (as the FP8 decode reads them); a launch that reads nothing and
+// writes the same 16 bytes per thread gives the floor of a 1024-workgroup launch.  32
+// input sets (2 GiB) are rotated so that no launch finds its data in the 256 MB
+// Infinity Cache.
 //
 //   hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops \
 //     -o /tmp/bench_stream_probe bench_stream_probe.hip
@@ -33,13 +37,13 @@ __device__ __forceinline__ uint4 load16(const uint4* p) {
   }
 }
 
-template <int THREADS, int SPLIT, bool NT = false>
+template <int THREADS, int SPLIT, bool NT = false, int UNITS = kUnits>
 __global__ __launch_bounds__(THREADS) void stream_k(const uint4* __restrict__ K, const uint4* __restrict__ V,
                                                      uint4* __restrict__ out) {
-  constexpr int PER = kUnits / SPLIT / THREADS;  // units per thread per tensor
+  constexpr int PER = UNITS / SPLIT / THREADS;  // units per thread per tensor
   const int ring = blockIdx.x / SPLIT, part = blockIdx.x % SPLIT;
-  const uint4* kb = K + (size_t)ring * kUnits + part * (kUnits / SPLIT);
-  const uint4* vb = V + (size_t)ring * kUnits + part * (kUnits / SPLIT);
+  const uint4* kb = K + (size_t)ring * UNITS + part * (UNITS / SPLIT);
+  const uint4* vb = V + (size_t)ring * UNITS + part * (UNITS / SPLIT);
   uint4 r[2 * PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) r[j] = load16<NT>(kb + j * THREADS + threadIdx.x);
@@ -49,6 +53,34 @@ __global__ __launch_bounds__(THREADS) void stream_k(const uint4* __restrict__ K,
 #pragma unroll
   for (int j = 1; j < 2 * PER; ++j) { acc.x ^= r[j].x; acc.y += r[j].y; acc.z ^= r[j].z; acc.w += r[j].w; }
   out[(size_t)blockIdx.x * THREADS + threadIdx.x] = acc;
+}
+
+// FP8-ring shape: 1024 16-byte units of K codes per ring read 16 bytes at a time, the V
+// codes 8 bytes at a time (2048 8-byte pieces per ring)
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void stream_fp8v8(const uint4* __restrict__ K, const uint4* __restrict__ V,
+                                                         uint4* __restrict__ out) {
+  constexpr int UNITS = kUnits / 2, PK = UNITS / THREADS, PV = 2 * UNITS / THREADS;
+  const uint4* kb = K + (size_t)blockIdx.x * UNITS;
+  const uint2* vb = reinterpret_cast<const uint2*>(V + (size_t)blockIdx.x * UNITS);
+  uint4 r[PK];
+  uint2 q[PV];
+#pragma unroll
+  for (int j = 0; j < PK; ++j) r[j] = kb[j * THREADS + threadIdx.x];
+#pragma unroll
+  for (int j = 0; j < PV; ++j) q[j] = vb[j * THREADS + threadIdx.x];
+  uint4 acc = r[0];
+#pragma unroll
+  for (int j = 1; j < PK; ++j) { acc.x ^= r[j].x; acc.y += r[j].y; acc.z ^= r[j].z; acc.w += r[j].w; }
+#pragma unroll
+  for (int j = 0; j < PV; ++j) { acc.x ^= q[j].x; acc.y += q[j].y; }
+  out[(size_t)blockIdx.x * THREADS + threadIdx.x] = acc;
+}
+
+// the same launch shape with no reads
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void write_only(uint4* __restrict__ out, unsigned seed) {
+  out[(size_t)blockIdx.x * THREADS + threadIdx.x] = make_uint4(seed, blockIdx.x, threadIdx.x, 0u);
 }
 
 // one wavefront per ring, loads issued in chunks of C units per lane in flight
@@ -130,6 +162,17 @@ int main() {
     printf("wave-per-ring chunk=%2d  %7.2f us  %6.0f GB/s\n", C, us, bytes / us / 1e3);             \
   }
   RUNW(8) RUNW(16) RUNW(32)
+  {
+    const double b8 = bytes / 2;
+    float us = time_it([&](int s) { stream_k<256, 1, false, kUnits / 2><<<kRings, 256>>>(K[s], V[s], out); }, iters);
+    printf("fp8-ring threads= 256 16-byte loads        %7.2f us  %6.0f GB/s\n", us, b8 / us / 1e3);
+    us = time_it([&](int s) { stream_k<256, 1, true, kUnits / 2><<<kRings, 256>>>(K[s], V[s], out); }, iters);
+    printf("fp8-ring threads= 256 16-byte loads, nt    %7.2f us  %6.0f GB/s\n", us, b8 / us / 1e3);
+    us = time_it([&](int s) { stream_fp8v8<256><<<kRings, 256>>>(K[s], V[s], out); }, iters);
+    printf("fp8-ring threads= 256 K 16-byte, V 8-byte  %7.2f us  %6.0f GB/s\n", us, b8 / us / 1e3);
+    us = time_it([&](int s) { write_only<256><<<kRings, 256>>>(out, (unsigned)s); }, iters);
+    printf("no reads threads= 256 wgs=1024             %7.2f us\n", us);
+  }
   CHECK(hipDeviceSynchronize());
   printf("done\n");
   return 0;
