@@ -961,6 +961,44 @@ def _oracle_decode_rope(x, window, base):
                                     window, io_dtype=io)
 
 
+@pytest.mark.parametrize("t_new", [1, 4])
+def test_decode_without_lse(t_new):
+    """return_lse=False takes the decode kernels' branch that writes no LSE: the outputs are
+    bitwise those of the same call with the LSE written (bf16 ring, FP8 ring, RoPE in the
+    kernel), and the bf16 ring's match the oracle."""
+    _say(f"decode T={t_new} without LSE (bf16 ring, FP8 ring, RoPE): bitwise vs with LSE, and vs the oracle")
+    x = wl.make_decode(16, t_new, 32, 4, 128, 128, "bf16", seed=4400 + t_new)
+    g = _gpu(x)
+    args = (g["q"], g["k_new"], g["v_new"], g["k_cache"], g["v_cache"], g["ring_head"], g["sinks"])
+    o1, lse1 = swa.swa_sink_decode(*args)
+    o0, lse0 = swa.swa_sink_decode(*args, return_lse=False)
+    torch.cuda.synchronize()
+    assert lse0 is None
+    assert torch.equal(o0, o1)
+    o_ref, l_ref = _oracle_decode(x, 128)
+    assert_close(torch.bfloat16, o0, o_ref, lse1, l_ref, f"decode T={t_new} without LSE")
+
+    xf = wl.make_decode_fp8(16, t_new, 32, 4, 128, 128, "bf16", seed=4500 + t_new)
+    gf = _gpu(xf)
+    fargs = (gf["q"], gf["k_new"], gf["v_new"], gf["k_cache"], gf["v_cache"], xf["k_scale"], xf["v_scale"],
+             gf["ring_head"], gf["sinks"])
+    o1, _ = swa.swa_sink_decode_fp8kv(*fargs)
+    o0, lse0 = swa.swa_sink_decode_fp8kv(*fargs, return_lse=False)
+    torch.cuda.synchronize()
+    assert lse0 is None
+    assert torch.equal(o0, o1)
+
+    xr = wl.make_decode_rope(16, t_new, 32, 4, 128, 128, "bf16", seed=4600 + t_new)
+    gr = _gpu(xr)
+    rargs = (gr["q"], gr["k_new"], gr["v_new"], gr["k_cache"], gr["v_cache"], gr["ring_head"], gr["positions"],
+             gr["sinks"], 10000.0)
+    o1, _ = swa.swa_sink_decode_rope(*rargs)
+    o0, lse0 = swa.swa_sink_decode_rope(*rargs, return_lse=False)
+    torch.cuda.synchronize()
+    assert lse0 is None
+    assert torch.equal(o0, o1)
+
+
 @pytest.mark.parametrize("t_new", [1, 2, 3, 4])
 def test_decode_rope_small(t_new):
     _say(f"decode with RoPE B=16 T={t_new} 32/4 D128 bf16 (matrix cores), positions up to 2^31")
