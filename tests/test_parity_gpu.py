@@ -1645,6 +1645,39 @@ def _sparse_gpu(x, idx, cnt, recent):
     return o, lse
 
 
+def test_prefill_and_sparse_without_lse():
+    """return_lse=False on the GA prefill, the prefill over E4M3 K/V and the sparse decode:
+    outputs bitwise those of the same call with the LSE written."""
+    _say("GA prefill, FP8-K/V prefill and sparse decode without LSE: bitwise vs with LSE")
+    x = wl.make_prefill([300, 77, 140], 32, 4, 128, "bf16", seed=4700)
+    g = _gpu(x)
+    o1, _ = swa.ga_causal_prefill(g["q"], g["k"], g["v"], g["cu_seqlens"])
+    o0, lse0 = swa.ga_causal_prefill(g["q"], g["k"], g["v"], g["cu_seqlens"], return_lse=False)
+    torch.cuda.synchronize()
+    assert lse0 is None
+    assert torch.equal(o0, o1)
+
+    f = wl.make_prefill_fp8([200, 45, 300], 32, 4, 128, "bf16", seed=4701)
+    gf = _gpu(f)
+    fargs = (gf["q"], gf["k"], gf["v"], f["k_scale"], f["v_scale"], gf["sinks"], gf["cu_seqlens"])
+    o1, _ = swa.swa_sink_prefill_fp8kv(*fargs, window=128)
+    o0, lse0 = swa.swa_sink_prefill_fp8kv(*fargs, window=128, return_lse=False)
+    torch.cuda.synchronize()
+    assert lse0 is None
+    assert torch.equal(o0, o1)
+
+    xs = wl.make_sparse(4, 32, 4, 128, 3000, "bf16", seed=4702, min_len=300)
+    idx, cnt = _topk_gpu(xs["scores"], xs["lengths"], 1024, 128)
+    gs = {k_: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k_, v in xs.items()}
+    sargs = (gs["q"], gs["k_cache"], gs["v_cache"], gs["lengths"], torch.as_tensor(idx, dtype=torch.int32).to(DEV),
+             torch.as_tensor(cnt, dtype=torch.int32).to(DEV), gs["sinks"])
+    o1, _ = swa.swa_sparse_decode(*sargs)
+    o0, lse0 = swa.swa_sparse_decode(*sargs, return_lse=False)
+    torch.cuda.synchronize()
+    assert lse0 is None
+    assert torch.equal(o0, o1)
+
+
 @pytest.mark.parametrize("case", [(8, 32, 4, 128, 6000, "bf16", 1024, 128, True),
                                   (6, 16, 2, 128, 3000, "bf16", 300, 37, False),
                                   (5, 8, 1, 128, 900, "bf16", 1024, 128, True),
