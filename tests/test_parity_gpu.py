@@ -1678,6 +1678,50 @@ def test_prefill_and_sparse_without_lse():
     assert torch.equal(o0, o1)
 
 
+def test_every_output_element_written():
+    """Outputs and LSE handed in filled with NaN come back equal, bit for bit, to freshly
+    allocated ones: every kernel writes every element of its outputs (ragged tails, an empty
+    sequence, sequence ends, the duplicate query columns of a decode with T < 4)."""
+    _say("every output element written: prefill (SWA, GA, FP8 K/V), decode T=1..4 (bf16, FP8, RoPE), sparse")
+
+    def check(fn, what):
+        o1, l1 = fn()
+        o2 = torch.full_like(o1, float("nan"))
+        l2 = torch.full_like(l1, float("nan"))
+        fn(out=o2, lse=l2)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, o1), what
+        assert torch.equal(l2, l1), what
+
+    x = wl.make_prefill([300, 0, 77, 141], 32, 4, 128, "bf16", seed=4800)
+    g = _gpu(x)
+    check(lambda **kw: swa.swa_sink_prefill(g["q"], g["k"], g["v"], g["sinks"], g["cu_seqlens"], **kw), "swa prefill")
+    check(lambda **kw: swa.ga_causal_prefill(g["q"], g["k"], g["v"], g["cu_seqlens"], **kw), "ga prefill")
+    f = wl.make_prefill_fp8([200, 0, 45, 133], 32, 4, 128, "bf16", seed=4801)
+    gf = _gpu(f)
+    check(lambda **kw: swa.swa_sink_prefill_fp8kv(gf["q"], gf["k"], gf["v"], f["k_scale"], f["v_scale"], gf["sinks"],
+                                                  gf["cu_seqlens"], **kw), "fp8 prefill")
+    for t_new in (1, 2, 3, 4):
+        d = _gpu(wl.make_decode(8, t_new, 32, 4, 128, 128, "bf16", seed=4810 + t_new))
+        check(lambda **kw: swa.swa_sink_decode(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"],
+                                               d["ring_head"], d["sinks"], **kw), f"decode T={t_new}")
+        df = wl.make_decode_fp8(8, t_new, 32, 4, 128, 128, "bf16", seed=4820 + t_new)
+        gd = _gpu(df)
+        check(lambda **kw: swa.swa_sink_decode_fp8kv(gd["q"], gd["k_new"], gd["v_new"], gd["k_cache"], gd["v_cache"],
+                                                     df["k_scale"], df["v_scale"], gd["ring_head"], gd["sinks"], **kw),
+              f"fp8 decode T={t_new}")
+        r = _gpu(wl.make_decode_rope(8, t_new, 32, 4, 128, 128, "bf16", seed=4830 + t_new))
+        check(lambda **kw: swa.swa_sink_decode_rope(r["q"], r["k_new"], r["v_new"], r["k_cache"], r["v_cache"],
+                                                    r["ring_head"], r["positions"], r["sinks"], 10000.0, **kw),
+              f"rope decode T={t_new}")
+    xs = wl.make_sparse(4, 32, 4, 128, 3000, "bf16", seed=4840, min_len=300)
+    idx, cnt = _topk_gpu(xs["scores"], xs["lengths"], 1024, 128)
+    gs = {k_: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k_, v in xs.items()}
+    ti, tc = torch.as_tensor(idx, dtype=torch.int32).to(DEV), torch.as_tensor(cnt, dtype=torch.int32).to(DEV)
+    check(lambda **kw: swa.swa_sparse_decode(gs["q"], gs["k_cache"], gs["v_cache"], gs["lengths"], ti, tc,
+                                             gs["sinks"], **kw), "sparse decode")
+
+
 @pytest.mark.parametrize("case", [(8, 32, 4, 128, 6000, "bf16", 1024, 128, True),
                                   (6, 16, 2, 128, 3000, "bf16", 300, 37, False),
                                   (5, 8, 1, 128, 900, "bf16", 1024, 128, True),
