@@ -1722,6 +1722,43 @@ def test_every_output_element_written():
                                              gs["sinks"], **kw), "sparse decode")
 
 
+def test_side_stream_and_repeat_are_bitwise_equal():
+    """Each entry point, called on torch's current stream, again on the same stream, and on a
+    second (default-priority) stream made current, gives the same bits: the kernels are
+    deterministic (no atomics, fixed reduction orders) and run on the stream they are given."""
+    _say("side stream and repeated calls: bitwise equal (SWA/GA prefill, decode T=4, FP8 decode, sparse)")
+    x = _gpu(wl.make_prefill([700, 33, 250], 32, 4, 128, "bf16", seed=4900))
+    d = _gpu(wl.make_decode(16, 4, 32, 4, 128, 128, "bf16", seed=4901))
+    df = wl.make_decode_fp8(16, 2, 32, 4, 128, 128, "bf16", seed=4902)
+    gd = _gpu(df)
+    xs = wl.make_sparse(4, 32, 4, 128, 3000, "bf16", seed=4903, min_len=300)
+    gs = {k_: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k_, v in xs.items()}
+
+    def run_all():
+        outs = list(swa.swa_sink_prefill(x["q"], x["k"], x["v"], x["sinks"], x["cu_seqlens"]))
+        outs += swa.ga_causal_prefill(x["q"], x["k"], x["v"], x["cu_seqlens"])
+        outs += swa.swa_sink_decode(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["ring_head"],
+                                    d["sinks"])
+        outs += swa.swa_sink_decode_fp8kv(gd["q"], gd["k_new"], gd["v_new"], gd["k_cache"], gd["v_cache"],
+                                          df["k_scale"], df["v_scale"], gd["ring_head"], gd["sinks"])
+        idx, cnt = swa.swa_topk_select(gs["scores"], gs["lengths"], k=1024, recent=128)
+        outs += [idx, cnt]
+        outs += swa.swa_sparse_decode(gs["q"], gs["k_cache"], gs["v_cache"], gs["lengths"], idx, cnt, gs["sinks"])
+        return outs
+
+    first = run_all()
+    again = run_all()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        on_side = run_all()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for a_, b_, c_ in zip(first, again, on_side):
+        assert torch.equal(a_, b_)
+        assert torch.equal(a_, c_)
+
+
 @pytest.mark.parametrize("case", [(8, 32, 4, 128, 6000, "bf16", 1024, 128, True),
                                   (6, 16, 2, 128, 3000, "bf16", 300, 37, False),
                                   (5, 8, 1, 128, 900, "bf16", 1024, 128, True),
