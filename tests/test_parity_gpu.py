@@ -1759,6 +1759,64 @@ def test_side_stream_and_repeat_are_bitwise_equal():
         assert torch.equal(a_, c_)
 
 
+def test_hip_graph_replays_match_eager():
+    """The library allocates nothing and issues no memset or synchronisation, so its calls can
+    be captured in a HIP graph: a graph holding a prefill, a decode (T = 4), a token selection
+    with its sparse decode and the backward on the library's own scratch array is replayed
+    three times, with new inputs copied in and eager work and synchronisations between the
+    replays, and every replay equals the eager calls on the same inputs bit for bit."""
+    _say("HIP graph: prefill + decode + selection/sparse decode + no-alloc backward, 3 replays vs eager")
+    x = _gpu(wl.make_prefill([500, 77], 32, 4, 128, "bf16", seed=5000))
+    d = _gpu(wl.make_decode(16, 4, 32, 4, 128, 128, "bf16", seed=5001))
+    xs = wl.make_sparse(4, 32, 4, 128, 3000, "bf16", seed=5002, min_len=300)
+    gs = {k_: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k_, v in xs.items()}
+    n, hq = x["q"].shape[0], x["q"].shape[1]
+    po, pl = torch.empty_like(x["q"]), torch.empty(n, hq, dtype=torch.float32, device=DEV)
+    do_, dl = torch.empty_like(d["q"]), torch.empty(d["q"].shape[:3], dtype=torch.float32, device=DEV)
+    ti = torch.empty(gs["scores"].shape[0], gs["scores"].shape[1], 1024, dtype=torch.int32, device=DEV)
+    tc = torch.empty(gs["scores"].shape[:2], dtype=torch.int32, device=DEV)
+    so, sl = torch.empty_like(gs["q"]), torch.empty(gs["q"].shape[:2], dtype=torch.float32, device=DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5003)
+    dout = torch.randn(x["q"].shape, generator=gen, device=DEV).to(torch.bfloat16)
+    grads = (torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"]),
+             torch.empty(hq, dtype=torch.float32, device=DEV))
+
+    def body():
+        swa.swa_sink_prefill(x["q"], x["k"], x["v"], x["sinks"], x["cu_seqlens"], out=po, lse=pl)
+        swa.swa_sink_decode(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["ring_head"], d["sinks"],
+                            out=do_, lse=dl)
+        swa.swa_topk_select(gs["scores"], gs["lengths"], k=1024, recent=128, indices=ti, counts=tc)
+        swa.swa_sparse_decode(gs["q"], gs["k_cache"], gs["v_cache"], gs["lengths"], ti, tc, gs["sinks"], out=so, lse=sl)
+        swa.swa_sink_prefill_backward(x["q"], x["k"], x["v"], x["sinks"], x["cu_seqlens"], po, pl, dout,
+                                      library_scratch=True, grads=grads)
+
+    side = torch.cuda.Stream()  # torch's capture recipe: warm up eagerly on a side stream
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        body()
+    torch.cuda.synchronize()
+    outs = (po, pl, do_, dl, ti, tc, so, sl) + grads
+    for rep in range(3):
+        x["q"].copy_(torch.randn(x["q"].shape, generator=gen, device=DEV).to(torch.bfloat16))
+        d["q"].copy_(torch.randn(d["q"].shape, generator=gen, device=DEV).to(torch.bfloat16))
+        gs["scores"].copy_(torch.randn(gs["scores"].shape, generator=gen, device=DEV))
+        dout.copy_(torch.randn(dout.shape, generator=gen, device=DEV).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in outs]
+        body()  # eager, same inputs, same buffers
+        torch.cuda.synchronize()
+        for i_, (a_, b_) in enumerate(zip(got, outs)):
+            assert torch.equal(a_, b_), f"replay {rep}: output {i_} differs from the eager call"
+
+
 @pytest.mark.parametrize("case", [(8, 32, 4, 128, 6000, "bf16", 1024, 128, True),
                                   (6, 16, 2, 128, 3000, "bf16", 300, 37, False),
                                   (5, 8, 1, 128, 900, "bf16", 1024, 128, True),
